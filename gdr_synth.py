@@ -1,0 +1,153 @@
+"""Seeded synthetic inputs for the gated delta-rule mixer.
+
+This module is the only code that both the GPU path's tests/benchmark and the
+CPU oracle's callers share. It draws random tensors and rounds them to their
+stored dtype; it contains none of the mixer's arithmetic.
+
+Recipe
+------
+* ``numpy.random.Generator(PCG64)``; one child stream per tensor from
+  ``SeedSequence(seed).spawn(8)``, in the fixed order q, k, v, beta, g, b, w,
+  S0 (a stream is spawned even when its tensor is absent, so adding a tensor
+  never shifts another one's numbers).
+* Draws are fp64. q and k are L2-normalised over d_k per (sequence, token,
+  head) in fp64. Every tensor is then rounded once, round-to-nearest-even,
+  to its stored dtype: bfloat16 (held as ``numpy.uint16`` bit patterns) or
+  float32. beta and g are always float32; b, w, q, k, v use the io dtype.
+* Distributions follow the workload texts: v ~ N(0,1); beta = sigmoid(N(0,1));
+  the decay alpha = exp(g) with g = log(sigmoid(N(2,1))) (small fp32 case),
+  g = -0.1 softplus(N(0,1)) (Qwen-shaped GDN prefill and decode), or
+  g = -0.05 softplus(N(0,1)) per key channel (KDA, Gated DeltaNet-2);
+  b, w = sigmoid(N(0,1)); the decode state S0 = 0.02 N(0,1) (0.02 read as a
+  standard deviation).
+* Prefill tensors are laid out [B, T, H, d]. Decode tensors are laid out
+  step-major, [steps, B, H, d], so each step's slice is contiguous;
+  ``as_sequence`` reorders them to [B, steps, H, d] for a sequential run.
+"""
+from __future__ import annotations
+
+import dataclasses
+from dataclasses import dataclass
+
+import numpy as np
+
+ORDER = ("q", "k", "v", "beta", "g", "b", "w", "S0")
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    T: int               # tokens per sequence (prefill) or consecutive steps (decode)
+    Hqk: int
+    Hv: int
+    dk: int
+    dv: int
+    io: str              # "bf16" | "f32"
+    decay: str           # "none" | "scalar" | "channel"
+    gates: str           # "beta" (tied) | "bw" (decoupled erase/write gates)
+    g_recipe: str        # "logsigmoid_n21" | "softplus_0.1" | "softplus_0.05" | "none"
+    S0: str = "zero"     # "zero" | "normal_0.02"
+    chunk: int = 64
+    scale: float = 1.0
+    decode: bool = False
+
+    def scaled(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+# The five workloads: small fp32 GDN; Qwen-shaped GDN prefill; GDN decode;
+# KDA prefill; Gated DeltaNet-2 long prefill.
+GDN_SMALL_F32 = Workload("gdn_small_f32_T64_d32", 1, 64, 1, 1, 32, 32, "f32", "scalar", "beta",
+                         "logsigmoid_n21")
+QWEN_GDN_PREFILL = Workload("qwen_gdn_prefill_T4096_Hqk16_Hv48_d128", 1, 4096, 16, 48, 128, 128,
+                            "bf16", "scalar", "beta", "softplus_0.1")
+QWEN_GDN_DECODE = Workload("qwen_gdn_decode_B64_Hv48_d128_256steps", 64, 256, 16, 48, 128, 128,
+                           "bf16", "scalar", "beta", "softplus_0.1", S0="normal_0.02", decode=True)
+KDA_PREFILL = Workload("kda_prefill_B2_T16384_H32_d128", 2, 16384, 32, 32, 128, 128, "bf16",
+                       "channel", "beta", "softplus_0.05")
+GDN2_PREFILL = Workload("gdn2_prefill_T65536_H16_d128", 1, 65536, 16, 16, 128, 128, "bf16",
+                        "channel", "bw", "softplus_0.05")
+WORKLOADS = (GDN_SMALL_F32, QWEN_GDN_PREFILL, QWEN_GDN_DECODE, KDA_PREFILL, GDN2_PREFILL)
+
+
+def bf16_bits(x) -> np.ndarray:
+    """Round fp64 values to bfloat16, nearest-even, in one step; return the bit
+    patterns as uint16. Values must lie in the normal float32 range (or be 0)."""
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    ax = np.abs(x)
+    if np.any((ax != 0) & ((ax < 2.0 ** -126) | (ax >= (2.0 - 2.0 ** -8) * 2.0 ** 127))) or not np.all(np.isfinite(x)):
+        raise ValueError("value outside the normal float32 range")
+    bits = x.view(np.uint64)
+    lsb = (bits >> np.uint64(45)) & np.uint64(1)
+    bits = (bits + np.uint64((1 << 44) - 1) + lsb) & ~np.uint64((1 << 45) - 1)
+    y = bits.view(np.float64).astype(np.float32)   # exact: 8 significant bits
+    return (y.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_to_f32(bits) -> np.ndarray:
+    return (np.asarray(bits).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _store(x, dtype):
+    return bf16_bits(x) if dtype == "bf16" else np.asarray(x, dtype=np.float64).astype(np.float32)
+
+
+def _sigmoid(x):
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def _softplus(x):
+    return np.logaddexp(0.0, x)
+
+
+def _l2n(x):
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+
+
+def make_inputs(wl: Workload, seed: int = 0) -> dict:
+    """Draw every input of ``wl``. Returns a dict of stored arrays (absent
+    tensors are None) plus ``"workload"`` and ``"seed"``."""
+    streams = dict(zip(ORDER, (np.random.Generator(np.random.PCG64(s))
+                               for s in np.random.SeedSequence(seed).spawn(len(ORDER)))))
+    lead = (wl.T, wl.B) if wl.decode else (wl.B, wl.T)
+    out = {"workload": wl, "seed": seed}
+    out["q"] = _store(_l2n(streams["q"].standard_normal(lead + (wl.Hqk, wl.dk))), wl.io)
+    out["k"] = _store(_l2n(streams["k"].standard_normal(lead + (wl.Hqk, wl.dk))), wl.io)
+    out["v"] = _store(streams["v"].standard_normal(lead + (wl.Hv, wl.dv)), wl.io)
+    if wl.gates == "beta":
+        out["beta"] = _store(_sigmoid(streams["beta"].standard_normal(lead + (wl.Hv,))), "f32")
+        out["b"] = out["w"] = None
+    else:
+        out["beta"] = None
+        out["b"] = _store(_sigmoid(streams["b"].standard_normal(lead + (wl.Hv, wl.dk))), wl.io)
+        out["w"] = _store(_sigmoid(streams["w"].standard_normal(lead + (wl.Hv, wl.dv))), wl.io)
+    if wl.decay == "none":
+        out["g"] = None
+    else:
+        gshape = lead + ((wl.Hv,) if wl.decay == "scalar" else (wl.Hv, wl.dk))
+        x = streams["g"].standard_normal(gshape)
+        if wl.g_recipe == "logsigmoid_n21":
+            g = -_softplus(-(2.0 + x))          # log(sigmoid(x')), x' ~ N(2, 1)
+        elif wl.g_recipe == "softplus_0.1":
+            g = -0.1 * _softplus(x)
+        elif wl.g_recipe == "softplus_0.05":
+            g = -0.05 * _softplus(x)
+        else:
+            raise ValueError(wl.g_recipe)
+        out["g"] = _store(g, "f32")
+    if wl.S0 == "normal_0.02":
+        out["S0"] = _store(0.02 * streams["S0"].standard_normal((wl.B, wl.Hv, wl.dk, wl.dv)), "f32")
+    else:
+        out["S0"] = None
+    return out
+
+
+def as_sequence(inp: dict) -> dict:
+    """Decode inputs are step-major [steps, B, ...]; return a copy with every
+    per-step tensor reordered to [B, steps, ...] (a sequential run's layout)."""
+    out = dict(inp)
+    for name in ("q", "k", "v", "beta", "g", "b", "w"):
+        if inp.get(name) is not None:
+            out[name] = np.ascontiguousarray(np.swapaxes(inp[name], 0, 1))
+    return out

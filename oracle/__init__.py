@@ -1,0 +1,158 @@
+"""CPU oracle for the gated delta-rule mixer.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import anything here. The GPU library
+(``gated_delta_rule_23_amd``) never imports this package, and this package
+never imports it: the two share no code. The only module both sides use is
+the seeded input generator ``gdr_synth``, which holds none of the method's
+arithmetic.
+
+Contents
+--------
+``recurrent``      the production oracle: the token-by-token recurrence in
+                   fp64 (plain C in ``gdr_oracle.c``, run on host threads).
+``forms``          check-oracles, each the literal form one page prints, in
+                   that page's own layout, for tiny sizes (numpy, fp64).
+``chunked``        the chunked (UT/WY) form on the CPU, fp64, used to pin the
+                   chunk algebra against the sequential result.
+
+Stored values: a ``numpy.uint16`` array holds bfloat16 bit patterns, a
+``float32`` or ``float64`` array holds its own values. Every value is widened
+exactly to fp64 before any arithmetic.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdr_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libgdr_oracle.so")
+_lib = None
+
+DECAY_NONE, DECAY_SCALAR, DECAY_CHANNEL = 0, 1, 2
+
+
+def build(force: bool = True) -> str:
+    """Compile ``gdr_oracle.c`` with gcc into ``libgdr_oracle.so``.
+
+    Plain IEEE double arithmetic: no fast-math, no FMA contraction, so every
+    operation rounds once in the order the source writes it.
+    """
+    global _lib
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared",
+               "-pthread", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+        _lib = None
+    return _LIB_PATH
+
+
+def load_library(path: str):
+    """Open a compiled oracle library and declare its entry point."""
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    lib.gdr_oracle_recurrent.restype = I
+    lib.gdr_oracle_recurrent.argtypes = [I, I, I, I, I, I, P, P, P, P, I, P, P, P,
+                                         ctypes.c_double, P, P, P, P, I, I, I, I]
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=True)
+        _lib = load_library(_LIB_PATH)
+    return _lib
+
+
+def upcast(a):
+    """Widen stored values exactly to fp64 (uint16 = bfloat16 bit patterns)."""
+    if a is None:
+        return None
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if a.dtype in (np.float32, np.float64):
+        return a.astype(np.float64)
+    raise TypeError(f"unsupported stored dtype {a.dtype}")
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def recurrent(q, k, v, *, g=None, beta=None, b=None, w=None, scale=1.0, S0=None,
+              heads=None, cols=None, nthreads=None, lib=None):
+    """Token-by-token fp64 recurrence (the production oracle).
+
+    Shapes: q, k [B,T,Hqk,dk]; v [B,T,Hv,dv]; g None, [B,T,Hv] (scalar decay)
+    or [B,T,Hv,dk] (per-channel decay); beta [B,T,Hv] (tied gates) or None
+    with b [B,T,Hv,dk] and w [B,T,Hv,dv] (decoupled gates); S0 None or
+    [B,Hv,dk,dv]. ``heads``: V heads to compute (default all); ``cols``:
+    (c0, c1) value-column range (default all); ``lib``: a library from
+    ``load_library`` to use instead of the built one. Entries of o and S_T outside
+    the selection are NaN.
+
+    Returns (o [B,T,Hv,dv], S_T [B,Hv,dk,dv]) in fp64.
+    """
+    q, k, v = (np.ascontiguousarray(upcast(x)) for x in (q, k, v))
+    B, T, Hqk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    if k.shape != q.shape or v.shape[:2] != (B, T):
+        raise ValueError("q, k, v shapes disagree")
+    if g is None:
+        decay = DECAY_NONE
+    else:
+        g = np.ascontiguousarray(upcast(g))
+        if g.shape == (B, T, Hv):
+            decay = DECAY_SCALAR
+        elif g.shape == (B, T, Hv, dk):
+            decay = DECAY_CHANNEL
+        else:
+            raise ValueError(f"g has shape {g.shape}")
+        if not np.all(np.isfinite(g)) or np.any(g > 0):
+            raise ValueError("g = log(alpha) must be finite and <= 0")
+    if beta is not None:
+        if b is not None or w is not None:
+            raise ValueError("beta and (b, w) are exclusive")
+        beta = np.ascontiguousarray(upcast(beta))
+        if beta.shape != (B, T, Hv):
+            raise ValueError("beta shape")
+    else:
+        if b is None or w is None:
+            raise ValueError("need beta, or both b and w")
+        b = np.ascontiguousarray(upcast(b))
+        w = np.ascontiguousarray(upcast(w))
+        if b.shape != (B, T, Hv, dk) or w.shape != (B, T, Hv, dv):
+            raise ValueError("b / w shape")
+    if S0 is not None:
+        S0 = np.ascontiguousarray(upcast(S0))
+        if S0.shape != (B, Hv, dk, dv):
+            raise ValueError("S0 shape")
+    hl = None if heads is None else np.ascontiguousarray(np.asarray(heads, dtype=np.int32))
+    c0, c1 = (0, dv) if cols is None else cols
+    o = np.full((B, T, Hv, dv), np.nan)
+    ST = np.full((B, Hv, dk, dv), np.nan)
+    nt = default_threads() if nthreads is None else nthreads
+    rc = (lib or _load()).gdr_oracle_recurrent(
+        B, T, Hqk, Hv, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(g), decay, _ptr(beta),
+        _ptr(b), _ptr(w), float(scale), _ptr(S0), _ptr(o), _ptr(ST), _ptr(hl),
+        0 if hl is None else len(hl), c0, c1, nt)
+    if rc != 0:
+        raise RuntimeError(f"gdr_oracle_recurrent failed with {rc}")
+    return o, ST
