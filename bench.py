@@ -1,0 +1,196 @@
+"""Benchmark of the gated delta-rule hot path on one MI355X.
+
+One step = one chunked prefill of the Qwen3.8-27B-shaped Gated DeltaNet layer
+(B=1, T=4096, 16 QK heads, 48 V heads, d=128, bf16 io, fp32 state, chunk 64)
+through gdr_chunk_fwd. In the same run the decode step is measured on its own
+workload (64 sequences x 48 V heads, 128 x 128 fp32 states, 256 consecutive
+gdr_decode_step calls). Inputs are seeded synthetic tensors already resident
+in device memory when timing starts. Timing uses HIP events recorded on the
+stream the kernels run on.
+
+Prints one JSON line: value = prefill tokens/s; "roofline" for the prefill
+call against HBM; "decode" with state GB/s and its own roofline; and
+"cpu_baseline", the fp64 CPU oracle timed on a bounded sample of the same
+prefill workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix, published
+
+
+def prefill_algorithmic(wl):
+    """Bytes and flops the prefill must move / compute (each input read once,
+    each QK head's q, k counted once, outputs and the final state written once;
+    chunked-form flops with dense C x C tiles)."""
+    esz = 2 if wl.io == "bf16" else 4
+    B, T, Hqk, Hv, D = wl.B, wl.T, wl.Hqk, wl.Hv, wl.dk
+    by = 2 * B * T * Hqk * D * esz + B * T * Hv * D * esz          # q, k, v
+    by += B * T * Hv * 4 if wl.gates == "beta" else 2 * B * T * Hv * D * esz   # beta or b, w
+    by += {"none": 0, "scalar": B * T * Hv * 4, "channel": B * T * Hv * D * 4}[wl.decay]
+    by += B * T * Hv * D * esz + B * Hv * D * D * 4                # o, S_T
+    C = wl.chunk
+    flops_per_token_head = 2 * C * (3 * D + 2 * D) + 6 * D * D
+    return by, flops_per_token_head * B * T * Hv
+
+
+def decode_algorithmic(wl):
+    esz = 2 if wl.io == "bf16" else 4
+    B, Hqk, Hv, D = wl.B, wl.Hqk, wl.Hv, wl.dk
+    state = 2 * B * Hv * D * D * 4
+    io = 2 * B * Hqk * D * esz + 2 * B * Hv * D * esz + 2 * B * Hv * 4
+    return state, state + io
+
+
+def cpu_baseline(wl, inp, heads):
+    import oracle
+    t0 = time.perf_counter()
+    oracle.recurrent(inp["q"], inp["k"], inp["v"], g=inp["g"], beta=inp["beta"], b=inp["b"], w=inp["w"],
+                     scale=wl.scale, S0=inp["S0"], heads=heads)
+    dt = time.perf_counter() - t0
+    toks = wl.B * wl.T * len(heads) / wl.Hv
+    return {"value": toks / dt, "unit": "tokens/s", "cores": oracle.default_threads(), "kind": "oracle",
+            "sample": f"fp64 token-by-token oracle on {len(heads)} of {wl.Hv} V heads, all {wl.T} tokens "
+                      f"(scaled to whole-layer tokens/s); {dt:.1f} s"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--cpu-heads", type=int, default=12, help="V heads in the CPU-oracle sample (0 = skip)")
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (the mixer shards over "
+              "sequences and heads with no communication); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import gated_delta_rule_23_amd as gdr
+    import gdr_synth as gs
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def up(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    # ---- prefill ----
+    wl = gs.QWEN_GDN_PREFILL
+    inp = gs.make_inputs(wl, seed=args.seed)
+    d = {n: up(inp[n]) for n in ("q", "k", "v", "g", "beta", "b", "w")}
+    desc = gdr.make_desc(wl.B, wl.T, wl.Hqk, wl.Hv, wl.dk, gdr.GDR_BF16, gdr.GDR_DECAY_SCALAR, wl.scale)
+    ws = torch.empty(gdr.gdr_chunk_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    o = torch.empty((wl.B, wl.T, wl.Hv, wl.dv), dtype=torch.bfloat16, device=dev)
+    ST = torch.empty((wl.B, wl.Hv, wl.dk, wl.dv), dtype=torch.float32, device=dev)
+
+    def prefill():
+        gdr.gdr_chunk_fwd(d["q"], d["k"], d["v"], g=d["g"], beta=d["beta"], b=d["b"], w=d["w"], S0=None,
+                          scale=wl.scale, o=o, ST=ST, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        prefill()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        prefill()
+        ev[i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    call_ms = [a.elapsed_time(b) for a, b in ev]
+    ms_per_step = total_ms / args.steps
+    avg_call_ms = sum(call_ms) / len(call_ms)
+    tokens = wl.B * wl.T
+    pbytes, pflops = prefill_algorithmic(wl)
+    achieved = pbytes / (avg_call_ms * 1e-3) / 1e9
+
+    # ---- decode ----
+    dwl = gs.QWEN_GDN_DECODE.scaled(T=args.decode_steps)
+    dinp = gs.make_inputs(dwl, seed=args.seed + 1)
+    dd = {n: up(dinp[n]) for n in ("q", "k", "v", "g", "beta", "b", "w")}
+    S = up(dinp["S0"]).clone()
+    do = torch.empty((dwl.B, dwl.Hv, dwl.dv), dtype=torch.bfloat16, device=dev)
+
+    def dstep(s):
+        pick = lambda t: None if t is None else t[s]
+        gdr.gdr_decode_step(pick(dd["q"]), pick(dd["k"]), pick(dd["v"]), S, g=pick(dd["g"]), beta=pick(dd["beta"]),
+                            b=pick(dd["b"]), w=pick(dd["w"]), scale=dwl.scale, o=do, stream=stream)
+
+    for s in range(min(8, dwl.T)):
+        dstep(s)
+    S.copy_(up(dinp["S0"]))
+    torch.cuda.synchronize()
+    dev_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(dwl.T)]
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    d0.record(stream)
+    for s in range(dwl.T):
+        dev_ev[s][0].record(stream)
+        dstep(s)
+        dev_ev[s][1].record(stream)
+    d1.record(stream)
+    torch.cuda.synchronize()
+    d_total_ms = d0.elapsed_time(d1)
+    d_step_ms = sorted(a.elapsed_time(b) for a, b in dev_ev)
+    d_avg_ms = sum(d_step_ms) / len(d_step_ms)
+    state_bytes, d_bytes = decode_algorithmic(dwl)
+    d_achieved = d_bytes / (d_avg_ms * 1e-3) / 1e9
+
+    out = {
+        "metric": "prefill tokens/s and decode state GB/s for gated delta rule, % of roofline",
+        "value": tokens / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), beta=sigmoid(N(0,1)), "
+                "g=-0.1*softplus(N(0,1)))",
+        "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "H_qk": wl.Hqk, "H_v": wl.Hv, "d_k": wl.dk,
+                   "d_v": wl.dv, "chunk": wl.chunk, "io": wl.io, "state": "fp32", "S0": "zeros"},
+        "roofline": {"kernel": "gdr_chunk_fwd (chunk_prep + chunk_sweep)", "bound": "hbm",
+                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": None, "algorithmic_bytes": pbytes, "avg_call_ms": avg_call_ms},
+        "mfma": {"algorithmic_tflops": pflops / (avg_call_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
+                 "frac": pflops / (avg_call_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, "algorithmic_flops": pflops},
+        "decode": {"workload": dwl.name, "steps": dwl.T, "ms_per_step": d_total_ms / dwl.T,
+                   "kernel_avg_ms": d_avg_ms, "kernel_median_ms": d_step_ms[len(d_step_ms) // 2],
+                   "state_GBps": state_bytes / (d_avg_ms * 1e-3) / 1e9,
+                   "tokens_per_s": dwl.B / (d_total_ms / dwl.T * 1e-3),
+                   "roofline": {"kernel": "decode_kernel", "bound": "hbm", "achieved": d_achieved,
+                                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": d_achieved / HBM_PEAK_GBPS,
+                                "traffic": None, "algorithmic_bytes": d_bytes}},
+    }
+    if args.cpu_heads > 0:
+        heads = list(range(0, wl.Hv, max(1, wl.Hv // args.cpu_heads)))[:args.cpu_heads]
+        out["cpu_baseline"] = cpu_baseline(wl, inp, heads)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

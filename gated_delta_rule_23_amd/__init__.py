@@ -1,0 +1,220 @@
+"""MI355X (gfx950) gated delta-rule mixer: Python binding of libgdr.
+
+The functions here carry the C ABI's names (``include/gdr.h``) and do only
+argument marshalling: shapes and dtypes are read from torch tensors, which
+provide device memory and the current stream; every step of the computation
+runs in the HIP kernels of ``libgdr.so``. There is no fallback: importing
+this package without a built ``libgdr.so`` raises.
+
+Tensor layouts (contiguous, on the same GPU):
+  prefill  q, k [B,T,Hqk,D]; v [B,T,Hv,D]; beta [B,T,Hv] f32;
+           g [B,T,Hv] or [B,T,Hv,D] f32; b [B,T,Hv,D]; w [B,T,Hv,D];
+           state [B,Hv,D,D] f32 (row = key channel, column = value channel)
+  decode   the same without the T axis.
+q, k, v, b, w and the output share one dtype: torch.bfloat16 or torch.float32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgdr.so")
+
+GDR_OK, GDR_E_INVAL, GDR_E_UNSUPPORTED, GDR_E_HIP, GDR_E_NOMEM = 0, -1, -2, -3, -4
+GDR_F32, GDR_BF16 = 0, 1
+GDR_DECAY_NONE, GDR_DECAY_SCALAR, GDR_DECAY_CHANNEL = 0, 1, 2
+CHUNK = 64
+
+# Every symbol include/gdr.h declares.
+EXPORTS = ("gdr_state_bytes", "gdr_state_alloc", "gdr_state_free", "gdr_chunk_workspace_bytes",
+           "gdr_chunk_fwd", "gdr_decode_step", "gdr_last_error", "gdr_version")
+
+
+class GdrError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"libgdr status {status}: {message}")
+        self.status = status
+
+
+class gdr_desc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("T", ctypes.c_int), ("H_qk", ctypes.c_int), ("H_v", ctypes.c_int),
+                ("d_k", ctypes.c_int), ("d_v", ctypes.c_int), ("io_dtype", ctypes.c_int),
+                ("decay", ctypes.c_int), ("chunk", ctypes.c_int), ("scale", ctypes.c_float)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run gated_delta_rule_23_amd/build.py "
+                          "(or __graft_entry__.build()) first; there is no non-HIP fallback")
+    # torch ships its own HIP runtime with the same SONAME (libamdhip64.so.7).
+    # Loading torch first makes libgdr.so bind to that runtime, so the library
+    # and torch share one runtime, one device context and the same streams.
+    try:
+        import torch  # noqa: F401
+    except ImportError:  # pragma: no cover - C-only use without torch
+        pass
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    D = ctypes.POINTER(gdr_desc)
+    lib.gdr_state_bytes.restype = S
+    lib.gdr_state_bytes.argtypes = [I, I, I, I]
+    lib.gdr_state_alloc.restype = I
+    lib.gdr_state_alloc.argtypes = [I, I, I, I, ctypes.POINTER(P), ctypes.POINTER(S), P]
+    lib.gdr_state_free.restype = I
+    lib.gdr_state_free.argtypes = [P]
+    lib.gdr_chunk_workspace_bytes.restype = I
+    lib.gdr_chunk_workspace_bytes.argtypes = [D, ctypes.POINTER(S)]
+    lib.gdr_chunk_fwd.restype = I
+    lib.gdr_chunk_fwd.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, S, P]
+    lib.gdr_decode_step.restype = I
+    lib.gdr_decode_step.argtypes = [D, P, P, P, P, P, P, P, P, P, P]
+    lib.gdr_last_error.restype = ctypes.c_char_p
+    lib.gdr_last_error.argtypes = []
+    lib.gdr_version.restype = I
+    lib.gdr_version.argtypes = []
+    return lib
+
+
+lib = _load()
+
+
+def _check(rc: int):
+    if rc != GDR_OK:
+        raise GdrError(rc, lib.gdr_last_error().decode())
+
+
+def gdr_last_error() -> str:
+    return lib.gdr_last_error().decode()
+
+
+def gdr_version() -> int:
+    return lib.gdr_version()
+
+
+def gdr_state_bytes(B: int, H_v: int, d_k: int, d_v: int) -> int:
+    return lib.gdr_state_bytes(B, H_v, d_k, d_v)
+
+
+def gdr_state_alloc(B: int, H_v: int, d_k: int, d_v: int, stream=None):
+    """Allocate a zero-filled fp32 state through the library. Returns (device
+    pointer as int, bytes); free it with gdr_state_free."""
+    p, n = ctypes.c_void_p(), ctypes.c_size_t()
+    _check(lib.gdr_state_alloc(B, H_v, d_k, d_v, ctypes.byref(p), ctypes.byref(n), _stream(stream)))
+    return p.value, n.value
+
+
+def gdr_state_free(ptr) -> None:
+    _check(lib.gdr_state_free(ptr))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        torch = _torch()
+        if torch.cuda.is_available():
+            return torch.cuda.current_stream().cuda_stream
+        return None
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def _io_dtype(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return GDR_BF16
+    if t.dtype == torch.float32:
+        return GDR_F32
+    raise TypeError(f"io tensors must be bfloat16 or float32, got {t.dtype}")
+
+
+def _require(t, name, shape=None, dtype=None, device=None):
+    if t is None:
+        return
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def make_desc(B, T, Hqk, Hv, D, io, decay, scale=1.0, chunk=CHUNK) -> gdr_desc:
+    return gdr_desc(B, T, Hqk, Hv, D, D, io, decay, chunk, float(scale))
+
+
+def gdr_chunk_workspace_bytes(desc: gdr_desc) -> int:
+    n = ctypes.c_size_t()
+    _check(lib.gdr_chunk_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def _decay_of(g, lead, Hv, D):
+    if g is None:
+        return GDR_DECAY_NONE
+    if tuple(g.shape) == tuple(lead) + (Hv,):
+        return GDR_DECAY_SCALAR
+    if tuple(g.shape) == tuple(lead) + (Hv, D):
+        return GDR_DECAY_CHANNEL
+    raise ValueError(f"g has shape {tuple(g.shape)}")
+
+
+def gdr_chunk_fwd(q, k, v, *, g=None, beta=None, b=None, w=None, S0=None, scale=1.0, chunk=CHUNK,
+                  o=None, ST=None, workspace=None, stream=None):
+    """Chunked prefill. Returns (o, ST); ST may be passed equal to S0 for an
+    in-place state update. ``workspace`` (a uint8 tensor of at least
+    gdr_chunk_workspace_bytes) is allocated here when not given."""
+    torch = _torch()
+    B, T, Hqk, D = q.shape
+    Hv = v.shape[2]
+    dev, io_t = q.device, q.dtype
+    for name, t, shape in (("q", q, (B, T, Hqk, D)), ("k", k, (B, T, Hqk, D)), ("v", v, (B, T, Hv, D)),
+                           ("b", b, (B, T, Hv, D)), ("w", w, (B, T, Hv, D))):
+        _require(t, name, shape, io_t, dev)
+    _require(beta, "beta", (B, T, Hv), torch.float32, dev)
+    _require(g, "g", None, torch.float32, dev)
+    _require(S0, "S0", (B, Hv, D, D), torch.float32, dev)
+    desc = make_desc(B, T, Hqk, Hv, D, _io_dtype(q), _decay_of(g, (B, T), Hv, D), scale, chunk)
+    if o is None:
+        o = torch.empty((B, T, Hv, D), dtype=io_t, device=dev)
+    if ST is None:
+        ST = torch.empty((B, Hv, D, D), dtype=torch.float32, device=dev)
+    _require(o, "o", (B, T, Hv, D), io_t, dev)
+    _require(ST, "ST", (B, Hv, D, D), torch.float32, dev)
+    nbytes = gdr_chunk_workspace_bytes(desc)
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.gdr_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(b),
+                             _ptr(w), _ptr(S0), _ptr(o), _ptr(ST), _ptr(workspace), wsz, _stream(stream)))
+    return o, ST
+
+
+def gdr_decode_step(q, k, v, S, *, g=None, beta=None, b=None, w=None, scale=1.0, o=None, stream=None):
+    """One decode step, updating S [B,Hv,D,D] in place. Returns o [B,Hv,D]."""
+    torch = _torch()
+    B, Hqk, D = q.shape
+    Hv = v.shape[1]
+    dev, io_t = q.device, q.dtype
+    for name, t, shape in (("q", q, (B, Hqk, D)), ("k", k, (B, Hqk, D)), ("v", v, (B, Hv, D)),
+                           ("b", b, (B, Hv, D)), ("w", w, (B, Hv, D))):
+        _require(t, name, shape, io_t, dev)
+    _require(beta, "beta", (B, Hv), torch.float32, dev)
+    _require(g, "g", None, torch.float32, dev)
+    _require(S, "S", (B, Hv, D, D), torch.float32, dev)
+    desc = make_desc(B, 1, Hqk, Hv, D, _io_dtype(q), _decay_of(g, (B,), Hv, D), scale)
+    if o is None:
+        o = torch.empty((B, Hv, D), dtype=io_t, device=dev)
+    _require(o, "o", (B, Hv, D), io_t, dev)
+    _check(lib.gdr_decode_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(b),
+                               _ptr(w), _ptr(S), _ptr(o), _stream(stream)))
+    return o

@@ -1,0 +1,181 @@
+// abi.hip -- the extern "C" boundary of libgdr (declared in include/gdr.h).
+//
+// Every entry point validates its arguments completely before touching the
+// HIP runtime, so a rejected call enqueues nothing and needs no GPU. Errors
+// are integer status codes plus a per-thread message (gdr_last_error).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "gdr.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int ok() {
+    g_err.clear();
+    return GDR_OK;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+    return fail(GDR_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool supported_dim(int d) { return d == 32 || d == 64 || d == 128; }
+
+// Largest element count of any [B, T, H, D] array must fit comfortably in
+// 64-bit offsets and in the 31-bit grid dimensions used by the launches.
+bool size_ok(long long B, long long T, long long H, long long D) {
+    const long long lim = (long long)1 << 40;
+    return B <= lim && T <= lim && H <= lim && D <= lim && B * T <= lim && B * T * H <= lim && B * T * H * D <= lim;
+}
+
+// Checks shared by prefill and decode. `prefill` selects the T / chunk checks.
+int validate(const gdr_desc *d, bool prefill, const void *q, const void *k, const void *v, const float *g,
+             const float *beta, const void *b, const void *w, const void *o) {
+    if (!d) return fail(GDR_E_INVAL, "desc is NULL");
+    if (d->B < 0) return fail(GDR_E_INVAL, "B = %d must be >= 0", d->B);
+    if (prefill && d->T < 0) return fail(GDR_E_INVAL, "T = %d must be >= 0", d->T);
+    if (d->H_qk <= 0 || d->H_v <= 0) return fail(GDR_E_INVAL, "H_qk = %d and H_v = %d must be > 0", d->H_qk, d->H_v);
+    if (d->H_v % d->H_qk != 0)
+        return fail(GDR_E_INVAL, "H_v = %d must be a multiple of H_qk = %d", d->H_v, d->H_qk);
+    if (d->d_k <= 0 || d->d_v <= 0) return fail(GDR_E_INVAL, "d_k = %d and d_v = %d must be > 0", d->d_k, d->d_v);
+    if (d->io_dtype != GDR_F32 && d->io_dtype != GDR_BF16) return fail(GDR_E_INVAL, "io_dtype = %d", d->io_dtype);
+    if (d->decay < GDR_DECAY_NONE || d->decay > GDR_DECAY_CHANNEL) return fail(GDR_E_INVAL, "decay = %d", d->decay);
+    if (!std::isfinite(d->scale)) return fail(GDR_E_INVAL, "scale must be finite");
+    if (d->d_k != d->d_v || !supported_dim(d->d_k))
+        return fail(GDR_E_UNSUPPORTED, "d_k = %d, d_v = %d: supported are d_k == d_v in {32, 64, 128}", d->d_k, d->d_v);
+    if (prefill) {
+        if (d->chunk != gdr::kChunk) return fail(GDR_E_UNSUPPORTED, "chunk = %d: only 64 is supported", d->chunk);
+        if (!gdr::chunk_supported(d->io_dtype == GDR_BF16 ? gdr::IO_BF16 : gdr::IO_F32, d->d_k))
+            return fail(GDR_E_UNSUPPORTED, "prefill with float32 io supports d in {32, 64}");
+    }
+    if (!size_ok(d->B, prefill ? d->T : 1, d->H_v, d->d_k) || !size_ok(d->B, prefill ? d->T : 1, d->H_qk, d->d_k))
+        return fail(GDR_E_INVAL, "sizes too large");
+    // An empty call (no sequences, or no tokens) reads and writes no per-token
+    // array, so those pointers may be NULL (empty tensors have no storage).
+    if (d->B == 0 || (prefill && d->T == 0)) return GDR_OK;
+    if (!q || !k || !v || !o) return fail(GDR_E_INVAL, "q, k, v and o must be non-NULL");
+    if ((d->decay == GDR_DECAY_NONE) != (g == nullptr))
+        return fail(GDR_E_INVAL, "g must be NULL exactly when decay is GDR_DECAY_NONE");
+    if (beta) {
+        if (b || w) return fail(GDR_E_INVAL, "beta given: b and w must be NULL (tied gates)");
+    } else {
+        if (!b || !w) return fail(GDR_E_INVAL, "beta NULL: both b and w must be given (decoupled gates)");
+    }
+    return GDR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *gdr_last_error(void) { return g_err.c_str(); }
+
+int gdr_version(void) { return 1; }
+
+size_t gdr_state_bytes(int B, int H_v, int d_k, int d_v) {
+    if (B <= 0 || H_v <= 0 || d_k <= 0 || d_v <= 0) return 0;
+    return (size_t)B * H_v * d_k * d_v * sizeof(float);
+}
+
+int gdr_state_alloc(int B, int H_v, int d_k, int d_v, float **state, size_t *bytes, void *stream) {
+    if (!state) return fail(GDR_E_INVAL, "state is NULL");
+    *state = nullptr;
+    const size_t n = gdr_state_bytes(B, H_v, d_k, d_v);
+    if (n == 0) return fail(GDR_E_INVAL, "sizes must be > 0");
+    void *p = nullptr;
+    hipError_t e = hipMalloc(&p, n);
+    if (e != hipSuccess) return fail(GDR_E_NOMEM, "hipMalloc(%zu): %s", n, hipGetErrorString(e));
+    e = gdr::launch_state_fill(static_cast<float *>(p), nullptr, n / sizeof(float), static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+        (void)hipFree(p);
+        return hip_fail(e, "zero fill");
+    }
+    *state = static_cast<float *>(p);
+    if (bytes) *bytes = n;
+    return ok();
+}
+
+int gdr_state_free(float *state) {
+    if (!state) return ok();
+    hipError_t e = hipFree(state);
+    if (e != hipSuccess) return hip_fail(e, "hipFree");
+    return ok();
+}
+
+int gdr_chunk_workspace_bytes(const gdr_desc *d, size_t *bytes) {
+    if (!bytes) return fail(GDR_E_INVAL, "bytes is NULL");
+    *bytes = 0;
+    // Pointers are not known here; validate the sizes with dummy non-NULL pointers.
+    static const char dummy = 0;
+    const void *p = &dummy;
+    const int rc = validate(d, true, p, p, p, d && d->decay != GDR_DECAY_NONE ? (const float *)p : nullptr,
+                            (const float *)p, nullptr, nullptr, p);
+    if (rc != GDR_OK) return rc;
+    const int NC = (d->T + gdr::kChunk - 1) / gdr::kChunk;
+    *bytes = gdr::chunk_ws_bytes(d->B, d->H_v, NC, d->d_k, d->io_dtype == GDR_BF16 ? gdr::IO_BF16 : gdr::IO_F32);
+    return ok();
+}
+
+int gdr_chunk_fwd(const gdr_desc *d, const void *q, const void *k, const void *v, const float *g, const float *beta,
+                  const void *b, const void *w, const float *S0, void *o, float *ST, void *workspace,
+                  size_t workspace_bytes, void *stream) {
+    int rc = validate(d, true, q, k, v, g, beta, b, w, o);
+    if (rc != GDR_OK) return rc;
+    if (!ST) return fail(GDR_E_INVAL, "ST must be non-NULL");
+    const int io = d->io_dtype == GDR_BF16 ? gdr::IO_BF16 : gdr::IO_F32;
+    const int NC = (d->T + gdr::kChunk - 1) / gdr::kChunk;
+    const size_t need = gdr::chunk_ws_bytes(d->B, d->H_v, NC, d->d_k, io);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(GDR_E_INVAL, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+    if (d->B == 0) return ok();
+    const size_t units = (size_t)d->B * d->H_v * NC;
+    if (units > 0x7fffffffull) return fail(GDR_E_UNSUPPORTED, "too many chunks for one launch");
+
+    gdr::ChunkArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.bg = b; a.wg = w;
+    a.S0 = S0; a.o = o; a.ST = ST;
+    a.ws_io = workspace;
+    a.ws_gamma = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                           gdr::align256(units * gdr::chunk_ws_io_elems(d->d_k) * (io == gdr::IO_BF16 ? 2 : 4)));
+    a.B = d->B; a.T = d->T; a.Hqk = d->H_qk; a.Hv = d->H_v; a.decay = d->decay; a.NC = NC;
+    a.scale = d->scale;
+    hipError_t e = gdr::launch_chunk(io, d->d_k, a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "chunk prefill launch");
+    return ok();
+}
+
+int gdr_decode_step(const gdr_desc *d, const void *q, const void *k, const void *v, const float *g, const float *beta,
+                    const void *b, const void *w, float *S, void *o, void *stream) {
+    int rc = validate(d, false, q, k, v, g, beta, b, w, o);
+    if (rc != GDR_OK) return rc;
+    if (!S) return fail(GDR_E_INVAL, "S must be non-NULL");
+    if (d->B == 0) return ok();
+    if ((long long)d->B * d->H_v > 0x7fffffffll) return fail(GDR_E_UNSUPPORTED, "B * H_v too large for one launch");
+    gdr::DecodeArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.bg = b; a.wg = w; a.S = S; a.o = o;
+    a.B = d->B; a.Hqk = d->H_qk; a.Hv = d->H_v; a.decay = d->decay; a.scale = d->scale;
+    hipError_t e = gdr::launch_decode(d->io_dtype == GDR_BF16 ? gdr::IO_BF16 : gdr::IO_F32, d->d_k, a,
+                                      static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,103 @@
+// common.hpp -- device helpers shared by the libgdr kernels (gfx950 only).
+//
+// Element types: bfloat16 is stored as uint16_t bit patterns; float32 as float.
+// Matrix-core tiles use the 16x16 output shape of gfx950's MFMA:
+//   bf16: v_mfma_f32_16x16x32_bf16  (K step 32; each lane feeds 8 bf16 of A and of B)
+//   f32:  v_mfma_f32_16x16x4_f32    (K step 4;  each lane feeds 1 float of A and of B)
+// Operand convention used everywhere: A is a 16 x K block of a row-major
+// matrix (K contiguous), and B is given as B^T, i.e. also 16 x K with K
+// contiguous. Lane l supplies row (l % 16) of each and K-slice (l / 16).
+// The 16x16 fp32 result: lane l holds rows 4*(l/16) + r, r = 0..3, of
+// column (l % 16).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdr {
+
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) unsigned short u16x8;
+typedef __attribute__((ext_vector_type(4))) unsigned short u16x4;
+
+typedef uint16_t bf16_t;
+
+__device__ __forceinline__ float bf2f(bf16_t u) { return __uint_as_float((uint32_t)u << 16); }
+
+// float -> bfloat16, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ bf16_t f2bf(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (bf16_t)(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    __device__ __forceinline__ static float load(const float *p) { return *p; }
+    __device__ __forceinline__ static float to(float x) { return x; }
+    __device__ __forceinline__ static float from(float x) { return x; }
+};
+template <> struct Elem<bf16_t> {
+    __device__ __forceinline__ static float load(const bf16_t *p) { return bf2f(*p); }
+    __device__ __forceinline__ static bf16_t to(float x) { return f2bf(x); }
+    __device__ __forceinline__ static float from(bf16_t x) { return bf2f(x); }
+};
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// 16x16 tile products on the matrix cores.
+//   load(M, ld): this lane's fragment of the 16 x KS block at M (row stride
+//                ld elements): row (l % 16), K-slice (l / 16).
+//   mma(acc, a, b): acc += A_block * (Bt_block)^T for fragments a of A and
+//                b of Bt (B given transposed, K contiguous).
+//   step(acc, A, lda, Bt, ldb): load both fragments and multiply.
+template <typename T> struct Mma;
+
+template <> struct Mma<bf16_t> {
+    static constexpr int KS = 32;
+    using Frag = u16x8;
+    __device__ __forceinline__ static Frag load(const bf16_t *M, int ld) {
+        const int l = lane_id();
+        return *reinterpret_cast<const u16x8 *>(M + (l & 15) * ld + (l >> 4) * 8);
+    }
+    __device__ __forceinline__ static f32x4 mma(f32x4 acc, Frag a, Frag b) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+    }
+    __device__ __forceinline__ static f32x4 step(f32x4 acc, const bf16_t *A, int lda, const bf16_t *Bt, int ldb) {
+        return mma(acc, load(A, lda), load(Bt, ldb));
+    }
+};
+
+template <> struct Mma<float> {
+    static constexpr int KS = 4;
+    using Frag = float;
+    __device__ __forceinline__ static Frag load(const float *M, int ld) {
+        const int l = lane_id();
+        return M[(l & 15) * ld + (l >> 4)];
+    }
+    __device__ __forceinline__ static f32x4 mma(f32x4 acc, Frag a, Frag b) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+    }
+    __device__ __forceinline__ static f32x4 step(f32x4 acc, const float *A, int lda, const float *Bt, int ldb) {
+        return mma(acc, load(A, lda), load(Bt, ldb));
+    }
+};
+
+// Four consecutive elements (8 or 16 bytes, aligned) widened to float, and back.
+__device__ __forceinline__ f32x4 load4f(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+__device__ __forceinline__ f32x4 load4f(const bf16_t *p) {
+    u16x4 u = *reinterpret_cast<const u16x4 *>(p);
+    return f32x4{bf2f(u[0]), bf2f(u[1]), bf2f(u[2]), bf2f(u[3])};
+}
+__device__ __forceinline__ void store4f(float *p, f32x4 x) { *reinterpret_cast<f32x4 *>(p) = x; }
+__device__ __forceinline__ void store4f(bf16_t *p, f32x4 x) {
+    u16x4 u = {f2bf(x[0]), f2bf(x[1]), f2bf(x[2]), f2bf(x[3])};
+    *reinterpret_cast<u16x4 *>(p) = u;
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+}  // namespace gdr

@@ -1,0 +1,152 @@
+/*
+ * gdr.h -- C ABI of the MI355X (gfx950) gated delta-rule mixer library, libgdr.
+ *
+ * The mixer keeps a fixed-size state S in R^{d_k x d_v} per (sequence, value
+ * head) and, per token t, with alpha_t = exp(g_t):
+ *
+ *   e_t  = beta_t k_t            (tied gates: Gated DeltaNet, KDA)
+ *        = b_t (.) k_t           (decoupled erase gate on the key axis: Gated DeltaNet-2)
+ *   z_t  = beta_t v_t  |  w_t (.) v_t   (write gate on the value axis)
+ *   S_t  = (I - k_t e_t^T) Diag(alpha_t) S_{t-1} + k_t z_t^T
+ *   o_t  = scale * S_t^T q_t     (read after the write)
+ *
+ * Sources, by page title and section:
+ *   "Resumo Técnico: Gated DeltaNet-2", section "Regra Delta Portão-2": the
+ *     update equation above, the erase gate b_t in [0,1]^{d_k} and write gate
+ *     w_t in [0,1]^{d_v}; tying b = w = beta recovers KDA, and a scalar alpha
+ *     recovers Gated DeltaNet.
+ *   "Uma análise das variantes de atenção linear da família DeltaNet",
+ *     sections "Gated DeltaNet: esquecer primeiro o estado inteiro" (forget,
+ *     predict, correct, write, in that order), "Kimi Delta Attention:
+ *     atenuação por canal" (per-key-channel decay, read after write, read
+ *     scale), "Transição diagonal-mais-baixo-posto" (g = log alpha <= 0 is
+ *     what is stored; the d_k x d_v state layout), "Kernel Triton recorrente
+ *     fundido para decode" (the recurrent form for decode) and "Chunkwise
+ *     KDA" (the chunked form gives exactly the same state and outputs).
+ *   "Gated DeltaNet: o mixer em 48 das 64 camadas", section "Conceito": 16 QK
+ *     heads serve 48 V heads; the fp32 state of 48 heads of 128 x 128 is
+ *     about 3 MiB per layer.
+ *
+ * Conventions for every call
+ * --------------------------
+ * - Pointers are device pointers to contiguous row-major arrays, owned by the
+ *   caller. The library never frees caller memory and keeps no pointer after
+ *   a call returns.
+ * - Layouts (io = the desc's io dtype, float32 or bfloat16):
+ *     q, k : [B, T, H_qk, d_k] io      v, o : [B, T, H_v, d_v] io
+ *     beta : [B, T, H_v] float32
+ *     g    : [B, T, H_v] float32 (GDR_DECAY_SCALAR) or [B, T, H_v, d_k] float32
+ *            (GDR_DECAY_CHANNEL); g = log(alpha) must be finite and <= 0
+ *     b    : [B, T, H_v, d_k] io       w : [B, T, H_v, d_v] io
+ *     S    : [B, H_v, d_k, d_v] float32; row i is key channel i, column j
+ *            value channel j.
+ *   For decode the T axis is absent (one token per sequence).
+ * - V head h reads QK head h / (H_v / H_qk): each QK head serves a contiguous
+ *   group of H_v / H_qk V heads.
+ * - Gate modes: beta != NULL and b == w == NULL (tied), or beta == NULL and
+ *   both b and w != NULL (decoupled). g == NULL exactly when decay is
+ *   GDR_DECAY_NONE (alpha = 1, plain DeltaNet). Anything else: GDR_E_INVAL.
+ * - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *   stream): they validate, enqueue kernels and return without synchronising.
+ *   Arguments are validated before any HIP call; a rejected call enqueues
+ *   nothing. Inputs are not checked for NaN/Inf (that would cost a pass over
+ *   memory): non-finite inputs give non-finite outputs.
+ * - Every call returns a gdr_status. On a non-OK status, gdr_last_error()
+ *   returns a message for the calling thread.
+ * - Supported: d_k, d_v in {32, 64, 128}; chunk == 64; io float32 or
+ *   bfloat16. Arithmetic: state and accumulation in float32; bfloat16 io runs
+ *   the chunk products on bf16 matrix cores, float32 io on float32 ones.
+ *   With GDR_DECAY_CHANNEL the cumulative log-decay inside one 64-token chunk
+ *   must stay above -80 (the chunk factors scale keys by exp(-G)); scalar
+ *   decay has no such limit.
+ */
+#ifndef GDR_H
+#define GDR_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDR_OK = 0,
+    GDR_E_INVAL = -1,        /* bad pointer, size or gate combination */
+    GDR_E_UNSUPPORTED = -2,  /* valid request this build does not implement */
+    GDR_E_HIP = -3,          /* a HIP runtime call or kernel launch failed */
+    GDR_E_NOMEM = -4         /* device allocation failed (gdr_state_alloc) */
+} gdr_status;
+
+typedef enum { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
+
+typedef enum { GDR_DECAY_NONE = 0, GDR_DECAY_SCALAR = 1, GDR_DECAY_CHANNEL = 2 } gdr_decay;
+
+typedef struct {
+    int B;         /* sequences */
+    int T;         /* tokens per sequence (prefill); ignored by decode */
+    int H_qk;      /* query/key heads */
+    int H_v;       /* value heads; a multiple of H_qk */
+    int d_k;       /* key head dim */
+    int d_v;       /* value head dim */
+    int io_dtype;  /* gdr_dtype of q, k, v, b, w, o */
+    int decay;     /* gdr_decay */
+    int chunk;     /* chunk length of the prefill schedule (64) */
+    float scale;   /* read scale s in o = s S^T q (1 for plain Gated DeltaNet) */
+} gdr_desc;
+
+/* Bytes of one fp32 state block [B, H_v, d_k, d_v]; 0 if a size is not
+ * positive. Needs no GPU. Example: (1, 48, 128, 128) -> 3,145,728 (3 MiB). */
+size_t gdr_state_bytes(int B, int H_v, int d_k, int d_v);
+
+/* Allocate a zero-filled fp32 state [B, H_v, d_k, d_v] on the current device
+ * (hipMalloc, then a zero fill enqueued on `stream`). *state receives the
+ * pointer and *bytes (if not NULL) its size. Free with gdr_state_free. */
+int gdr_state_alloc(int B, int H_v, int d_k, int d_v, float **state, size_t *bytes, void *stream);
+
+/* Free a state from gdr_state_alloc (NULL is a no-op). Synchronises the
+ * device like hipFree. */
+int gdr_state_free(float *state);
+
+/* Device workspace bytes gdr_chunk_fwd needs for `desc`; needs no GPU.
+ * The workspace holds, per (sequence, V head, chunk), the chunk's
+ * precomputed factors: erase-side WY factor Y and query factor
+ * (C x d_k each), keys decayed to the chunk end (d_k x C), write-side factor
+ * U_z and in-chunk output (d_v x C each), all in bfloat16 (float32 for
+ * float32 io), plus the end-of-chunk decay (d_k float32). */
+int gdr_chunk_workspace_bytes(const gdr_desc *desc, size_t *bytes);
+
+/* Chunkwise-parallel prefill over T tokens: "Chunkwise KDA" and "Pipeline
+ * Triton da versão por chunks" (family analysis page); "Treinamento Paralelo
+ * Eficiente por Blocos" (Gated DeltaNet-2 summary page). Per 64-token chunk:
+ * cumulative log decay, decay absorbed into the erase/write factors, the
+ * unit-lower-triangular (I + T) system solved on chip, then one sweep over
+ * chunks that carries the fp32 state.
+ *   S0: initial state, or NULL for zeros. ST: final state; may equal S0
+ *   (in-place update). o: outputs. T may be any positive length (the last
+ *   chunk may be partial). workspace: at least gdr_chunk_workspace_bytes;
+ *   its contents on entry are ignored. */
+int gdr_chunk_fwd(const gdr_desc *desc, const void *q, const void *k, const void *v,
+                  const float *g, const float *beta, const void *b, const void *w,
+                  const float *S0, void *o, float *ST, void *workspace, size_t workspace_bytes,
+                  void *stream);
+
+/* One recurrent decode step for B sequences, one token each ("Kernel Triton
+ * recorrente fundido para decode", family analysis page): reads and writes
+ * every state S[b, h] in place exactly once. q, k: [B, H_qk, d_k];
+ * v, o: [B, H_v, d_v]; beta: [B, H_v]; g: [B, H_v] or [B, H_v, d_k];
+ * b: [B, H_v, d_k]; w: [B, H_v, d_v]. desc->T and desc->chunk are ignored. */
+int gdr_decode_step(const gdr_desc *desc, const void *q, const void *k, const void *v,
+                    const float *g, const float *beta, const void *b, const void *w,
+                    float *S, void *o, void *stream);
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+const char *gdr_last_error(void);
+
+/* Library ABI version: 1. */
+int gdr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H */

@@ -1,0 +1,94 @@
+"""Helpers for the GPU parity tests: move seeded inputs to the GPU, run the
+HIP path through the C ABI's Python binding, run the CPU oracle on the same
+stored values, and compare.
+
+Comparison (per output tensor, o and S_T separately): max |X - X_ref| divided
+by max |X_ref|, against 2e-2 for bfloat16 io with the fp32 state and 1e-4 on
+the all-float32 path.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import gdr_synth as gs
+import oracle
+
+TOL = {"bf16": 2e-2, "f32": 1e-4}
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a, dev="cuda:0"):
+    import torch
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def from_dev(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return oracle.upcast(t.view(torch.int16).cpu().numpy().view(np.uint16))
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+def rel_err(x, ref):
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert x.shape == ref.shape, (x.shape, ref.shape)
+    assert np.all(np.isfinite(ref)), "reference has non-finite entries"
+    if not np.all(np.isfinite(x)):
+        return float("inf")
+    den = np.max(np.abs(ref))
+    return float(np.max(np.abs(x - ref)) / (den if den > 0 else 1.0))
+
+
+def gpu_prefill(inp, S0=None, ST=None, scale=None, T_slice=None):
+    """Run gdr_chunk_fwd on the stored inputs; returns torch (o, ST)."""
+    import gated_delta_rule_23_amd as gdr
+    wl = inp["workload"]
+    sl = (lambda a: a) if T_slice is None else (lambda a: None if a is None else np.ascontiguousarray(a[:, T_slice]))
+    d = {n: to_dev(sl(inp[n])) for n in ("q", "k", "v", "g", "beta", "b", "w")}
+    return gdr.gdr_chunk_fwd(d["q"], d["k"], d["v"], g=d["g"], beta=d["beta"], b=d["b"], w=d["w"],
+                             S0=S0, ST=ST, scale=wl.scale if scale is None else scale)
+
+
+def oracle_prefill(inp, heads=None, cols=None, S0=None):
+    wl = inp["workload"]
+    return oracle.recurrent(inp["q"], inp["k"], inp["v"], g=inp["g"], beta=inp["beta"], b=inp["b"], w=inp["w"],
+                            scale=wl.scale, S0=S0 if S0 is not None else inp["S0"], heads=heads, cols=cols)
+
+
+def gpu_decode(inp, steps=None):
+    """Run the step-major decode inputs through gdr_decode_step; returns
+    (o [steps,B,Hv,D] fp64, final S fp64)."""
+    import torch
+    import gated_delta_rule_23_amd as gdr
+    wl = inp["workload"]
+    n = wl.T if steps is None else steps
+    dev = {k: to_dev(inp[k]) for k in ("q", "k", "v", "g", "beta", "b", "w")}
+    if inp["S0"] is not None:
+        S = to_dev(inp["S0"]).clone()
+    else:
+        S = torch.zeros((wl.B, wl.Hv, wl.dk, wl.dv), dtype=torch.float32, device="cuda:0")
+    outs = []
+    for s in range(n):
+        pick = lambda t: None if t is None else t[s]
+        outs.append(gdr.gdr_decode_step(pick(dev["q"]), pick(dev["k"]), pick(dev["v"]), S, g=pick(dev["g"]),
+                                        beta=pick(dev["beta"]), b=pick(dev["b"]), w=pick(dev["w"]),
+                                        scale=wl.scale))
+    torch.cuda.synchronize()
+    return np.stack([from_dev(o) for o in outs]), from_dev(S)
+
+
+def small_workload(io, D, decay, gates, T, B=2, Hqk=1, Hv=2, S0=False, decode=False, scale=1.0):
+    g_recipe = {"none": "none", "scalar": "softplus_0.1", "channel": "softplus_0.05"}[decay]
+    return gs.Workload(f"small_{io}_D{D}_{decay}_{gates}_T{T}", B, T, Hqk, Hv, D, D, io, decay, gates, g_recipe,
+                       S0="normal_0.02" if S0 else "zero", scale=scale, decode=decode)

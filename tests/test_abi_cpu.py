@@ -1,0 +1,133 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and
+rejects bad arguments before any HIP call (so no GPU is needed here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdr.h")
+
+gdr = pytest.importorskip("gated_delta_rule_23_amd")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdr_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared_functions()
+    assert set(names) == set(gdr.EXPORTS)
+    raw = ctypes.CDLL(gdr.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_version():
+    assert gdr.gdr_version() == 1
+
+
+def test_state_size_pin():
+    """"Gated DeltaNet: o mixer em 48 das 64 camadas", "Conceito": 48 V heads of
+    128 x 128 fp32 state are about 3 MiB per layer; "Linear attention e fast
+    weights", "Conceito": about 144 MiB over the 48 DeltaNet layers."""
+    per_layer = gdr.gdr_state_bytes(1, 48, 128, 128)
+    assert per_layer == 3 * 2 ** 20
+    assert 48 * per_layer == 144 * 2 ** 20
+    assert gdr.gdr_state_bytes(0, 48, 128, 128) == 0
+
+
+def test_workspace_bytes():
+    d = gdr.make_desc(1, 4096, 16, 48, 128, gdr.GDR_BF16, gdr.GDR_DECAY_SCALAR)
+    units = 48 * 64
+    io = units * 5 * 64 * 128 * 2
+    assert gdr.gdr_chunk_workspace_bytes(d) == ((io + 255) // 256) * 256 + units * 128 * 4
+    d0 = gdr.make_desc(1, 0, 16, 48, 128, gdr.GDR_BF16, gdr.GDR_DECAY_SCALAR)
+    assert gdr.gdr_chunk_workspace_bytes(d0) == 0
+
+
+P = 0x1000  # a fake non-NULL device pointer: validation never dereferences it
+
+
+def _fwd(desc, q=P, k=P, v=P, g=P, beta=P, b=None, w=None, S0=None, o=P, ST=P, ws=P, wsz=1 << 40):
+    return gdr.lib.gdr_chunk_fwd(ctypes.byref(desc), q, k, v, g, beta, b, w, S0, o, ST, ws, wsz, None)
+
+
+def _dec(desc, q=P, k=P, v=P, g=P, beta=P, b=None, w=None, S=P, o=P):
+    return gdr.lib.gdr_decode_step(ctypes.byref(desc), q, k, v, g, beta, b, w, S, o, None)
+
+
+def _desc(**kw):
+    base = dict(B=1, T=128, Hqk=2, Hv=6, D=64, io=gdr.GDR_BF16, decay=gdr.GDR_DECAY_SCALAR)
+    base.update(kw)
+    return gdr.make_desc(base["B"], base["T"], base["Hqk"], base["Hv"], base["D"], base["io"], base["decay"])
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(desc=dict(Hv=5)), gdr.GDR_E_INVAL),
+    (dict(desc=dict(Hqk=0)), gdr.GDR_E_INVAL),
+    (dict(desc=dict(B=-1)), gdr.GDR_E_INVAL),
+    (dict(desc=dict(T=-3)), gdr.GDR_E_INVAL),
+    (dict(desc=dict(D=96)), gdr.GDR_E_UNSUPPORTED),
+    (dict(desc=dict(D=256)), gdr.GDR_E_UNSUPPORTED),
+    (dict(desc=dict(io=7)), gdr.GDR_E_INVAL),
+    (dict(desc=dict(decay=5)), gdr.GDR_E_INVAL),
+    (dict(desc=dict(io=gdr.GDR_F32, D=128)), gdr.GDR_E_UNSUPPORTED),
+    (dict(args=dict(q=None)), gdr.GDR_E_INVAL),
+    (dict(args=dict(o=None)), gdr.GDR_E_INVAL),
+    (dict(args=dict(ST=None)), gdr.GDR_E_INVAL),
+    (dict(args=dict(g=None)), gdr.GDR_E_INVAL),                      # decay scalar needs g
+    (dict(desc=dict(decay=gdr.GDR_DECAY_NONE)), gdr.GDR_E_INVAL),    # g given without decay
+    (dict(args=dict(b=P, w=P)), gdr.GDR_E_INVAL),                    # beta and b, w together
+    (dict(args=dict(beta=None, b=P)), gdr.GDR_E_INVAL),              # b without w
+    (dict(args=dict(beta=None)), gdr.GDR_E_INVAL),                   # no gate at all
+    (dict(args=dict(ws=None)), gdr.GDR_E_INVAL),
+    (dict(args=dict(wsz=100)), gdr.GDR_E_INVAL),
+])
+def test_prefill_rejections(case, expect):
+    d = _desc(**case.get("desc", {}))
+    rc = _fwd(d, **case.get("args", {}))
+    assert rc == expect
+    assert gdr.gdr_last_error() != ""
+
+
+def test_prefill_rejects_other_chunk_sizes():
+    d = _desc()
+    d.chunk = 32
+    assert _fwd(d) == gdr.GDR_E_UNSUPPORTED
+    assert "chunk" in gdr.gdr_last_error()
+
+
+def test_zero_batch_is_a_noop_without_gpu():
+    assert _fwd(_desc(B=0)) == gdr.GDR_OK
+    assert gdr.gdr_last_error() == ""
+    assert _dec(_desc(B=0)) == gdr.GDR_OK
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(desc=dict(Hv=4, Hqk=3)), gdr.GDR_E_INVAL),
+    (dict(desc=dict(D=48)), gdr.GDR_E_UNSUPPORTED),
+    (dict(args=dict(S=None)), gdr.GDR_E_INVAL),
+    (dict(args=dict(g=None)), gdr.GDR_E_INVAL),
+    (dict(args=dict(beta=None, b=P, w=None)), gdr.GDR_E_INVAL),
+])
+def test_decode_rejections(case, expect):
+    d = _desc(**case.get("desc", {}))
+    assert _dec(d, **case.get("args", {})) == expect
+
+
+def test_state_alloc_rejects_bad_sizes():
+    p, n = ctypes.c_void_p(), ctypes.c_size_t()
+    assert gdr.lib.gdr_state_alloc(0, 48, 128, 128, ctypes.byref(p), ctypes.byref(n), None) == gdr.GDR_E_INVAL
+    assert gdr.lib.gdr_state_alloc(1, 48, 128, 128, None, None, None) == gdr.GDR_E_INVAL
+    assert gdr.lib.gdr_state_free(None) == gdr.GDR_OK
+
+
+def test_binding_rejects_bad_tensors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 4, 1, 32, dtype=torch.float64)
+    with pytest.raises((TypeError, ValueError)):
+        gdr.gdr_chunk_fwd(q, q, q, beta=torch.zeros(1, 4, 1))

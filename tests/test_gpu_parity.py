@@ -1,0 +1,186 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU oracle.
+
+Small shapes span several chunks and a ragged tail in every gate mode, value
+dimension and io dtype; the five full-size workloads are compared on sampled
+(head, value-column) outputs the oracle computes one by one (value columns and
+heads evolve independently). Plus properties that hold at any size.
+"""
+import numpy as np
+import pytest
+
+import gdr_synth as gs
+from parity_util import (TOL, from_dev, gpu_decode, gpu_prefill, oracle_prefill, rel_err, say, small_workload,
+                         to_dev)
+
+torch = pytest.importorskip("torch")
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+MODES = [("none", "beta"), ("scalar", "beta"), ("channel", "beta"), ("channel", "bw"), ("scalar", "bw")]
+PREFILL_DIMS = [("bf16", 32), ("bf16", 64), ("bf16", 128), ("f32", 32), ("f32", 64)]
+
+
+# ---------------------------------------------------------------------------
+# Decode.
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("decay,gates", MODES[:4])
+def test_decode_small(io, D, decay, gates):
+    wl = small_workload(io, D, decay, gates, T=6, B=3, Hqk=2, Hv=4, S0=True, decode=True,
+                        scale=D ** -0.5 if decay == "channel" else 1.0)
+    inp = gs.make_inputs(wl, seed=D + len(decay))
+    say(f"decode {wl.name}")
+    o_gpu, S_gpu = gpu_decode(inp)
+    o_ref, S_ref = oracle_prefill(gs.as_sequence(inp))
+    assert rel_err(o_gpu, np.swapaxes(o_ref, 0, 1)) < TOL[io]
+    assert rel_err(S_gpu, S_ref) < TOL[io]
+
+
+def test_decode_qwen_shape_256_steps():
+    """64 sequences x 48 V heads (16 QK heads), 128 x 128 fp32 states, 256
+    consecutive steps; every step's outputs and the final states of sampled
+    heads against the oracle."""
+    wl = gs.QWEN_GDN_DECODE
+    inp = gs.make_inputs(wl, seed=2)
+    say(f"decode {wl.name}")
+    o_gpu, S_gpu = gpu_decode(inp)
+    heads = [0, 1, 2, 25, 47]
+    o_ref, S_ref = oracle_prefill(gs.as_sequence(inp), heads=heads)
+    assert rel_err(o_gpu[:, :, heads], np.swapaxes(o_ref, 0, 1)[:, :, heads]) < TOL["bf16"]
+    assert rel_err(S_gpu[:, heads], S_ref[:, heads]) < TOL["bf16"]
+    assert np.all(np.isfinite(S_gpu))
+
+
+# ---------------------------------------------------------------------------
+# Prefill, small shapes.
+
+@pytest.mark.parametrize("io,D", PREFILL_DIMS)
+@pytest.mark.parametrize("decay,gates", MODES)
+@pytest.mark.parametrize("T", [1, 64, 150])
+def test_prefill_small(io, D, decay, gates, T):
+    wl = small_workload(io, D, decay, gates, T=T, B=2, Hqk=1, Hv=2, S0=(T != 64))
+    inp = gs.make_inputs(wl, seed=T + D)
+    say(f"prefill {wl.name}")
+    S0 = to_dev(inp["S0"])
+    o, ST = gpu_prefill(inp, S0=S0)
+    o_ref, S_ref = oracle_prefill(inp)
+    assert rel_err(from_dev(o), o_ref) < TOL[io]
+    assert rel_err(from_dev(ST), S_ref) < TOL[io]
+
+
+@pytest.mark.parametrize("io,D", [("bf16", 128), ("f32", 64)])
+def test_prefill_grouped_heads_and_scale(io, D):
+    """Two QK heads serving three V heads each, read scale d^-1/2, strong
+    per-channel decay, many chunks."""
+    wl = small_workload(io, D, "channel", "beta", T=333, B=2, Hqk=2, Hv=6, S0=True, scale=D ** -0.5)
+    wl = wl.scaled(g_recipe="logsigmoid_n21")
+    inp = gs.make_inputs(wl, seed=7)
+    say(f"prefill {wl.name}")
+    o, ST = gpu_prefill(inp, S0=to_dev(inp["S0"]))
+    o_ref, S_ref = oracle_prefill(inp)
+    assert rel_err(from_dev(o), o_ref) < TOL[io]
+    assert rel_err(from_dev(ST), S_ref) < TOL[io]
+
+
+# ---------------------------------------------------------------------------
+# Prefill, the workloads at full size.
+
+def test_prefill_gdn_small_f32_full():
+    wl = gs.GDN_SMALL_F32
+    inp = gs.make_inputs(wl, seed=0)
+    say(f"prefill {wl.name}")
+    o, ST = gpu_prefill(inp)
+    o_ref, S_ref = oracle_prefill(inp)
+    assert rel_err(from_dev(o), o_ref) < TOL["f32"]
+    assert rel_err(from_dev(ST), S_ref) < TOL["f32"]
+
+
+@pytest.mark.parametrize("wl,heads,cols", [
+    (gs.QWEN_GDN_PREFILL, [0, 1, 2, 3, 24, 47], None),
+    (gs.KDA_PREFILL, [0, 17, 31], (0, 48)),
+    (gs.GDN2_PREFILL, [0, 9, 15], (80, 128)),
+], ids=lambda x: getattr(x, "name", None))
+def test_prefill_full_size_sampled(wl, heads, cols):
+    inp = gs.make_inputs(wl, seed=1)
+    say(f"prefill {wl.name}")
+    o, ST = gpu_prefill(inp)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_prefill(inp, heads=heads, cols=cols)
+    c0, c1 = cols if cols else (0, wl.dv)
+    o_g = from_dev(o[:, :, heads, c0:c1])
+    S_g = from_dev(ST[:, heads, :, c0:c1])
+    assert rel_err(o_g, o_ref[:, :, heads, c0:c1]) < TOL["bf16"]
+    assert rel_err(S_g, S_ref[:, heads, :, c0:c1]) < TOL["bf16"]
+    assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(ST).all())
+
+
+# ---------------------------------------------------------------------------
+# Properties.
+
+def test_prefill_split_resume_matches_one_pass():
+    wl = small_workload("bf16", 128, "channel", "bw", T=300, B=1, Hqk=2, Hv=4, S0=True)
+    inp = gs.make_inputs(wl, seed=11)
+    S0 = to_dev(inp["S0"])
+    o_all, S_all = gpu_prefill(inp, S0=S0)
+    o1, S1 = gpu_prefill(inp, S0=S0, T_slice=slice(0, 100))
+    o2, S2 = gpu_prefill(inp, S0=S1, T_slice=slice(100, 300))
+    assert rel_err(from_dev(torch.cat([o1, o2], dim=1)), from_dev(o_all)) < TOL["bf16"]
+    assert rel_err(from_dev(S2), from_dev(S_all)) < TOL["bf16"]
+
+
+def test_prefill_equals_decode_steps():
+    wl = small_workload("f32", 64, "channel", "beta", T=70, B=2, Hqk=1, Hv=2, S0=True)
+    inp = gs.make_inputs(wl, seed=12)
+    o_p, S_p = gpu_prefill(inp, S0=to_dev(inp["S0"]))
+    step_major = {n: (None if inp[n] is None else np.ascontiguousarray(np.swapaxes(inp[n], 0, 1)))
+                  for n in ("q", "k", "v", "g", "beta", "b", "w")}
+    dec = dict(inp, **step_major)
+    dec["workload"] = wl.scaled(decode=True)
+    o_d, S_d = gpu_decode(dec)
+    assert rel_err(np.swapaxes(o_d, 0, 1), from_dev(o_p)) < TOL["f32"]
+    assert rel_err(S_d, from_dev(S_p)) < TOL["f32"]
+
+
+def test_prefill_in_place_state_and_determinism():
+    wl = small_workload("bf16", 64, "scalar", "beta", T=200, B=2, Hqk=1, Hv=2, S0=True)
+    inp = gs.make_inputs(wl, seed=13)
+    S0 = to_dev(inp["S0"])
+    o1, S1 = gpu_prefill(inp, S0=S0)
+    o2, S2 = gpu_prefill(inp, S0=S0)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)          # run to run, bit for bit
+    S_inplace = S0.clone()
+    o3, S3 = gpu_prefill(inp, S0=S_inplace, ST=S_inplace)       # ST aliases S0
+    assert S3.data_ptr() == S_inplace.data_ptr()
+    assert torch.equal(o3, o1) and torch.equal(S_inplace, S1)
+
+
+def test_prefill_empty_sequence_copies_state():
+    import gated_delta_rule_23_amd as gdr
+    wl = small_workload("bf16", 64, "scalar", "beta", T=8, B=2, Hqk=1, Hv=2, S0=True)
+    inp = gs.make_inputs(wl, seed=14)
+    S0 = to_dev(inp["S0"])
+    o, ST = gpu_prefill(inp, S0=S0, T_slice=slice(0, 0))
+    torch.cuda.synchronize()
+    assert o.shape[1] == 0 and torch.equal(ST, S0)
+    o, ST = gpu_prefill(inp, S0=None, T_slice=slice(0, 0))
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(ST) == 0
+    assert gdr.gdr_last_error() == ""
+
+
+def test_state_alloc_is_zeroed():
+    import gated_delta_rule_23_amd as gdr
+    ptr, n = gdr.gdr_state_alloc(2, 3, 64, 64)
+    try:
+        assert n == 2 * 3 * 64 * 64 * 4
+        # Use the library-allocated state as the decode state: with beta = 0 and
+        # no decay the step is a no-op and the read returns S^T q = 0.
+        class _View:
+            __cuda_array_interface__ = {"shape": (2, 3, 64, 64), "typestr": "<f4", "data": (ptr, False),
+                                        "version": 3, "strides": None}
+        S = torch.as_tensor(_View(), device="cuda:0")
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(S) == 0
+    finally:
+        gdr.gdr_state_free(ptr)
