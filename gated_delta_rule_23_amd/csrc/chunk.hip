@@ -42,42 +42,6 @@ constexpr int C = kChunk;
 __host__ __device__ constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 __host__ __device__ constexpr size_t a16(size_t x) { return (x + 15) & ~(size_t)15; }
 
-template <typename IO, int D>
-struct PrepLayout {
-    static constexpr int NT = 256;
-    static constexpr int PD = D + 8;  // row stride of [C x D] row-major tiles
-    static constexpr int PT = C + 8;  // row stride of [D x C] transposed tiles
-    static constexpr int PF = C + 1;  // row stride of fp32 [C x C] matrices
-    static constexpr size_t SLOT = a16(cmax((size_t)C * PD, (size_t)D * PT) * sizeof(IO));
-    static constexpr size_t F32 = a16(cmax(cmax((size_t)2 * C * PF * 4, (size_t)C * D * 4), (size_t)D * PT * sizeof(IO)));
-    static constexpr size_t LA = a16(cmax((size_t)2 * C * PT * sizeof(IO), (size_t)D * PT * sizeof(IO)));
-    static constexpr size_t OFF_F32 = 5 * SLOT;
-    static constexpr size_t OFF_LA = OFF_F32 + F32;
-    static constexpr size_t BYTES = OFF_LA + LA;
-};
-
-// 8 consecutive elements widened to float.
-__device__ __forceinline__ void load8(const bf16_t *p, float *x) {
-    u16x8 u = *reinterpret_cast<const u16x8 *>(p);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = bf2f(u[j]);
-}
-__device__ __forceinline__ void load8(const float *p, float *x) {
-    f32x4 a = *reinterpret_cast<const f32x4 *>(p), b = *reinterpret_cast<const f32x4 *>(p + 4);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) { x[j] = a[j]; x[4 + j] = b[j]; }
-}
-__device__ __forceinline__ void store8(bf16_t *p, const float *x) {
-    u16x8 u;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) u[j] = f2bf(x[j]);
-    *reinterpret_cast<u16x8 *>(p) = u;
-}
-__device__ __forceinline__ void store8(float *p, const float *x) {
-    *reinterpret_cast<f32x4 *>(p) = f32x4{x[0], x[1], x[2], x[3]};
-    *reinterpret_cast<f32x4 *>(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
-}
-
 // Copy a rows x cols block between row strides, 16 bytes per access.
 template <typename T>
 __device__ __forceinline__ void copy_block(T *dst, int dld, const T *src, int sld, int rows, int cols, int tid, int nt) {
@@ -95,286 +59,506 @@ __device__ __forceinline__ void lower_tile(int idx, int &ti, int &tj) {
     tj = idx - ti * (ti + 1) / 2;
 }
 
+// exp(x) = 2^(x log2 e) on the hardware exp2 (v_exp_f32, ~1 ulp).
+__device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+
+// acc += A[16 x 16] * (Bt[16 x 16])^T. For bf16 this is one 16x16x32 step:
+// columns 16..31 of A must be zero and those of Bt finite.
+template <typename IO>
+__device__ __forceinline__ f32x4 mma_k16(f32x4 acc, const IO *A, int lda, const IO *Bt, int ldb) {
+    using M = Mma<IO>;
+#pragma unroll
+    for (int ks = 0; ks < (16 + M::KS - 1) / M::KS; ++ks) acc = M::step(acc, A + ks * M::KS, lda, Bt + ks * M::KS, ldb);
+    return acc;
+}
+
 template <typename IO, int D>
-__global__ __launch_bounds__(256) void chunk_prep(ChunkArgs a) {
+struct PrepCfg {
+    static constexpr int NW = D / 16 < 4 ? D / 16 : 4;  // waves per workgroup
+    static constexpr int NT = 64 * NW;
+    static constexpr int CQ = D / 4;         // channel quads
+    static constexpr int NGRP = NT / CQ;     // token groups (threads per channel quad)
+    static constexpr int TPT = C / NGRP;     // tokens per thread in the elementwise phase
+    static constexpr int NCTS = 2 * D / NW / 16;  // 16-wide right-hand-side column tiles per wave
+    static constexpr int PD = D + 8;    // row stride of [C x D] row-major tiles
+    static constexpr int PT = C + 8;    // row stride of token-contiguous tiles
+    static constexpr int PDB = sizeof(IO) == 2 ? 40 : 20;   // D_b rows (bf16: K padded to 32 with zeros)
+    static constexpr int PTMP = sizeof(IO) == 2 ? 32 : 20;  // per-wave solve temporary rows
+    static constexpr size_t SLOT = a16(cmax((size_t)C * PD, (size_t)D * PT) * sizeof(IO));
+    static constexpr size_t XT = a16((size_t)2 * D * PT * sizeof(IO));
+    static constexpr size_t TA = a16((size_t)2 * C * PT * sizeof(IO));
+    static constexpr size_t TD = a16((size_t)4 * 16 * 17 * 4);
+    static constexpr size_t DB = a16((size_t)4 * 16 * PDB * sizeof(IO));
+    static constexpr size_t PART = a16((size_t)NGRP * D * 4);
+    static constexpr size_t OFF_K = SLOT, OFF_Q = 2 * SLOT, OFF_XT = 3 * SLOT, OFF_TA = OFF_XT + XT,
+                            OFF_TD = OFF_TA + TA, OFF_DB = OFF_TD + TD, OFF_PART = OFF_DB + DB,
+                            BYTES = OFF_PART + PART;
+    static_assert(TA >= (size_t)D * PT * sizeof(IO), "Kend^T staging");
+    static_assert((size_t)NW * 16 * NCTS * PTMP * sizeof(IO) <= SLOT, "solve temporaries");
+    static_assert(NGRP * TPT == C && TPT % 4 == 0, "elementwise mapping");
+    static_assert(BYTES <= 160 * 1024, "LDS budget");
+};
+
+// One thread's raw inputs for a chunk: 4 tokens x 4 channels of q, k, v (and
+// b, w, per-channel g) plus the 4 tokens' beta; lane l of every wave also
+// holds token l's scalar g for the in-wave prefix scan. Kept raw so that the
+// loads for the next chunk are issued early and waited for only when used.
+template <typename IO, int D, bool CHAN, bool BW>
+struct PrepIn {
+    using R4 = Raw4<IO>;
+    static constexpr int TPT = PrepCfg<IO, D>::TPT;
+    typename R4::type q[TPT], k[TPT], v[TPT], bg[BW ? TPT : 1], wg[BW ? TPT : 1];
+    f32x4 g[CHAN ? TPT : 1];
+    float betal, gs;  // lane l of every wave: token l's beta and scalar g
+
+    __device__ __forceinline__ void load(const ChunkArgs &a, int u, int cq, int grp) {
+        const int NC = a.NC, c = u % NC, bh = u / NC, b = bh / a.Hv, h = bh - b * a.Hv;
+        const int hq = h / (a.Hv / a.Hqk), t0 = c * C, n = min(C, a.T - t0);
+        const int l = threadIdx.x & 63;
+#pragma unroll
+        for (int j = 0; j < TPT; ++j) {
+            const size_t tok = (size_t)b * a.T + t0 + min(TPT * grp + j, n - 1);  // clamped: padded tokens are zeroed at use
+            q[j] = R4::load(static_cast<const IO *>(a.q) + (tok * a.Hqk + hq) * D + 4 * cq);
+            k[j] = R4::load(static_cast<const IO *>(a.k) + (tok * a.Hqk + hq) * D + 4 * cq);
+            v[j] = R4::load(static_cast<const IO *>(a.v) + (tok * a.Hv + h) * D + 4 * cq);
+            if constexpr (BW) {
+                bg[j] = R4::load(static_cast<const IO *>(a.bg) + (tok * a.Hv + h) * D + 4 * cq);
+                wg[j] = R4::load(static_cast<const IO *>(a.wg) + (tok * a.Hv + h) * D + 4 * cq);
+            }
+            if constexpr (CHAN) g[j] = *reinterpret_cast<const f32x4 *>(a.g + (tok * a.Hv + h) * D + 4 * cq);
+        }
+        const size_t tl = ((size_t)b * a.T + t0 + min(l, n - 1)) * a.Hv + h;
+        if constexpr (!BW) betal = a.beta[tl];
+        if constexpr (!CHAN) gs = a.decay == DECAY_SCALAR ? a.g[tl] : 0.f;
+    }
+};
+
+// Everything in a chunk that does not depend on the state, for every
+// (sequence, V head, chunk) unit; persistent over units, with the next unit's
+// inputs prefetched while the current one is processed. Per unit:
+//  A. decay prefix sums and decay absorption; E~ (row-major, and token-
+//     contiguous as the right-hand side), K~, Q~, Z; Kend^T; gamma.
+//  B. Gram products T = E~ K~^T and A = Q~ K~^T on the matrix cores (lower tiles).
+//     Scalar decay (and none) uses the raw Gram with exp(G_i - G_j) applied per
+//     entry, so no factor can overflow; per-channel decay uses the factored form.
+//  C. (I + T) X = [E~ | Z] by blocked forward substitution over four 16-token
+//     blocks: the 16 x 16 diagonal blocks are inverted in fp32, the rest are
+//     matrix-core products; each wave solves its own 32 right-hand-side columns.
+//  D. W_q = s (Q~ - A Y), O_z = s A U_z, and the workspace stores.
+template <typename IO, int D, bool CHAN, bool BW>
+__global__ __launch_bounds__(D >= 64 ? 256 : 128) void chunk_prep(ChunkArgs a) {  // = PrepCfg<IO, D>::NT
     using E = Elem<IO>;
     using M = Mma<IO>;
-    using Lay = PrepLayout<IO, D>;
-    constexpr int NT = Lay::NT, PD = Lay::PD, PT = Lay::PT, PF = Lay::PF;
-    constexpr int KS = M::KS;
-    constexpr int CT = D / 16;  // 16-wide column tiles over D
+    using R4 = Raw4<IO>;
+    using Cfg = PrepCfg<IO, D>;
+    constexpr int NW = Cfg::NW, NT = Cfg::NT, CQ = Cfg::CQ, PD = Cfg::PD, PT = Cfg::PT;
+    constexpr int NGRP = Cfg::NGRP, TPT = Cfg::TPT, NCTS = Cfg::NCTS, WC = 16 * NCTS;  // WC: columns per wave
+    static_assert(NT == (D >= 64 ? 256 : 128), "launch bounds");
+    constexpr int PDB = Cfg::PDB, PTMP = Cfg::PTMP, KS = M::KS;
+    constexpr int NG = (20 + NW - 1) / NW;  // Gram tile products per wave
 
     extern __shared__ __align__(16) unsigned char smem[];
-    IO *sE = reinterpret_cast<IO *>(smem + 0 * Lay::SLOT);    // E~ [C][PD]; later -Y^T [D][PT]
-    IO *sK = reinterpret_cast<IO *>(smem + 1 * Lay::SLOT);    // K~ [C][PD]; later U_z^T [D][PT]
-    IO *sQ = reinterpret_cast<IO *>(smem + 2 * Lay::SLOT);    // Q~ [C][PD]
-    IO *sET = reinterpret_cast<IO *>(smem + 3 * Lay::SLOT);   // E~^T [D][PT]; later Y staging [C][PD]
-    IO *sZT = reinterpret_cast<IO *>(smem + 4 * Lay::SLOT);   // Z^T [D][PT]; later W_q staging [C][PD]
-    float *sG = reinterpret_cast<float *>(smem + Lay::OFF_F32);  // G [C][D] or [C]
-    float *sTf = sG;                                             // T [C][PF] (after sG is dead)
-    float *sLf = sG + C * PF;                                    // L [C][PF]
-    IO *sOzs = reinterpret_cast<IO *>(smem + Lay::OFF_F32);      // O_z^T staging [D][PT] (after L is dead)
-    IO *sL = reinterpret_cast<IO *>(smem + Lay::OFF_LA);         // L in io dtype [C][PT]
-    IO *sA = sL + C * PT;                                        // A [C][PT]
-    IO *sKTs = sL;                                               // Kend^T staging [D][PT] (before L, A)
-    IO *sYT = sE;
-    IO *sUzT = sK;
-    IO *sYs = sET;
-    IO *sWs = sZT;
+    IO *sE = reinterpret_cast<IO *>(smem);                    // E~ (or raw e) [C][PD]; then solve temporaries
+    IO *sK = reinterpret_cast<IO *>(smem + Cfg::OFF_K);       // K~ (or raw k) [C][PD]; then W_q staging [C][PD]
+    IO *sQ = reinterpret_cast<IO *>(smem + Cfg::OFF_Q);       // Q~ (or raw q) [C][PD]
+    IO *sXT = reinterpret_cast<IO *>(smem + Cfg::OFF_XT);     // [E~ | Z]^T [2D][PT] -> [Y | U_z]^T in place
+    IO *sTo = reinterpret_cast<IO *>(smem + Cfg::OFF_TA);     // -T without its diagonal blocks [C][PT]
+    IO *sA = sTo + C * PT;                                     // A [C][PT]
+    IO *sKT = sTo;                                             // Kend^T staging [D][PT] (phase A only)
+    float *sTd = reinterpret_cast<float *>(smem + Cfg::OFF_TD);  // T diagonal blocks [4][16][17] fp32
+    IO *sDb = reinterpret_cast<IO *>(smem + Cfg::OFF_DB);        // their inverses [4][16][PDB]
+    float *sPart = reinterpret_cast<float *>(smem + Cfg::OFF_PART);  // [16][D] per-group channel sums
+    IO *sWs = sK;
 
-    const int NC = a.NC;
-    const int u = blockIdx.x;
-    const int c = u % NC;
-    const int bh = u / NC;
-    const int b = bh / a.Hv, h = bh - (bh / a.Hv) * a.Hv;
-    const int hq = h / (a.Hv / a.Hqk);
-    const int t0 = c * C;
-    const int n = min(C, a.T - t0);
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lq = l >> 4;
+    const int cq = tid % CQ, grp = tid / CQ;
+    const int units = a.B * a.Hv * a.NC;
+    constexpr bool chan = CHAN;
 
-    IO *ws = static_cast<IO *>(a.ws_io) + (size_t)u * chunk_ws_io_elems(D);
-    IO *wY = ws, *wWq = ws + C * D, *wKT = ws + 2 * C * D, *wUzT = ws + 3 * C * D, *wOzT = ws + 4 * C * D;
+    // D_b's padding columns (bf16 K = 32 steps) stay zero for the whole kernel.
+    for (int i = tid; i < 4 * 16 * PDB; i += NT) sDb[i] = E::to(0.f);
 
-    // ---- Cumulative log decay inside the chunk (padded tokens add 0). ----
-    if (a.decay == DECAY_CHANNEL) {
-        if (tid < D) {
-            float acc = 0.f;
-            const float *gp = a.g + (((size_t)b * a.T + t0) * a.Hv + h) * D + tid;
-#pragma unroll 8
-            for (int i = 0; i < C; ++i) {
-                acc += i < n ? gp[(size_t)i * a.Hv * D] : 0.f;
-                sG[i * D + tid] = acc;
-            }
-        }
-    } else if (a.decay == DECAY_SCALAR) {
-        if (w == 0) {
-            float x = l < n ? a.g[((size_t)b * a.T + t0 + l) * a.Hv + h] : 0.f;
+    PrepIn<IO, D, CHAN, BW> in;
+    if ((int)blockIdx.x < units) in.load(a, blockIdx.x, cq, grp);
+
+    for (int u = blockIdx.x; u < units; u += gridDim.x) {
+        const int NC = a.NC, c = u % NC, bh = u / NC;
+        const int n = min(C, a.T - c * C);
+        IO *ws = static_cast<IO *>(a.ws_io) + (size_t)u * chunk_ws_io_elems(D);
+        IO *wY = ws, *wWq = ws + C * D, *wKT = ws + 2 * C * D, *wUzT = ws + 3 * C * D, *wOzT = ws + 4 * C * D;
+        __syncthreads();  // the previous unit's readers of shared memory are done
+
+        // ---- A. prefix sums and decay absorption ----
+        // Scalar decay: each wave scans the 64 token values itself (lane = token).
+        float Gl = 0.f;
+        if (!CHAN) {
+            Gl = l < n ? in.gs : 0.f;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(x, off);
-                if (l >= off) x += y;
+                const float y = __shfl_up(Gl, off);
+                if (l >= off) Gl += y;
             }
-            sG[l] = x;
         }
-    }
-    __syncthreads();
-
-    // ---- Decay absorbed into the factors (fp32 math, stored in the io dtype). ----
-    {
-        constexpr int G8 = D / 8;
-        for (int item = tid; item < C * G8; item += NT) {
-            const int i = item / G8, c8 = (item - (item / G8) * G8) * 8;
-            float qv[8], kv[8], vv[8], ev[8], zv[8];
-            if (i < n) {
-                const size_t tok = (size_t)b * a.T + t0 + i;
-                load8(static_cast<const IO *>(a.q) + (tok * a.Hqk + hq) * D + c8, qv);
-                load8(static_cast<const IO *>(a.k) + (tok * a.Hqk + hq) * D + c8, kv);
-                load8(static_cast<const IO *>(a.v) + (tok * a.Hv + h) * D + c8, vv);
-                if (a.beta) {
-                    const float bt = a.beta[tok * a.Hv + h];
+        const float Gend_s = __shfl(Gl, 63);
+        float G[TPT][4];
+        if constexpr (CHAN) {
+            // Running sums over this thread's tokens, then add the totals of the
+            // earlier token groups.
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) { ev[j] = bt * kv[j]; zv[j] = bt * vv[j]; }
-                } else {
-                    float bg[8], wg[8];
-                    load8(static_cast<const IO *>(a.bg) + (tok * a.Hv + h) * D + c8, bg);
-                    load8(static_cast<const IO *>(a.wg) + (tok * a.Hv + h) * D + c8, wg);
+            for (int j = 0; j < TPT; ++j)
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) { ev[j] = bg[j] * kv[j]; zv[j] = wg[j] * vv[j]; }
-                }
+                for (int ch = 0; ch < 4; ++ch)
+                    G[j][ch] = (TPT * grp + j < n ? in.g[CHAN ? j : 0][ch] : 0.f) + (j > 0 ? G[j - 1][ch] : 0.f);
+            store4f(sPart + grp * D + 4 * cq, f32x4{G[TPT - 1][0], G[TPT - 1][1], G[TPT - 1][2], G[TPT - 1][3]});
+        }
+        __syncthreads();
+        float Gend[4];
+        if constexpr (CHAN) {
+            f32x4 off = zero4(), tot = zero4();
+#pragma unroll
+            for (int g2 = 0; g2 < NGRP; ++g2) {
+                const f32x4 p = load4f(sPart + g2 * D + 4 * cq);
+                if (g2 < grp) off += p;
+                tot += p;
+            }
+#pragma unroll
+            for (int j = 0; j < TPT; ++j)
+#pragma unroll
+                for (int ch = 0; ch < 4; ++ch) G[j][ch] += off[ch];
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch) Gend[ch] = tot[ch];
+        } else {
+#pragma unroll
+            for (int j = 0; j < TPT; ++j) {
+                const float Gt = __shfl(Gl, TPT * grp + j);
+#pragma unroll
+                for (int ch = 0; ch < 4; ++ch) G[j][ch] = Gt;
+            }
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch) Gend[ch] = Gend_s;
+        }
+        // Per token: operands for the Gram (row-major), and the token-contiguous
+        // right-hand side E~, Z and Kend^T (4 tokens per 8/16-byte store).
+        float xE[4][4], xZ[4][4], xKe[4][4];
+#pragma unroll
+        for (int j = 0; j < TPT; ++j) {
+            const int tk = TPT * grp + j;
+            const bool valid = tk < n;
+            const f32x4 kk = R4::widen(in.k[j]), qq = R4::widen(in.q[j]), vv = R4::widen(in.v[j]);
+            f32x4 eb, wz;
+            if constexpr (BW) {
+                eb = R4::widen(in.bg[j]);
+                wz = R4::widen(in.wg[j]);
             } else {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) qv[j] = kv[j] = vv[j] = ev[j] = zv[j] = 0.f;
+                const float bt = __shfl(in.betal, tk);
+                eb = f32x4{bt, bt, bt, bt};
+                wz = eb;
             }
-            float xe[8], xk[8], xq[8], xend[8];
+            float gE[4], gK[4], gQ[4];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                float G = 0.f, Gend = 0.f;
-                if (a.decay == DECAY_CHANNEL) { G = sG[i * D + c8 + j]; Gend = sG[(C - 1) * D + c8 + j]; }
-                else if (a.decay == DECAY_SCALAR) { G = sG[i]; Gend = sG[C - 1]; }
-                const float eg = expf(G);
-                xe[j] = ev[j] * eg;
-                xq[j] = qv[j] * eg;
-                xk[j] = kv[j] * expf(-G);
-                xend[j] = kv[j] * expf(Gend - G);
+            for (int ch = 0; ch < 4; ++ch) {
+                const float kv = valid ? kk[ch] : 0.f, qv = valid ? qq[ch] : 0.f;
+                const float ev = eb[ch] * kv;
+                const float eg = fast_exp(G[j][ch]);
+                xE[j & 3][ch] = ev * eg;
+                xZ[j & 3][ch] = valid ? wz[ch] * vv[ch] : 0.f;
+                xKe[j & 3][ch] = kv * fast_exp(Gend[ch] - G[j][ch]);
+                if (chan) {  // factored form for the Gram
+                    gE[ch] = ev * eg;
+                    gK[ch] = kv * __builtin_amdgcn_rcpf(eg);
+                    gQ[ch] = qv * eg;
+                } else {     // raw operands; the decay is applied to the Gram entries
+                    gE[ch] = ev;
+                    gK[ch] = kv;
+                    gQ[ch] = qv;
+                }
             }
-            store8(sE + i * PD + c8, xe);
-            store8(sK + i * PD + c8, xk);
-            store8(sQ + i * PD + c8, xq);
+            store4f(sE + tk * PD + 4 * cq, f32x4{gE[0], gE[1], gE[2], gE[3]});
+            store4f(sK + tk * PD + 4 * cq, f32x4{gK[0], gK[1], gK[2], gK[3]});
+            store4f(sQ + tk * PD + 4 * cq, f32x4{gQ[0], gQ[1], gQ[2], gQ[3]});
+            if ((j & 3) == 3) {
+                const int t4 = tk - 3;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                sET[(c8 + j) * PT + i] = E::to(xe[j]);
-                sZT[(c8 + j) * PT + i] = E::to(zv[j]);
-                sKTs[(c8 + j) * PT + i] = E::to(xend[j]);
+                for (int ch = 0; ch < 4; ++ch) {
+                    const int cc = 4 * cq + ch;
+                    store4f(sXT + cc * PT + t4, f32x4{xE[0][ch], xE[1][ch], xE[2][ch], xE[3][ch]});
+                    store4f(sXT + (D + cc) * PT + t4, f32x4{xZ[0][ch], xZ[1][ch], xZ[2][ch], xZ[3][ch]});
+                    store4f(sKT + cc * PT + t4, f32x4{xKe[0][ch], xKe[1][ch], xKe[2][ch], xKe[3][ch]});
+                }
             }
         }
-        if (tid < D) {
-            float Gend = 0.f;
-            if (a.decay == DECAY_CHANNEL) Gend = sG[(C - 1) * D + tid];
-            else if (a.decay == DECAY_SCALAR) Gend = sG[C - 1];
-            a.ws_gamma[(size_t)u * D + tid] = expf(Gend);
-        }
-    }
-    __syncthreads();
-    copy_block(wKT, C, sKTs, PT, D, C, tid, NT);
+        if (grp == NGRP - 1)
+            store4f(a.ws_gamma + (size_t)u * D + 4 * cq,
+                    f32x4{fast_exp(Gend[0]), fast_exp(Gend[1]), fast_exp(Gend[2]), fast_exp(Gend[3])});
+        // The raw inputs are consumed: fetch the next unit's now.
+        if (u + (int)gridDim.x < units) in.load(a, u + gridDim.x, cq, grp);
+        __syncthreads();
+        copy_block(wKT, C, sKT, PT, D, C, tid, NT);
 
-    // ---- Gram products on the matrix cores: T = E~ K~^T, A = Q~ K~^T (lower tiles). ----
-    f32x4 gacc[5];
+        // ---- B. Gram products (20 lower 16x16 tiles: 10 of T, 10 of A) ----
+        f32x4 gacc[NG];
 #pragma unroll
-    for (int s = 0; s < 5; ++s) {
-        const int p = w + 4 * s;
-        const int kind = p / 10;
-        int ti, tj;
-        lower_tile(p - kind * 10, ti, tj);
-        const IO *X = kind == 0 ? sE : sQ;
-        f32x4 acc = zero4();
+        for (int s = 0; s < NG; ++s) {
+            const int p = w + NW * s;
+            gacc[s] = zero4();
+            if (p < 20) {
+                const int kind = p / 10;
+                int ti, tj;
+                lower_tile(p - kind * 10, ti, tj);
+                const IO *X = kind == 0 ? sE : sQ;
 #pragma unroll
-        for (int ks = 0; ks < D / KS; ++ks)
-            acc = M::step(acc, X + ti * 16 * PD + ks * KS, PD, sK + tj * 16 * PD + ks * KS, PD);
-        gacc[s] = acc;
-    }
-    __syncthreads();  // Kend^T staging copied out; sG dead
-#pragma unroll
-    for (int s = 0; s < 5; ++s) {
-        const int p = w + 4 * s;
-        const int kind = p / 10;
-        int ti, tj;
-        lower_tile(p - kind * 10, ti, tj);
-        const int col = tj * 16 + lr;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = ti * 16 + 4 * lq + r;
-            if (kind == 0) sTf[row * PF + col] = col < row ? gacc[s][r] : 0.f;
-            else sA[row * PT + col] = E::to(col <= row ? gacc[s][r] : 0.f);
-        }
-    }
-    // Upper tiles of A are zero (products below run K over whole 32-token steps).
-    for (int i = tid; i < C * C; i += NT) {
-        const int row = i / C, col = i - (i / C) * C;
-        if ((col >> 4) > (row >> 4)) sA[row * PT + col] = E::to(0.f);
-    }
-    __syncthreads();
-
-    // ---- L = (I + T)^-1 in fp32. ----
-    // Diagonal 16 x 16 blocks by forward substitution, one column per thread.
-    if (tid < 64) {
-        const int blk = tid >> 4, j = tid & 15, o = blk * 16;
-        float x[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float s = i == j ? 1.f : 0.f;
-#pragma unroll
-            for (int m = 0; m < i; ++m) s -= sTf[(o + i) * PF + o + m] * x[m];
-            x[i] = s;
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sLf[(o + i) * PF + o + j] = x[i];
-    }
-    __syncthreads();
-    // Off-diagonal blocks, one block row at a time:
-    //   L_{bi,cj} = -L_{bi,bi} * sum_{m=cj}^{bi-1} T_{bi,m} L_{m,cj}
-    {
-        const int r = tid >> 4, cc = tid & 15;
-        for (int bi = 1; bi < 4; ++bi) {
-            float wv[3];
-            for (int cj = 0; cj < bi; ++cj) {
-                float s = 0.f;
-                for (int m = cj; m < bi; ++m)
-#pragma unroll
-                    for (int kk = 0; kk < 16; ++kk)
-                        s += sTf[(bi * 16 + r) * PF + m * 16 + kk] * sLf[(m * 16 + kk) * PF + cj * 16 + cc];
-                wv[cj] = s;
+                for (int ks = 0; ks < D / KS; ++ks)
+                    gacc[s] = M::step(gacc[s], X + ti * 16 * PD + ks * KS, PD, sK + tj * 16 * PD + ks * KS, PD);
             }
-            for (int cj = 0; cj < bi; ++cj) sLf[(bi * 16 + r) * PF + cj * 16 + cc] = wv[cj];
-            __syncthreads();
-            for (int cj = 0; cj < bi; ++cj) {
-                float s = 0.f;
+        }
+        __syncthreads();  // Kend^T staging copied out (its space becomes -T and A)
 #pragma unroll
-                for (int kk = 0; kk < 16; ++kk)
-                    s -= sLf[(bi * 16 + r) * PF + bi * 16 + kk] * sLf[(bi * 16 + kk) * PF + cj * 16 + cc];
-                wv[cj] = s;
+        for (int s = 0; s < NG; ++s) {
+            const int p = w + NW * s;
+            if (p < 20) {
+                const int kind = p / 10;
+                int ti, tj;
+                lower_tile(p - kind * 10, ti, tj);
+                const int col = tj * 16 + lr;
+                const float Gc = __shfl(Gl, col);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = ti * 16 + 4 * lq + r;
+                    float x = gacc[s][r];
+                    if (!chan) x *= fast_exp(fminf(__shfl(Gl, row) - Gc, 0.f));
+                    if (kind == 0) {
+                        if (ti == tj) sTd[(ti * 16 + 4 * lq + r) * 17 + lr] = col < row ? x : 0.f;
+                        else sTo[row * PT + col] = E::to(-x);
+                    } else {
+                        sA[row * PT + col] = E::to(col <= row ? x : 0.f);
+                    }
+                }
             }
-            __syncthreads();
-            for (int cj = 0; cj < bi; ++cj) sLf[(bi * 16 + r) * PF + cj * 16 + cc] = wv[cj];
-            __syncthreads();
         }
-    }
-    for (int i = tid; i < C * C; i += NT) {
-        const int row = i / C, col = i - (i / C) * C;
-        sL[row * PT + col] = E::to(col <= row ? sLf[row * PF + col] : 0.f);
-    }
-    __syncthreads();
+        // Zero tiles: -T on and above the diagonal blocks, A above them.
+        for (int i = tid; i < C * C; i += NT) {
+            const int row = i / C, col = i - (i / C) * C;
+            if ((col >> 4) >= (row >> 4)) sTo[row * PT + col] = E::to(0.f);
+            if ((col >> 4) > (row >> 4)) sA[row * PT + col] = E::to(0.f);
+        }
+        __syncthreads();
 
-    // ---- Y = L E~, U_z = L Z: wave w computes token rows 16w..16w+15. ----
-    const int nks = (16 * (w + 1) + KS - 1) / KS;  // L is lower: K runs over tokens <= 16w+15
-    f32x4 accY[CT], accU[CT];
+        // ---- C. diagonal block inverses (fp32 forward substitution) ----
+        for (int blk = w; blk < 4; blk += NW) {
+            if (lr == l) {  // lanes 0..15: one column each
+                const float *Tb = sTd + blk * 16 * 17;
+                float x[16];
 #pragma unroll
-    for (int tc = 0; tc < CT; ++tc) { accY[tc] = zero4(); accU[tc] = zero4(); }
-    for (int ks = 0; ks < nks; ++ks) {
-        const typename M::Frag la = M::load(sL + w * 16 * PT + ks * KS, PT);
+                for (int i = 0; i < 16; ++i) {
+                    float s = i == lr ? 1.f : 0.f;
 #pragma unroll
-        for (int tc = 0; tc < CT; ++tc) {
-            accY[tc] = M::mma(accY[tc], la, M::load(sET + tc * 16 * PT + ks * KS, PT));
-            accU[tc] = M::mma(accU[tc], la, M::load(sZT + tc * 16 * PT + ks * KS, PT));
+                    for (int m = 0; m < i; ++m) s -= Tb[i * 17 + m] * x[m];
+                    x[i] = s;
+                }
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sDb[(blk * 16 + i) * PDB + lr] = E::to(x[i]);
+            }
         }
-    }
-    // -Y^T and U_z^T for the next products (transposed: 4 consecutive tokens per lane).
-#pragma unroll
-    for (int tc = 0; tc < CT; ++tc) {
-        const int col = tc * 16 + lr, tok = w * 16 + 4 * lq;
-        store4f(sYT + col * PT + tok, -accY[tc]);
-        store4f(sUzT + col * PT + tok, accU[tc]);
-    }
-    __syncthreads();  // E~^T and Z^T are dead from here
-#pragma unroll
-    for (int tc = 0; tc < CT; ++tc)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sYs[(w * 16 + 4 * lq + r) * PD + tc * 16 + lr] = E::to(accY[tc][r]);
-    __syncthreads();
-    copy_block(wY, D, sYs, PD, C, D, tid, NT);
-    copy_block(wUzT, C, sUzT, PT, D, C, tid, NT);
+        __syncthreads();
 
-    // ---- W_q = s (Q~ - A Y), O_z = s A U_z. ----
-    f32x4 accW[CT], accO[CT];
+        // ---- C. blocked forward substitution; wave w owns columns WC*w..WC*w+WC-1 of [E~ | Z] ----
+        IO *tmp = sE + w * WC * PTMP;
+        if (PTMP > 16)  // bf16: the 32-deep K step reads temporary columns 16..31; keep them zero
+            for (int i = l; i < WC * (PTMP - 16); i += 64)
+                tmp[(i / (PTMP - 16)) * PTMP + 16 + i % (PTMP - 16)] = E::to(0.f);
 #pragma unroll
-    for (int tc = 0; tc < CT; ++tc) {
+        for (int blk = 0; blk < 4; ++blk) {
+            f32x4 acc[NCTS];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) accW[tc][r] = E::from(sQ[(w * 16 + 4 * lq + r) * PD + tc * 16 + lr]);
-        accO[tc] = zero4();
-    }
-    for (int ks = 0; ks < nks; ++ks) {
-        const typename M::Frag aa = M::load(sA + w * 16 * PT + ks * KS, PT);
+            for (int ct = 0; ct < NCTS; ++ct)
+                acc[ct] = R4::widen(R4::load(sXT + (WC * w + 16 * ct + lr) * PT + 16 * blk + 4 * lq));
 #pragma unroll
-        for (int tc = 0; tc < CT; ++tc) {
-            accW[tc] = M::mma(accW[tc], aa, M::load(sYT + tc * 16 * PT + ks * KS, PT));
-            accO[tc] = M::mma(accO[tc], aa, M::load(sUzT + tc * 16 * PT + ks * KS, PT));
+            for (int ks = 0; ks < (16 * blk + KS - 1) / KS; ++ks)
+#pragma unroll
+                for (int ct = 0; ct < NCTS; ++ct)
+                    acc[ct] = M::step(acc[ct], sTo + 16 * blk * PT + ks * KS, PT,
+                                      sXT + (WC * w + 16 * ct) * PT + ks * KS, PT);
+#pragma unroll
+            for (int ct = 0; ct < NCTS; ++ct) store4f(tmp + (16 * ct + lr) * PTMP + 4 * lq, acc[ct]);
+#pragma unroll
+            for (int ct = 0; ct < NCTS; ++ct) {
+                const f32x4 x = mma_k16<IO>(zero4(), sDb + blk * 16 * PDB, PDB, tmp + 16 * ct * PTMP, PTMP);
+                store4f(sXT + (WC * w + 16 * ct + lr) * PT + 16 * blk + 4 * lq, x);
+            }
         }
-    }
-    const float sc = a.scale;
+
+        // ---- D. P = A [Y | U_z] on this wave's columns; W_q = s (Q~ - P), O_z = s P ----
+        const float sc = a.scale;
+        const bool yside = WC * w < D;
 #pragma unroll
-    for (int tc = 0; tc < CT; ++tc) {
-        const int col = tc * 16 + lr, tok = w * 16 + 4 * lq;
+        for (int rt = 0; rt < 4; ++rt) {
+            f32x4 acc[NCTS];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sWs[(tok + r) * PD + col] = E::to(sc * accW[tc][r]);
-        store4f(sOzs + col * PT + tok, sc * accO[tc]);
+            for (int ct = 0; ct < NCTS; ++ct) acc[ct] = zero4();
+#pragma unroll
+            for (int ks = 0; ks < (16 * (rt + 1) + KS - 1) / KS; ++ks)
+#pragma unroll
+                for (int ct = 0; ct < NCTS; ++ct)
+                    acc[ct] = M::step(acc[ct], sA + 16 * rt * PT + ks * KS, PT, sXT + (WC * w + 16 * ct) * PT + ks * KS,
+                                      PT);
+#pragma unroll
+            for (int ct = 0; ct < NCTS; ++ct) {
+                const int col = WC * w + 16 * ct + lr, tok = 16 * rt + 4 * lq;
+                if (yside) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        float qd = E::from(sQ[(tok + r) * PD + col]);
+                        if (!chan) qd *= fast_exp(__shfl(Gl, tok + r));
+                        sWs[(tok + r) * PD + col] = E::to(sc * (qd - acc[ct][r]));
+                    }
+                } else {
+                    store4f(wOzT + (size_t)(col - D) * C + tok, sc * acc[ct]);
+                }
+            }
+        }
+        __syncthreads();
+
+        // Workspace stores: Y row-major (transposed read of Y^T), U_z^T, W_q.
+        {
+            constexpr int V = 16 / sizeof(IO), PER = D / V;
+            for (int i = tid; i < C * PER; i += NT) {
+                const int tok = i / PER, c0 = (i - tok * PER) * V;
+                IO vals[V];
+#pragma unroll
+                for (int j = 0; j < V; ++j) vals[j] = sXT[(c0 + j) * PT + tok];
+                *reinterpret_cast<uint4 *>(wY + tok * D + c0) = *reinterpret_cast<const uint4 *>(vals);
+            }
+        }
+        copy_block(wUzT, C, sXT + D * PT, PT, D, C, tid, NT);
+        copy_block(wWq, D, sWs, PD, C, D, tid, NT);
     }
-    __syncthreads();
-    copy_block(wWq, D, sWs, PD, C, D, tid, NT);
-    copy_block(wOzT, C, sOzs, PT, D, C, tid, NT);
 }
 
 // Sequential sweep over chunks for one (sequence, V head, value tile of BV =
 // 16*NCT columns). NW = D/32 waves; wave w keeps state rows 32w..32w+31 in
 // accumulator layout and computes token tiles [w*TPW, (w+1)*TPW) of P, R.
+// Each wave reads only its own slice of a chunk's factors (its token rows of
+// Y and W_q, its channel rows of Kend^T), so those slices are prefetched into
+// registers PF chunks ahead and the global-memory latency leaves the chain.
 template <typename IO, int D, int NCT>
-__global__ __launch_bounds__(2 * D) void chunk_sweep(ChunkArgs a, int NVT, int G) {
-    using E = Elem<IO>;
+struct SweepOps {
     using M = Mma<IO>;
     using F = typename M::Frag;
-    constexpr int NW = D / 32, BV = 16 * NCT, TPW = 4 / NW;
-    constexpr int KS = M::KS, KD = D / KS, KC = C / KS;
-    constexpr int LS = D + 8, LU = C + 8;
+    static constexpr int NW = D / 32, TPW = 4 / NW, KD = D / M::KS, KC = C / M::KS;
+    using R4 = Raw4<IO>;
+    F ya[TPW][KD], wa[TPW][KD], ka[2][KC];
+    typename R4::type uz[TPW][NCT], oz[TPW][NCT];
+    f32x4 g4[2];
+
+    __device__ __forceinline__ void load(const IO *wsb, const float *wsg, size_t u, int w, int col0) {
+        const int l = threadIdx.x & 63, lr = l & 15, lq = l >> 4;
+        const IO *Y = wsb + u * chunk_ws_io_elems(D), *Wq = Y + C * D, *KT = Wq + C * D, *UzT = KT + D * C,
+                 *OzT = UzT + D * C;
+        const float *gam = wsg + u * D;
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt) {
+            const int T0 = (w * TPW + tt) * 16;
+#pragma unroll
+            for (int ks = 0; ks < KD; ++ks) {
+                ya[tt][ks] = M::load(Y + T0 * D + ks * M::KS, D);
+                wa[tt][ks] = M::load(Wq + T0 * D + ks * M::KS, D);
+            }
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                const size_t off = (size_t)(col0 + 16 * ct + lr) * C + T0 + 4 * lq;
+                uz[tt][ct] = R4::load(UzT + off);
+                oz[tt][ct] = R4::load(OzT + off);
+            }
+        }
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            const int ch0 = 32 * w + 16 * rt;
+#pragma unroll
+            for (int ks = 0; ks < KC; ++ks) ka[rt][ks] = M::load(KT + ch0 * C + ks * M::KS, C);
+            g4[rt] = load4f(gam + ch0 + 4 * lq);
+        }
+    }
+};
+
+// One chunk of the sweep. TAIL = the chunk may hold fewer than C tokens
+// (only the last one), so output rows are stored under a predicate; every
+// other chunk stores unconditionally, which keeps the number of memory
+// operations in flight static and lets the prefetches stay in flight.
+template <typename IO, int D, int NCT, bool TAIL>
+__device__ __forceinline__ void sweep_chunk(const SweepOps<IO, D, NCT> &op, f32x4 (&S)[2][NCT], IO *sST, IO *sUT,
+                                            IO *sO, IO *orow0, size_t orow_stride, int n_valid) {
+    using M = Mma<IO>;
+    using F = typename M::Frag;
+    using Ops = SweepOps<IO, D, NCT>;
+    constexpr int BV = 16 * NCT, TPW = Ops::TPW, KS = M::KS, KD = Ops::KD, KC = Ops::KC;
+    constexpr int LS = D + 8, LU = C + 8, LO = BV + 8;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, lr = l & 15, lq = l >> 4;
+
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+            store4f(sST + (16 * ct + lr) * LS + 32 * w + 16 * rt + 4 * lq, S[rt][ct]);
+    __syncthreads();
+
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+        const int T0 = (w * TPW + tt) * 16;
+        f32x4 accP[NCT], accR[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) { accP[ct] = zero4(); accR[ct] = zero4(); }
+#pragma unroll
+        for (int ks = 0; ks < KD; ++ks) {
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                const F sb = M::load(sST + 16 * ct * LS + ks * KS, LS);
+                accP[ct] = M::mma(accP[ct], op.ya[tt][ks], sb);
+                accR[ct] = M::mma(accR[ct], op.wa[tt][ks], sb);
+            }
+        }
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            const int col = 16 * ct + lr, tok = T0 + 4 * lq;
+            const f32x4 U = Ops::R4::widen(op.uz[tt][ct]) - accP[ct];
+            const f32x4 O = accR[ct] + Ops::R4::widen(op.oz[tt][ct]);
+            store4f(sUT + col * LU + tok, U);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sO[(tok + r) * LO + col] = Elem<IO>::to(O[r]);
+        }
+    }
+    __syncthreads();
+
+    // Output rows: 16 bytes per thread, contiguous within each token row.
+    {
+        constexpr int V = 16 / sizeof(IO), PER = BV / V;
+        for (int i = threadIdx.x; i < C * PER; i += blockDim.x) {
+            const int tok = i / PER, c8 = (i - tok * PER) * V;
+            if (!TAIL || tok < n_valid)
+                *reinterpret_cast<uint4 *>(orow0 + tok * orow_stride + c8) =
+                    *reinterpret_cast<const uint4 *>(sO + tok * LO + c8);
+        }
+    }
+
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) S[rt][ct] *= op.g4[rt];
+#pragma unroll
+        for (int ks = 0; ks < KC; ++ks)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+                S[rt][ct] = M::mma(S[rt][ct], op.ka[rt][ks], M::load(sUT + 16 * ct * LU + ks * KS, LU));
+    }
+}
+
+template <typename IO, int D, int NCT, int PF>
+__global__ __launch_bounds__(2 * D) void chunk_sweep(ChunkArgs a, int NVT, int G) {
+    using Ops = SweepOps<IO, D, NCT>;
+    constexpr int BV = 16 * NCT;
+    constexpr int LS = D + 8, LU = C + 8, LO = BV + 8;
     __shared__ __align__(16) IO sST[BV * LS];  // S_c^T in the io dtype
     __shared__ __align__(16) IO sUT[BV * LU];  // U^T in the io dtype
+    __shared__ __align__(16) IO sO[C * LO];    // output tile, token rows
 
     // Work index: blocks that share an XCD (blockIdx % 8) take consecutive
     // work items, so the value tiles of one head read its chunk factors
@@ -398,65 +582,33 @@ __global__ __launch_bounds__(2 * D) void chunk_sweep(ChunkArgs a, int NVT, int G
             }
 
     const IO *wsb = static_cast<const IO *>(a.ws_io);
-    const size_t UE = chunk_ws_io_elems(D);
-    IO *o = static_cast<IO *>(a.o);
-    for (int c = 0; c < a.NC; ++c) {
-        const size_t u = (size_t)bh * a.NC + c;
-        const IO *Y = wsb + u * UE, *Wq = Y + C * D, *KT = Wq + C * D, *UzT = KT + D * C, *OzT = UzT + D * C;
-        const float *gam = a.ws_gamma + u * D;
+    const size_t u0 = (size_t)bh * a.NC;
+    const int NC = a.NC;
+    const size_t orow_stride = (size_t)a.Hv * D;
+    IO *obase = static_cast<IO *>(a.o) + ((size_t)b * a.T * a.Hv + h) * D + col0;
 
+    if (NC > 0) {
+        Ops ring[PF];
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
-                store4f(sST + (16 * ct + lr) * LS + 32 * w + 16 * rt + 4 * lq, S[rt][ct]);
-        __syncthreads();
+        for (int j = 0; j < PF; ++j) ring[j].load(wsb, a.ws_gamma, u0 + min(j, NC - 1), w, col0);
 
+        // Pipelined part: every chunk but the last is full (C tokens).
+        int c = 0;
+        for (; c + PF <= NC - 1; c += PF) {
 #pragma unroll
-        for (int tt = 0; tt < TPW; ++tt) {
-            const int T0 = (w * TPW + tt) * 16;
-            f32x4 accP[NCT], accR[NCT];
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) { accP[ct] = zero4(); accR[ct] = zero4(); }
-#pragma unroll
-            for (int ks = 0; ks < KD; ++ks) {
-                const F ya = M::load(Y + T0 * D + ks * KS, D);
-                const F wa = M::load(Wq + T0 * D + ks * KS, D);
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) {
-                    const F sb = M::load(sST + 16 * ct * LS + ks * KS, LS);
-                    accP[ct] = M::mma(accP[ct], ya, sb);
-                    accR[ct] = M::mma(accR[ct], wa, sb);
-                }
-            }
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                const int col = 16 * ct + lr, tok = T0 + 4 * lq;
-                const f32x4 U = load4f(UzT + (size_t)(col0 + col) * C + tok) - accP[ct];
-                const f32x4 O = accR[ct] + load4f(OzT + (size_t)(col0 + col) * C + tok);
-                store4f(sUT + col * LU + tok, U);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = c * C + tok + r;
-                    if (t < a.T) o[(((size_t)b * a.T + t) * a.Hv + h) * D + col0 + col] = E::to(O[r]);
-                }
+            for (int j = 0; j < PF; ++j) {
+                sweep_chunk<IO, D, NCT, false>(ring[j], S, sST, sUT, sO, obase + (size_t)(c + j) * C * orow_stride,
+                                               orow_stride, C);
+                ring[j].load(wsb, a.ws_gamma, u0 + min(c + j + PF, NC - 1), w, col0);
             }
         }
-        __syncthreads();
-
+        // Remainder: ring slot j holds chunk c + j (clamped); the last chunk may be partial.
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            const int ch0 = 32 * w + 16 * rt;
-            const f32x4 g4 = load4f(gam + ch0 + 4 * lq);
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) S[rt][ct] *= g4;
-#pragma unroll
-            for (int ks = 0; ks < KC; ++ks) {
-                const F ka = M::load(KT + ch0 * C + ks * KS, C);
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct)
-                    S[rt][ct] = M::mma(S[rt][ct], ka, M::load(sUT + 16 * ct * LU + ks * KS, LU));
-            }
+        for (int j = 0; j < PF; ++j) {
+            const int cj = c + j;
+            if (cj < NC)
+                sweep_chunk<IO, D, NCT, true>(ring[j], S, sST, sUT, sO, obase + (size_t)cj * C * orow_stride,
+                                              orow_stride, a.T - cj * C);
         }
     }
 
@@ -471,27 +623,50 @@ __global__ __launch_bounds__(2 * D) void chunk_sweep(ChunkArgs a, int NVT, int G
             }
 }
 
+static int device_cus() {
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+            cus = n;
+        else
+            cus = 256;
+    }
+    return cus;
+}
+
 template <typename IO, int D, int NCT>
 static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t s) {
-    using Lay = PrepLayout<IO, D>;
-    static_assert(Lay::BYTES <= 160 * 1024, "LDS budget");
+    using Cfg = PrepCfg<IO, D>;
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_prep<IO, D>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lay::BYTES);
-        if (e != hipSuccess) return e;
+        const void *fns[4] = {reinterpret_cast<const void *>(&chunk_prep<IO, D, false, false>),
+                              reinterpret_cast<const void *>(&chunk_prep<IO, D, false, true>),
+                              reinterpret_cast<const void *>(&chunk_prep<IO, D, true, false>),
+                              reinterpret_cast<const void *>(&chunk_prep<IO, D, true, true>)};
+        for (const void *f : fns) {
+            hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::BYTES);
+            if (e != hipSuccess) return e;
+        }
         attr_set = true;
     }
-    const size_t units = (size_t)a.B * a.Hv * a.NC;
+    const long long units = (long long)a.B * a.Hv * a.NC;
     if (units > 0) {
-        hipLaunchKernelGGL((chunk_prep<IO, D>), dim3((unsigned)units), dim3(256), Lay::BYTES, s, a);
+        // Persistent: one workgroup per compute unit (the LDS footprint allows one).
+        const long long grid = units < device_cus() ? units : device_cus();
+        const bool chan = a.decay == DECAY_CHANNEL, bw = a.beta == nullptr;
+        if (chan && bw) hipLaunchKernelGGL((chunk_prep<IO, D, true, true>), dim3((unsigned)grid), dim3(Cfg::NT), Cfg::BYTES, s, a);
+        else if (chan) hipLaunchKernelGGL((chunk_prep<IO, D, true, false>), dim3((unsigned)grid), dim3(Cfg::NT), Cfg::BYTES, s, a);
+        else if (bw) hipLaunchKernelGGL((chunk_prep<IO, D, false, true>), dim3((unsigned)grid), dim3(Cfg::NT), Cfg::BYTES, s, a);
+        else hipLaunchKernelGGL((chunk_prep<IO, D, false, false>), dim3((unsigned)grid), dim3(Cfg::NT), Cfg::BYTES, s, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     constexpr int NVT = D / (16 * NCT);
     const int G = a.B * a.Hv * NVT;
     const int grid = (G + 7) / 8 * 8;
-    hipLaunchKernelGGL((chunk_sweep<IO, D, NCT>), dim3(grid), dim3(2 * D), 0, s, a, NVT, G);
+    constexpr int PF = sizeof(IO) == 2 ? 3 : 1;  // prefetch depth (fp32 fragments are 2x larger)
+    hipLaunchKernelGGL((chunk_sweep<IO, D, NCT, PF>), dim3(grid), dim3(2 * D), 0, s, a, NVT, G);
     return hipGetLastError();
 }
 

@@ -25,12 +25,14 @@ typedef uint16_t bf16_t;
 
 __device__ __forceinline__ float bf2f(bf16_t u) { return __uint_as_float((uint32_t)u << 16); }
 
-// float -> bfloat16, round to nearest even; NaN stays a (quiet) NaN.
-__device__ __forceinline__ bf16_t f2bf(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (bf16_t)(u >> 16);
+// float -> bfloat16, round to nearest even (gfx950 converts in hardware,
+// v_cvt_pk_bf16_f32; NaN stays NaN).
+__device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
+
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+__device__ __forceinline__ uint32_t f2bf2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
 template <typename T> struct Elem;
@@ -94,9 +96,22 @@ __device__ __forceinline__ f32x4 load4f(const bf16_t *p) {
 }
 __device__ __forceinline__ void store4f(float *p, f32x4 x) { *reinterpret_cast<f32x4 *>(p) = x; }
 __device__ __forceinline__ void store4f(bf16_t *p, f32x4 x) {
-    u16x4 u = {f2bf(x[0]), f2bf(x[1]), f2bf(x[2]), f2bf(x[3])};
-    *reinterpret_cast<u16x4 *>(p) = u;
+    *reinterpret_cast<uint2 *>(p) = uint2{f2bf2(x[0], x[1]), f2bf2(x[2], x[3])};
 }
+
+// Four consecutive stored elements kept raw in registers (no conversion at
+// load time, so a prefetch does not wait for its data), widened at use.
+template <typename T> struct Raw4;
+template <> struct Raw4<float> {
+    using type = f32x4;
+    __device__ __forceinline__ static type load(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+    __device__ __forceinline__ static f32x4 widen(type r) { return r; }
+};
+template <> struct Raw4<bf16_t> {
+    using type = u16x4;
+    __device__ __forceinline__ static type load(const bf16_t *p) { return *reinterpret_cast<const u16x4 *>(p); }
+    __device__ __forceinline__ static f32x4 widen(type u) { return f32x4{bf2f(u[0]), bf2f(u[1]), bf2f(u[2]), bf2f(u[3])}; }
+};
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
