@@ -88,6 +88,26 @@ template <> struct Mma<float> {
     }
 };
 
+// acc += A[16 x 16] * (Bt[16 x 16])^T: bf16 on v_mfma_f32_16x16x16_bf16 (lane l
+// feeds 4 elements: row l % 16, K-slice 4*(l/16)); fp32 as four K=4 steps.
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+template <typename T> struct Mma16;
+template <> struct Mma16<bf16_t> {
+    __device__ __forceinline__ static f32x4 step(f32x4 acc, const bf16_t *A, int lda, const bf16_t *Bt, int ldb) {
+        const int l = lane_id();
+        const s16x4 a = *reinterpret_cast<const s16x4 *>(A + (l & 15) * lda + (l >> 4) * 4);
+        const s16x4 b = *reinterpret_cast<const s16x4 *>(Bt + (l & 15) * ldb + (l >> 4) * 4);
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc, 0, 0, 0);
+    }
+};
+template <> struct Mma16<float> {
+    __device__ __forceinline__ static f32x4 step(f32x4 acc, const float *A, int lda, const float *Bt, int ldb) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) acc = Mma<float>::step(acc, A + 4 * ks, lda, Bt + 4 * ks, ldb);
+        return acc;
+    }
+};
+
 // Four consecutive elements (8 or 16 bytes, aligned) widened to float, and back.
 __device__ __forceinline__ f32x4 load4f(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
 __device__ __forceinline__ f32x4 load4f(const bf16_t *p) {

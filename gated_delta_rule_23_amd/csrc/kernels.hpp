@@ -30,14 +30,14 @@ struct ChunkArgs {
     const float *S0;         // [B,Hv,D,D] or null
     void *o;                 // [B,T,Hv,D]
     float *ST;               // [B,Hv,D,D]
-    void *ws_io;             // per chunk unit: Y, Wq (C x D), KendT, UzT, OzT (D x C), io dtype
+    void *ws_io;             // per chunk unit: Y, Q~ (C x D), Kend^T, U_z^T (D x C), A (C x C), io dtype
     float *ws_gamma;         // per chunk unit: end-of-chunk decay, D floats
     int B, T, Hqk, Hv, decay, NC;
     float scale;
 };
 
 // Elements of the io-dtype workspace per chunk unit, and the byte layout.
-__host__ __device__ inline size_t chunk_ws_io_elems(int D) { return (size_t)5 * kChunk * D; }
+__host__ __device__ inline size_t chunk_ws_io_elems(int D) { return (size_t)4 * kChunk * D + (size_t)kChunk * kChunk; }
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 inline size_t chunk_ws_bytes(int B, int Hv, int NC, int D, int io) {
     const size_t units = (size_t)B * Hv * NC;

@@ -108,11 +108,11 @@ int gdr_state_alloc(int B, int H_v, int d_k, int d_v, float **state, size_t *byt
 int gdr_state_free(float *state);
 
 /* Device workspace bytes gdr_chunk_fwd needs for `desc`; needs no GPU.
- * The workspace holds, per (sequence, V head, chunk), the chunk's
- * precomputed factors: erase-side WY factor Y and query factor
- * (C x d_k each), keys decayed to the chunk end (d_k x C), write-side factor
- * U_z and in-chunk output (d_v x C each), all in bfloat16 (float32 for
- * float32 io), plus the end-of-chunk decay (d_k float32). */
+ * The workspace holds, per (sequence, V head, chunk), the chunk's factors
+ * that do not depend on the state: the erase-side WY factor Y and the decayed
+ * queries (C x d_k each), the keys decayed to the chunk end and the
+ * write-side factor U_z (d_k x C and d_v x C), the in-chunk read matrix A
+ * (C x C), all in the io dtype, plus the end-of-chunk decay (d_k float32). */
 int gdr_chunk_workspace_bytes(const gdr_desc *desc, size_t *bytes);
 
 /* Chunkwise-parallel prefill over T tokens: "Chunkwise KDA" and "Pipeline

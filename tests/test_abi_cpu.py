@@ -43,7 +43,7 @@ def test_state_size_pin():
 def test_workspace_bytes():
     d = gdr.make_desc(1, 4096, 16, 48, 128, gdr.GDR_BF16, gdr.GDR_DECAY_SCALAR)
     units = 48 * 64
-    io = units * 5 * 64 * 128 * 2
+    io = units * (4 * 64 * 128 + 64 * 64) * 2   # Y, Q~, Kend^T, U_z^T (64 x 128) and A (64 x 64), bf16
     assert gdr.gdr_chunk_workspace_bytes(d) == ((io + 255) // 256) * 256 + units * 128 * 4
     d0 = gdr.make_desc(1, 0, 16, 48, 128, gdr.GDR_BF16, gdr.GDR_DECAY_SCALAR)
     assert gdr.gdr_chunk_workspace_bytes(d0) == 0
