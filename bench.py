@@ -48,16 +48,22 @@ def decode_algorithmic(wl):
     return state, state + io
 
 
-def cpu_baseline(wl, inp, heads):
+def cpu_baseline(wl, inp, heads, min_seconds=10.0, max_reps=20):
+    """Time the fp64 oracle (as it stands) on the given V heads of the prefill
+    workload, repeating the run until about min_seconds of CPU work."""
     import oracle
-    t0 = time.perf_counter()
-    oracle.recurrent(inp["q"], inp["k"], inp["v"], g=inp["g"], beta=inp["beta"], b=inp["b"], w=inp["w"],
-                     scale=wl.scale, S0=inp["S0"], heads=heads)
-    dt = time.perf_counter() - t0
+    reps, total = 0, 0.0
+    while reps < max_reps and (reps == 0 or total < min_seconds):
+        t0 = time.perf_counter()
+        oracle.recurrent(inp["q"], inp["k"], inp["v"], g=inp["g"], beta=inp["beta"], b=inp["b"], w=inp["w"],
+                         scale=wl.scale, S0=inp["S0"], heads=heads)
+        total += time.perf_counter() - t0
+        reps += 1
+    dt = total / reps
     toks = wl.B * wl.T * len(heads) / wl.Hv
     return {"value": toks / dt, "unit": "tokens/s", "cores": oracle.default_threads(), "kind": "oracle",
-            "sample": f"fp64 token-by-token oracle on {len(heads)} of {wl.Hv} V heads, all {wl.T} tokens "
-                      f"(scaled to whole-layer tokens/s); {dt:.1f} s"}
+            "sample": f"fp64 token-by-token oracle on {len(heads)} of {wl.Hv} V heads, all {wl.T} tokens, "
+                      f"{reps} runs, {dt:.2f} s per run (tokens/s scaled to the whole layer)"}
 
 
 def main(argv=None):
@@ -66,8 +72,10 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-steps", type=int, default=256)
-    ap.add_argument("--cpu-heads", type=int, default=12, help="V heads in the CPU-oracle sample (0 = skip)")
+    ap.add_argument("--cpu-heads", type=int, default=48, help="V heads in the CPU-oracle sample (0 = skip)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (for scaling memory counters)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (the mixer shards over "
@@ -88,6 +96,14 @@ def main(argv=None):
         if a.dtype == np.uint16:
             return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(a).to(dev)
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * 2 ** 20 // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---- prefill ----
     wl = gs.QWEN_GDN_PREFILL

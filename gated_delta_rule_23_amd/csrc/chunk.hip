@@ -38,6 +38,12 @@
 namespace gdr {
 
 constexpr int C = kChunk;
+#ifndef SWEEP_PF
+#define SWEEP_PF 3
+#endif
+#ifndef SWEEP_NCT128
+#define SWEEP_NCT128 2
+#endif
 
 __host__ __device__ constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 __host__ __device__ constexpr size_t a16(size_t x) { return (x + 15) & ~(size_t)15; }
@@ -50,6 +56,66 @@ __device__ __forceinline__ void copy_block(T *dst, int dld, const T *src, int sl
     for (int i = tid; i < rows * per_row; i += nt) {
         const int r = i / per_row, c = (i - r * per_row) * V;
         *reinterpret_cast<uint4 *>(dst + (size_t)r * dld + c) = *reinterpret_cast<const uint4 *>(src + (size_t)r * sld + c);
+    }
+}
+
+// Workspace matrices are stored in "fragment order": the data one wave's
+// matrix-core operand load needs is contiguous. For a row-major R x K matrix
+// read as A (or B^T) operand fragments, the fragment (row tile rt, K step ks)
+// is one block of 64 lanes x FE elements (FE = KS / 4: 8 for bf16, 1 for
+// fp32), lane l holding row 16 rt + l % 16, columns KS ks + FE (l / 16) ...
+template <typename IO>
+__device__ __forceinline__ size_t frag_off(int r, int c, int K) {
+    constexpr int KS = Mma<IO>::KS, FE = KS / 4;
+    const int lane = (r & 15) + 16 * ((c % KS) / FE);
+    return ((size_t)((r >> 4) * (K / KS) + c / KS) * 64 + lane) * FE + c % FE;
+}
+template <typename IO>
+__device__ __forceinline__ typename Mma<IO>::Frag load_frag(const IO *M, int rt, int ks, int K) {
+    constexpr int KS = Mma<IO>::KS, FE = KS / 4;
+    return *reinterpret_cast<const typename Mma<IO>::Frag *>(M + ((size_t)(rt * (K / KS) + ks) * 64 + (threadIdx.x & 63)) * FE);
+}
+// ... and a token-contiguous D x C matrix read in accumulator layout (lane
+// l = col % 16 + 16 (tok % 16) / 4 holds 4 consecutive tokens of one column)
+// is stored as one block of 64 lanes x 4 elements per (token tile, column tile).
+template <int D>
+__device__ __forceinline__ size_t cfrag_off(int col, int tok) {
+    const int lane = (col & 15) + 16 * ((tok & 15) >> 2);
+    return ((size_t)((tok >> 4) * (D / 16) + (col >> 4)) * 64 + lane) * 4 + (tok & 3);
+}
+
+// Store a row-major R x K matrix from shared memory in fragment order,
+// optionally scaling row r by rowscale[r].
+template <typename IO>
+__device__ __forceinline__ void store_frag_rows(IO *dst, int R, int K, const IO *src, int sld, const float *rowscale,
+                                                int tid, int nt) {
+    constexpr int V = 16 / sizeof(IO);
+    const int per = K / V;
+    for (int i = tid; i < R * per; i += nt) {
+        const int r = i / per, c0 = (i - r * per) * V;
+        IO vals[V];
+        *reinterpret_cast<uint4 *>(vals) = *reinterpret_cast<const uint4 *>(src + r * sld + c0);
+        if (rowscale) {
+            const float sc = rowscale[r];
+#pragma unroll
+            for (int j = 0; j < V; ++j) vals[j] = Elem<IO>::to(Elem<IO>::from(vals[j]) * sc);
+        }
+        if constexpr (sizeof(IO) == 2) {  // V == FE: one fragment slot
+            *reinterpret_cast<uint4 *>(dst + frag_off<IO>(r, c0, K)) = *reinterpret_cast<const uint4 *>(vals);
+        } else {
+#pragma unroll
+            for (int j = 0; j < V; ++j) dst[frag_off<IO>(r, c0 + j, K)] = vals[j];
+        }
+    }
+}
+
+// Store a token-contiguous D x C matrix (row stride sld) in accumulator fragment order.
+template <typename IO, int D>
+__device__ __forceinline__ void store_cfrag(IO *dst, const IO *src, int sld, int tid, int nt) {
+    for (int i = tid; i < D * (C / 4); i += nt) {
+        const int col = i / (C / 4), t4 = (i - col * (C / 4)) * 4;
+        *reinterpret_cast<typename Raw4<IO>::type *>(dst + cfrag_off<D>(col, t4)) =
+            *reinterpret_cast<const typename Raw4<IO>::type *>(src + col * sld + t4);
     }
 }
 
@@ -143,8 +209,8 @@ struct PrepIn {
 //  C. (I + T) X = [E~ | Z] by blocked forward substitution over four 16-token
 //     blocks: the 16 x 16 diagonal blocks are inverted in fp32, the rest are
 //     matrix-core products; each wave solves its own WC right-hand-side columns.
-// Workspace per unit: Y and Q~ row-major, Kend^T and U_z^T token-contiguous,
-// A row-major, gamma. Threads of the elementwise phase run token-fast
+// Workspace per unit, in fragment order: Y, Q~ (C x D), Kend^T (D x C), A
+// (C x C) as matrix-core operands, U_z^T in accumulator layout; gamma. Threads of the elementwise phase run token-fast
 // (grp = tid % NGRP) so the token-contiguous stores of neighbouring lanes are
 // adjacent in LDS.
 template <typename IO, int D, bool CHAN, bool BW>
@@ -297,24 +363,9 @@ __global__ __launch_bounds__(D >= 64 ? 256 : 128) void chunk_prep(ChunkArgs a) {
         // The raw inputs are consumed: fetch the next unit's now.
         if (u + (int)gridDim.x < units) in.load(a, u + gridDim.x, cq, grp);
         __syncthreads();
-        copy_block(wKT, C, sKT, PT, D, C, tid, NT);
-        // Q~ row-major for the sweep (scalar decay: the stored raw q times exp(G) per token).
-        {
-            constexpr int V = 16 / sizeof(IO), PER = D / V;
-#pragma unroll
-            for (int i = tid; i < C * PER; i += NT) {
-                const int tok = i / PER, c0 = (i - tok * PER) * V;
-                if constexpr (CHAN) {
-                    *reinterpret_cast<uint4 *>(wQ + tok * D + c0) = *reinterpret_cast<const uint4 *>(sQ + tok * PD + c0);
-                } else {
-                    const float eg = sEG[tok];
-                    IO vals[V];
-#pragma unroll
-                    for (int j = 0; j < V; ++j) vals[j] = E::to(E::from(sQ[tok * PD + c0 + j]) * eg);
-                    *reinterpret_cast<uint4 *>(wQ + tok * D + c0) = *reinterpret_cast<const uint4 *>(vals);
-                }
-            }
-        }
+        store_frag_rows(wKT, D, C, sKT, PT, nullptr, tid, NT);
+        // Q~ for the sweep (scalar decay: the stored raw q times exp(G) per token).
+        store_frag_rows(wQ, C, D, sQ, PD, CHAN ? nullptr : sEG, tid, NT);
 
         // ---- B. Gram products (20 lower 16x16 tiles: 10 of T, 10 of A) ----
         f32x4 gacc[NG];
@@ -371,7 +422,7 @@ __global__ __launch_bounds__(D >= 64 ? 256 : 128) void chunk_prep(ChunkArgs a) {
             }
         }
         __syncthreads();
-        copy_block(wA, C, sA, PT, C, C, tid, NT);
+        store_frag_rows(wA, C, C, sA, PT, nullptr, tid, NT);
 
         // ---- C. diagonal block inverses: right-looking fp32 substitution, one column per lane ----
         for (int blk = w; blk < 4; blk += NW) {
@@ -423,8 +474,8 @@ __global__ __launch_bounds__(D >= 64 ? 256 : 128) void chunk_prep(ChunkArgs a) {
         __syncthreads();
 
         // Workspace stores: Y row-major; U_z^T.
-        copy_block(wY, D, sYs, PD, C, D, tid, NT);
-        copy_block(wUzT, C, sXT + D * PT, PT, D, C, tid, NT);
+        store_frag_rows(wY, C, D, sYs, PD, nullptr, tid, NT);
+        store_cfrag<IO, D>(wUzT, sXT + D * PT, PT, tid, NT);
     }
 }
 
@@ -450,28 +501,29 @@ struct SweepOps {
     f32x4 g4[2];
 
     __device__ __forceinline__ void load(const IO *wsb, const float *wsg, size_t u, int w, int col0) {
-        const int l = threadIdx.x & 63, lr = l & 15, lq = l >> 4;
+        const int l = threadIdx.x & 63, lq = l >> 4;
         const IO *Y = wsb + u * chunk_ws_io_elems(D), *Qt = Y + C * D, *KT = Qt + C * D, *UzT = KT + D * C,
                  *A = UzT + D * C;
         const float *gam = wsg + u * D;
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
-            const int T0 = (w * TPW + tt) * 16;
+            const int rt = w * TPW + tt;
 #pragma unroll
             for (int ks = 0; ks < KD; ++ks) {
-                ya[tt][ks] = M::load(Y + T0 * D + ks * M::KS, D);
-                qa[tt][ks] = M::load(Qt + T0 * D + ks * M::KS, D);
+                ya[tt][ks] = load_frag(Y, rt, ks, D);
+                qa[tt][ks] = load_frag(Qt, rt, ks, D);
             }
 #pragma unroll
-            for (int ks = 0; ks < KC; ++ks) aa[tt][ks] = M::load(A + T0 * C + ks * M::KS, C);
+            for (int ks = 0; ks < KC; ++ks) aa[tt][ks] = load_frag(A, rt, ks, C);
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) uz[tt][ct] = R4::load(UzT + (size_t)(col0 + 16 * ct + lr) * C + T0 + 4 * lq);
+            for (int ct = 0; ct < NCT; ++ct)
+                uz[tt][ct] = R4::load(UzT + ((size_t)(rt * (D / 16) + col0 / 16 + ct) * 64 + l) * 4);
         }
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
             const int ch0 = 32 * w + 16 * rt;
 #pragma unroll
-            for (int ks = 0; ks < KC; ++ks) ka[rt][ks] = M::load(KT + ch0 * C + ks * M::KS, C);
+            for (int ks = 0; ks < KC; ++ks) ka[rt][ks] = load_frag(KT, ch0 / 16, ks, C);
             g4[rt] = load4f(gam + ch0 + 4 * lq);
         }
     }
@@ -529,8 +581,11 @@ __device__ __forceinline__ void sweep_chunk(const SweepOps<IO, D, NCT> &op, f32x
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) {
         const int T0 = (w * TPW + tt) * 16;
+        // All K steps (A is zero above its diagonal tiles): a trip count that
+        // depends on the wave would put branches around the prefetch
+        // bookkeeping and force a full drain of the loads in flight.
 #pragma unroll
-        for (int ks = 0; ks < ((T0 + 16) + KS - 1) / KS; ++ks)  // A is lower triangular
+        for (int ks = 0; ks < KC; ++ks)
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) accR[tt][ct] = M::mma(accR[tt][ct], op.aa[tt][ks], ub[ks][ct]);
 #pragma unroll
@@ -674,7 +729,7 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t s) {
     constexpr int NVT = D / (16 * NCT);
     const int G = a.B * a.Hv * NVT;
     const int grid = (G + 7) / 8 * 8;
-    constexpr int PF = sizeof(IO) == 2 ? 3 : 1;  // prefetch depth (fp32 fragments are 2x larger)
+    constexpr int PF = sizeof(IO) == 2 ? SWEEP_PF : 1;  // prefetch depth (fp32 fragments are 2x larger)
     hipLaunchKernelGGL((chunk_sweep<IO, D, NCT, PF>), dim3(grid), dim3(2 * D), 0, s, a, NVT, G);
     return hipGetLastError();
 }
@@ -688,7 +743,7 @@ hipError_t launch_chunk(int io, int D, const ChunkArgs &a, hipStream_t s) {
     if (io == IO_BF16) {
         if (D == 32) return launch_chunk_t<bf16_t, 32, 1>(a, s);
         if (D == 64) return launch_chunk_t<bf16_t, 64, 2>(a, s);
-        if (D == 128) return launch_chunk_t<bf16_t, 128, 2>(a, s);
+        if (D == 128) return launch_chunk_t<bf16_t, 128, SWEEP_NCT128>(a, s);
     } else {
         if (D == 32) return launch_chunk_t<float, 32, 1>(a, s);
         if (D == 64) return launch_chunk_t<float, 64, 2>(a, s);
