@@ -8,6 +8,10 @@ gdr_decode_step calls). Inputs are seeded synthetic tensors already resident
 in device memory when timing starts. Timing uses HIP events recorded on the
 stream the kernels run on.
 
+--workload picks another prefill workload for the timed step (the KDA and
+Gated DeltaNet-2 layers, or the small fp32 case); --decode-steps 0 skips the
+decode measurement.
+
 Prints one JSON line: value = prefill tokens/s; "roofline" for the prefill
 call against HBM; "decode" with state GB/s and its own roofline; and
 "cpu_baseline", the fp64 CPU oracle timed on a bounded sample of the same
@@ -23,6 +27,36 @@ import time
 
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix, published
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "gated_delta_rule_23_amd", "csrc")
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash():
+    """sha256 over the kernel sources, to tell whether recorded memory
+    counters still describe the kernels as built."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".hpp")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(key):
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
+    (scaled by a plain copy of known size) for the kernels as they were when
+    the counters were taken; None once the kernel sources differ."""
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch", {}).get(key)
 
 
 def prefill_algorithmic(wl):
@@ -48,7 +82,7 @@ def decode_algorithmic(wl):
     return state, state + io
 
 
-def cpu_baseline(wl, inp, heads, min_seconds=10.0, max_reps=20):
+def cpu_baseline(wl, inp, heads, min_seconds=10.0, max_reps=200):
     """Time the fp64 oracle (as it stands) on the given V heads of the prefill
     workload, repeating the run until about min_seconds of CPU work."""
     import oracle
@@ -71,7 +105,10 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--decode-steps", type=int, default=256, help="consecutive decode steps timed (0 = skip decode)")
+    ap.add_argument("--workload", default="qwen_gdn_prefill",
+                    choices=["qwen_gdn_prefill", "kda_prefill", "gdn2_prefill", "gdn_small_f32"],
+                    help="prefill workload of the timed step (default: the Qwen-shaped GDN layer, T=4096)")
     ap.add_argument("--cpu-heads", type=int, default=48, help="V heads in the CPU-oracle sample (0 = skip)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -106,12 +143,16 @@ def main(argv=None):
         del src, dst
 
     # ---- prefill ----
-    wl = gs.QWEN_GDN_PREFILL
+    wl = {"qwen_gdn_prefill": gs.QWEN_GDN_PREFILL, "kda_prefill": gs.KDA_PREFILL, "gdn2_prefill": gs.GDN2_PREFILL,
+          "gdn_small_f32": gs.GDN_SMALL_F32}[args.workload]
     inp = gs.make_inputs(wl, seed=args.seed)
     d = {n: up(inp[n]) for n in ("q", "k", "v", "g", "beta", "b", "w")}
-    desc = gdr.make_desc(wl.B, wl.T, wl.Hqk, wl.Hv, wl.dk, gdr.GDR_BF16, gdr.GDR_DECAY_SCALAR, wl.scale)
+    io_t = torch.bfloat16 if wl.io == "bf16" else torch.float32
+    desc = gdr.make_desc(wl.B, wl.T, wl.Hqk, wl.Hv, wl.dk, gdr.GDR_BF16 if wl.io == "bf16" else gdr.GDR_F32,
+                         {"none": gdr.GDR_DECAY_NONE, "scalar": gdr.GDR_DECAY_SCALAR,
+                          "channel": gdr.GDR_DECAY_CHANNEL}[wl.decay], wl.scale)
     ws = torch.empty(gdr.gdr_chunk_workspace_bytes(desc), dtype=torch.uint8, device=dev)
-    o = torch.empty((wl.B, wl.T, wl.Hv, wl.dv), dtype=torch.bfloat16, device=dev)
+    o = torch.empty((wl.B, wl.T, wl.Hv, wl.dv), dtype=io_t, device=dev)
     ST = torch.empty((wl.B, wl.Hv, wl.dk, wl.dv), dtype=torch.float32, device=dev)
 
     def prefill():
@@ -140,35 +181,47 @@ def main(argv=None):
     achieved = pbytes / (avg_call_ms * 1e-3) / 1e9
 
     # ---- decode ----
-    dwl = gs.QWEN_GDN_DECODE.scaled(T=args.decode_steps)
-    dinp = gs.make_inputs(dwl, seed=args.seed + 1)
-    dd = {n: up(dinp[n]) for n in ("q", "k", "v", "g", "beta", "b", "w")}
-    S = up(dinp["S0"]).clone()
-    do = torch.empty((dwl.B, dwl.Hv, dwl.dv), dtype=torch.bfloat16, device=dev)
+    dec = None
+    if args.decode_steps > 0:
+        dwl = gs.QWEN_GDN_DECODE.scaled(T=args.decode_steps,
+                                        name=f"qwen_gdn_decode_B64_Hv48_d128_{args.decode_steps}steps")
+        dinp = gs.make_inputs(dwl, seed=args.seed + 1)
+        dd = {n: up(dinp[n]) for n in ("q", "k", "v", "g", "beta", "b", "w")}
+        S = up(dinp["S0"]).clone()
+        do = torch.empty((dwl.B, dwl.Hv, dwl.dv), dtype=torch.bfloat16, device=dev)
 
-    def dstep(s):
-        pick = lambda t: None if t is None else t[s]
-        gdr.gdr_decode_step(pick(dd["q"]), pick(dd["k"]), pick(dd["v"]), S, g=pick(dd["g"]), beta=pick(dd["beta"]),
-                            b=pick(dd["b"]), w=pick(dd["w"]), scale=dwl.scale, o=do, stream=stream)
+        def dstep(s):
+            pick = lambda t: None if t is None else t[s]
+            gdr.gdr_decode_step(pick(dd["q"]), pick(dd["k"]), pick(dd["v"]), S, g=pick(dd["g"]),
+                                beta=pick(dd["beta"]), b=pick(dd["b"]), w=pick(dd["w"]), scale=dwl.scale, o=do,
+                                stream=stream)
 
-    for s in range(min(8, dwl.T)):
-        dstep(s)
-    S.copy_(up(dinp["S0"]))
-    torch.cuda.synchronize()
-    dev_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(dwl.T)]
-    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    d0.record(stream)
-    for s in range(dwl.T):
-        dev_ev[s][0].record(stream)
-        dstep(s)
-        dev_ev[s][1].record(stream)
-    d1.record(stream)
-    torch.cuda.synchronize()
-    d_total_ms = d0.elapsed_time(d1)
-    d_step_ms = sorted(a.elapsed_time(b) for a, b in dev_ev)
-    d_avg_ms = sum(d_step_ms) / len(d_step_ms)
-    state_bytes, d_bytes = decode_algorithmic(dwl)
-    d_achieved = d_bytes / (d_avg_ms * 1e-3) / 1e9
+        for s in range(min(8, dwl.T)):
+            dstep(s)
+        S.copy_(up(dinp["S0"]))
+        torch.cuda.synchronize()
+        dev_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(dwl.T)]
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        d0.record(stream)
+        for s in range(dwl.T):
+            dev_ev[s][0].record(stream)
+            dstep(s)
+            dev_ev[s][1].record(stream)
+        d1.record(stream)
+        torch.cuda.synchronize()
+        d_total_ms = d0.elapsed_time(d1)
+        d_step_ms = sorted(a.elapsed_time(b) for a, b in dev_ev)
+        d_avg_ms = sum(d_step_ms) / len(d_step_ms)
+        state_bytes, d_bytes = decode_algorithmic(dwl)
+        d_achieved = d_bytes / (d_avg_ms * 1e-3) / 1e9
+        dec = {"workload": dwl.name, "steps": dwl.T, "ms_per_step": d_total_ms / dwl.T,
+               "kernel_avg_ms": d_avg_ms, "kernel_median_ms": d_step_ms[len(d_step_ms) // 2],
+               "state_GBps": state_bytes / (d_avg_ms * 1e-3) / 1e9,
+               "tokens_per_s": dwl.B / (d_total_ms / dwl.T * 1e-3),
+               "roofline": {"kernel": "decode_kernel", "bound": "hbm", "achieved": d_achieved,
+                            "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": d_achieved / HBM_PEAK_GBPS,
+                            "traffic": recorded_traffic(dwl.name) if dwl.T == 256 else None,
+                            "algorithmic_bytes": d_bytes}}
 
     out = {
         "metric": "prefill tokens/s and decode state GB/s for gated delta rule, % of roofline",
@@ -181,26 +234,20 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), beta=sigmoid(N(0,1)), "
-                "g=-0.1*softplus(N(0,1)))",
+        "dtype": wl.io,
+        "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), gates and decay per the workload recipe)",
         "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "H_qk": wl.Hqk, "H_v": wl.Hv, "d_k": wl.dk,
-                   "d_v": wl.dv, "chunk": wl.chunk, "io": wl.io, "state": "fp32", "S0": "zeros"},
+                   "d_v": wl.dv, "chunk": wl.chunk, "io": wl.io, "decay": wl.decay, "gates": wl.gates,
+                   "state": "fp32", "S0": "zeros"},
         "roofline": {"kernel": "gdr_chunk_fwd (chunk_prep + chunk_sweep)", "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": None, "algorithmic_bytes": pbytes, "avg_call_ms": avg_call_ms},
+                     "traffic": recorded_traffic(wl.name), "algorithmic_bytes": pbytes, "avg_call_ms": avg_call_ms},
         "mfma": {"algorithmic_tflops": pflops / (avg_call_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
                  "frac": pflops / (avg_call_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, "algorithmic_flops": pflops},
-        "decode": {"workload": dwl.name, "steps": dwl.T, "ms_per_step": d_total_ms / dwl.T,
-                   "kernel_avg_ms": d_avg_ms, "kernel_median_ms": d_step_ms[len(d_step_ms) // 2],
-                   "state_GBps": state_bytes / (d_avg_ms * 1e-3) / 1e9,
-                   "tokens_per_s": dwl.B / (d_total_ms / dwl.T * 1e-3),
-                   "roofline": {"kernel": "decode_kernel", "bound": "hbm", "achieved": d_achieved,
-                                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": d_achieved / HBM_PEAK_GBPS,
-                                "traffic": None, "algorithmic_bytes": d_bytes}},
+        "decode": dec,
     }
     if args.cpu_heads > 0:
-        heads = list(range(0, wl.Hv, max(1, wl.Hv // args.cpu_heads)))[:args.cpu_heads]
+        heads = list(range(0, wl.Hv, max(1, wl.Hv // min(args.cpu_heads, wl.Hv))))[:args.cpu_heads]
         out["cpu_baseline"] = cpu_baseline(wl, inp, heads)
     else:
         out["cpu_baseline"] = None

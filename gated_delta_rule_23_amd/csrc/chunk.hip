@@ -14,18 +14,19 @@
 //   L = (I + T)^-1                 (unit lower triangular; no dense solve)
 //   Y = L E~        U_z = L Z      (erase side / write side of the WY form)
 //   U = U_z - Y S_c                (the resolved errors)
-//   O = s (Q~ S_c + A U) = (s (Q~ - A Y)) S_c + s A U_z
+//   O = s (Q~ S_c + A U)
 //   S_{c+1} = Diag(gamma) S_c + Kend^T U
 //
 // Two kernels. chunk_prep is parallel over every (sequence, V head, chunk):
 // it does everything that does not depend on the state -- prefix sums, decay
-// absorption, both Gram products, the triangular inverse, and the products
-// Y, U_z, W_q = s (Q~ - A Y), O_z = s A U_z -- and stores them in a
-// workspace. chunk_sweep is the single sequential pass over chunks: per
-// (sequence, V head, value tile) it keeps the fp32 state in matrix-core
-// accumulator registers and per chunk does U = U_z - Y S_c,
-// O = W_q S_c + O_z and S_{c+1} = gamma . S_c + Kend^T U. Value columns of the
-// state evolve independently, so the sweep is split over value tiles.
+// absorption, both Gram products, the triangular solve for Y and U_z -- and
+// stores Y, Q~, Kend^T, U_z^T, A and gamma in a workspace, each matrix in
+// the order the sweep's matrix-core operand loads read it. chunk_sweep is the
+// single sequential pass over chunks: per (sequence, V head, value tile) it
+// keeps the fp32 state in matrix-core accumulator registers and per chunk
+// does U = U_z - Y S_c, O = s (Q~ S_c + A U) and
+// S_{c+1} = gamma . S_c + Kend^T U. Value columns of the state evolve
+// independently, so the sweep is split over value tiles.
 //
 // Matrix products run on gfx950 MFMA: bf16 operands with fp32 accumulation
 // for bfloat16 io, fp32 operands for float32 io. The triangular inverse is
