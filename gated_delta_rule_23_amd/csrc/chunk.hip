@@ -49,32 +49,23 @@ constexpr int C = kChunk;
 __host__ __device__ constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 __host__ __device__ constexpr size_t a16(size_t x) { return (x + 15) & ~(size_t)15; }
 
-// Copy a rows x cols block between row strides, 16 bytes per access.
-template <typename T>
-__device__ __forceinline__ void copy_block(T *dst, int dld, const T *src, int sld, int rows, int cols, int tid, int nt) {
-    constexpr int V = 16 / sizeof(T);
-    const int per_row = cols / V;
-    for (int i = tid; i < rows * per_row; i += nt) {
-        const int r = i / per_row, c = (i - r * per_row) * V;
-        *reinterpret_cast<uint4 *>(dst + (size_t)r * dld + c) = *reinterpret_cast<const uint4 *>(src + (size_t)r * sld + c);
-    }
-}
-
 // Workspace matrices are stored in "fragment order": the data one wave's
 // matrix-core operand load needs is contiguous. For a row-major R x K matrix
 // read as A (or B^T) operand fragments, the fragment (row tile rt, K step ks)
 // is one block of 64 lanes x FE elements (FE = KS / 4: 8 for bf16, 1 for
 // fp32), lane l holding row 16 rt + l % 16, columns KS ks + FE (l / 16) ...
 template <typename IO>
-__device__ __forceinline__ size_t frag_off(int r, int c, int K) {
+__device__ __forceinline__ size_t frag_slot(int rt, int ks, int K) {
     constexpr int KS = Mma<IO>::KS, FE = KS / 4;
-    const int lane = (r & 15) + 16 * ((c % KS) / FE);
-    return ((size_t)((r >> 4) * (K / KS) + c / KS) * 64 + lane) * FE + c % FE;
+    return ((size_t)(rt * (K / KS) + ks) * 64 + (threadIdx.x & 63)) * FE;
 }
 template <typename IO>
 __device__ __forceinline__ typename Mma<IO>::Frag load_frag(const IO *M, int rt, int ks, int K) {
-    constexpr int KS = Mma<IO>::KS, FE = KS / 4;
-    return *reinterpret_cast<const typename Mma<IO>::Frag *>(M + ((size_t)(rt * (K / KS) + ks) * 64 + (threadIdx.x & 63)) * FE);
+    return *reinterpret_cast<const typename Mma<IO>::Frag *>(M + frag_slot<IO>(rt, ks, K));
+}
+template <typename IO>
+__device__ __forceinline__ void store_frag(IO *M, int rt, int ks, int K, typename Mma<IO>::Frag f) {
+    *reinterpret_cast<typename Mma<IO>::Frag *>(M + frag_slot<IO>(rt, ks, K)) = f;
 }
 // ... and a token-contiguous D x C matrix read in accumulator layout (lane
 // l = col % 16 + 16 (tok % 16) / 4 holds 4 consecutive tokens of one column)
@@ -83,41 +74,6 @@ template <int D>
 __device__ __forceinline__ size_t cfrag_off(int col, int tok) {
     const int lane = (col & 15) + 16 * ((tok & 15) >> 2);
     return ((size_t)((tok >> 4) * (D / 16) + (col >> 4)) * 64 + lane) * 4 + (tok & 3);
-}
-
-// Store a row-major R x K matrix from shared memory in fragment order,
-// optionally scaling row r by rowscale[r].
-template <typename IO>
-__device__ __forceinline__ void store_frag_rows(IO *dst, int R, int K, const IO *src, int sld, const float *rowscale,
-                                                int tid, int nt) {
-    constexpr int V = 16 / sizeof(IO);
-    const int per = K / V;
-    for (int i = tid; i < R * per; i += nt) {
-        const int r = i / per, c0 = (i - r * per) * V;
-        IO vals[V];
-        *reinterpret_cast<uint4 *>(vals) = *reinterpret_cast<const uint4 *>(src + r * sld + c0);
-        if (rowscale) {
-            const float sc = rowscale[r];
-#pragma unroll
-            for (int j = 0; j < V; ++j) vals[j] = Elem<IO>::to(Elem<IO>::from(vals[j]) * sc);
-        }
-        if constexpr (sizeof(IO) == 2) {  // V == FE: one fragment slot
-            *reinterpret_cast<uint4 *>(dst + frag_off<IO>(r, c0, K)) = *reinterpret_cast<const uint4 *>(vals);
-        } else {
-#pragma unroll
-            for (int j = 0; j < V; ++j) dst[frag_off<IO>(r, c0 + j, K)] = vals[j];
-        }
-    }
-}
-
-// Store a token-contiguous D x C matrix (row stride sld) in accumulator fragment order.
-template <typename IO, int D>
-__device__ __forceinline__ void store_cfrag(IO *dst, const IO *src, int sld, int tid, int nt) {
-    for (int i = tid; i < D * (C / 4); i += nt) {
-        const int col = i / (C / 4), t4 = (i - col * (C / 4)) * 4;
-        *reinterpret_cast<typename Raw4<IO>::type *>(dst + cfrag_off<D>(col, t4)) =
-            *reinterpret_cast<const typename Raw4<IO>::type *>(src + col * sld + t4);
-    }
 }
 
 // The 10 lower-triangular 16 x 16 tiles of a 64 x 64 matrix.
@@ -129,67 +85,188 @@ __device__ __forceinline__ void lower_tile(int idx, int &ti, int &tj) {
 // exp(x) = 2^(x log2 e) on the hardware exp2 (v_exp_f32, ~1 ulp).
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
-template <typename IO, int D>
-struct PrepCfg {
-    static constexpr int NW = D / 16 < 4 ? D / 16 : 4;  // waves per workgroup
-    static constexpr int NT = 64 * NW;
-    static constexpr int CQ = D / 4;              // channel quads
-    static constexpr int NGRP = NT / CQ;          // token groups
-    static constexpr int TPT = C / NGRP;          // tokens per thread in the elementwise phase
-    static constexpr int NCTS = 2 * D / NW / 16;  // 16-wide right-hand-side column tiles per wave
-    static constexpr int WC = 16 * NCTS;          // right-hand-side columns per wave
-    static constexpr int PD = D + 8;              // row stride of [C x D] row-major tiles
-    static constexpr int PT = C + 8;              // row stride of token-contiguous tiles
-    static constexpr int PDB = sizeof(IO) == 2 ? 24 : 20;   // D_b rows (16 + pad)
-    static constexpr int PTMP = sizeof(IO) == 2 ? 24 : 20;  // solve temporaries (16 tokens + pad)
-    static constexpr size_t SLOT = a16(cmax((size_t)C * PD, (size_t)D * PT) * sizeof(IO));
-    static constexpr size_t SLOT_E = a16(cmax(SLOT, (size_t)NW * WC * PTMP * sizeof(IO)));
-    static constexpr size_t XT = a16((size_t)2 * D * PT * sizeof(IO));
-    static constexpr size_t TA = a16((size_t)2 * C * PT * sizeof(IO));
-    static constexpr size_t TD = a16((size_t)4 * 16 * 17 * 4);
-    static constexpr size_t DB = a16((size_t)4 * 16 * PDB * sizeof(IO));
-    static constexpr size_t PART = a16((size_t)NGRP * D * 4);
-    static constexpr size_t GT = a16((size_t)4 * C * 4);  // per-token G, exp(G), exp(G_end - G), beta
-    static constexpr size_t OFF_K = SLOT_E, OFF_Q = OFF_K + SLOT, OFF_XT = OFF_Q + SLOT, OFF_TA = OFF_XT + XT,
-                            OFF_TD = OFF_TA + TA, OFF_DB = OFF_TD + TD, OFF_PART = OFF_DB + DB,
-                            OFF_GT = OFF_PART + PART, BYTES = OFF_GT + GT;
-    static_assert(TA >= (size_t)D * PT * sizeof(IO), "Kend^T staging");
-    static_assert(NGRP * TPT == C && TPT % 4 == 0, "elementwise mapping");
-    static_assert(BYTES <= 160 * 1024, "LDS budget");
+// Orders this wave's shared-memory accesses around a point where lanes read
+// what other lanes of the same wave wrote (a wave executes its LDS accesses
+// in order; this keeps the compiler from moving them).
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ---------------------------------------------------------------------------
+// Operands from shared memory in either orientation. Mma<IO>::load reads a
+// fragment from storage where the operand's K index is contiguous. Km<IO>
+// reads the same fragment from "K-major" storage, where element (row r, k)
+// sits at M[k * ld + r]. For bfloat16 that is the gfx950 LDS transpose read
+// ds_read_b64_tr_b16, whose lane layout (checked on the device) is: inside
+// each group of 16 lanes, lane s supplies the address of 4 consecutive 16-bit
+// elements, and lane j receives element j % 4 of the words supplied by lanes
+// j / 4, 4 + j / 4, 8 + j / 4 and 12 + j / 4, in that order. Lane s pointing
+// at rows 4 (s % 4) .. 4 (s % 4) + 3 of K-row k0 + s / 4 therefore hands lane
+// j row j of K-rows k0 .. k0 + 3.
+__device__ __forceinline__ s16x4 ds_tr16(const bf16_t *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
+}
+
+template <typename IO> struct Km;
+template <> struct Km<bf16_t> {
+    // 16 x 32 fragment (the operand of v_mfma_f32_16x16x32_bf16).
+    __device__ __forceinline__ static u16x8 frag(const bf16_t *M, int ld) {
+        const int l = lane_id(), s = l & 15, g = l >> 4;
+        const bf16_t *p = M + (8 * g + (s >> 2)) * ld + 4 * (s & 3);
+        const s16x4 lo = ds_tr16(p), hi = ds_tr16(p + 4 * ld);
+        return __builtin_bit_cast(u16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+    // acc += A * Bt^T for 16 x 16 blocks: A K-major at A, Bt with K contiguous.
+    __device__ __forceinline__ static f32x4 mma16(f32x4 acc, const bf16_t *A, int lda, const bf16_t *Bt, int ldb) {
+        const int l = lane_id(), s = l & 15, g = l >> 4;
+        const s16x4 av = ds_tr16(A + (4 * g + (s >> 2)) * lda + 4 * (s & 3));
+        const s16x4 bv = *reinterpret_cast<const s16x4 *>(Bt + s * ldb + 4 * g);
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, acc, 0, 0, 0);
+    }
+    // Multiply the 8 elements of a fragment (8 consecutive K indices) by f[0..7].
+    __device__ __forceinline__ static u16x8 scale(u16x8 x, const float *f) {
+        const f32x4 f0 = load4f(f), f1 = load4f(f + 4);
+        typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+        const u32x4 r = {f2bf2(bf2f(x[0]) * f0[0], bf2f(x[1]) * f0[1]), f2bf2(bf2f(x[2]) * f0[2], bf2f(x[3]) * f0[3]),
+                         f2bf2(bf2f(x[4]) * f1[0], bf2f(x[5]) * f1[1]), f2bf2(bf2f(x[6]) * f1[2], bf2f(x[7]) * f1[3])};
+        return __builtin_bit_cast(u16x8, r);
+    }
+    __device__ __forceinline__ static u16x8 scale(u16x8 x, float f) {
+        typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+        const u32x4 r = {f2bf2(bf2f(x[0]) * f, bf2f(x[1]) * f), f2bf2(bf2f(x[2]) * f, bf2f(x[3]) * f),
+                         f2bf2(bf2f(x[4]) * f, bf2f(x[5]) * f), f2bf2(bf2f(x[6]) * f, bf2f(x[7]) * f)};
+        return __builtin_bit_cast(u16x8, r);
+    }
+};
+template <> struct Km<float> {
+    __device__ __forceinline__ static float frag(const float *M, int ld) {
+        const int l = lane_id();
+        return M[(l >> 4) * ld + (l & 15)];
+    }
+    __device__ __forceinline__ static f32x4 mma16(f32x4 acc, const float *A, int lda, const float *Bt, int ldb) {
+        const int l = lane_id(), s = l & 15, g = l >> 4;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[(4 * ks + g) * lda + s], Bt[s * ldb + 4 * ks + g], acc, 0, 0, 0);
+        return acc;
+    }
+    __device__ __forceinline__ static float scale(float x, const float *f) { return x * f[0]; }
+    __device__ __forceinline__ static float scale(float x, float f) { return x * f; }
 };
 
-// One thread's raw inputs for a chunk: TPT tokens x 4 channels of q, k, v
-// (and b, w, per-channel g); lane l of every wave also holds token l's beta
-// and scalar g. Kept raw so that the loads for the next chunk are issued
-// early and waited for only when used.
+// 16 bytes of stored elements (8 bf16 or 4 fp32) kept raw in registers, so a
+// prefetch does not wait for its data; widened to float at use.
+template <typename IO> struct Raw16;
+template <> struct Raw16<bf16_t> {
+    static constexpr int N = 8;
+    __device__ __forceinline__ static void widen(uint4 r, float *f) {
+        const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = __uint_as_float(w[i] << 16);
+            f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+    __device__ __forceinline__ static uint4 pack(const float *f) {
+        return uint4{f2bf2(f[0], f[1]), f2bf2(f[2], f[3]), f2bf2(f[4], f[5]), f2bf2(f[6], f[7])};
+    }
+};
+template <> struct Raw16<float> {
+    static constexpr int N = 4;
+    __device__ __forceinline__ static void widen(uint4 r, float *f) {
+        f[0] = __uint_as_float(r.x); f[1] = __uint_as_float(r.y); f[2] = __uint_as_float(r.z); f[3] = __uint_as_float(r.w);
+    }
+    __device__ __forceinline__ static uint4 pack(const float *f) {
+        return uint4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3])};
+    }
+};
+__device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+// ---------------------------------------------------------------------------
+// chunk_prep: everything in a chunk that does not depend on the state, for
+// every (sequence, V head, chunk) unit; persistent over units, with the next
+// unit's inputs prefetched into registers while the current one is processed.
+//
+// Shared memory holds the chunk's token-major tiles (row t = token, 16-byte
+// channel groups): q, k and z = gated v; for decoupled gates or per-channel
+// decay also the erase key; for per-channel decay the tiles already carry the
+// decay (Q~, K~, E~) and Kend has its own tile. With a scalar decay the tiles
+// stay undecayed and the decay is applied where they are read: to Gram
+// entries as exp(G_i - G_j) (no factor can overflow), and per token to the
+// E~ and Kend operands.
+//  A. prefix sums of g, token tables, the tiles; gamma.
+//  B. Gram products T = E~ K~^T, A = Q~ K~^T on the matrix cores (20 lower
+//     16 x 16 tiles); T and A kept column-major; Q~ and Kend^T go to the
+//     workspace straight from the tiles.
+//  C. A to the workspace; L = (I + T)^-1: the 16 x 16 diagonal blocks by fp32
+//     substitution, then column block j by block forward substitution,
+//     X_i = -D_i sum_{j <= k < i} T_ik X_k, one wave per column block.
+//  D. [Y | U_z] = L [E~ | Z] on the matrix cores, each wave a slice of the
+//     2 d columns; U_z^T goes to the workspace from the accumulators, Y
+//     through a column-major staging tile.
+//  E. Y to the workspace.
+template <typename IO, int D>
+struct PrepCfg {
+    static constexpr int NW = 4, NT = 64 * NW;
+    static constexpr int V = 16 / sizeof(IO);  // elements per 16-byte access
+    static constexpr int CO = D / V;           // 16-byte channel groups per token row
+    static constexpr int NGRP = NT / CO;       // token groups in phase A
+    static constexpr int TPT = C / NGRP;       // tokens per thread in phase A
+    static constexpr int KS = Mma<IO>::KS;
+    static constexpr int PD = D + V;           // token-major tile row stride
+    static constexpr int LC = C + V;           // column-major 64 x 64 stride (T, A, L)
+    static constexpr int LY = C + V;           // column-major Y staging stride
+    static constexpr int LT = 16 + V;          // per-wave 16 x 16 temporary stride
+    static constexpr int WC = 2 * D / NW;      // columns of [E~ | Z] per wave in phase D
+    static constexpr int NCTS = WC / 16;
+    static constexpr size_t TILE = a16((size_t)C * PD * sizeof(IO));
+    static constexpr size_t R1 = a16(cmax((size_t)C * PD, (size_t)D * LY) * sizeof(IO));
+    static constexpr size_t MAT = a16((size_t)C * LC * sizeof(IO));
+    static constexpr size_t TMP = a16((size_t)NW * 16 * LT * sizeof(IO));
+    static constexpr size_t TD = a16((size_t)4 * 16 * 17 * 4);
+    static constexpr size_t TAB = a16((size_t)5 * C * 4);
+    static constexpr size_t PART = a16((size_t)NGRP * D * 4);
+    static_assert(NT % CO == 0 && NGRP * TPT == C && WC % 16 == 0, "phase mappings");
+    static constexpr size_t bytes(bool has_e, bool chan) {
+        return R1 + TILE * (2 + (has_e ? 1 : 0) + (chan ? 1 : 0)) + 2 * MAT + TMP + TD + TAB + (chan ? PART : 0);
+    }
+};
+
+// One thread's raw inputs for a chunk: TPT tokens x one 16-byte channel group
+// of q, k, v (and b, w, per-channel g); lane l of wave 0 also holds token l's
+// beta and scalar g.
 template <typename IO, int D, bool CHAN, bool BW>
 struct PrepIn {
-    using R4 = Raw4<IO>;
-    static constexpr int TPT = PrepCfg<IO, D>::TPT;
-    typename R4::type q[TPT], k[TPT], v[TPT], bg[BW ? TPT : 1], wg[BW ? TPT : 1];
-    f32x4 g[CHAN ? TPT : 1];
+    using Cfg = PrepCfg<IO, D>;
+    static constexpr int TPT = Cfg::TPT, V = Cfg::V;
+    uint4 q[TPT], k[TPT], v[TPT], bg[BW ? TPT : 1], wg[BW ? TPT : 1];
+    f32x4 g[CHAN ? TPT * V / 4 : 1];
     float betal, gs;
 
-    __device__ __forceinline__ void load(const ChunkArgs &a, int u, int cq, int grp) {
+    __device__ __forceinline__ void load(const ChunkArgs &a, int u, int co, int grp) {
         const int NC = a.NC, c = u % NC, bh = u / NC, b = bh / a.Hv, h = bh - b * a.Hv;
         const int hq = h / (a.Hv / a.Hqk), t0 = c * C, n = min(C, a.T - t0);
         const int l = threadIdx.x & 63;
         const size_t row0 = (size_t)b * a.T + t0;  // first token row of the chunk
-        const IO *qb = static_cast<const IO *>(a.q) + (row0 * a.Hqk + hq) * D + 4 * cq;
-        const IO *kb = static_cast<const IO *>(a.k) + (row0 * a.Hqk + hq) * D + 4 * cq;
-        const size_t vo = (row0 * a.Hv + h) * D + 4 * cq;
-        const int sqk = a.Hqk * D, sv = a.Hv * D;  // token strides (elements)
+        const IO *qb = static_cast<const IO *>(a.q) + (row0 * a.Hqk + hq) * D + V * co;
+        const IO *kb = static_cast<const IO *>(a.k) + (row0 * a.Hqk + hq) * D + V * co;
+        const size_t vo = (row0 * a.Hv + h) * D + V * co;
+        const size_t sqk = (size_t)a.Hqk * D, sv = (size_t)a.Hv * D;  // token strides (elements)
 #pragma unroll
         for (int j = 0; j < TPT; ++j) {
             const int t = min(TPT * grp + j, n - 1);  // clamped: padded tokens are zeroed at use
-            q[j] = R4::load(qb + t * sqk);
-            k[j] = R4::load(kb + t * sqk);
-            v[j] = R4::load(static_cast<const IO *>(a.v) + vo + t * sv);
+            q[j] = ld16(qb + t * sqk);
+            k[j] = ld16(kb + t * sqk);
+            v[j] = ld16(static_cast<const IO *>(a.v) + vo + t * sv);
             if constexpr (BW) {
-                bg[j] = R4::load(static_cast<const IO *>(a.bg) + vo + t * sv);
-                wg[j] = R4::load(static_cast<const IO *>(a.wg) + vo + t * sv);
+                bg[j] = ld16(static_cast<const IO *>(a.bg) + vo + t * sv);
+                wg[j] = ld16(static_cast<const IO *>(a.wg) + vo + t * sv);
             }
-            if constexpr (CHAN) g[j] = *reinterpret_cast<const f32x4 *>(a.g + vo + t * sv);
+            if constexpr (CHAN)
+#pragma unroll
+                for (int i = 0; i < V / 4; ++i) g[j * (V / 4) + i] = load4f(a.g + vo + t * sv + 4 * i);
         }
         if (threadIdx.x < 64) {  // wave 0: one token per lane
             const size_t tl = (row0 + min(l, n - 1)) * a.Hv + h;
@@ -199,284 +276,305 @@ struct PrepIn {
     }
 };
 
-// Everything in a chunk that does not depend on the state, for every
-// (sequence, V head, chunk) unit; persistent over units, with the next unit's
-// inputs prefetched while the current one is processed. Per unit:
-//  A. decay prefix sums and decay absorption; E~ (row-major, and token-
-//     contiguous as the right-hand side), K~, Q~, Z; Kend^T; gamma.
-//  B. Gram products T = E~ K~^T and A = Q~ K~^T on the matrix cores (lower tiles).
-//     Scalar decay (and none) uses the raw Gram with exp(G_i - G_j) applied per
-//     entry, so no factor can overflow; per-channel decay uses the factored form.
-//  C. (I + T) X = [E~ | Z] by blocked forward substitution over four 16-token
-//     blocks: the 16 x 16 diagonal blocks are inverted in fp32, the rest are
-//     matrix-core products; each wave solves its own WC right-hand-side columns.
-// Workspace per unit, in fragment order: Y, Q~ (C x D), Kend^T (D x C), A
-// (C x C) as matrix-core operands, U_z^T in accumulator layout; gamma. Threads of the elementwise phase run token-fast
-// (grp = tid % NGRP) so the token-contiguous stores of neighbouring lanes are
-// adjacent in LDS.
 template <typename IO, int D, bool CHAN, bool BW>
-__global__ __launch_bounds__(D >= 64 ? 256 : 128) void chunk_prep(ChunkArgs a) {  // = PrepCfg<IO, D>::NT
-    using E = Elem<IO>;
+__global__ __launch_bounds__(256) void chunk_prep(ChunkArgs a) {
     using M = Mma<IO>;
-    using R4 = Raw4<IO>;
+    using K = Km<IO>;
+    using R = Raw16<IO>;
+    using Frag = typename M::Frag;
     using Cfg = PrepCfg<IO, D>;
-    constexpr int NW = Cfg::NW, NT = Cfg::NT, PD = Cfg::PD, PT = Cfg::PT;
-    constexpr int NGRP = Cfg::NGRP, TPT = Cfg::TPT, NCTS = Cfg::NCTS, WC = Cfg::WC;
-    constexpr int PDB = Cfg::PDB, PTMP = Cfg::PTMP, KS = M::KS;
-    constexpr int NG = (20 + NW - 1) / NW;  // Gram tile products per wave
-    static_assert(NT == (D >= 64 ? 256 : 128), "launch bounds");
+    constexpr int NW = Cfg::NW, NT = Cfg::NT, V = Cfg::V, CO = Cfg::CO, NGRP = Cfg::NGRP, TPT = Cfg::TPT;
+    constexpr int KS = M::KS, FE = KS / 4, PD = Cfg::PD, LC = Cfg::LC, LY = Cfg::LY, LT = Cfg::LT;
+    constexpr int WC = Cfg::WC, NCTS = Cfg::NCTS;
+    constexpr bool HAS_E = CHAN || BW;
+    static_assert(NT == 256, "launch bounds");
 
     extern __shared__ __align__(16) unsigned char smem[];
-    IO *sE = reinterpret_cast<IO *>(smem);                    // E~ (or raw e) [C][PD] -> solve temporaries
-    IO *sK = reinterpret_cast<IO *>(smem + Cfg::OFF_K);       // K~ (or raw k) [C][PD] -> Y staging [C][PD]
-    IO *sQ = reinterpret_cast<IO *>(smem + Cfg::OFF_Q);       // Q~ (or raw q) [C][PD]
-    IO *sXT = reinterpret_cast<IO *>(smem + Cfg::OFF_XT);     // [E~ | Z]^T [2D][PT] -> [Y | U_z]^T in place
-    IO *sTo = reinterpret_cast<IO *>(smem + Cfg::OFF_TA);     // -T without its diagonal blocks [C][PT]
-    IO *sA = sTo + C * PT;                                     // A [C][PT]
-    IO *sKT = sTo;                                             // Kend^T staging [D][PT] (phase A only)
-    float *sTd = reinterpret_cast<float *>(smem + Cfg::OFF_TD);      // T diagonal blocks, column-major [4][16][17]
-    IO *sDb = reinterpret_cast<IO *>(smem + Cfg::OFF_DB);            // their inverses [4][16][PDB]
-    float *sPart = reinterpret_cast<float *>(smem + Cfg::OFF_PART);  // [NGRP][D] per-group channel sums
-    float *sG = reinterpret_cast<float *>(smem + Cfg::OFF_GT);       // per token: G,
-    float *sEG = sG + C;                                             //   exp(G),
-    float *sER = sG + 2 * C;                                         //   exp(G_end - G),
-    float *sBt = sG + 3 * C;                                         //   beta
-    IO *sYs = sK;
+    unsigned char *sp = smem;
+    IO *tQ = reinterpret_cast<IO *>(sp);  sp += Cfg::R1;    // q (Q~), token-major; later Y staging [D][LY]
+    IO *tK = reinterpret_cast<IO *>(sp);  sp += Cfg::TILE;  // k (K~)
+    IO *tZ = reinterpret_cast<IO *>(sp);  sp += Cfg::TILE;  // z
+    IO *tE = reinterpret_cast<IO *>(sp);  sp += HAS_E ? Cfg::TILE : 0;  // erase key (E~)
+    IO *tKe = reinterpret_cast<IO *>(sp); sp += CHAN ? Cfg::TILE : 0;   // Kend (per-channel decay)
+    IO *sTc = reinterpret_cast<IO *>(sp); sp += Cfg::MAT;   // T(i, j) at sTc[j * LC + i], blocks below the diagonal
+    IO *sAc = reinterpret_cast<IO *>(sp); sp += Cfg::MAT;   // A, same layout; then L
+    IO *sLc = sAc;
+    IO *sTmp = reinterpret_cast<IO *>(sp); sp += Cfg::TMP;  // per-wave 16 x 16 temporaries
+    float *sTd = reinterpret_cast<float *>(sp); sp += Cfg::TD;  // T's diagonal blocks, fp32, [blk][col][17]
+    float *sG = reinterpret_cast<float *>(sp); sp += Cfg::TAB;  // per token: G,
+    float *sEG = sG + C;                                          //   exp(G),
+    float *sER = sG + 2 * C;                                      //   exp(G_end - G),
+    float *sBt = sG + 3 * C;                                      //   beta,
+    float *sSE = sG + 4 * C;                                      //   the E~ factor of a raw erase-key tile
+    float *sPart = reinterpret_cast<float *>(sp);                 // [NGRP][D] per-group channel sums
+    IO *sYc = tQ;                                                 // Y(t, c) at sYc[c * LY + t]
 
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lq = l >> 4;
-    const int grp = tid % NGRP, cq = tid / NGRP;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
+    const int co = tid % CO, grp = tid / CO;
     const int units = a.B * a.Hv * a.NC;
-    IO *tmp = sE + w * WC * PTMP;
 
     PrepIn<IO, D, CHAN, BW> in;
-    if ((int)blockIdx.x < units) in.load(a, blockIdx.x, cq, grp);
+    if ((int)blockIdx.x < units) in.load(a, blockIdx.x, co, grp);
 
     for (int u = blockIdx.x; u < units; u += gridDim.x) {
         const int NC = a.NC, c = u % NC;
         const int n = min(C, a.T - c * C);
         IO *ws = static_cast<IO *>(a.ws_io) + (size_t)u * chunk_ws_io_elems(D);
         IO *wY = ws, *wQ = ws + C * D, *wKT = ws + 2 * C * D, *wUzT = ws + 3 * C * D, *wA = ws + 4 * C * D;
-        __syncthreads();  // the previous unit's readers of shared memory are done
+        __syncthreads();  // the previous unit is done with shared memory
 
-        // ---- A. prefix sums and decay absorption ----
-        float G[TPT][4];
+        // ---- A. prefix sums, token tables, tiles ----
+        float G[CHAN ? TPT : 1][V];
         if constexpr (CHAN) {
 #pragma unroll
             for (int j = 0; j < TPT; ++j)
 #pragma unroll
-                for (int ch = 0; ch < 4; ++ch)
-                    G[j][ch] = (TPT * grp + j < n ? in.g[j][ch] : 0.f) + (j > 0 ? G[j - 1][ch] : 0.f);
-            store4f(sPart + grp * D + 4 * cq, f32x4{G[TPT - 1][0], G[TPT - 1][1], G[TPT - 1][2], G[TPT - 1][3]});
-        } else if (w == 0) {
-            // Scalar decay: wave 0 scans the 64 token values (lane = token) into tables.
-            float Gl = l < n ? in.gs : 0.f;
+                for (int ch = 0; ch < V; ++ch)
+                    G[j][ch] = (TPT * grp + j < n ? in.g[j * (V / 4) + ch / 4][ch % 4] : 0.f) + (j > 0 ? G[j - 1][ch] : 0.f);
 #pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(Gl, off);
-                if (l >= off) Gl += y;
-            }
-            sG[l] = Gl;
-            sEG[l] = fast_exp(Gl);
-            sER[l] = fast_exp(__shfl(Gl, 63) - Gl);
+            for (int i = 0; i < V / 4; ++i)
+                store4f(sPart + grp * D + V * co + 4 * i,
+                        f32x4{G[TPT - 1][4 * i], G[TPT - 1][4 * i + 1], G[TPT - 1][4 * i + 2], G[TPT - 1][4 * i + 3]});
         }
-        if constexpr (!BW)
-            if (w == 0) sBt[l] = in.betal;
-        __syncthreads();
-        float Gend[4], eGend[4];
-        if constexpr (CHAN) {
-            f32x4 off = zero4(), tot = zero4();
+        if (w == 0) {
+            float eg = 1.f;
+            if constexpr (!CHAN) {
+                // Scalar decay: lane = token; inclusive scan of g over the chunk.
+                float Gl = l < n ? in.gs : 0.f;
 #pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const float y = __shfl_up(Gl, off);
+                    if (l >= off) Gl += y;
+                }
+                eg = fast_exp(Gl);
+                sG[l] = Gl;
+                sEG[l] = eg;
+                sER[l] = fast_exp(__shfl(Gl, 63) - Gl);
+            }
+            if constexpr (!BW) sBt[l] = in.betal;
+            sSE[l] = BW ? eg : in.betal * eg;
+        }
+        __syncthreads();
+        float eGend[V];
+        if constexpr (CHAN) {
+            float off[V], tot[V];
+#pragma unroll
+            for (int ch = 0; ch < V; ++ch) off[ch] = tot[ch] = 0.f;
             for (int g2 = 0; g2 < NGRP; ++g2) {
-                const f32x4 p = load4f(sPart + g2 * D + 4 * cq);
-                if (g2 < grp) off += p;
-                tot += p;
+#pragma unroll
+                for (int i = 0; i < V / 4; ++i) {
+                    const f32x4 p = load4f(sPart + g2 * D + V * co + 4 * i);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        if (g2 < grp) off[4 * i + r] += p[r];
+                        tot[4 * i + r] += p[r];
+                    }
+                }
             }
 #pragma unroll
-            for (int j = 0; j < TPT; ++j)
-#pragma unroll
-                for (int ch = 0; ch < 4; ++ch) G[j][ch] += off[ch];
-#pragma unroll
-            for (int ch = 0; ch < 4; ++ch) {
-                Gend[ch] = tot[ch];
+            for (int ch = 0; ch < V; ++ch) {
                 eGend[ch] = fast_exp(tot[ch]);
+#pragma unroll
+                for (int j = 0; j < TPT; ++j) G[j][ch] += off[ch];
             }
         } else {
             const float e = sEG[C - 1];
 #pragma unroll
-            for (int ch = 0; ch < 4; ++ch) eGend[ch] = e;
+            for (int ch = 0; ch < V; ++ch) eGend[ch] = e;
         }
-
 #pragma unroll
-        for (int h4 = 0; h4 < TPT / 4; ++h4) {  // 4 tokens at a time
-            const int t4 = TPT * grp + 4 * h4;
-            f32x4 egt4 = zero4(), ert4 = zero4(), bt4 = zero4();
-            if constexpr (!CHAN) { egt4 = load4f(sEG + t4); ert4 = load4f(sER + t4); }
-            if constexpr (!BW) bt4 = load4f(sBt + t4);
-            float xE[4][4], xZ[4][4], xKe[4][4];
+        for (int j = 0; j < TPT; ++j) {
+            const int t = TPT * grp + j;
+            const bool valid = t < n;
+            float qq[V], kk[V], vv[V], eb[V], wz[V];
+            R::widen(in.q[j], qq);
+            R::widen(in.k[j], kk);
+            R::widen(in.v[j], vv);
+            if constexpr (BW) {
+                R::widen(in.bg[j], eb);
+                R::widen(in.wg[j], wz);
+            } else {
+                const float bt = sBt[t];
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int j = 4 * h4 + jj, tk = t4 + jj;
-                const bool valid = tk < n;
-                const f32x4 kk = R4::widen(in.k[j]), qq = R4::widen(in.q[j]), vv = R4::widen(in.v[j]);
-                f32x4 eb, wz;
-                if constexpr (BW) {
-                    eb = R4::widen(in.bg[j]);
-                    wz = R4::widen(in.wg[j]);
+                for (int ch = 0; ch < V; ++ch) eb[ch] = wz[ch] = bt;
+            }
+            float oq[V], ok[V], oz[V], oe[V], oke[V];
+#pragma unroll
+            for (int ch = 0; ch < V; ++ch) {
+                const float kv = valid ? kk[ch] : 0.f, qv = valid ? qq[ch] : 0.f;
+                oz[ch] = valid ? wz[ch] * vv[ch] : 0.f;
+                if constexpr (CHAN) {
+                    const float eg = fast_exp(G[j][ch]), emg = __builtin_amdgcn_rcpf(eg);
+                    oq[ch] = qv * eg;
+                    ok[ch] = kv * emg;
+                    oe[ch] = eb[ch] * kv * eg;
+                    oke[ch] = kv * (eGend[ch] * emg);
                 } else {
-                    eb = f32x4{bt4[jj], bt4[jj], bt4[jj], bt4[jj]};
-                    wz = eb;
+                    oq[ch] = qv;
+                    ok[ch] = kv;
+                    oe[ch] = eb[ch] * kv;
                 }
-                float gE[4], gK[4], gQ[4];
-#pragma unroll
-                for (int ch = 0; ch < 4; ++ch) {
-                    const float kv = valid ? kk[ch] : 0.f, qv = valid ? qq[ch] : 0.f;
-                    const float ev = eb[ch] * kv;
-                    xZ[jj][ch] = valid ? wz[ch] * vv[ch] : 0.f;
-                    if constexpr (CHAN) {  // factored form for the Gram
-                        const float eg = fast_exp(G[j][ch]), emg = __builtin_amdgcn_rcpf(eg);
-                        xE[jj][ch] = ev * eg;
-                        xKe[jj][ch] = kv * (eGend[ch] * emg);
-                        gE[ch] = xE[jj][ch];
-                        gK[ch] = kv * emg;
-                        gQ[ch] = qv * eg;
-                    } else {  // raw operands; the decay is applied to the Gram entries
-                        xE[jj][ch] = ev * egt4[jj];
-                        xKe[jj][ch] = kv * ert4[jj];
-                        gE[ch] = ev;
-                        gK[ch] = kv;
-                        gQ[ch] = qv;
-                    }
-                }
-                store4f(sE + tk * PD + 4 * cq, f32x4{gE[0], gE[1], gE[2], gE[3]});
-                store4f(sK + tk * PD + 4 * cq, f32x4{gK[0], gK[1], gK[2], gK[3]});
-                store4f(sQ + tk * PD + 4 * cq, f32x4{gQ[0], gQ[1], gQ[2], gQ[3]});
             }
-#pragma unroll
-            for (int ch = 0; ch < 4; ++ch) {
-                const int cc = 4 * cq + ch;
-                store4f(sXT + cc * PT + t4, f32x4{xE[0][ch], xE[1][ch], xE[2][ch], xE[3][ch]});
-                store4f(sXT + (D + cc) * PT + t4, f32x4{xZ[0][ch], xZ[1][ch], xZ[2][ch], xZ[3][ch]});
-                store4f(sKT + cc * PT + t4, f32x4{xKe[0][ch], xKe[1][ch], xKe[2][ch], xKe[3][ch]});
-            }
+            const int o = t * PD + V * co;
+            *reinterpret_cast<uint4 *>(tQ + o) = R::pack(oq);
+            *reinterpret_cast<uint4 *>(tK + o) = R::pack(ok);
+            *reinterpret_cast<uint4 *>(tZ + o) = R::pack(oz);
+            if constexpr (HAS_E) *reinterpret_cast<uint4 *>(tE + o) = R::pack(oe);
+            if constexpr (CHAN) *reinterpret_cast<uint4 *>(tKe + o) = R::pack(oke);
         }
         if (grp == NGRP - 1)
-            store4f(a.ws_gamma + (size_t)u * D + 4 * cq, f32x4{eGend[0], eGend[1], eGend[2], eGend[3]});
-        // The raw inputs are consumed: fetch the next unit's now.
-        if (u + (int)gridDim.x < units) in.load(a, u + gridDim.x, cq, grp);
-        __syncthreads();
-        store_frag_rows(wKT, D, C, sKT, PT, nullptr, tid, NT);
-        // Q~ for the sweep (scalar decay: the stored raw q times exp(G) per token).
-        store_frag_rows(wQ, C, D, sQ, PD, CHAN ? nullptr : sEG, tid, NT);
-
-        // ---- B. Gram products (20 lower 16x16 tiles: 10 of T, 10 of A) ----
-        f32x4 gacc[NG];
 #pragma unroll
-        for (int s = 0; s < NG; ++s) {
-            const int p = w + NW * s;
-            gacc[s] = zero4();
-            if (p < 20) {
-                const int kind = p / 10;
+            for (int i = 0; i < V / 4; ++i)
+                store4f(a.ws_gamma + (size_t)u * D + V * co + 4 * i,
+                        f32x4{eGend[4 * i], eGend[4 * i + 1], eGend[4 * i + 2], eGend[4 * i + 3]});
+        // The raw inputs are consumed: fetch the next unit's now.
+        if (u + (int)gridDim.x < units) in.load(a, u + gridDim.x, co, grp);
+        __syncthreads();
+
+        // ---- B. Gram products: 20 lower 16 x 16 tiles, 10 of T and 10 of A ----
+        {
+            const IO *TL = HAS_E ? tE : tK;  // left factor of T (raw k times beta for tied gates)
+#pragma unroll
+            for (int s = 0; s < 5; ++s) {
+                const int p = w + NW * s, kind = p / 10;
                 int ti, tj;
                 lower_tile(p - kind * 10, ti, tj);
-                const IO *X = kind == 0 ? sE : sQ;
+                const IO *X = kind == 0 ? TL : tQ;
+                f32x4 x = zero4();
 #pragma unroll
                 for (int ks = 0; ks < D / KS; ++ks)
-                    gacc[s] = M::step(gacc[s], X + ti * 16 * PD + ks * KS, PD, sK + tj * 16 * PD + ks * KS, PD);
-            }
-        }
-        __syncthreads();  // Kend^T staging copied out (its space becomes -T and A); E~, K~ are dead
-#pragma unroll
-        for (int s = 0; s < NG; ++s) {
-            const int p = w + NW * s;
-            if (p < 20) {
-                const int kind = p / 10;
-                int ti, tj;
-                lower_tile(p - kind * 10, ti, tj);
-                const int col = tj * 16 + lr, row0 = ti * 16 + 4 * lq;
-                f32x4 x = gacc[s];
+                    x = M::step(x, X + ti * 16 * PD + ks * KS, PD, tK + tj * 16 * PD + ks * KS, PD);
+                const int col = tj * 16 + lr, row0 = ti * 16 + 4 * lg;
                 if constexpr (!CHAN) {
                     const f32x4 Gr = load4f(sG + row0);
                     const float Gc = sG[col];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) x[r] *= fast_exp(fminf(Gr[r] - Gc, 0.f));
+                    if constexpr (!BW)
+                        if (kind == 0) {
+                            const f32x4 br = load4f(sBt + row0);
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) x[r] *= br[r];
+                        }
                 }
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = row0 + r;
-                    if (kind == 0) {
-                        if (ti == tj) sTd[(ti * 16 + lr) * 17 + 4 * lq + r] = col < row ? x[r] : 0.f;  // column-major
-                        else sTo[row * PT + col] = E::to(-x[r]);
-                    } else {
-                        sA[row * PT + col] = E::to(col <= row ? x[r] : 0.f);
-                    }
+                for (int r = 0; r < 4; ++r)
+                    if (kind == 0 ? col >= row0 + r : col > row0 + r) x[r] = 0.f;
+                if (kind == 0 && ti == tj) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sTd[(ti * 16 + lr) * 17 + 4 * lg + r] = x[r];
+                } else {
+                    store4f((kind == 0 ? sTc : sAc) + col * LC + row0, x);
                 }
             }
+            // A is zero above its diagonal tiles.
+            for (int z = w; z < 6; z += NW) {
+                const int ti = z < 3 ? 0 : z < 5 ? 1 : 2, tj = z < 3 ? z + 1 : z < 5 ? z - 1 : 3;
+                store4f(sAc + (tj * 16 + lr) * LC + ti * 16 + 4 * lg, zero4());
+            }
+            // Q~ fragments for the workspace (scalar decay: the row's exp(G)).
+            for (int f = w; f < (C / 16) * (D / KS); f += NW) {
+                const int rt = f / (D / KS), ks = f - rt * (D / KS);
+                Frag x = M::load(tQ + rt * 16 * PD + ks * KS, PD);
+                if constexpr (!CHAN) x = K::scale(x, sEG[rt * 16 + lr]);
+                store_frag<IO>(wQ, rt, ks, D, x);
+            }
+            // Kend^T fragments (rows = channels, K = tokens), read K-major from the tiles.
+            for (int f = w; f < (D / 16) * (C / KS); f += NW) {
+                const int rt = f / (C / KS), ks = f - rt * (C / KS);
+                Frag x = K::frag((CHAN ? tKe : tK) + ks * KS * PD + rt * 16, PD);
+                if constexpr (!CHAN) x = K::scale(x, sER + ks * KS + FE * lg);
+                store_frag<IO>(wKT, rt, ks, C, x);
+            }
         }
-        // Zero tiles, 16 bytes at a time: -T on and above the diagonal blocks, A above them.
+        __syncthreads();
+
+        // ---- C. A to the workspace; L = (I + T)^-1 ----
+        for (int f = w; f < (C / 16) * (C / KS); f += NW) {
+            const int rt = f / (C / KS), ks = f - rt * (C / KS);
+            store_frag<IO>(wA, rt, ks, C, K::frag(sAc + ks * KS * LC + rt * 16, LC));
+        }
+        // Diagonal block w of L: (I + T_ww)^-1 by fp32 substitution, lane lr < 16 forms column lr.
+        float xd[16];
+        if (l < 16) {
+            const float *Tb = sTd + w * 16 * 17;  // T(i, m) of the block at Tb[m * 17 + i]
+#pragma unroll
+            for (int i = 0; i < 16; ++i) xd[i] = i == lr ? 1.f : 0.f;
+#pragma unroll
+            for (int m = 0; m < 15; ++m) {
+                float col[16];
+#pragma unroll
+                for (int i = m + 1; i < 16; ++i) col[i] = Tb[m * 17 + i];
+#pragma unroll
+                for (int i = m + 1; i < 16; ++i) xd[i] -= col[i] * xd[m];
+            }
+        }
+        __syncthreads();  // A has been read out: its space becomes L
+        if (l < 16) {
+            IO *dst = sLc + (16 * w + lr) * LC + 16 * w;
+#pragma unroll
+            for (int i = 0; i < 16; i += 4) store4f(dst + i, f32x4{xd[i], xd[i + 1], xd[i + 2], xd[i + 3]});
+        } else if (l < 32 && (w == 1 || w == 3)) {
+            // Blocks (0,1) and (2,3) above the diagonal: phase D's 32-wide K steps read them.
+            IO *dst = sLc + (16 * w + lr) * LC + 16 * (w - 1);
+#pragma unroll
+            for (int i = 0; i < 16; i += 4) store4f(dst + i, zero4());
+        }
+        __syncthreads();
+        if (w < 3) {  // column block w: X_i = -D_i sum_{w <= k < i} T_ik X_k
+            IO *tmp = sTmp + w * 16 * LT;
+            for (int i = w + 1; i < 4; ++i) {
+                f32x4 acc = zero4();
+                for (int k = w; k < i; ++k)
+                    acc = K::mma16(acc, sTc + 16 * k * LC + 16 * i, LC, sLc + 16 * w * LC + 16 * k, LC);
+                store4f(tmp + lr * LT + 4 * lg, acc);
+                wave_sync();
+                const f32x4 x = K::mma16(zero4(), sLc + 16 * i * LC + 16 * i, LC, tmp, LT);
+                store4f(sLc + (16 * w + lr) * LC + 16 * i + 4 * lg, -x);
+                wave_sync();
+            }
+        }
+        __syncthreads();
+
+        // ---- D. [Y | U_z] = L [E~ | Z] ----
         {
-            constexpr int V = 16 / sizeof(IO);
+            constexpr int NKS = C / KS;
+            Frag la[4][NKS];
 #pragma unroll
-            for (int i = tid; i < C * C / V; i += NT) {
-                const int row = i / (C / V), col = (i - row * (C / V)) * V;
-                if ((col >> 4) >= (row >> 4)) *reinterpret_cast<uint4 *>(sTo + row * PT + col) = uint4{0, 0, 0, 0};
-                if ((col >> 4) > (row >> 4)) *reinterpret_cast<uint4 *>(sA + row * PT + col) = uint4{0, 0, 0, 0};
-            }
-        }
-        __syncthreads();
-        store_frag_rows(wA, C, C, sA, PT, nullptr, tid, NT);
-
-        // ---- C. diagonal block inverses: right-looking fp32 substitution, one column per lane ----
-        for (int blk = w; blk < 4; blk += NW) {
-            if (lr == l) {  // lanes 0..15
-                const float *Tb = sTd + blk * 16 * 17;  // column m at Tb + 17 m
-                float x[16];
+            for (int ri = 0; ri < 4; ++ri)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) x[i] = i == lr ? 1.f : 0.f;
-#pragma unroll
-                for (int m = 0; m < 15; ++m) {
-                    float col[16];
-#pragma unroll
-                    for (int i = m + 1; i < 16; ++i) col[i] = Tb[m * 17 + i];
-#pragma unroll
-                    for (int i = m + 1; i < 16; ++i) x[i] -= col[i] * x[m];
-                }
-#pragma unroll
-                for (int i = 0; i < 16; ++i) sDb[(blk * 16 + i) * PDB + lr] = E::to(x[i]);
-            }
-        }
-        __syncthreads();
-
-        // ---- C. blocked forward substitution; wave w owns columns WC*w..WC*w+WC-1 of [E~ | Z] ----
-        const bool yside = WC * w < D;
-#pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-            f32x4 acc[NCTS];
-#pragma unroll
-            for (int ct = 0; ct < NCTS; ++ct)
-                acc[ct] = R4::widen(R4::load(sXT + (WC * w + 16 * ct + lr) * PT + 16 * blk + 4 * lq));
-#pragma unroll
-            for (int ks = 0; ks < (16 * blk + KS - 1) / KS; ++ks)
-#pragma unroll
-                for (int ct = 0; ct < NCTS; ++ct)
-                    acc[ct] = M::step(acc[ct], sTo + 16 * blk * PT + ks * KS, PT,
-                                      sXT + (WC * w + 16 * ct) * PT + ks * KS, PT);
-#pragma unroll
-            for (int ct = 0; ct < NCTS; ++ct) store4f(tmp + (16 * ct + lr) * PTMP + 4 * lq, acc[ct]);
+                for (int ks = 0; ks < NKS; ++ks)
+                    if (ks * KS < 16 * ri + 16) la[ri][ks] = K::frag(sLc + ks * KS * LC + 16 * ri, LC);
 #pragma unroll
             for (int ct = 0; ct < NCTS; ++ct) {
-                const f32x4 x = Mma16<IO>::step(zero4(), sDb + blk * 16 * PDB, PDB, tmp + 16 * ct * PTMP, PTMP);
-                const int col = WC * w + 16 * ct + lr, tok = 16 * blk + 4 * lq;
-                store4f(sXT + col * PT + tok, x);
-                if (yside)  // Y also row-major, for the workspace
+                const int c0 = WC * w + 16 * ct;
+                const bool zside = c0 >= D;
+                const IO *src = zside ? tZ + (c0 - D) : (HAS_E ? tE : tK) + c0;
+                Frag bf[NKS];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) sYs[(tok + r) * PD + col] = E::to(x[r]);
+                for (int ks = 0; ks < NKS; ++ks) {
+                    bf[ks] = K::frag(src + ks * KS * PD, PD);
+                    if constexpr (!CHAN)
+                        if (!zside) bf[ks] = K::scale(bf[ks], sSE + ks * KS + FE * lg);
+                }
+#pragma unroll
+                for (int ri = 0; ri < 4; ++ri) {
+                    f32x4 acc = zero4();
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks)
+                        if (ks * KS < 16 * ri + 16) acc = M::mma(acc, la[ri][ks], bf[ks]);
+                    if (zside) store4f(wUzT + cfrag_off<D>(c0 - D + lr, 16 * ri + 4 * lg), acc);
+                    else store4f(sYc + (c0 + lr) * LY + 16 * ri + 4 * lg, acc);
+                }
             }
         }
         __syncthreads();
 
-        // Workspace stores: Y row-major; U_z^T.
-        store_frag_rows(wY, C, D, sYs, PD, nullptr, tid, NT);
-        store_cfrag<IO, D>(wUzT, sXT + D * PT, PT, tid, NT);
+        // ---- E. Y to the workspace ----
+        for (int f = w; f < (C / 16) * (D / KS); f += NW) {
+            const int rt = f / (D / KS), ks = f - rt * (D / KS);
+            store_frag<IO>(wY, rt, ks, D, K::frag(sYc + ks * KS * LY + rt * 16, LY));
+        }
     }
 }
 
@@ -703,27 +801,32 @@ static int device_cus() {
 template <typename IO, int D, int NCT>
 static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t s) {
     using Cfg = PrepCfg<IO, D>;
+    // Shared memory per prep variant (CHAN, BW): the per-channel-decay and
+    // decoupled-gate variants keep more tiles.
     static bool attr_set = false;
     if (!attr_set) {
         const void *fns[4] = {reinterpret_cast<const void *>(&chunk_prep<IO, D, false, false>),
                               reinterpret_cast<const void *>(&chunk_prep<IO, D, false, true>),
                               reinterpret_cast<const void *>(&chunk_prep<IO, D, true, false>),
                               reinterpret_cast<const void *>(&chunk_prep<IO, D, true, true>)};
-        for (const void *f : fns) {
-            hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::BYTES);
+        const size_t lds[4] = {Cfg::bytes(false, false), Cfg::bytes(true, false), Cfg::bytes(true, true),
+                               Cfg::bytes(true, true)};
+        for (int i = 0; i < 4; ++i) {
+            hipError_t e = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds[i]);
             if (e != hipSuccess) return e;
         }
         attr_set = true;
     }
     const long long units = (long long)a.B * a.Hv * a.NC;
     if (units > 0) {
-        // Persistent: one workgroup per compute unit (the LDS footprint allows one).
+        // Persistent: one workgroup per compute unit.
         const long long grid = units < device_cus() ? units : device_cus();
         const bool chan = a.decay == DECAY_CHANNEL, bw = a.beta == nullptr;
-        if (chan && bw) hipLaunchKernelGGL((chunk_prep<IO, D, true, true>), dim3((unsigned)grid), dim3(Cfg::NT), Cfg::BYTES, s, a);
-        else if (chan) hipLaunchKernelGGL((chunk_prep<IO, D, true, false>), dim3((unsigned)grid), dim3(Cfg::NT), Cfg::BYTES, s, a);
-        else if (bw) hipLaunchKernelGGL((chunk_prep<IO, D, false, true>), dim3((unsigned)grid), dim3(Cfg::NT), Cfg::BYTES, s, a);
-        else hipLaunchKernelGGL((chunk_prep<IO, D, false, false>), dim3((unsigned)grid), dim3(Cfg::NT), Cfg::BYTES, s, a);
+        const dim3 g((unsigned)grid), b(Cfg::NT);
+        if (chan && bw) hipLaunchKernelGGL((chunk_prep<IO, D, true, true>), g, b, Cfg::bytes(true, true), s, a);
+        else if (chan) hipLaunchKernelGGL((chunk_prep<IO, D, true, false>), g, b, Cfg::bytes(true, true), s, a);
+        else if (bw) hipLaunchKernelGGL((chunk_prep<IO, D, false, true>), g, b, Cfg::bytes(true, false), s, a);
+        else hipLaunchKernelGGL((chunk_prep<IO, D, false, false>), g, b, Cfg::bytes(false, false), s, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
