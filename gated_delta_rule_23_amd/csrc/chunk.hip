@@ -309,7 +309,10 @@ __global__ __launch_bounds__(256) void chunk_prep(ChunkArgs a) {
     float *sPart = reinterpret_cast<float *>(sp);                 // [NGRP][D] per-group channel sums
     IO *sYc = tQ;                                                 // Y(t, c) at sYc[c * LY + t]
 
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
+    // The wave index is uniform across the wave: keep it in a scalar register
+    // so that per-wave choices below are scalar branches, not masked ones.
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, lr = l & 15,
+              lg = l >> 4;
     const int co = tid % CO, grp = tid / CO;
     const int units = a.B * a.Hv * a.NC;
 
@@ -434,37 +437,51 @@ __global__ __launch_bounds__(256) void chunk_prep(ChunkArgs a) {
         // ---- B. Gram products: 20 lower 16 x 16 tiles, 10 of T and 10 of A ----
         {
             const IO *TL = HAS_E ? tE : tK;  // left factor of T (raw k times beta for tied gates)
+            constexpr int KD = D / KS;
+            f32x4 x[5];
 #pragma unroll
             for (int s = 0; s < 5; ++s) {
                 const int p = w + NW * s, kind = p / 10;
                 int ti, tj;
                 lower_tile(p - kind * 10, ti, tj);
-                const IO *X = kind == 0 ? TL : tQ;
-                f32x4 x = zero4();
+                const IO *X = (kind == 0 ? TL : tQ) + ti * 16 * PD, *Y = tK + tj * 16 * PD;
+                Frag fa[KD], fb[KD];
 #pragma unroll
-                for (int ks = 0; ks < D / KS; ++ks)
-                    x = M::step(x, X + ti * 16 * PD + ks * KS, PD, tK + tj * 16 * PD + ks * KS, PD);
+                for (int ks = 0; ks < KD; ++ks) {
+                    fa[ks] = M::load(X + ks * KS, PD);
+                    fb[ks] = M::load(Y + ks * KS, PD);
+                }
+                x[s] = zero4();
+#pragma unroll
+                for (int ks = 0; ks < KD; ++ks) x[s] = M::mma(x[s], fa[ks], fb[ks]);
+            }
+#pragma unroll
+            for (int s = 0; s < 5; ++s) {
+                const int p = w + NW * s, kind = p / 10;
+                int ti, tj;
+                lower_tile(p - kind * 10, ti, tj);
                 const int col = tj * 16 + lr, row0 = ti * 16 + 4 * lg;
+                f32x4 y = x[s];
                 if constexpr (!CHAN) {
                     const f32x4 Gr = load4f(sG + row0);
                     const float Gc = sG[col];
+                    f32x4 f;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) x[r] *= fast_exp(fminf(Gr[r] - Gc, 0.f));
+                    for (int r = 0; r < 4; ++r) f[r] = fast_exp(fminf(Gr[r] - Gc, 0.f));
                     if constexpr (!BW)
-                        if (kind == 0) {
-                            const f32x4 br = load4f(sBt + row0);
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) x[r] *= br[r];
-                        }
+                        if (kind == 0) f *= load4f(sBt + row0);
+                    y *= f;
                 }
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (kind == 0 ? col >= row0 + r : col > row0 + r) x[r] = 0.f;
+                for (int r = 0; r < 4; ++r) {
+                    const bool keep = kind == 0 ? col < row0 + r : col <= row0 + r;
+                    y[r] = keep ? y[r] : 0.f;
+                }
                 if (kind == 0 && ti == tj) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) sTd[(ti * 16 + lr) * 17 + 4 * lg + r] = x[r];
+                    for (int r = 0; r < 4; ++r) sTd[(ti * 16 + lr) * 17 + 4 * lg + r] = y[r];
                 } else {
-                    store4f((kind == 0 ? sTc : sAc) + col * LC + row0, x);
+                    store4f((kind == 0 ? sTc : sAc) + col * LC + row0, y);
                 }
             }
             // A is zero above its diagonal tiles.
@@ -640,7 +657,7 @@ __device__ __forceinline__ void sweep_chunk(const SweepOps<IO, D, NCT> &op, f32x
     using Ops = SweepOps<IO, D, NCT>;
     constexpr int BV = 16 * NCT, TPW = Ops::TPW, KS = M::KS, KD = Ops::KD, KC = Ops::KC;
     constexpr int LS = D + 8, LU = C + 8, LO = BV + 8;
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, lr = l & 15, lq = l >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63, lr = l & 15, lq = l >> 4;
 
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
@@ -731,7 +748,7 @@ __global__ __launch_bounds__(2 * D) void chunk_sweep(ChunkArgs a, int NVT, int G
     if (wi >= G) return;
     const int bh = wi / NVT, vt = wi - (wi / NVT) * NVT, col0 = vt * BV;
     const int b = bh / a.Hv, h = bh - (bh / a.Hv) * a.Hv;
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, lr = l & 15, lq = l >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63, lr = l & 15, lq = l >> 4;
 
     f32x4 S[2][NCT];
 #pragma unroll
