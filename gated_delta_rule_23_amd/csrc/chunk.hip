@@ -276,8 +276,13 @@ struct PrepIn {
     }
 };
 
+// Workgroups per compute unit: the scalar-decay, tied-gate variant fits two
+// in shared memory and registers, which hides each one's latencies.
 template <typename IO, int D, bool CHAN, bool BW>
-__global__ __launch_bounds__(256) void chunk_prep(ChunkArgs a) {
+constexpr int prep_occupancy() { return (CHAN || BW) ? 1 : 2; }
+
+template <typename IO, int D, bool CHAN, bool BW>
+__global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chunk_prep(ChunkArgs a) {
     using M = Mma<IO>;
     using K = Km<IO>;
     using R = Raw16<IO>;
@@ -836,9 +841,12 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t s) {
     }
     const long long units = (long long)a.B * a.Hv * a.NC;
     if (units > 0) {
-        // Persistent: one workgroup per compute unit.
-        const long long grid = units < device_cus() ? units : device_cus();
+        // Persistent: as many workgroups as fit on the device at once.
         const bool chan = a.decay == DECAY_CHANNEL, bw = a.beta == nullptr;
+        const int occ = !chan && !bw && 2 * Cfg::bytes(false, false) <= (size_t)160 * 1024
+                            ? prep_occupancy<IO, D, false, false>() : 1;
+        const long long slots = (long long)occ * device_cus();
+        const long long grid = units < slots ? units : slots;
         const dim3 g((unsigned)grid), b(Cfg::NT);
         if (chan && bw) hipLaunchKernelGGL((chunk_prep<IO, D, true, true>), g, b, Cfg::bytes(true, true), s, a);
         else if (chan) hipLaunchKernelGGL((chunk_prep<IO, D, true, false>), g, b, Cfg::bytes(true, true), s, a);
