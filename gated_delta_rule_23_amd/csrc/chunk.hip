@@ -601,41 +601,44 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
 }
 
 // Sequential sweep over chunks for one (sequence, V head, value tile of BV =
-// 16*NCT columns). NW = D/32 waves; wave w keeps state rows 32w..32w+31 in
-// accumulator layout and computes token tiles [w*TPW, (w+1)*TPW) of the
-// outputs. Per chunk:
-//   P = Y S_c, R = Q~ S_c          (S_c^T shared through LDS)
-//   U = U_z - P                    (U^T shared through LDS)
-//   O = s (R + A U)
-//   S_{c+1} = gamma . S_c + Kend^T U
-// Each wave reads only its own slice of a chunk's factors (its token rows of
-// Y, Q~ and A, its channel rows of Kend^T), so those slices are prefetched
-// into registers PF chunks ahead and the global-memory latency leaves the chain.
+// 16*NCT columns), with two kinds of waves. NWC = D/32 "chain" waves carry
+// the state: chain wave w keeps state rows 32w..32w+31 in accumulator layout
+// and per chunk forms P = Y S_c and U = U_z - P for its token tiles
+// [w*TPW, (w+1)*TPW), then S_{c+1} = gamma . S_c + Kend^T U. NWC "output"
+// waves form O = s (Q~ S_c + A U) for the same token tiles. Both kinds meet
+// at two barriers per chunk: once S_c^T is in shared memory (the output waves
+// then form Q~ S_c while the chain forms U) and once U^T is (the output waves
+// then add A U and store O while the chain updates the state), so the output
+// work and its loads stay off the state's critical path. Every wave
+// prefetches its own slice of the chunk factors PF chunks ahead.
 template <typename IO, int D, int NCT>
-struct SweepOps {
+struct SweepShape {
     using M = Mma<IO>;
-    using F = typename M::Frag;
+    static constexpr int NWC = D / 32, TPW = 4 / NWC, KD = D / M::KS, KC = C / M::KS;
+    static constexpr int BV = 16 * NCT, LS = D + 8, LU = C + 8, LO = BV + 8;
+};
+
+// Workspace slices of one chunk unit.
+template <typename IO, int D>
+__device__ __forceinline__ const IO *ws_unit(const IO *wsb, size_t u) { return wsb + u * chunk_ws_io_elems(D); }
+
+template <typename IO, int D, int NCT>
+struct ChainOps {  // Y rows and U_z columns of the wave's token tiles; Kend^T rows of its state rows; gamma
+    using Sh = SweepShape<IO, D, NCT>;
+    using F = typename Sh::M::Frag;
     using R4 = Raw4<IO>;
-    static constexpr int NW = D / 32, TPW = 4 / NW, KD = D / M::KS, KC = C / M::KS;
-    F ya[TPW][KD], qa[TPW][KD], aa[TPW][KC], ka[2][KC];
-    typename R4::type uz[TPW][NCT];
+    F ya[Sh::TPW][Sh::KD], ka[2][Sh::KC];
+    typename R4::type uz[Sh::TPW][NCT];
     f32x4 g4[2];
 
     __device__ __forceinline__ void load(const IO *wsb, const float *wsg, size_t u, int w, int col0) {
         const int l = threadIdx.x & 63, lq = l >> 4;
-        const IO *Y = wsb + u * chunk_ws_io_elems(D), *Qt = Y + C * D, *KT = Qt + C * D, *UzT = KT + D * C,
-                 *A = UzT + D * C;
-        const float *gam = wsg + u * D;
+        const IO *Y = ws_unit<IO, D>(wsb, u), *KT = Y + 2 * C * D, *UzT = Y + 3 * C * D;
 #pragma unroll
-        for (int tt = 0; tt < TPW; ++tt) {
-            const int rt = w * TPW + tt;
+        for (int tt = 0; tt < Sh::TPW; ++tt) {
+            const int rt = w * Sh::TPW + tt;
 #pragma unroll
-            for (int ks = 0; ks < KD; ++ks) {
-                ya[tt][ks] = load_frag(Y, rt, ks, D);
-                qa[tt][ks] = load_frag(Qt, rt, ks, D);
-            }
-#pragma unroll
-            for (int ks = 0; ks < KC; ++ks) aa[tt][ks] = load_frag(A, rt, ks, C);
+            for (int ks = 0; ks < Sh::KD; ++ks) ya[tt][ks] = load_frag(Y, rt, ks, D);
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
                 uz[tt][ct] = R4::load(UzT + ((size_t)(rt * (D / 16) + col0 / 16 + ct) * 64 + l) * 4);
@@ -644,69 +647,116 @@ struct SweepOps {
         for (int rt = 0; rt < 2; ++rt) {
             const int ch0 = 32 * w + 16 * rt;
 #pragma unroll
-            for (int ks = 0; ks < KC; ++ks) ka[rt][ks] = load_frag(KT, ch0 / 16, ks, C);
-            g4[rt] = load4f(gam + ch0 + 4 * lq);
+            for (int ks = 0; ks < Sh::KC; ++ks) ka[rt][ks] = load_frag(KT, ch0 / 16, ks, C);
+            g4[rt] = load4f(wsg + u * D + ch0 + 4 * lq);
         }
     }
 };
 
-// One chunk of the sweep. TAIL = the chunk may hold fewer than C tokens
-// (only the last one), so output rows are stored under a predicate; every
-// other chunk stores unconditionally, which keeps the number of memory
-// operations in flight static and lets the prefetches stay in flight.
-template <typename IO, int D, int NCT, bool TAIL>
-__device__ __forceinline__ void sweep_chunk(const SweepOps<IO, D, NCT> &op, f32x4 (&S)[2][NCT], IO *sST, IO *sUT,
-                                            IO *sO, IO *orow0, size_t orow_stride, int n_valid, float scale) {
-    using M = Mma<IO>;
-    using F = typename M::Frag;
-    using Ops = SweepOps<IO, D, NCT>;
-    constexpr int BV = 16 * NCT, TPW = Ops::TPW, KS = M::KS, KD = Ops::KD, KC = Ops::KC;
-    constexpr int LS = D + 8, LU = C + 8, LO = BV + 8;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63, lr = l & 15, lq = l >> 4;
+template <typename IO, int D, int NCT>
+struct OutOps {  // Q~ and A rows of the wave's token tiles
+    using Sh = SweepShape<IO, D, NCT>;
+    using F = typename Sh::M::Frag;
+    F qa[Sh::TPW][Sh::KD], aa[Sh::TPW][Sh::KC];
 
+    __device__ __forceinline__ void load(const IO *wsb, size_t u, int w) {
+        const IO *Qt = ws_unit<IO, D>(wsb, u) + C * D, *A = ws_unit<IO, D>(wsb, u) + 4 * C * D;
+#pragma unroll
+        for (int tt = 0; tt < Sh::TPW; ++tt) {
+            const int rt = w * Sh::TPW + tt;
+#pragma unroll
+            for (int ks = 0; ks < Sh::KD; ++ks) qa[tt][ks] = load_frag(Qt, rt, ks, D);
+#pragma unroll
+            for (int ks = 0; ks < Sh::KC; ++ks) aa[tt][ks] = load_frag(A, rt, ks, C);
+        }
+    }
+};
+
+// One chunk on a chain wave.
+template <typename IO, int D, int NCT>
+__device__ __forceinline__ void chain_chunk(const ChainOps<IO, D, NCT> &op, f32x4 (&S)[2][NCT], IO *sST, IO *sUT,
+                                            int w) {
+    using Sh = SweepShape<IO, D, NCT>;
+    using M = typename Sh::M;
+    using F = typename M::Frag;
+    constexpr int KS = M::KS, LS = Sh::LS, LU = Sh::LU;
+    const int l = threadIdx.x & 63, lr = l & 15, lq = l >> 4;
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
             store4f(sST + (16 * ct + lr) * LS + 32 * w + 16 * rt + 4 * lq, S[rt][ct]);
-    __syncthreads();
-
-    f32x4 accR[TPW][NCT];
+    __syncthreads();  // S_c^T is shared
 #pragma unroll
-    for (int tt = 0; tt < TPW; ++tt) {
-        const int T0 = (w * TPW + tt) * 16;
+    for (int tt = 0; tt < Sh::TPW; ++tt) {
+        const int T0 = (w * Sh::TPW + tt) * 16;
         f32x4 accP[NCT];
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) { accP[ct] = zero4(); accR[tt][ct] = zero4(); }
+        for (int ct = 0; ct < NCT; ++ct) accP[ct] = zero4();
 #pragma unroll
-        for (int ks = 0; ks < KD; ++ks) {
+        for (int ks = 0; ks < Sh::KD; ++ks)
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                const F sb = M::load(sST + 16 * ct * LS + ks * KS, LS);
-                accP[ct] = M::mma(accP[ct], op.ya[tt][ks], sb);
-                accR[tt][ct] = M::mma(accR[tt][ct], op.qa[tt][ks], sb);
-            }
-        }
+            for (int ct = 0; ct < NCT; ++ct)
+                accP[ct] = M::mma(accP[ct], op.ya[tt][ks], M::load(sST + 16 * ct * LS + ks * KS, LS));
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
-            store4f(sUT + (16 * ct + lr) * LU + T0 + 4 * lq, Ops::R4::widen(op.uz[tt][ct]) - accP[ct]);
+            store4f(sUT + (16 * ct + lr) * LU + T0 + 4 * lq, Raw4<IO>::widen(op.uz[tt][ct]) - accP[ct]);
     }
-    __syncthreads();
-
-    // O = s (R + A U); U fragments come from LDS and also feed the state update.
-    F ub[KC][NCT];
+    __syncthreads();  // U^T is shared
+    F ub[Sh::KC][NCT];
 #pragma unroll
-    for (int ks = 0; ks < KC; ++ks)
+    for (int ks = 0; ks < Sh::KC; ++ks)
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) ub[ks][ct] = M::load(sUT + 16 * ct * LU + ks * KS, LU);
 #pragma unroll
-    for (int tt = 0; tt < TPW; ++tt) {
-        const int T0 = (w * TPW + tt) * 16;
+    for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) S[rt][ct] *= op.g4[rt];
+#pragma unroll
+        for (int ks = 0; ks < Sh::KC; ++ks)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) S[rt][ct] = M::mma(S[rt][ct], op.ka[rt][ks], ub[ks][ct]);
+    }
+}
+
+// One chunk on an output wave (w = its index among the output waves). TAIL =
+// the chunk may hold fewer than C tokens (only the last one), so output rows
+// are stored under a predicate; every other chunk stores unconditionally,
+// which keeps the number of memory operations in flight static.
+template <typename IO, int D, int NCT, bool TAIL>
+__device__ __forceinline__ void out_chunk(const OutOps<IO, D, NCT> &op, const IO *sST, const IO *sUT, IO *sO,
+                                          IO *orow0, size_t orow_stride, int n_valid, float scale, int w) {
+    using Sh = SweepShape<IO, D, NCT>;
+    using M = typename Sh::M;
+    using F = typename M::Frag;
+    constexpr int KS = M::KS, LS = Sh::LS, LU = Sh::LU, LO = Sh::LO, BV = Sh::BV;
+    const int l = threadIdx.x & 63, lr = l & 15, lq = l >> 4;
+    f32x4 accR[Sh::TPW][NCT];
+    __syncthreads();  // S_c^T is shared
+#pragma unroll
+    for (int tt = 0; tt < Sh::TPW; ++tt) {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) accR[tt][ct] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < Sh::KD; ++ks)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+                accR[tt][ct] = M::mma(accR[tt][ct], op.qa[tt][ks], M::load(sST + 16 * ct * LS + ks * KS, LS));
+    }
+    __syncthreads();  // U^T is shared
+    F ub[Sh::KC][NCT];
+#pragma unroll
+    for (int ks = 0; ks < Sh::KC; ++ks)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) ub[ks][ct] = M::load(sUT + 16 * ct * LU + ks * KS, LU);
+#pragma unroll
+    for (int tt = 0; tt < Sh::TPW; ++tt) {
+        const int T0 = (w * Sh::TPW + tt) * 16;
         // All K steps (A is zero above its diagonal tiles): a trip count that
         // depends on the wave would put branches around the prefetch
         // bookkeeping and force a full drain of the loads in flight.
 #pragma unroll
-        for (int ks = 0; ks < KC; ++ks)
+        for (int ks = 0; ks < Sh::KC; ++ks)
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) accR[tt][ct] = M::mma(accR[tt][ct], op.aa[tt][ks], ub[ks][ct]);
 #pragma unroll
@@ -724,26 +774,15 @@ __device__ __forceinline__ void sweep_chunk(const SweepOps<IO, D, NCT> &op, f32x
                     *reinterpret_cast<const uint4 *>(sO + tok * LO + c8);
         }
     }
-
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) S[rt][ct] *= op.g4[rt];
-#pragma unroll
-        for (int ks = 0; ks < KC; ++ks)
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) S[rt][ct] = M::mma(S[rt][ct], op.ka[rt][ks], ub[ks][ct]);
-    }
 }
 
 template <typename IO, int D, int NCT, int PF>
-__global__ __launch_bounds__(2 * D) void chunk_sweep(ChunkArgs a, int NVT, int G) {
-    using Ops = SweepOps<IO, D, NCT>;
-    constexpr int BV = 16 * NCT;
-    constexpr int LS = D + 8, LU = C + 8, LO = BV + 8;
+__global__ __launch_bounds__(4 * D) void chunk_sweep(ChunkArgs a, int NVT, int G) {
+    using Sh = SweepShape<IO, D, NCT>;
+    constexpr int BV = Sh::BV, LS = Sh::LS, LU = Sh::LU, LO = Sh::LO, NWC = Sh::NWC;
     __shared__ __align__(16) IO sST[BV * LS];  // S_c^T in the io dtype
     __shared__ __align__(16) IO sUT[BV * LU];  // U^T in the io dtype
-    __shared__ __align__(16) IO sO[C * LO];    // output rows (each wave stages its own)
+    __shared__ __align__(16) IO sO[C * LO];    // output rows (each output wave stages its own)
 
     // Work index: blocks that share an XCD (blockIdx % 8) take consecutive
     // work items, so the value tiles of one head read its chunk factors
@@ -753,59 +792,73 @@ __global__ __launch_bounds__(2 * D) void chunk_sweep(ChunkArgs a, int NVT, int G
     if (wi >= G) return;
     const int bh = wi / NVT, vt = wi - (wi / NVT) * NVT, col0 = vt * BV;
     const int b = bh / a.Hv, h = bh - (bh / a.Hv) * a.Hv;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63, lr = l & 15, lq = l >> 4;
-
-    f32x4 S[2][NCT];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int ch = 32 * w + 16 * rt + 4 * lq + r, col = col0 + 16 * ct + lr;
-                S[rt][ct][r] = a.S0 ? a.S0[((size_t)bh * D + ch) * D + col] : 0.f;
-            }
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63, lr = l & 15, lq = l >> 4;
 
     const IO *wsb = static_cast<const IO *>(a.ws_io);
     const size_t u0 = (size_t)bh * a.NC;
     const int NC = a.NC;
-    const size_t orow_stride = (size_t)a.Hv * D;
-    IO *obase = static_cast<IO *>(a.o) + ((size_t)b * a.T * a.Hv + h) * D + col0;
 
-    if (NC > 0) {
-        Ops ring[PF];
+    if (wv < NWC) {  // ---- chain wave ----
+        const int w = wv;
+        f32x4 S[2][NCT];
 #pragma unroll
-        for (int j = 0; j < PF; ++j) ring[j].load(wsb, a.ws_gamma, u0 + min(j, NC - 1), w, col0);
-
-        // Pipelined part: every chunk but the last is full (C tokens).
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int ch = 32 * w + 16 * rt + 4 * lq + r, col = col0 + 16 * ct + lr;
+                    S[rt][ct][r] = a.S0 ? a.S0[((size_t)bh * D + ch) * D + col] : 0.f;
+                }
+        if (NC > 0) {
+            ChainOps<IO, D, NCT> ring[PF];
+#pragma unroll
+            for (int j = 0; j < PF; ++j) ring[j].load(wsb, a.ws_gamma, u0 + min(j, NC - 1), w, col0);
+            int c = 0;
+            for (; c + PF <= NC - 1; c += PF) {
+#pragma unroll
+                for (int j = 0; j < PF; ++j) {
+                    chain_chunk<IO, D, NCT>(ring[j], S, sST, sUT, w);
+                    ring[j].load(wsb, a.ws_gamma, u0 + min(c + j + PF, NC - 1), w, col0);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < PF; ++j)
+                if (c + j < NC) chain_chunk<IO, D, NCT>(ring[j], S, sST, sUT, w);
+        }
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int ch = 32 * w + 16 * rt + 4 * lq + r, col = col0 + 16 * ct + lr;
+                    a.ST[((size_t)bh * D + ch) * D + col] = S[rt][ct][r];
+                }
+    } else if (NC > 0) {  // ---- output wave: same chunk sequence, same barriers ----
+        const int w = wv - NWC;
+        const size_t orow_stride = (size_t)a.Hv * D;
+        IO *obase = static_cast<IO *>(a.o) + ((size_t)b * a.T * a.Hv + h) * D + col0;
+        OutOps<IO, D, NCT> ring[PF];
+#pragma unroll
+        for (int j = 0; j < PF; ++j) ring[j].load(wsb, u0 + min(j, NC - 1), w);
         int c = 0;
         for (; c + PF <= NC - 1; c += PF) {
 #pragma unroll
             for (int j = 0; j < PF; ++j) {
-                sweep_chunk<IO, D, NCT, false>(ring[j], S, sST, sUT, sO, obase + (size_t)(c + j) * C * orow_stride,
-                                               orow_stride, C, a.scale);
-                ring[j].load(wsb, a.ws_gamma, u0 + min(c + j + PF, NC - 1), w, col0);
+                out_chunk<IO, D, NCT, false>(ring[j], sST, sUT, sO, obase + (size_t)(c + j) * C * orow_stride,
+                                             orow_stride, C, a.scale, w);
+                ring[j].load(wsb, u0 + min(c + j + PF, NC - 1), w);
             }
         }
-        // Remainder: ring slot j holds chunk c + j (clamped); the last chunk may be partial.
 #pragma unroll
         for (int j = 0; j < PF; ++j) {
             const int cj = c + j;
             if (cj < NC)
-                sweep_chunk<IO, D, NCT, true>(ring[j], S, sST, sUT, sO, obase + (size_t)cj * C * orow_stride,
-                                              orow_stride, a.T - cj * C, a.scale);
+                out_chunk<IO, D, NCT, true>(ring[j], sST, sUT, sO, obase + (size_t)cj * C * orow_stride, orow_stride,
+                                            a.T - cj * C, a.scale, w);
         }
     }
-
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int ch = 32 * w + 16 * rt + 4 * lq + r, col = col0 + 16 * ct + lr;
-                a.ST[((size_t)bh * D + ch) * D + col] = S[rt][ct][r];
-            }
 }
 
 static int device_cus() {
@@ -859,7 +912,7 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t s) {
     const int G = a.B * a.Hv * NVT;
     const int grid = (G + 7) / 8 * 8;
     constexpr int PF = sizeof(IO) == 2 ? SWEEP_PF : 1;  // prefetch depth (fp32 fragments are 2x larger)
-    hipLaunchKernelGGL((chunk_sweep<IO, D, NCT, PF>), dim3(grid), dim3(2 * D), 0, s, a, NVT, G);
+    hipLaunchKernelGGL((chunk_sweep<IO, D, NCT, PF>), dim3(grid), dim3(4 * D), 0, s, a, NVT, G);
     return hipGetLastError();
 }
 
