@@ -130,7 +130,8 @@ int gdr_chunk_workspace_bytes(const gdr_desc *d, size_t *bytes) {
                             (const float *)p, nullptr, nullptr, p);
     if (rc != GDR_OK) return rc;
     const int NC = (d->T + gdr::kChunk - 1) / gdr::kChunk;
-    *bytes = gdr::chunk_ws_bytes(d->B, d->H_v, NC, d->d_k, d->io_dtype == GDR_BF16 ? gdr::IO_BF16 : gdr::IO_F32);
+    *bytes = gdr::chunk_ws_layout(d->B, d->H_qk, d->H_v, NC, d->d_k, d->io_dtype == GDR_BF16 ? gdr::IO_BF16 : gdr::IO_F32,
+                                  d->decay == GDR_DECAY_CHANNEL).total();
     return ok();
 }
 
@@ -142,7 +143,8 @@ int gdr_chunk_fwd(const gdr_desc *d, const void *q, const void *k, const void *v
     if (!ST) return fail(GDR_E_INVAL, "ST must be non-NULL");
     const int io = d->io_dtype == GDR_BF16 ? gdr::IO_BF16 : gdr::IO_F32;
     const int NC = (d->T + gdr::kChunk - 1) / gdr::kChunk;
-    const size_t need = gdr::chunk_ws_bytes(d->B, d->H_v, NC, d->d_k, io);
+    const gdr::ChunkWsLayout L = gdr::chunk_ws_layout(d->B, d->H_qk, d->H_v, NC, d->d_k, io, d->decay == GDR_DECAY_CHANNEL);
+    const size_t need = L.total();
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(GDR_E_INVAL, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
     if (d->B == 0) return ok();
@@ -153,8 +155,8 @@ int gdr_chunk_fwd(const gdr_desc *d, const void *q, const void *k, const void *v
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.bg = b; a.wg = w;
     a.S0 = S0; a.o = o; a.ST = ST;
     a.ws_io = workspace;
-    a.ws_gamma = reinterpret_cast<float *>(static_cast<char *>(workspace) +
-                                           gdr::align256(units * gdr::chunk_ws_io_elems(d->d_k) * (io == gdr::IO_BF16 ? 2 : 4)));
+    a.ws_tab = reinterpret_cast<float *>(static_cast<char *>(workspace) + L.io_bytes);
+    a.ws_kT = L.kT_bytes ? static_cast<char *>(workspace) + L.io_bytes + L.tab_bytes : nullptr;
     a.B = d->B; a.T = d->T; a.Hqk = d->H_qk; a.Hv = d->H_v; a.decay = d->decay; a.NC = NC;
     a.scale = d->scale;
     hipError_t e = gdr::launch_chunk(io, d->d_k, a, static_cast<hipStream_t>(stream));

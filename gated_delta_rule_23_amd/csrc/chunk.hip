@@ -308,7 +308,6 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
     float *sTd = reinterpret_cast<float *>(sp); sp += Cfg::TD;  // T's diagonal blocks, fp32, [blk][col][17]
     float *sG = reinterpret_cast<float *>(sp); sp += Cfg::TAB;  // per token: G,
     float *sEG = sG + C;                                          //   exp(G),
-    float *sER = sG + 2 * C;                                      //   exp(G_end - G),
     float *sBt = sG + 3 * C;                                      //   beta,
     float *sSE = sG + 4 * C;                                      //   the E~ factor of a raw erase-key tile
     float *sPart = reinterpret_cast<float *>(sp);                 // [NGRP][D] per-group channel sums
@@ -325,10 +324,15 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
     if ((int)blockIdx.x < units) in.load(a, blockIdx.x, co, grp);
 
     for (int u = blockIdx.x; u < units; u += gridDim.x) {
-        const int NC = a.NC, c = u % NC;
+        const int NC = a.NC, c = u % NC, bh = u / NC, h = bh % a.Hv, grpsz = a.Hv / a.Hqk;
         const int n = min(C, a.T - c * C);
-        IO *ws = static_cast<IO *>(a.ws_io) + (size_t)u * chunk_ws_io_elems(D);
-        IO *wY = ws, *wQ = ws + C * D, *wKT = ws + 2 * C * D, *wUzT = ws + 3 * C * D, *wA = ws + 4 * C * D;
+        IO *ws = static_cast<IO *>(a.ws_io) + (size_t)u * chunk_ws_io_elems(D, CHAN);
+        IO *wY = ws, *wQ = ws + C * D, *wUzT = ws + ws_off_uz(D, CHAN), *wA = ws + ws_off_a(D, CHAN);
+        // Kend^T per unit (per-channel decay), or k^T once per QK head, written by its first V head.
+        IO *wKT = CHAN ? ws + 2 * C * D
+                       : static_cast<IO *>(a.ws_kT) + ((size_t)(bh / a.Hv * a.Hqk + h / grpsz) * NC + c) * (D * C);
+        const bool write_kT = CHAN || h % grpsz == 0;
+        float *tab = a.ws_tab + (size_t)u * kTab;
         __syncthreads();  // the previous unit is done with shared memory
 
         // ---- A. prefix sums, token tables, tiles ----
@@ -355,9 +359,11 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
                     if (l >= off) Gl += y;
                 }
                 eg = fast_exp(Gl);
+                const float er = fast_exp(__shfl(Gl, 63) - Gl);
                 sG[l] = Gl;
                 sEG[l] = eg;
-                sER[l] = fast_exp(__shfl(Gl, 63) - Gl);
+                tab[l] = eg;       // per-token decay factors for the sweep
+                tab[C + l] = er;
             }
             if constexpr (!BW) sBt[l] = in.betal;
             sSE[l] = BW ? eg : in.betal * eg;
@@ -430,11 +436,11 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
             if constexpr (HAS_E) *reinterpret_cast<uint4 *>(tE + o) = R::pack(oe);
             if constexpr (CHAN) *reinterpret_cast<uint4 *>(tKe + o) = R::pack(oke);
         }
-        if (grp == NGRP - 1)
+        if constexpr (CHAN)
+            if (grp == NGRP - 1)
 #pragma unroll
-            for (int i = 0; i < V / 4; ++i)
-                store4f(a.ws_gamma + (size_t)u * D + V * co + 4 * i,
-                        f32x4{eGend[4 * i], eGend[4 * i + 1], eGend[4 * i + 2], eGend[4 * i + 3]});
+                for (int i = 0; i < V / 4; ++i)
+                    store4f(tab + V * co + 4 * i, f32x4{eGend[4 * i], eGend[4 * i + 1], eGend[4 * i + 2], eGend[4 * i + 3]});
         // The raw inputs are consumed: fetch the next unit's now.
         if (u + (int)gridDim.x < units) in.load(a, u + gridDim.x, co, grp);
         __syncthreads();
@@ -494,20 +500,17 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
                 const int ti = z < 3 ? 0 : z < 5 ? 1 : 2, tj = z < 3 ? z + 1 : z < 5 ? z - 1 : 3;
                 store4f(sAc + (tj * 16 + lr) * LC + ti * 16 + 4 * lg, zero4());
             }
-            // Q~ fragments for the workspace (scalar decay: the row's exp(G)).
-            for (int f = w; f < (C / 16) * (D / KS); f += NW) {
-                const int rt = f / (D / KS), ks = f - rt * (D / KS);
-                Frag x = M::load(tQ + rt * 16 * PD + ks * KS, PD);
-                if constexpr (!CHAN) x = K::scale(x, sEG[rt * 16 + lr]);
-                store_frag<IO>(wQ, rt, ks, D, x);
-            }
-            // Kend^T fragments (rows = channels, K = tokens), read K-major from the tiles.
-            for (int f = w; f < (D / 16) * (C / KS); f += NW) {
-                const int rt = f / (C / KS), ks = f - rt * (C / KS);
-                Frag x = K::frag((CHAN ? tKe : tK) + ks * KS * PD + rt * 16, PD);
-                if constexpr (!CHAN) x = K::scale(x, sER + ks * KS + FE * lg);
-                store_frag<IO>(wKT, rt, ks, C, x);
-            }
+            if constexpr (CHAN)  // Q~ fragments for the workspace
+                for (int f = w; f < (C / 16) * (D / KS); f += NW) {
+                    const int rt = f / (D / KS), ks = f - rt * (D / KS);
+                    store_frag<IO>(wQ, rt, ks, D, M::load(tQ + rt * 16 * PD + ks * KS, PD));
+                }
+            // Kend^T (or raw k^T) fragments: rows = channels, K = tokens, read K-major from the tiles.
+            if (write_kT)
+                for (int f = w; f < (D / 16) * (C / KS); f += NW) {
+                    const int rt = f / (C / KS), ks = f - rt * (C / KS);
+                    store_frag<IO>(wKT, rt, ks, C, K::frag((CHAN ? tKe : tK) + ks * KS * PD + rt * 16, PD));
+                }
         }
         __syncthreads();
 
@@ -611,6 +614,11 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
 // then add A U and store O while the chain updates the state), so the output
 // work and its loads stay off the state's critical path. Every wave
 // prefetches its own slice of the chunk factors PF chunks ahead.
+//
+// With a scalar decay (CHAN false) the workspace holds neither Q~ nor Kend^T:
+// the output waves read q itself and scale the rows of q S_c by exp(G_t), and
+// the chain waves read the QK head's k^T and use the rows of U scaled by
+// exp(G_end - G_t) for the state update (Kend^T U = k^T Diag(exp(G_end - G)) U).
 template <typename IO, int D, int NCT>
 struct SweepShape {
     using M = Mma<IO>;
@@ -618,22 +626,33 @@ struct SweepShape {
     static constexpr int BV = 16 * NCT, LS = D + 8, LU = C + 8, LO = BV + 8;
 };
 
-// Workspace slices of one chunk unit.
-template <typename IO, int D>
-__device__ __forceinline__ const IO *ws_unit(const IO *wsb, size_t u) { return wsb + u * chunk_ws_io_elems(D); }
+// Where one sweep work item finds its chunk factors.
+template <typename IO>
+struct SweepSrc {
+    const IO *ws;     // io workspace
+    const float *tab; // per-unit float tables
+    const IO *kT;     // k^T of this QK head, chunk 0 (scalar decay)
+    const IO *q;      // q of this sequence and QK head, token 0 (scalar decay)
+    size_t u0;        // unit of chunk 0
+    int qstride;      // token stride of q (elements)
+};
 
-template <typename IO, int D, int NCT>
-struct ChainOps {  // Y rows and U_z columns of the wave's token tiles; Kend^T rows of its state rows; gamma
+template <typename IO, int D, int NCT, bool CHAN>
+struct ChainOps {  // Y rows and U_z columns of the wave's token tiles; Kend^T (k^T) rows of its state rows; decay
     using Sh = SweepShape<IO, D, NCT>;
     using F = typename Sh::M::Frag;
     using R4 = Raw4<IO>;
     F ya[Sh::TPW][Sh::KD], ka[2][Sh::KC];
     typename R4::type uz[Sh::TPW][NCT];
-    f32x4 g4[2];
+    f32x4 g4[2];                     // gamma of the wave's state rows
+    f32x4 er[CHAN ? 1 : Sh::TPW];    // exp(G_end - G) of the wave's token rows (scalar decay)
 
-    __device__ __forceinline__ void load(const IO *wsb, const float *wsg, size_t u, int w, int col0) {
+    __device__ __forceinline__ void load(const SweepSrc<IO> &src, int c, int w, int col0) {
         const int l = threadIdx.x & 63, lq = l >> 4;
-        const IO *Y = ws_unit<IO, D>(wsb, u), *KT = Y + 2 * C * D, *UzT = Y + 3 * C * D;
+        const size_t u = src.u0 + c;
+        const IO *Y = src.ws + u * chunk_ws_io_elems(D, CHAN), *UzT = Y + ws_off_uz(D, CHAN);
+        const IO *KT = CHAN ? Y + 2 * C * D : src.kT + (size_t)c * D * C;
+        const float *tab = src.tab + u * kTab;
 #pragma unroll
         for (int tt = 0; tt < Sh::TPW; ++tt) {
             const int rt = w * Sh::TPW + tt;
@@ -642,30 +661,46 @@ struct ChainOps {  // Y rows and U_z columns of the wave's token tiles; Kend^T r
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
                 uz[tt][ct] = R4::load(UzT + ((size_t)(rt * (D / 16) + col0 / 16 + ct) * 64 + l) * 4);
+            if constexpr (!CHAN) er[tt] = load4f(tab + C + rt * 16 + 4 * lq);
         }
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
             const int ch0 = 32 * w + 16 * rt;
 #pragma unroll
             for (int ks = 0; ks < Sh::KC; ++ks) ka[rt][ks] = load_frag(KT, ch0 / 16, ks, C);
-            g4[rt] = load4f(wsg + u * D + ch0 + 4 * lq);
+            if constexpr (CHAN) g4[rt] = load4f(tab + ch0 + 4 * lq);
+            else { const float gm = tab[C - 1]; g4[rt] = f32x4{gm, gm, gm, gm}; }
         }
     }
 };
 
-template <typename IO, int D, int NCT>
-struct OutOps {  // Q~ and A rows of the wave's token tiles
+template <typename IO, int D, int NCT, bool CHAN>
+struct OutOps {  // Q~ (q) and A rows of the wave's token tiles
     using Sh = SweepShape<IO, D, NCT>;
     using F = typename Sh::M::Frag;
     F qa[Sh::TPW][Sh::KD], aa[Sh::TPW][Sh::KC];
+    f32x4 eg[CHAN ? 1 : Sh::TPW];    // exp(G) of the wave's token rows (scalar decay)
 
-    __device__ __forceinline__ void load(const IO *wsb, size_t u, int w) {
-        const IO *Qt = ws_unit<IO, D>(wsb, u) + C * D, *A = ws_unit<IO, D>(wsb, u) + 4 * C * D;
+    __device__ __forceinline__ void load(const SweepSrc<IO> &src, int c, int n_valid, int w) {
+        constexpr int KS = Sh::M::KS, FE = KS / 4;
+        const int l = threadIdx.x & 63, lq = l >> 4;
+        const size_t u = src.u0 + c;
+        const IO *unit = src.ws + u * chunk_ws_io_elems(D, CHAN), *A = unit + ws_off_a(D, CHAN);
 #pragma unroll
         for (int tt = 0; tt < Sh::TPW; ++tt) {
             const int rt = w * Sh::TPW + tt;
+            if constexpr (CHAN) {
 #pragma unroll
-            for (int ks = 0; ks < Sh::KD; ++ks) qa[tt][ks] = load_frag(Qt, rt, ks, D);
+                for (int ks = 0; ks < Sh::KD; ++ks) qa[tt][ks] = load_frag(unit + C * D, rt, ks, D);
+            } else {
+                // q rows of this chunk straight from the input (rows past the end clamped; never stored)
+                const int t = min(rt * 16 + (l & 15), n_valid - 1);
+                const IO *qr = src.q + ((size_t)c * C + t) * src.qstride + FE * (l >> 4);
+#pragma unroll
+                for (int ks = 0; ks < Sh::KD; ++ks)
+                    qa[tt][ks] = *reinterpret_cast<const F *>(qr + ks * KS);
+                eg[tt] = load4f(src.tab + u * kTab + rt * 16 + 4 * lq);
+            }
 #pragma unroll
             for (int ks = 0; ks < Sh::KC; ++ks) aa[tt][ks] = load_frag(A, rt, ks, C);
         }
@@ -673,9 +708,9 @@ struct OutOps {  // Q~ and A rows of the wave's token tiles
 };
 
 // One chunk on a chain wave.
-template <typename IO, int D, int NCT>
-__device__ __forceinline__ void chain_chunk(const ChainOps<IO, D, NCT> &op, f32x4 (&S)[2][NCT], IO *sST, IO *sUT,
-                                            int w) {
+template <typename IO, int D, int NCT, bool CHAN>
+__device__ __forceinline__ void chain_chunk(const ChainOps<IO, D, NCT, CHAN> &op, f32x4 (&S)[2][NCT], IO *sST,
+                                            IO *sUT, IO *sUK, int w) {
     using Sh = SweepShape<IO, D, NCT>;
     using M = typename Sh::M;
     using F = typename M::Frag;
@@ -699,15 +734,19 @@ __device__ __forceinline__ void chain_chunk(const ChainOps<IO, D, NCT> &op, f32x
             for (int ct = 0; ct < NCT; ++ct)
                 accP[ct] = M::mma(accP[ct], op.ya[tt][ks], M::load(sST + 16 * ct * LS + ks * KS, LS));
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-            store4f(sUT + (16 * ct + lr) * LU + T0 + 4 * lq, Raw4<IO>::widen(op.uz[tt][ct]) - accP[ct]);
+        for (int ct = 0; ct < NCT; ++ct) {
+            const f32x4 U = Raw4<IO>::widen(op.uz[tt][ct]) - accP[ct];
+            store4f(sUT + (16 * ct + lr) * LU + T0 + 4 * lq, U);
+            if constexpr (!CHAN) store4f(sUK + (16 * ct + lr) * LU + T0 + 4 * lq, U * op.er[tt]);
+        }
     }
     __syncthreads();  // U^T is shared
+    const IO *sU = CHAN ? sUT : sUK;
     F ub[Sh::KC][NCT];
 #pragma unroll
     for (int ks = 0; ks < Sh::KC; ++ks)
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) ub[ks][ct] = M::load(sUT + 16 * ct * LU + ks * KS, LU);
+        for (int ct = 0; ct < NCT; ++ct) ub[ks][ct] = M::load(sU + 16 * ct * LU + ks * KS, LU);
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
@@ -723,8 +762,8 @@ __device__ __forceinline__ void chain_chunk(const ChainOps<IO, D, NCT> &op, f32x
 // the chunk may hold fewer than C tokens (only the last one), so output rows
 // are stored under a predicate; every other chunk stores unconditionally,
 // which keeps the number of memory operations in flight static.
-template <typename IO, int D, int NCT, bool TAIL>
-__device__ __forceinline__ void out_chunk(const OutOps<IO, D, NCT> &op, const IO *sST, const IO *sUT, IO *sO,
+template <typename IO, int D, int NCT, bool CHAN, bool TAIL>
+__device__ __forceinline__ void out_chunk(const OutOps<IO, D, NCT, CHAN> &op, const IO *sST, const IO *sUT, IO *sO,
                                           IO *orow0, size_t orow_stride, int n_valid, float scale, int w) {
     using Sh = SweepShape<IO, D, NCT>;
     using M = typename Sh::M;
@@ -742,6 +781,9 @@ __device__ __forceinline__ void out_chunk(const OutOps<IO, D, NCT> &op, const IO
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
                 accR[tt][ct] = M::mma(accR[tt][ct], op.qa[tt][ks], M::load(sST + 16 * ct * LS + ks * KS, LS));
+        if constexpr (!CHAN)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) accR[tt][ct] *= op.eg[tt];
     }
     __syncthreads();  // U^T is shared
     F ub[Sh::KC][NCT];
@@ -776,13 +818,14 @@ __device__ __forceinline__ void out_chunk(const OutOps<IO, D, NCT> &op, const IO
     }
 }
 
-template <typename IO, int D, int NCT, int PF>
+template <typename IO, int D, int NCT, int PF, bool CHAN>
 __global__ __launch_bounds__(4 * D) void chunk_sweep(ChunkArgs a, int NVT, int G) {
     using Sh = SweepShape<IO, D, NCT>;
     constexpr int BV = Sh::BV, LS = Sh::LS, LU = Sh::LU, LO = Sh::LO, NWC = Sh::NWC;
-    __shared__ __align__(16) IO sST[BV * LS];  // S_c^T in the io dtype
-    __shared__ __align__(16) IO sUT[BV * LU];  // U^T in the io dtype
-    __shared__ __align__(16) IO sO[C * LO];    // output rows (each output wave stages its own)
+    __shared__ __align__(16) IO sST[BV * LS];                 // S_c^T in the io dtype
+    __shared__ __align__(16) IO sUT[BV * LU];                 // U^T in the io dtype
+    __shared__ __align__(16) IO sUK[CHAN ? 1 : BV * LU];      // (Diag(exp(G_end - G)) U)^T (scalar decay)
+    __shared__ __align__(16) IO sO[C * LO];                   // output rows (each output wave stages its own)
 
     // Work index: blocks that share an XCD (blockIdx % 8) take consecutive
     // work items, so the value tiles of one head read its chunk factors
@@ -791,12 +834,17 @@ __global__ __launch_bounds__(4 * D) void chunk_sweep(ChunkArgs a, int NVT, int G
     const int wi = (x & 7) * (int)(gridDim.x >> 3) + (x >> 3);
     if (wi >= G) return;
     const int bh = wi / NVT, vt = wi - (wi / NVT) * NVT, col0 = vt * BV;
-    const int b = bh / a.Hv, h = bh - (bh / a.Hv) * a.Hv;
+    const int b = bh / a.Hv, h = bh - (bh / a.Hv) * a.Hv, hq = h / (a.Hv / a.Hqk);
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63, lr = l & 15, lq = l >> 4;
-
-    const IO *wsb = static_cast<const IO *>(a.ws_io);
-    const size_t u0 = (size_t)bh * a.NC;
     const int NC = a.NC;
+
+    SweepSrc<IO> src;
+    src.ws = static_cast<const IO *>(a.ws_io);
+    src.tab = a.ws_tab;
+    src.u0 = (size_t)bh * NC;
+    src.kT = CHAN ? nullptr : static_cast<const IO *>(a.ws_kT) + (size_t)(b * a.Hqk + hq) * NC * (D * C);
+    src.q = static_cast<const IO *>(a.q) + ((size_t)b * a.T * a.Hqk + hq) * D;
+    src.qstride = a.Hqk * D;
 
     if (wv < NWC) {  // ---- chain wave ----
         const int w = wv;
@@ -811,20 +859,20 @@ __global__ __launch_bounds__(4 * D) void chunk_sweep(ChunkArgs a, int NVT, int G
                     S[rt][ct][r] = a.S0 ? a.S0[((size_t)bh * D + ch) * D + col] : 0.f;
                 }
         if (NC > 0) {
-            ChainOps<IO, D, NCT> ring[PF];
+            ChainOps<IO, D, NCT, CHAN> ring[PF];
 #pragma unroll
-            for (int j = 0; j < PF; ++j) ring[j].load(wsb, a.ws_gamma, u0 + min(j, NC - 1), w, col0);
+            for (int j = 0; j < PF; ++j) ring[j].load(src, min(j, NC - 1), w, col0);
             int c = 0;
             for (; c + PF <= NC - 1; c += PF) {
 #pragma unroll
                 for (int j = 0; j < PF; ++j) {
-                    chain_chunk<IO, D, NCT>(ring[j], S, sST, sUT, w);
-                    ring[j].load(wsb, a.ws_gamma, u0 + min(c + j + PF, NC - 1), w, col0);
+                    chain_chunk<IO, D, NCT, CHAN>(ring[j], S, sST, sUT, sUK, w);
+                    ring[j].load(src, min(c + j + PF, NC - 1), w, col0);
                 }
             }
 #pragma unroll
             for (int j = 0; j < PF; ++j)
-                if (c + j < NC) chain_chunk<IO, D, NCT>(ring[j], S, sST, sUT, w);
+                if (c + j < NC) chain_chunk<IO, D, NCT, CHAN>(ring[j], S, sST, sUT, sUK, w);
         }
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
@@ -839,24 +887,26 @@ __global__ __launch_bounds__(4 * D) void chunk_sweep(ChunkArgs a, int NVT, int G
         const int w = wv - NWC;
         const size_t orow_stride = (size_t)a.Hv * D;
         IO *obase = static_cast<IO *>(a.o) + ((size_t)b * a.T * a.Hv + h) * D + col0;
-        OutOps<IO, D, NCT> ring[PF];
+        const auto nv = [&](int cj) { return min(C, a.T - cj * C); };
+        OutOps<IO, D, NCT, CHAN> ring[PF];
 #pragma unroll
-        for (int j = 0; j < PF; ++j) ring[j].load(wsb, u0 + min(j, NC - 1), w);
+        for (int j = 0; j < PF; ++j) ring[j].load(src, min(j, NC - 1), nv(min(j, NC - 1)), w);
         int c = 0;
         for (; c + PF <= NC - 1; c += PF) {
 #pragma unroll
             for (int j = 0; j < PF; ++j) {
-                out_chunk<IO, D, NCT, false>(ring[j], sST, sUT, sO, obase + (size_t)(c + j) * C * orow_stride,
-                                             orow_stride, C, a.scale, w);
-                ring[j].load(wsb, u0 + min(c + j + PF, NC - 1), w);
+                out_chunk<IO, D, NCT, CHAN, false>(ring[j], sST, sUT, sO, obase + (size_t)(c + j) * C * orow_stride,
+                                                   orow_stride, C, a.scale, w);
+                const int cn = min(c + j + PF, NC - 1);
+                ring[j].load(src, cn, nv(cn), w);
             }
         }
 #pragma unroll
         for (int j = 0; j < PF; ++j) {
             const int cj = c + j;
             if (cj < NC)
-                out_chunk<IO, D, NCT, true>(ring[j], sST, sUT, sO, obase + (size_t)cj * C * orow_stride, orow_stride,
-                                            a.T - cj * C, a.scale, w);
+                out_chunk<IO, D, NCT, CHAN, true>(ring[j], sST, sUT, sO, obase + (size_t)cj * C * orow_stride,
+                                                  orow_stride, nv(cj), a.scale, w);
         }
     }
 }
@@ -912,7 +962,10 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t s) {
     const int G = a.B * a.Hv * NVT;
     const int grid = (G + 7) / 8 * 8;
     constexpr int PF = sizeof(IO) == 2 ? SWEEP_PF : 1;  // prefetch depth (fp32 fragments are 2x larger)
-    hipLaunchKernelGGL((chunk_sweep<IO, D, NCT, PF>), dim3(grid), dim3(4 * D), 0, s, a, NVT, G);
+    if (a.decay == DECAY_CHANNEL)
+        hipLaunchKernelGGL((chunk_sweep<IO, D, NCT, PF, true>), dim3(grid), dim3(4 * D), 0, s, a, NVT, G);
+    else
+        hipLaunchKernelGGL((chunk_sweep<IO, D, NCT, PF, false>), dim3(grid), dim3(4 * D), 0, s, a, NVT, G);
     return hipGetLastError();
 }
 

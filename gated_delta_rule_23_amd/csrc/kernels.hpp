@@ -30,19 +30,38 @@ struct ChunkArgs {
     const float *S0;         // [B,Hv,D,D] or null
     void *o;                 // [B,T,Hv,D]
     float *ST;               // [B,Hv,D,D]
-    void *ws_io;             // per chunk unit: Y, Q~ (C x D), Kend^T, U_z^T (D x C), A (C x C), io dtype
-    float *ws_gamma;         // per chunk unit: end-of-chunk decay, D floats
+    void *ws_io;             // per chunk unit, io dtype, matrix-core fragment order: Y (C x D); with
+                             // per-channel decay also Q~ (C x D) and Kend^T (D x C); U_z^T (D x C); A (C x C)
+    float *ws_tab;           // per chunk unit, kTab floats: per-channel decay: gamma (D);
+                             // otherwise exp(G_t) and exp(G_end - G_t) (C each)
+    void *ws_kT;             // scalar or no decay: k^T (D x C, fragment order) per (sequence, QK head, chunk)
     int B, T, Hqk, Hv, decay, NC;
     float scale;
 };
 
-// Elements of the io-dtype workspace per chunk unit, and the byte layout.
-__host__ __device__ inline size_t chunk_ws_io_elems(int D) { return (size_t)4 * kChunk * D + (size_t)kChunk * kChunk; }
+constexpr int kTab = 2 * kChunk;  // floats per chunk unit in ws_tab (>= D for every supported D)
+
+// Workspace layout. With a scalar decay (or none) the queries and the
+// end-of-chunk keys are not stored per V head: the sweep reads q directly and
+// one k^T per QK head, and applies the per-token decay factors itself.
+__host__ __device__ inline size_t chunk_ws_io_elems(int D, bool chan) {
+    return (size_t)(chan ? 4 : 2) * kChunk * D + (size_t)kChunk * kChunk;
+}
+__host__ __device__ inline size_t ws_off_uz(int D, bool chan) { return (size_t)(chan ? 3 : 1) * kChunk * D; }
+__host__ __device__ inline size_t ws_off_a(int D, bool chan) { return (size_t)(chan ? 4 : 2) * kChunk * D; }
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-inline size_t chunk_ws_bytes(int B, int Hv, int NC, int D, int io) {
+struct ChunkWsLayout {
+    size_t io_bytes, tab_bytes, kT_bytes;
+    size_t total() const { return io_bytes + tab_bytes + kT_bytes; }
+};
+inline ChunkWsLayout chunk_ws_layout(int B, int Hqk, int Hv, int NC, int D, int io, bool chan) {
     const size_t units = (size_t)B * Hv * NC;
     const size_t esz = io == IO_BF16 ? 2 : 4;
-    return align256(units * chunk_ws_io_elems(D) * esz) + units * D * sizeof(float);
+    ChunkWsLayout L;
+    L.io_bytes = align256(units * chunk_ws_io_elems(D, chan) * esz);
+    L.tab_bytes = align256(units * kTab * sizeof(float));
+    L.kT_bytes = chan ? 0 : align256((size_t)B * Hqk * NC * D * kChunk * esz);
+    return L;
 }
 
 hipError_t launch_decode(int io, int D, const DecodeArgs &a, hipStream_t s);

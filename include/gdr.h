@@ -109,10 +109,13 @@ int gdr_state_free(float *state);
 
 /* Device workspace bytes gdr_chunk_fwd needs for `desc`; needs no GPU.
  * The workspace holds, per (sequence, V head, chunk), the chunk's factors
- * that do not depend on the state: the erase-side WY factor Y and the decayed
- * queries (C x d_k each), the keys decayed to the chunk end and the
- * write-side factor U_z (d_k x C and d_v x C), the in-chunk read matrix A
- * (C x C), all in the io dtype, plus the end-of-chunk decay (d_k float32). */
+ * that do not depend on the state: the erase-side WY factor Y (C x d_k), the
+ * write-side factor U_z (d_v x C) and the in-chunk read matrix A (C x C), in
+ * the io dtype; with per-channel decay also the decayed queries (C x d_k) and
+ * the keys decayed to the chunk end (d_k x C), and the end-of-chunk decay
+ * (d_k float32); with a scalar decay (or none) instead two per-token decay
+ * tables (2 C float32) and one k^T (d_k x C, io dtype) per (sequence, QK
+ * head, chunk). Returns 0 bytes when B or T is 0. */
 int gdr_chunk_workspace_bytes(const gdr_desc *desc, size_t *bytes);
 
 /* Chunkwise-parallel prefill over T tokens: "Chunkwise KDA" and "Pipeline

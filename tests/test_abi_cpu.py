@@ -40,11 +40,22 @@ def test_state_size_pin():
     assert gdr.gdr_state_bytes(0, 48, 128, 128) == 0
 
 
+def _a256(x):
+    return (x + 255) // 256 * 256
+
+
 def test_workspace_bytes():
+    """Scalar decay: Y, U_z^T and A per (sequence, V head, chunk), two per-token
+    decay tables, and one k^T per (sequence, QK head, chunk). Per-channel decay:
+    also Q~ and Kend^T per unit, and gamma in the table."""
+    NC, units = 64, 48 * 64
     d = gdr.make_desc(1, 4096, 16, 48, 128, gdr.GDR_BF16, gdr.GDR_DECAY_SCALAR)
-    units = 48 * 64
-    io = units * (4 * 64 * 128 + 64 * 64) * 2   # Y, Q~, Kend^T, U_z^T (64 x 128) and A (64 x 64), bf16
-    assert gdr.gdr_chunk_workspace_bytes(d) == ((io + 255) // 256) * 256 + units * 128 * 4
+    io = units * (2 * 64 * 128 + 64 * 64) * 2
+    expect = _a256(io) + _a256(units * 128 * 4) + _a256(16 * NC * 128 * 64 * 2)
+    assert gdr.gdr_chunk_workspace_bytes(d) == expect
+    dc = gdr.make_desc(1, 4096, 16, 48, 128, gdr.GDR_BF16, gdr.GDR_DECAY_CHANNEL)
+    io = units * (4 * 64 * 128 + 64 * 64) * 2
+    assert gdr.gdr_chunk_workspace_bytes(dc) == _a256(io) + _a256(units * 128 * 4)
     d0 = gdr.make_desc(1, 0, 16, 48, 128, gdr.GDR_BF16, gdr.GDR_DECAY_SCALAR)
     assert gdr.gdr_chunk_workspace_bytes(d0) == 0
 
