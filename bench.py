@@ -34,14 +34,19 @@ TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_source_hash():
-    """sha256 over the kernel sources, to tell whether recorded memory
-    counters still describe the kernels as built."""
+    """sha256 over the kernel sources with comments and blank space removed, to
+    tell whether recorded memory counters still describe the kernels as built."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
         if name.endswith((".hip", ".hpp")):
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+            with open(os.path.join(CSRC, name)) as f:
+                src = f.read()
+            src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+            src = re.sub(r"//[^\n]*", " ", src)
+            src = " ".join(src.split())
+            h.update(name.encode() + b"\0" + src.encode())
     return h.hexdigest()
 
 

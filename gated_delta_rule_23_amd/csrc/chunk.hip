@@ -20,8 +20,10 @@
 // Two kernels. chunk_prep is parallel over every (sequence, V head, chunk):
 // it does everything that does not depend on the state -- prefix sums, decay
 // absorption, both Gram products, the triangular solve for Y and U_z -- and
-// stores Y, Q~, Kend^T, U_z^T, A and gamma in a workspace, each matrix in
-// the order the sweep's matrix-core operand loads read it. chunk_sweep is the
+// stores Y, U_z^T and A (with per-channel decay also Q~, Kend^T and gamma;
+// with a scalar decay per-token decay factors and one k^T per QK head) in a
+// workspace, each matrix in the order the sweep's matrix-core operand loads
+// read it. chunk_sweep is the
 // single sequential pass over chunks: per (sequence, V head, value tile) it
 // keeps the fp32 state in matrix-core accumulator registers and per chunk
 // does U = U_z - Y S_c, O = s (Q~ S_c + A U) and
