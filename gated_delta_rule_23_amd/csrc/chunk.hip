@@ -247,39 +247,50 @@ struct PrepIn {
     f32x4 g[CHAN ? TPT * V / 4 : 1];
     float betal, gs;
 
+    // The loads are issued in three parts (PART 0: q, k; 1: v, per-channel g;
+    // 2: b, w, beta, scalar g) at different points of the previous unit, so
+    // the memory queue drains behind computation instead of stalling a burst.
+    template <int PART>
     __device__ __forceinline__ void load(const ChunkArgs &a, int u, int co, int grp) {
         const int NC = a.NC, c = u % NC, bh = u / NC, b = bh / a.Hv, h = bh - b * a.Hv;
         const int hq = h / (a.Hv / a.Hqk), t0 = c * C, n = min(C, a.T - t0);
         const int l = threadIdx.x & 63;
         const size_t row0 = (size_t)b * a.T + t0;  // first token row of the chunk
-        const IO *qb = static_cast<const IO *>(a.q) + (row0 * a.Hqk + hq) * D + V * co;
-        const IO *kb = static_cast<const IO *>(a.k) + (row0 * a.Hqk + hq) * D + V * co;
+        const size_t qko = (row0 * a.Hqk + hq) * D + V * co;
         const size_t vo = (row0 * a.Hv + h) * D + V * co;
         const size_t sqk = (size_t)a.Hqk * D, sv = (size_t)a.Hv * D;  // token strides (elements)
 #pragma unroll
         for (int j = 0; j < TPT; ++j) {
             const int t = min(TPT * grp + j, n - 1);  // clamped: padded tokens are zeroed at use
-            q[j] = ld16(qb + t * sqk);
-            k[j] = ld16(kb + t * sqk);
-            v[j] = ld16(static_cast<const IO *>(a.v) + vo + t * sv);
-            if constexpr (BW) {
+            if constexpr (PART == 0) {
+                q[j] = ld16(static_cast<const IO *>(a.q) + qko + t * sqk);
+                k[j] = ld16(static_cast<const IO *>(a.k) + qko + t * sqk);
+            }
+            if constexpr (PART == 1) {
+                v[j] = ld16(static_cast<const IO *>(a.v) + vo + t * sv);
+                if constexpr (CHAN)
+#pragma unroll
+                    for (int i = 0; i < V / 4; ++i) g[j * (V / 4) + i] = load4f(a.g + vo + t * sv + 4 * i);
+            }
+            if constexpr (PART == 2 && BW) {
                 bg[j] = ld16(static_cast<const IO *>(a.bg) + vo + t * sv);
                 wg[j] = ld16(static_cast<const IO *>(a.wg) + vo + t * sv);
             }
-            if constexpr (CHAN)
-#pragma unroll
-                for (int i = 0; i < V / 4; ++i) g[j * (V / 4) + i] = load4f(a.g + vo + t * sv + 4 * i);
         }
-        if (threadIdx.x < 64) {  // wave 0: one token per lane
-            const size_t tl = (row0 + min(l, n - 1)) * a.Hv + h;
-            if constexpr (!BW) betal = a.beta[tl];
-            if constexpr (!CHAN) gs = a.decay == DECAY_SCALAR ? a.g[tl] : 0.f;
-        }
+        if constexpr (PART == 2)
+            if (threadIdx.x < 64) {  // wave 0: one token per lane
+                const size_t tl = (row0 + min(l, n - 1)) * a.Hv + h;
+                if constexpr (!BW) betal = a.beta[tl];
+                if constexpr (!CHAN) gs = a.decay == DECAY_SCALAR ? a.g[tl] : 0.f;
+            }
+    }
+    __device__ __forceinline__ void load_all(const ChunkArgs &a, int u, int co, int grp) {
+        load<0>(a, u, co, grp);
+        load<1>(a, u, co, grp);
+        load<2>(a, u, co, grp);
     }
 };
 
-// Workgroups per compute unit: the scalar-decay, tied-gate variant fits two
-// in shared memory and registers, which hides each one's latencies.
 template <typename IO, int D, bool CHAN, bool BW>
 constexpr int prep_occupancy() { return (CHAN || BW) ? 1 : 2; }
 
@@ -323,7 +334,7 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
     const int units = a.B * a.Hv * a.NC;
 
     PrepIn<IO, D, CHAN, BW> in;
-    if ((int)blockIdx.x < units) in.load(a, blockIdx.x, co, grp);
+    if ((int)blockIdx.x < units) in.load_all(a, blockIdx.x, co, grp);
 
     for (int u = blockIdx.x; u < units; u += gridDim.x) {
         const int NC = a.NC, c = u % NC, bh = u / NC, h = bh % a.Hv, grpsz = a.Hv / a.Hqk;
@@ -443,8 +454,9 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
 #pragma unroll
                 for (int i = 0; i < V / 4; ++i)
                     store4f(tab + V * co + 4 * i, f32x4{eGend[4 * i], eGend[4 * i + 1], eGend[4 * i + 2], eGend[4 * i + 3]});
-        // The raw inputs are consumed: fetch the next unit's now.
-        if (u + (int)gridDim.x < units) in.load(a, u + gridDim.x, co, grp);
+        // The raw inputs are consumed: start fetching the next unit's.
+        const int un = u + (int)gridDim.x;
+        if (un < units) in.template load<0>(a, un, co, grp);
         __syncthreads();
 
         // ---- B. Gram products: 20 lower 16 x 16 tiles, 10 of T and 10 of A ----
@@ -516,6 +528,8 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
         }
         __syncthreads();
 
+        if (un < units) in.template load<1>(a, un, co, grp);
+
         // ---- C. A to the workspace; L = (I + T)^-1 ----
         for (int f = w; f < (C / 16) * (C / KS); f += NW) {
             const int rt = f / (C / KS), ks = f - rt * (C / KS);
@@ -562,6 +576,8 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
             }
         }
         __syncthreads();
+
+        if (un < units) in.template load<2>(a, un, co, grp);
 
         // ---- D. [Y | U_z] = L [E~ | Z] ----
         {
