@@ -157,6 +157,10 @@ int gdr_chunk_fwd(const gdr_desc *d, const void *q, const void *k, const void *v
     a.ws_io = workspace;
     a.ws_tab = reinterpret_cast<float *>(static_cast<char *>(workspace) + L.io_bytes);
     a.ws_kT = L.kT_bytes ? static_cast<char *>(workspace) + L.io_bytes + L.tab_bytes : nullptr;
+    a.ws_seg = L.seg_bytes ? reinterpret_cast<float *>(static_cast<char *>(workspace) + L.io_bytes + L.tab_bytes +
+                                                       L.kT_bytes)
+                           : nullptr;
+    gdr::chunk_segments(d->B, d->H_v, d->d_k, NC, a.P, a.L);
     a.B = d->B; a.T = d->T; a.Hqk = d->H_qk; a.Hv = d->H_v; a.decay = d->decay; a.NC = NC;
     a.scale = d->scale;
     hipError_t e = gdr::launch_chunk(io, d->d_k, a, static_cast<hipStream_t>(stream));

@@ -728,7 +728,7 @@ struct OutOps {  // Q~ (q) and A rows of the wave's token tiles
 // One chunk on a chain wave.
 template <typename IO, int D, int NCT, bool CHAN>
 __device__ __forceinline__ void chain_chunk(const ChainOps<IO, D, NCT, CHAN> &op, f32x4 (&S)[2][NCT], IO *sST,
-                                            IO *sUT, IO *sUK, int w) {
+                                            IO *sUT, IO *sUK, int w, bool zero_uz = false) {
     using Sh = SweepShape<IO, D, NCT>;
     using M = typename Sh::M;
     using F = typename M::Frag;
@@ -753,7 +753,7 @@ __device__ __forceinline__ void chain_chunk(const ChainOps<IO, D, NCT, CHAN> &op
                 accP[ct] = M::mma(accP[ct], op.ya[tt][ks], M::load(sST + 16 * ct * LS + ks * KS, LS));
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
-            const f32x4 U = Raw4<IO>::widen(op.uz[tt][ct]) - accP[ct];
+            const f32x4 U = (zero_uz ? zero4() : Raw4<IO>::widen(op.uz[tt][ct])) - accP[ct];
             store4f(sUT + (16 * ct + lr) * LU + T0 + 4 * lq, U);
             if constexpr (!CHAN) store4f(sUK + (16 * ct + lr) * LU + T0 + 4 * lq, U * op.er[tt]);
         }
@@ -851,17 +851,21 @@ __global__ __launch_bounds__(4 * D) void chunk_sweep(ChunkArgs a, int NVT, int G
     const int x = blockIdx.x;
     const int wi = (x & 7) * (int)(gridDim.x >> 3) + (x >> 3);
     if (wi >= G) return;
-    const int bh = wi / NVT, vt = wi - (wi / NVT) * NVT, col0 = vt * BV;
+    // Work item ((sequence, V head), segment, value tile); one segment unless the sweep is split.
+    const int vt = wi % NVT, bs = wi / NVT, sg = bs % a.P, bh = bs / a.P, col0 = vt * BV;
     const int b = bh / a.Hv, h = bh - (bh / a.Hv) * a.Hv, hq = h / (a.Hv / a.Hqk);
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63, lr = l & 15, lq = l >> 4;
-    const int NC = a.NC;
+    const int cb = sg * a.L, NC = min(a.L, a.NC - cb);  // this segment's chunks [cb, cb + NC)
+    // Entry state: S0 for the first segment, else the one the segment scan found.
+    const float *Sin = sg == 0 ? a.S0 : a.ws_seg + ((size_t)(bh * (a.P - 1) + sg - 1) * 3 + 2) * D * D;
+    const bool last = sg == a.P - 1;
 
     SweepSrc<IO> src;
     src.ws = static_cast<const IO *>(a.ws_io);
     src.tab = a.ws_tab;
-    src.u0 = (size_t)bh * NC;
-    src.kT = CHAN ? nullptr : static_cast<const IO *>(a.ws_kT) + (size_t)(b * a.Hqk + hq) * NC * (D * C);
-    src.q = static_cast<const IO *>(a.q) + ((size_t)b * a.T * a.Hqk + hq) * D;
+    src.u0 = (size_t)bh * a.NC + cb;
+    src.kT = CHAN ? nullptr : static_cast<const IO *>(a.ws_kT) + ((size_t)(b * a.Hqk + hq) * a.NC + cb) * (D * C);
+    src.q = static_cast<const IO *>(a.q) + (((size_t)b * a.T + (size_t)cb * C) * a.Hqk + hq) * D;
     src.qstride = a.Hqk * D;
 
     if (wv < NWC) {  // ---- chain wave ----
@@ -874,7 +878,7 @@ __global__ __launch_bounds__(4 * D) void chunk_sweep(ChunkArgs a, int NVT, int G
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int ch = 32 * w + 16 * rt + 4 * lq + r, col = col0 + 16 * ct + lr;
-                    S[rt][ct][r] = a.S0 ? a.S0[((size_t)bh * D + ch) * D + col] : 0.f;
+                    S[rt][ct][r] = Sin ? Sin[(sg == 0 ? (size_t)bh * D * D : 0) + (size_t)ch * D + col] : 0.f;
                 }
         if (NC > 0) {
             ChainOps<IO, D, NCT, CHAN> ring[PF];
@@ -892,20 +896,21 @@ __global__ __launch_bounds__(4 * D) void chunk_sweep(ChunkArgs a, int NVT, int G
             for (int j = 0; j < PF; ++j)
                 if (c + j < NC) chain_chunk<IO, D, NCT, CHAN>(ring[j], S, sST, sUT, sUK, w);
         }
+        if (last)
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+            for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
+                for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int ch = 32 * w + 16 * rt + 4 * lq + r, col = col0 + 16 * ct + lr;
-                    a.ST[((size_t)bh * D + ch) * D + col] = S[rt][ct][r];
-                }
+                    for (int r = 0; r < 4; ++r) {
+                        const int ch = 32 * w + 16 * rt + 4 * lq + r, col = col0 + 16 * ct + lr;
+                        a.ST[((size_t)bh * D + ch) * D + col] = S[rt][ct][r];
+                    }
     } else if (NC > 0) {  // ---- output wave: same chunk sequence, same barriers ----
         const int w = wv - NWC;
         const size_t orow_stride = (size_t)a.Hv * D;
-        IO *obase = static_cast<IO *>(a.o) + ((size_t)b * a.T * a.Hv + h) * D + col0;
-        const auto nv = [&](int cj) { return min(C, a.T - cj * C); };
+        IO *obase = static_cast<IO *>(a.o) + (((size_t)b * a.T + (size_t)cb * C) * a.Hv + h) * D + col0;
+        const auto nv = [&](int cj) { return min(C, a.T - (cb + cj) * C); };
         OutOps<IO, D, NCT, CHAN> ring[PF];
 #pragma unroll
         for (int j = 0; j < PF; ++j) ring[j].load(src, min(j, NC - 1), nv(min(j, NC - 1)), w);
@@ -926,6 +931,106 @@ __global__ __launch_bounds__(4 * D) void chunk_sweep(ChunkArgs a, int NVT, int G
                 out_chunk<IO, D, NCT, CHAN, true>(ring[j], sST, sUT, sO, obase + (size_t)cj * C * orow_stride,
                                                   orow_stride, nv(cj), a.scale, w);
         }
+    }
+}
+
+// Segmented sweep, first pass: for every segment but the last, run the state
+// chain from a zero entry state to get the segment's end state N, and on d_k
+// more columns from the identity with U_z = 0 to get its transition M (the
+// state after the segment is M S_in + N). Chain waves only.
+template <typename IO, int D, int NCT, int PF, bool CHAN>
+__global__ __launch_bounds__(2 * D) void chunk_seg_state(ChunkArgs a, int NVT, int G) {
+    using Sh = SweepShape<IO, D, NCT>;
+    constexpr int BV = Sh::BV, LS = Sh::LS, LU = Sh::LU;
+    __shared__ __align__(16) IO sST[BV * LS];
+    __shared__ __align__(16) IO sUT[BV * LU];
+    __shared__ __align__(16) IO sUK[CHAN ? 1 : BV * LU];
+    const int x = blockIdx.x;
+    const int wi = (x & 7) * (int)(gridDim.x >> 3) + (x >> 3);
+    if (wi >= G) return;
+    const int NT2 = 2 * NVT;  // value tiles of N, then of M (d_k = d_v)
+    const int t = wi % NT2, bs = wi / NT2, sg = bs % (a.P - 1), bh = bs / (a.P - 1);
+    const bool mpart = t >= NVT;
+    const int col0 = (mpart ? t - NVT : t) * BV;
+    const int b = bh / a.Hv, h = bh - (bh / a.Hv) * a.Hv, hq = h / (a.Hv / a.Hqk);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63, lr = l & 15, lq = l >> 4;
+    const int cb = sg * a.L, NC = a.L;  // a full segment: only the last one can be shorter
+
+    SweepSrc<IO> src;
+    src.ws = static_cast<const IO *>(a.ws_io);
+    src.tab = a.ws_tab;
+    src.u0 = (size_t)bh * a.NC + cb;
+    src.kT = CHAN ? nullptr : static_cast<const IO *>(a.ws_kT) + ((size_t)(b * a.Hqk + hq) * a.NC + cb) * (D * C);
+    src.q = nullptr;
+    src.qstride = 0;
+
+    f32x4 S[2][NCT];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int ch = 32 * w + 16 * rt + 4 * lq + r, col = col0 + 16 * ct + lr;
+                S[rt][ct][r] = mpart && ch == col ? 1.f : 0.f;
+            }
+    ChainOps<IO, D, NCT, CHAN> ring[PF];
+#pragma unroll
+    for (int j = 0; j < PF; ++j) ring[j].load(src, min(j, NC - 1), w, col0);
+    int c = 0;
+    for (; c + PF <= NC - 1; c += PF) {
+#pragma unroll
+        for (int j = 0; j < PF; ++j) {
+            chain_chunk<IO, D, NCT, CHAN>(ring[j], S, sST, sUT, sUK, w, mpart);
+            ring[j].load(src, min(c + j + PF, NC - 1), w, col0);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < PF; ++j)
+        if (c + j < NC) chain_chunk<IO, D, NCT, CHAN>(ring[j], S, sST, sUT, sUK, w, mpart);
+
+    float *dst = a.ws_seg + ((size_t)(bh * (a.P - 1) + sg) * 3 + (mpart ? 0 : 1)) * D * D;
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int ch = 32 * w + 16 * rt + 4 * lq + r, col = col0 + 16 * ct + lr;
+                dst[(size_t)ch * D + col] = S[rt][ct][r];
+            }
+}
+
+// Segmented sweep, scan over segments: S_in(s + 1) = M_s S_in(s) + N_s, fp32,
+// one workgroup per (sequence, V head, 16 state columns).
+template <int D>
+__global__ __launch_bounds__(256) void chunk_seg_combine(ChunkArgs a) {
+    constexpr int NTC = 16;
+    __shared__ float sIn[D * NTC];
+    const int bh = blockIdx.x / (D / NTC), c0 = (blockIdx.x % (D / NTC)) * NTC;
+    const int tid = threadIdx.x, j = tid % NTC, r0 = tid / NTC;  // column j; rows r0, r0 + 16, ...
+    for (int i = tid; i < D * NTC; i += 256)
+        sIn[i] = a.S0 ? a.S0[((size_t)bh * D + i / NTC) * D + c0 + i % NTC] : 0.f;
+    __syncthreads();
+    for (int s = 0; s < a.P - 1; ++s) {
+        const float *M = a.ws_seg + ((size_t)(bh * (a.P - 1) + s) * 3) * D * D, *N = M + D * D;
+        float *Sn = const_cast<float *>(M) + 2 * D * D;
+        float acc[D / 16];
+#pragma unroll
+        for (int k = 0; k < D / 16; ++k) {
+            const int r = r0 + 16 * k;
+            float x = N[(size_t)r * D + c0 + j];
+            for (int m = 0; m < D; ++m) x += M[(size_t)r * D + m] * sIn[m * NTC + j];
+            acc[k] = x;
+        }
+        __syncthreads();  // everyone has read S_in(s)
+#pragma unroll
+        for (int k = 0; k < D / 16; ++k) {
+            const int r = r0 + 16 * k;
+            sIn[r * NTC + j] = acc[k];
+            Sn[(size_t)r * D + c0 + j] = acc[k];
+        }
+        __syncthreads();
     }
 }
 
@@ -977,9 +1082,20 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     constexpr int NVT = D / (16 * NCT);
-    const int G = a.B * a.Hv * NVT;
-    const int grid = (G + 7) / 8 * 8;
     constexpr int PF = sizeof(IO) == 2 ? SWEEP_PF : 1;  // prefetch depth (fp32 fragments are 2x larger)
+    if (a.P > 1) {  // segmented: transitions and end states, then the scan over segments
+        const int G1 = a.B * a.Hv * (a.P - 1) * 2 * NVT;
+        const int grid1 = (G1 + 7) / 8 * 8;
+        if (a.decay == DECAY_CHANNEL)
+            hipLaunchKernelGGL((chunk_seg_state<IO, D, NCT, PF, true>), dim3(grid1), dim3(2 * D), 0, s, a, NVT, G1);
+        else
+            hipLaunchKernelGGL((chunk_seg_state<IO, D, NCT, PF, false>), dim3(grid1), dim3(2 * D), 0, s, a, NVT, G1);
+        hipLaunchKernelGGL((chunk_seg_combine<D>), dim3(a.B * a.Hv * (D / 16)), dim3(256), 0, s, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int G = a.B * a.Hv * a.P * NVT;
+    const int grid = (G + 7) / 8 * 8;
     if (a.decay == DECAY_CHANNEL)
         hipLaunchKernelGGL((chunk_sweep<IO, D, NCT, PF, true>), dim3(grid), dim3(4 * D), 0, s, a, NVT, G);
     else

@@ -35,7 +35,11 @@ struct ChunkArgs {
     float *ws_tab;           // per chunk unit, kTab floats: per-channel decay: gamma (D);
                              // otherwise exp(G_t) and exp(G_end - G_t) (C each)
     void *ws_kT;             // scalar or no decay: k^T (D x C, fragment order) per (sequence, QK head, chunk)
+    float *ws_seg;           // segmented sweep (P > 1): per (sequence, V head, segment < P - 1) the
+                             // segment's transition M (D x D), its end state from zero N (D x D), and the
+                             // entry state of the next segment (D x D), fp32
     int B, T, Hqk, Hv, decay, NC;
+    int P, L;                // sweep segments and their length in chunks (P = 1: one pass)
     float scale;
 };
 
@@ -51,9 +55,26 @@ __host__ __device__ inline size_t ws_off_uz(int D, bool chan) { return (size_t)(
 __host__ __device__ inline size_t ws_off_a(int D, bool chan) { return (size_t)(chan ? 4 : 2) * kChunk * D; }
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct ChunkWsLayout {
-    size_t io_bytes, tab_bytes, kT_bytes;
-    size_t total() const { return io_bytes + tab_bytes + kT_bytes; }
+    size_t io_bytes, tab_bytes, kT_bytes, seg_bytes;
+    size_t total() const { return io_bytes + tab_bytes + kT_bytes + seg_bytes; }
 };
+// Segments of the sequential sweep. When few (sequence, head, value tile)
+// work items would leave most of the device idle and the sequence is long,
+// the chunks are split into P segments that run in parallel from their true
+// entry states, found by a short scan over the segments' transitions. The
+// policy depends only on the shapes (sized for MI355X's 256 compute units),
+// so the workspace size needs no device query.
+constexpr int kSegCUs = 256, kSegMinChunks = 16, kSegMax = 8;
+inline void chunk_segments(int B, int Hv, int D, int NC, int &P, int &L) {
+    const long long items = (long long)B * Hv * (D / 32);
+    long long p = items > 0 ? kSegCUs / items : 1;
+    p = p < NC / kSegMinChunks ? p : NC / kSegMinChunks;
+    p = p < kSegMax ? p : kSegMax;
+    if (p < 2) { P = 1; L = NC; return; }
+    L = (int)((NC + p - 1) / p);
+    P = (NC + L - 1) / L;
+}
+
 inline ChunkWsLayout chunk_ws_layout(int B, int Hqk, int Hv, int NC, int D, int io, bool chan) {
     const size_t units = (size_t)B * Hv * NC;
     const size_t esz = io == IO_BF16 ? 2 : 4;
@@ -61,6 +82,9 @@ inline ChunkWsLayout chunk_ws_layout(int B, int Hqk, int Hv, int NC, int D, int 
     L.io_bytes = align256(units * chunk_ws_io_elems(D, chan) * esz);
     L.tab_bytes = align256(units * kTab * sizeof(float));
     L.kT_bytes = chan ? 0 : align256((size_t)B * Hqk * NC * D * kChunk * esz);
+    int P, Ls;
+    chunk_segments(B, Hv, D, NC, P, Ls);
+    L.seg_bytes = P > 1 ? align256((size_t)3 * B * Hv * (P - 1) * D * D * sizeof(float)) : 0;
     return L;
 }
 

@@ -115,6 +115,39 @@ def test_prefill_full_size_sampled(wl, heads, cols):
     assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(ST).all())
 
 
+def _sweep_segments(B, Hv, D, T):
+    """The library's split of a long sweep (256 compute units, at least 16
+    chunks per segment, at most 8 segments), restated to check that a test
+    takes the segmented path."""
+    NC = -(-T // 64)
+    p = min(256 // (B * Hv * (D // 32)), NC // 16, 8)
+    if p < 2:
+        return 1
+    L = -(-NC // p)
+    return -(-NC // L)
+
+
+@pytest.mark.parametrize("io,D,decay,gates,T,Hv", [
+    ("bf16", 64, "scalar", "beta", 2500, 2),
+    ("bf16", 128, "scalar", "bw", 4096, 2),
+    ("bf16", 128, "channel", "bw", 4113, 1),
+    ("f32", 32, "channel", "beta", 2100, 1),
+])
+def test_prefill_segmented_sweep(io, D, decay, gates, T, Hv):
+    """Long sequences with few heads split the sequential sweep into segments
+    that run in parallel from entry states found by a scan over the segments'
+    transitions; the result is still the token-by-token recurrence, here from
+    a non-zero initial state and with a partial last chunk in one case."""
+    assert _sweep_segments(1, Hv, D, T) > 1
+    wl = small_workload(io, D, decay, gates, T, B=1, Hqk=1, Hv=Hv, S0=True)
+    inp = gs.make_inputs(wl, seed=7)
+    say(f"segmented {wl.name}")
+    o, ST = gpu_prefill(inp, S0=to_dev(inp["S0"]))
+    o_ref, S_ref = oracle_prefill(inp)
+    assert rel_err(from_dev(o), o_ref) < TOL[io]
+    assert rel_err(from_dev(ST), S_ref) < TOL[io]
+
+
 # ---------------------------------------------------------------------------
 # Properties.
 
