@@ -48,6 +48,7 @@ constexpr int C = kChunk;
 #define SWEEP_NCT128 2
 #endif
 
+
 __host__ __device__ constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 __host__ __device__ constexpr size_t a16(size_t x) { return (x + 15) & ~(size_t)15; }
 
@@ -1001,36 +1002,47 @@ __global__ __launch_bounds__(2 * D) void chunk_seg_state(ChunkArgs a, int NVT, i
             }
 }
 
-// Segmented sweep, scan over segments: S_in(s + 1) = M_s S_in(s) + N_s, fp32,
-// one workgroup per (sequence, V head, 16 state columns).
+// Segmented sweep, scan over segments: S_in(s + 1) = M_s S_in(s) + N_s in fp32
+// on the matrix cores (v_mfma_f32_16x16x4_f32), one workgroup per (sequence,
+// V head, 16 state columns); S_in(s) stays in shared memory.
 template <int D>
 __global__ __launch_bounds__(256) void chunk_seg_combine(ChunkArgs a) {
     constexpr int NTC = 16;
-    __shared__ float sIn[D * NTC];
+    __shared__ __align__(16) float sIn[D * NTC];
     const int bh = blockIdx.x / (D / NTC), c0 = (blockIdx.x % (D / NTC)) * NTC;
-    const int tid = threadIdx.x, j = tid % NTC, r0 = tid / NTC;  // column j; rows r0, r0 + 16, ...
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, lr = l & 15, lg = l >> 4;
     for (int i = tid; i < D * NTC; i += 256)
         sIn[i] = a.S0 ? a.S0[((size_t)bh * D + i / NTC) * D + c0 + i % NTC] : 0.f;
-    __syncthreads();
+    constexpr int RPW = (D / 16 + 3) / 4;  // row tiles per wave
     for (int s = 0; s < a.P - 1; ++s) {
         const float *M = a.ws_seg + ((size_t)(bh * (a.P - 1) + s) * 3) * D * D, *N = M + D * D;
         float *Sn = const_cast<float *>(M) + 2 * D * D;
-        float acc[D / 16];
+        __syncthreads();  // S_in(s) complete
+        f32x4 acc[RPW];
 #pragma unroll
-        for (int k = 0; k < D / 16; ++k) {
-            const int r = r0 + 16 * k;
-            float x = N[(size_t)r * D + c0 + j];
-            for (int m = 0; m < D; ++m) x += M[(size_t)r * D + m] * sIn[m * NTC + j];
-            acc[k] = x;
+        for (int i = 0; i < RPW; ++i) {
+            const int rt = w + 4 * i;
+            if (rt < D / 16) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[i][r] = N[(size_t)(16 * rt + 4 * lg + r) * D + c0 + lr];
+                const float *Mr = M + (size_t)(16 * rt + lr) * D + lg;
+#pragma unroll 8
+                for (int ks = 0; ks < D / 4; ++ks)
+                    acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(Mr[4 * ks], sIn[(4 * ks + lg) * NTC + lr], acc[i], 0, 0, 0);
+            }
         }
         __syncthreads();  // everyone has read S_in(s)
 #pragma unroll
-        for (int k = 0; k < D / 16; ++k) {
-            const int r = r0 + 16 * k;
-            sIn[r * NTC + j] = acc[k];
-            Sn[(size_t)r * D + c0 + j] = acc[k];
+        for (int i = 0; i < RPW; ++i) {
+            const int rt = w + 4 * i;
+            if (rt < D / 16)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * rt + 4 * lg + r;
+                    sIn[row * NTC + lr] = acc[i][r];
+                    Sn[(size_t)row * D + c0 + lr] = acc[i][r];
+                }
         }
-        __syncthreads();
     }
 }
 
@@ -1084,12 +1096,13 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t s) {
     constexpr int NVT = D / (16 * NCT);
     constexpr int PF = sizeof(IO) == 2 ? SWEEP_PF : 1;  // prefetch depth (fp32 fragments are 2x larger)
     if (a.P > 1) {  // segmented: transitions and end states, then the scan over segments
-        const int G1 = a.B * a.Hv * (a.P - 1) * 2 * NVT;
+        constexpr int NCT1 = NCT, NVT1 = NVT;
+        const int G1 = a.B * a.Hv * (a.P - 1) * 2 * NVT1;
         const int grid1 = (G1 + 7) / 8 * 8;
         if (a.decay == DECAY_CHANNEL)
-            hipLaunchKernelGGL((chunk_seg_state<IO, D, NCT, PF, true>), dim3(grid1), dim3(2 * D), 0, s, a, NVT, G1);
+            hipLaunchKernelGGL((chunk_seg_state<IO, D, NCT1, PF, true>), dim3(grid1), dim3(2 * D), 0, s, a, NVT1, G1);
         else
-            hipLaunchKernelGGL((chunk_seg_state<IO, D, NCT, PF, false>), dim3(grid1), dim3(2 * D), 0, s, a, NVT, G1);
+            hipLaunchKernelGGL((chunk_seg_state<IO, D, NCT1, PF, false>), dim3(grid1), dim3(2 * D), 0, s, a, NVT1, G1);
         hipLaunchKernelGGL((chunk_seg_combine<D>), dim3(a.B * a.Hv * (D / 16)), dim3(256), 0, s, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
