@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <initializer_list>
 #include <string>
 
 #include "gdr.h"
@@ -82,6 +83,17 @@ int validate(const gdr_desc *d, bool prefill, const void *q, const void *k, cons
     return GDR_OK;
 }
 
+// The kernels read and write the io arrays, the state and the workspace with
+// 16-byte vector accesses; beta and a scalar decay are read per element.
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+int check_alignment(const gdr_desc *d, std::initializer_list<const void *> vec16, const float *g, const float *beta) {
+    for (const void *p : vec16)
+        if (p && !aligned(p, 16)) return fail(GDR_E_INVAL, "array pointers must be 16-byte aligned");
+    if (g && !aligned(g, d->decay == GDR_DECAY_CHANNEL ? 16 : 4)) return fail(GDR_E_INVAL, "g is misaligned");
+    if (beta && !aligned(beta, 4)) return fail(GDR_E_INVAL, "beta is misaligned");
+    return GDR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -141,6 +153,8 @@ int gdr_chunk_fwd(const gdr_desc *d, const void *q, const void *k, const void *v
     int rc = validate(d, true, q, k, v, g, beta, b, w, o);
     if (rc != GDR_OK) return rc;
     if (!ST) return fail(GDR_E_INVAL, "ST must be non-NULL");
+    rc = check_alignment(d, {q, k, v, b, w, o, S0, ST, workspace}, g, beta);
+    if (rc != GDR_OK) return rc;
     const int io = d->io_dtype == GDR_BF16 ? gdr::IO_BF16 : gdr::IO_F32;
     const int NC = (d->T + gdr::kChunk - 1) / gdr::kChunk;
     const gdr::ChunkWsLayout L = gdr::chunk_ws_layout(d->B, d->H_qk, d->H_v, NC, d->d_k, io, d->decay == GDR_DECAY_CHANNEL);
@@ -173,6 +187,8 @@ int gdr_decode_step(const gdr_desc *d, const void *q, const void *k, const void 
     int rc = validate(d, false, q, k, v, g, beta, b, w, o);
     if (rc != GDR_OK) return rc;
     if (!S) return fail(GDR_E_INVAL, "S must be non-NULL");
+    rc = check_alignment(d, {q, k, v, b, w, o, S}, g, beta);
+    if (rc != GDR_OK) return rc;
     if (d->B == 0) return ok();
     if ((long long)d->B * d->H_v > 0x7fffffffll) return fail(GDR_E_UNSUPPORTED, "B * H_v too large for one launch");
     gdr::DecodeArgs a{};

@@ -41,6 +41,9 @@
  *     S    : [B, H_v, d_k, d_v] float32; row i is key channel i, column j
  *            value channel j.
  *   For decode the T axis is absent (one token per sequence).
+ * - Alignment: every array pointer must be 16-byte aligned (the kernels use
+ *   16-byte vector accesses), except beta and a scalar-decay g, which need
+ *   4 bytes. A misaligned pointer is rejected with GDR_E_INVAL.
  * - V head h reads QK head h / (H_v / H_qk): each QK head serves a contiguous
  *   group of H_v / H_qk V heads.
  * - Gate modes: beta != NULL and b == w == NULL (tied), or beta == NULL and

@@ -97,6 +97,10 @@ def _desc(**kw):
     (dict(args=dict(beta=None)), gdr.GDR_E_INVAL),                   # no gate at all
     (dict(args=dict(ws=None)), gdr.GDR_E_INVAL),
     (dict(args=dict(wsz=100)), gdr.GDR_E_INVAL),
+    (dict(args=dict(q=P + 8)), gdr.GDR_E_INVAL),                     # 16-byte alignment
+    (dict(args=dict(o=P + 4)), gdr.GDR_E_INVAL),
+    (dict(args=dict(ws=P + 8)), gdr.GDR_E_INVAL),
+    (dict(args=dict(beta=P + 2)), gdr.GDR_E_INVAL),
 ])
 def test_prefill_rejections(case, expect):
     d = _desc(**case.get("desc", {}))
@@ -124,6 +128,8 @@ def test_zero_batch_is_a_noop_without_gpu():
     (dict(args=dict(S=None)), gdr.GDR_E_INVAL),
     (dict(args=dict(g=None)), gdr.GDR_E_INVAL),
     (dict(args=dict(beta=None, b=P, w=None)), gdr.GDR_E_INVAL),
+    (dict(args=dict(S=P + 8)), gdr.GDR_E_INVAL),
+    (dict(args=dict(k=P + 2)), gdr.GDR_E_INVAL),
 ])
 def test_decode_rejections(case, expect):
     d = _desc(**case.get("desc", {}))
