@@ -344,7 +344,8 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
         IO *wY = ws, *wQ = ws + C * D, *wUzT = ws + ws_off_uz(D, CHAN), *wA = ws + ws_off_a(D, CHAN);
         // Kend^T per unit (per-channel decay), or k^T once per QK head, written by its first V head.
         IO *wKT = CHAN ? ws + 2 * C * D
-                       : static_cast<IO *>(a.ws_kT) + ((size_t)(bh / a.Hv * a.Hqk + h / grpsz) * NC + c) * (D * C);
+                       : static_cast<IO *>(a.ws_kT) + ((size_t)(bh / a.Hv * a.Hqk + h / grpsz) * NC + c) * (2 * D * C);
+        IO *wQh = wKT + D * C;
         const bool write_kT = CHAN || h % grpsz == 0;
         float *tab = a.ws_tab + (size_t)u * kTab;
         __syncthreads();  // the previous unit is done with shared memory
@@ -515,10 +516,10 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
                 const int ti = z < 3 ? 0 : z < 5 ? 1 : 2, tj = z < 3 ? z + 1 : z < 5 ? z - 1 : 3;
                 store4f(sAc + (tj * 16 + lr) * LC + ti * 16 + 4 * lg, zero4());
             }
-            if constexpr (CHAN)  // Q~ fragments for the workspace
+            if (write_kT)
                 for (int f = w; f < (C / 16) * (D / KS); f += NW) {
                     const int rt = f / (D / KS), ks = f - rt * (D / KS);
-                    store_frag<IO>(wQ, rt, ks, D, M::load(tQ + rt * 16 * PD + ks * KS, PD));
+                    store_frag<IO>(CHAN ? wQ : wQh, rt, ks, D, M::load(tQ + rt * 16 * PD + ks * KS, PD));
                 }
             // Kend^T (or raw k^T) fragments: rows = channels, K = tokens, read K-major from the tiles.
             if (write_kT)
@@ -634,10 +635,11 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
 // work and its loads stay off the state's critical path. Every wave
 // prefetches its own slice of the chunk factors PF chunks ahead.
 //
-// With a scalar decay (CHAN false) the workspace holds neither Q~ nor Kend^T:
-// the output waves read q itself and scale the rows of q S_c by exp(G_t), and
-// the chain waves read the QK head's k^T and use the rows of U scaled by
-// exp(G_end - G_t) for the state update (Kend^T U = k^T Diag(exp(G_end - G)) U).
+// With a scalar decay (CHAN false) the workspace holds neither Q~ nor Kend^T
+// per V head: the output waves read the QK head's q and scale the rows of
+// q S_c by exp(G_t), and the chain waves read its k^T and use the rows of U
+// scaled by exp(G_end - G_t) for the state update
+// (Kend^T U = k^T Diag(exp(G_end - G)) U).
 template <typename IO, int D, int NCT>
 struct SweepShape {
     using M = Mma<IO>;
@@ -650,10 +652,8 @@ template <typename IO>
 struct SweepSrc {
     const IO *ws;     // io workspace
     const float *tab; // per-unit float tables
-    const IO *kT;     // k^T of this QK head, chunk 0 (scalar decay)
-    const IO *q;      // q of this sequence and QK head, token 0 (scalar decay)
+    const IO *kT;     // k^T and q of this QK head, chunk 0 (scalar decay)
     size_t u0;        // unit of chunk 0
-    int qstride;      // token stride of q (elements)
 };
 
 template <typename IO, int D, int NCT, bool CHAN>
@@ -670,7 +670,7 @@ struct ChainOps {  // Y rows and U_z columns of the wave's token tiles; Kend^T (
         const int l = threadIdx.x & 63, lq = l >> 4;
         const size_t u = src.u0 + c;
         const IO *Y = src.ws + u * chunk_ws_io_elems(D, CHAN), *UzT = Y + ws_off_uz(D, CHAN);
-        const IO *KT = CHAN ? Y + 2 * C * D : src.kT + (size_t)c * D * C;
+        const IO *KT = CHAN ? Y + 2 * C * D : src.kT + (size_t)c * 2 * D * C;
         const float *tab = src.tab + u * kTab;
 #pragma unroll
         for (int tt = 0; tt < Sh::TPW; ++tt) {
@@ -700,8 +700,7 @@ struct OutOps {  // Q~ (q) and A rows of the wave's token tiles
     F qa[Sh::TPW][Sh::KD], aa[Sh::TPW][Sh::KC];
     f32x4 eg[CHAN ? 1 : Sh::TPW];    // exp(G) of the wave's token rows (scalar decay)
 
-    __device__ __forceinline__ void load(const SweepSrc<IO> &src, int c, int n_valid, int w) {
-        constexpr int KS = Sh::M::KS, FE = KS / 4;
+    __device__ __forceinline__ void load(const SweepSrc<IO> &src, int c, int w) {
         const int l = threadIdx.x & 63, lq = l >> 4;
         const size_t u = src.u0 + c;
         const IO *unit = src.ws + u * chunk_ws_io_elems(D, CHAN), *A = unit + ws_off_a(D, CHAN);
@@ -712,12 +711,9 @@ struct OutOps {  // Q~ (q) and A rows of the wave's token tiles
 #pragma unroll
                 for (int ks = 0; ks < Sh::KD; ++ks) qa[tt][ks] = load_frag(unit + C * D, rt, ks, D);
             } else {
-                // q rows of this chunk straight from the input (rows past the end clamped; never stored)
-                const int t = min(rt * 16 + (l & 15), n_valid - 1);
-                const IO *qr = src.q + ((size_t)c * C + t) * src.qstride + FE * (l >> 4);
+                const IO *Qf = src.kT + (size_t)c * 2 * D * C + D * C;
 #pragma unroll
-                for (int ks = 0; ks < Sh::KD; ++ks)
-                    qa[tt][ks] = *reinterpret_cast<const F *>(qr + ks * KS);
+                for (int ks = 0; ks < Sh::KD; ++ks) qa[tt][ks] = load_frag(Qf, rt, ks, D);
                 eg[tt] = load4f(src.tab + u * kTab + rt * 16 + 4 * lq);
             }
 #pragma unroll
@@ -865,9 +861,7 @@ __global__ __launch_bounds__(4 * D) void chunk_sweep(ChunkArgs a, int NVT, int G
     src.ws = static_cast<const IO *>(a.ws_io);
     src.tab = a.ws_tab;
     src.u0 = (size_t)bh * a.NC + cb;
-    src.kT = CHAN ? nullptr : static_cast<const IO *>(a.ws_kT) + ((size_t)(b * a.Hqk + hq) * a.NC + cb) * (D * C);
-    src.q = static_cast<const IO *>(a.q) + (((size_t)b * a.T + (size_t)cb * C) * a.Hqk + hq) * D;
-    src.qstride = a.Hqk * D;
+    src.kT = CHAN ? nullptr : static_cast<const IO *>(a.ws_kT) + ((size_t)(b * a.Hqk + hq) * a.NC + cb) * (2 * D * C);
 
     if (wv < NWC) {  // ---- chain wave ----
         const int w = wv;
@@ -914,7 +908,7 @@ __global__ __launch_bounds__(4 * D) void chunk_sweep(ChunkArgs a, int NVT, int G
         const auto nv = [&](int cj) { return min(C, a.T - (cb + cj) * C); };
         OutOps<IO, D, NCT, CHAN> ring[PF];
 #pragma unroll
-        for (int j = 0; j < PF; ++j) ring[j].load(src, min(j, NC - 1), nv(min(j, NC - 1)), w);
+        for (int j = 0; j < PF; ++j) ring[j].load(src, min(j, NC - 1), w);
         int c = 0;
         for (; c + PF <= NC - 1; c += PF) {
 #pragma unroll
@@ -922,7 +916,7 @@ __global__ __launch_bounds__(4 * D) void chunk_sweep(ChunkArgs a, int NVT, int G
                 out_chunk<IO, D, NCT, CHAN, false>(ring[j], sST, sUT, sO, obase + (size_t)(c + j) * C * orow_stride,
                                                    orow_stride, C, a.scale, w);
                 const int cn = min(c + j + PF, NC - 1);
-                ring[j].load(src, cn, nv(cn), w);
+                ring[j].load(src, cn, w);
             }
         }
 #pragma unroll
@@ -961,9 +955,7 @@ __global__ __launch_bounds__(2 * D) void chunk_seg_state(ChunkArgs a, int NVT, i
     src.ws = static_cast<const IO *>(a.ws_io);
     src.tab = a.ws_tab;
     src.u0 = (size_t)bh * a.NC + cb;
-    src.kT = CHAN ? nullptr : static_cast<const IO *>(a.ws_kT) + ((size_t)(b * a.Hqk + hq) * a.NC + cb) * (D * C);
-    src.q = nullptr;
-    src.qstride = 0;
+    src.kT = CHAN ? nullptr : static_cast<const IO *>(a.ws_kT) + ((size_t)(b * a.Hqk + hq) * a.NC + cb) * (2 * D * C);
 
     f32x4 S[2][NCT];
 #pragma unroll

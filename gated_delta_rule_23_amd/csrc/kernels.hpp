@@ -34,7 +34,8 @@ struct ChunkArgs {
                              // per-channel decay also Q~ (C x D) and Kend^T (D x C); U_z^T (D x C); A (C x C)
     float *ws_tab;           // per chunk unit, kTab floats: per-channel decay: gamma (D);
                              // otherwise exp(G_t) and exp(G_end - G_t) (C each)
-    void *ws_kT;             // scalar or no decay: k^T (D x C, fragment order) per (sequence, QK head, chunk)
+    void *ws_kT;             // scalar or no decay: k^T (D x C) then q (C x D), fragment order, per
+                             // (sequence, QK head, chunk)
     float *ws_seg;           // segmented sweep (P > 1): per (sequence, V head, segment < P - 1) the
                              // segment's transition M (D x D), its end state from zero N (D x D), and the
                              // entry state of the next segment (D x D), fp32
@@ -46,8 +47,8 @@ struct ChunkArgs {
 constexpr int kTab = 2 * kChunk;  // floats per chunk unit in ws_tab (>= D for every supported D)
 
 // Workspace layout. With a scalar decay (or none) the queries and the
-// end-of-chunk keys are not stored per V head: the sweep reads q directly and
-// one k^T per QK head, and applies the per-token decay factors itself.
+// end-of-chunk keys are not stored per V head: the sweep reads one k^T and one
+// q per QK head and applies the per-token decay factors itself.
 __host__ __device__ inline size_t chunk_ws_io_elems(int D, bool chan) {
     return (size_t)(chan ? 4 : 2) * kChunk * D + (size_t)kChunk * kChunk;
 }
@@ -81,7 +82,7 @@ inline ChunkWsLayout chunk_ws_layout(int B, int Hqk, int Hv, int NC, int D, int 
     ChunkWsLayout L;
     L.io_bytes = align256(units * chunk_ws_io_elems(D, chan) * esz);
     L.tab_bytes = align256(units * kTab * sizeof(float));
-    L.kT_bytes = chan ? 0 : align256((size_t)B * Hqk * NC * D * kChunk * esz);
+    L.kT_bytes = chan ? 0 : align256((size_t)2 * B * Hqk * NC * D * kChunk * esz);
     int P, Ls;
     chunk_segments(B, Hv, D, NC, P, Ls);
     L.seg_bytes = P > 1 ? align256((size_t)3 * B * Hv * (P - 1) * D * D * sizeof(float)) : 0;

@@ -46,12 +46,12 @@ def _a256(x):
 
 def test_workspace_bytes():
     """Scalar decay: Y, U_z^T and A per (sequence, V head, chunk), two per-token
-    decay tables, and one k^T per (sequence, QK head, chunk). Per-channel decay:
-    also Q~ and Kend^T per unit, and gamma in the table."""
+    decay tables, and one k^T and one q per (sequence, QK head, chunk).
+    Per-channel decay: also Q~ and Kend^T per unit, and gamma in the table."""
     NC, units = 64, 48 * 64
     d = gdr.make_desc(1, 4096, 16, 48, 128, gdr.GDR_BF16, gdr.GDR_DECAY_SCALAR)
     io = units * (2 * 64 * 128 + 64 * 64) * 2
-    expect = _a256(io) + _a256(units * 128 * 4) + _a256(16 * NC * 128 * 64 * 2)
+    expect = _a256(io) + _a256(units * 128 * 4) + _a256(16 * NC * 2 * 128 * 64 * 2)
     assert gdr.gdr_chunk_workspace_bytes(d) == expect
     dc = gdr.make_desc(1, 4096, 16, 48, 128, gdr.GDR_BF16, gdr.GDR_DECAY_CHANNEL)
     io = units * (4 * 64 * 128 + 64 * 64) * 2
