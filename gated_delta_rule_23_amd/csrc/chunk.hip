@@ -1038,15 +1038,15 @@ __global__ __launch_bounds__(256) void chunk_seg_combine(ChunkArgs a) {
     }
 }
 
+// Compute units of the device in use when first asked (thread-safe; 256 if unknown).
 static int device_cus() {
-    static int cus = 0;
-    if (cus == 0) {
+    static const int cus = [] {
         int dev = 0, n = 0;
-        if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-            cus = n;
-        else
-            cus = 256;
-    }
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+            return n;
+        return 256;
+    }();
     return cus;
 }
 
@@ -1055,8 +1055,8 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t s) {
     using Cfg = PrepCfg<IO, D>;
     // Shared memory per prep variant (CHAN, BW): the per-channel-decay and
     // decoupled-gate variants keep more tiles.
-    static bool attr_set = false;
-    if (!attr_set) {
+    // Once per process (thread-safe): allow each variant its shared memory.
+    static const hipError_t attr_err = [] {
         const void *fns[4] = {reinterpret_cast<const void *>(&chunk_prep<IO, D, false, false>),
                               reinterpret_cast<const void *>(&chunk_prep<IO, D, false, true>),
                               reinterpret_cast<const void *>(&chunk_prep<IO, D, true, false>),
@@ -1067,8 +1067,9 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t s) {
             hipError_t e = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds[i]);
             if (e != hipSuccess) return e;
         }
-        attr_set = true;
-    }
+        return hipSuccess;
+    }();
+    if (attr_err != hipSuccess) return attr_err;
     const long long units = (long long)a.B * a.Hv * a.NC;
     if (units > 0) {
         // Persistent: as many workgroups as fit on the device at once.

@@ -127,19 +127,20 @@ def _sweep_segments(B, Hv, D, T):
     return -(-NC // L)
 
 
-@pytest.mark.parametrize("io,D,decay,gates,T,Hv", [
-    ("bf16", 64, "scalar", "beta", 2500, 2),
-    ("bf16", 128, "scalar", "bw", 4096, 2),
-    ("bf16", 128, "channel", "bw", 4113, 1),
-    ("f32", 32, "channel", "beta", 2100, 1),
+@pytest.mark.parametrize("io,D,decay,gates,T,Hv,B", [
+    ("bf16", 64, "scalar", "beta", 2500, 2, 1),
+    ("bf16", 128, "scalar", "bw", 4096, 2, 1),
+    ("bf16", 128, "channel", "bw", 4113, 1, 1),
+    ("f32", 32, "channel", "beta", 2100, 1, 1),
+    ("bf16", 64, "channel", "beta", 2100, 1, 2),
 ])
-def test_prefill_segmented_sweep(io, D, decay, gates, T, Hv):
+def test_prefill_segmented_sweep(io, D, decay, gates, T, Hv, B):
     """Long sequences with few heads split the sequential sweep into segments
     that run in parallel from entry states found by a scan over the segments'
     transitions; the result is still the token-by-token recurrence, here from
     a non-zero initial state and with a partial last chunk in one case."""
-    assert _sweep_segments(1, Hv, D, T) > 1
-    wl = small_workload(io, D, decay, gates, T, B=1, Hqk=1, Hv=Hv, S0=True)
+    assert _sweep_segments(B, Hv, D, T) > 1
+    wl = small_workload(io, D, decay, gates, T, B=B, Hqk=1, Hv=Hv, S0=True)
     inp = gs.make_inputs(wl, seed=7)
     say(f"segmented {wl.name}")
     o, ST = gpu_prefill(inp, S0=to_dev(inp["S0"]))
