@@ -5,8 +5,11 @@ One step = one chunked prefill of the Qwen3.8-27B-shaped Gated DeltaNet layer
 through gdr_chunk_fwd. In the same run the decode step is measured on its own
 workload (64 sequences x 48 V heads, 128 x 128 fp32 states, 256 consecutive
 gdr_decode_step calls). Inputs are seeded synthetic tensors already resident
-in device memory when timing starts. Timing uses HIP events recorded on the
-stream the kernels run on.
+in device memory when timing starts. The timed calls are captured once as a
+HIP graph (the way a serving loop launches them, without per-launch host
+overhead) and timed over one replay with HIP events on the stream the graph
+runs on; the JSON also gives the eager per-call time (events around each
+call) for reference.
 
 --workload picks another prefill workload for the timed step (the KDA and
 Gated DeltaNet-2 layers, or the small fp32 case); --decode-steps 0 skips the
@@ -130,7 +133,6 @@ def main(argv=None):
     import gdr_synth as gs
 
     dev = torch.device("cuda:0")
-    stream = torch.cuda.current_stream()
 
     def up(a):
         if a is None:
@@ -160,27 +162,41 @@ def main(argv=None):
     o = torch.empty((wl.B, wl.T, wl.Hv, wl.dv), dtype=io_t, device=dev)
     ST = torch.empty((wl.B, wl.Hv, wl.dk, wl.dv), dtype=torch.float32, device=dev)
 
+    cur = torch.cuda.current_stream  # the stream a call is made on (inside a capture: the capture stream)
+
     def prefill():
         gdr.gdr_chunk_fwd(d["q"], d["k"], d["v"], g=d["g"], beta=d["beta"], b=d["b"], w=d["w"], S0=None,
-                          scale=wl.scale, o=o, ST=ST, workspace=ws, stream=stream)
+                          scale=wl.scale, o=o, ST=ST, workspace=ws, stream=cur())
 
     for _ in range(args.warmup):
         prefill()
     torch.cuda.synchronize()
+    # Reference: HIP events around each of K eager calls.
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev[i][0].record(cur())
+        prefill()
+        ev[i][1].record(cur())
+    torch.cuda.synchronize()
+    eager_call_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    # Timed region: the K calls captured once as a HIP graph (as a serving loop
+    # launches them), replayed once untimed, then timed over one replay.
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(args.steps):
+            prefill()
+    graph.replay()
+    torch.cuda.synchronize()
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        prefill()
-        ev[i][1].record(stream)
-    t_end.record(stream)
+    t_start.record(cur())
+    graph.replay()
+    t_end.record(cur())
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
-    call_ms = [a.elapsed_time(b) for a, b in ev]
     ms_per_step = total_ms / args.steps
-    avg_call_ms = sum(call_ms) / len(call_ms)
+    avg_call_ms = ms_per_step
+    del graph
     tokens = wl.B * wl.T
     pbytes, pflops = prefill_algorithmic(wl)
     achieved = pbytes / (avg_call_ms * 1e-3) / 1e9
@@ -192,37 +208,51 @@ def main(argv=None):
                                         name=f"qwen_gdn_decode_B64_Hv48_d128_{args.decode_steps}steps")
         dinp = gs.make_inputs(dwl, seed=args.seed + 1)
         dd = {n: up(dinp[n]) for n in ("q", "k", "v", "g", "beta", "b", "w")}
-        S = up(dinp["S0"]).clone()
+        S0d = up(dinp["S0"])
+        S = S0d.clone()
         do = torch.empty((dwl.B, dwl.Hv, dwl.dv), dtype=torch.bfloat16, device=dev)
 
         def dstep(s):
             pick = lambda t: None if t is None else t[s]
             gdr.gdr_decode_step(pick(dd["q"]), pick(dd["k"]), pick(dd["v"]), S, g=pick(dd["g"]),
                                 beta=pick(dd["beta"]), b=pick(dd["b"]), w=pick(dd["w"]), scale=dwl.scale, o=do,
-                                stream=stream)
+                                stream=cur())
 
         for s in range(min(8, dwl.T)):
             dstep(s)
-        S.copy_(up(dinp["S0"]))
+        S.copy_(S0d)
         torch.cuda.synchronize()
+        # Reference: events around each eager step.
         dev_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(dwl.T)]
-        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        d0.record(stream)
         for s in range(dwl.T):
-            dev_ev[s][0].record(stream)
+            dev_ev[s][0].record(cur())
             dstep(s)
-            dev_ev[s][1].record(stream)
-        d1.record(stream)
+            dev_ev[s][1].record(cur())
         torch.cuda.synchronize()
-        d_total_ms = d0.elapsed_time(d1)
-        d_step_ms = sorted(a.elapsed_time(b) for a, b in dev_ev)
-        d_avg_ms = sum(d_step_ms) / len(d_step_ms)
+        d_eager_ms = sum(a.elapsed_time(b) for a, b in dev_ev) / dwl.T
+        # Timed: the consecutive steps as one HIP graph replay, from the initial state.
+        S.copy_(S0d)
+        dgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(dgraph):
+            for s in range(dwl.T):
+                dstep(s)
+        S.copy_(S0d)
+        dgraph.replay()
+        S.copy_(S0d)
+        torch.cuda.synchronize()
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        d0.record(cur())
+        dgraph.replay()
+        d1.record(cur())
+        torch.cuda.synchronize()
+        del dgraph
+        d_step_ms = d0.elapsed_time(d1) / dwl.T
         state_bytes, d_bytes = decode_algorithmic(dwl)
-        d_achieved = d_bytes / (d_avg_ms * 1e-3) / 1e9
-        dec = {"workload": dwl.name, "steps": dwl.T, "ms_per_step": d_total_ms / dwl.T,
-               "kernel_avg_ms": d_avg_ms, "kernel_median_ms": d_step_ms[len(d_step_ms) // 2],
-               "state_GBps": state_bytes / (d_avg_ms * 1e-3) / 1e9,
-               "tokens_per_s": dwl.B / (d_total_ms / dwl.T * 1e-3),
+        d_achieved = d_bytes / (d_step_ms * 1e-3) / 1e9
+        dec = {"workload": dwl.name, "steps": dwl.T, "launch": "hip_graph", "ms_per_step": d_step_ms,
+               "eager_ms_per_step": d_eager_ms,
+               "state_GBps": state_bytes / (d_step_ms * 1e-3) / 1e9,
+               "tokens_per_s": dwl.B / (d_step_ms * 1e-3),
                "roofline": {"kernel": "decode_kernel", "bound": "hbm", "achieved": d_achieved,
                             "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": d_achieved / HBM_PEAK_GBPS,
                             "traffic": recorded_traffic(dwl.name) if dwl.T == 256 else None,
@@ -243,10 +273,11 @@ def main(argv=None):
         "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), gates and decay per the workload recipe)",
         "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "H_qk": wl.Hqk, "H_v": wl.Hv, "d_k": wl.dk,
                    "d_v": wl.dv, "chunk": wl.chunk, "io": wl.io, "decay": wl.decay, "gates": wl.gates,
-                   "state": "fp32", "S0": "zeros"},
+                   "state": "fp32", "S0": "zeros", "launch": "hip_graph"},
         "roofline": {"kernel": "gdr_chunk_fwd (chunk_prep + chunk_sweep)", "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": recorded_traffic(wl.name), "algorithmic_bytes": pbytes, "avg_call_ms": avg_call_ms},
+                     "traffic": recorded_traffic(wl.name), "algorithmic_bytes": pbytes, "avg_call_ms": avg_call_ms,
+                     "eager_call_ms": eager_call_ms},
         "mfma": {"algorithmic_tflops": pflops / (avg_call_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
                  "frac": pflops / (avg_call_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, "algorithmic_flops": pflops},
         "decode": dec,

@@ -189,6 +189,72 @@ def test_prefill_in_place_state_and_determinism():
     assert torch.equal(o3, o1) and torch.equal(S_inplace, S1)
 
 
+def test_hip_graph_replay_matches_eager():
+    """Prefill and decode calls captured in a HIP graph, as a serving loop
+    would run them, give the eager result bit for bit on every replay, with
+    eager work and synchronisations between the replays. The library enqueues
+    only kernels (no memset or allocation) once its workspace is given."""
+    import gated_delta_rule_23_amd as gdr
+    cur = torch.cuda.current_stream
+    for wl in (small_workload("bf16", 128, "scalar", "beta", T=300, B=1, Hqk=1, Hv=3, S0=True),
+               small_workload("bf16", 64, "channel", "bw", T=2100, B=1, Hqk=1, Hv=1, S0=True)):
+        inp = gs.make_inputs(wl, seed=21)
+        say(f"graph {wl.name}")
+        d = {n: to_dev(inp[n]) for n in ("q", "k", "v", "g", "beta", "b", "w")}
+        S0 = to_dev(inp["S0"])
+        desc = gdr.make_desc(wl.B, wl.T, wl.Hqk, wl.Hv, wl.dk, gdr.GDR_BF16,
+                             gdr.GDR_DECAY_SCALAR if wl.decay == "scalar" else gdr.GDR_DECAY_CHANNEL)
+        ws = torch.empty(gdr.gdr_chunk_workspace_bytes(desc), dtype=torch.uint8, device="cuda:0")
+        o = torch.empty((wl.B, wl.T, wl.Hv, wl.dv), dtype=torch.bfloat16, device="cuda:0")
+        ST = torch.empty((wl.B, wl.Hv, wl.dk, wl.dv), dtype=torch.float32, device="cuda:0")
+
+        def call():
+            gdr.gdr_chunk_fwd(d["q"], d["k"], d["v"], g=d["g"], beta=d["beta"], b=d["b"], w=d["w"], S0=S0, o=o,
+                              ST=ST, workspace=ws, stream=cur())
+
+        call()
+        torch.cuda.synchronize()
+        o_ref, S_ref = o.clone(), ST.clone()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            call()
+        for _ in range(3):
+            o.zero_()
+            ST.zero_()
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(o, o_ref) and torch.equal(ST, S_ref)
+
+    wl = gs.QWEN_GDN_DECODE.scaled(B=4, Hqk=2, Hv=6, T=8)
+    inp = gs.make_inputs(wl, seed=22)
+    dd = {n: to_dev(inp[n]) for n in ("q", "k", "v", "g", "beta", "b", "w")}
+    S_init = to_dev(inp["S0"])
+    S = S_init.clone()
+    outs = [torch.empty((wl.B, wl.Hv, wl.dv), dtype=torch.bfloat16, device="cuda:0") for _ in range(wl.T)]
+
+    def steps():
+        for s in range(wl.T):
+            gdr.gdr_decode_step(dd["q"][s], dd["k"][s], dd["v"][s], S, g=dd["g"][s], beta=dd["beta"][s],
+                                scale=wl.scale, o=outs[s], stream=cur())
+
+    steps()
+    torch.cuda.synchronize()
+    o_ref, S_ref = [x.clone() for x in outs], S.clone()
+    S.copy_(S_init)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        steps()
+    for _ in range(3):
+        S.copy_(S_init)
+        for x in outs:
+            x.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(S, S_ref) and all(torch.equal(x, r) for x, r in zip(outs, o_ref))
+
+
 def test_prefill_empty_sequence_copies_state():
     import gated_delta_rule_23_amd as gdr
     wl = small_workload("bf16", 64, "scalar", "beta", T=8, B=2, Hqk=1, Hv=2, S0=True)
