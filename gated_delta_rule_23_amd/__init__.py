@@ -11,6 +11,7 @@ Tensor layouts (contiguous, on the same GPU):
            g [B,T,Hv] or [B,T,Hv,D] f32; b [B,T,Hv,D]; w [B,T,Hv,D];
            state [B,Hv,D,D] f32 (row = key channel, column = value channel)
   decode   the same without the T axis.
+  recurrent (short runs from a live state) as prefill.
 q, k, v, b, w and the output share one dtype: torch.bfloat16 or torch.float32.
 """
 from __future__ import annotations
@@ -28,7 +29,7 @@ CHUNK = 64
 
 # Every symbol include/gdr.h declares.
 EXPORTS = ("gdr_state_bytes", "gdr_state_alloc", "gdr_state_free", "gdr_chunk_workspace_bytes",
-           "gdr_chunk_fwd", "gdr_decode_step", "gdr_last_error", "gdr_version")
+           "gdr_chunk_fwd", "gdr_decode_step", "gdr_recurrent_fwd", "gdr_last_error", "gdr_version")
 
 
 class GdrError(RuntimeError):
@@ -69,6 +70,8 @@ def _load():
     lib.gdr_chunk_fwd.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, S, P]
     lib.gdr_decode_step.restype = I
     lib.gdr_decode_step.argtypes = [D, P, P, P, P, P, P, P, P, P, P]
+    lib.gdr_recurrent_fwd.restype = I
+    lib.gdr_recurrent_fwd.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P]
     lib.gdr_last_error.restype = ctypes.c_char_p
     lib.gdr_last_error.argtypes = []
     lib.gdr_version.restype = I
@@ -218,3 +221,30 @@ def gdr_decode_step(q, k, v, S, *, g=None, beta=None, b=None, w=None, scale=1.0,
     _check(lib.gdr_decode_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(b),
                                _ptr(w), _ptr(S), _ptr(o), _stream(stream)))
     return o
+
+
+def gdr_recurrent_fwd(q, k, v, *, g=None, beta=None, b=None, w=None, S0=None, scale=1.0, o=None, ST=None,
+                      stream=None):
+    """Fused recurrent forward over the T tokens of q [B,T,Hqk,D] from S0
+    (None = zeros). Returns (o, ST); ST may be passed equal to S0 for an
+    in-place state update. Same layouts and results as gdr_chunk_fwd."""
+    torch = _torch()
+    B, T, Hqk, D = q.shape
+    Hv = v.shape[2]
+    dev, io_t = q.device, q.dtype
+    for name, t, shape in (("q", q, (B, T, Hqk, D)), ("k", k, (B, T, Hqk, D)), ("v", v, (B, T, Hv, D)),
+                           ("b", b, (B, T, Hv, D)), ("w", w, (B, T, Hv, D))):
+        _require(t, name, shape, io_t, dev)
+    _require(beta, "beta", (B, T, Hv), torch.float32, dev)
+    _require(g, "g", None, torch.float32, dev)
+    _require(S0, "S0", (B, Hv, D, D), torch.float32, dev)
+    desc = make_desc(B, T, Hqk, Hv, D, _io_dtype(q), _decay_of(g, (B, T), Hv, D), scale)
+    if o is None:
+        o = torch.empty((B, T, Hv, D), dtype=io_t, device=dev)
+    if ST is None:
+        ST = torch.empty((B, Hv, D, D), dtype=torch.float32, device=dev)
+    _require(o, "o", (B, T, Hv, D), io_t, dev)
+    _require(ST, "ST", (B, Hv, D, D), torch.float32, dev)
+    _check(lib.gdr_recurrent_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(b),
+                                 _ptr(w), _ptr(S0), _ptr(o), _ptr(ST), _stream(stream)))
+    return o, ST

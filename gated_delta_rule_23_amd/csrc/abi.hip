@@ -47,9 +47,12 @@ bool size_ok(long long B, long long T, long long H, long long D) {
     return B <= lim && T <= lim && H <= lim && D <= lim && B * T <= lim && B * T * H <= lim && B * T * H * D <= lim;
 }
 
-// Checks shared by prefill and decode. `prefill` selects the T / chunk checks.
-int validate(const gdr_desc *d, bool prefill, const void *q, const void *k, const void *v, const float *g,
+// Checks shared by every compute call. Decode has no T axis; the chunked
+// prefill also checks the chunk length and its supported dtypes.
+enum CallKind { CALL_DECODE, CALL_CHUNK, CALL_RECURRENT };
+int validate(const gdr_desc *d, CallKind kind, const void *q, const void *k, const void *v, const float *g,
              const float *beta, const void *b, const void *w, const void *o) {
+    const bool prefill = kind != CALL_DECODE;
     if (!d) return fail(GDR_E_INVAL, "desc is NULL");
     if (d->B < 0) return fail(GDR_E_INVAL, "B = %d must be >= 0", d->B);
     if (prefill && d->T < 0) return fail(GDR_E_INVAL, "T = %d must be >= 0", d->T);
@@ -62,7 +65,7 @@ int validate(const gdr_desc *d, bool prefill, const void *q, const void *k, cons
     if (!std::isfinite(d->scale)) return fail(GDR_E_INVAL, "scale must be finite");
     if (d->d_k != d->d_v || !supported_dim(d->d_k))
         return fail(GDR_E_UNSUPPORTED, "d_k = %d, d_v = %d: supported are d_k == d_v in {32, 64, 128}", d->d_k, d->d_v);
-    if (prefill) {
+    if (kind == CALL_CHUNK) {
         if (d->chunk != gdr::kChunk) return fail(GDR_E_UNSUPPORTED, "chunk = %d: only 64 is supported", d->chunk);
         if (!gdr::chunk_supported(d->io_dtype == GDR_BF16 ? gdr::IO_BF16 : gdr::IO_F32, d->d_k))
             return fail(GDR_E_UNSUPPORTED, "prefill with float32 io supports d in {32, 64}");
@@ -138,7 +141,7 @@ int gdr_chunk_workspace_bytes(const gdr_desc *d, size_t *bytes) {
     // Pointers are not known here; validate the sizes with dummy non-NULL pointers.
     static const char dummy = 0;
     const void *p = &dummy;
-    const int rc = validate(d, true, p, p, p, d && d->decay != GDR_DECAY_NONE ? (const float *)p : nullptr,
+    const int rc = validate(d, CALL_CHUNK, p, p, p, d && d->decay != GDR_DECAY_NONE ? (const float *)p : nullptr,
                             (const float *)p, nullptr, nullptr, p);
     if (rc != GDR_OK) return rc;
     const int NC = (d->T + gdr::kChunk - 1) / gdr::kChunk;
@@ -150,7 +153,7 @@ int gdr_chunk_workspace_bytes(const gdr_desc *d, size_t *bytes) {
 int gdr_chunk_fwd(const gdr_desc *d, const void *q, const void *k, const void *v, const float *g, const float *beta,
                   const void *b, const void *w, const float *S0, void *o, float *ST, void *workspace,
                   size_t workspace_bytes, void *stream) {
-    int rc = validate(d, true, q, k, v, g, beta, b, w, o);
+    int rc = validate(d, CALL_CHUNK, q, k, v, g, beta, b, w, o);
     if (rc != GDR_OK) return rc;
     if (!ST) return fail(GDR_E_INVAL, "ST must be non-NULL");
     rc = check_alignment(d, {q, k, v, b, w, o, S0, ST, workspace}, g, beta);
@@ -184,7 +187,7 @@ int gdr_chunk_fwd(const gdr_desc *d, const void *q, const void *k, const void *v
 
 int gdr_decode_step(const gdr_desc *d, const void *q, const void *k, const void *v, const float *g, const float *beta,
                     const void *b, const void *w, float *S, void *o, void *stream) {
-    int rc = validate(d, false, q, k, v, g, beta, b, w, o);
+    int rc = validate(d, CALL_DECODE, q, k, v, g, beta, b, w, o);
     if (rc != GDR_OK) return rc;
     if (!S) return fail(GDR_E_INVAL, "S must be non-NULL");
     rc = check_alignment(d, {q, k, v, b, w, o, S}, g, beta);
@@ -197,6 +200,32 @@ int gdr_decode_step(const gdr_desc *d, const void *q, const void *k, const void 
     hipError_t e = gdr::launch_decode(d->io_dtype == GDR_BF16 ? gdr::IO_BF16 : gdr::IO_F32, d->d_k, a,
                                       static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "decode launch");
+    return ok();
+}
+
+int gdr_recurrent_fwd(const gdr_desc *d, const void *q, const void *k, const void *v, const float *g,
+                      const float *beta, const void *b, const void *w, const float *S0, void *o, float *ST,
+                      void *stream) {
+    int rc = validate(d, CALL_RECURRENT, q, k, v, g, beta, b, w, o);
+    if (rc != GDR_OK) return rc;
+    if (!ST) return fail(GDR_E_INVAL, "ST must be non-NULL");
+    rc = check_alignment(d, {q, k, v, b, w, o, S0, ST}, g, beta);
+    if (rc != GDR_OK) return rc;
+    if (S0 && S0 != ST) {
+        const size_t n = gdr_state_bytes(d->B, d->H_v, d->d_k, d->d_v);
+        const char *s0 = reinterpret_cast<const char *>(S0), *st = reinterpret_cast<const char *>(ST);
+        if (s0 < st + n && st < s0 + n) return fail(GDR_E_INVAL, "ST must equal S0 or not overlap it");
+    }
+    if (d->B == 0) return ok();
+    // At most two workgroups per (sequence, V head).
+    if ((long long)d->B * d->H_v * 2 > 0x7fffffffll) return fail(GDR_E_UNSUPPORTED, "B * H_v too large for one launch");
+    gdr::RecurArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.bg = b; a.wg = w;
+    a.S0 = S0; a.ST = ST; a.o = o;
+    a.B = d->B; a.T = d->T; a.Hqk = d->H_qk; a.Hv = d->H_v; a.decay = d->decay; a.scale = d->scale;
+    hipError_t e = gdr::launch_recurrent(d->io_dtype == GDR_BF16 ? gdr::IO_BF16 : gdr::IO_F32, d->d_k, a,
+                                         static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "recurrent launch");
     return ok();
 }
 

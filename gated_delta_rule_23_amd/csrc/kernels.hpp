@@ -22,6 +22,19 @@ struct DecodeArgs {
     float scale;
 };
 
+// Multi-token recurrent forward: the prefill layouts and gate modes, no workspace.
+struct RecurArgs {
+    const void *q, *k, *v;   // [B,T,Hqk,D], [B,T,Hqk,D], [B,T,Hv,D]
+    const float *g;          // [B,T,Hv] or [B,T,Hv,D] or null
+    const float *beta;       // [B,T,Hv] or null
+    const void *bg, *wg;     // [B,T,Hv,D] or null
+    const float *S0;         // [B,Hv,D,D] or null (zeros)
+    float *ST;               // [B,Hv,D,D]; may equal S0
+    void *o;                 // [B,T,Hv,D]
+    int B, T, Hqk, Hv, decay;
+    float scale;
+};
+
 struct ChunkArgs {
     const void *q, *k, *v;   // [B,T,Hqk,D], [B,T,Hqk,D], [B,T,Hv,D]
     const float *g;          // [B,T,Hv] or [B,T,Hv,D] or null
@@ -91,6 +104,7 @@ inline ChunkWsLayout chunk_ws_layout(int B, int Hqk, int Hv, int NC, int D, int 
 
 hipError_t launch_decode(int io, int D, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_chunk(int io, int D, const ChunkArgs &a, hipStream_t s);
+hipError_t launch_recurrent(int io, int D, const RecurArgs &a, hipStream_t s);
 hipError_t launch_state_fill(float *dst, const float *src, size_t n, hipStream_t s);
 bool chunk_supported(int io, int D);
 

@@ -1,0 +1,216 @@
+// recurrent.hip -- fused recurrent forward over a run of tokens.
+//
+// The recurrent form of the mixer ("Kernel Triton recorrente fundido para
+// decode", family analysis page "Uma análise das variantes de atenção linear
+// da família DeltaNet"): one program per (sequence, V head, value tile) walks
+// the tokens in order with its block of the state held on chip, so the state
+// crosses HBM once each way per call, whatever the number of tokens. Per
+// token, with alpha = exp(g):
+//
+//   r = Sbar^T e = S^T (alpha . e)      p = Sbar^T q = S^T (alpha . q)
+//   u = z - r                           o = scale * (p + (q . k) u)
+//   S = Diag(alpha) S + k u^T
+//
+// o is the read after the write, scale * S_new^T q, written out as
+// p + (q . k) u so that one pass over the state serves both reductions.
+//
+// Value columns of the state never mix: u_j, o_j and the update of column j
+// use column j and the key-axis vectors only. So each wave owns CW columns
+// and all D rows of one head, and both key-axis reductions stay inside the
+// wave: lane (r, c) holds float4 column group c of rows r*RPL ... r*RPL +
+// RPL-1 in registers, and the NRL lanes sharing a column group sum their
+// partial results with an all-reduce of DPP row permutations (no LDS, no
+// barrier). The waves of a workgroup share only the token inputs, staged in
+// LDS TB tokens at a time already combined into alpha.e, alpha.q, k (and
+// alpha per key channel), z and q . k; one barrier per staged block.
+//
+// Work per token and head is about 4 D^2 flops against D^2 fp32 of state
+// that is read and written once per call: a run of a few tokens is bound by
+// HBM, a long one by the vector ALUs (long prefills belong to the chunked
+// path, whose products run on the matrix cores).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace gdr {
+
+template <int D, int CW, bool CHAN>
+struct RecurCfg {
+    static constexpr int NCG = CW / 4;             // float4 column groups per wave
+    static constexpr int NRL = 64 / NCG;           // lanes sharing a column group
+    static constexpr int RPL = D / NRL;            // rows per lane
+    static constexpr int NWB = D / CW < 4 ? D / CW : 4;  // waves per workgroup
+    static constexpr int NT = 64 * NWB;
+    static constexpr int TILES = D / (NWB * CW);   // workgroups per (sequence, V head)
+    static constexpr int TB = 8;                   // tokens staged per block
+    // Staged token layout (floats). Key-axis arrays are stored per lane row
+    // block with 4 floats of padding, so the NRL distinct 16-byte reads of a
+    // wave fall in different LDS banks.
+    static constexpr int RP = RPL + 4;
+    static constexpr int DP = NRL * RP;
+    static constexpr int OFF_AE = 0, OFF_AQ = DP, OFF_K = 2 * DP, OFF_AL = 3 * DP;
+    static constexpr int OFF_Z = (CHAN ? 4 : 3) * DP;
+    static constexpr int OFF_MISC = OFF_Z + D;     // q . k, scalar alpha
+    static constexpr int STR = OFF_MISC + 4;
+    static_assert(RPL % 4 == 0 && NRL >= 8 && NRL <= 16 && D % (NWB * CW) == 0, "recurrent tile shape");
+};
+
+// Sum over the NRL (8 or 16) consecutive lanes of a DPP row, result in every
+// one of them: swap neighbours, swap pairs, then fold each 8-lane half onto
+// its mirror image, and for 16 lanes the two halves of the row likewise.
+template <int NRL>
+__device__ __forceinline__ float rows_allreduce(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));  // half-row mirror
+    if constexpr (NRL == 16)
+        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));  // row mirror
+    return x;
+}
+
+__device__ __forceinline__ f32x4 exp4(f32x4 g) { return f32x4{expf(g[0]), expf(g[1]), expf(g[2]), expf(g[3])}; }
+
+template <typename IO, int D, int CW, bool CHAN>
+__global__ __launch_bounds__((RecurCfg<D, CW, CHAN>::NT)) void recurrent_kernel(RecurArgs a) {
+    using C = RecurCfg<D, CW, CHAN>;
+    constexpr int G = D / 4;  // 4-element groups of one token's key or value vector
+    __shared__ __align__(16) float lds[C::TB * C::STR];
+
+    const int tile = blockIdx.x % C::TILES;
+    const int bh = blockIdx.x / C::TILES;
+    const int b = bh / a.Hv, h = bh - b * a.Hv;
+    const int hq = h / (a.Hv / a.Hqk);
+    const int tid = threadIdx.x;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, r = lane % C::NRL, cg = lane / C::NRL;
+    const int col = (tile * C::NWB + wv) * CW + 4 * cg;  // first of this lane's four value columns
+    const size_t sbase = (size_t)bh * D * D + (size_t)(r * C::RPL) * D + col;
+
+    f32x4 st[C::RPL];
+#pragma unroll
+    for (int m = 0; m < C::RPL; ++m) st[m] = a.S0 ? load4f(a.S0 + sbase + (size_t)m * D) : f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const IO *qg = static_cast<const IO *>(a.q), *kg = static_cast<const IO *>(a.k);
+    const IO *vg = static_cast<const IO *>(a.v);
+    const IO *bgp = static_cast<const IO *>(a.bg), *wgp = static_cast<const IO *>(a.wg);
+    IO *og = static_cast<IO *>(a.o);
+
+    for (int t0 = 0; t0 < a.T; t0 += C::TB) {
+        const int nt = a.T - t0 < C::TB ? a.T - t0 : C::TB;
+        if (t0 > 0) __syncthreads();  // every wave is done with the previous block
+        // Stage: one thread per (token, 4 key/value channels); a token's G
+        // threads are consecutive lanes of one wave.
+        for (int u = tid; u < nt * G; u += C::NT) {
+            const int tt = u / G, i0 = 4 * (u - tt * G);
+            const size_t tok = (size_t)b * a.T + t0 + tt;
+            const size_t xk = (tok * a.Hqk + hq) * D + i0;
+            const size_t xs = tok * a.Hv + h;
+            const size_t xv = xs * D + i0;
+            const f32x4 q = load4f(qg + xk), k = load4f(kg + xk), v = load4f(vg + xv);
+            f32x4 e, z;
+            if (a.beta) {
+                const float bt = a.beta[xs];
+                e = bt * k;
+                z = bt * v;
+            } else {
+                e = load4f(bgp + xv) * k;
+                z = load4f(wgp + xv) * v;
+            }
+            float as = 1.f;
+            f32x4 al;
+            if constexpr (CHAN) {
+                al = exp4(load4f(a.g + xv));
+            } else {
+                if (a.decay == DECAY_SCALAR) as = expf(a.g[xs]);
+                al = f32x4{as, as, as, as};
+            }
+            float *L = lds + tt * C::STR;
+            const int p = (i0 / C::RPL) * C::RP + i0 % C::RPL;
+            store4f(L + C::OFF_AE + p, al * e);
+            store4f(L + C::OFF_AQ + p, al * q);
+            store4f(L + C::OFF_K + p, k);
+            if constexpr (CHAN) store4f(L + C::OFF_AL + p, al);
+            store4f(L + C::OFF_Z + i0, z);
+            float qk = q[0] * k[0] + q[1] * k[1] + q[2] * k[2] + q[3] * k[3];
+#pragma unroll
+            for (int off = 1; off < G; off <<= 1) qk += __shfl_xor(qk, off);
+            if (i0 == 0) {
+                L[C::OFF_MISC] = qk;
+                L[C::OFF_MISC + 1] = as;
+            }
+        }
+        __syncthreads();
+
+        for (int tt = 0; tt < nt; ++tt) {
+            const float *L = lds + tt * C::STR;
+            const float *Lr = L + r * C::RP;
+            f32x4 pr{0.f, 0.f, 0.f, 0.f}, pp{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m4 = 0; m4 < C::RPL / 4; ++m4) {
+                const f32x4 ae = load4f(Lr + C::OFF_AE + 4 * m4), aq = load4f(Lr + C::OFF_AQ + 4 * m4);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    pr += st[4 * m4 + j] * ae[j];
+                    pp += st[4 * m4 + j] * aq[j];
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                pr[c] = rows_allreduce<C::NRL>(pr[c]);
+                pp[c] = rows_allreduce<C::NRL>(pp[c]);
+            }
+            const f32x4 u = load4f(L + C::OFF_Z + col) - pr;
+            if (r == 0) {
+                const size_t tok = (size_t)b * a.T + t0 + tt;
+                store4f(og + (tok * a.Hv + h) * D + col, a.scale * (pp + L[C::OFF_MISC] * u));
+            }
+            const float as = L[C::OFF_MISC + 1];
+#pragma unroll
+            for (int m4 = 0; m4 < C::RPL / 4; ++m4) {
+                const f32x4 k4 = load4f(Lr + C::OFF_K + 4 * m4);
+                f32x4 al4;
+                if constexpr (CHAN) al4 = load4f(Lr + C::OFF_AL + 4 * m4);
+                else al4 = f32x4{as, as, as, as};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) st[4 * m4 + j] = st[4 * m4 + j] * al4[j] + k4[j] * u;
+            }
+        }
+    }
+
+#pragma unroll
+    for (int m = 0; m < C::RPL; ++m) store4f(a.ST + sbase + (size_t)m * D, st[m]);
+}
+
+template <typename IO, int D, int CW, bool CHAN>
+static hipError_t launch_rec_t(const RecurArgs &a, hipStream_t s) {
+    using C = RecurCfg<D, CW, CHAN>;
+    const unsigned grid = (unsigned)a.B * (unsigned)a.Hv * (unsigned)C::TILES;
+    hipLaunchKernelGGL((recurrent_kernel<IO, D, CW, CHAN>), dim3(grid), dim3(C::NT), 0, s, a);
+    return hipGetLastError();
+}
+
+template <typename IO, int D>
+static hipError_t launch_rec_d(const RecurArgs &a, hipStream_t s) {
+    const bool chan = a.decay == DECAY_CHANNEL;
+    // 32 value columns per wave fill the device once there are about four
+    // waves per SIMD; with fewer heads, 16 columns per wave double the waves.
+    const bool narrow = D >= 64 && (long long)a.B * a.Hv * (D / 32) < 4096;
+    if constexpr (D >= 64) {
+        if (narrow) return chan ? launch_rec_t<IO, D, 16, true>(a, s) : launch_rec_t<IO, D, 16, false>(a, s);
+    }
+    return chan ? launch_rec_t<IO, D, 32, true>(a, s) : launch_rec_t<IO, D, 32, false>(a, s);
+}
+
+hipError_t launch_recurrent(int io, int D, const RecurArgs &a, hipStream_t s) {
+    if (io == IO_BF16) {
+        if (D == 32) return launch_rec_d<bf16_t, 32>(a, s);
+        if (D == 64) return launch_rec_d<bf16_t, 64>(a, s);
+        if (D == 128) return launch_rec_d<bf16_t, 128>(a, s);
+    } else {
+        if (D == 32) return launch_rec_d<float, 32>(a, s);
+        if (D == 64) return launch_rec_d<float, 64>(a, s);
+        if (D == 128) return launch_rec_d<float, 128>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdr

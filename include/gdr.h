@@ -147,6 +147,24 @@ int gdr_decode_step(const gdr_desc *desc, const void *q, const void *k, const vo
                     const float *g, const float *beta, const void *b, const void *w,
                     float *S, void *o, void *stream);
 
+/* Fused recurrent forward over T tokens from a persistent state ("Kernel
+ * Triton recorrente fundido para decode", family analysis page): the
+ * token-by-token recurrence with each state block held in registers, so every
+ * state is read once and written once per call whatever T is. Meant for short
+ * runs from a live state (a few new tokens per sequence in serving, or
+ * checking k drafted tokens), where the chunked form's per-chunk factors cost
+ * more than they save. Arithmetic is about 4 d_k d_v flops per token and head
+ * on the vector units, so long prefills belong to gdr_chunk_fwd.
+ *   Layouts, gate modes and results (up to rounding order) as gdr_chunk_fwd;
+ *   desc->chunk is ignored and no workspace is needed. S0: initial state, or
+ *   NULL for zeros. ST: final state; may equal S0 (in-place update) and must
+ *   not otherwise overlap it (GDR_E_INVAL). T == 0 writes S0 (or zeros) to ST
+ *   and touches no per-token array. Supported: d_k == d_v in {32, 64, 128},
+ *   io float32 or bfloat16. */
+int gdr_recurrent_fwd(const gdr_desc *desc, const void *q, const void *k, const void *v,
+                      const float *g, const float *beta, const void *b, const void *w,
+                      const float *S0, void *o, float *ST, void *stream);
+
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char *gdr_last_error(void);
 

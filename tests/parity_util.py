@@ -60,6 +60,16 @@ def gpu_prefill(inp, S0=None, ST=None, scale=None, T_slice=None):
                              S0=S0, ST=ST, scale=wl.scale if scale is None else scale)
 
 
+def gpu_recurrent(inp, S0=None, ST=None, scale=None, T_slice=None):
+    """Run gdr_recurrent_fwd on the stored [B, T, ...] inputs; returns torch (o, ST)."""
+    import gated_delta_rule_23_amd as gdr
+    wl = inp["workload"]
+    sl = (lambda a: a) if T_slice is None else (lambda a: None if a is None else np.ascontiguousarray(a[:, T_slice]))
+    d = {n: to_dev(sl(inp[n])) for n in ("q", "k", "v", "g", "beta", "b", "w")}
+    return gdr.gdr_recurrent_fwd(d["q"], d["k"], d["v"], g=d["g"], beta=d["beta"], b=d["b"], w=d["w"],
+                                 S0=S0, ST=ST, scale=wl.scale if scale is None else scale)
+
+
 def oracle_prefill(inp, heads=None, cols=None, S0=None):
     wl = inp["workload"]
     return oracle.recurrent(inp["q"], inp["k"], inp["v"], g=inp["g"], beta=inp["beta"], b=inp["b"], w=inp["w"],

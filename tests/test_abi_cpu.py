@@ -136,6 +136,37 @@ def test_decode_rejections(case, expect):
     assert _dec(d, **case.get("args", {})) == expect
 
 
+def _rec(desc, q=P, k=P, v=P, g=P, beta=P, b=None, w=None, S0=None, o=P, ST=P):
+    return gdr.lib.gdr_recurrent_fwd(ctypes.byref(desc), q, k, v, g, beta, b, w, S0, o, ST, None)
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(desc=dict(Hv=5)), gdr.GDR_E_INVAL),
+    (dict(desc=dict(T=-1)), gdr.GDR_E_INVAL),
+    (dict(desc=dict(D=96)), gdr.GDR_E_UNSUPPORTED),
+    (dict(args=dict(ST=None)), gdr.GDR_E_INVAL),
+    (dict(args=dict(v=None)), gdr.GDR_E_INVAL),
+    (dict(args=dict(g=None)), gdr.GDR_E_INVAL),
+    (dict(args=dict(beta=None, w=P)), gdr.GDR_E_INVAL),
+    (dict(args=dict(S0=P + 8)), gdr.GDR_E_INVAL),                    # misaligned
+    (dict(args=dict(S0=P, ST=P + 4096)), gdr.GDR_E_INVAL),           # overlapping, not equal
+    (dict(args=dict(S0=P + 4096, ST=P)), gdr.GDR_E_INVAL),
+])
+def test_recurrent_rejections(case, expect):
+    d = _desc(**case.get("desc", {}))
+    assert _rec(d, **case.get("args", {})) == expect
+    assert gdr.gdr_last_error() != ""
+
+
+def test_recurrent_accepts_what_the_chunked_path_does_not():
+    """No chunk-length or float32-dimension limits: the chunk field is
+    ignored and float32 io runs at d = 128. B = 0 is a no-op on the CPU."""
+    d = _desc(B=0, io=gdr.GDR_F32, D=128)
+    d.chunk = 32
+    assert _rec(d) == gdr.GDR_OK
+    assert gdr.gdr_last_error() == ""
+
+
 def test_state_alloc_rejects_bad_sizes():
     p, n = ctypes.c_void_p(), ctypes.c_size_t()
     assert gdr.lib.gdr_state_alloc(0, 48, 128, 128, ctypes.byref(p), ctypes.byref(n), None) == gdr.GDR_E_INVAL

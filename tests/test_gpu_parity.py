@@ -9,8 +9,8 @@ import numpy as np
 import pytest
 
 import gdr_synth as gs
-from parity_util import (TOL, from_dev, gpu_decode, gpu_prefill, oracle_prefill, rel_err, say, small_workload,
-                         to_dev)
+from parity_util import (TOL, from_dev, gpu_decode, gpu_prefill, gpu_recurrent, oracle_prefill, rel_err, say,
+                         small_workload, to_dev)
 
 torch = pytest.importorskip("torch")
 pytestmark = [pytest.mark.gpu,
@@ -267,6 +267,153 @@ def test_prefill_empty_sequence_copies_state():
     torch.cuda.synchronize()
     assert torch.count_nonzero(ST) == 0
     assert gdr.gdr_last_error() == ""
+
+
+# ---------------------------------------------------------------------------
+# Multi-token recurrent forward (short runs from a live state).
+
+def _recurrent_wide(B, Hv, D):
+    """True when the library runs 32 value columns per wave (many heads);
+    with fewer heads it runs 16 (d >= 64). Restated so that a test can check
+    which variant it exercises."""
+    return D == 32 or B * Hv * (D // 32) >= 4096
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("decay,gates", MODES)
+@pytest.mark.parametrize("T", [1, 9, 20])
+def test_recurrent_small(io, D, decay, gates, T):
+    wl = small_workload(io, D, decay, gates, T=T, B=2, Hqk=1, Hv=2, S0=True)
+    inp = gs.make_inputs(wl, seed=3 * T + D)
+    say(f"recurrent {wl.name}")
+    o, ST = gpu_recurrent(inp, S0=to_dev(inp["S0"]))
+    o_ref, S_ref = oracle_prefill(inp)
+    assert rel_err(from_dev(o), o_ref) < TOL[io]
+    assert rel_err(from_dev(ST), S_ref) < TOL[io]
+
+
+@pytest.mark.parametrize("io,D,decay,gates,T", [
+    ("bf16", 128, "scalar", "beta", 4),
+    ("bf16", 128, "channel", "bw", 11),
+    ("f32", 64, "channel", "beta", 3),
+    ("bf16", 64, "scalar", "bw", 8),
+])
+def test_recurrent_many_heads(io, D, decay, gates, T):
+    """Serving shapes (64 sequences, 48 or 64 V heads, 16 QK heads): the
+    variant with 32 value columns per wave; a few new tokens per sequence from
+    a non-zero state, sampled heads against the oracle."""
+    Hv = 48 if D == 128 else 64
+    assert _recurrent_wide(64, Hv, D)
+    wl = small_workload(io, D, decay, gates, T=T, B=64, Hqk=16, Hv=Hv, S0=True, scale=D ** -0.5)
+    inp = gs.make_inputs(wl, seed=31)
+    say(f"recurrent {wl.name}")
+    o, ST = gpu_recurrent(inp, S0=to_dev(inp["S0"]))
+    heads = [0, 5, Hv // 2, Hv - 1]
+    o_ref, S_ref = oracle_prefill(inp, heads=heads)
+    assert rel_err(from_dev(o[:, :, heads]), o_ref[:, :, heads]) < TOL[io]
+    assert rel_err(from_dev(ST[:, heads]), S_ref[:, heads]) < TOL[io]
+    assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(ST).all())
+
+
+@pytest.mark.parametrize("io,D", [("bf16", 128), ("f32", 64), ("f32", 128)])
+def test_recurrent_grouped_heads_strong_decay(io, D):
+    wl = small_workload(io, D, "channel", "beta", T=37, B=2, Hqk=2, Hv=6, S0=True, scale=D ** -0.5)
+    wl = wl.scaled(g_recipe="logsigmoid_n21")
+    inp = gs.make_inputs(wl, seed=8)
+    say(f"recurrent {wl.name}")
+    o, ST = gpu_recurrent(inp, S0=to_dev(inp["S0"]))
+    o_ref, S_ref = oracle_prefill(inp)
+    assert rel_err(from_dev(o), o_ref) < TOL[io]
+    assert rel_err(from_dev(ST), S_ref) < TOL[io]
+
+
+def test_recurrent_equals_decode_steps_and_chunked():
+    """The three schedules compute one recurrence: a T-token recurrent call
+    equals T decode steps (float32, same per-token arithmetic up to reduction
+    order) and the chunked prefill (bfloat16 io, within its tolerance)."""
+    wl = small_workload("f32", 64, "channel", "bw", T=12, B=2, Hqk=1, Hv=2, S0=True)
+    inp = gs.make_inputs(wl, seed=15)
+    o_r, S_r = gpu_recurrent(inp, S0=to_dev(inp["S0"]))
+    step_major = {n: (None if inp[n] is None else np.ascontiguousarray(np.swapaxes(inp[n], 0, 1)))
+                  for n in ("q", "k", "v", "g", "beta", "b", "w")}
+    dec = dict(inp, **step_major)
+    dec["workload"] = wl.scaled(decode=True)
+    o_d, S_d = gpu_decode(dec)
+    assert rel_err(from_dev(o_r), np.swapaxes(o_d, 0, 1)) < 1e-5
+    assert rel_err(from_dev(S_r), S_d) < 1e-5
+
+    wl = small_workload("bf16", 128, "scalar", "beta", T=100, B=1, Hqk=1, Hv=3, S0=True)
+    inp = gs.make_inputs(wl, seed=16)
+    S0 = to_dev(inp["S0"])
+    o_r, S_r = gpu_recurrent(inp, S0=S0)
+    o_c, S_c = gpu_prefill(inp, S0=S0)
+    assert rel_err(from_dev(o_r), from_dev(o_c)) < TOL["bf16"]
+    assert rel_err(from_dev(S_r), from_dev(S_c)) < TOL["bf16"]
+
+
+def test_recurrent_split_resume_in_place_and_determinism():
+    """Verify-k style use: the state advances in place over consecutive short
+    calls and ends where one call over all the tokens ends, bit for bit (the
+    same per-token arithmetic in the same order); repeated calls agree bit for
+    bit."""
+    wl = small_workload("bf16", 128, "channel", "bw", T=21, B=3, Hqk=1, Hv=4, S0=True)
+    inp = gs.make_inputs(wl, seed=17)
+    S0 = to_dev(inp["S0"])
+    o_all, S_all = gpu_recurrent(inp, S0=S0)
+    o_again, S_again = gpu_recurrent(inp, S0=S0)
+    assert torch.equal(o_all, o_again) and torch.equal(S_all, S_again)
+    S = S0.clone()
+    outs = []
+    for a, b in ((0, 5), (5, 6), (6, 14), (14, 21)):
+        o, S_ret = gpu_recurrent(inp, S0=S, ST=S, T_slice=slice(a, b))
+        assert S_ret.data_ptr() == S.data_ptr()
+        outs.append(o)
+    assert torch.equal(torch.cat(outs, dim=1), o_all) and torch.equal(S, S_all)
+
+
+def test_recurrent_zero_tokens_copies_state():
+    import gated_delta_rule_23_amd as gdr
+    wl = small_workload("bf16", 64, "scalar", "beta", T=8, B=2, Hqk=1, Hv=2, S0=True)
+    inp = gs.make_inputs(wl, seed=18)
+    S0 = to_dev(inp["S0"])
+    o, ST = gpu_recurrent(inp, S0=S0, T_slice=slice(0, 0))
+    torch.cuda.synchronize()
+    assert o.shape[1] == 0 and torch.equal(ST, S0)
+    ST.fill_(1.0)
+    o, ST = gpu_recurrent(inp, S0=None, ST=ST, T_slice=slice(0, 0))
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(ST) == 0
+    assert gdr.gdr_last_error() == ""
+
+
+def test_recurrent_graph_replay_matches_eager():
+    import gated_delta_rule_23_amd as gdr
+    wl = small_workload("bf16", 128, "channel", "beta", T=4, B=8, Hqk=2, Hv=6, S0=True)
+    inp = gs.make_inputs(wl, seed=23)
+    d = {n: to_dev(inp[n]) for n in ("q", "k", "v", "g", "beta", "b", "w")}
+    S_init = to_dev(inp["S0"])
+    S = S_init.clone()
+    o = torch.empty((wl.B, wl.T, wl.Hv, wl.dv), dtype=torch.bfloat16, device="cuda:0")
+
+    def call():
+        gdr.gdr_recurrent_fwd(d["q"], d["k"], d["v"], g=d["g"], beta=d["beta"], S0=S, ST=S, o=o,
+                              stream=torch.cuda.current_stream())
+
+    call()
+    torch.cuda.synchronize()
+    o_ref, S_ref = o.clone(), S.clone()
+    S.copy_(S_init)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for _ in range(3):
+        S.copy_(S_init)
+        o.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(S, S_ref)
 
 
 def test_state_alloc_is_zeroed():
