@@ -13,7 +13,10 @@ call) for reference.
 
 --workload picks another prefill workload for the timed step (the KDA and
 Gated DeltaNet-2 layers, or the small fp32 case); --decode-steps 0 skips the
-decode measurement.
+decode measurement. Decode is also timed with the states of four layers
+advanced in turn, and the multi-token recurrent forward (gdr_recurrent_fwd,
+--recurrent-T tokens per sequence at the decode shape, four layers' states in
+turn) gets its own object; --recurrent-T 0 skips it.
 
 Prints one JSON line: value = prefill tokens/s; "roofline" for the prefill
 call against HBM; "decode" with state GB/s and its own roofline; and
@@ -29,6 +32,7 @@ import sys
 import time
 
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, published
+DECODE_COLD_LAYERS = 4        # states cycled in the decode "layers in turn" timing
 BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix, published
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -90,6 +94,17 @@ def decode_algorithmic(wl):
     return state, state + io
 
 
+def recurrent_algorithmic(wl):
+    """Bytes of one multi-token recurrent call: the state read and written once,
+    each token's inputs read once (q, k per QK head) and outputs written once."""
+    esz = 2 if wl.io == "bf16" else 4
+    B, T, Hqk, Hv, D = wl.B, wl.T, wl.Hqk, wl.Hv, wl.dk
+    by = 2 * B * Hv * D * D * 4 + 2 * B * T * Hqk * D * esz + 2 * B * T * Hv * D * esz
+    by += B * T * Hv * 4 if wl.gates == "beta" else 2 * B * T * Hv * D * esz
+    by += {"none": 0, "scalar": B * T * Hv * 4, "channel": B * T * Hv * D * 4}[wl.decay]
+    return by
+
+
 def cpu_baseline(wl, inp, heads, min_seconds=10.0, max_reps=200):
     """Time the fp64 oracle (as it stands) on the given V heads of the prefill
     workload, repeating the run until about min_seconds of CPU work."""
@@ -114,6 +129,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-steps", type=int, default=256, help="consecutive decode steps timed (0 = skip decode)")
+    ap.add_argument("--recurrent-T", type=int, default=4,
+                    help="tokens per sequence of the multi-token recurrent call timed at the decode shape (0 = skip)")
     ap.add_argument("--workload", default="qwen_gdn_prefill",
                     choices=["qwen_gdn_prefill", "kda_prefill", "gdn2_prefill", "gdn_small_f32"],
                     help="prefill workload of the timed step (default: the Qwen-shaped GDN layer, T=4096)")
@@ -247,16 +264,85 @@ def main(argv=None):
         torch.cuda.synchronize()
         del dgraph
         d_step_ms = d0.elapsed_time(d1) / dwl.T
+        # The same steps over the states of LAYERS layers in turn (step s
+        # advances layer s % LAYERS), as in a model where every other layer's
+        # state passes through the memory-side cache between two steps of one
+        # layer: a 201 MB state alone fits the 256 MB cache, so consecutive
+        # steps on one state could be served partly from it.
+        layers = [S] + [S0d.clone() for _ in range(DECODE_COLD_LAYERS - 1)]
+
+        def dstep_layer(s):
+            pick = lambda t: None if t is None else t[s]
+            gdr.gdr_decode_step(pick(dd["q"]), pick(dd["k"]), pick(dd["v"]), layers[s % len(layers)],
+                                g=pick(dd["g"]), beta=pick(dd["beta"]), b=pick(dd["b"]), w=pick(dd["w"]),
+                                scale=dwl.scale, o=do, stream=cur())
+
+        cgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(cgraph):
+            for s in range(dwl.T):
+                dstep_layer(s)
+        cgraph.replay()
+        torch.cuda.synchronize()
+        d0.record(cur())
+        cgraph.replay()
+        d1.record(cur())
+        torch.cuda.synchronize()
+        del cgraph, layers
+        d_cold_ms = d0.elapsed_time(d1) / dwl.T
         state_bytes, d_bytes = decode_algorithmic(dwl)
         d_achieved = d_bytes / (d_step_ms * 1e-3) / 1e9
         dec = {"workload": dwl.name, "steps": dwl.T, "launch": "hip_graph", "ms_per_step": d_step_ms,
                "eager_ms_per_step": d_eager_ms,
                "state_GBps": state_bytes / (d_step_ms * 1e-3) / 1e9,
                "tokens_per_s": dwl.B / (d_step_ms * 1e-3),
+               "layers_in_turn": {"layers": DECODE_COLD_LAYERS, "ms_per_step": d_cold_ms,
+                                  "state_GBps": state_bytes / (d_cold_ms * 1e-3) / 1e9,
+                                  "hbm_frac": d_bytes / (d_cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS},
                "roofline": {"kernel": "decode_kernel", "bound": "hbm", "achieved": d_achieved,
                             "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": d_achieved / HBM_PEAK_GBPS,
                             "traffic": recorded_traffic(dwl.name) if dwl.T == 256 else None,
                             "algorithmic_bytes": d_bytes}}
+
+    # ---- multi-token recurrent forward (a few tokens per sequence from a live state) ----
+    rec = None
+    if args.recurrent_T > 0:
+        rwl = gs.QWEN_GDN_DECODE.scaled(T=args.recurrent_T, decode=False,
+                                        name=f"qwen_gdn_verify_B64_Hv48_d128_T{args.recurrent_T}")
+        rinp = gs.make_inputs(rwl, seed=args.seed + 2)
+        rd = {n: up(rinp[n]) for n in ("q", "k", "v", "g", "beta", "b", "w")}
+        r_states = [up(rinp["S0"]) for _ in range(DECODE_COLD_LAYERS)]
+        ro = torch.empty((rwl.B, rwl.T, rwl.Hv, rwl.dv), dtype=torch.bfloat16, device=dev)
+        n_calls = 64
+
+        def rcall(i):
+            Sl = r_states[i % len(r_states)]
+            gdr.gdr_recurrent_fwd(rd["q"], rd["k"], rd["v"], g=rd["g"], beta=rd["beta"], b=rd["b"], w=rd["w"],
+                                  S0=Sl, ST=Sl, scale=rwl.scale, o=ro, stream=cur())
+
+        for i in range(len(r_states)):
+            rcall(i)
+        torch.cuda.synchronize()
+        rgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(rgraph):
+            for i in range(n_calls):
+                rcall(i)
+        rgraph.replay()
+        torch.cuda.synchronize()
+        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        r0.record(cur())
+        rgraph.replay()
+        r1.record(cur())
+        torch.cuda.synchronize()
+        del rgraph, r_states
+        r_ms = r0.elapsed_time(r1) / n_calls
+        r_state, _ = decode_algorithmic(rwl)
+        r_bytes = recurrent_algorithmic(rwl)
+        rec = {"workload": rwl.name, "calls": n_calls, "layers_in_turn": DECODE_COLD_LAYERS, "launch": "hip_graph",
+               "ms_per_call": r_ms, "tokens_per_s": rwl.B * rwl.T / (r_ms * 1e-3),
+               "state_GBps": r_state / (r_ms * 1e-3) / 1e9,
+               "roofline": {"kernel": "recurrent_kernel", "bound": "hbm",
+                            "achieved": r_bytes / (r_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                            "frac": r_bytes / (r_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, "algorithmic_bytes": r_bytes}}
 
     out = {
         "metric": "prefill tokens/s and decode state GB/s for gated delta rule, % of roofline",
@@ -281,6 +367,7 @@ def main(argv=None):
         "mfma": {"algorithmic_tflops": pflops / (avg_call_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
                  "frac": pflops / (avg_call_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, "algorithmic_flops": pflops},
         "decode": dec,
+        "recurrent": rec,
     }
     if args.cpu_heads > 0:
         heads = list(range(0, wl.Hv, max(1, wl.Hv // min(args.cpu_heads, wl.Hv))))[:args.cpu_heads]

@@ -115,6 +115,17 @@ __device__ __forceinline__ f32x4 load4f(const bf16_t *p) {
     return f32x4{bf2f(u[0]), bf2f(u[1]), bf2f(u[2]), bf2f(u[3])};
 }
 __device__ __forceinline__ void store4f(float *p, f32x4 x) { *reinterpret_cast<f32x4 *>(p) = x; }
+
+// Four consecutive fp32 state entries (16-byte aligned) read or written with a
+// non-temporal hint: state blocks are streamed once per call and not reused
+// before they would be evicted, so they are kept from displacing other data in
+// the caches (MI355X's memory-side cache included).
+__device__ __forceinline__ f32x4 load_state4(const float *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+}
+__device__ __forceinline__ void store_state4(float *p, f32x4 x) {
+    __builtin_nontemporal_store(x, reinterpret_cast<f32x4 *>(p));
+}
 __device__ __forceinline__ void store4f(bf16_t *p, f32x4 x) {
     *reinterpret_cast<uint2 *>(p) = uint2{f2bf2(x[0], x[1]), f2bf2(x[2], x[3])};
 }

@@ -20,6 +20,9 @@
 // accesses, and the state crosses HBM exactly once each way. The k-axis
 // reductions combine lanes of a wave by shuffles and the waves through LDS.
 // No matrix cores: the step is 0.9 flop per byte of state, bandwidth bound.
+// The state is read and written with non-temporal accesses: nothing reuses it
+// before the next step, by which time a model has streamed every other
+// layer's state through the memory-side cache.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -47,10 +50,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const int wave = tid >> 6, lane = tid & 63;
 
     float *S = a.S + (size_t)bh * D * D;
-    float4 st[NR];
+    f32x4 st[NR];
 #pragma unroll
-    for (int m = 0; m < NR; ++m)
-        st[m] = *reinterpret_cast<const float4 *>(S + (size_t)(ty + m * RS) * D + 4 * tx);
+    for (int m = 0; m < NR; ++m) st[m] = load_state4(S + (size_t)(ty + m * RS) * D + 4 * tx);
 
     const IO *qp = static_cast<const IO *>(a.q) + ((size_t)b * a.Hqk + hq) * D;
     const IO *kp = static_cast<const IO *>(a.k) + ((size_t)b * a.Hqk + hq) * D;
@@ -71,9 +73,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     for (int m = 0; m < NR; ++m) {
         const int i = ty + m * RS;
         const float al = s_al[i], e = s_e[i], qv = s_q[i];
-        st[m].x *= al; st[m].y *= al; st[m].z *= al; st[m].w *= al;
-        pr[0] += st[m].x * e; pr[1] += st[m].y * e; pr[2] += st[m].z * e; pr[3] += st[m].w * e;
-        pp[0] += st[m].x * qv; pp[1] += st[m].y * qv; pp[2] += st[m].z * qv; pp[3] += st[m].w * qv;
+        st[m] *= al;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            pr[c] += st[m][c] * e;
+            pp[c] += st[m][c] * qv;
+        }
     }
 #pragma unroll
     for (int off = CG; off < 64; off <<= 1) {
@@ -119,8 +124,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int m = 0; m < NR; ++m) {
         const float ki = s_k[ty + m * RS];
-        st[m].x += ki * u[0]; st[m].y += ki * u[1]; st[m].z += ki * u[2]; st[m].w += ki * u[3];
-        *reinterpret_cast<float4 *>(S + (size_t)(ty + m * RS) * D + 4 * tx) = st[m];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) st[m][c] += ki * u[c];
+        store_state4(S + (size_t)(ty + m * RS) * D + 4 * tx, st[m]);
     }
     if (ty == 0) {
         IO *op = static_cast<IO *>(a.o) + (size_t)bh * D + 4 * tx;

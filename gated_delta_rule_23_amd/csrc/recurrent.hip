@@ -24,7 +24,9 @@
 // LDS TB tokens at a time already combined into alpha.e, alpha.q, k (and
 // alpha per key channel), z and q . k; one barrier per staged block.
 //
-// Work per token and head is about 4 D^2 flops against D^2 fp32 of state
+// The state is streamed with non-temporal loads and stores (it is not reused
+// within the call, and a model touches every other layer's state before this
+// one's next call). Work per token and head is about 4 D^2 flops against D^2 fp32 of state
 // that is read and written once per call: a run of a few tokens is bound by
 // HBM, a long one by the vector ALUs (long prefills belong to the chunked
 // path, whose products run on the matrix cores).
@@ -87,7 +89,7 @@ __global__ __launch_bounds__((RecurCfg<D, CW, CHAN>::NT)) void recurrent_kernel(
 
     f32x4 st[C::RPL];
 #pragma unroll
-    for (int m = 0; m < C::RPL; ++m) st[m] = a.S0 ? load4f(a.S0 + sbase + (size_t)m * D) : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < C::RPL; ++m) st[m] = a.S0 ? load_state4(a.S0 + sbase + (size_t)m * D) : f32x4{0.f, 0.f, 0.f, 0.f};
 
     const IO *qg = static_cast<const IO *>(a.q), *kg = static_cast<const IO *>(a.k);
     const IO *vg = static_cast<const IO *>(a.v);
@@ -177,7 +179,7 @@ __global__ __launch_bounds__((RecurCfg<D, CW, CHAN>::NT)) void recurrent_kernel(
     }
 
 #pragma unroll
-    for (int m = 0; m < C::RPL; ++m) store4f(a.ST + sbase + (size_t)m * D, st[m]);
+    for (int m = 0; m < C::RPL; ++m) store_state4(a.ST + sbase + (size_t)m * D, st[m]);
 }
 
 template <typename IO, int D, int CW, bool CHAN>
