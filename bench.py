@@ -342,7 +342,8 @@ def main(argv=None):
                "state_GBps": r_state / (r_ms * 1e-3) / 1e9,
                "roofline": {"kernel": "recurrent_kernel", "bound": "hbm",
                             "achieved": r_bytes / (r_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                            "frac": r_bytes / (r_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, "algorithmic_bytes": r_bytes}}
+                            "frac": r_bytes / (r_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                            "traffic": recorded_traffic(rwl.name), "algorithmic_bytes": r_bytes}}
 
     out = {
         "metric": "prefill tokens/s and decode state GB/s for gated delta rule, % of roofline",

@@ -131,13 +131,11 @@ template <> struct Km<bf16_t> {
     // Multiply the 8 elements of a fragment (8 consecutive K indices) by f[0..7].
     __device__ __forceinline__ static u16x8 scale(u16x8 x, const float *f) {
         const f32x4 f0 = load4f(f), f1 = load4f(f + 4);
-        typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
         const u32x4 r = {f2bf2(bf2f(x[0]) * f0[0], bf2f(x[1]) * f0[1]), f2bf2(bf2f(x[2]) * f0[2], bf2f(x[3]) * f0[3]),
                          f2bf2(bf2f(x[4]) * f1[0], bf2f(x[5]) * f1[1]), f2bf2(bf2f(x[6]) * f1[2], bf2f(x[7]) * f1[3])};
         return __builtin_bit_cast(u16x8, r);
     }
     __device__ __forceinline__ static u16x8 scale(u16x8 x, float f) {
-        typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
         const u32x4 r = {f2bf2(bf2f(x[0]) * f, bf2f(x[1]) * f), f2bf2(bf2f(x[2]) * f, bf2f(x[3]) * f),
                          f2bf2(bf2f(x[4]) * f, bf2f(x[5]) * f), f2bf2(bf2f(x[6]) * f, bf2f(x[7]) * f)};
         return __builtin_bit_cast(u16x8, r);
@@ -186,6 +184,10 @@ template <> struct Raw16<float> {
     }
 };
 __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
+// 16-byte store with a non-temporal hint, for outputs nothing here reads back.
+__device__ __forceinline__ void st16_stream(void *p, uint4 x) {
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, x), reinterpret_cast<u32x4 *>(p));
+}
 
 // ---------------------------------------------------------------------------
 // chunk_prep: everything in a chunk that does not depend on the state, for
@@ -827,8 +829,7 @@ __device__ __forceinline__ void out_chunk(const OutOps<IO, D, NCT, CHAN> &op, co
         for (int i = l; i < 16 * PER; i += 64) {
             const int tok = T0 + i / PER, c8 = (i % PER) * V;
             if (!TAIL || tok < n_valid)
-                *reinterpret_cast<uint4 *>(orow0 + tok * orow_stride + c8) =
-                    *reinterpret_cast<const uint4 *>(sO + tok * LO + c8);
+                st16_stream(orow0 + tok * orow_stride + c8, *reinterpret_cast<const uint4 *>(sO + tok * LO + c8));
         }
     }
 }

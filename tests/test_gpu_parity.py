@@ -372,6 +372,33 @@ def test_recurrent_split_resume_in_place_and_determinism():
     assert torch.equal(torch.cat(outs, dim=1), o_all) and torch.equal(S, S_all)
 
 
+@pytest.mark.parametrize("io,decay,D", [("f32", "channel", 64), ("bf16", "channel", 128), ("f32", "scalar", 32),
+                                         ("bf16", "scalar", 128)])
+def test_recurrent_extreme_decay(io, decay, D):
+    """Very negative log decays: whole key channels (or heads) forgetting
+    within a few tokens, including alpha that underflows to zero in fp32
+    (g = -200), against the oracle."""
+    wl = small_workload(io, D, decay, "beta", T=21, B=2, Hqk=1, Hv=2, S0=True)
+    inp = gs.make_inputs(wl, seed=19)
+    g = inp["g"].copy()
+    if decay == "channel":
+        g[:, 3, :, : D // 4] = -30.0
+        g[:, 4, :, : D // 8] = -15.0
+        g[:, 10, 1, 5] = -200.0            # alpha = 0 in fp32
+        g[:, 17, 0, :] = -45.0             # every channel of one head at once
+    else:
+        g[:, 2, :] = -45.0
+        g[:, 9, 1] = -200.0
+        g[:, 12, 0] = -25.0
+        g[:, 13, 0] = -25.0
+    inp = dict(inp, g=g)
+    say(f"recurrent extreme decay {wl.name}")
+    o, ST = gpu_recurrent(inp, S0=to_dev(inp["S0"]))
+    o_ref, S_ref = oracle_prefill(inp)
+    assert rel_err(from_dev(o), o_ref) < TOL[io]
+    assert rel_err(from_dev(ST), S_ref) < TOL[io]
+
+
 def test_recurrent_zero_tokens_copies_state():
     import gated_delta_rule_23_amd as gdr
     wl = small_workload("bf16", 64, "scalar", "beta", T=8, B=2, Hqk=1, Hv=2, S0=True)
