@@ -143,6 +143,54 @@ def make_inputs(wl: Workload, seed: int = 0) -> dict:
     return out
 
 
+RAW_ORDER = ORDER + ("conv_w", "conv_in")
+
+
+def make_raw_inputs(wl: Workload, seed: int = 0, conv_state: bool = True) -> dict:
+    """Draw the raw inputs of the input stage for ``wl`` (prefill layout
+    [B, T, ...]): q, k, v ~ N(0, 1) before the convolution (not normalised);
+    per-channel convolution taps ~ N(0, 0.5^2), shape [2 Hqk dk + Hv dv, 4];
+    an incoming convolution state of 3 raw tokens ~ N(0, 1) (None when
+    conv_state is False); gate inputs ~ N(0, 1) (sigmoid inputs for beta,
+    b, w); decay inputs x with a per-V-head constant c such that
+    -c softplus(x) follows the workload's decay recipe (x ~ N(0, 1) and
+    c = 0.1 or 0.05, or x = -(2 + N(0, 1)) and c = 1 for log sigmoid
+    N(2, 1)). Same stream scheme as make_inputs, with two more streams."""
+    streams = dict(zip(RAW_ORDER, (np.random.Generator(np.random.PCG64(s))
+                                   for s in np.random.SeedSequence(seed).spawn(len(RAW_ORDER)))))
+    lead = (wl.B, wl.T)
+    ch = 2 * wl.Hqk * wl.dk + wl.Hv * wl.dv
+    out = {"workload": wl, "seed": seed}
+    out["q"] = _store(streams["q"].standard_normal(lead + (wl.Hqk, wl.dk)), wl.io)
+    out["k"] = _store(streams["k"].standard_normal(lead + (wl.Hqk, wl.dk)), wl.io)
+    out["v"] = _store(streams["v"].standard_normal(lead + (wl.Hv, wl.dv)), wl.io)
+    out["conv_w"] = _store(0.5 * streams["conv_w"].standard_normal((ch, 4)), "f32")
+    out["conv_in"] = _store(streams["conv_in"].standard_normal((wl.B, 3, ch)), wl.io) if conv_state else None
+    if wl.gates == "beta":
+        out["beta"] = _store(streams["beta"].standard_normal(lead + (wl.Hv,)), "f32")
+        out["b"] = out["w"] = None
+    else:
+        out["beta"] = None
+        out["b"] = _store(streams["b"].standard_normal(lead + (wl.Hv, wl.dk)), wl.io)
+        out["w"] = _store(streams["w"].standard_normal(lead + (wl.Hv, wl.dv)), wl.io)
+    out["decay_scale"] = None
+    if wl.decay == "none":
+        out["g"] = None
+    else:
+        gshape = lead + ((wl.Hv,) if wl.decay == "scalar" else (wl.Hv, wl.dk))
+        x = streams["g"].standard_normal(gshape)
+        c = {"logsigmoid_n21": 1.0, "softplus_0.1": 0.1, "softplus_0.05": 0.05}[wl.g_recipe]
+        if wl.g_recipe == "logsigmoid_n21":
+            x = -(2.0 + x)
+        out["g"] = _store(x, "f32")
+        out["decay_scale"] = np.full(wl.Hv, c, dtype=np.float32)
+    if wl.S0 == "normal_0.02":
+        out["S0"] = _store(0.02 * streams["S0"].standard_normal((wl.B, wl.Hv, wl.dk, wl.dv)), "f32")
+    else:
+        out["S0"] = None
+    return out
+
+
 def as_sequence(inp: dict) -> dict:
     """Decode inputs are step-major [steps, B, ...]; return a copy with every
     per-step tensor reordered to [B, steps, ...] (a sequential run's layout)."""
