@@ -29,13 +29,19 @@ CHUNK = 64
 
 # Every symbol include/gdr.h declares.
 EXPORTS = ("gdr_state_bytes", "gdr_state_alloc", "gdr_state_free", "gdr_chunk_workspace_bytes",
-           "gdr_chunk_fwd", "gdr_decode_step", "gdr_recurrent_fwd", "gdr_last_error", "gdr_version")
+           "gdr_chunk_fwd", "gdr_decode_step", "gdr_recurrent_fwd", "gdr_recurrent_fwd_in", "gdr_last_error",
+           "gdr_version")
 
 
 class GdrError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"libgdr status {status}: {message}")
         self.status = status
+
+
+class gdr_input_stage(ctypes.Structure):
+    _fields_ = [("conv_w", ctypes.c_void_p), ("conv_in", ctypes.c_void_p), ("conv_out", ctypes.c_void_p),
+                ("decay_scale", ctypes.c_void_p)]
 
 
 class gdr_desc(ctypes.Structure):
@@ -72,6 +78,8 @@ def _load():
     lib.gdr_decode_step.argtypes = [D, P, P, P, P, P, P, P, P, P, P]
     lib.gdr_recurrent_fwd.restype = I
     lib.gdr_recurrent_fwd.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P]
+    lib.gdr_recurrent_fwd_in.restype = I
+    lib.gdr_recurrent_fwd_in.argtypes = [D, ctypes.POINTER(gdr_input_stage), P, P, P, P, P, P, P, P, P, P, P]
     lib.gdr_last_error.restype = ctypes.c_char_p
     lib.gdr_last_error.argtypes = []
     lib.gdr_version.restype = I
@@ -248,3 +256,42 @@ def gdr_recurrent_fwd(q, k, v, *, g=None, beta=None, b=None, w=None, S0=None, sc
     _check(lib.gdr_recurrent_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(b),
                                  _ptr(w), _ptr(S0), _ptr(o), _ptr(ST), _stream(stream)))
     return o, ST
+
+
+def gdr_recurrent_fwd_in(q, k, v, conv_w, *, conv_in=None, conv_out=None, decay_scale=None, g=None, beta=None,
+                         b=None, w=None, S0=None, scale=1.0, o=None, ST=None, stream=None):
+    """gdr_recurrent_fwd with the input stage fused in: q [B,T,Hqk,D], k, v
+    are raw projections; beta, b, w gate inputs before the sigmoid; g the
+    decay input before -c softplus; conv_w [(2 Hqk + Hv) D, 4] float32 taps;
+    conv_in [B, 3, (2 Hqk + Hv) D] (io dtype) or None for zeros; decay_scale
+    [Hv] float32 or None. Returns (o, ST, conv_out); conv_out (the last 3 raw
+    tokens) is allocated when None and not written when False."""
+    torch = _torch()
+    B, T, Hqk, D = q.shape
+    Hv = v.shape[2]
+    dev, io_t = q.device, q.dtype
+    ch = (2 * Hqk + Hv) * D
+    for name, t, shape in (("q", q, (B, T, Hqk, D)), ("k", k, (B, T, Hqk, D)), ("v", v, (B, T, Hv, D)),
+                           ("b", b, (B, T, Hv, D)), ("w", w, (B, T, Hv, D)), ("conv_in", conv_in, (B, 3, ch))):
+        _require(t, name, shape, io_t, dev)
+    _require(conv_w, "conv_w", (ch, 4), torch.float32, dev)
+    _require(decay_scale, "decay_scale", (Hv,), torch.float32, dev)
+    _require(beta, "beta", (B, T, Hv), torch.float32, dev)
+    _require(g, "g", None, torch.float32, dev)
+    _require(S0, "S0", (B, Hv, D, D), torch.float32, dev)
+    desc = make_desc(B, T, Hqk, Hv, D, _io_dtype(q), _decay_of(g, (B, T), Hv, D), scale)
+    if o is None:
+        o = torch.empty((B, T, Hv, D), dtype=io_t, device=dev)
+    if ST is None:
+        ST = torch.empty((B, Hv, D, D), dtype=torch.float32, device=dev)
+    if conv_out is None:
+        conv_out = torch.empty((B, 3, ch), dtype=io_t, device=dev)
+    elif conv_out is False:
+        conv_out = None
+    _require(o, "o", (B, T, Hv, D), io_t, dev)
+    _require(ST, "ST", (B, Hv, D, D), torch.float32, dev)
+    _require(conv_out, "conv_out", (B, 3, ch), io_t, dev)
+    stage = gdr_input_stage(_ptr(conv_w), _ptr(conv_in), _ptr(conv_out), _ptr(decay_scale))
+    _check(lib.gdr_recurrent_fwd_in(ctypes.byref(desc), ctypes.byref(stage), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                    _ptr(beta), _ptr(b), _ptr(w), _ptr(S0), _ptr(o), _ptr(ST), _stream(stream)))
+    return o, ST, conv_out

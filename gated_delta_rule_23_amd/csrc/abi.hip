@@ -89,6 +89,10 @@ int validate(const gdr_desc *d, CallKind kind, const void *q, const void *k, con
 // The kernels read and write the io arrays, the state and the workspace with
 // 16-byte vector accesses; beta and a scalar decay are read per element.
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+bool overlap(const void *x, const void *y, size_t n) {
+    const char *a = static_cast<const char *>(x), *b = static_cast<const char *>(y);
+    return a < b + n && b < a + n;
+}
 int check_alignment(const gdr_desc *d, std::initializer_list<const void *> vec16, const float *g, const float *beta) {
     for (const void *p : vec16)
         if (p && !aligned(p, 16)) return fail(GDR_E_INVAL, "array pointers must be 16-byte aligned");
@@ -203,9 +207,9 @@ int gdr_decode_step(const gdr_desc *d, const void *q, const void *k, const void 
     return ok();
 }
 
-int gdr_recurrent_fwd(const gdr_desc *d, const void *q, const void *k, const void *v, const float *g,
-                      const float *beta, const void *b, const void *w, const float *S0, void *o, float *ST,
-                      void *stream) {
+static int recurrent_call(const gdr_desc *d, const gdr_input_stage *stage, const void *q, const void *k,
+                          const void *v, const float *g, const float *beta, const void *b, const void *w,
+                          const float *S0, void *o, float *ST, void *stream) {
     int rc = validate(d, CALL_RECURRENT, q, k, v, g, beta, b, w, o);
     if (rc != GDR_OK) return rc;
     if (!ST) return fail(GDR_E_INVAL, "ST must be non-NULL");
@@ -213,8 +217,18 @@ int gdr_recurrent_fwd(const gdr_desc *d, const void *q, const void *k, const voi
     if (rc != GDR_OK) return rc;
     if (S0 && S0 != ST) {
         const size_t n = gdr_state_bytes(d->B, d->H_v, d->d_k, d->d_v);
-        const char *s0 = reinterpret_cast<const char *>(S0), *st = reinterpret_cast<const char *>(ST);
-        if (s0 < st + n && st < s0 + n) return fail(GDR_E_INVAL, "ST must equal S0 or not overlap it");
+        if (overlap(S0, ST, n)) return fail(GDR_E_INVAL, "ST must equal S0 or not overlap it");
+    }
+    if (stage) {
+        if (!stage->conv_w) return fail(GDR_E_INVAL, "the input stage needs conv_w");
+        if (!aligned(stage->conv_w, 16) || (stage->conv_in && !aligned(stage->conv_in, 16)) ||
+            (stage->conv_out && !aligned(stage->conv_out, 16)) ||
+            (stage->decay_scale && !aligned(stage->decay_scale, 4)))
+            return fail(GDR_E_INVAL, "input-stage arrays are misaligned");
+        const size_t conv_bytes = (size_t)d->B * 3 * (2 * (size_t)d->H_qk + d->H_v) * d->d_k *
+                                  (d->io_dtype == GDR_BF16 ? 2 : 4);
+        if (stage->conv_in && stage->conv_out && overlap(stage->conv_in, stage->conv_out, conv_bytes))
+            return fail(GDR_E_INVAL, "conv_out must not overlap conv_in");
     }
     if (d->B == 0) return ok();
     // At most two workgroups per (sequence, V head).
@@ -223,10 +237,29 @@ int gdr_recurrent_fwd(const gdr_desc *d, const void *q, const void *k, const voi
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.bg = b; a.wg = w;
     a.S0 = S0; a.ST = ST; a.o = o;
     a.B = d->B; a.T = d->T; a.Hqk = d->H_qk; a.Hv = d->H_v; a.decay = d->decay; a.scale = d->scale;
+    if (stage) {
+        a.conv_w = stage->conv_w;
+        a.conv_in = stage->conv_in;
+        a.conv_out = stage->conv_out;
+        a.decay_scale = stage->decay_scale;
+    }
     hipError_t e = gdr::launch_recurrent(d->io_dtype == GDR_BF16 ? gdr::IO_BF16 : gdr::IO_F32, d->d_k, a,
                                          static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "recurrent launch");
     return ok();
+}
+
+int gdr_recurrent_fwd(const gdr_desc *d, const void *q, const void *k, const void *v, const float *g,
+                      const float *beta, const void *b, const void *w, const float *S0, void *o, float *ST,
+                      void *stream) {
+    return recurrent_call(d, nullptr, q, k, v, g, beta, b, w, S0, o, ST, stream);
+}
+
+int gdr_recurrent_fwd_in(const gdr_desc *d, const gdr_input_stage *stage, const void *q, const void *k,
+                         const void *v, const float *g, const float *beta, const void *b, const void *w,
+                         const float *S0, void *o, float *ST, void *stream) {
+    if (!stage) return fail(GDR_E_INVAL, "stage is NULL");
+    return recurrent_call(d, stage, q, k, v, g, beta, b, w, S0, o, ST, stream);
 }
 
 }  // extern "C"

@@ -33,6 +33,12 @@ struct RecurArgs {
     void *o;                 // [B,T,Hv,D]
     int B, T, Hqk, Hv, decay;
     float scale;
+    // Input stage (conv_w non-null): q, k, v are raw projections and the
+    // gate and decay arrays hold their inputs before the activations.
+    const float *conv_w;     // [(2 Hqk + Hv) D, 4] taps
+    const void *conv_in;     // [B, 3, (2 Hqk + Hv) D] or null (zeros)
+    void *conv_out;          // same layout, or null
+    const float *decay_scale;  // [Hv] or null (1)
 };
 
 struct ChunkArgs {

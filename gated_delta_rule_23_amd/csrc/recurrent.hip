@@ -71,7 +71,40 @@ __device__ __forceinline__ float rows_allreduce(float x) {
 
 __device__ __forceinline__ f32x4 exp4(f32x4 g) { return f32x4{expf(g[0]), expf(g[1]), expf(g[2]), expf(g[3])}; }
 
-template <typename IO, int D, int CW, bool CHAN>
+// q and k are normalised as x / sqrt(sum x^2 + kNormEps).
+constexpr float kNormEps = 1e-12f;
+
+// Input-stage activations: the logistic function for the gates, and
+// softplus(x) = max(x, 0) + log(1 + exp(-|x|)) for the decay.
+__device__ __forceinline__ float sigmoid1(float x) { return 1.f / (1.f + expf(-x)); }
+__device__ __forceinline__ f32x4 sigmoid4(f32x4 x) {
+    return f32x4{sigmoid1(x[0]), sigmoid1(x[1]), sigmoid1(x[2]), sigmoid1(x[3])};
+}
+__device__ __forceinline__ float softplus1(float x) { return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))); }
+
+// One 4-channel slice of the input stage for token t of sequence b: the
+// depthwise causal convolution of kernel 4 over tokens t-3 .. t (tokens
+// before 0 from the convolution state, zeros without one). x points at
+// channel group i0 of token 0 of the sequence in a [T, H, D] array (token
+// stride ts); cin at the same channels of the state's first row (row
+// stride ch) or null; taps at this slice's [4][4] taps (channel-major).
+template <typename IO>
+__device__ __forceinline__ f32x4 conv4_slice(const IO *x, size_t ts, int t, const IO *cin, size_t ch,
+                                             const float *taps) {
+    f32x4 acc{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int tj = t - 3 + j;
+        f32x4 xj{0.f, 0.f, 0.f, 0.f};
+        if (tj >= 0) xj = load4f(x + (size_t)tj * ts);
+        else if (cin) xj = load4f(cin + (size_t)(3 + tj) * ch);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] += taps[4 * c + j] * xj[c];
+    }
+    return acc;
+}
+
+template <typename IO, int D, int CW, bool CHAN, bool RAW>
 __global__ __launch_bounds__((RecurCfg<D, CW, CHAN>::NT)) void recurrent_kernel(RecurArgs a) {
     using C = RecurCfg<D, CW, CHAN>;
     constexpr int G = D / 4;  // 4-element groups of one token's key or value vector
@@ -107,23 +140,66 @@ __global__ __launch_bounds__((RecurCfg<D, CW, CHAN>::NT)) void recurrent_kernel(
             const size_t xk = (tok * a.Hqk + hq) * D + i0;
             const size_t xs = tok * a.Hv + h;
             const size_t xv = xs * D + i0;
-            const f32x4 q = load4f(qg + xk), k = load4f(kg + xk), v = load4f(vg + xv);
-            f32x4 e, z;
-            if (a.beta) {
-                const float bt = a.beta[xs];
-                e = bt * k;
-                z = bt * v;
-            } else {
-                e = load4f(bgp + xv) * k;
-                z = load4f(wgp + xv) * v;
-            }
+            f32x4 q, k, v, e, z, al;
             float as = 1.f;
-            f32x4 al;
-            if constexpr (CHAN) {
-                al = exp4(load4f(a.g + xv));
+            if constexpr (RAW) {
+                // Input stage: convolve the raw projections, normalise q and k
+                // over the head (the token's G lanes), gates from their inputs.
+                const int t = t0 + tt;
+                const size_t ch = (size_t)(2 * a.Hqk + a.Hv) * D;
+                const size_t sqk = (size_t)a.Hqk * D, sv = (size_t)a.Hv * D;
+                const size_t cq = (size_t)hq * D + i0, ck = sqk + cq, cv = 2 * sqk + (size_t)h * D + i0;
+                const IO *cin = static_cast<const IO *>(a.conv_in) + (size_t)b * 3 * ch;
+                const bool has_in = a.conv_in != nullptr;
+                const size_t seq_qk = (size_t)b * a.T * sqk, seq_v = (size_t)b * a.T * sv;
+                q = conv4_slice(qg + seq_qk + cq, sqk, t, has_in ? cin + cq : nullptr, ch, a.conv_w + cq * 4);
+                k = conv4_slice(kg + seq_qk + cq, sqk, t, has_in ? cin + ck : nullptr, ch, a.conv_w + ck * 4);
+                v = conv4_slice(vg + seq_v + (size_t)h * D + i0, sv, t, has_in ? cin + cv : nullptr, ch,
+                                a.conv_w + cv * 4);
+                float nq = q[0] * q[0] + q[1] * q[1] + q[2] * q[2] + q[3] * q[3];
+                float nk = k[0] * k[0] + k[1] * k[1] + k[2] * k[2] + k[3] * k[3];
+#pragma unroll
+                for (int off = 1; off < G; off <<= 1) {
+                    nq += __shfl_xor(nq, off);
+                    nk += __shfl_xor(nk, off);
+                }
+                q *= 1.f / sqrtf(nq + kNormEps);
+                k *= 1.f / sqrtf(nk + kNormEps);
+                if (a.beta) {
+                    const float bt = sigmoid1(a.beta[xs]);
+                    e = bt * k;
+                    z = bt * v;
+                } else {
+                    e = sigmoid4(load4f(bgp + xv)) * k;
+                    z = sigmoid4(load4f(wgp + xv)) * v;
+                }
+                const float c = a.decay_scale ? a.decay_scale[h] : 1.f;
+                if constexpr (CHAN) {
+                    const f32x4 gi = load4f(a.g + xv);
+                    al = exp4(f32x4{-c * softplus1(gi[0]), -c * softplus1(gi[1]), -c * softplus1(gi[2]),
+                                    -c * softplus1(gi[3])});
+                } else {
+                    if (a.decay == DECAY_SCALAR) as = expf(-c * softplus1(a.g[xs]));
+                    al = f32x4{as, as, as, as};
+                }
             } else {
-                if (a.decay == DECAY_SCALAR) as = expf(a.g[xs]);
-                al = f32x4{as, as, as, as};
+                q = load4f(qg + xk);
+                k = load4f(kg + xk);
+                v = load4f(vg + xv);
+                if (a.beta) {
+                    const float bt = a.beta[xs];
+                    e = bt * k;
+                    z = bt * v;
+                } else {
+                    e = load4f(bgp + xv) * k;
+                    z = load4f(wgp + xv) * v;
+                }
+                if constexpr (CHAN) {
+                    al = exp4(load4f(a.g + xv));
+                } else {
+                    if (a.decay == DECAY_SCALAR) as = expf(a.g[xs]);
+                    al = f32x4{as, as, as, as};
+                }
             }
             float *L = lds + tt * C::STR;
             const int p = (i0 / C::RPL) * C::RP + i0 % C::RPL;
@@ -180,13 +256,45 @@ __global__ __launch_bounds__((RecurCfg<D, CW, CHAN>::NT)) void recurrent_kernel(
 
 #pragma unroll
     for (int m = 0; m < C::RPL; ++m) store_state4(a.ST + sbase + (size_t)m * D, st[m]);
+
+    if constexpr (RAW) {
+        // The convolution state after the call: the last 3 raw tokens
+        // (token T-3+j in row j; rows before token 0 come from the incoming
+        // state). Tile 0 of each V head writes its v channels; the first V
+        // head of each QK group also writes the group's q and k channels.
+        if (a.conv_out && tile == 0) {
+            const bool qk_too = h % (a.Hv / a.Hqk) == 0;
+            const size_t ch = (size_t)(2 * a.Hqk + a.Hv) * D;
+            const size_t sqk = (size_t)a.Hqk * D, sv = (size_t)a.Hv * D;
+            const IO *cin = static_cast<const IO *>(a.conv_in);
+            IO *cout = static_cast<IO *>(a.conv_out) + (size_t)b * 3 * ch;
+            for (int u = tid; u < 3 * 3 * G; u += C::NT) {
+                const int part = u / (3 * G), j = (u / G) % 3, i0 = 4 * (u % G);  // part 0: v, 1: q, 2: k
+                if (part > 0 && !qk_too) continue;
+                const int tj = a.T - 3 + j;
+                const size_t c0 = part == 0 ? 2 * sqk + (size_t)h * D + i0 : (part == 2 ? sqk : 0) + (size_t)hq * D + i0;
+                f32x4 x{0.f, 0.f, 0.f, 0.f};
+                if (tj >= 0) {
+                    const IO *src = part == 0 ? vg + ((size_t)b * a.T + tj) * sv + (size_t)h * D + i0
+                                              : (part == 1 ? qg : kg) + ((size_t)b * a.T + tj) * sqk + (size_t)hq * D + i0;
+                    x = load4f(src);
+                } else if (cin) {
+                    x = load4f(cin + ((size_t)b * 3 + 3 + tj) * ch + c0);
+                }
+                store4f(cout + (size_t)j * ch + c0, x);
+            }
+        }
+    }
 }
 
 template <typename IO, int D, int CW, bool CHAN>
 static hipError_t launch_rec_t(const RecurArgs &a, hipStream_t s) {
     using C = RecurCfg<D, CW, CHAN>;
     const unsigned grid = (unsigned)a.B * (unsigned)a.Hv * (unsigned)C::TILES;
-    hipLaunchKernelGGL((recurrent_kernel<IO, D, CW, CHAN>), dim3(grid), dim3(C::NT), 0, s, a);
+    if (a.conv_w)
+        hipLaunchKernelGGL((recurrent_kernel<IO, D, CW, CHAN, true>), dim3(grid), dim3(C::NT), 0, s, a);
+    else
+        hipLaunchKernelGGL((recurrent_kernel<IO, D, CW, CHAN, false>), dim3(grid), dim3(C::NT), 0, s, a);
     return hipGetLastError();
 }
 

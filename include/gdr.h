@@ -165,6 +165,44 @@ int gdr_recurrent_fwd(const gdr_desc *desc, const void *q, const void *k, const 
                       const float *g, const float *beta, const void *b, const void *w,
                       const float *S0, void *o, float *ST, void *stream);
 
+/* The input stage: the step just before the recurrence, turning raw
+ * projections into q, k, v and gates ("Gated DeltaNet: o mixer em 48 das 64
+ * camadas", section "Conceito": a short causal depthwise convolution of
+ * kernel 4 over the projected sequences; family analysis page, "Notação e
+ * ordem da derivação": normalised keys; Gated DeltaNet-2 post, its code
+ * listing: sigmoid erase and write gates). With it, per token t:
+ *   x'_t = sum_{j=0..3} conv_w[c][j] x_{t-3+j}   per channel c, tokens before
+ *          t = 0 taken from conv_in (zeros if NULL); no activation follows
+ *   q = x'_q / sqrt(|x'_q|^2 + 1e-12), k likewise (per token and head over
+ *          d_k); v = x'_v
+ *   beta = sigmoid(beta_in); b = sigmoid(b_in); w = sigmoid(w_in)
+ *   g = -c_h softplus(g_in), c_h = decay_scale[h] (1 if NULL)
+ * Convolution channels are ordered: the H_qk*d_k channels of q, then those
+ * of k, then the H_v*d_v channels of v (head-major in each).
+ * Alignment: conv_w, conv_in and conv_out 16 bytes; decay_scale 4 bytes. */
+typedef struct {
+    const float *conv_w;       /* [2*H_qk*d_k + H_v*d_v, 4] float32 taps; tap 3
+                                  multiplies the current token. Required. */
+    const void *conv_in;       /* [B, 3, channels] io: the 3 raw tokens before
+                                  this call (row 2 = the latest); NULL = zeros */
+    void *conv_out;            /* [B, 3, channels] io: written with the last 3
+                                  raw tokens (rows before the call's first
+                                  token come from conv_in), the next call's
+                                  conv_in; NULL = not written. Must not
+                                  overlap conv_in (ping-pong two buffers). */
+    const float *decay_scale;  /* [H_v] float32 c_h > 0, or NULL for 1 */
+} gdr_input_stage;
+
+/* gdr_recurrent_fwd with the input stage fused into its token loop: q, k, v
+ * are the raw projections (before the convolution), beta, b, w the gate
+ * inputs before the sigmoid and g the decay input before -c softplus, in
+ * gdr_recurrent_fwd's layouts. A decode step is the T = 1 call, with conv_in
+ * and conv_out alternating between two buffers. stage must be non-NULL with
+ * conv_w set; GDR_E_INVAL otherwise (or if conv_out overlaps conv_in). */
+int gdr_recurrent_fwd_in(const gdr_desc *desc, const gdr_input_stage *stage, const void *q, const void *k,
+                         const void *v, const float *g, const float *beta, const void *b, const void *w,
+                         const float *S0, void *o, float *ST, void *stream);
+
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char *gdr_last_error(void);
 

@@ -70,6 +70,32 @@ def gpu_recurrent(inp, S0=None, ST=None, scale=None, T_slice=None):
                                  S0=S0, ST=ST, scale=wl.scale if scale is None else scale)
 
 
+def gpu_recurrent_in(raw, S0=None, ST=None, conv_in="stored", conv_out=None, T_slice=None):
+    """Run gdr_recurrent_fwd_in on raw inputs from gdr_synth.make_raw_inputs;
+    returns torch (o, ST, conv_out). conv_in="stored" uses the drawn state."""
+    import gated_delta_rule_23_amd as gdr
+    wl = raw["workload"]
+    sl = (lambda a: a) if T_slice is None else (lambda a: None if a is None else np.ascontiguousarray(a[:, T_slice]))
+    d = {n: to_dev(sl(raw[n])) for n in ("q", "k", "v", "g", "beta", "b", "w")}
+    cin = to_dev(raw["conv_in"]) if isinstance(conv_in, str) else conv_in
+    return gdr.gdr_recurrent_fwd_in(d["q"], d["k"], d["v"], to_dev(raw["conv_w"]), conv_in=cin, conv_out=conv_out,
+                                    decay_scale=to_dev(raw["decay_scale"]), g=d["g"], beta=d["beta"], b=d["b"],
+                                    w=d["w"], S0=S0, ST=ST, scale=wl.scale)
+
+
+def oracle_input_stage(raw, heads=None, cols=None, S0="stored", conv_in="stored"):
+    """The input-stage oracle, then the recurrence oracle. Returns (o, S_T,
+    conv_out) in fp64."""
+    from oracle import input_stage as ist
+    wl = raw["workload"]
+    cin = raw["conv_in"] if isinstance(conv_in, str) else conv_in
+    st, conv_out = ist.input_stage(raw["q"], raw["k"], raw["v"], raw["conv_w"], conv_in=cin, g=raw["g"],
+                                   beta=raw["beta"], b=raw["b"], w=raw["w"], decay_scale=raw["decay_scale"])
+    o, S = oracle.recurrent(st["q"], st["k"], st["v"], g=st["g"], beta=st["beta"], b=st["b"], w=st["w"],
+                            scale=wl.scale, S0=raw["S0"] if isinstance(S0, str) else S0, heads=heads, cols=cols)
+    return o, S, conv_out
+
+
 def oracle_prefill(inp, heads=None, cols=None, S0=None):
     wl = inp["workload"]
     return oracle.recurrent(inp["q"], inp["k"], inp["v"], g=inp["g"], beta=inp["beta"], b=inp["b"], w=inp["w"],

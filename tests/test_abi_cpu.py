@@ -158,6 +158,31 @@ def test_recurrent_rejections(case, expect):
     assert gdr.gdr_last_error() != ""
 
 
+def _rec_in(desc, stage, q=P, k=P, v=P, g=P, beta=P, b=None, w=None, S0=None, o=P, ST=P):
+    st = None if stage is None else ctypes.byref(gdr.gdr_input_stage(*stage))
+    return gdr.lib.gdr_recurrent_fwd_in(ctypes.byref(desc), st, q, k, v, g, beta, b, w, S0, o, ST, None)
+
+
+@pytest.mark.parametrize("stage,expect", [
+    (None, gdr.GDR_E_INVAL),                                        # no stage
+    ((None, None, None, None), gdr.GDR_E_INVAL),                    # no taps
+    ((P + 8, None, None, None), gdr.GDR_E_INVAL),                   # misaligned taps
+    ((P, P + 4, P + (1 << 20), None), gdr.GDR_E_INVAL),            # misaligned conv_in
+    ((P, P, P + 64, None), gdr.GDR_E_INVAL),                        # conv_out overlaps conv_in
+    ((P, P + 64, P, None), gdr.GDR_E_INVAL),
+    ((P, None, None, P + 2), gdr.GDR_E_INVAL),                      # misaligned decay_scale
+])
+def test_recurrent_input_stage_rejections(stage, expect):
+    assert _rec_in(_desc(), stage) == expect
+    assert gdr.gdr_last_error() != ""
+
+
+def test_recurrent_input_stage_zero_batch_and_separate_conv_buffers():
+    d = _desc(B=0)
+    assert _rec_in(d, (P, P, P + (1 << 20), P)) == gdr.GDR_OK
+    assert gdr.gdr_last_error() == ""
+
+
 def test_recurrent_accepts_what_the_chunked_path_does_not():
     """No chunk-length or float32-dimension limits: the chunk field is
     ignored and float32 io runs at d = 128. B = 0 is a no-op on the CPU."""

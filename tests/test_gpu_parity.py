@@ -9,8 +9,8 @@ import numpy as np
 import pytest
 
 import gdr_synth as gs
-from parity_util import (TOL, from_dev, gpu_decode, gpu_prefill, gpu_recurrent, oracle_prefill, rel_err, say,
-                         small_workload, to_dev)
+from parity_util import (TOL, from_dev, gpu_decode, gpu_prefill, gpu_recurrent, gpu_recurrent_in,
+                         oracle_input_stage, oracle_prefill, rel_err, say, small_workload, to_dev)
 
 torch = pytest.importorskip("torch")
 pytestmark = [pytest.mark.gpu,
@@ -441,6 +441,86 @@ def test_recurrent_graph_replay_matches_eager():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(o, o_ref) and torch.equal(S, S_ref)
+
+
+# ---------------------------------------------------------------------------
+# Input stage fused into the recurrent forward (raw projections in).
+
+def _conv_equal(c_gpu, c_ref):
+    """The convolution state is a copy of stored raw values: exact."""
+    return np.array_equal(from_dev(c_gpu), np.asarray(c_ref, dtype=np.float64))
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("decay,gates", MODES)
+@pytest.mark.parametrize("T", [1, 2, 9])
+def test_recurrent_input_stage_small(io, D, decay, gates, T):
+    """T = 1 and 2 take part of the convolution window from the incoming
+    convolution state; T = 9 spans two staged blocks."""
+    wl = small_workload(io, D, decay, gates, T=T, B=2, Hqk=1, Hv=2, S0=True, scale=D ** -0.5)
+    raw = gs.make_raw_inputs(wl, seed=5 * T + D)
+    say(f"input stage {wl.name}")
+    o, ST, cout = gpu_recurrent_in(raw, S0=to_dev(raw["S0"]))
+    o_ref, S_ref, c_ref = oracle_input_stage(raw)
+    assert rel_err(from_dev(o), o_ref) < TOL[io]
+    assert rel_err(from_dev(ST), S_ref) < TOL[io]
+    assert _conv_equal(cout, c_ref)
+
+
+@pytest.mark.parametrize("io,D,decay,gates", [("bf16", 128, "scalar", "beta"), ("bf16", 64, "channel", "bw")])
+def test_recurrent_input_stage_without_conv_state(io, D, decay, gates):
+    wl = small_workload(io, D, decay, gates, T=5, B=3, Hqk=2, Hv=4, S0=False)
+    raw = gs.make_raw_inputs(wl, seed=41, conv_state=False)
+    o, ST, cout = gpu_recurrent_in(raw, conv_in=None)
+    o_ref, S_ref, c_ref = oracle_input_stage(raw, conv_in=None)
+    assert rel_err(from_dev(o), o_ref) < TOL[io]
+    assert rel_err(from_dev(ST), S_ref) < TOL[io]
+    assert _conv_equal(cout, c_ref)
+
+
+def test_recurrent_input_stage_serving_shape():
+    """64 sequences, 16 QK heads, 48 V heads, d = 128, 4 raw tokens per call
+    from a live state and convolution state (the variant with 32 value
+    columns per wave); sampled heads against the oracle, the whole
+    convolution state exactly."""
+    wl = gs.QWEN_GDN_DECODE.scaled(T=4, decode=False)
+    raw = gs.make_raw_inputs(wl, seed=43)
+    say(f"input stage {wl.name}")
+    o, ST, cout = gpu_recurrent_in(raw, S0=to_dev(raw["S0"]))
+    heads = [0, 1, 2, 30, 47]
+    o_ref, S_ref, c_ref = oracle_input_stage(raw, heads=heads)
+    assert rel_err(from_dev(o[:, :, heads]), o_ref[:, :, heads]) < TOL["bf16"]
+    assert rel_err(from_dev(ST[:, heads]), S_ref[:, heads]) < TOL["bf16"]
+    assert _conv_equal(cout, c_ref)
+
+
+def test_recurrent_input_stage_decode_steps_equal_one_call():
+    """Decode as T = 1 calls with the convolution state alternating between
+    two buffers and the state updated in place gives, bit for bit, what one
+    call over all the tokens gives (same per-token arithmetic)."""
+    wl = small_workload("bf16", 128, "channel", "bw", T=7, B=2, Hqk=2, Hv=4, S0=True)
+    raw = gs.make_raw_inputs(wl, seed=44)
+    S0 = to_dev(raw["S0"])
+    o_all, S_all, c_all = gpu_recurrent_in(raw, S0=S0)
+    S = S0.clone()
+    bufs = [to_dev(raw["conv_in"]).clone(), torch.empty_like(c_all)]
+    outs = []
+    for t in range(wl.T):
+        o, _, _ = gpu_recurrent_in(raw, S0=S, ST=S, conv_in=bufs[t % 2], conv_out=bufs[(t + 1) % 2],
+                                   T_slice=slice(t, t + 1))
+        outs.append(o)
+    assert torch.equal(torch.cat(outs, dim=1), o_all) and torch.equal(S, S_all)
+    assert torch.equal(bufs[wl.T % 2], c_all)
+
+
+def test_recurrent_input_stage_zero_tokens():
+    wl = small_workload("bf16", 64, "scalar", "beta", T=4, B=2, Hqk=1, Hv=2, S0=True)
+    raw = gs.make_raw_inputs(wl, seed=45)
+    S0 = to_dev(raw["S0"])
+    o, ST, cout = gpu_recurrent_in(raw, S0=S0, T_slice=slice(0, 0))
+    torch.cuda.synchronize()
+    assert torch.equal(ST, S0) and torch.equal(cout, to_dev(raw["conv_in"]))
 
 
 def test_state_alloc_is_zeroed():
