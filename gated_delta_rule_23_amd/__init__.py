@@ -29,7 +29,7 @@ CHUNK = 64
 
 # Every symbol include/gdr.h declares.
 EXPORTS = ("gdr_state_bytes", "gdr_state_alloc", "gdr_state_free", "gdr_chunk_workspace_bytes",
-           "gdr_chunk_fwd", "gdr_decode_step", "gdr_recurrent_fwd", "gdr_recurrent_fwd_in", "gdr_last_error",
+           "gdr_chunk_fwd", "gdr_decode_step", "gdr_recurrent_fwd", "gdr_recurrent_fwd_in", "gdr_chunk_fwd_in", "gdr_last_error",
            "gdr_version")
 
 
@@ -80,6 +80,8 @@ def _load():
     lib.gdr_recurrent_fwd.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P]
     lib.gdr_recurrent_fwd_in.restype = I
     lib.gdr_recurrent_fwd_in.argtypes = [D, ctypes.POINTER(gdr_input_stage), P, P, P, P, P, P, P, P, P, P, P]
+    lib.gdr_chunk_fwd_in.restype = I
+    lib.gdr_chunk_fwd_in.argtypes = [D, ctypes.POINTER(gdr_input_stage), P, P, P, P, P, P, P, P, P, P, P, S, P]
     lib.gdr_last_error.restype = ctypes.c_char_p
     lib.gdr_last_error.argtypes = []
     lib.gdr_version.restype = I
@@ -258,6 +260,57 @@ def gdr_recurrent_fwd(q, k, v, *, g=None, beta=None, b=None, w=None, S0=None, sc
     return o, ST
 
 
+def _stage_args(q, v, conv_w, conv_in, conv_out, decay_scale):
+    """Shared checks of the input-stage arguments; returns (stage struct,
+    conv_out tensor or None)."""
+    torch = _torch()
+    B, _, Hqk, D = q.shape
+    Hv = v.shape[2]
+    ch = (2 * Hqk + Hv) * D
+    _require(conv_in, "conv_in", (B, 3, ch), q.dtype, q.device)
+    _require(conv_w, "conv_w", (ch, 4), torch.float32, q.device)
+    _require(decay_scale, "decay_scale", (Hv,), torch.float32, q.device)
+    if conv_out is None:
+        conv_out = torch.empty((B, 3, ch), dtype=q.dtype, device=q.device)
+    elif conv_out is False:
+        conv_out = None
+    _require(conv_out, "conv_out", (B, 3, ch), q.dtype, q.device)
+    return gdr_input_stage(_ptr(conv_w), _ptr(conv_in), _ptr(conv_out), _ptr(decay_scale)), conv_out
+
+
+def gdr_chunk_fwd_in(q, k, v, conv_w, *, conv_in=None, conv_out=None, decay_scale=None, g=None, beta=None, b=None,
+                     w=None, S0=None, scale=1.0, chunk=CHUNK, o=None, ST=None, workspace=None, stream=None):
+    """gdr_chunk_fwd with the input stage fused into its load stage; the
+    arguments of gdr_recurrent_fwd_in plus the workspace. Returns (o, ST,
+    conv_out)."""
+    torch = _torch()
+    B, T, Hqk, D = q.shape
+    Hv = v.shape[2]
+    dev, io_t = q.device, q.dtype
+    for name, t, shape in (("q", q, (B, T, Hqk, D)), ("k", k, (B, T, Hqk, D)), ("v", v, (B, T, Hv, D)),
+                           ("b", b, (B, T, Hv, D)), ("w", w, (B, T, Hv, D))):
+        _require(t, name, shape, io_t, dev)
+    _require(beta, "beta", (B, T, Hv), torch.float32, dev)
+    _require(g, "g", None, torch.float32, dev)
+    _require(S0, "S0", (B, Hv, D, D), torch.float32, dev)
+    stage, conv_out = _stage_args(q, v, conv_w, conv_in, conv_out, decay_scale)
+    desc = make_desc(B, T, Hqk, Hv, D, _io_dtype(q), _decay_of(g, (B, T), Hv, D), scale, chunk)
+    if o is None:
+        o = torch.empty((B, T, Hv, D), dtype=io_t, device=dev)
+    if ST is None:
+        ST = torch.empty((B, Hv, D, D), dtype=torch.float32, device=dev)
+    _require(o, "o", (B, T, Hv, D), io_t, dev)
+    _require(ST, "ST", (B, Hv, D, D), torch.float32, dev)
+    nbytes = gdr_chunk_workspace_bytes(desc)
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.gdr_chunk_fwd_in(ctypes.byref(desc), ctypes.byref(stage), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                _ptr(beta), _ptr(b), _ptr(w), _ptr(S0), _ptr(o), _ptr(ST), _ptr(workspace), wsz,
+                                _stream(stream)))
+    return o, ST, conv_out
+
+
 def gdr_recurrent_fwd_in(q, k, v, conv_w, *, conv_in=None, conv_out=None, decay_scale=None, g=None, beta=None,
                          b=None, w=None, S0=None, scale=1.0, o=None, ST=None, stream=None):
     """gdr_recurrent_fwd with the input stage fused in: q [B,T,Hqk,D], k, v
@@ -270,12 +323,9 @@ def gdr_recurrent_fwd_in(q, k, v, conv_w, *, conv_in=None, conv_out=None, decay_
     B, T, Hqk, D = q.shape
     Hv = v.shape[2]
     dev, io_t = q.device, q.dtype
-    ch = (2 * Hqk + Hv) * D
     for name, t, shape in (("q", q, (B, T, Hqk, D)), ("k", k, (B, T, Hqk, D)), ("v", v, (B, T, Hv, D)),
-                           ("b", b, (B, T, Hv, D)), ("w", w, (B, T, Hv, D)), ("conv_in", conv_in, (B, 3, ch))):
+                           ("b", b, (B, T, Hv, D)), ("w", w, (B, T, Hv, D))):
         _require(t, name, shape, io_t, dev)
-    _require(conv_w, "conv_w", (ch, 4), torch.float32, dev)
-    _require(decay_scale, "decay_scale", (Hv,), torch.float32, dev)
     _require(beta, "beta", (B, T, Hv), torch.float32, dev)
     _require(g, "g", None, torch.float32, dev)
     _require(S0, "S0", (B, Hv, D, D), torch.float32, dev)
@@ -284,14 +334,9 @@ def gdr_recurrent_fwd_in(q, k, v, conv_w, *, conv_in=None, conv_out=None, decay_
         o = torch.empty((B, T, Hv, D), dtype=io_t, device=dev)
     if ST is None:
         ST = torch.empty((B, Hv, D, D), dtype=torch.float32, device=dev)
-    if conv_out is None:
-        conv_out = torch.empty((B, 3, ch), dtype=io_t, device=dev)
-    elif conv_out is False:
-        conv_out = None
+    stage, conv_out = _stage_args(q, v, conv_w, conv_in, conv_out, decay_scale)
     _require(o, "o", (B, T, Hv, D), io_t, dev)
     _require(ST, "ST", (B, Hv, D, D), torch.float32, dev)
-    _require(conv_out, "conv_out", (B, 3, ch), io_t, dev)
-    stage = gdr_input_stage(_ptr(conv_w), _ptr(conv_in), _ptr(conv_out), _ptr(decay_scale))
     _check(lib.gdr_recurrent_fwd_in(ctypes.byref(desc), ctypes.byref(stage), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                     _ptr(beta), _ptr(b), _ptr(w), _ptr(S0), _ptr(o), _ptr(ST), _stream(stream)))
     return o, ST, conv_out

@@ -101,6 +101,104 @@ int check_alignment(const gdr_desc *d, std::initializer_list<const void *> vec16
     return GDR_OK;
 }
 
+// Bytes of one convolution state [B, 3, (2 H_qk + H_v) d] in the io dtype.
+size_t conv_state_bytes(const gdr_desc *d) {
+    return (size_t)d->B * 3 * (2 * (size_t)d->H_qk + d->H_v) * d->d_k * (d->io_dtype == GDR_BF16 ? 2 : 4);
+}
+
+// The input stage's own checks (stage may be NULL: no input stage).
+int check_stage(const gdr_desc *d, const gdr_input_stage *stage) {
+    if (!stage) return GDR_OK;
+    if (!stage->conv_w) return fail(GDR_E_INVAL, "the input stage needs conv_w");
+    if (!aligned(stage->conv_w, 16) || (stage->conv_in && !aligned(stage->conv_in, 16)) ||
+        (stage->conv_out && !aligned(stage->conv_out, 16)) || (stage->decay_scale && !aligned(stage->decay_scale, 4)))
+        return fail(GDR_E_INVAL, "input-stage arrays are misaligned");
+    if (stage->conv_in && stage->conv_out && overlap(stage->conv_in, stage->conv_out, conv_state_bytes(d)))
+        return fail(GDR_E_INVAL, "conv_out must not overlap conv_in");
+    return GDR_OK;
+}
+
+int chunk_call(const gdr_desc *d, const gdr_input_stage *stage, const void *q, const void *k, const void *v,
+                      const float *g, const float *beta, const void *b, const void *w, const float *S0, void *o,
+                      float *ST, void *workspace, size_t workspace_bytes, void *stream) {
+    int rc = validate(d, CALL_CHUNK, q, k, v, g, beta, b, w, o);
+    if (rc != GDR_OK) return rc;
+    if (!ST) return fail(GDR_E_INVAL, "ST must be non-NULL");
+    rc = check_alignment(d, {q, k, v, b, w, o, S0, ST, workspace}, g, beta);
+    if (rc != GDR_OK) return rc;
+    rc = check_stage(d, stage);
+    if (rc != GDR_OK) return rc;
+    const int io = d->io_dtype == GDR_BF16 ? gdr::IO_BF16 : gdr::IO_F32;
+    const int NC = (d->T + gdr::kChunk - 1) / gdr::kChunk;
+    const gdr::ChunkWsLayout L = gdr::chunk_ws_layout(d->B, d->H_qk, d->H_v, NC, d->d_k, io, d->decay == GDR_DECAY_CHANNEL);
+    const size_t need = L.total();
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(GDR_E_INVAL, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+    if (d->B == 0) return ok();
+    const size_t units = (size_t)d->B * d->H_v * NC;
+    if (units > 0x7fffffffull) return fail(GDR_E_UNSUPPORTED, "too many chunks for one launch");
+
+    gdr::ChunkArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.bg = b; a.wg = w;
+    a.S0 = S0; a.o = o; a.ST = ST;
+    a.ws_io = workspace;
+    a.ws_tab = reinterpret_cast<float *>(static_cast<char *>(workspace) + L.io_bytes);
+    a.ws_kT = L.kT_bytes ? static_cast<char *>(workspace) + L.io_bytes + L.tab_bytes : nullptr;
+    a.ws_seg = L.seg_bytes ? reinterpret_cast<float *>(static_cast<char *>(workspace) + L.io_bytes + L.tab_bytes +
+                                                       L.kT_bytes)
+                           : nullptr;
+    gdr::chunk_segments(d->B, d->H_v, d->d_k, NC, a.P, a.L);
+    a.B = d->B; a.T = d->T; a.Hqk = d->H_qk; a.Hv = d->H_v; a.decay = d->decay; a.NC = NC;
+    a.scale = d->scale;
+    if (stage) {
+        a.conv_w = stage->conv_w;
+        a.conv_in = stage->conv_in;
+        a.conv_out = stage->conv_out;
+        a.decay_scale = stage->decay_scale;
+    }
+    hipError_t e = gdr::launch_chunk(io, d->d_k, a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "chunk prefill launch");
+    if (stage && stage->conv_out && NC == 0) {  // no chunk: the state passes through unchanged
+        e = gdr::launch_state_fill(static_cast<float *>(stage->conv_out), static_cast<const float *>(stage->conv_in),
+                                   conv_state_bytes(d) / sizeof(float), static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return hip_fail(e, "convolution state copy");
+    }
+    return ok();
+}
+
+int recurrent_call(const gdr_desc *d, const gdr_input_stage *stage, const void *q, const void *k,
+                          const void *v, const float *g, const float *beta, const void *b, const void *w,
+                          const float *S0, void *o, float *ST, void *stream) {
+    int rc = validate(d, CALL_RECURRENT, q, k, v, g, beta, b, w, o);
+    if (rc != GDR_OK) return rc;
+    if (!ST) return fail(GDR_E_INVAL, "ST must be non-NULL");
+    rc = check_alignment(d, {q, k, v, b, w, o, S0, ST}, g, beta);
+    if (rc != GDR_OK) return rc;
+    if (S0 && S0 != ST) {
+        const size_t n = gdr_state_bytes(d->B, d->H_v, d->d_k, d->d_v);
+        if (overlap(S0, ST, n)) return fail(GDR_E_INVAL, "ST must equal S0 or not overlap it");
+    }
+    rc = check_stage(d, stage);
+    if (rc != GDR_OK) return rc;
+    if (d->B == 0) return ok();
+    // At most two workgroups per (sequence, V head).
+    if ((long long)d->B * d->H_v * 2 > 0x7fffffffll) return fail(GDR_E_UNSUPPORTED, "B * H_v too large for one launch");
+    gdr::RecurArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.bg = b; a.wg = w;
+    a.S0 = S0; a.ST = ST; a.o = o;
+    a.B = d->B; a.T = d->T; a.Hqk = d->H_qk; a.Hv = d->H_v; a.decay = d->decay; a.scale = d->scale;
+    if (stage) {
+        a.conv_w = stage->conv_w;
+        a.conv_in = stage->conv_in;
+        a.conv_out = stage->conv_out;
+        a.decay_scale = stage->decay_scale;
+    }
+    hipError_t e = gdr::launch_recurrent(d->io_dtype == GDR_BF16 ? gdr::IO_BF16 : gdr::IO_F32, d->d_k, a,
+                                         static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "recurrent launch");
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -154,40 +252,6 @@ int gdr_chunk_workspace_bytes(const gdr_desc *d, size_t *bytes) {
     return ok();
 }
 
-int gdr_chunk_fwd(const gdr_desc *d, const void *q, const void *k, const void *v, const float *g, const float *beta,
-                  const void *b, const void *w, const float *S0, void *o, float *ST, void *workspace,
-                  size_t workspace_bytes, void *stream) {
-    int rc = validate(d, CALL_CHUNK, q, k, v, g, beta, b, w, o);
-    if (rc != GDR_OK) return rc;
-    if (!ST) return fail(GDR_E_INVAL, "ST must be non-NULL");
-    rc = check_alignment(d, {q, k, v, b, w, o, S0, ST, workspace}, g, beta);
-    if (rc != GDR_OK) return rc;
-    const int io = d->io_dtype == GDR_BF16 ? gdr::IO_BF16 : gdr::IO_F32;
-    const int NC = (d->T + gdr::kChunk - 1) / gdr::kChunk;
-    const gdr::ChunkWsLayout L = gdr::chunk_ws_layout(d->B, d->H_qk, d->H_v, NC, d->d_k, io, d->decay == GDR_DECAY_CHANNEL);
-    const size_t need = L.total();
-    if (need > 0 && (!workspace || workspace_bytes < need))
-        return fail(GDR_E_INVAL, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
-    if (d->B == 0) return ok();
-    const size_t units = (size_t)d->B * d->H_v * NC;
-    if (units > 0x7fffffffull) return fail(GDR_E_UNSUPPORTED, "too many chunks for one launch");
-
-    gdr::ChunkArgs a{};
-    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.bg = b; a.wg = w;
-    a.S0 = S0; a.o = o; a.ST = ST;
-    a.ws_io = workspace;
-    a.ws_tab = reinterpret_cast<float *>(static_cast<char *>(workspace) + L.io_bytes);
-    a.ws_kT = L.kT_bytes ? static_cast<char *>(workspace) + L.io_bytes + L.tab_bytes : nullptr;
-    a.ws_seg = L.seg_bytes ? reinterpret_cast<float *>(static_cast<char *>(workspace) + L.io_bytes + L.tab_bytes +
-                                                       L.kT_bytes)
-                           : nullptr;
-    gdr::chunk_segments(d->B, d->H_v, d->d_k, NC, a.P, a.L);
-    a.B = d->B; a.T = d->T; a.Hqk = d->H_qk; a.Hv = d->H_v; a.decay = d->decay; a.NC = NC;
-    a.scale = d->scale;
-    hipError_t e = gdr::launch_chunk(io, d->d_k, a, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "chunk prefill launch");
-    return ok();
-}
 
 int gdr_decode_step(const gdr_desc *d, const void *q, const void *k, const void *v, const float *g, const float *beta,
                     const void *b, const void *w, float *S, void *o, void *stream) {
@@ -207,52 +271,24 @@ int gdr_decode_step(const gdr_desc *d, const void *q, const void *k, const void 
     return ok();
 }
 
-static int recurrent_call(const gdr_desc *d, const gdr_input_stage *stage, const void *q, const void *k,
-                          const void *v, const float *g, const float *beta, const void *b, const void *w,
-                          const float *S0, void *o, float *ST, void *stream) {
-    int rc = validate(d, CALL_RECURRENT, q, k, v, g, beta, b, w, o);
-    if (rc != GDR_OK) return rc;
-    if (!ST) return fail(GDR_E_INVAL, "ST must be non-NULL");
-    rc = check_alignment(d, {q, k, v, b, w, o, S0, ST}, g, beta);
-    if (rc != GDR_OK) return rc;
-    if (S0 && S0 != ST) {
-        const size_t n = gdr_state_bytes(d->B, d->H_v, d->d_k, d->d_v);
-        if (overlap(S0, ST, n)) return fail(GDR_E_INVAL, "ST must equal S0 or not overlap it");
-    }
-    if (stage) {
-        if (!stage->conv_w) return fail(GDR_E_INVAL, "the input stage needs conv_w");
-        if (!aligned(stage->conv_w, 16) || (stage->conv_in && !aligned(stage->conv_in, 16)) ||
-            (stage->conv_out && !aligned(stage->conv_out, 16)) ||
-            (stage->decay_scale && !aligned(stage->decay_scale, 4)))
-            return fail(GDR_E_INVAL, "input-stage arrays are misaligned");
-        const size_t conv_bytes = (size_t)d->B * 3 * (2 * (size_t)d->H_qk + d->H_v) * d->d_k *
-                                  (d->io_dtype == GDR_BF16 ? 2 : 4);
-        if (stage->conv_in && stage->conv_out && overlap(stage->conv_in, stage->conv_out, conv_bytes))
-            return fail(GDR_E_INVAL, "conv_out must not overlap conv_in");
-    }
-    if (d->B == 0) return ok();
-    // At most two workgroups per (sequence, V head).
-    if ((long long)d->B * d->H_v * 2 > 0x7fffffffll) return fail(GDR_E_UNSUPPORTED, "B * H_v too large for one launch");
-    gdr::RecurArgs a{};
-    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.bg = b; a.wg = w;
-    a.S0 = S0; a.ST = ST; a.o = o;
-    a.B = d->B; a.T = d->T; a.Hqk = d->H_qk; a.Hv = d->H_v; a.decay = d->decay; a.scale = d->scale;
-    if (stage) {
-        a.conv_w = stage->conv_w;
-        a.conv_in = stage->conv_in;
-        a.conv_out = stage->conv_out;
-        a.decay_scale = stage->decay_scale;
-    }
-    hipError_t e = gdr::launch_recurrent(d->io_dtype == GDR_BF16 ? gdr::IO_BF16 : gdr::IO_F32, d->d_k, a,
-                                         static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "recurrent launch");
-    return ok();
-}
 
 int gdr_recurrent_fwd(const gdr_desc *d, const void *q, const void *k, const void *v, const float *g,
                       const float *beta, const void *b, const void *w, const float *S0, void *o, float *ST,
                       void *stream) {
     return recurrent_call(d, nullptr, q, k, v, g, beta, b, w, S0, o, ST, stream);
+}
+
+int gdr_chunk_fwd(const gdr_desc *d, const void *q, const void *k, const void *v, const float *g, const float *beta,
+                  const void *b, const void *w, const float *S0, void *o, float *ST, void *workspace,
+                  size_t workspace_bytes, void *stream) {
+    return chunk_call(d, nullptr, q, k, v, g, beta, b, w, S0, o, ST, workspace, workspace_bytes, stream);
+}
+
+int gdr_chunk_fwd_in(const gdr_desc *d, const gdr_input_stage *stage, const void *q, const void *k, const void *v,
+                     const float *g, const float *beta, const void *b, const void *w, const float *S0, void *o,
+                     float *ST, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!stage) return fail(GDR_E_INVAL, "stage is NULL");
+    return chunk_call(d, stage, q, k, v, g, beta, b, w, S0, o, ST, workspace, workspace_bytes, stream);
 }
 
 int gdr_recurrent_fwd_in(const gdr_desc *d, const gdr_input_stage *stage, const void *q, const void *k,

@@ -173,6 +173,10 @@ template <> struct Raw16<bf16_t> {
     __device__ __forceinline__ static uint4 pack(const float *f) {
         return uint4{f2bf2(f[0], f[1]), f2bf2(f[2], f[3]), f2bf2(f[4], f[5]), f2bf2(f[6], f[7])};
     }
+    __device__ __forceinline__ static float at(uint4 r, int i) {  // element i (i a constant after unrolling)
+        const uint32_t w = i < 2 ? r.x : i < 4 ? r.y : i < 6 ? r.z : r.w;
+        return __uint_as_float(i % 2 ? w & 0xffff0000u : w << 16);
+    }
 };
 template <> struct Raw16<float> {
     static constexpr int N = 4;
@@ -181,6 +185,9 @@ template <> struct Raw16<float> {
     }
     __device__ __forceinline__ static uint4 pack(const float *f) {
         return uint4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3])};
+    }
+    __device__ __forceinline__ static float at(uint4 r, int i) {
+        return __uint_as_float(i == 0 ? r.x : i == 1 ? r.y : i == 2 ? r.z : r.w);
     }
 };
 __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
@@ -239,16 +246,30 @@ struct PrepCfg {
     }
 };
 
+// Input stage (raw projections in): q and k are normalised as
+// x / sqrt(sum x^2 + kStageNormEps); the gates are logistic functions of
+// their inputs, and the decay is g = -c softplus(x).
+constexpr float kStageNormEps = 1e-12f;
+__device__ __forceinline__ float sigmoidf(float x) { return 1.f / (1.f + expf(-x)); }
+template <bool RAW>
+__device__ __forceinline__ float stage_decay(float x, float c) {
+    if constexpr (RAW) return -c * (fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))));
+    else return x;
+}
+
 // One thread's raw inputs for a chunk: TPT tokens x one 16-byte channel group
 // of q, k, v (and b, w, per-channel g); lane l of wave 0 also holds token l's
 // beta and scalar g.
-template <typename IO, int D, bool CHAN, bool BW>
+template <typename IO, int D, bool CHAN, bool BW, bool RAW>
 struct PrepIn {
     using Cfg = PrepCfg<IO, D>;
     static constexpr int TPT = Cfg::TPT, V = Cfg::V;
     uint4 q[TPT], k[TPT], v[TPT], bg[BW ? TPT : 1], wg[BW ? TPT : 1];
     f32x4 g[CHAN ? TPT * V / 4 : 1];
     float betal, gs;
+    // Input stage: token c*C - 3 + grp of the raw q, k, v (groups 0-2), the
+    // chunk's convolution window before its first token.
+    uint4 halo_q, halo_k, halo_v;
 
     // The loads are issued in three parts (PART 0: q, k; 1: v, per-channel g;
     // 2: b, w, beta, scalar g) at different points of the previous unit, so
@@ -280,6 +301,21 @@ struct PrepIn {
                 wg[j] = ld16(static_cast<const IO *>(a.wg) + vo + t * sv);
             }
         }
+        if constexpr (RAW && PART == 2)  // late: short live range for the window registers
+            if (grp < 3) {
+                const int th = t0 - 3 + grp;  // < 0: from the incoming convolution state (zeros without one)
+                const size_t ch = 2 * sqk + sv;
+                const IO *cin = th < 0 && a.conv_in ? static_cast<const IO *>(a.conv_in) + ((size_t)b * 3 + 3 + th) * ch
+                                                    : nullptr;
+                const uint4 zero = uint4{0u, 0u, 0u, 0u};
+                const size_t cq = (size_t)hq * D + V * co;
+                halo_q = th >= 0 ? ld16(static_cast<const IO *>(a.q) + qko + (ptrdiff_t)(th - t0) * (ptrdiff_t)sqk)
+                                 : cin ? ld16(cin + cq) : zero;
+                halo_k = th >= 0 ? ld16(static_cast<const IO *>(a.k) + qko + (ptrdiff_t)(th - t0) * (ptrdiff_t)sqk)
+                                 : cin ? ld16(cin + sqk + cq) : zero;
+                halo_v = th >= 0 ? ld16(static_cast<const IO *>(a.v) + vo + (ptrdiff_t)(th - t0) * (ptrdiff_t)sv)
+                                 : cin ? ld16(cin + 2 * sqk + (size_t)h * D + V * co) : zero;
+            }
         if constexpr (PART == 2)
             if (threadIdx.x < 64) {  // wave 0: one token per lane
                 const size_t tl = (row0 + min(l, n - 1)) * a.Hv + h;
@@ -297,7 +333,7 @@ struct PrepIn {
 template <typename IO, int D, bool CHAN, bool BW>
 constexpr int prep_occupancy() { return (CHAN || BW) ? 1 : 2; }
 
-template <typename IO, int D, bool CHAN, bool BW>
+template <typename IO, int D, bool CHAN, bool BW, bool RAW>
 __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chunk_prep(ChunkArgs a) {
     using M = Mma<IO>;
     using K = Km<IO>;
@@ -336,7 +372,7 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
     const int co = tid % CO, grp = tid / CO;
     const int units = a.B * a.Hv * a.NC;
 
-    PrepIn<IO, D, CHAN, BW> in;
+    PrepIn<IO, D, CHAN, BW, RAW> in;
     if ((int)blockIdx.x < units) in.load_all(a, blockIdx.x, co, grp);
 
     for (int u = blockIdx.x; u < units; u += gridDim.x) {
@@ -350,6 +386,8 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
         IO *wQh = wKT + D * C;
         const bool write_kT = CHAN || h % grpsz == 0;
         float *tab = a.ws_tab + (size_t)u * kTab;
+        // Input stage: g holds the decay's input x, g = -dsc softplus(x).
+        const float dsc = RAW && a.decay_scale ? a.decay_scale[h] : 1.f;
         __syncthreads();  // the previous unit is done with shared memory
 
         // ---- A. prefix sums, token tables, tiles ----
@@ -359,7 +397,8 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
             for (int j = 0; j < TPT; ++j)
 #pragma unroll
                 for (int ch = 0; ch < V; ++ch)
-                    G[j][ch] = (TPT * grp + j < n ? in.g[j * (V / 4) + ch / 4][ch % 4] : 0.f) + (j > 0 ? G[j - 1][ch] : 0.f);
+                    G[j][ch] = (TPT * grp + j < n ? stage_decay<RAW>(in.g[j * (V / 4) + ch / 4][ch % 4], dsc) : 0.f) +
+                               (j > 0 ? G[j - 1][ch] : 0.f);
 #pragma unroll
             for (int i = 0; i < V / 4; ++i)
                 store4f(sPart + grp * D + V * co + 4 * i,
@@ -369,7 +408,7 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
             float eg = 1.f;
             if constexpr (!CHAN) {
                 // Scalar decay: lane = token; inclusive scan of g over the chunk.
-                float Gl = l < n ? in.gs : 0.f;
+                float Gl = l < n && a.decay == DECAY_SCALAR ? stage_decay<RAW>(in.gs, dsc) : 0.f;
 #pragma unroll
                 for (int off = 1; off < 64; off <<= 1) {
                     const float y = __shfl_up(Gl, off);
@@ -382,10 +421,88 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
                 tab[l] = eg;       // per-token decay factors for the sweep
                 tab[C + l] = er;
             }
-            if constexpr (!BW) sBt[l] = in.betal;
-            sSE[l] = BW ? eg : in.betal * eg;
+            const float bt = BW ? 0.f : RAW ? sigmoidf(in.betal) : in.betal;
+            if constexpr (!BW) sBt[l] = bt;
+            sSE[l] = BW ? eg : bt * eg;
+        }
+        IO *sHalo = sTmp;  // input stage: [3 tokens][q, k, v][D], the window before the chunk
+        if constexpr (RAW) {
+            // The raw rows go to the tiles (token-major, as the processed
+            // ones will) and the 3 tokens before the chunk to sHalo, so that
+            // each thread can read the 3 rows before its own.
+#pragma unroll
+            for (int j = 0; j < TPT; ++j) {
+                const int o = (TPT * grp + j) * PD + V * co;
+                *reinterpret_cast<uint4 *>(tQ + o) = in.q[j];
+                *reinterpret_cast<uint4 *>(tK + o) = in.k[j];
+                *reinterpret_cast<uint4 *>(tZ + o) = in.v[j];
+            }
+            if (grp < 3) {
+                *reinterpret_cast<uint4 *>(sHalo + (3 * grp + 0) * D + V * co) = in.halo_q;
+                *reinterpret_cast<uint4 *>(sHalo + (3 * grp + 1) * D + V * co) = in.halo_k;
+                *reinterpret_cast<uint4 *>(sHalo + (3 * grp + 2) * D + V * co) = in.halo_v;
+            }
         }
         __syncthreads();
+        if constexpr (RAW) {
+            const size_t sqk = (size_t)a.Hqk * D, ch = 2 * sqk + (size_t)a.Hv * D;
+            const int hq = h / grpsz, b = bh / a.Hv;
+            const size_t cq = (size_t)hq * D + V * co, ck = sqk + cq, cv = 2 * sqk + (size_t)h * D + V * co;
+            // Raw row of token t of this chunk (t >= -3) for tensor x (0 q, 1 k, 2 v).
+            const auto raw_row = [&](int x, int t) -> uint4 {
+                const IO *tile = x == 0 ? tQ : x == 1 ? tK : tZ;
+                return t >= 0 ? *reinterpret_cast<const uint4 *>(tile + t * PD + V * co)
+                              : *reinterpret_cast<const uint4 *>(sHalo + (3 * (3 + t) + x) * D + V * co);
+            };
+            // The convolution state after the last chunk: its last 3 raw tokens.
+            if (a.conv_out && c == NC - 1 && grp < 3) {
+                IO *cout = static_cast<IO *>(a.conv_out) + ((size_t)b * 3 + grp) * ch;
+                const int t = n - 3 + grp;
+                if (h % grpsz == 0) {
+                    *reinterpret_cast<uint4 *>(cout + cq) = raw_row(0, t);
+                    *reinterpret_cast<uint4 *>(cout + ck) = raw_row(1, t);
+                }
+                *reinterpret_cast<uint4 *>(cout + cv) = raw_row(2, t);
+            }
+            // Convolve this thread's tokens (window: 3 rows before them, then
+            // their own), normalise q and k over the head, and keep the
+            // results in place of the raw rows.
+            const auto stage = [&](uint4(&x)[TPT], int xi, size_t cbase, bool norm) {
+                uint4 wnd[TPT + 3];  // raw, widened one channel at a time
+                float out[TPT][V];
+#pragma unroll
+                for (int r = 0; r < 3; ++r) wnd[r] = raw_row(xi, TPT * grp - 3 + r);
+#pragma unroll
+                for (int j = 0; j < TPT; ++j) wnd[3 + j] = x[j];
+#pragma unroll
+                for (int c4 = 0; c4 < V; ++c4) {
+                    const f32x4 tp = load4f(a.conv_w + (cbase + c4) * 4);
+                    float xc[TPT + 3];
+#pragma unroll
+                    for (int r = 0; r < TPT + 3; ++r) xc[r] = R::at(wnd[r], c4);
+#pragma unroll
+                    for (int j = 0; j < TPT; ++j)
+                        out[j][c4] = tp[0] * xc[j] + tp[1] * xc[j + 1] + tp[2] * xc[j + 2] + tp[3] * xc[j + 3];
+                }
+#pragma unroll
+                for (int j = 0; j < TPT; ++j) {
+                    if (norm) {
+                        float ss = 0.f;
+#pragma unroll
+                        for (int c4 = 0; c4 < V; ++c4) ss += out[j][c4] * out[j][c4];
+                        ss = lanes_allreduce<CO>(ss);
+                        const float f = 1.f / sqrtf(ss + kStageNormEps);
+#pragma unroll
+                        for (int c4 = 0; c4 < V; ++c4) out[j][c4] *= f;
+                    }
+                    x[j] = R::pack(out[j]);
+                }
+            };
+            stage(in.q, 0, cq, true);
+            stage(in.k, 1, ck, true);
+            stage(in.v, 2, cv, false);
+            __syncthreads();  // every window read before the tiles are overwritten
+        }
         float eGend[V];
         if constexpr (CHAN) {
             float off[V], tot[V];
@@ -424,6 +541,12 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
             if constexpr (BW) {
                 R::widen(in.bg[j], eb);
                 R::widen(in.wg[j], wz);
+                if constexpr (RAW)
+#pragma unroll
+                    for (int ch = 0; ch < V; ++ch) {
+                        eb[ch] = sigmoidf(eb[ch]);
+                        wz[ch] = sigmoidf(wz[ch]);
+                    }
             } else {
                 const float bt = sBt[t];
 #pragma unroll
@@ -1058,14 +1181,18 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t s) {
     // decoupled-gate variants keep more tiles.
     // Once per process (thread-safe): allow each variant its shared memory.
     static const hipError_t attr_err = [] {
-        const void *fns[4] = {reinterpret_cast<const void *>(&chunk_prep<IO, D, false, false>),
-                              reinterpret_cast<const void *>(&chunk_prep<IO, D, false, true>),
-                              reinterpret_cast<const void *>(&chunk_prep<IO, D, true, false>),
-                              reinterpret_cast<const void *>(&chunk_prep<IO, D, true, true>)};
+        const void *fns[8] = {reinterpret_cast<const void *>(&chunk_prep<IO, D, false, false, false>),
+                              reinterpret_cast<const void *>(&chunk_prep<IO, D, false, true, false>),
+                              reinterpret_cast<const void *>(&chunk_prep<IO, D, true, false, false>),
+                              reinterpret_cast<const void *>(&chunk_prep<IO, D, true, true, false>),
+                              reinterpret_cast<const void *>(&chunk_prep<IO, D, false, false, true>),
+                              reinterpret_cast<const void *>(&chunk_prep<IO, D, false, true, true>),
+                              reinterpret_cast<const void *>(&chunk_prep<IO, D, true, false, true>),
+                              reinterpret_cast<const void *>(&chunk_prep<IO, D, true, true, true>)};
         const size_t lds[4] = {Cfg::bytes(false, false), Cfg::bytes(true, false), Cfg::bytes(true, true),
                                Cfg::bytes(true, true)};
-        for (int i = 0; i < 4; ++i) {
-            hipError_t e = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds[i]);
+        for (int i = 0; i < 8; ++i) {
+            hipError_t e = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds[i % 4]);
             if (e != hipSuccess) return e;
         }
         return hipSuccess;
@@ -1080,10 +1207,17 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t s) {
         const long long slots = (long long)occ * device_cus();
         const long long grid = units < slots ? units : slots;
         const dim3 g((unsigned)grid), b(Cfg::NT);
-        if (chan && bw) hipLaunchKernelGGL((chunk_prep<IO, D, true, true>), g, b, Cfg::bytes(true, true), s, a);
-        else if (chan) hipLaunchKernelGGL((chunk_prep<IO, D, true, false>), g, b, Cfg::bytes(true, true), s, a);
-        else if (bw) hipLaunchKernelGGL((chunk_prep<IO, D, false, true>), g, b, Cfg::bytes(true, false), s, a);
-        else hipLaunchKernelGGL((chunk_prep<IO, D, false, false>), g, b, Cfg::bytes(false, false), s, a);
+        if (a.conv_w) {
+            if (chan && bw) hipLaunchKernelGGL((chunk_prep<IO, D, true, true, true>), g, b, Cfg::bytes(true, true), s, a);
+            else if (chan) hipLaunchKernelGGL((chunk_prep<IO, D, true, false, true>), g, b, Cfg::bytes(true, true), s, a);
+            else if (bw) hipLaunchKernelGGL((chunk_prep<IO, D, false, true, true>), g, b, Cfg::bytes(true, false), s, a);
+            else hipLaunchKernelGGL((chunk_prep<IO, D, false, false, true>), g, b, Cfg::bytes(false, false), s, a);
+        } else {
+            if (chan && bw) hipLaunchKernelGGL((chunk_prep<IO, D, true, true, false>), g, b, Cfg::bytes(true, true), s, a);
+            else if (chan) hipLaunchKernelGGL((chunk_prep<IO, D, true, false, false>), g, b, Cfg::bytes(true, true), s, a);
+            else if (bw) hipLaunchKernelGGL((chunk_prep<IO, D, false, true, false>), g, b, Cfg::bytes(true, false), s, a);
+            else hipLaunchKernelGGL((chunk_prep<IO, D, false, false, false>), g, b, Cfg::bytes(false, false), s, a);
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

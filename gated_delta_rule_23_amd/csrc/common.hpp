@@ -109,6 +109,22 @@ template <> struct Mma16<float> {
     }
 };
 
+// Sum over NL (4, 8 or 16) consecutive lanes, aligned to NL, result in every
+// one of them, by DPP row permutations: swap neighbours, swap pairs, then
+// fold each 8-lane half onto its mirror image, and for 16 lanes the two
+// halves of the row likewise (each step adds a disjoint partial sum).
+template <int NL>
+__device__ __forceinline__ float lanes_allreduce(float x) {
+    static_assert(NL == 4 || NL == 8 || NL == 16, "DPP row groups");
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
+    if constexpr (NL >= 8)
+        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));  // half-row mirror
+    if constexpr (NL == 16)
+        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));  // row mirror
+    return x;
+}
+
 // Four consecutive elements (8 or 16 bytes, aligned) widened to float, and back.
 __device__ __forceinline__ f32x4 load4f(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
 __device__ __forceinline__ f32x4 load4f(const bf16_t *p) {

@@ -61,6 +61,11 @@ struct ChunkArgs {
     int B, T, Hqk, Hv, decay, NC;
     int P, L;                // sweep segments and their length in chunks (P = 1: one pass)
     float scale;
+    // Input stage (conv_w non-null), as in RecurArgs.
+    const float *conv_w;
+    const void *conv_in;
+    void *conv_out;
+    const float *decay_scale;
 };
 
 constexpr int kTab = 2 * kChunk;  // floats per chunk unit in ws_tab (>= D for every supported D)

@@ -56,19 +56,6 @@ struct RecurCfg {
     static_assert(RPL % 4 == 0 && NRL >= 8 && NRL <= 16 && D % (NWB * CW) == 0, "recurrent tile shape");
 };
 
-// Sum over the NRL (8 or 16) consecutive lanes of a DPP row, result in every
-// one of them: swap neighbours, swap pairs, then fold each 8-lane half onto
-// its mirror image, and for 16 lanes the two halves of the row likewise.
-template <int NRL>
-__device__ __forceinline__ float rows_allreduce(float x) {
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));  // half-row mirror
-    if constexpr (NRL == 16)
-        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));  // row mirror
-    return x;
-}
-
 __device__ __forceinline__ f32x4 exp4(f32x4 g) { return f32x4{expf(g[0]), expf(g[1]), expf(g[2]), expf(g[3])}; }
 
 // q and k are normalised as x / sqrt(sum x^2 + kNormEps).
@@ -233,8 +220,8 @@ __global__ __launch_bounds__((RecurCfg<D, CW, CHAN>::NT)) void recurrent_kernel(
             }
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                pr[c] = rows_allreduce<C::NRL>(pr[c]);
-                pp[c] = rows_allreduce<C::NRL>(pp[c]);
+                pr[c] = lanes_allreduce<C::NRL>(pr[c]);
+                pp[c] = lanes_allreduce<C::NRL>(pp[c]);
             }
             const f32x4 u = load4f(L + C::OFF_Z + col) - pr;
             if (r == 0) {

@@ -193,6 +193,19 @@ typedef struct {
     const float *decay_scale;  /* [H_v] float32 c_h > 0, or NULL for 1 */
 } gdr_input_stage;
 
+/* gdr_chunk_fwd with the input stage fused into the prefill's load stage:
+ * the per-chunk kernel reads the raw projections (plus the 3 tokens before
+ * each chunk) and applies the convolution, the normalisation and the
+ * activations before building the chunk's factors, so the processed q, k, v
+ * never travel through memory. Arguments as gdr_recurrent_fwd_in, plus the
+ * workspace of gdr_chunk_fwd (same size, gdr_chunk_workspace_bytes). The
+ * chunk products run on bf16 matrix cores for bf16 io, so the processed q, k
+ * and v are rounded to bf16 there, as the io values of gdr_chunk_fwd are. */
+int gdr_chunk_fwd_in(const gdr_desc *desc, const gdr_input_stage *stage, const void *q, const void *k,
+                     const void *v, const float *g, const float *beta, const void *b, const void *w,
+                     const float *S0, void *o, float *ST, void *workspace, size_t workspace_bytes,
+                     void *stream);
+
 /* gdr_recurrent_fwd with the input stage fused into its token loop: q, k, v
  * are the raw projections (before the convolution), beta, b, w the gate
  * inputs before the sigmoid and g the decay input before -c softplus, in

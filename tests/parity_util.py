@@ -83,6 +83,18 @@ def gpu_recurrent_in(raw, S0=None, ST=None, conv_in="stored", conv_out=None, T_s
                                     w=d["w"], S0=S0, ST=ST, scale=wl.scale)
 
 
+def gpu_prefill_in(raw, S0=None, ST=None, conv_in="stored", conv_out=None, T_slice=None):
+    """Run gdr_chunk_fwd_in on raw inputs; returns torch (o, ST, conv_out)."""
+    import gated_delta_rule_23_amd as gdr
+    wl = raw["workload"]
+    sl = (lambda a: a) if T_slice is None else (lambda a: None if a is None else np.ascontiguousarray(a[:, T_slice]))
+    d = {n: to_dev(sl(raw[n])) for n in ("q", "k", "v", "g", "beta", "b", "w")}
+    cin = to_dev(raw["conv_in"]) if isinstance(conv_in, str) else conv_in
+    return gdr.gdr_chunk_fwd_in(d["q"], d["k"], d["v"], to_dev(raw["conv_w"]), conv_in=cin, conv_out=conv_out,
+                                decay_scale=to_dev(raw["decay_scale"]), g=d["g"], beta=d["beta"], b=d["b"],
+                                w=d["w"], S0=S0, ST=ST, scale=wl.scale)
+
+
 def oracle_input_stage(raw, heads=None, cols=None, S0="stored", conv_in="stored"):
     """The input-stage oracle, then the recurrence oracle. Returns (o, S_T,
     conv_out) in fp64."""

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import gdr_synth as gs
-from parity_util import (TOL, from_dev, gpu_decode, gpu_prefill, gpu_recurrent, gpu_recurrent_in,
+from parity_util import (TOL, from_dev, gpu_decode, gpu_prefill, gpu_prefill_in, gpu_recurrent, gpu_recurrent_in,
                          oracle_input_stage, oracle_prefill, rel_err, say, small_workload, to_dev)
 
 torch = pytest.importorskip("torch")
@@ -521,6 +521,98 @@ def test_recurrent_input_stage_zero_tokens():
     o, ST, cout = gpu_recurrent_in(raw, S0=S0, T_slice=slice(0, 0))
     torch.cuda.synchronize()
     assert torch.equal(ST, S0) and torch.equal(cout, to_dev(raw["conv_in"]))
+
+
+# ---------------------------------------------------------------------------
+# Input stage fused into the chunked prefill's load stage.
+
+@pytest.mark.parametrize("io,D", PREFILL_DIMS)
+@pytest.mark.parametrize("decay,gates", MODES)
+@pytest.mark.parametrize("T", [1, 2, 64, 150])
+def test_prefill_input_stage_small(io, D, decay, gates, T):
+    """T = 1 and 2: the whole window and part of the outgoing state come from
+    the incoming convolution state; T = 150: chunks 2 and 3 take their first
+    window from the chunk before."""
+    wl = small_workload(io, D, decay, gates, T=T, B=2, Hqk=1, Hv=2, S0=True, scale=D ** -0.5)
+    raw = gs.make_raw_inputs(wl, seed=7 * T + D)
+    say(f"prefill input stage {wl.name}")
+    o, ST, cout = gpu_prefill_in(raw, S0=to_dev(raw["S0"]))
+    o_ref, S_ref, c_ref = oracle_input_stage(raw)
+    assert rel_err(from_dev(o), o_ref) < TOL[io]
+    assert rel_err(from_dev(ST), S_ref) < TOL[io]
+    assert _conv_equal(cout, c_ref)
+
+
+@pytest.mark.parametrize("io,D,decay,gates,T,Hqk,Hv,B", [
+    ("bf16", 128, "scalar", "beta", 333, 2, 6, 2),      # grouped heads, no incoming convolution state
+    ("bf16", 64, "channel", "bw", 2500, 1, 2, 1),       # segmented sweep
+    ("f32", 64, "scalar", "bw", 200, 1, 3, 2),
+])
+def test_prefill_input_stage_larger(io, D, decay, gates, T, Hqk, Hv, B):
+    wl = small_workload(io, D, decay, gates, T=T, B=B, Hqk=Hqk, Hv=Hv, S0=True)
+    raw = gs.make_raw_inputs(wl, seed=47, conv_state=(T != 333))
+    say(f"prefill input stage {wl.name}")
+    o, ST, cout = gpu_prefill_in(raw, S0=to_dev(raw["S0"]), conv_in="stored" if T != 333 else None)
+    o_ref, S_ref, c_ref = oracle_input_stage(raw, conv_in="stored" if T != 333 else None)
+    assert rel_err(from_dev(o), o_ref) < TOL[io]
+    assert rel_err(from_dev(ST), S_ref) < TOL[io]
+    assert _conv_equal(cout, c_ref)
+
+
+def test_prefill_input_stage_qwen_full_size_sampled():
+    """The Qwen-shaped layer (T = 4096, 16 QK heads, 48 V heads, d = 128)
+    from raw projections, as the benchmark times it: sampled heads against
+    the oracle, the whole outgoing convolution state exactly."""
+    wl = gs.QWEN_GDN_PREFILL
+    raw = gs.make_raw_inputs(wl, seed=48)
+    say(f"prefill input stage {wl.name}")
+    o, ST, cout = gpu_prefill_in(raw)
+    torch.cuda.synchronize()
+    heads = [0, 2, 25, 47]
+    o_ref, S_ref, c_ref = oracle_input_stage(raw, heads=heads, S0=None)
+    assert rel_err(from_dev(o[:, :, heads]), o_ref[:, :, heads]) < TOL["bf16"]
+    assert rel_err(from_dev(ST[:, heads]), S_ref[:, heads]) < TOL["bf16"]
+    assert _conv_equal(cout, c_ref)
+
+
+def test_prefill_input_stage_split_and_serving_handoff():
+    """A prefill in two calls, the second taking the first's convolution state
+    and final state, equals one call; decode steps from there (T = 1 calls of
+    the recurrent forward with the handed-over states) equal the tail of one
+    long recurrent call."""
+    wl = small_workload("bf16", 128, "scalar", "beta", T=210, B=2, Hqk=2, Hv=4, S0=True)
+    raw = gs.make_raw_inputs(wl, seed=49)
+    S0 = to_dev(raw["S0"])
+    o_all, S_all, c_all = gpu_prefill_in(raw, S0=S0)
+    o1, S1, c1 = gpu_prefill_in(raw, S0=S0, T_slice=slice(0, 130))
+    o2, S2, c2 = gpu_prefill_in(raw, S0=S1, conv_in=c1, T_slice=slice(130, 200))
+    o3, S3, c3 = gpu_prefill_in(raw, S0=S2, conv_in=c2, T_slice=slice(200, 210))
+    assert rel_err(from_dev(torch.cat([o1, o2, o3], dim=1)), from_dev(o_all)) < TOL["bf16"]
+    assert rel_err(from_dev(S3), from_dev(S_all)) < TOL["bf16"]
+    assert torch.equal(c3, c_all)
+    o_r, S_r, c_r = gpu_recurrent_in(raw, S0=S0)
+    assert rel_err(from_dev(o_r), from_dev(o_all)) < TOL["bf16"]
+    assert torch.equal(c_r, c_all)
+    S = S2.clone()
+    bufs = [c2.clone(), torch.empty_like(c2)]
+    for t in range(200, 210):
+        o, _, _ = gpu_recurrent_in(raw, S0=S, ST=S, conv_in=bufs[t % 2], conv_out=bufs[(t + 1) % 2],
+                                   T_slice=slice(t, t + 1))
+        assert rel_err(from_dev(o), from_dev(o_all[:, t:t + 1])) < TOL["bf16"]
+    assert torch.equal(bufs[210 % 2], c_all)
+    assert rel_err(from_dev(S), from_dev(S_all)) < TOL["bf16"]
+
+
+def test_prefill_input_stage_zero_tokens():
+    wl = small_workload("bf16", 64, "channel", "bw", T=4, B=2, Hqk=1, Hv=2, S0=True)
+    raw = gs.make_raw_inputs(wl, seed=50)
+    S0 = to_dev(raw["S0"])
+    o, ST, cout = gpu_prefill_in(raw, S0=S0, T_slice=slice(0, 0))
+    torch.cuda.synchronize()
+    assert torch.equal(ST, S0) and torch.equal(cout, to_dev(raw["conv_in"]))
+    o, ST, cout = gpu_prefill_in(raw, S0=S0, conv_in=None, T_slice=slice(0, 0))
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(cout) == 0
 
 
 def test_state_alloc_is_zeroed():
