@@ -13,7 +13,10 @@ call) for reference.
 
 --workload picks another prefill workload for the timed step (the KDA and
 Gated DeltaNet-2 layers, or the small fp32 case); --decode-steps 0 skips the
-decode measurement. Decode is also timed with the states of four layers
+decode measurement. "input_stage" times the same prefill from raw
+projections through gdr_chunk_fwd_in (convolution, normalisation and gate
+activations fused into the load stage; --input-stage 0 skips it). Decode is
+also timed with the states of four layers
 advanced in turn, and the multi-token recurrent forward (gdr_recurrent_fwd,
 --recurrent-T tokens per sequence at the decode shape, four layers' states in
 turn) gets its own object; --recurrent-T 0 skips it.
@@ -129,6 +132,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-steps", type=int, default=256, help="consecutive decode steps timed (0 = skip decode)")
+    ap.add_argument("--input-stage", type=int, default=1,
+                    help="also time the prefill from raw projections (input stage fused; 0 = skip)")
     ap.add_argument("--recurrent-T", type=int, default=4,
                     help="tokens per sequence of the multi-token recurrent call timed at the decode shape (0 = skip)")
     ap.add_argument("--workload", default="qwen_gdn_prefill",
@@ -217,6 +222,43 @@ def main(argv=None):
     tokens = wl.B * wl.T
     pbytes, pflops = prefill_algorithmic(wl)
     achieved = pbytes / (avg_call_ms * 1e-3) / 1e9
+
+    # ---- the same layer from raw projections: input stage fused into the prefill ----
+    stage = None
+    if args.input_stage:
+        raw = gs.make_raw_inputs(wl, seed=args.seed + 3)
+        rd = {n: up(raw[n]) for n in ("q", "k", "v", "g", "beta", "b", "w", "conv_w", "conv_in", "decay_scale")}
+        conv_out = torch.empty_like(rd["conv_in"])
+
+        def prefill_in():
+            gdr.gdr_chunk_fwd_in(rd["q"], rd["k"], rd["v"], rd["conv_w"], conv_in=rd["conv_in"], conv_out=conv_out,
+                                 decay_scale=rd["decay_scale"], g=rd["g"], beta=rd["beta"], b=rd["b"], w=rd["w"],
+                                 S0=None, scale=wl.scale, o=o, ST=ST, workspace=ws, stream=cur())
+
+        for _ in range(args.warmup):
+            prefill_in()
+        torch.cuda.synchronize()
+        sgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(sgraph):
+            for _ in range(args.steps):
+                prefill_in()
+        sgraph.replay()
+        torch.cuda.synchronize()
+        t_start.record(cur())
+        sgraph.replay()
+        t_end.record(cur())
+        torch.cuda.synchronize()
+        del sgraph
+        s_ms = t_start.elapsed_time(t_end) / args.steps
+        s_bytes = pbytes + raw["conv_w"].nbytes + 2 * raw["conv_in"].nbytes + (raw["decay_scale"].nbytes
+                                                                               if raw["decay_scale"] is not None else 0)
+        stage = {"entry": "gdr_chunk_fwd_in", "ms_per_call": s_ms, "tokens_per_s": tokens / (s_ms * 1e-3),
+                 "extra_ms_vs_gdr_chunk_fwd": s_ms - avg_call_ms,
+                 "unfused_round_trip_bytes": 2 * (d["q"].nbytes + d["k"].nbytes + d["v"].nbytes),
+                 "roofline": {"bound": "hbm", "achieved": s_bytes / (s_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
+                              "unit": "GB/s", "frac": s_bytes / (s_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                              "algorithmic_bytes": s_bytes}}
+        del raw, rd, conv_out
 
     # ---- decode ----
     dec = None
@@ -367,6 +409,7 @@ def main(argv=None):
                      "eager_call_ms": eager_call_ms},
         "mfma": {"algorithmic_tflops": pflops / (avg_call_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
                  "frac": pflops / (avg_call_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, "algorithmic_flops": pflops},
+        "input_stage": stage,
         "decode": dec,
         "recurrent": rec,
     }
