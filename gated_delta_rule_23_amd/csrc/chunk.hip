@@ -978,7 +978,13 @@ __global__ __launch_bounds__(4 * D) void chunk_sweep(ChunkArgs a, int NVT, int G
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63, lr = l & 15, lq = l >> 4;
     const int cb = sg * a.L, NC = min(a.L, a.NC - cb);  // this segment's chunks [cb, cb + NC)
     // Entry state: S0 for the first segment, else the one the segment scan found.
-    const float *Sin = sg == 0 ? a.S0 : a.ws_seg + ((size_t)(bh * (a.P - 1) + sg - 1) * 3 + 2) * D * D;
+    // Entry state: the one the segment scan found; for the first segment the
+    // scan's copy of S0 when the sweep is split (the last segment's S_T may
+    // overwrite S0 in place while the first segment has not read it yet),
+    // else S0 itself.
+    const float *Sin = sg > 0 ? a.ws_seg + ((size_t)(bh * (a.P - 1) + sg - 1) * 3 + 2) * D * D
+                       : a.P > 1 ? a.ws_seg + ((size_t)bh * (a.P - 1) * 3 + 1) * D * D
+                       : a.S0 ? a.S0 + (size_t)bh * D * D : nullptr;
     const bool last = sg == a.P - 1;
 
     SweepSrc<IO> src;
@@ -997,7 +1003,7 @@ __global__ __launch_bounds__(4 * D) void chunk_sweep(ChunkArgs a, int NVT, int G
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int ch = 32 * w + 16 * rt + 4 * lq + r, col = col0 + 16 * ct + lr;
-                    S[rt][ct][r] = Sin ? Sin[(sg == 0 ? (size_t)bh * D * D : 0) + (size_t)ch * D + col] : 0.f;
+                    S[rt][ct][r] = Sin ? Sin[(size_t)ch * D + col] : 0.f;
                 }
         if (NC > 0) {
             ChainOps<IO, D, NCT, CHAN> ring[PF];
@@ -1140,7 +1146,13 @@ __global__ __launch_bounds__(256) void chunk_seg_combine(ChunkArgs a) {
             const int rt = w + 4 * i;
             if (rt < D / 16) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[i][r] = N[(size_t)(16 * rt + 4 * lg + r) * D + c0 + lr];
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * rt + 4 * lg + r;
+                    acc[i][r] = N[(size_t)row * D + c0 + lr];
+                    // Once read, N_0 keeps a copy of S0 for the sweep's first
+                    // segment (S_T may alias S0).
+                    if (s == 0) const_cast<float *>(N)[(size_t)row * D + c0 + lr] = sIn[row * NTC + lr];
+                }
                 const float *Mr = M + (size_t)(16 * rt + lr) * D + lg;
 #pragma unroll 8
                 for (int ks = 0; ks < D / 4; ++ks)

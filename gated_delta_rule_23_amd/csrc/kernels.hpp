@@ -56,8 +56,9 @@ struct ChunkArgs {
     void *ws_kT;             // scalar or no decay: k^T (D x C) then q (C x D), fragment order, per
                              // (sequence, QK head, chunk)
     float *ws_seg;           // segmented sweep (P > 1): per (sequence, V head, segment < P - 1) the
-                             // segment's transition M (D x D), its end state from zero N (D x D), and the
-                             // entry state of the next segment (D x D), fp32
+                             // segment's transition M (D x D), its end state from zero N (D x D; for
+                             // segment 0, a copy of S0 once the scan has read N), and the entry state of
+                             // the next segment (D x D), fp32
     int B, T, Hqk, Hv, decay, NC;
     int P, L;                // sweep segments and their length in chunks (P = 1: one pass)
     float scale;

@@ -149,6 +149,22 @@ def test_prefill_segmented_sweep(io, D, decay, gates, T, Hv, B):
     assert rel_err(from_dev(ST), S_ref) < TOL[io]
 
 
+def test_prefill_segmented_sweep_in_place():
+    """With the sweep split, the first segment starts from a copy of S0 that
+    the segment scan keeps, so S_T may alias S0: the in-place call gives the
+    out-of-place result bit for bit."""
+    wl = small_workload("bf16", 128, "scalar", "beta", 3000, B=1, Hqk=1, Hv=2, S0=True)
+    assert _sweep_segments(1, 2, 128, 3000) > 1
+    inp = gs.make_inputs(wl, seed=9)
+    S0 = to_dev(inp["S0"])
+    o1, S1 = gpu_prefill(inp, S0=S0)
+    S = S0.clone()
+    o2, S2 = gpu_prefill(inp, S0=S, ST=S)
+    assert torch.equal(o1, o2) and torch.equal(S, S1)
+    o_ref, S_ref = oracle_prefill(inp)
+    assert rel_err(from_dev(o2), o_ref) < TOL["bf16"] and rel_err(from_dev(S), S_ref) < TOL["bf16"]
+
+
 # ---------------------------------------------------------------------------
 # Properties.
 
