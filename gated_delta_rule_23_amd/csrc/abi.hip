@@ -261,7 +261,8 @@ int gdr_decode_step(const gdr_desc *d, const void *q, const void *k, const void 
     rc = check_alignment(d, {q, k, v, b, w, o, S}, g, beta);
     if (rc != GDR_OK) return rc;
     if (d->B == 0) return ok();
-    if ((long long)d->B * d->H_v > 0x7fffffffll) return fail(GDR_E_UNSUPPORTED, "B * H_v too large for one launch");
+    // At most two workgroups per (sequence, V head).
+    if ((long long)d->B * d->H_v * 2 > 0x7fffffffll) return fail(GDR_E_UNSUPPORTED, "B * H_v too large for one launch");
     gdr::DecodeArgs a{};
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.bg = b; a.wg = w; a.S = S; a.o = o;
     a.B = d->B; a.Hqk = d->H_qk; a.Hv = d->H_v; a.decay = d->decay; a.scale = d->scale;

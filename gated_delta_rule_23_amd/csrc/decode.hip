@@ -28,28 +28,29 @@
 
 namespace gdr {
 
-template <typename IO, int D>
+template <typename IO, int D, int SPLIT>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     using E = Elem<IO>;
     constexpr int NT = 256;
-    constexpr int CG = D / 4;    // float4 column groups per row
-    constexpr int RS = NT / CG;  // row stride between a thread's rows
-    constexpr int NR = D / RS;   // rows per thread
+    constexpr int DC = D / SPLIT;  // value columns of this workgroup
+    constexpr int CG = DC / 4;     // float4 column groups per row
+    constexpr int RS = NT / CG;    // row stride between a thread's rows
+    constexpr int NR = D / RS;     // rows per thread
     constexpr int NW = NT / 64;
-    static_assert(NT % CG == 0 && D % RS == 0 && CG <= 64, "tile shape");
+    static_assert(NT % CG == 0 && D % RS == 0 && CG <= 64 && DC % 4 == 0, "tile shape");
 
     __shared__ float s_q[D], s_k[D], s_e[D], s_al[D];
-    __shared__ float s_red[NW][2][D];
+    __shared__ float s_red[NW][2][DC];
     __shared__ float s_qk;
 
-    const int bh = blockIdx.x;
+    const int bh = blockIdx.x / SPLIT, c0 = (blockIdx.x % SPLIT) * DC;
     const int b = bh / a.Hv;
     const int h = bh - b * a.Hv;
     const int hq = h / (a.Hv / a.Hqk);
     const int tid = threadIdx.x, tx = tid % CG, ty = tid / CG;
     const int wave = tid >> 6, lane = tid & 63;
 
-    float *S = a.S + (size_t)bh * D * D;
+    float *S = a.S + (size_t)bh * D * D + c0;
     f32x4 st[NR];
 #pragma unroll
     for (int m = 0; m < NR; ++m) st[m] = load_state4(S + (size_t)(ty + m * RS) * D + 4 * tx);
@@ -104,7 +105,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     }
     __syncthreads();
 
-    const IO *vp = static_cast<const IO *>(a.v) + (size_t)bh * D + 4 * tx;
+    const IO *vp = static_cast<const IO *>(a.v) + (size_t)bh * D + c0 + 4 * tx;
     const float bt = a.beta ? a.beta[bh] : 0.f;
     const float qk = s_qk;
     float u[4], o[4];
@@ -117,7 +118,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
             p += s_red[w][1][4 * tx + c];
         }
         const float vv = E::load(vp + c);
-        const float z = a.beta ? bt * vv : E::load(static_cast<const IO *>(a.wg) + (size_t)bh * D + 4 * tx + c) * vv;
+        const float z = a.beta ? bt * vv : E::load(static_cast<const IO *>(a.wg) + (size_t)bh * D + c0 + 4 * tx + c) * vv;
         u[c] = z - r;
         o[c] = a.scale * (p + qk * u[c]);
     }
@@ -129,16 +130,20 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         store_state4(S + (size_t)(ty + m * RS) * D + 4 * tx, st[m]);
     }
     if (ty == 0) {
-        IO *op = static_cast<IO *>(a.o) + (size_t)bh * D + 4 * tx;
+        IO *op = static_cast<IO *>(a.o) + (size_t)bh * D + c0 + 4 * tx;
 #pragma unroll
         for (int c = 0; c < 4; ++c) op[c] = E::to(o[c]);
     }
 }
 
+// 128 x 128 states are split over two workgroups by value columns (32 KiB of
+// state each): streaming 32 KiB per workgroup reaches a higher HBM rate on
+// MI355X than 64 KiB, and the columns are independent.
 template <typename IO, int D>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t s) {
-    const unsigned grid = (unsigned)a.B * (unsigned)a.Hv;
-    hipLaunchKernelGGL((decode_kernel<IO, D>), dim3(grid), dim3(256), 0, s, a);
+    constexpr int SPLIT = D == 128 ? 2 : 1;
+    const unsigned grid = (unsigned)a.B * (unsigned)a.Hv * SPLIT;
+    hipLaunchKernelGGL((decode_kernel<IO, D, SPLIT>), dim3(grid), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
