@@ -257,7 +257,7 @@ def main(argv=None):
                  "unfused_round_trip_bytes": 2 * (d["q"].nbytes + d["k"].nbytes + d["v"].nbytes),
                  "roofline": {"bound": "hbm", "achieved": s_bytes / (s_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
                               "unit": "GB/s", "frac": s_bytes / (s_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                              "algorithmic_bytes": s_bytes}}
+                              "traffic": recorded_traffic(wl.name + "_input_stage"), "algorithmic_bytes": s_bytes}}
         del raw, rd, conv_out
 
     # ---- decode ----

@@ -250,10 +250,10 @@ struct PrepCfg {
 // x / sqrt(sum x^2 + kStageNormEps); the gates are logistic functions of
 // their inputs, and the decay is g = -c softplus(x).
 constexpr float kStageNormEps = 1e-12f;
-__device__ __forceinline__ float sigmoidf(float x) { return 1.f / (1.f + expf(-x)); }
+__device__ __forceinline__ float sigmoidf(float x) { return act_sigmoid(x); }
 template <bool RAW>
 __device__ __forceinline__ float stage_decay(float x, float c) {
-    if constexpr (RAW) return -c * (fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))));
+    if constexpr (RAW) return -c * act_softplus(x);
     else return x;
 }
 
@@ -391,6 +391,21 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
         __syncthreads();  // the previous unit is done with shared memory
 
         // ---- A. prefix sums, token tables, tiles ----
+        // Input stage: this thread's convolution taps (q, k and v channels).
+        // The one-workgroup-per-CU variants have the registers to request
+        // them first, so that their latency hides behind phase A; the others
+        // load each tensor's taps where they are used.
+        constexpr bool EARLY_TAPS = RAW && prep_occupancy<IO, D, CHAN, BW>() == 1;
+        f32x4 taps[EARLY_TAPS ? 3 * V : 1];
+        if constexpr (EARLY_TAPS) {
+            const size_t sqk = (size_t)a.Hqk * D;
+            const size_t cq = (size_t)(h / grpsz) * D + V * co;
+            const size_t cb[3] = {cq, sqk + cq, 2 * sqk + (size_t)h * D + V * co};
+#pragma unroll
+            for (int x = 0; x < 3; ++x)
+#pragma unroll
+                for (int c4 = 0; c4 < V; ++c4) taps[x * V + c4] = load4f(a.conv_w + (cb[x] + c4) * 4);
+        }
         float G[CHAN ? TPT : 1][V];
         if constexpr (CHAN) {
 #pragma unroll
@@ -476,7 +491,9 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
                 for (int j = 0; j < TPT; ++j) wnd[3 + j] = x[j];
 #pragma unroll
                 for (int c4 = 0; c4 < V; ++c4) {
-                    const f32x4 tp = load4f(a.conv_w + (cbase + c4) * 4);
+                    f32x4 tp;
+                    if constexpr (EARLY_TAPS) tp = taps[xi * V + c4];
+                    else tp = load4f(a.conv_w + (cbase + c4) * 4);
                     float xc[TPT + 3];
 #pragma unroll
                     for (int r = 0; r < TPT + 3; ++r) xc[r] = R::at(wnd[r], c4);

@@ -109,6 +109,18 @@ template <> struct Mma16<float> {
     }
 };
 
+// Input-stage activations on the hardware's base-2 exp and log (v_exp_f32,
+// v_log_f32, about 1 ulp each), written from the definitions:
+//   sigmoid(x)  = 1 / (1 + e^-x)
+//   softplus(x) = max(x, 0) + ln(1 + e^-|x|)   (no overflow for any x)
+__device__ __forceinline__ float act_sigmoid(float x) {
+    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
+}
+__device__ __forceinline__ float act_softplus(float x) {
+    return fmaxf(x, 0.f) +
+           0.6931471805599453f * __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * fabsf(x)));
+}
+
 // Sum over NL (4, 8 or 16) consecutive lanes, aligned to NL, result in every
 // one of them, by DPP row permutations: swap neighbours, swap pairs, then
 // fold each 8-lane half onto its mirror image, and for 16 lanes the two

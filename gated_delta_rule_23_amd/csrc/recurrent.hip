@@ -61,13 +61,13 @@ __device__ __forceinline__ f32x4 exp4(f32x4 g) { return f32x4{expf(g[0]), expf(g
 // q and k are normalised as x / sqrt(sum x^2 + kNormEps).
 constexpr float kNormEps = 1e-12f;
 
-// Input-stage activations: the logistic function for the gates, and
-// softplus(x) = max(x, 0) + log(1 + exp(-|x|)) for the decay.
-__device__ __forceinline__ float sigmoid1(float x) { return 1.f / (1.f + expf(-x)); }
+// Input-stage activations: the logistic function for the gates, softplus
+// for the decay.
+__device__ __forceinline__ float sigmoid1(float x) { return act_sigmoid(x); }
 __device__ __forceinline__ f32x4 sigmoid4(f32x4 x) {
     return f32x4{sigmoid1(x[0]), sigmoid1(x[1]), sigmoid1(x[2]), sigmoid1(x[3])};
 }
-__device__ __forceinline__ float softplus1(float x) { return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))); }
+__device__ __forceinline__ float softplus1(float x) { return act_softplus(x); }
 
 // One 4-channel slice of the input stage for token t of sequence b: the
 // depthwise causal convolution of kernel 4 over tokens t-3 .. t (tokens
