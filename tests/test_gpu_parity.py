@@ -631,6 +631,50 @@ def test_prefill_input_stage_zero_tokens():
     assert torch.count_nonzero(cout) == 0
 
 
+# ---------------------------------------------------------------------------
+# Seeded random configurations across every entry point.
+
+def _random_config(seed):
+    rng = np.random.default_rng(1000 + seed)
+    io = ["bf16", "f32"][rng.integers(2)]
+    D = [32, 64, 128][seed % 3]
+    decay, gates = MODES[rng.integers(len(MODES))]
+    B, Hqk = int(rng.integers(1, 4)), int(rng.integers(1, 3))
+    Hv = Hqk * int(rng.integers(1, 4))
+    T = int(rng.integers(1, 300))
+    scale = [1.0, D ** -0.5][rng.integers(2)]
+    return io, D, decay, gates, B, Hqk, Hv, T, bool(rng.integers(2)), scale
+
+
+@pytest.mark.parametrize("seed", range(15))
+def test_random_configurations(seed):
+    """Dtype, head dimension, gate and decay mode, batch, head grouping,
+    length, initial state and read scale drawn from a fixed seed; the
+    chunked prefill (where the dtype and dimension are supported), the
+    recurrent forward and both input-stage entry points against the oracle."""
+    io, D, decay, gates, B, Hqk, Hv, T, has_s0, scale = _random_config(seed)
+    wl = small_workload(io, D, decay, gates, T=T, B=B, Hqk=Hqk, Hv=Hv, S0=has_s0, scale=scale)
+    inp = gs.make_inputs(wl, seed=seed)
+    say(f"random {seed}: {wl.name} B={B} Hqk={Hqk} Hv={Hv} scale={scale:.3f}")
+    S0 = to_dev(inp["S0"])
+    o_ref, S_ref = oracle_prefill(inp)
+    if io == "bf16" or D <= 64:
+        o, ST = gpu_prefill(inp, S0=S0)
+        assert rel_err(from_dev(o), o_ref) < TOL[io] and rel_err(from_dev(ST), S_ref) < TOL[io]
+    o, ST = gpu_recurrent(inp, S0=S0)
+    assert rel_err(from_dev(o), o_ref) < TOL[io] and rel_err(from_dev(ST), S_ref) < TOL[io]
+    raw = gs.make_raw_inputs(wl, seed=seed, conv_state=bool(seed % 2))
+    cin = "stored" if seed % 2 else None
+    o_ref, S_ref, c_ref = oracle_input_stage(raw, conv_in=cin)
+    S0 = to_dev(raw["S0"])
+    runs = [gpu_recurrent_in(raw, S0=S0, conv_in=cin)]
+    if io == "bf16" or D <= 64:
+        runs.append(gpu_prefill_in(raw, S0=S0, conv_in=cin))
+    for o, ST, cout in runs:
+        assert rel_err(from_dev(o), o_ref) < TOL[io] and rel_err(from_dev(ST), S_ref) < TOL[io]
+        assert _conv_equal(cout, c_ref)
+
+
 def test_state_alloc_is_zeroed():
     import gated_delta_rule_23_amd as gdr
     ptr, n = gdr.gdr_state_alloc(2, 3, 64, 64)
