@@ -78,6 +78,22 @@ def test_l2norm_unit_and_zero():
     assert not np.any(ist.l2norm(np.zeros((2, 8))))
 
 
+def test_stage_normalises_q_and_k_not_v():
+    """From arbitrary raw inputs (impulse taps), q and k leave the stage with
+    unit norm per (token, head) and their directions unchanged; v keeps its
+    raw values."""
+    rng = np.random.default_rng(8)
+    B, T, Hqk, Hv, d = 2, 5, 2, 4, 16
+    xq, xk = 3.0 * rng.standard_normal((B, T, Hqk, d)), 0.2 * rng.standard_normal((B, T, Hqk, d))
+    xv = 5.0 * rng.standard_normal((B, T, Hv, d))
+    taps = np.tile([0.0, 0.0, 0.0, 1.0], (ist.conv_channels(Hqk, Hv, d, d), 1))
+    out, _ = ist.input_stage(xq, xk, xv, taps, beta=np.zeros((B, T, Hv)))
+    for name, raw in (("q", xq), ("k", xk)):
+        assert np.allclose(np.linalg.norm(out[name], axis=-1), 1.0, rtol=0, atol=1e-10)   # eps 1e-12 inside the root
+        assert np.allclose(out[name] * np.linalg.norm(raw, axis=-1, keepdims=True), raw, rtol=1e-10)
+    assert np.array_equal(out["v"], xv)
+
+
 def test_gate_functions_closed_forms():
     assert ist.sigmoid(np.array([0.0]))[0] == 0.5
     xs = np.array([-30.0, -2.5, -0.1, 0.3, 4.0, 700.0, -700.0])
