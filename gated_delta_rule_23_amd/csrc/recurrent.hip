@@ -26,10 +26,16 @@
 //
 // The state is streamed with non-temporal loads and stores (it is not reused
 // within the call, and a model touches every other layer's state before this
-// one's next call). Work per token and head is about 4 D^2 flops against D^2 fp32 of state
-// that is read and written once per call: a run of a few tokens is bound by
-// HBM, a long one by the vector ALUs (long prefills belong to the chunked
-// path, whose products run on the matrix cores).
+// one's next call). Work per token and head is about 4 D^2 flops against
+// D^2 fp32 of state that is read and written once per call: a run of a few
+// tokens is bound by HBM, a long one by the vector ALUs (long prefills belong
+// to the chunked path, whose products run on the matrix cores).
+//
+// With the input stage (RAW), q, k and v arrive as raw projections: the
+// staging pass convolves each token's 4-token window (the depthwise causal
+// convolution of kernel 4; tokens before the call from the convolution
+// state), normalises q and k over the head, and applies the gate and decay
+// activations before staging; the processed values exist only on chip.
 #include "common.hpp"
 #include "kernels.hpp"
 
