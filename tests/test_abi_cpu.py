@@ -204,3 +204,24 @@ def test_binding_rejects_bad_tensors():
     q = torch.zeros(1, 4, 1, 32, dtype=torch.float64)
     with pytest.raises((TypeError, ValueError)):
         gdr.gdr_chunk_fwd(q, q, q, beta=torch.zeros(1, 4, 1))
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """include/gdr.h compiles as C99 with warnings as errors, and a C program
+    linked against libgdr.so gets the documented results from the calls that
+    need no GPU (tests/c_abi/abi_check.c)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not found")
+    here = os.path.dirname(os.path.abspath(__file__))
+    root = os.path.dirname(here)
+    libdir = os.path.dirname(gdr.LIB_PATH)
+    exe = str(tmp_path / "abi_check")
+    cmd = [gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", os.path.join(root, "include"),
+           os.path.join(here, "c_abi", "abi_check.c"), "-L", libdir, "-lgdr", "-Wl,-rpath," + libdir, "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
