@@ -809,10 +809,14 @@ struct ChainOps {  // Y rows and U_z columns of the wave's token tiles; Kend^T (
     f32x4 er[CHAN ? 1 : Sh::TPW];    // exp(G_end - G) of the wave's token rows (scalar decay)
 
     __device__ __forceinline__ void load(const SweepSrc<IO> &src, int c, int w, int col0) {
+        load_a(src, c, w, col0);
+        load_b(src, c, w);
+    }
+    // The operands of U = U_z - Y S_c.
+    __device__ __forceinline__ void load_a(const SweepSrc<IO> &src, int c, int w, int col0) {
         const int l = threadIdx.x & 63, lq = l >> 4;
         const size_t u = src.u0 + c;
         const IO *Y = src.ws + u * chunk_ws_io_elems(D, CHAN), *UzT = Y + ws_off_uz(D, CHAN);
-        const IO *KT = CHAN ? Y + 2 * C * D : src.kT + (size_t)c * 2 * D * C;
         const float *tab = src.tab + u * kTab;
 #pragma unroll
         for (int tt = 0; tt < Sh::TPW; ++tt) {
@@ -824,6 +828,14 @@ struct ChainOps {  // Y rows and U_z columns of the wave's token tiles; Kend^T (
                 uz[tt][ct] = R4::load(UzT + ((size_t)(rt * (D / 16) + col0 / 16 + ct) * 64 + l) * 4);
             if constexpr (!CHAN) er[tt] = load4f(tab + C + rt * 16 + 4 * lq);
         }
+    }
+    // The operands of the state update.
+    __device__ __forceinline__ void load_b(const SweepSrc<IO> &src, int c, int w) {
+        const int l = threadIdx.x & 63, lq = l >> 4;
+        const size_t u = src.u0 + c;
+        const IO *Y = src.ws + u * chunk_ws_io_elems(D, CHAN);
+        const IO *KT = CHAN ? Y + 2 * C * D : src.kT + (size_t)c * 2 * D * C;
+        const float *tab = src.tab + u * kTab;
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
             const int ch0 = 32 * w + 16 * rt;
@@ -843,9 +855,14 @@ struct OutOps {  // Q~ (q) and A rows of the wave's token tiles
     f32x4 eg[CHAN ? 1 : Sh::TPW];    // exp(G) of the wave's token rows (scalar decay)
 
     __device__ __forceinline__ void load(const SweepSrc<IO> &src, int c, int w) {
+        load_a(src, c, w);
+        load_b(src, c, w);
+    }
+    // The operands of Q~ S_c.
+    __device__ __forceinline__ void load_a(const SweepSrc<IO> &src, int c, int w) {
         const int l = threadIdx.x & 63, lq = l >> 4;
         const size_t u = src.u0 + c;
-        const IO *unit = src.ws + u * chunk_ws_io_elems(D, CHAN), *A = unit + ws_off_a(D, CHAN);
+        const IO *unit = src.ws + u * chunk_ws_io_elems(D, CHAN);
 #pragma unroll
         for (int tt = 0; tt < Sh::TPW; ++tt) {
             const int rt = w * Sh::TPW + tt;
@@ -858,16 +875,27 @@ struct OutOps {  // Q~ (q) and A rows of the wave's token tiles
                 for (int ks = 0; ks < Sh::KD; ++ks) qa[tt][ks] = load_frag(Qf, rt, ks, D);
                 eg[tt] = load4f(src.tab + u * kTab + rt * 16 + 4 * lq);
             }
-#pragma unroll
-            for (int ks = 0; ks < Sh::KC; ++ks) aa[tt][ks] = load_frag(A, rt, ks, C);
         }
+    }
+    // The operand of A U.
+    __device__ __forceinline__ void load_b(const SweepSrc<IO> &src, int c, int w) {
+        const size_t u = src.u0 + c;
+        const IO *A = src.ws + u * chunk_ws_io_elems(D, CHAN) + ws_off_a(D, CHAN);
+#pragma unroll
+        for (int tt = 0; tt < Sh::TPW; ++tt)
+#pragma unroll
+            for (int ks = 0; ks < Sh::KC; ++ks) aa[tt][ks] = load_frag(A, w * Sh::TPW + tt, ks, C);
     }
 };
 
 // One chunk on a chain wave.
-template <typename IO, int D, int NCT, bool CHAN>
-__device__ __forceinline__ void chain_chunk(const ChainOps<IO, D, NCT, CHAN> &op, f32x4 (&S)[2][NCT], IO *sST,
-                                            IO *sUT, IO *sUK, int w, bool zero_uz = false) {
+// With RELOAD, the wave refills op with chunk cn's operands as soon as each
+// part has been consumed (the U operands before the second barrier, the
+// state-update operands at the end), spreading its loads over the chunk.
+template <typename IO, int D, int NCT, bool CHAN, bool RELOAD = false>
+__device__ __forceinline__ void chain_chunk(ChainOps<IO, D, NCT, CHAN> &op, f32x4 (&S)[2][NCT], IO *sST,
+                                            IO *sUT, IO *sUK, int w, bool zero_uz = false,
+                                            const SweepSrc<IO> *src = nullptr, int cn = 0, int col0 = 0) {
     using Sh = SweepShape<IO, D, NCT>;
     using M = typename Sh::M;
     using F = typename M::Frag;
@@ -897,6 +925,7 @@ __device__ __forceinline__ void chain_chunk(const ChainOps<IO, D, NCT, CHAN> &op
             if constexpr (!CHAN) store4f(sUK + (16 * ct + lr) * LU + T0 + 4 * lq, U * op.er[tt]);
         }
     }
+    if constexpr (RELOAD) op.load_a(*src, cn, w, col0);
     __syncthreads();  // U^T is shared
     const IO *sU = CHAN ? sUT : sUK;
     F ub[Sh::KC][NCT];
@@ -913,15 +942,17 @@ __device__ __forceinline__ void chain_chunk(const ChainOps<IO, D, NCT, CHAN> &op
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) S[rt][ct] = M::mma(S[rt][ct], op.ka[rt][ks], ub[ks][ct]);
     }
+    if constexpr (RELOAD) op.load_b(*src, cn, w);
 }
 
 // One chunk on an output wave (w = its index among the output waves). TAIL =
 // the chunk may hold fewer than C tokens (only the last one), so output rows
 // are stored under a predicate; every other chunk stores unconditionally,
 // which keeps the number of memory operations in flight static.
-template <typename IO, int D, int NCT, bool CHAN, bool TAIL>
-__device__ __forceinline__ void out_chunk(const OutOps<IO, D, NCT, CHAN> &op, const IO *sST, const IO *sUT, IO *sO,
-                                          IO *orow0, size_t orow_stride, int n_valid, float scale, int w) {
+template <typename IO, int D, int NCT, bool CHAN, bool TAIL, bool RELOAD = false>
+__device__ __forceinline__ void out_chunk(OutOps<IO, D, NCT, CHAN> &op, const IO *sST, const IO *sUT, IO *sO,
+                                          IO *orow0, size_t orow_stride, int n_valid, float scale, int w,
+                                          const SweepSrc<IO> *src = nullptr, int cn = 0) {
     using Sh = SweepShape<IO, D, NCT>;
     using M = typename Sh::M;
     using F = typename M::Frag;
@@ -942,6 +973,7 @@ __device__ __forceinline__ void out_chunk(const OutOps<IO, D, NCT, CHAN> &op, co
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) accR[tt][ct] *= op.eg[tt];
     }
+    if constexpr (RELOAD) op.load_a(*src, cn, w);
     __syncthreads();  // U^T is shared
     F ub[Sh::KC][NCT];
 #pragma unroll
@@ -972,6 +1004,7 @@ __device__ __forceinline__ void out_chunk(const OutOps<IO, D, NCT, CHAN> &op, co
                 st16_stream(orow0 + tok * orow_stride + c8, *reinterpret_cast<const uint4 *>(sO + tok * LO + c8));
         }
     }
+    if constexpr (RELOAD) op.load_b(*src, cn, w);
 }
 
 template <typename IO, int D, int NCT, int PF, bool CHAN>
@@ -1029,10 +1062,9 @@ __global__ __launch_bounds__(4 * D) void chunk_sweep(ChunkArgs a, int NVT, int G
             int c = 0;
             for (; c + PF <= NC - 1; c += PF) {
 #pragma unroll
-                for (int j = 0; j < PF; ++j) {
-                    chain_chunk<IO, D, NCT, CHAN>(ring[j], S, sST, sUT, sUK, w);
-                    ring[j].load(src, min(c + j + PF, NC - 1), w, col0);
-                }
+                for (int j = 0; j < PF; ++j)
+                    chain_chunk<IO, D, NCT, CHAN, true>(ring[j], S, sST, sUT, sUK, w, false, &src,
+                                                        min(c + j + PF, NC - 1), col0);
             }
 #pragma unroll
             for (int j = 0; j < PF; ++j)
@@ -1059,12 +1091,10 @@ __global__ __launch_bounds__(4 * D) void chunk_sweep(ChunkArgs a, int NVT, int G
         int c = 0;
         for (; c + PF <= NC - 1; c += PF) {
 #pragma unroll
-            for (int j = 0; j < PF; ++j) {
-                out_chunk<IO, D, NCT, CHAN, false>(ring[j], sST, sUT, sO, obase + (size_t)(c + j) * C * orow_stride,
-                                                   orow_stride, C, a.scale, w);
-                const int cn = min(c + j + PF, NC - 1);
-                ring[j].load(src, cn, w);
-            }
+            for (int j = 0; j < PF; ++j)
+                out_chunk<IO, D, NCT, CHAN, false, true>(ring[j], sST, sUT, sO,
+                                                         obase + (size_t)(c + j) * C * orow_stride, orow_stride, C,
+                                                         a.scale, w, &src, min(c + j + PF, NC - 1));
         }
 #pragma unroll
         for (int j = 0; j < PF; ++j) {
