@@ -852,7 +852,7 @@ struct OutOps {  // Q~ (q) and A rows of the wave's token tiles
     using Sh = SweepShape<IO, D, NCT>;
     using F = typename Sh::M::Frag;
     F qa[Sh::TPW][Sh::KD], aa[Sh::TPW][Sh::KC];
-    f32x4 eg[CHAN ? 1 : Sh::TPW];    // exp(G) of the wave's token rows (scalar decay)
+    float eg[CHAN ? 1 : Sh::TPW];    // exp(G) of this lane's token in each of the wave's tiles (scalar decay)
 
     __device__ __forceinline__ void load(const SweepSrc<IO> &src, int c, int w) {
         load_a(src, c, w);
@@ -860,7 +860,7 @@ struct OutOps {  // Q~ (q) and A rows of the wave's token tiles
     }
     // The operands of Q~ S_c.
     __device__ __forceinline__ void load_a(const SweepSrc<IO> &src, int c, int w) {
-        const int l = threadIdx.x & 63, lq = l >> 4;
+        const int lr = threadIdx.x & 15;
         const size_t u = src.u0 + c;
         const IO *unit = src.ws + u * chunk_ws_io_elems(D, CHAN);
 #pragma unroll
@@ -873,7 +873,7 @@ struct OutOps {  // Q~ (q) and A rows of the wave's token tiles
                 const IO *Qf = src.kT + (size_t)c * 2 * D * C + D * C;
 #pragma unroll
                 for (int ks = 0; ks < Sh::KD; ++ks) qa[tt][ks] = load_frag(Qf, rt, ks, D);
-                eg[tt] = load4f(src.tab + u * kTab + rt * 16 + 4 * lq);
+                eg[tt] = src.tab[u * kTab + rt * 16 + lr];
             }
         }
     }
@@ -945,10 +945,15 @@ __device__ __forceinline__ void chain_chunk(ChainOps<IO, D, NCT, CHAN> &op, f32x
     if constexpr (RELOAD) op.load_b(*src, cn, w);
 }
 
-// One chunk on an output wave (w = its index among the output waves). TAIL =
-// the chunk may hold fewer than C tokens (only the last one), so output rows
-// are stored under a predicate; every other chunk stores unconditionally,
-// which keeps the number of memory operations in flight static.
+// One chunk on an output wave (w = its index among the output waves). The
+// wave forms its token tiles of O transposed, O^T = S_c^T Q~^T + U^T A^T (the
+// matrix-core operands swapped), so each lane holds 4 consecutive value
+// columns of one token: they go to the staging rows as one 8- or 16-byte
+// write. With RELOAD the wave refills op with chunk cn's Q~ once the second
+// barrier has passed and its A at the end. TAIL = the chunk may hold fewer
+// than C tokens (only the last one), so output rows are stored under a
+// predicate; every other chunk stores unconditionally, which keeps the number
+// of memory operations in flight static.
 template <typename IO, int D, int NCT, bool CHAN, bool TAIL, bool RELOAD = false>
 __device__ __forceinline__ void out_chunk(OutOps<IO, D, NCT, CHAN> &op, const IO *sST, const IO *sUT, IO *sO,
                                           IO *orow0, size_t orow_stride, int n_valid, float scale, int w,
@@ -968,13 +973,13 @@ __device__ __forceinline__ void out_chunk(OutOps<IO, D, NCT, CHAN> &op, const IO
         for (int ks = 0; ks < Sh::KD; ++ks)
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
-                accR[tt][ct] = M::mma(accR[tt][ct], op.qa[tt][ks], M::load(sST + 16 * ct * LS + ks * KS, LS));
+                accR[tt][ct] = M::mma(accR[tt][ct], M::load(sST + 16 * ct * LS + ks * KS, LS), op.qa[tt][ks]);
         if constexpr (!CHAN)
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) accR[tt][ct] *= op.eg[tt];
     }
-    if constexpr (RELOAD) op.load_a(*src, cn, w);
     __syncthreads();  // U^T is shared
+    if constexpr (RELOAD) op.load_a(*src, cn, w);
     F ub[Sh::KC][NCT];
 #pragma unroll
     for (int ks = 0; ks < Sh::KC; ++ks)
@@ -989,12 +994,9 @@ __device__ __forceinline__ void out_chunk(OutOps<IO, D, NCT, CHAN> &op, const IO
 #pragma unroll
         for (int ks = 0; ks < Sh::KC; ++ks)
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) accR[tt][ct] = M::mma(accR[tt][ct], op.aa[tt][ks], ub[ks][ct]);
+            for (int ct = 0; ct < NCT; ++ct) accR[tt][ct] = M::mma(accR[tt][ct], ub[ks][ct], op.aa[tt][ks]);
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                sO[(T0 + 4 * lq + r) * LO + 16 * ct + lr] = Elem<IO>::to(scale * accR[tt][ct][r]);
+        for (int ct = 0; ct < NCT; ++ct) store4f(sO + (T0 + lr) * LO + 16 * ct + 4 * lq, scale * accR[tt][ct]);
         // This wave's output rows, 16 bytes per lane (wave-local staging).
         constexpr int V = 16 / sizeof(IO), PER = BV / V;
 #pragma unroll
