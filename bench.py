@@ -5,7 +5,9 @@ One step = one chunked prefill of the Qwen3.8-27B-shaped Gated DeltaNet layer
 through gdr_chunk_fwd. In the same run the decode step is measured on its own
 workload (64 sequences x 48 V heads, 128 x 128 fp32 states, 256 consecutive
 gdr_decode_step calls). Inputs are seeded synthetic tensors already resident
-in device memory when timing starts. The timed calls are captured once as a
+in device memory when timing starts, after the warmup steps and a further
+--warmup-s seconds of untimed calls (the GPU's clocks take that long to
+settle). The timed calls are captured once as a
 HIP graph (the way a serving loop launches them, without per-launch host
 overhead) and timed over one replay with HIP events on the stream the graph
 runs on; the JSON also gives the eager per-call time (events around each
@@ -131,6 +133,9 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup-s", type=float, default=1.0,
+                    help="after the warmup steps, keep running untimed steps for this many seconds so that the "
+                         "GPU's clocks have settled before anything is timed")
     ap.add_argument("--decode-steps", type=int, default=256, help="consecutive decode steps timed (0 = skip decode)")
     ap.add_argument("--input-stage", type=int, default=1,
                     help="also time the prefill from raw projections (input stage fused; 0 = skip)")
@@ -163,6 +168,14 @@ def main(argv=None):
             return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(a).to(dev)
 
+    def settle(fn):
+        """Untimed calls of fn for --warmup-s seconds: the GPU's clocks settle under load."""
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < args.warmup_s:
+            for _ in range(8):
+                fn()
+            torch.cuda.synchronize()
+
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib * 2 ** 20 // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -193,6 +206,7 @@ def main(argv=None):
     for _ in range(args.warmup):
         prefill()
     torch.cuda.synchronize()
+    settle(prefill)
     # Reference: HIP events around each of K eager calls.
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for i in range(args.steps):
@@ -238,6 +252,7 @@ def main(argv=None):
         for _ in range(args.warmup):
             prefill_in()
         torch.cuda.synchronize()
+        settle(prefill_in)
         sgraph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(sgraph):
             for _ in range(args.steps):
@@ -279,6 +294,8 @@ def main(argv=None):
 
         for s in range(min(8, dwl.T)):
             dstep(s)
+        wstep = iter(range(1 << 62))
+        settle(lambda: dstep(next(wstep) % dwl.T))
         S.copy_(S0d)
         torch.cuda.synchronize()
         # Reference: events around each eager step.
@@ -363,6 +380,10 @@ def main(argv=None):
 
         for i in range(len(r_states)):
             rcall(i)
+        wcall = iter(range(1 << 62))
+        settle(lambda: rcall(next(wcall)))
+        for Sl in r_states:
+            Sl.copy_(up(rinp["S0"]))
         torch.cuda.synchronize()
         rgraph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(rgraph):
@@ -394,6 +415,7 @@ def main(argv=None):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_s": args.warmup_s,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
