@@ -216,13 +216,14 @@ def main(argv=None):
     torch.cuda.synchronize()
     eager_call_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
     # Timed region: the K calls captured once as a HIP graph (as a serving loop
-    # launches them), replayed once untimed, then timed over one replay.
+    # launches them), replayed untimed for --warmup-s seconds (the GPU idles
+    # while the graph is captured, and its clocks drop), then timed over one
+    # replay.
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         for _ in range(args.steps):
             prefill()
-    graph.replay()
-    torch.cuda.synchronize()
+    settle(graph.replay)
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(cur())
@@ -257,8 +258,7 @@ def main(argv=None):
         with torch.cuda.graph(sgraph):
             for _ in range(args.steps):
                 prefill_in()
-        sgraph.replay()
-        torch.cuda.synchronize()
+        settle(sgraph.replay)
         t_start.record(cur())
         sgraph.replay()
         t_end.record(cur())
@@ -312,8 +312,7 @@ def main(argv=None):
         with torch.cuda.graph(dgraph):
             for s in range(dwl.T):
                 dstep(s)
-        S.copy_(S0d)
-        dgraph.replay()
+        settle(dgraph.replay)
         S.copy_(S0d)
         torch.cuda.synchronize()
         d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -340,8 +339,7 @@ def main(argv=None):
         with torch.cuda.graph(cgraph):
             for s in range(dwl.T):
                 dstep_layer(s)
-        cgraph.replay()
-        torch.cuda.synchronize()
+        settle(cgraph.replay)
         d0.record(cur())
         cgraph.replay()
         d1.record(cur())
@@ -389,8 +387,7 @@ def main(argv=None):
         with torch.cuda.graph(rgraph):
             for i in range(n_calls):
                 rcall(i)
-        rgraph.replay()
-        torch.cuda.synchronize()
+        settle(rgraph.replay)
         r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         r0.record(cur())
         rgraph.replay()
