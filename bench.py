@@ -24,9 +24,11 @@ advanced in turn, and the multi-token recurrent forward (gdr_recurrent_fwd,
 turn) gets its own object; --recurrent-T 0 skips it.
 
 Prints one JSON line: value = prefill tokens/s; "roofline" for the prefill
-call against HBM; "decode" with state GB/s and its own roofline; and
-"cpu_baseline", the fp64 CPU oracle timed on a bounded sample of the same
-prefill workload on this host's cores.
+call against HBM; "decode" with state GB/s and its own roofline; "copy", the
+bandwidth of a plain 1 GiB device copy timed in the same run, against which
+every HBM roofline also gives "frac_of_copy"; and "cpu_baseline", the fp64
+CPU oracle timed on a bounded sample of the same prefill workload on this
+host's cores.
 """
 from __future__ import annotations
 
@@ -146,6 +148,9 @@ def main(argv=None):
                     help="prefill workload of the timed step (default: the Qwen-shaped GDN layer, T=4096)")
     ap.add_argument("--cpu-heads", type=int, default=48, help="V heads in the CPU-oracle sample (0 = skip)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copy-mib", type=int, default=1024,
+                    help="size of each buffer of the plain device-to-device copy timed in the same run, the "
+                         "measured bandwidth the HBM rooflines are also reported against (0 = skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (for scaling memory counters)")
     args = ap.parse_args(argv)
@@ -182,6 +187,24 @@ def main(argv=None):
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
+        del src, dst
+
+    # ---- measured copy bandwidth: a plain device-to-device copy, read + write bytes ----
+    copy = None
+    if args.copy_mib > 0:
+        n = args.copy_mib * 2 ** 20 // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        settle(lambda: dst.copy_(src))
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 20
+        c0.record(torch.cuda.current_stream())
+        for _ in range(reps):
+            dst.copy_(src)
+        c1.record(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        copy = {"GBps": 2 * n * 4 * reps / (c0.elapsed_time(c1) * 1e-3) / 1e9, "bytes_per_copy": 2 * n * 4,
+                "kind": "torch device-to-device copy of %d MiB (bytes read + written)" % args.copy_mib}
         del src, dst
 
     # ---- prefill ----
@@ -432,6 +455,12 @@ def main(argv=None):
         "decode": dec,
         "recurrent": rec,
     }
+    out["copy"] = copy
+    if copy:  # the HBM rooflines also against the bandwidth a plain copy reaches on this GPU
+        for r in (out["roofline"], (stage or {}).get("roofline"), (dec or {}).get("roofline"),
+                  (rec or {}).get("roofline")):
+            if r:
+                r["frac_of_copy"] = r["achieved"] / copy["GBps"]
     if args.cpu_heads > 0:
         heads = list(range(0, wl.Hv, max(1, wl.Hv // min(args.cpu_heads, wl.Hv))))[:args.cpu_heads]
         out["cpu_baseline"] = cpu_baseline(wl, inp, heads)
