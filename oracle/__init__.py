@@ -15,6 +15,10 @@ Contents
                    that page's own layout, for tiny sizes (numpy, fp64).
 ``chunked``        the chunked (UT/WY) form on the CPU, fp64, used to pin the
                    chunk algebra against the sequential result.
+``input_stage``    the convolution, normalisation and gate activations before
+                   the recurrence (numpy, fp64).
+``backward``       the gradients of the recurrence by reverse-mode
+                   differentiation (numpy, fp64).
 
 Stored values: a ``numpy.uint16`` array holds bfloat16 bit patterns, a
 ``float32`` or ``float64`` array holds its own values. Every value is widened
