@@ -41,6 +41,7 @@ import time
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, published
 DECODE_COLD_LAYERS = 4        # states cycled in the decode "layers in turn" timing
 BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix, published
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "gated_delta_rule_23_amd", "csrc")
@@ -112,6 +113,23 @@ def recurrent_algorithmic(wl):
     return by
 
 
+def backward_algorithmic(wl):
+    """Bytes and flops of one backward call (gdr_recurrent_bwd) without S0:
+    every input read once (q, k per QK head; dO; dL/dS_T) and every gradient
+    written once in float32. Flops: the reverse step's 8 multiply-adds per
+    state entry and token (dS += s q do^T, dq, du, dk, de, dSbar, dalpha,
+    dS = alpha dSbar); the forward recomputation is not counted."""
+    esz = 2 if wl.io == "bf16" else 4
+    B, T, Hqk, Hv, D = wl.B, wl.T, wl.Hqk, wl.Hv, wl.dk
+    gate = B * T * Hv * 4 if wl.gates == "beta" else 2 * B * T * Hv * D
+    dec = {"none": 0, "scalar": B * T * Hv, "channel": B * T * Hv * D}[wl.decay]
+    reads = 2 * B * T * Hqk * D * esz + 2 * B * T * Hv * D * esz + B * Hv * D * D * 4
+    reads += (gate if wl.gates == "beta" else gate * esz) + dec * 4
+    writes = (2 * B * T * Hqk * D + B * T * Hv * D + B * Hv * D * D) * 4 + dec * 4
+    writes += B * T * Hv * 4 if wl.gates == "beta" else 2 * B * T * Hv * D * 4
+    return reads + writes, 16 * B * T * Hv * D * D
+
+
 def cpu_baseline(wl, inp, heads, min_seconds=10.0, max_reps=200):
     """Time the fp64 oracle (as it stands) on the given V heads of the prefill
     workload, repeating the run until about min_seconds of CPU work."""
@@ -143,6 +161,8 @@ def main(argv=None):
                     help="also time the prefill from raw projections (input stage fused; 0 = skip)")
     ap.add_argument("--recurrent-T", type=int, default=4,
                     help="tokens per sequence of the multi-token recurrent call timed at the decode shape (0 = skip)")
+    ap.add_argument("--backward", type=int, default=1,
+                    help="also time gdr_recurrent_bwd on the prefill workload (0 = skip)")
     ap.add_argument("--workload", default="qwen_gdn_prefill",
                     choices=["qwen_gdn_prefill", "kda_prefill", "gdn2_prefill", "gdn_small_f32"],
                     help="prefill workload of the timed step (default: the Qwen-shaped GDN layer, T=4096)")
@@ -298,6 +318,46 @@ def main(argv=None):
                               "traffic": recorded_traffic(wl.name + "_input_stage"), "algorithmic_bytes": s_bytes}}
         del raw, rd, conv_out
 
+    # ---- backward (gradients of the recurrence) on the prefill workload ----
+    bwd = None
+    if args.backward:
+        grads = gs.make_output_grads(wl, seed=args.seed + 3)
+        do_d, dST_d = up(grads["do"]), up(grads["dST"])
+        bdesc = gdr.make_desc(wl.B, wl.T, wl.Hqk, wl.Hv, wl.dk, gdr.GDR_BF16 if wl.io == "bf16" else gdr.GDR_F32,
+                              {"none": gdr.GDR_DECAY_NONE, "scalar": gdr.GDR_DECAY_SCALAR,
+                               "channel": gdr.GDR_DECAY_CHANNEL}[wl.decay], wl.scale)
+        bws = torch.empty(gdr.gdr_recurrent_bwd_workspace_bytes(bdesc), dtype=torch.uint8, device=dev)
+
+        def backward():
+            gdr.gdr_recurrent_bwd(d["q"], d["k"], d["v"], do_d, g=d["g"], beta=d["beta"], b=d["b"], w=d["w"],
+                                  dST=dST_d, scale=wl.scale, workspace=bws, stream=cur())
+
+        backward()
+        torch.cuda.synchronize()
+        n_b = max(2, min(args.steps, 10))
+        bgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(bgraph):
+            for _ in range(n_b):
+                backward()
+        settle(bgraph.replay)
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b0.record(cur())
+        bgraph.replay()
+        b1.record(cur())
+        torch.cuda.synchronize()
+        del bgraph
+        b_ms = b0.elapsed_time(b1) / n_b
+        b_bytes, b_flops = backward_algorithmic(wl)
+        bwd = {"entry": "gdr_recurrent_bwd", "workload": wl.name, "calls": n_b, "launch": "hip_graph",
+               "ms_per_call": b_ms, "tokens_per_s": wl.B * wl.T / (b_ms * 1e-3),
+               "roofline": {"kernel": "bwd_ckpt_kernel + bwd_kernel + bwd_reduce_kernel", "bound": "alu",
+                            "achieved": b_flops / (b_ms * 1e-3) / 1e12, "peak": FP32_VECTOR_PEAK_TFLOPS,
+                            "unit": "TFLOP/s", "frac": b_flops / (b_ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
+                            "algorithmic_flops": b_flops},
+               "hbm": {"achieved": b_bytes / (b_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                       "frac": b_bytes / (b_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, "algorithmic_bytes": b_bytes}}
+        del bws, do_d, dST_d
+
     # ---- decode ----
     dec = None
     if args.decode_steps > 0:
@@ -452,6 +512,7 @@ def main(argv=None):
         "mfma": {"algorithmic_tflops": pflops / (avg_call_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
                  "frac": pflops / (avg_call_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, "algorithmic_flops": pflops},
         "input_stage": stage,
+        "backward": bwd,
         "decode": dec,
         "recurrent": rec,
     }

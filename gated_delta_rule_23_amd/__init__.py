@@ -29,8 +29,8 @@ CHUNK = 64
 
 # Every symbol include/gdr.h declares.
 EXPORTS = ("gdr_state_bytes", "gdr_state_alloc", "gdr_state_free", "gdr_chunk_workspace_bytes",
-           "gdr_chunk_fwd", "gdr_decode_step", "gdr_recurrent_fwd", "gdr_recurrent_fwd_in", "gdr_chunk_fwd_in", "gdr_last_error",
-           "gdr_version")
+           "gdr_chunk_fwd", "gdr_decode_step", "gdr_recurrent_fwd", "gdr_recurrent_fwd_in", "gdr_chunk_fwd_in",
+           "gdr_recurrent_bwd_workspace_bytes", "gdr_recurrent_bwd", "gdr_last_error", "gdr_version")
 
 
 class GdrError(RuntimeError):
@@ -82,6 +82,10 @@ def _load():
     lib.gdr_recurrent_fwd_in.argtypes = [D, ctypes.POINTER(gdr_input_stage), P, P, P, P, P, P, P, P, P, P, P]
     lib.gdr_chunk_fwd_in.restype = I
     lib.gdr_chunk_fwd_in.argtypes = [D, ctypes.POINTER(gdr_input_stage), P, P, P, P, P, P, P, P, P, P, P, S, P]
+    lib.gdr_recurrent_bwd_workspace_bytes.restype = I
+    lib.gdr_recurrent_bwd_workspace_bytes.argtypes = [D, ctypes.POINTER(S)]
+    lib.gdr_recurrent_bwd.restype = I
+    lib.gdr_recurrent_bwd.argtypes = [D] + [P] * 19 + [S, P]
     lib.gdr_last_error.restype = ctypes.c_char_p
     lib.gdr_last_error.argtypes = []
     lib.gdr_version.restype = I
@@ -340,3 +344,50 @@ def gdr_recurrent_fwd_in(q, k, v, conv_w, *, conv_in=None, conv_out=None, decay_
     _check(lib.gdr_recurrent_fwd_in(ctypes.byref(desc), ctypes.byref(stage), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                     _ptr(beta), _ptr(b), _ptr(w), _ptr(S0), _ptr(o), _ptr(ST), _stream(stream)))
     return o, ST, conv_out
+
+
+def gdr_recurrent_bwd_workspace_bytes(desc: gdr_desc) -> int:
+    n = ctypes.c_size_t()
+    _check(lib.gdr_recurrent_bwd_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def gdr_recurrent_bwd(q, k, v, do, *, g=None, beta=None, b=None, w=None, S0=None, dST=None, scale=1.0,
+                      want_dS0=True, workspace=None, stream=None):
+    """Gradients of the recurrence for dL/do = do [B,T,Hv,D] (io dtype) and
+    dL/dS_T = dST ([B,Hv,D,D] float32, or None for zeros). Inputs as given to
+    the forward call. Returns a dict of float32 tensors: dq, dk, dv, and dg,
+    dbeta, db, dw, dS0 where they apply (dS0 only when want_dS0)."""
+    torch = _torch()
+    B, T, Hqk, D = q.shape
+    Hv = v.shape[2]
+    dev, io_t = q.device, q.dtype
+    for name, t, shape in (("q", q, (B, T, Hqk, D)), ("k", k, (B, T, Hqk, D)), ("v", v, (B, T, Hv, D)),
+                           ("b", b, (B, T, Hv, D)), ("w", w, (B, T, Hv, D)), ("do", do, (B, T, Hv, D))):
+        _require(t, name, shape, io_t, dev)
+    _require(beta, "beta", (B, T, Hv), torch.float32, dev)
+    _require(g, "g", None, torch.float32, dev)
+    _require(S0, "S0", (B, Hv, D, D), torch.float32, dev)
+    _require(dST, "dST", (B, Hv, D, D), torch.float32, dev)
+    desc = make_desc(B, T, Hqk, Hv, D, _io_dtype(q), _decay_of(g, (B, T), Hv, D), scale)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {"dq": torch.empty((B, T, Hqk, D), **f32), "dk": torch.empty((B, T, Hqk, D), **f32),
+           "dv": torch.empty((B, T, Hv, D), **f32)}
+    if g is not None:
+        out["dg"] = torch.empty(g.shape, **f32)
+    if beta is not None:
+        out["dbeta"] = torch.empty((B, T, Hv), **f32)
+    if b is not None:
+        out["db"] = torch.empty((B, T, Hv, D), **f32)
+        out["dw"] = torch.empty((B, T, Hv, D), **f32)
+    if want_dS0:
+        out["dS0"] = torch.empty((B, Hv, D, D), **f32)
+    nbytes = gdr_recurrent_bwd_workspace_bytes(desc)
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.gdr_recurrent_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(b),
+                                 _ptr(w), _ptr(S0), _ptr(do), _ptr(dST), _ptr(out["dq"]), _ptr(out["dk"]),
+                                 _ptr(out["dv"]), _ptr(out.get("dg")), _ptr(out.get("dbeta")), _ptr(out.get("db")),
+                                 _ptr(out.get("dw")), _ptr(out.get("dS0")), _ptr(workspace), wsz, _stream(stream)))
+    return out

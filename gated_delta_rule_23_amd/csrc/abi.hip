@@ -199,6 +199,27 @@ int recurrent_call(const gdr_desc *d, const gdr_input_stage *stage, const void *
     return ok();
 }
 
+// Byte ranges: an output must overlap neither another output nor any input
+// (NULL or empty ranges are skipped).
+struct Span {
+    const void *p;
+    size_t n;
+};
+bool spans_overlap(const Span &x, const Span &y) {
+    if (!x.p || !x.n || !y.p || !y.n) return false;
+    const char *a = static_cast<const char *>(x.p), *b = static_cast<const char *>(y.p);
+    return a < b + y.n && b < a + x.n;
+}
+bool any_overlap(std::initializer_list<Span> outs, std::initializer_list<Span> ins) {
+    for (auto x = outs.begin(); x != outs.end(); ++x) {
+        for (auto y = x + 1; y != outs.end(); ++y)
+            if (spans_overlap(*x, *y)) return true;
+        for (const Span &y : ins)
+            if (spans_overlap(*x, y)) return true;
+    }
+    return false;
+}
+
 }  // namespace
 
 extern "C" {
@@ -297,6 +318,75 @@ int gdr_recurrent_fwd_in(const gdr_desc *d, const gdr_input_stage *stage, const 
                          const float *S0, void *o, float *ST, void *stream) {
     if (!stage) return fail(GDR_E_INVAL, "stage is NULL");
     return recurrent_call(d, stage, q, k, v, g, beta, b, w, S0, o, ST, stream);
+}
+
+int gdr_recurrent_bwd_workspace_bytes(const gdr_desc *d, size_t *bytes) {
+    if (!bytes) return fail(GDR_E_INVAL, "bytes is NULL");
+    *bytes = 0;
+    static const char dummy = 0;
+    const void *p = &dummy;
+    const int rc = validate(d, CALL_RECURRENT, p, p, p, d && d->decay != GDR_DECAY_NONE ? (const float *)p : nullptr,
+                            (const float *)p, nullptr, nullptr, p);
+    if (rc != GDR_OK) return rc;
+    *bytes = gdr::bwd_ws_layout(d->B, d->T, d->H_v, d->d_k).total();
+    return ok();
+}
+
+int gdr_recurrent_bwd(const gdr_desc *d, const void *q, const void *k, const void *v, const float *g,
+                      const float *beta, const void *b, const void *w, const float *S0, const void *dO,
+                      const float *dST, float *dq, float *dk, float *dv, float *dg, float *dbeta, float *db,
+                      float *dw, float *dS0, void *workspace, size_t workspace_bytes, void *stream) {
+    if (d && d->B > 0 && d->T > 0 && !dO) return fail(GDR_E_INVAL, "dO must be non-NULL");
+    int rc = validate(d, CALL_RECURRENT, q, k, v, g, beta, b, w, dO);
+    if (rc != GDR_OK) return rc;
+    rc = check_alignment(d, {q, k, v, b, w, dO, S0, dST, dq, dk, dv, db, dw, dS0, workspace}, g, beta);
+    if (rc != GDR_OK) return rc;
+    const bool chan = d->decay == GDR_DECAY_CHANNEL;
+    if ((dg && !aligned(dg, chan ? 16 : 4)) || (dbeta && !aligned(dbeta, 4)))
+        return fail(GDR_E_INVAL, "dg or dbeta is misaligned");
+    const size_t BT = (size_t)d->B * d->T, D = d->d_k;
+    const size_t esz = d->io_dtype == GDR_BF16 ? 2 : 4;
+    const size_t nqk = BT * d->H_qk * D, nv = BT * d->H_v * D, nh = BT * d->H_v;
+    const size_t state = gdr_state_bytes(d->B, d->H_v, d->d_k, d->d_v);
+    const gdr::BwdWsLayout L = gdr::bwd_ws_layout(d->B, d->T, d->H_v, d->d_k);
+    if (d->B > 0 && d->T > 0) {
+        if (!dq || !dk || !dv) return fail(GDR_E_INVAL, "dq, dk and dv must be non-NULL");
+        if ((g == nullptr) != (dg == nullptr)) return fail(GDR_E_INVAL, "dg must be given exactly when g is");
+        if ((beta == nullptr) != (dbeta == nullptr)) return fail(GDR_E_INVAL, "dbeta must be given exactly when beta is");
+        if ((b == nullptr) != (db == nullptr) || (w == nullptr) != (dw == nullptr))
+            return fail(GDR_E_INVAL, "db and dw must be given exactly when b and w are");
+        if (!workspace || workspace_bytes < L.total())
+            return fail(GDR_E_INVAL, "workspace of %zu bytes needed, %zu given", L.total(),
+                        workspace ? workspace_bytes : 0);
+    }
+    const size_t ng = g ? (chan ? nv : nh) * 4 : 0;
+    if (any_overlap({{dq, nqk * 4}, {dk, nqk * 4}, {dv, nv * 4}, {dg, ng}, {dbeta, dbeta ? nh * 4 : 0},
+                     {db, db ? nv * 4 : 0}, {dw, dw ? nv * 4 : 0}, {dS0, dS0 ? state : 0}},
+                    {{q, nqk * esz}, {k, nqk * esz}, {v, nv * esz}, {g, ng}, {beta, beta ? nh * 4 : 0},
+                     {b, b ? nv * esz : 0}, {w, w ? nv * esz : 0}, {S0, S0 ? state : 0}, {dO, nv * esz},
+                     {dST, dST ? state : 0}, {workspace, workspace ? L.total() : 0}}))
+        return fail(GDR_E_INVAL, "gradient arrays must not overlap one another, the inputs or the workspace");
+    if (d->B == 0) return ok();
+    if ((long long)d->B * d->H_v * (d->d_k / gdr::kBwdCols) > 0x7fffffffll ||
+        (long long)d->B * d->T * d->H_qk > 0x7fffffffll)
+        return fail(GDR_E_UNSUPPORTED, "too many work items for one launch");
+    if (d->T == 0) {  // no token: the gradient reaching S0 is dL/dS_T itself
+        if (dS0) {
+            hipError_t e = gdr::launch_state_fill(dS0, dST, state / sizeof(float), static_cast<hipStream_t>(stream));
+            if (e != hipSuccess) return hip_fail(e, "dS0 copy");
+        }
+        return ok();
+    }
+    gdr::BwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.bg = b; a.wg = w; a.S0 = S0; a.dO = dO; a.dST = dST;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.db = db; a.dw = dw; a.dS0 = dS0;
+    a.ws_ck = static_cast<float *>(workspace);
+    a.ws_part = reinterpret_cast<float *>(static_cast<char *>(workspace) + L.ck_bytes);
+    a.B = d->B; a.T = d->T; a.Hqk = d->H_qk; a.Hv = d->H_v; a.decay = d->decay; a.scale = d->scale;
+    hipError_t e = gdr::launch_backward(d->io_dtype == GDR_BF16 ? gdr::IO_BF16 : gdr::IO_F32, d->d_k, a,
+                                        static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "backward launch");
+    return ok();
 }
 
 }  // extern "C"

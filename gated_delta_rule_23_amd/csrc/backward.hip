@@ -1,0 +1,371 @@
+// backward.hip -- gradients of the gated delta-rule recurrence, recurrent form.
+//
+// The page "Resumo Técnico: Gated DeltaNet-2", section "Treinamento Paralelo
+// Eficiente por Blocos", names a backward pass in which the per-channel
+// gates enter the gradient accumulation; it prints no formula. What is
+// computed here is the exact gradient of the forward recurrence for given
+// dL/do and dL/dS_T. Per (sequence, V head), walking the tokens in reverse
+// with dS = dL/dS_T:
+//
+//   dS    += s q_t do_t^T        dq_t = s S_t do_t
+//   du_t   = dS^T k_t            dk_t = dS u_t + (beta_t or b_t) . de_t
+//   dSbar  = dS - e_t du_t^T     de_t = -Sbar_t du_t,   dz_t = du_t
+//   dalpha = rowsum(dSbar . S_{t-1}),   dg_t = alpha_t . dalpha
+//   dS     = Diag(alpha_t) dSbar
+//
+// with Sbar_t = Diag(alpha_t) S_{t-1}, u_t = z_t - Sbar_t^T e_t and
+// S_t = Sbar_t + k_t u_t^T, then dv, dw, db, dbeta through e = beta k or b.k
+// and z = beta v or w.v.
+//
+// Three kernels:
+//  1. bwd_ckpt_kernel runs the forward recurrence and stores the state that
+//     enters every block of kBwdBlock = 8 tokens.
+//  2. bwd_kernel walks the blocks from the last: it replays the block from
+//     its checkpoint, keeping each state entering a token in shared memory,
+//     then runs the reverse recurrence above over the block with dS in
+//     registers.
+//  3. bwd_reduce_kernel sums what the value-column tiles contributed to the
+//     key-axis gradients (dq, dk, de, dalpha) and forms the gate gradients.
+//
+// A work item of kernels 1-2 is (sequence, V head, tile of kBwdCols = 32
+// value columns); 256 threads, thread (rg, c4) holding float4 column group c4
+// of state rows rg, rg + 32, ... Sums over the key axis (per column) combine
+// lanes by shuffles and the four waves through shared memory; sums over the
+// tile's columns (per row) combine the 8 lanes of a row group. Vector ALU
+// only: the step is a few operations per state entry.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace gdr {
+
+namespace {
+
+constexpr int BL = kBwdBlock;
+constexpr int CT = kBwdCols;
+constexpr int NTB = 256;
+
+template <int D>
+struct BwdShape {
+    static constexpr int NRW = D / 32;  // state rows per thread
+    static constexpr int TILES = D / CT;
+};
+
+// One block of tokens' inputs, staged in shared memory.
+template <int D>
+struct BwdStage {
+    float q[BL][D], k[BL][D], e[BL][D], al[BL][D];  // key-axis vectors
+    float z[BL][CT], dO[BL][CT], v[BL][CT], wv[BL][CT];  // this tile's value columns; wv = the write gate
+    float red[2][4][CT];                              // per-wave column sums, two slots used in turn
+};
+
+__device__ __forceinline__ float dot4(f32x4 a, f32x4 b) { return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3]; }
+
+// Sum over the 8 lanes of a row group (the tile's 32 value columns).
+__device__ __forceinline__ float rowsum8(float x) {
+    x += __shfl_xor(x, 1);
+    x += __shfl_xor(x, 2);
+    x += __shfl_xor(x, 4);
+    return x;
+}
+
+// Sum over the key axis for this thread's 4 columns: the 8 row groups of the
+// wave by shuffles, then the 4 waves through red (one __syncthreads). Every
+// thread gets the total.
+__device__ __forceinline__ f32x4 colsum(f32x4 p, float *red) {
+#pragma unroll
+    for (int off = 8; off < 64; off <<= 1)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) p[c] += __shfl_xor(p[c], off);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, c4 = lane & 7;
+    if (lane < 8) store4f(red + wave * CT + 4 * c4, p);
+    __syncthreads();
+    f32x4 s = load4f(red + 4 * c4);
+#pragma unroll
+    for (int w = 1; w < 4; ++w) s += load4f(red + w * CT + 4 * c4);
+    return s;
+}
+
+template <typename IO, int D, bool BWD>
+__device__ __forceinline__ void bwd_stage(const BwdArgs &a, BwdStage<D> &s, int b, int h, int hq, int col0, int t0,
+                                          int n) {
+    using E = Elem<IO>;
+    const int tid = threadIdx.x;
+    for (int x = tid; x < BL * D; x += NTB) {
+        const int tok = x / D, i = x - tok * D;
+        float qq = 0.f, kk = 0.f, ee = 0.f, al = 1.f;
+        if (tok < n) {
+            const size_t t = (size_t)b * a.T + t0 + tok;
+            const size_t qi = (t * a.Hqk + hq) * D + i, vi = (t * a.Hv + h) * D + i;
+            kk = E::load(static_cast<const IO *>(a.k) + qi);
+            if (BWD) qq = E::load(static_cast<const IO *>(a.q) + qi);
+            ee = (a.beta ? a.beta[t * a.Hv + h] : E::load(static_cast<const IO *>(a.bg) + vi)) * kk;
+            if (a.decay == DECAY_SCALAR) al = expf(a.g[t * a.Hv + h]);
+            else if (a.decay == DECAY_CHANNEL) al = expf(a.g[vi]);
+        }
+        s.q[tok][i] = qq;
+        s.k[tok][i] = kk;
+        s.e[tok][i] = ee;
+        s.al[tok][i] = al;
+    }
+    for (int x = tid; x < BL * CT; x += NTB) {
+        const int tok = x / CT, c = x - tok * CT;
+        float zz = 0.f, dd = 0.f, vv = 0.f, ww = 0.f;
+        if (tok < n) {
+            const size_t t = (size_t)b * a.T + t0 + tok;
+            const size_t vi = (t * a.Hv + h) * D + col0 + c;
+            vv = E::load(static_cast<const IO *>(a.v) + vi);
+            ww = a.beta ? a.beta[t * a.Hv + h] : E::load(static_cast<const IO *>(a.wg) + vi);
+            zz = ww * vv;
+            if (BWD) dd = E::load(static_cast<const IO *>(a.dO) + vi);
+        }
+        s.z[tok][c] = zz;
+        s.dO[tok][c] = dd;
+        s.v[tok][c] = vv;
+        s.wv[tok][c] = ww;
+    }
+}
+
+// One forward step of this thread's part of the state: S <- Sbar + k u^T,
+// returning u for its 4 columns.
+template <int D>
+__device__ __forceinline__ f32x4 fwd_step(f32x4 (&S)[BwdShape<D>::NRW], BwdStage<D> &s, int tok, int slot) {
+    const int tid = threadIdx.x, c4 = tid & 7, rg = tid >> 3;
+    f32x4 pr = zero4();
+#pragma unroll
+    for (int j = 0; j < BwdShape<D>::NRW; ++j) {
+        const int r = rg + 32 * j;
+        S[j] *= s.al[tok][r];
+        pr += S[j] * s.e[tok][r];
+    }
+    const f32x4 rr = colsum(pr, &s.red[slot][0][0]);
+    const f32x4 u = load4f(&s.z[tok][4 * c4]) - rr;
+#pragma unroll
+    for (int j = 0; j < BwdShape<D>::NRW; ++j) S[j] += s.k[tok][rg + 32 * j] * u;
+    return u;
+}
+
+template <typename IO, int D>
+__global__ __launch_bounds__(NTB) void bwd_ckpt_kernel(BwdArgs a) {
+    using Sh = BwdShape<D>;
+    extern __shared__ __align__(16) unsigned char smem[];
+    BwdStage<D> &s = *reinterpret_cast<BwdStage<D> *>(smem);
+    const int tile = blockIdx.x % Sh::TILES, bh = blockIdx.x / Sh::TILES, b = bh / a.Hv, h = bh - b * a.Hv;
+    const int hq = h / (a.Hv / a.Hqk), col0 = tile * CT;
+    const int tid = threadIdx.x, c4 = tid & 7, rg = tid >> 3;
+    f32x4 S[Sh::NRW];
+#pragma unroll
+    for (int j = 0; j < Sh::NRW; ++j)
+        S[j] = a.S0 ? load4f(a.S0 + ((size_t)bh * D + rg + 32 * j) * D + col0 + 4 * c4) : zero4();
+    const int NB = (a.T + BL - 1) / BL;
+    int slot = 0;
+    for (int m = 0; m < NB; ++m) {
+        float *ck = a.ws_ck + ((size_t)m * a.B * a.Hv + bh) * D * D;
+#pragma unroll
+        for (int j = 0; j < Sh::NRW; ++j) store4f(ck + (size_t)(rg + 32 * j) * D + col0 + 4 * c4, S[j]);
+        const int t0 = m * BL, n = min(BL, a.T - t0);
+        __syncthreads();  // the previous block's inputs are no longer read
+        bwd_stage<IO, D, false>(a, s, b, h, hq, col0, t0, n);
+        __syncthreads();
+        for (int tok = 0; tok < n; ++tok) {
+            (void)fwd_step<D>(S, s, tok, slot);
+            slot ^= 1;
+        }
+    }
+}
+
+template <typename IO, int D>
+__global__ __launch_bounds__(NTB) void bwd_kernel(BwdArgs a) {
+    using Sh = BwdShape<D>;
+    constexpr int NRW = Sh::NRW, TILES = Sh::TILES;
+    extern __shared__ __align__(16) unsigned char smem[];
+    BwdStage<D> &s = *reinterpret_cast<BwdStage<D> *>(smem);
+    // The states entering each token of the block, thread-private: [token][row j][thread].
+    f32x4 *Sx = reinterpret_cast<f32x4 *>(smem + sizeof(BwdStage<D>));
+    const int tile = blockIdx.x % TILES, bh = blockIdx.x / TILES, b = bh / a.Hv, h = bh - b * a.Hv;
+    const int hq = h / (a.Hv / a.Hqk), col0 = tile * CT;
+    const int tid = threadIdx.x, c4 = tid & 7, rg = tid >> 3;
+    const size_t TH = (size_t)a.B * a.T * a.Hv;
+    float *Pq = a.ws_part + (size_t)(0 * TILES + tile) * TH * D, *Pk = a.ws_part + (size_t)(1 * TILES + tile) * TH * D;
+    float *Pe = a.ws_part + (size_t)(2 * TILES + tile) * TH * D, *Pa = a.ws_part + (size_t)(3 * TILES + tile) * TH * D;
+    float *Pb = a.ws_part + (size_t)4 * TILES * TH * D + (size_t)tile * TH;
+
+    f32x4 dS[NRW];
+#pragma unroll
+    for (int j = 0; j < NRW; ++j)
+        dS[j] = a.dST ? load4f(a.dST + ((size_t)bh * D + rg + 32 * j) * D + col0 + 4 * c4) : zero4();
+    const int NB = (a.T + BL - 1) / BL;
+    int slot = 0;
+    for (int m = NB - 1; m >= 0; --m) {
+        const int t0 = m * BL, n = min(BL, a.T - t0);
+        const float *ck = a.ws_ck + ((size_t)m * a.B * a.Hv + bh) * D * D;
+        f32x4 S[NRW];
+#pragma unroll
+        for (int j = 0; j < NRW; ++j) S[j] = load4f(ck + (size_t)(rg + 32 * j) * D + col0 + 4 * c4);
+        __syncthreads();  // the previous block's inputs are no longer read
+        bwd_stage<IO, D, true>(a, s, b, h, hq, col0, t0, n);
+        __syncthreads();
+        // Replay: the state entering each token, and each token's u.
+        f32x4 u[BL];
+#pragma unroll
+        for (int tok = 0; tok < BL; ++tok) {
+            if (tok < n) {
+#pragma unroll
+                for (int j = 0; j < NRW; ++j) Sx[(tok * NRW + j) * NTB + tid] = S[j];
+                u[tok] = fwd_step<D>(S, s, tok, slot);
+                slot ^= 1;
+            }
+        }
+        // Reverse recurrence over the block.
+#pragma unroll
+        for (int tok = BL - 1; tok >= 0; --tok) {
+            if (tok < n) {
+                const size_t row = ((size_t)b * a.T + t0 + tok) * a.Hv + h;  // (b, t, h)
+                const f32x4 dO4 = load4f(&s.dO[tok][4 * c4]);
+                f32x4 Sp[NRW], Sb[NRW], pd = zero4();
+                float xq[NRW], xk[NRW];
+#pragma unroll
+                for (int j = 0; j < NRW; ++j) {
+                    const int r = rg + 32 * j;
+                    Sp[j] = Sx[(tok * NRW + j) * NTB + tid];
+                    Sb[j] = Sp[j] * s.al[tok][r];
+                    const float kk = s.k[tok][r];
+                    const f32x4 St = Sb[j] + kk * u[tok];
+                    dS[j] += (a.scale * s.q[tok][r]) * dO4;
+                    xq[j] = a.scale * dot4(St, dO4);
+                    xk[j] = dot4(dS[j], u[tok]);
+                    pd += dS[j] * kk;
+                }
+                const f32x4 du = colsum(pd, &s.red[slot][0][0]);
+                slot ^= 1;
+#pragma unroll
+                for (int j = 0; j < NRW; ++j) {
+                    const int r = rg + 32 * j;
+                    const float xe = -dot4(Sb[j], du);
+                    const f32x4 dSb = dS[j] - s.e[tok][r] * du;
+                    const float xa = dot4(dSb, Sp[j]);
+                    dS[j] = dSb * s.al[tok][r];
+                    const float q1 = rowsum8(xq[j]), k1 = rowsum8(xk[j]), e1 = rowsum8(xe), a1 = rowsum8(xa);
+                    if (c4 == 0) {
+                        Pq[row * D + r] = q1;
+                        Pk[row * D + r] = k1;
+                        Pe[row * D + r] = e1;
+                        Pa[row * D + r] = a1;
+                    }
+                }
+                // dz = du: the value-column gradients, from row group 0 (which holds du for its columns).
+                const f32x4 v4 = load4f(&s.v[tok][4 * c4]);
+                if (rg == 0) {
+                    float *dvp = a.dv + row * D + col0 + 4 * c4;
+                    store4f(dvp, load4f(&s.wv[tok][4 * c4]) * du);
+                    if (a.dw) store4f(a.dw + row * D + col0 + 4 * c4, v4 * du);
+                }
+                if (a.dbeta) {
+                    const float xb = rowsum8(rg == 0 ? dot4(v4, du) : 0.f);
+                    if (tid == 0) Pb[row] = xb;
+                }
+            }
+        }
+    }
+    if (a.dS0)
+#pragma unroll
+        for (int j = 0; j < NRW; ++j) store4f(a.dS0 + ((size_t)bh * D + rg + 32 * j) * D + col0 + 4 * c4, dS[j]);
+}
+
+// One workgroup per (sequence, token, QK head): sums the tiles' partials of
+// every V head of the group into dq and dk, and forms that token's gate
+// gradients.
+template <typename IO, int D>
+__global__ __launch_bounds__(128) void bwd_reduce_kernel(BwdArgs a) {
+    using E = Elem<IO>;
+    constexpr int TILES = BwdShape<D>::TILES;
+    __shared__ float red[2][2];
+    const int hq = blockIdx.x % a.Hqk;
+    const size_t bt = blockIdx.x / a.Hqk;  // b * T + t
+    const int i = threadIdx.x, lane = i & 63, wave = i >> 6, grp = a.Hv / a.Hqk;
+    const bool on = i < D;
+    const size_t TH = (size_t)a.B * a.T * a.Hv;
+    const size_t qi = (bt * a.Hqk + hq) * D + i;
+    const float kk = on ? E::load(static_cast<const IO *>(a.k) + qi) : 0.f;
+    float dq = 0.f, dk = 0.f;
+    for (int hh = 0; hh < grp; ++hh) {
+        const size_t row = bt * a.Hv + (size_t)hq * grp + hh;
+        float pq = 0.f, pk = 0.f, pe = 0.f, pa = 0.f;
+        if (on)
+#pragma unroll
+            for (int t = 0; t < TILES; ++t) {
+                pq += a.ws_part[((size_t)(0 * TILES + t) * TH + row) * D + i];
+                pk += a.ws_part[((size_t)(1 * TILES + t) * TH + row) * D + i];
+                pe += a.ws_part[((size_t)(2 * TILES + t) * TH + row) * D + i];
+                pa += a.ws_part[((size_t)(3 * TILES + t) * TH + row) * D + i];
+            }
+        const float ge = a.beta ? a.beta[row] : (on ? E::load(static_cast<const IO *>(a.bg) + row * D + i) : 0.f);
+        dq += pq;
+        dk += pk + ge * pe;
+        if (a.db && on) a.db[row * D + i] = kk * pe;
+        if (a.decay == DECAY_CHANNEL && on) a.dg[row * D + i] = expf(a.g[row * D + i]) * pa;
+        if (a.decay == DECAY_SCALAR || a.beta) {
+            float sa = pa, sb = kk * pe;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) {
+                sa += __shfl_xor(sa, off);
+                sb += __shfl_xor(sb, off);
+            }
+            if (lane == 0) {
+                red[0][wave] = sa;
+                red[1][wave] = sb;
+            }
+            __syncthreads();
+            if (i == 0) {
+                if (a.decay == DECAY_SCALAR) a.dg[row] = expf(a.g[row]) * (red[0][0] + red[0][1]);
+                if (a.beta) {
+                    float zb = 0.f;
+                    for (int t = 0; t < TILES; ++t) zb += a.ws_part[(size_t)4 * TILES * TH * D + (size_t)t * TH + row];
+                    a.dbeta[row] = red[1][0] + red[1][1] + zb;
+                }
+            }
+            __syncthreads();
+        }
+    }
+    if (on) {
+        a.dq[qi] = dq;
+        a.dk[qi] = dk;
+    }
+}
+
+template <typename IO, int D>
+hipError_t launch_backward_t(const BwdArgs &a, hipStream_t s) {
+    using Sh = BwdShape<D>;
+    constexpr size_t lds_ck = sizeof(BwdStage<D>);
+    constexpr size_t lds_bw = sizeof(BwdStage<D>) + (size_t)BL * Sh::NRW * NTB * sizeof(f32x4);
+    static_assert(lds_bw <= 160 * 1024, "shared memory");
+    static const hipError_t attr = [] {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&bwd_ckpt_kernel<IO, D>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_ck);
+        if (e != hipSuccess) return e;
+        return hipFuncSetAttribute(reinterpret_cast<const void *>(&bwd_kernel<IO, D>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bw);
+    }();
+    if (attr != hipSuccess) return attr;
+    const unsigned grid = (unsigned)a.B * (unsigned)a.Hv * Sh::TILES;
+    hipLaunchKernelGGL((bwd_ckpt_kernel<IO, D>), dim3(grid), dim3(NTB), lds_ck, s, a);
+    hipLaunchKernelGGL((bwd_kernel<IO, D>), dim3(grid), dim3(NTB), lds_bw, s, a);
+    hipLaunchKernelGGL((bwd_reduce_kernel<IO, D>), dim3((unsigned)((size_t)a.B * a.T * a.Hqk)), dim3(128), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_backward(int io, int D, const BwdArgs &a, hipStream_t s) {
+    if (io == IO_BF16) {
+        if (D == 32) return launch_backward_t<bf16_t, 32>(a, s);
+        if (D == 64) return launch_backward_t<bf16_t, 64>(a, s);
+        if (D == 128) return launch_backward_t<bf16_t, 128>(a, s);
+    } else {
+        if (D == 32) return launch_backward_t<float, 32>(a, s);
+        if (D == 64) return launch_backward_t<float, 64>(a, s);
+        if (D == 128) return launch_backward_t<float, 128>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdr

@@ -114,7 +114,47 @@ inline ChunkWsLayout chunk_ws_layout(int B, int Hqk, int Hv, int NC, int D, int 
     return L;
 }
 
+// Gradients of the recurrence (recurrent form). Work items are (sequence, V
+// head, tile of kBwdCols value columns); the state is checkpointed every
+// kBwdBlock tokens by a forward pass, and each block is replayed before it is
+// walked in reverse.
+constexpr int kBwdBlock = 8, kBwdCols = 32;
+struct BwdArgs {
+    const void *q, *k, *v;   // [B,T,Hqk,D], [B,T,Hqk,D], [B,T,Hv,D] (io dtype)
+    const float *g;          // [B,T,Hv] or [B,T,Hv,D] or null
+    const float *beta;       // [B,T,Hv] or null
+    const void *bg, *wg;     // [B,T,Hv,D] or null
+    const float *S0;         // [B,Hv,D,D] or null (zeros)
+    const void *dO;          // [B,T,Hv,D] (io dtype)
+    const float *dST;        // [B,Hv,D,D] or null (zeros)
+    float *dq, *dk;          // [B,T,Hqk,D]
+    float *dv;               // [B,T,Hv,D]
+    float *dg;               // shape of g, or null
+    float *dbeta;            // [B,T,Hv] (tied gates) or null
+    float *db, *dw;          // [B,T,Hv,D] (decoupled gates) or null
+    float *dS0;              // [B,Hv,D,D] or null (not written)
+    float *ws_ck;            // state entering every block of kBwdBlock tokens: [NB][B][Hv][D][D]
+    float *ws_part;          // per-tile partial sums over the tile's value columns, [B][T][Hv][D] each:
+                             // s S_t do, dS u, -Sbar du, rowsum(dSbar . S_{t-1}) for every tile; then
+                             // v . dz per tile, [B][T][Hv]
+    int B, T, Hqk, Hv, decay;
+    float scale;
+};
+struct BwdWsLayout {
+    size_t ck_bytes, part_bytes;
+    size_t total() const { return ck_bytes + part_bytes; }
+};
+inline BwdWsLayout bwd_ws_layout(int B, int T, int Hv, int D) {
+    const size_t NB = ((size_t)T + kBwdBlock - 1) / kBwdBlock, tiles = (size_t)D / kBwdCols;
+    const size_t th = (size_t)B * T * Hv;
+    BwdWsLayout L;
+    L.ck_bytes = align256(NB * B * Hv * D * D * sizeof(float));
+    L.part_bytes = align256((4 * tiles * th * D + tiles * th) * sizeof(float));
+    return L;
+}
+
 hipError_t launch_decode(int io, int D, const DecodeArgs &a, hipStream_t s);
+hipError_t launch_backward(int io, int D, const BwdArgs &a, hipStream_t s);
 hipError_t launch_chunk(int io, int D, const ChunkArgs &a, hipStream_t s);
 hipError_t launch_recurrent(int io, int D, const RecurArgs &a, hipStream_t s);
 hipError_t launch_state_fill(float *dst, const float *src, size_t n, hipStream_t s);

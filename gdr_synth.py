@@ -143,6 +143,17 @@ def make_inputs(wl: Workload, seed: int = 0) -> dict:
     return out
 
 
+def make_output_grads(wl: Workload, seed: int = 0, dST: bool = True) -> dict:
+    """Draw the incoming gradients of a backward pass for ``wl`` (prefill
+    layout): do = dL/do ~ N(0, 1) in the io dtype, [B, T, Hv, dv]; dST =
+    dL/dS_T ~ 0.1 N(0, 1) float32, [B, Hv, dk, dv] (None when dST is False).
+    Two streams of their own, seeded from ``seed``."""
+    s_do, s_st = (np.random.Generator(np.random.PCG64(s)) for s in np.random.SeedSequence([seed, 7]).spawn(2))
+    out = {"do": _store(s_do.standard_normal((wl.B, wl.T, wl.Hv, wl.dv)), wl.io)}
+    out["dST"] = _store(0.1 * s_st.standard_normal((wl.B, wl.Hv, wl.dk, wl.dv)), "f32") if dST else None
+    return out
+
+
 RAW_ORDER = ORDER + ("conv_w", "conv_in")
 
 

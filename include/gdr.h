@@ -216,6 +216,43 @@ int gdr_recurrent_fwd_in(const gdr_desc *desc, const gdr_input_stage *stage, con
                          const void *v, const float *g, const float *beta, const void *b, const void *w,
                          const float *S0, void *o, float *ST, void *stream);
 
+/* Gradients of the recurrence ("Resumo Técnico: Gated DeltaNet-2", section
+ * "Treinamento Paralelo Eficiente por Blocos", names a gate-aware backward
+ * pass; what is computed is the exact gradient of the forward recurrence of
+ * gdr_recurrent_fwd / gdr_chunk_fwd, walking the tokens in reverse):
+ *   dS    += s q_t dO_t^T,  dq_t = s S_t dO_t,  du_t = dS^T k_t
+ *   dk_t   = dS u_t + (beta_t or b_t) . de_t,   de_t = -Sbar_t du_t
+ *   dSbar  = dS - e_t du_t^T,  dg_t = alpha_t . rowsum(dSbar . S_{t-1})
+ *            (summed over d_k for a scalar decay),  dS = Diag(alpha_t) dSbar
+ *   tied gates: dbeta_t = k_t . de_t + v_t . du_t, dv_t = beta_t du_t
+ *   decoupled:  db_t = k_t . de_t, dw_t = v_t . du_t, dv_t = w_t . du_t
+ * with Sbar_t = Diag(alpha_t) S_{t-1}, u_t = z_t - Sbar_t^T e_t. Keys and
+ * queries shared by grouped V heads receive the sum over those heads.
+ *   Inputs: q, k, v, g, beta, b, w, S0 exactly as given to the forward call
+ *   (same desc; desc->chunk is ignored); dO [B,T,H_v,d_v] in the io dtype
+ *   (dL/do); dST [B,H_v,d_k,d_v] float32 (dL/dS_T) or NULL for zeros.
+ *   Outputs, all float32, in the layouts of the matching inputs: dq, dk
+ *   [B,T,H_qk,d_k] and dv [B,T,H_v,d_v] (required); dg (exactly when g is
+ *   given), dbeta (exactly when beta is), db and dw (exactly when b and w
+ *   are); dS0 [B,H_v,d_k,d_v] (dL/dS0) or NULL (not written).
+ *   Outputs must not overlap one another, the inputs or the workspace
+ *   (GDR_E_INVAL). Alignment as the forward calls; dg 16 bytes for a
+ *   per-channel decay, else 4; dbeta 4.
+ *   workspace: gdr_recurrent_bwd_workspace_bytes bytes, owned by the caller,
+ *   holding the state entering every block of 8 tokens
+ *   (ceil(T/8) * B * H_v * d_k * d_v floats) and per-column-tile partial
+ *   sums (about 16 * B * T * H_v * d_k bytes per 32 value columns).
+ *   Work: a forward pass that stores the checkpoints, a reverse pass that
+ *   replays each block of 8 tokens from its checkpoint before walking it
+ *   backwards, and a reduction over column tiles and grouped heads; vector
+ *   units only. T == 0 writes dST (or zeros) to dS0 and touches nothing
+ *   else. Supported: d_k == d_v in {32, 64, 128}, io float32 or bfloat16. */
+int gdr_recurrent_bwd_workspace_bytes(const gdr_desc *desc, size_t *bytes);
+int gdr_recurrent_bwd(const gdr_desc *desc, const void *q, const void *k, const void *v, const float *g,
+                      const float *beta, const void *b, const void *w, const float *S0, const void *dO,
+                      const float *dST, float *dq, float *dk, float *dv, float *dg, float *dbeta, float *db,
+                      float *dw, float *dS0, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char *gdr_last_error(void);
 

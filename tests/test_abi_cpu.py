@@ -192,6 +192,65 @@ def test_recurrent_accepts_what_the_chunked_path_does_not():
     assert gdr.gdr_last_error() == ""
 
 
+# Backward: distinct, non-overlapping fake buffers 4 GiB apart, so a case fails
+# only for the one thing it changes (validation never dereferences them).
+_BWD_NAMES = ("q", "k", "v", "g", "beta", "b", "w", "S0", "dO", "dST", "dq", "dk", "dv", "dg", "dbeta", "db",
+              "dw", "dS0", "ws")
+_BWD_BASE = {n: (i + 1) << 32 for i, n in enumerate(_BWD_NAMES)}
+
+
+def _bwd(desc, wsz=1 << 40, **kw):
+    ptr = dict(_BWD_BASE, b=None, w=None, db=None, dw=None)
+    ptr.update(kw)
+    return gdr.lib.gdr_recurrent_bwd(ctypes.byref(desc), *(ptr[n] for n in _BWD_NAMES), wsz, None)
+
+
+def test_backward_workspace_bytes():
+    """Checkpoints of the state entering every block of 8 tokens, then the
+    per-tile partial sums (four [B,T,H_v,D] arrays and one [B,T,H_v] per 32
+    value columns), each rounded up to 256 bytes."""
+    d = gdr.make_desc(1, 100, 2, 4, 128, gdr.GDR_BF16, gdr.GDR_DECAY_SCALAR)
+    ck = 13 * 4 * 128 * 128 * 4
+    part = (4 * 4 * 100 * 4 * 128 + 4 * 100 * 4) * 4
+    assert gdr.gdr_recurrent_bwd_workspace_bytes(d) == _a256(ck) + _a256(part)
+    assert gdr.gdr_recurrent_bwd_workspace_bytes(gdr.make_desc(1, 0, 2, 4, 128, gdr.GDR_BF16,
+                                                               gdr.GDR_DECAY_SCALAR)) == 0
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(desc=dict(D=96)), gdr.GDR_E_UNSUPPORTED),
+    (dict(desc=dict(Hv=5)), gdr.GDR_E_INVAL),
+    (dict(args=dict(dO=None)), gdr.GDR_E_INVAL),
+    (dict(args=dict(dq=None)), gdr.GDR_E_INVAL),
+    (dict(args=dict(dv=None)), gdr.GDR_E_INVAL),
+    (dict(args=dict(dg=None)), gdr.GDR_E_INVAL),                       # g given, dg missing
+    (dict(desc=dict(decay=gdr.GDR_DECAY_NONE), args=dict(g=None)), gdr.GDR_E_INVAL),  # dg without g
+    (dict(args=dict(dbeta=None)), gdr.GDR_E_INVAL),                    # beta given, dbeta missing
+    (dict(args=dict(db=_BWD_BASE["db"], dw=_BWD_BASE["dw"])), gdr.GDR_E_INVAL),      # db, dw with tied gates
+    (dict(args=dict(beta=None, dbeta=None, b=_BWD_BASE["b"], w=_BWD_BASE["w"],
+                    db=_BWD_BASE["db"], dw=None)), gdr.GDR_E_INVAL),   # decoupled gates, dw missing
+    (dict(args=dict(ws=None)), gdr.GDR_E_INVAL),
+    (dict(wsz=100), gdr.GDR_E_INVAL),
+    (dict(args=dict(dq=_BWD_BASE["q"])), gdr.GDR_E_INVAL),             # gradient over an input
+    (dict(args=dict(dk=_BWD_BASE["dq"] + 64)), gdr.GDR_E_INVAL),       # two gradients overlap
+    (dict(args=dict(dS0=_BWD_BASE["dST"])), gdr.GDR_E_INVAL),
+    (dict(args=dict(dv=_BWD_BASE["ws"] + 256)), gdr.GDR_E_INVAL),      # gradient inside the workspace
+    (dict(args=dict(dq=_BWD_BASE["dq"] + 4)), gdr.GDR_E_INVAL),        # 16-byte alignment
+    (dict(args=dict(dg=_BWD_BASE["dg"] + 2)), gdr.GDR_E_INVAL),
+    (dict(args=dict(dbeta=_BWD_BASE["dbeta"] + 1)), gdr.GDR_E_INVAL),
+    (dict(args=dict(dST=_BWD_BASE["dST"] + 8)), gdr.GDR_E_INVAL),
+])
+def test_backward_rejections(case, expect):
+    d = _desc(**case.get("desc", {}))
+    assert _bwd(d, wsz=case.get("wsz", 1 << 40), **case.get("args", {})) == expect
+    assert gdr.gdr_last_error() != ""
+
+
+def test_backward_zero_batch_is_a_noop_without_gpu():
+    assert _bwd(_desc(B=0)) == gdr.GDR_OK
+    assert gdr.gdr_last_error() == ""
+
+
 def test_state_alloc_rejects_bad_sizes():
     p, n = ctypes.c_void_p(), ctypes.c_size_t()
     assert gdr.lib.gdr_state_alloc(0, 48, 128, 128, ctypes.byref(p), ctypes.byref(n), None) == gdr.GDR_E_INVAL
