@@ -53,29 +53,37 @@ struct BwdShape {
 // One block of tokens' inputs, staged in shared memory.
 template <int D>
 struct BwdStage {
-    float q[BL][D], k[BL][D], e[BL][D], al[BL][D];  // key-axis vectors
+    f32x4 rv[BL][D];                                  // per token and key channel: (q, k, e, alpha)
     float z[BL][CT], dO[BL][CT], v[BL][CT], wv[BL][CT];  // this tile's value columns; wv = the write gate
     float red[2][4][CT];                              // per-wave column sums, two slots used in turn
+};
+
+// The same inputs in registers, loaded one block ahead of their use: the
+// key-axis entries x = tid + NTB i and the value-column entry x = tid.
+template <int D>
+struct BwdIn {
+    static constexpr int NE = BL * D / NTB;
+    static_assert(BL * CT == NTB, "one value-column entry per thread");
+    f32x4 rv[NE];
+    float z, dO, v, wv;
 };
 
 __device__ __forceinline__ float dot4(f32x4 a, f32x4 b) { return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3]; }
 
 // Sum over the 8 lanes of a row group (the tile's 32 value columns).
-__device__ __forceinline__ float rowsum8(float x) {
-    x += __shfl_xor(x, 1);
-    x += __shfl_xor(x, 2);
-    x += __shfl_xor(x, 4);
-    return x;
-}
+__device__ __forceinline__ float rowsum8(float x) { return lanes_allreduce<8>(x); }
 
 // Sum over the key axis for this thread's 4 columns: the 8 row groups of the
-// wave by shuffles, then the 4 waves through red (one __syncthreads). Every
-// thread gets the total.
+// wave (lanes 8 apart: a rotation by 8 within each 16-lane row, then lanes 16
+// and 32 apart by shuffles), then the 4 waves through red (one
+// __syncthreads). Every thread gets the total.
 __device__ __forceinline__ f32x4 colsum(f32x4 p, float *red) {
 #pragma unroll
-    for (int off = 8; off < 64; off <<= 1)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) p[c] += __shfl_xor(p[c], off);
+    for (int c = 0; c < 4; ++c) {
+        p[c] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(p[c]), 0x128, 0xF, 0xF, false));  // row_ror:8
+        p[c] += __shfl_xor(p[c], 16);
+        p[c] += __shfl_xor(p[c], 32);
+    }
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, c4 = lane & 7;
     if (lane < 8) store4f(red + wave * CT + 4 * c4, p);
     __syncthreads();
@@ -86,43 +94,51 @@ __device__ __forceinline__ f32x4 colsum(f32x4 p, float *red) {
 }
 
 template <typename IO, int D, bool BWD>
-__device__ __forceinline__ void bwd_stage(const BwdArgs &a, BwdStage<D> &s, int b, int h, int hq, int col0, int t0,
-                                          int n) {
+__device__ __forceinline__ void bwd_load(const BwdArgs &a, BwdIn<D> &in, int b, int h, int hq, int col0, int t0,
+                                         int n) {
     using E = Elem<IO>;
     const int tid = threadIdx.x;
-    for (int x = tid; x < BL * D; x += NTB) {
-        const int tok = x / D, i = x - tok * D;
-        float qq = 0.f, kk = 0.f, ee = 0.f, al = 1.f;
+#pragma unroll
+    for (int e = 0; e < BwdIn<D>::NE; ++e) {
+        const int x = tid + NTB * e, tok = x / D, i = x - tok * D;
+        f32x4 r = f32x4{0.f, 0.f, 0.f, 1.f};
         if (tok < n) {
             const size_t t = (size_t)b * a.T + t0 + tok;
             const size_t qi = (t * a.Hqk + hq) * D + i, vi = (t * a.Hv + h) * D + i;
-            kk = E::load(static_cast<const IO *>(a.k) + qi);
-            if (BWD) qq = E::load(static_cast<const IO *>(a.q) + qi);
-            ee = (a.beta ? a.beta[t * a.Hv + h] : E::load(static_cast<const IO *>(a.bg) + vi)) * kk;
-            if (a.decay == DECAY_SCALAR) al = expf(a.g[t * a.Hv + h]);
-            else if (a.decay == DECAY_CHANNEL) al = expf(a.g[vi]);
+            const float kk = E::load(static_cast<const IO *>(a.k) + qi);
+            r[0] = BWD ? E::load(static_cast<const IO *>(a.q) + qi) : 0.f;
+            r[1] = kk;
+            r[2] = (a.beta ? a.beta[t * a.Hv + h] : E::load(static_cast<const IO *>(a.bg) + vi)) * kk;
+            if (a.decay == DECAY_SCALAR) r[3] = expf(a.g[t * a.Hv + h]);
+            else if (a.decay == DECAY_CHANNEL) r[3] = expf(a.g[vi]);
         }
-        s.q[tok][i] = qq;
-        s.k[tok][i] = kk;
-        s.e[tok][i] = ee;
-        s.al[tok][i] = al;
+        in.rv[e] = r;
     }
-    for (int x = tid; x < BL * CT; x += NTB) {
-        const int tok = x / CT, c = x - tok * CT;
-        float zz = 0.f, dd = 0.f, vv = 0.f, ww = 0.f;
-        if (tok < n) {
-            const size_t t = (size_t)b * a.T + t0 + tok;
-            const size_t vi = (t * a.Hv + h) * D + col0 + c;
-            vv = E::load(static_cast<const IO *>(a.v) + vi);
-            ww = a.beta ? a.beta[t * a.Hv + h] : E::load(static_cast<const IO *>(a.wg) + vi);
-            zz = ww * vv;
-            if (BWD) dd = E::load(static_cast<const IO *>(a.dO) + vi);
-        }
-        s.z[tok][c] = zz;
-        s.dO[tok][c] = dd;
-        s.v[tok][c] = vv;
-        s.wv[tok][c] = ww;
+    const int tok = tid / CT, c = tid - tok * CT;
+    in.z = in.dO = in.v = in.wv = 0.f;
+    if (tok < n) {
+        const size_t t = (size_t)b * a.T + t0 + tok;
+        const size_t vi = (t * a.Hv + h) * D + col0 + c;
+        in.v = E::load(static_cast<const IO *>(a.v) + vi);
+        in.wv = a.beta ? a.beta[t * a.Hv + h] : E::load(static_cast<const IO *>(a.wg) + vi);
+        in.z = in.wv * in.v;
+        if (BWD) in.dO = E::load(static_cast<const IO *>(a.dO) + vi);
     }
+}
+
+template <int D>
+__device__ __forceinline__ void bwd_put(const BwdIn<D> &in, BwdStage<D> &s) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int e = 0; e < BwdIn<D>::NE; ++e) {
+        const int x = tid + NTB * e;
+        s.rv[x / D][x % D] = in.rv[e];
+    }
+    const int tok = tid / CT, c = tid - tok * CT;
+    s.z[tok][c] = in.z;
+    s.dO[tok][c] = in.dO;
+    s.v[tok][c] = in.v;
+    s.wv[tok][c] = in.wv;
 }
 
 // One forward step of this thread's part of the state: S <- Sbar + k u^T,
@@ -130,17 +146,17 @@ __device__ __forceinline__ void bwd_stage(const BwdArgs &a, BwdStage<D> &s, int 
 template <int D>
 __device__ __forceinline__ f32x4 fwd_step(f32x4 (&S)[BwdShape<D>::NRW], BwdStage<D> &s, int tok, int slot) {
     const int tid = threadIdx.x, c4 = tid & 7, rg = tid >> 3;
-    f32x4 pr = zero4();
+    f32x4 pr = zero4(), rv[BwdShape<D>::NRW];
 #pragma unroll
     for (int j = 0; j < BwdShape<D>::NRW; ++j) {
-        const int r = rg + 32 * j;
-        S[j] *= s.al[tok][r];
-        pr += S[j] * s.e[tok][r];
+        rv[j] = s.rv[tok][rg + 32 * j];
+        S[j] *= rv[j][3];
+        pr += S[j] * rv[j][2];
     }
     const f32x4 rr = colsum(pr, &s.red[slot][0][0]);
     const f32x4 u = load4f(&s.z[tok][4 * c4]) - rr;
 #pragma unroll
-    for (int j = 0; j < BwdShape<D>::NRW; ++j) S[j] += s.k[tok][rg + 32 * j] * u;
+    for (int j = 0; j < BwdShape<D>::NRW; ++j) S[j] += rv[j][1] * u;
     return u;
 }
 
@@ -158,14 +174,17 @@ __global__ __launch_bounds__(NTB) void bwd_ckpt_kernel(BwdArgs a) {
         S[j] = a.S0 ? load4f(a.S0 + ((size_t)bh * D + rg + 32 * j) * D + col0 + 4 * c4) : zero4();
     const int NB = (a.T + BL - 1) / BL;
     int slot = 0;
+    BwdIn<D> in;
+    bwd_load<IO, D, false>(a, in, b, h, hq, col0, 0, min(BL, a.T));
     for (int m = 0; m < NB; ++m) {
         float *ck = a.ws_ck + ((size_t)m * a.B * a.Hv + bh) * D * D;
 #pragma unroll
         for (int j = 0; j < Sh::NRW; ++j) store4f(ck + (size_t)(rg + 32 * j) * D + col0 + 4 * c4, S[j]);
         const int t0 = m * BL, n = min(BL, a.T - t0);
         __syncthreads();  // the previous block's inputs are no longer read
-        bwd_stage<IO, D, false>(a, s, b, h, hq, col0, t0, n);
+        bwd_put<D>(in, s);
         __syncthreads();
+        if (m + 1 < NB) bwd_load<IO, D, false>(a, in, b, h, hq, col0, t0 + BL, min(BL, a.T - t0 - BL));
         for (int tok = 0; tok < n; ++tok) {
             (void)fwd_step<D>(S, s, tok, slot);
             slot ^= 1;
@@ -195,15 +214,26 @@ __global__ __launch_bounds__(NTB) void bwd_kernel(BwdArgs a) {
         dS[j] = a.dST ? load4f(a.dST + ((size_t)bh * D + rg + 32 * j) * D + col0 + 4 * c4) : zero4();
     const int NB = (a.T + BL - 1) / BL;
     int slot = 0;
+    // Block m's inputs and checkpoint are loaded while block m + 1 is processed.
+    const auto ckpt = [&](int m) { return a.ws_ck + ((size_t)m * a.B * a.Hv + bh) * D * D; };
+    BwdIn<D> in;
+    f32x4 Sn[NRW];
+    bwd_load<IO, D, true>(a, in, b, h, hq, col0, (NB - 1) * BL, a.T - (NB - 1) * BL);
+#pragma unroll
+    for (int j = 0; j < NRW; ++j) Sn[j] = load4f(ckpt(NB - 1) + (size_t)(rg + 32 * j) * D + col0 + 4 * c4);
     for (int m = NB - 1; m >= 0; --m) {
         const int t0 = m * BL, n = min(BL, a.T - t0);
-        const float *ck = a.ws_ck + ((size_t)m * a.B * a.Hv + bh) * D * D;
         f32x4 S[NRW];
 #pragma unroll
-        for (int j = 0; j < NRW; ++j) S[j] = load4f(ck + (size_t)(rg + 32 * j) * D + col0 + 4 * c4);
+        for (int j = 0; j < NRW; ++j) S[j] = Sn[j];
         __syncthreads();  // the previous block's inputs are no longer read
-        bwd_stage<IO, D, true>(a, s, b, h, hq, col0, t0, n);
+        bwd_put<D>(in, s);
         __syncthreads();
+        if (m > 0) {
+            bwd_load<IO, D, true>(a, in, b, h, hq, col0, t0 - BL, BL);
+#pragma unroll
+            for (int j = 0; j < NRW; ++j) Sn[j] = load4f(ckpt(m - 1) + (size_t)(rg + 32 * j) * D + col0 + 4 * c4);
+        }
         // Replay: the state entering each token, and each token's u.
         f32x4 u[BL];
 #pragma unroll
@@ -223,17 +253,17 @@ __global__ __launch_bounds__(NTB) void bwd_kernel(BwdArgs a) {
                 const f32x4 dO4 = load4f(&s.dO[tok][4 * c4]);
                 f32x4 Sp[NRW], Sb[NRW], pd = zero4();
                 float xq[NRW], xk[NRW];
+                f32x4 rv[NRW];
 #pragma unroll
                 for (int j = 0; j < NRW; ++j) {
-                    const int r = rg + 32 * j;
+                    rv[j] = s.rv[tok][rg + 32 * j];  // (q, k, e, alpha)
                     Sp[j] = Sx[(tok * NRW + j) * NTB + tid];
-                    Sb[j] = Sp[j] * s.al[tok][r];
-                    const float kk = s.k[tok][r];
-                    const f32x4 St = Sb[j] + kk * u[tok];
-                    dS[j] += (a.scale * s.q[tok][r]) * dO4;
+                    Sb[j] = Sp[j] * rv[j][3];
+                    const f32x4 St = Sb[j] + rv[j][1] * u[tok];
+                    dS[j] += (a.scale * rv[j][0]) * dO4;
                     xq[j] = a.scale * dot4(St, dO4);
                     xk[j] = dot4(dS[j], u[tok]);
-                    pd += dS[j] * kk;
+                    pd += dS[j] * rv[j][1];
                 }
                 const f32x4 du = colsum(pd, &s.red[slot][0][0]);
                 slot ^= 1;
@@ -241,9 +271,9 @@ __global__ __launch_bounds__(NTB) void bwd_kernel(BwdArgs a) {
                 for (int j = 0; j < NRW; ++j) {
                     const int r = rg + 32 * j;
                     const float xe = -dot4(Sb[j], du);
-                    const f32x4 dSb = dS[j] - s.e[tok][r] * du;
+                    const f32x4 dSb = dS[j] - rv[j][2] * du;
                     const float xa = dot4(dSb, Sp[j]);
-                    dS[j] = dSb * s.al[tok][r];
+                    dS[j] = dSb * rv[j][3];
                     const float q1 = rowsum8(xq[j]), k1 = rowsum8(xk[j]), e1 = rowsum8(xe), a1 = rowsum8(xa);
                     if (c4 == 0) {
                         Pq[row * D + r] = q1;
