@@ -118,7 +118,7 @@ inline ChunkWsLayout chunk_ws_layout(int B, int Hqk, int Hv, int NC, int D, int 
 // head, tile of kBwdCols value columns); the state is checkpointed every
 // kBwdBlock tokens by a forward pass, and each block is replayed before it is
 // walked in reverse.
-constexpr int kBwdBlock = 8, kBwdCols = 32;
+constexpr int kBwdBlock = 4, kBwdCols = 32;
 struct BwdArgs {
     const void *q, *k, *v;   // [B,T,Hqk,D], [B,T,Hqk,D], [B,T,Hv,D] (io dtype)
     const float *g;          // [B,T,Hv] or [B,T,Hv,D] or null

@@ -239,11 +239,11 @@ int gdr_recurrent_fwd_in(const gdr_desc *desc, const gdr_input_stage *stage, con
  *   (GDR_E_INVAL). Alignment as the forward calls; dg 16 bytes for a
  *   per-channel decay, else 4; dbeta 4.
  *   workspace: gdr_recurrent_bwd_workspace_bytes bytes, owned by the caller,
- *   holding the state entering every block of 8 tokens
- *   (ceil(T/8) * B * H_v * d_k * d_v floats) and per-column-tile partial
+ *   holding the state entering every block of 4 tokens
+ *   (ceil(T/4) * B * H_v * d_k * d_v floats) and per-column-tile partial
  *   sums (about 16 * B * T * H_v * d_k bytes per 32 value columns).
  *   Work: a forward pass that stores the checkpoints, a reverse pass that
- *   replays each block of 8 tokens from its checkpoint before walking it
+ *   replays each block of 4 tokens from its checkpoint before walking it
  *   backwards, and a reduction over column tiles and grouped heads; vector
  *   units only. T == 0 writes dST (or zeros) to dS0 and touches nothing
  *   else. Supported: d_k == d_v in {32, 64, 128}, io float32 or bfloat16. */

@@ -206,11 +206,11 @@ def _bwd(desc, wsz=1 << 40, **kw):
 
 
 def test_backward_workspace_bytes():
-    """Checkpoints of the state entering every block of 8 tokens, then the
+    """Checkpoints of the state entering every block of 4 tokens, then the
     per-tile partial sums (four [B,T,H_v,D] arrays and one [B,T,H_v] per 32
     value columns), each rounded up to 256 bytes."""
     d = gdr.make_desc(1, 100, 2, 4, 128, gdr.GDR_BF16, gdr.GDR_DECAY_SCALAR)
-    ck = 13 * 4 * 128 * 128 * 4
+    ck = 25 * 4 * 128 * 128 * 4
     part = (4 * 4 * 100 * 4 * 128 + 4 * 100 * 4) * 4
     assert gdr.gdr_recurrent_bwd_workspace_bytes(d) == _a256(ck) + _a256(part)
     assert gdr.gdr_recurrent_bwd_workspace_bytes(gdr.make_desc(1, 0, 2, 4, 128, gdr.GDR_BF16,
