@@ -274,8 +274,10 @@ struct PrepIn {
     // The loads are issued in three parts (PART 0: q, k; 1: v, per-channel g;
     // 2: b, w, beta, scalar g) at different points of the previous unit, so
     // the memory queue drains behind computation instead of stalling a burst.
+    // qk false: q and k are already in registers (the same QK head's chunk),
+    // so the convolution window of neither is fetched.
     template <int PART>
-    __device__ __forceinline__ void load(const ChunkArgs &a, int u, int co, int grp) {
+    __device__ __forceinline__ void load(const ChunkArgs &a, int u, int co, int grp, bool qk = true) {
         const int NC = a.NC, c = u % NC, bh = u / NC, b = bh / a.Hv, h = bh - b * a.Hv;
         const int hq = h / (a.Hv / a.Hqk), t0 = c * C, n = min(C, a.T - t0);
         const int l = threadIdx.x & 63;
@@ -309,10 +311,12 @@ struct PrepIn {
                                                     : nullptr;
                 const uint4 zero = uint4{0u, 0u, 0u, 0u};
                 const size_t cq = (size_t)hq * D + V * co;
-                halo_q = th >= 0 ? ld16(static_cast<const IO *>(a.q) + qko + (ptrdiff_t)(th - t0) * (ptrdiff_t)sqk)
-                                 : cin ? ld16(cin + cq) : zero;
-                halo_k = th >= 0 ? ld16(static_cast<const IO *>(a.k) + qko + (ptrdiff_t)(th - t0) * (ptrdiff_t)sqk)
-                                 : cin ? ld16(cin + sqk + cq) : zero;
+                if (qk) {
+                    halo_q = th >= 0 ? ld16(static_cast<const IO *>(a.q) + qko + (ptrdiff_t)(th - t0) * (ptrdiff_t)sqk)
+                                     : cin ? ld16(cin + cq) : zero;
+                    halo_k = th >= 0 ? ld16(static_cast<const IO *>(a.k) + qko + (ptrdiff_t)(th - t0) * (ptrdiff_t)sqk)
+                                     : cin ? ld16(cin + sqk + cq) : zero;
+                }
                 halo_v = th >= 0 ? ld16(static_cast<const IO *>(a.v) + vo + (ptrdiff_t)(th - t0) * (ptrdiff_t)sv)
                                  : cin ? ld16(cin + 2 * sqk + (size_t)h * D + V * co) : zero;
             }
@@ -370,13 +374,33 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, lr = l & 15,
               lg = l >> 4;
     const int co = tid % CO, grp = tid / CO;
-    const int units = a.B * a.Hv * a.NC;
+    // With the input stage, a scalar decay and tied gates, a work item is a
+    // (sequence, chunk) and PG consecutive V heads of one QK head, run one
+    // after another: q and k are loaded, convolved and normalised once and
+    // stay in registers for the later heads. Otherwise a work item is one
+    // unit: without the input stage the shared q and k would only save
+    // loads, and the register-bound per-channel and decoupled-gate variants
+    // measured slower with the grouped loop.
+    constexpr bool GROUPED = RAW && !CHAN && !BW;
+    const int grpsz = a.Hv / a.Hqk, PG = GROUPED ? a.prep_grp : 1, HG = a.Hv / PG, gunits = a.B * HG * a.NC;
+    const auto unit_of = [&](int gu, int hh) {
+        if constexpr (!GROUPED) return gu;
+        const int c = gu % a.NC, bq = gu / a.NC, b = bq / HG, hg = bq - b * HG;
+        return (b * a.Hv + hg * PG + hh) * a.NC + c;
+    };
 
     PrepIn<IO, D, CHAN, BW, RAW> in;
-    if ((int)blockIdx.x < units) in.load_all(a, blockIdx.x, co, grp);
+    if ((int)blockIdx.x < gunits) in.load_all(a, unit_of(blockIdx.x, 0), co, grp);
 
-    for (int u = blockIdx.x; u < units; u += gridDim.x) {
-        const int NC = a.NC, c = u % NC, bh = u / NC, h = bh % a.Hv, grpsz = a.Hv / a.Hqk;
+    for (int gu = blockIdx.x, hh = 0; gu < gunits;) {
+        const int u = unit_of(gu, hh);
+        const bool first = !GROUPED || hh == 0;  // q and k are not yet formed for this work item
+        // The next unit: the item's next V head, else the next item's first.
+        const int gun = gu + (int)gridDim.x;
+        const bool next_same = GROUPED && hh + 1 < PG;
+        const bool has_next = next_same || gun < gunits;
+        const int un = next_same ? unit_of(gu, hh + 1) : unit_of(gun, 0);
+        const int NC = a.NC, c = u % NC, bh = u / NC, h = bh % a.Hv;
         const int n = min(C, a.T - c * C);
         IO *ws = static_cast<IO *>(a.ws_io) + (size_t)u * chunk_ws_io_elems(D, CHAN);
         IO *wY = ws, *wQ = ws + C * D, *wUzT = ws + ws_off_uz(D, CHAN), *wA = ws + ws_off_a(D, CHAN);
@@ -403,8 +427,9 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
             const size_t cb[3] = {cq, sqk + cq, 2 * sqk + (size_t)h * D + V * co};
 #pragma unroll
             for (int x = 0; x < 3; ++x)
+                if (x == 2 || first)
 #pragma unroll
-                for (int c4 = 0; c4 < V; ++c4) taps[x * V + c4] = load4f(a.conv_w + (cb[x] + c4) * 4);
+                    for (int c4 = 0; c4 < V; ++c4) taps[x * V + c4] = load4f(a.conv_w + (cb[x] + c4) * 4);
         }
         float G[CHAN ? TPT : 1][V];
         if constexpr (CHAN) {
@@ -448,13 +473,17 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
 #pragma unroll
             for (int j = 0; j < TPT; ++j) {
                 const int o = (TPT * grp + j) * PD + V * co;
-                *reinterpret_cast<uint4 *>(tQ + o) = in.q[j];
-                *reinterpret_cast<uint4 *>(tK + o) = in.k[j];
+                if (first) {
+                    *reinterpret_cast<uint4 *>(tQ + o) = in.q[j];
+                    *reinterpret_cast<uint4 *>(tK + o) = in.k[j];
+                }
                 *reinterpret_cast<uint4 *>(tZ + o) = in.v[j];
             }
             if (grp < 3) {
-                *reinterpret_cast<uint4 *>(sHalo + (3 * grp + 0) * D + V * co) = in.halo_q;
-                *reinterpret_cast<uint4 *>(sHalo + (3 * grp + 1) * D + V * co) = in.halo_k;
+                if (first) {
+                    *reinterpret_cast<uint4 *>(sHalo + (3 * grp + 0) * D + V * co) = in.halo_q;
+                    *reinterpret_cast<uint4 *>(sHalo + (3 * grp + 1) * D + V * co) = in.halo_k;
+                }
                 *reinterpret_cast<uint4 *>(sHalo + (3 * grp + 2) * D + V * co) = in.halo_v;
             }
         }
@@ -515,8 +544,10 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
                     x[j] = R::pack(out[j]);
                 }
             };
-            stage(in.q, 0, cq, true);
-            stage(in.k, 1, ck, true);
+            if (first) {
+                stage(in.q, 0, cq, true);
+                stage(in.k, 1, ck, true);
+            }
             stage(in.v, 2, cv, false);
             __syncthreads();  // every window read before the tiles are overwritten
         }
@@ -599,8 +630,7 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
                 for (int i = 0; i < V / 4; ++i)
                     store4f(tab + V * co + 4 * i, f32x4{eGend[4 * i], eGend[4 * i + 1], eGend[4 * i + 2], eGend[4 * i + 3]});
         // The raw inputs are consumed: start fetching the next unit's.
-        const int un = u + (int)gridDim.x;
-        if (un < units) in.template load<0>(a, un, co, grp);
+        if (has_next && !next_same) in.template load<0>(a, un, co, grp);
         __syncthreads();
 
         // ---- B. Gram products: 20 lower 16 x 16 tiles, 10 of T and 10 of A ----
@@ -672,7 +702,7 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
         }
         __syncthreads();
 
-        if (un < units) in.template load<1>(a, un, co, grp);
+        if (has_next) in.template load<1>(a, un, co, grp);
 
         // ---- C. A to the workspace; L = (I + T)^-1 ----
         for (int f = w; f < (C / 16) * (C / KS); f += NW) {
@@ -721,7 +751,7 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
         }
         __syncthreads();
 
-        if (un < units) in.template load<2>(a, un, co, grp);
+        if (has_next) in.template load<2>(a, un, co, grp, !next_same);
 
         // ---- D. [Y | U_z] = L [E~ | Z] ----
         {
@@ -761,6 +791,10 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
         for (int f = w; f < (C / 16) * (D / KS); f += NW) {
             const int rt = f / (D / KS), ks = f - rt * (D / KS);
             store_frag<IO>(wY, rt, ks, D, K::frag(sYc + ks * KS * LY + rt * 16, LY));
+        }
+        if (!GROUPED || ++hh == PG) {
+            hh = 0;
+            gu += (int)gridDim.x;
         }
     }
 }
@@ -1266,18 +1300,33 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t s) {
         const int occ = !chan && !bw && 2 * Cfg::bytes(false, false) <= (size_t)160 * 1024
                             ? prep_occupancy<IO, D, false, false>() : 1;
         const long long slots = (long long)occ * device_cus();
-        const long long grid = units < slots ? units : slots;
+        // V heads per work item: a divisor of the group size, the one with
+        // the shortest schedule counted in units (rounds of work items times
+        // heads per item), the largest of those that tie.
+        // (Grouped variant only; 1 otherwise.)
+        const int grpsz = a.conv_w && !chan && !bw ? a.Hv / a.Hqk : 1;
+        int pg = 1;
+        long long best = -1;
+        for (int d = 1; d <= grpsz; ++d) {
+            if (grpsz % d) continue;
+            const long long span = (units / d + slots - 1) / slots * d;
+            if (best < 0 || span <= best) { best = span; pg = d; }
+        }
+        ChunkArgs ap = a;
+        ap.prep_grp = pg;
+        const long long items = units / pg;
+        const long long grid = items < slots ? items : slots;
         const dim3 g((unsigned)grid), b(Cfg::NT);
         if (a.conv_w) {
-            if (chan && bw) hipLaunchKernelGGL((chunk_prep<IO, D, true, true, true>), g, b, Cfg::bytes(true, true), s, a);
-            else if (chan) hipLaunchKernelGGL((chunk_prep<IO, D, true, false, true>), g, b, Cfg::bytes(true, true), s, a);
-            else if (bw) hipLaunchKernelGGL((chunk_prep<IO, D, false, true, true>), g, b, Cfg::bytes(true, false), s, a);
-            else hipLaunchKernelGGL((chunk_prep<IO, D, false, false, true>), g, b, Cfg::bytes(false, false), s, a);
+            if (chan && bw) hipLaunchKernelGGL((chunk_prep<IO, D, true, true, true>), g, b, Cfg::bytes(true, true), s, ap);
+            else if (chan) hipLaunchKernelGGL((chunk_prep<IO, D, true, false, true>), g, b, Cfg::bytes(true, true), s, ap);
+            else if (bw) hipLaunchKernelGGL((chunk_prep<IO, D, false, true, true>), g, b, Cfg::bytes(true, false), s, ap);
+            else hipLaunchKernelGGL((chunk_prep<IO, D, false, false, true>), g, b, Cfg::bytes(false, false), s, ap);
         } else {
-            if (chan && bw) hipLaunchKernelGGL((chunk_prep<IO, D, true, true, false>), g, b, Cfg::bytes(true, true), s, a);
-            else if (chan) hipLaunchKernelGGL((chunk_prep<IO, D, true, false, false>), g, b, Cfg::bytes(true, true), s, a);
-            else if (bw) hipLaunchKernelGGL((chunk_prep<IO, D, false, true, false>), g, b, Cfg::bytes(true, false), s, a);
-            else hipLaunchKernelGGL((chunk_prep<IO, D, false, false, false>), g, b, Cfg::bytes(false, false), s, a);
+            if (chan && bw) hipLaunchKernelGGL((chunk_prep<IO, D, true, true, false>), g, b, Cfg::bytes(true, true), s, ap);
+            else if (chan) hipLaunchKernelGGL((chunk_prep<IO, D, true, false, false>), g, b, Cfg::bytes(true, true), s, ap);
+            else if (bw) hipLaunchKernelGGL((chunk_prep<IO, D, false, true, false>), g, b, Cfg::bytes(true, false), s, ap);
+            else hipLaunchKernelGGL((chunk_prep<IO, D, false, false, false>), g, b, Cfg::bytes(false, false), s, ap);
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

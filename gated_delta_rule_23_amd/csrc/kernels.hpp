@@ -67,6 +67,9 @@ struct ChunkArgs {
     const void *conv_in;
     void *conv_out;
     const float *decay_scale;
+    // chunk_prep: V heads of one QK head that a work item runs back to back
+    // (divides Hv / Hqk; chosen by the launcher, 0 from callers).
+    int prep_grp;
 };
 
 constexpr int kTab = 2 * kChunk;  // floats per chunk unit in ws_tab (>= D for every supported D)

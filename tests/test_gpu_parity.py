@@ -591,6 +591,23 @@ def test_prefill_input_stage_qwen_full_size_sampled():
     assert _conv_equal(cout, c_ref)
 
 
+def test_prefill_input_stage_wide_groups_sampled():
+    """Four V heads per QK head and enough chunks that the load stage runs
+    several V heads of a QK head back to back in one workgroup (the later
+    ones reusing the first one's convolved and normalised q and k): sampled
+    heads at every position in a group against the oracle."""
+    wl = small_workload("bf16", 128, "scalar", "beta", T=4096, B=4, Hqk=2, Hv=8, S0=True, scale=128 ** -0.5)
+    raw = gs.make_raw_inputs(wl, seed=51)
+    say(f"prefill input stage {wl.name}")
+    o, ST, cout = gpu_prefill_in(raw, S0=to_dev(raw["S0"]))
+    torch.cuda.synchronize()
+    heads = [0, 1, 6, 7]
+    o_ref, S_ref, c_ref = oracle_input_stage(raw, heads=heads)
+    assert rel_err(from_dev(o[:, :, heads]), o_ref[:, :, heads]) < TOL["bf16"]
+    assert rel_err(from_dev(ST[:, heads]), S_ref[:, heads]) < TOL["bf16"]
+    assert _conv_equal(cout, c_ref)
+
+
 def test_prefill_input_stage_split_and_serving_handoff():
     """A prefill in two calls, the second taking the first's convolution state
     and final state, equals one call; decode steps from there (T = 1 calls of
