@@ -30,7 +30,8 @@ CHUNK = 64
 # Every symbol include/gdr.h declares.
 EXPORTS = ("gdr_state_bytes", "gdr_state_alloc", "gdr_state_free", "gdr_chunk_workspace_bytes",
            "gdr_chunk_fwd", "gdr_decode_step", "gdr_recurrent_fwd", "gdr_recurrent_fwd_in", "gdr_chunk_fwd_in",
-           "gdr_recurrent_bwd_workspace_bytes", "gdr_recurrent_bwd", "gdr_last_error", "gdr_version")
+           "gdr_recurrent_bwd_workspace_bytes", "gdr_recurrent_bwd", "gdr_chunk_bwd_workspace_bytes", "gdr_chunk_bwd",
+           "gdr_last_error", "gdr_version")
 
 
 class GdrError(RuntimeError):
@@ -86,6 +87,10 @@ def _load():
     lib.gdr_recurrent_bwd_workspace_bytes.argtypes = [D, ctypes.POINTER(S)]
     lib.gdr_recurrent_bwd.restype = I
     lib.gdr_recurrent_bwd.argtypes = [D] + [P] * 19 + [S, P]
+    lib.gdr_chunk_bwd_workspace_bytes.restype = I
+    lib.gdr_chunk_bwd_workspace_bytes.argtypes = [D, ctypes.POINTER(S)]
+    lib.gdr_chunk_bwd.restype = I
+    lib.gdr_chunk_bwd.argtypes = [D] + [P] * 19 + [S, P]
     lib.gdr_last_error.restype = ctypes.c_char_p
     lib.gdr_last_error.argtypes = []
     lib.gdr_version.restype = I
@@ -352,12 +357,29 @@ def gdr_recurrent_bwd_workspace_bytes(desc: gdr_desc) -> int:
     return n.value
 
 
+def gdr_chunk_bwd_workspace_bytes(desc: gdr_desc) -> int:
+    n = ctypes.c_size_t()
+    _check(lib.gdr_chunk_bwd_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
 def gdr_recurrent_bwd(q, k, v, do, *, g=None, beta=None, b=None, w=None, S0=None, dST=None, scale=1.0,
                       want_dS0=True, workspace=None, stream=None):
     """Gradients of the recurrence for dL/do = do [B,T,Hv,D] (io dtype) and
     dL/dS_T = dST ([B,Hv,D,D] float32, or None for zeros). Inputs as given to
     the forward call. Returns a dict of float32 tensors: dq, dk, dv, and dg,
     dbeta, db, dw, dS0 where they apply (dS0 only when want_dS0)."""
+    return _bwd(False, q, k, v, do, g, beta, b, w, S0, dST, scale, want_dS0, workspace, stream)
+
+
+def gdr_chunk_bwd(q, k, v, do, *, g=None, beta=None, b=None, w=None, S0=None, dST=None, scale=1.0,
+                  want_dS0=True, workspace=None, stream=None):
+    """gdr_recurrent_bwd's gradients in chunked form (parallel over chunks of
+    64 tokens); same arguments and result."""
+    return _bwd(True, q, k, v, do, g, beta, b, w, S0, dST, scale, want_dS0, workspace, stream)
+
+
+def _bwd(chunked, q, k, v, do, g, beta, b, w, S0, dST, scale, want_dS0, workspace, stream):
     torch = _torch()
     B, T, Hqk, D = q.shape
     Hv = v.shape[2]
@@ -382,12 +404,13 @@ def gdr_recurrent_bwd(q, k, v, do, *, g=None, beta=None, b=None, w=None, S0=None
         out["dw"] = torch.empty((B, T, Hv, D), **f32)
     if want_dS0:
         out["dS0"] = torch.empty((B, Hv, D, D), **f32)
-    nbytes = gdr_recurrent_bwd_workspace_bytes(desc)
+    nbytes = (gdr_chunk_bwd_workspace_bytes if chunked else gdr_recurrent_bwd_workspace_bytes)(desc)
     if workspace is None and nbytes > 0:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib.gdr_recurrent_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(b),
-                                 _ptr(w), _ptr(S0), _ptr(do), _ptr(dST), _ptr(out["dq"]), _ptr(out["dk"]),
-                                 _ptr(out["dv"]), _ptr(out.get("dg")), _ptr(out.get("dbeta")), _ptr(out.get("db")),
-                                 _ptr(out.get("dw")), _ptr(out.get("dS0")), _ptr(workspace), wsz, _stream(stream)))
+    fn = lib.gdr_chunk_bwd if chunked else lib.gdr_recurrent_bwd
+    _check(fn(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(b), _ptr(w), _ptr(S0),
+              _ptr(do), _ptr(dST), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out.get("dg")),
+              _ptr(out.get("dbeta")), _ptr(out.get("db")), _ptr(out.get("dw")), _ptr(out.get("dS0")),
+              _ptr(workspace), wsz, _stream(stream)))
     return out

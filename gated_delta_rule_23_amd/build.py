@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgdr.so")
-SOURCES = ["abi.hip", "decode.hip", "chunk.hip", "recurrent.hip", "backward.hip"]
+SOURCES = ["abi.hip", "decode.hip", "chunk.hip", "recurrent.hip", "backward.hip", "chunk_bwd.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

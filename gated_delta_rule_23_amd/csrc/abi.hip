@@ -49,7 +49,7 @@ bool size_ok(long long B, long long T, long long H, long long D) {
 
 // Checks shared by every compute call. Decode has no T axis; the chunked
 // prefill also checks the chunk length and its supported dtypes.
-enum CallKind { CALL_DECODE, CALL_CHUNK, CALL_RECURRENT };
+enum CallKind { CALL_DECODE, CALL_CHUNK, CALL_RECURRENT, CALL_CHUNK_BWD };
 int validate(const gdr_desc *d, CallKind kind, const void *q, const void *k, const void *v, const float *g,
              const float *beta, const void *b, const void *w, const void *o) {
     const bool prefill = kind != CALL_DECODE;
@@ -65,9 +65,9 @@ int validate(const gdr_desc *d, CallKind kind, const void *q, const void *k, con
     if (!std::isfinite(d->scale)) return fail(GDR_E_INVAL, "scale must be finite");
     if (d->d_k != d->d_v || !supported_dim(d->d_k))
         return fail(GDR_E_UNSUPPORTED, "d_k = %d, d_v = %d: supported are d_k == d_v in {32, 64, 128}", d->d_k, d->d_v);
-    if (kind == CALL_CHUNK) {
+    if (kind == CALL_CHUNK || kind == CALL_CHUNK_BWD) {
         if (d->chunk != gdr::kChunk) return fail(GDR_E_UNSUPPORTED, "chunk = %d: only 64 is supported", d->chunk);
-        if (!gdr::chunk_supported(d->io_dtype == GDR_BF16 ? gdr::IO_BF16 : gdr::IO_F32, d->d_k))
+        if (kind == CALL_CHUNK && !gdr::chunk_supported(d->io_dtype == GDR_BF16 ? gdr::IO_BF16 : gdr::IO_F32, d->d_k))
             return fail(GDR_E_UNSUPPORTED, "prefill with float32 io supports d in {32, 64}");
     }
     if (!size_ok(d->B, prefill ? d->T : 1, d->H_v, d->d_k) || !size_ok(d->B, prefill ? d->T : 1, d->H_qk, d->d_k))
@@ -220,6 +220,101 @@ bool any_overlap(std::initializer_list<Span> outs, std::initializer_list<Span> i
     return false;
 }
 
+size_t bwd_workspace(const gdr_desc *d, bool chunked) {
+    return chunked ? gdr::chunk_bwd_ws_layout(d->B, d->T, d->H_qk, d->H_v, d->d_k).total()
+                   : gdr::bwd_ws_layout(d->B, d->T, d->H_v, d->d_k).total();
+}
+
+int bwd_workspace_bytes(const gdr_desc *d, size_t *bytes, bool chunked) {
+    if (!bytes) return fail(GDR_E_INVAL, "bytes is NULL");
+    *bytes = 0;
+    static const char dummy = 0;
+    const void *p = &dummy;
+    const int rc = validate(d, chunked ? CALL_CHUNK_BWD : CALL_RECURRENT, p, p, p,
+                            d && d->decay != GDR_DECAY_NONE ? (const float *)p : nullptr, (const float *)p, nullptr,
+                            nullptr, p);
+    if (rc != GDR_OK) return rc;
+    *bytes = bwd_workspace(d, chunked);
+    return ok();
+}
+
+int bwd_call(bool chunked, const gdr_desc *d, const void *q, const void *k, const void *v, const float *g,
+             const float *beta, const void *b, const void *w, const float *S0, const void *dO, const float *dST,
+             float *dq, float *dk, float *dv, float *dg, float *dbeta, float *db, float *dw, float *dS0,
+             void *workspace, size_t workspace_bytes, void *stream) {
+    if (d && d->B > 0 && d->T > 0 && !dO) return fail(GDR_E_INVAL, "dO must be non-NULL");
+    int rc = validate(d, chunked ? CALL_CHUNK_BWD : CALL_RECURRENT, q, k, v, g, beta, b, w, dO);
+    if (rc != GDR_OK) return rc;
+    rc = check_alignment(d, {q, k, v, b, w, dO, S0, dST, dq, dk, dv, db, dw, dS0, workspace}, g, beta);
+    if (rc != GDR_OK) return rc;
+    const bool chan = d->decay == GDR_DECAY_CHANNEL;
+    if ((dg && !aligned(dg, chan ? 16 : 4)) || (dbeta && !aligned(dbeta, 4)))
+        return fail(GDR_E_INVAL, "dg or dbeta is misaligned");
+    const size_t BT = (size_t)d->B * d->T, D = d->d_k;
+    const size_t esz = d->io_dtype == GDR_BF16 ? 2 : 4;
+    const size_t nqk = BT * d->H_qk * D, nv = BT * d->H_v * D, nh = BT * d->H_v;
+    const size_t state = gdr_state_bytes(d->B, d->H_v, d->d_k, d->d_v);
+    const size_t wsb = bwd_workspace(d, chunked);
+    if (d->B > 0 && d->T > 0) {
+        if (!dq || !dk || !dv) return fail(GDR_E_INVAL, "dq, dk and dv must be non-NULL");
+        if ((g == nullptr) != (dg == nullptr)) return fail(GDR_E_INVAL, "dg must be given exactly when g is");
+        if ((beta == nullptr) != (dbeta == nullptr)) return fail(GDR_E_INVAL, "dbeta must be given exactly when beta is");
+        if ((b == nullptr) != (db == nullptr) || (w == nullptr) != (dw == nullptr))
+            return fail(GDR_E_INVAL, "db and dw must be given exactly when b and w are");
+        if (!workspace || workspace_bytes < wsb)
+            return fail(GDR_E_INVAL, "workspace of %zu bytes needed, %zu given", wsb, workspace ? workspace_bytes : 0);
+    }
+    const size_t ng = g ? (chan ? nv : nh) * 4 : 0;
+    if (any_overlap({{dq, nqk * 4}, {dk, nqk * 4}, {dv, nv * 4}, {dg, ng}, {dbeta, dbeta ? nh * 4 : 0},
+                     {db, db ? nv * 4 : 0}, {dw, dw ? nv * 4 : 0}, {dS0, dS0 ? state : 0}},
+                    {{q, nqk * esz}, {k, nqk * esz}, {v, nv * esz}, {g, ng}, {beta, beta ? nh * 4 : 0},
+                     {b, b ? nv * esz : 0}, {w, w ? nv * esz : 0}, {S0, S0 ? state : 0}, {dO, nv * esz},
+                     {dST, dST ? state : 0}, {workspace, workspace ? wsb : 0}}))
+        return fail(GDR_E_INVAL, "gradient arrays must not overlap one another, the inputs or the workspace");
+    if (d->B == 0) return ok();
+    const long long chunks = ((long long)d->T + gdr::kChunk - 1) / gdr::kChunk;
+    if ((long long)d->B * d->H_v * (d->d_k / gdr::kBwdCols) > 0x7fffffffll ||
+        (long long)d->B * d->T * d->H_qk > 0x7fffffffll || (chunked && (long long)d->B * d->H_v * chunks > 0x7fffffffll))
+        return fail(GDR_E_UNSUPPORTED, "too many work items for one launch");
+    if (d->T == 0) {  // no token: the gradient reaching S0 is dL/dS_T itself
+        if (dS0) {
+            hipError_t e = gdr::launch_state_fill(dS0, dST, state / sizeof(float), static_cast<hipStream_t>(stream));
+            if (e != hipSuccess) return hip_fail(e, "dS0 copy");
+        }
+        return ok();
+    }
+    const int io = d->io_dtype == GDR_BF16 ? gdr::IO_BF16 : gdr::IO_F32;
+    hipError_t e;
+    if (chunked) {
+        gdr::ChunkBwdArgs a{};
+        a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.bg = b; a.wg = w; a.S0 = S0; a.dO = dO; a.dST = dST;
+        a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.db = db; a.dw = dw; a.dS0 = dS0;
+        const gdr::ChunkBwdWsLayout L = gdr::chunk_bwd_ws_layout(d->B, d->T, d->H_qk, d->H_v, d->d_k);
+        float **arr[gdr::kChunkBwdArrays] = {&a.wY, &a.wUz, &a.wKe, &a.wQt, &a.wU, &a.wdU, &a.wdE, &a.wdQ, &a.wdK,
+                                             &a.wA, &a.wT, &a.wdA, &a.wdT, &a.wS, &a.wdS, &a.wG, &a.wGam, &a.wdGam,
+                                             &a.wdq, &a.wdk};
+        char *p = static_cast<char *>(workspace);
+        for (int i = 0; i < gdr::kChunkBwdArrays; ++i) {
+            *arr[i] = L.floats[i] ? reinterpret_cast<float *>(p) : nullptr;
+            p += gdr::align256(L.floats[i] * 4);
+        }
+        a.B = d->B; a.T = d->T; a.Hqk = d->H_qk; a.Hv = d->H_v; a.decay = d->decay; a.scale = d->scale;
+        a.NC = (int)chunks;
+        e = gdr::launch_chunk_backward(io, d->d_k, a, static_cast<hipStream_t>(stream));
+    } else {
+        const gdr::BwdWsLayout L = gdr::bwd_ws_layout(d->B, d->T, d->H_v, d->d_k);
+        gdr::BwdArgs a{};
+        a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.bg = b; a.wg = w; a.S0 = S0; a.dO = dO; a.dST = dST;
+        a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.db = db; a.dw = dw; a.dS0 = dS0;
+        a.ws_ck = static_cast<float *>(workspace);
+        a.ws_part = reinterpret_cast<float *>(static_cast<char *>(workspace) + L.ck_bytes);
+        a.B = d->B; a.T = d->T; a.Hqk = d->H_qk; a.Hv = d->H_v; a.decay = d->decay; a.scale = d->scale;
+        e = gdr::launch_backward(io, d->d_k, a, static_cast<hipStream_t>(stream));
+    }
+    if (e != hipSuccess) return hip_fail(e, "backward launch");
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -320,73 +415,24 @@ int gdr_recurrent_fwd_in(const gdr_desc *d, const gdr_input_stage *stage, const 
     return recurrent_call(d, stage, q, k, v, g, beta, b, w, S0, o, ST, stream);
 }
 
-int gdr_recurrent_bwd_workspace_bytes(const gdr_desc *d, size_t *bytes) {
-    if (!bytes) return fail(GDR_E_INVAL, "bytes is NULL");
-    *bytes = 0;
-    static const char dummy = 0;
-    const void *p = &dummy;
-    const int rc = validate(d, CALL_RECURRENT, p, p, p, d && d->decay != GDR_DECAY_NONE ? (const float *)p : nullptr,
-                            (const float *)p, nullptr, nullptr, p);
-    if (rc != GDR_OK) return rc;
-    *bytes = gdr::bwd_ws_layout(d->B, d->T, d->H_v, d->d_k).total();
-    return ok();
-}
+int gdr_recurrent_bwd_workspace_bytes(const gdr_desc *d, size_t *bytes) { return bwd_workspace_bytes(d, bytes, false); }
 
 int gdr_recurrent_bwd(const gdr_desc *d, const void *q, const void *k, const void *v, const float *g,
                       const float *beta, const void *b, const void *w, const float *S0, const void *dO,
                       const float *dST, float *dq, float *dk, float *dv, float *dg, float *dbeta, float *db,
                       float *dw, float *dS0, void *workspace, size_t workspace_bytes, void *stream) {
-    if (d && d->B > 0 && d->T > 0 && !dO) return fail(GDR_E_INVAL, "dO must be non-NULL");
-    int rc = validate(d, CALL_RECURRENT, q, k, v, g, beta, b, w, dO);
-    if (rc != GDR_OK) return rc;
-    rc = check_alignment(d, {q, k, v, b, w, dO, S0, dST, dq, dk, dv, db, dw, dS0, workspace}, g, beta);
-    if (rc != GDR_OK) return rc;
-    const bool chan = d->decay == GDR_DECAY_CHANNEL;
-    if ((dg && !aligned(dg, chan ? 16 : 4)) || (dbeta && !aligned(dbeta, 4)))
-        return fail(GDR_E_INVAL, "dg or dbeta is misaligned");
-    const size_t BT = (size_t)d->B * d->T, D = d->d_k;
-    const size_t esz = d->io_dtype == GDR_BF16 ? 2 : 4;
-    const size_t nqk = BT * d->H_qk * D, nv = BT * d->H_v * D, nh = BT * d->H_v;
-    const size_t state = gdr_state_bytes(d->B, d->H_v, d->d_k, d->d_v);
-    const gdr::BwdWsLayout L = gdr::bwd_ws_layout(d->B, d->T, d->H_v, d->d_k);
-    if (d->B > 0 && d->T > 0) {
-        if (!dq || !dk || !dv) return fail(GDR_E_INVAL, "dq, dk and dv must be non-NULL");
-        if ((g == nullptr) != (dg == nullptr)) return fail(GDR_E_INVAL, "dg must be given exactly when g is");
-        if ((beta == nullptr) != (dbeta == nullptr)) return fail(GDR_E_INVAL, "dbeta must be given exactly when beta is");
-        if ((b == nullptr) != (db == nullptr) || (w == nullptr) != (dw == nullptr))
-            return fail(GDR_E_INVAL, "db and dw must be given exactly when b and w are");
-        if (!workspace || workspace_bytes < L.total())
-            return fail(GDR_E_INVAL, "workspace of %zu bytes needed, %zu given", L.total(),
-                        workspace ? workspace_bytes : 0);
-    }
-    const size_t ng = g ? (chan ? nv : nh) * 4 : 0;
-    if (any_overlap({{dq, nqk * 4}, {dk, nqk * 4}, {dv, nv * 4}, {dg, ng}, {dbeta, dbeta ? nh * 4 : 0},
-                     {db, db ? nv * 4 : 0}, {dw, dw ? nv * 4 : 0}, {dS0, dS0 ? state : 0}},
-                    {{q, nqk * esz}, {k, nqk * esz}, {v, nv * esz}, {g, ng}, {beta, beta ? nh * 4 : 0},
-                     {b, b ? nv * esz : 0}, {w, w ? nv * esz : 0}, {S0, S0 ? state : 0}, {dO, nv * esz},
-                     {dST, dST ? state : 0}, {workspace, workspace ? L.total() : 0}}))
-        return fail(GDR_E_INVAL, "gradient arrays must not overlap one another, the inputs or the workspace");
-    if (d->B == 0) return ok();
-    if ((long long)d->B * d->H_v * (d->d_k / gdr::kBwdCols) > 0x7fffffffll ||
-        (long long)d->B * d->T * d->H_qk > 0x7fffffffll)
-        return fail(GDR_E_UNSUPPORTED, "too many work items for one launch");
-    if (d->T == 0) {  // no token: the gradient reaching S0 is dL/dS_T itself
-        if (dS0) {
-            hipError_t e = gdr::launch_state_fill(dS0, dST, state / sizeof(float), static_cast<hipStream_t>(stream));
-            if (e != hipSuccess) return hip_fail(e, "dS0 copy");
-        }
-        return ok();
-    }
-    gdr::BwdArgs a{};
-    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.bg = b; a.wg = w; a.S0 = S0; a.dO = dO; a.dST = dST;
-    a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.db = db; a.dw = dw; a.dS0 = dS0;
-    a.ws_ck = static_cast<float *>(workspace);
-    a.ws_part = reinterpret_cast<float *>(static_cast<char *>(workspace) + L.ck_bytes);
-    a.B = d->B; a.T = d->T; a.Hqk = d->H_qk; a.Hv = d->H_v; a.decay = d->decay; a.scale = d->scale;
-    hipError_t e = gdr::launch_backward(d->io_dtype == GDR_BF16 ? gdr::IO_BF16 : gdr::IO_F32, d->d_k, a,
-                                        static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "backward launch");
-    return ok();
+    return bwd_call(false, d, q, k, v, g, beta, b, w, S0, dO, dST, dq, dk, dv, dg, dbeta, db, dw, dS0, workspace,
+                    workspace_bytes, stream);
+}
+
+int gdr_chunk_bwd_workspace_bytes(const gdr_desc *d, size_t *bytes) { return bwd_workspace_bytes(d, bytes, true); }
+
+int gdr_chunk_bwd(const gdr_desc *d, const void *q, const void *k, const void *v, const float *g, const float *beta,
+                  const void *b, const void *w, const float *S0, const void *dO, const float *dST, float *dq,
+                  float *dk, float *dv, float *dg, float *dbeta, float *db, float *dw, float *dS0, void *workspace,
+                  size_t workspace_bytes, void *stream) {
+    return bwd_call(true, d, q, k, v, g, beta, b, w, S0, dO, dST, dq, dk, dv, dg, dbeta, db, dw, dS0, workspace,
+                    workspace_bytes, stream);
 }
 
 }  // extern "C"

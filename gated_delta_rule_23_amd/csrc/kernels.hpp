@@ -157,7 +157,47 @@ inline BwdWsLayout bwd_ws_layout(int B, int T, int Hv, int D) {
 }
 
 hipError_t launch_decode(int io, int D, const DecodeArgs &a, hipStream_t s);
+// Chunked backward (chunk_bwd.hip). Per chunk unit u = (b * Hv + h) * NC + c
+// the workspace holds fp32 arrays, row-major:
+struct ChunkBwdArgs {
+    const void *q, *k, *v;   // as BwdArgs
+    const float *g, *beta;
+    const void *bg, *wg;
+    const float *S0;
+    const void *dO;
+    const float *dST;
+    float *dq, *dk, *dv, *dg, *dbeta, *db, *dw, *dS0;
+    float *wY, *wUz, *wKe, *wQt;  // [units][C][D]: Y = L E~, U_z = L Z, Kend, Q~
+    float *wU, *wdU;              // [units][C][D]: U of the chunk; dU, then dR = L^T dU
+    float *wdE, *wdQ, *wdK;       // [units][C][D]: -dR S^T, s dO S^T, U dS_next^T
+    float *wA, *wT, *wdA, *wdT;   // [units][C][C]
+    float *wS, *wdS;              // [units][D][D]: state entering the chunk; dL/d(state leaving it)
+    float *wG;                    // [units][C][D] (per-channel decay) or [units][C]: in-chunk log-decay sums
+    float *wGam, *wdGam;          // [units][D]: exp(G_end); rowsum(dS_next . S)
+    float *wdq, *wdk;             // [B][T][Hv][D] per-V-head parts (grouped heads), else null
+    int B, T, Hqk, Hv, decay, NC;
+    float scale;
+};
+// The workspace is carved into kChunkBwdArrays arrays in the order of the
+// pointer fields wY .. wdk above, each starting on a 256-byte boundary.
+constexpr int kChunkBwdArrays = 20;
+struct ChunkBwdWsLayout {
+    size_t floats[kChunkBwdArrays];
+    size_t total() const {
+        size_t t = 0;
+        for (int i = 0; i < kChunkBwdArrays; ++i) t += align256(floats[i] * 4);
+        return t;
+    }
+};
+inline ChunkBwdWsLayout chunk_bwd_ws_layout(int B, int T, int Hqk, int Hv, int D) {
+    const size_t units = (size_t)B * Hv * ((T + kChunk - 1) / kChunk);
+    const size_t cd = units * kChunk * D, cc = units * kChunk * kChunk, dd = units * D * D, vd = units * D;
+    const size_t part = Hv > Hqk ? (size_t)B * T * Hv * D : 0;
+    return ChunkBwdWsLayout{{cd, cd, cd, cd, cd, cd, cd, cd, cd, cc, cc, cc, cc, dd, dd, cd, vd, vd, part, part}};
+}
+
 hipError_t launch_backward(int io, int D, const BwdArgs &a, hipStream_t s);
+hipError_t launch_chunk_backward(int io, int D, const ChunkBwdArgs &a, hipStream_t s);
 hipError_t launch_chunk(int io, int D, const ChunkArgs &a, hipStream_t s);
 hipError_t launch_recurrent(int io, int D, const RecurArgs &a, hipStream_t s);
 hipError_t launch_state_fill(float *dst, const float *src, size_t n, hipStream_t s);

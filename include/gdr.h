@@ -253,6 +253,37 @@ int gdr_recurrent_bwd(const gdr_desc *desc, const void *q, const void *k, const 
                       const float *dST, float *dq, float *dk, float *dv, float *dg, float *dbeta, float *db,
                       float *dw, float *dS0, void *workspace, size_t workspace_bytes, void *stream);
 
+/* The same gradients in chunked form, parallel over chunks of 64 tokens
+ * ("Resumo Técnico: Gated DeltaNet-2", section "Treinamento Paralelo
+ * Eficiente por Blocos"; the chunked forward of "Gated Delta Networks",
+ * differentiated line by line). Per chunk, with S the state entering it,
+ * G the in-chunk sums of g, E~ = e . exp(G), Q~ = q . exp(G),
+ * Kend = k . exp(G_end - G), Gamma = exp(G_end), T and A the decayed
+ * products of e, q with k below the diagonal, L = (I + T)^-1, Y = L E~ and
+ * U = L Z - Y S:
+ *   dU = s A^T dO + Kend dS_next,  dS = Gamma . dS_next + s Q~^T dO - Y^T dU
+ *   dR = L^T dU (= dZ),  dT = -dR U^T,  dA = s dO U^T,
+ *   dE~ = -dR S^T + dT K~,  dQ~ = s dO S^T + dA K~,  dKend = U dS_next^T,
+ * then the gates and the exponentials as in the recurrence's gradient.
+ *   Arguments, outputs, overlap and alignment rules: as gdr_recurrent_bwd,
+ *   with desc->chunk == 64 (GDR_E_UNSUPPORTED otherwise).
+ *   workspace: gdr_chunk_bwd_workspace_bytes bytes, owned by the caller:
+ *   float32 per chunk unit (sequence, V head, chunk), about
+ *   4 * (10 * 64 * d + 4 * 64 * 64 + 2 * d * d) bytes, plus two
+ *   B * T * H_v * d_k float32 arrays when H_v > H_qk.
+ *   Work: five launches (a per-chunk pass forming the factors and solving
+ *   the unit lower triangular system, a forward pass over chunks storing the
+ *   states, a backward pass over chunks storing dS and dU, and two per-chunk
+ *   gradient passes), plus a sum over grouped V heads; fp32 vector
+ *   arithmetic. T == 0 writes dST (or zeros) to dS0 and touches nothing
+ *   else. Supported: d_k == d_v in {32, 64, 128}, io float32 or bfloat16,
+ *   every decay and gate mode. */
+int gdr_chunk_bwd_workspace_bytes(const gdr_desc *desc, size_t *bytes);
+int gdr_chunk_bwd(const gdr_desc *desc, const void *q, const void *k, const void *v, const float *g,
+                  const float *beta, const void *b, const void *w, const float *S0, const void *dO,
+                  const float *dST, float *dq, float *dk, float *dv, float *dg, float *dbeta, float *db, float *dw,
+                  float *dS0, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char *gdr_last_error(void);
 

@@ -199,10 +199,10 @@ _BWD_NAMES = ("q", "k", "v", "g", "beta", "b", "w", "S0", "dO", "dST", "dq", "dk
 _BWD_BASE = {n: (i + 1) << 32 for i, n in enumerate(_BWD_NAMES)}
 
 
-def _bwd(desc, wsz=1 << 40, **kw):
+def _bwd(desc, wsz=1 << 40, entry="gdr_recurrent_bwd", **kw):
     ptr = dict(_BWD_BASE, b=None, w=None, db=None, dw=None)
     ptr.update(kw)
-    return gdr.lib.gdr_recurrent_bwd(ctypes.byref(desc), *(ptr[n] for n in _BWD_NAMES), wsz, None)
+    return getattr(gdr.lib, entry)(ctypes.byref(desc), *(ptr[n] for n in _BWD_NAMES), wsz, None)
 
 
 def test_backward_workspace_bytes():
@@ -217,6 +217,34 @@ def test_backward_workspace_bytes():
                                                                gdr.GDR_DECAY_SCALAR)) == 0
 
 
+def test_chunk_backward_workspace_bytes():
+    """Per chunk unit (sequence, V head, chunk of 64): ten 64 x D arrays, four
+    64 x 64, two D x D and two of D floats; with grouped heads two more
+    [B,T,H_v,D] arrays; each array rounded up to 256 bytes."""
+    d = gdr.make_desc(1, 100, 2, 4, 128, gdr.GDR_BF16, gdr.GDR_DECAY_SCALAR)
+    units = 1 * 4 * 2
+    per = [64 * 128] * 10 + [64 * 64] * 4 + [128 * 128] * 2 + [128] * 2
+    want = sum(_a256(units * f * 4) for f in per) + 2 * _a256(100 * 4 * 128 * 4)
+    assert gdr.gdr_chunk_bwd_workspace_bytes(d) == want
+    d = gdr.make_desc(2, 64, 4, 4, 64, gdr.GDR_F32, gdr.GDR_DECAY_CHANNEL)  # no grouping, float32 io, d = 64
+    units = 2 * 4 * 1
+    per = [64 * 64] * 10 + [64 * 64] * 4 + [64 * 64] * 2 + [64] * 2
+    assert gdr.gdr_chunk_bwd_workspace_bytes(d) == sum(_a256(units * f * 4) for f in per)
+    assert gdr.gdr_chunk_bwd_workspace_bytes(gdr.make_desc(1, 0, 2, 4, 128, gdr.GDR_BF16,
+                                                           gdr.GDR_DECAY_SCALAR)) == 0
+    d = gdr.make_desc(1, 100, 2, 4, 128, gdr.GDR_BF16, gdr.GDR_DECAY_SCALAR, chunk=32)
+    with pytest.raises(gdr.GdrError):
+        gdr.gdr_chunk_bwd_workspace_bytes(d)
+
+
+def test_chunk_backward_rejects_other_chunk_lengths():
+    d = _desc()
+    d.chunk = 32
+    assert _bwd(d, entry="gdr_chunk_bwd") == gdr.GDR_E_UNSUPPORTED
+    assert gdr.gdr_last_error() != ""
+
+
+@pytest.mark.parametrize("entry", ["gdr_recurrent_bwd", "gdr_chunk_bwd"])
 @pytest.mark.parametrize("case,expect", [
     (dict(desc=dict(D=96)), gdr.GDR_E_UNSUPPORTED),
     (dict(desc=dict(Hv=5)), gdr.GDR_E_INVAL),
@@ -240,14 +268,15 @@ def test_backward_workspace_bytes():
     (dict(args=dict(dbeta=_BWD_BASE["dbeta"] + 1)), gdr.GDR_E_INVAL),
     (dict(args=dict(dST=_BWD_BASE["dST"] + 8)), gdr.GDR_E_INVAL),
 ])
-def test_backward_rejections(case, expect):
+def test_backward_rejections(entry, case, expect):
     d = _desc(**case.get("desc", {}))
-    assert _bwd(d, wsz=case.get("wsz", 1 << 40), **case.get("args", {})) == expect
+    assert _bwd(d, wsz=case.get("wsz", 1 << 40), entry=entry, **case.get("args", {})) == expect
     assert gdr.gdr_last_error() != ""
 
 
-def test_backward_zero_batch_is_a_noop_without_gpu():
-    assert _bwd(_desc(B=0)) == gdr.GDR_OK
+@pytest.mark.parametrize("entry", ["gdr_recurrent_bwd", "gdr_chunk_bwd"])
+def test_backward_zero_batch_is_a_noop_without_gpu(entry):
+    assert _bwd(_desc(B=0), entry=entry) == gdr.GDR_OK
     assert gdr.gdr_last_error() == ""
 
 
