@@ -30,6 +30,10 @@
 // K~ = k . exp(-G) (as in the forward); with a scalar decay the exponentials
 // are kept per entry, exp(G_t - G_j) <= 1, so strong decays stay finite.
 //
+// Shared-memory tiles keep 16-byte aligned rows (stride a multiple of 4
+// floats) and the inner loops read them 16 bytes at a time; global arrays
+// are staged through registers with 16-byte (8-byte for bf16) loads.
+//
 // Five launches, all arithmetic in fp32:
 //  1. cb_prep (per chunk unit): G, the factors above, T and A, and the
 //     triangular solve (I + T)[Y | U_z] = [E~ | Z] by forward substitution.
@@ -49,14 +53,30 @@ namespace gdr {
 namespace {
 
 constexpr int C = kChunk;
-constexpr int NT = 256;  // threads per workgroup
-constexpr int BV = 32;   // value columns per sweep workgroup
-constexpr int PB = BV + 1, PC = C + 1;
+constexpr int NT = 256;     // threads per workgroup
+constexpr int BV = 32;      // value columns per sweep workgroup
+constexpr int LB = BV + 4;  // row stride of 32-column tiles
+constexpr int LC = C + 4;   // row stride of 64-column tiles
 
-template <typename IO>
-__device__ __forceinline__ float ldio(const void *p, size_t i) {
-    return Elem<IO>::load(static_cast<const IO *>(p) + i);
+template <int D>
+struct Cfg {
+    static constexpr int LD = D + 4;              // row stride of D-column tiles
+    static constexpr int NL = C * D / (4 * NT);   // 4-element groups per thread of a C x D array
+    static constexpr int NTL = D / BV, TPR = NT / D, CPT = BV / TPR;  // sweep state rows: threads per row, columns each
+    static constexpr int NCG = D / 4, RT = D / 16, NRG = NT / NCG;     // cb_grad_out: column groups, rows per thread
+};
+
+__device__ __forceinline__ f32x4 lds4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+__device__ __forceinline__ void sts4(float *p, f32x4 v) { *reinterpret_cast<f32x4 *>(p) = v; }
+__device__ __forceinline__ f32x4 splat(float x) { return f32x4{x, x, x, x}; }
+__device__ __forceinline__ float dot4(f32x4 a, f32x4 b, float acc) {
+    return fmaf(a[3], b[3], fmaf(a[2], b[2], fmaf(a[1], b[1], fmaf(a[0], b[0], acc))));
 }
+template <typename IO>
+__device__ __forceinline__ f32x4 ld4io(const void *p, size_t i) {  // 4 consecutive io elements, widened
+    return Raw4<IO>::widen(Raw4<IO>::load(static_cast<const IO *>(p) + i));
+}
+__device__ __forceinline__ f32x4 exp4(f32x4 x) { return f32x4{expf(x[0]), expf(x[1]), expf(x[2]), expf(x[3])}; }
 
 struct Unit {
     int b, h, hq, c, t0, n;
@@ -75,6 +95,13 @@ __device__ __forceinline__ Unit decode(const ChunkBwdArgs &a, int u) {
     x.rowv = ((size_t)x.b * a.T + x.t0) * a.Hv + x.h;
     return x;
 }
+// Element e (a multiple of 4) of a row-major C x D array: token row and column.
+template <int D>
+__device__ __forceinline__ void rc(int l, int &e, int &t, int &d) {
+    e = 4 * (l * NT + (int)threadIdx.x);
+    t = e / D;
+    d = e - t * D;
+}
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -82,58 +109,114 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// (I + T) x = r for one column x (in registers, r on entry), T strictly
+// lower triangular, row-major with row stride C in shared memory:
+// x_i = r_i - sum_{m < i} T_im x_m, rows in order.
+__device__ __forceinline__ void solve_lower(float (&x)[C], const float *sT) {
+#pragma unroll
+    for (int i = 1; i < C; ++i) {
+        float acc = x[i];
+#pragma unroll
+        for (int m4 = 0; m4 < i; m4 += 4) {
+            const f32x4 t = lds4(sT + i * C + m4);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (m4 + r < i) acc = fmaf(-t[r], x[m4 + r], acc);
+        }
+        x[i] = acc;
+    }
+}
+// (I + T)^T x = r, with sTt = T^T (row i = column i of T), rows from the
+// last: x_i = r_i - sum_{m > i} T_mi x_m.
+__device__ __forceinline__ void solve_upper(float (&x)[C], const float *sTt) {
+#pragma unroll
+    for (int i = C - 2; i >= 0; --i) {
+        float acc = x[i];
+#pragma unroll
+        for (int m4 = (i + 1) & ~3; m4 < C; m4 += 4) {
+            const f32x4 t = lds4(sTt + i * C + m4);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (m4 + r > i) acc = fmaf(-t[r], x[m4 + r], acc);
+        }
+        x[i] = acc;
+    }
+}
+
 template <int D>
 constexpr size_t prep_smem() {
-    return ((size_t)(C * (D + 1) > C * PC ? C * (D + 1) : C * PC) + 3 * (size_t)C * (D + 1) + C) * 4;
+    constexpr size_t LD = D + 4, R0 = C * LD > C * C ? C * LD : C * C;
+    return (R0 + 3 * C * LD + C) * 4;
+}
+template <int D>
+constexpr size_t fsweep_smem() {
+    return ((size_t)D * LB + (size_t)C * LB + (size_t)C * (D + 4) + (size_t)D * LC) * 4;
+}
+template <int D>
+constexpr size_t bsweep_smem() {
+    return ((size_t)D * LB + 2 * (size_t)C * LB + (size_t)C * LC + (size_t)C * (D + 4) + 2 * (size_t)D * LC) * 4;
 }
 template <int D>
 constexpr size_t grad_s_smem() {
-    return ((size_t)C * PC + 3 * (size_t)C * (D + 1) + 32 * (size_t)(D + 1)) * 4;
+    constexpr size_t LD = D + 4, R0 = C * C > 32 * LD ? C * C : 32 * LD;
+    return (R0 + 3 * C * LD + 32 * LD) * 4;
 }
 template <int D>
 constexpr size_t grad_out_smem() {
-    return (3 * (size_t)C * (D + 1) + 2 * (size_t)C * PC + 2 * C + 4 * C + 2 * 16 * C + 16 * (size_t)D + D) * 4;
+    return (3 * (size_t)C * (D + 4) + 2 * (size_t)C * LC + 2 * C + 16 * C + 2 * 32 * C + 1024 + D) * 4;
 }
 
 // ---------------------------------------------------------------------------
 // 1. Per chunk unit: G, E~, Q~, Kend, Gamma, T, A, then [Y | U_z].
 template <typename IO, int D, bool CHAN, bool BW>
 __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
-    constexpr int PD = D + 1, R0 = C * PD > C * PC ? C * PD : C * PC;
+    constexpr int LD = Cfg<D>::LD, NL = Cfg<D>::NL, R0 = C * LD > C * C ? C * LD : C * C;
     extern __shared__ __align__(16) float smem[];
-    float *sQ = smem;           // q (Q~ with a per-channel decay); then T
+    float *sQ = smem;           // q (Q~ with a per-channel decay); then T, row stride C
     float *sK = sQ + R0;        // k (K~)
-    float *sE = sK + C * PD;    // e, then E~, then Y
-    float *sZ = sE + C * PD;    // per-channel decay: g, then G; then z, then U_z
-    float *sGs = sZ + C * PD;   // scalar decay: G per token
+    float *sE = sK + C * LD;    // e, then E~, then Y
+    float *sZ = sE + C * LD;    // per-channel decay: g, then G; then z, then U_z
+    float *sGs = sZ + C * LD;   // scalar decay: G per token
     const int tid = threadIdx.x, u = blockIdx.x;
     const Unit x = decode(a, u);
     const size_t ucd = (size_t)u * C * D;
-
-    for (int i = tid; i < C * D; i += NT) {
-        const int t = i / D, d = i - t * D;
-        float qv = 0.f, kv = 0.f, ev = 0.f, gv = 0.f;
-        if (t < x.n) {
-            const size_t iq = (x.rowq + (size_t)t * a.Hqk) * D + d, iv = (x.rowv + (size_t)t * a.Hv) * D + d;
-            qv = ldio<IO>(a.q, iq);
-            kv = ldio<IO>(a.k, iq);
-            ev = (BW ? ldio<IO>(a.bg, iv) : a.beta[x.rowv + (size_t)t * a.Hv]) * kv;
-            if (CHAN) gv = a.g[iv];
+    {
+        f32x4 rq[NL], rk[NL], re[NL], rg[CHAN ? NL : 1];
+#pragma unroll
+        for (int l = 0; l < NL; ++l) {
+            int e, t, d;
+            rc<D>(l, e, t, d);
+            rq[l] = rk[l] = re[l] = zero4();
+            if (CHAN) rg[l] = zero4();
+            if (t < x.n) {
+                const size_t iq = (x.rowq + (size_t)t * a.Hqk) * D + d, iv = (x.rowv + (size_t)t * a.Hv) * D + d;
+                rq[l] = ld4io<IO>(a.q, iq);
+                rk[l] = ld4io<IO>(a.k, iq);
+                re[l] = BW ? ld4io<IO>(a.bg, iv) : splat(a.beta[x.rowv + (size_t)t * a.Hv]);
+                if (CHAN) rg[l] = lds4(a.g + iv);
+            }
         }
-        sQ[t * PD + d] = qv;
-        sK[t * PD + d] = kv;
-        sE[t * PD + d] = ev;
-        if (CHAN) sZ[t * PD + d] = gv;
+#pragma unroll
+        for (int l = 0; l < NL; ++l) {
+            int e, t, d;
+            rc<D>(l, e, t, d);
+            sts4(sQ + t * LD + d, rq[l]);
+            sts4(sK + t * LD + d, rk[l]);
+            sts4(sE + t * LD + d, re[l] * rk[l]);
+            if (CHAN) sts4(sZ + t * LD + d, rg[l]);
+        }
     }
     if (!CHAN && tid < C) sGs[tid] = a.g && tid < x.n ? a.g[x.rowv + (size_t)tid * a.Hv] : 0.f;
     __syncthreads();
     if (CHAN) {
-        if (tid < D) {
-            float acc = 0.f;
-            for (int t = 0; t < C; ++t) {
-                acc += sZ[t * PD + tid];
-                sZ[t * PD + tid] = acc;
-            }
+        if (tid < D) {  // per channel: the column into registers, summed, written back
+            float gc[C];
+#pragma unroll
+            for (int t = 0; t < C; ++t) gc[t] = sZ[t * LD + tid];
+#pragma unroll
+            for (int t = 1; t < C; ++t) gc[t] += gc[t - 1];
+#pragma unroll
+            for (int t = 0; t < C; ++t) sZ[t * LD + tid] = gc[t];
         }
     } else if (tid < 64) {
         float G = sGs[tid];
@@ -147,22 +230,24 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
     __syncthreads();
 
     float *wG = a.wG + ucd;  // [C][D] per-channel decay, [C] scalar
-    for (int i = tid; i < C * D; i += NT) {
-        const int t = i / D, d = i - t * D;
-        const float G = CHAN ? sZ[t * PD + d] : sGs[t];
-        const float Ge = CHAN ? sZ[(C - 1) * PD + d] : sGs[C - 1];
-        const float eg = expf(G), qv = sQ[t * PD + d], kv = sK[t * PD + d];
-        a.wQt[ucd + i] = qv * eg;
-        a.wKe[ucd + i] = kv * expf(Ge - G);
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+        int e, t, d;
+        rc<D>(l, e, t, d);
+        const f32x4 G = CHAN ? lds4(sZ + t * LD + d) : splat(sGs[t]);
+        const f32x4 Ge = CHAN ? lds4(sZ + (C - 1) * LD + d) : splat(sGs[C - 1]);
+        const f32x4 eg = exp4(G), qv = lds4(sQ + t * LD + d), kv = lds4(sK + t * LD + d);
+        sts4(a.wQt + ucd + e, qv * eg);
+        sts4(a.wKe + ucd + e, kv * exp4(Ge - G));
         if (CHAN) {
-            wG[i] = G;
-            sQ[t * PD + d] = qv * eg;
-            sK[t * PD + d] = kv * expf(-G);
-            sE[t * PD + d] *= eg;
+            sts4(wG + e, G);
+            sts4(sQ + t * LD + d, qv * eg);
+            sts4(sK + t * LD + d, kv * exp4(-G));
+            sts4(sE + t * LD + d, lds4(sE + t * LD + d) * eg);
         }
     }
     if (!CHAN && tid < C) wG[tid] = sGs[tid];
-    if (tid < D) a.wGam[(size_t)u * D + tid] = expf(CHAN ? sZ[(C - 1) * PD + tid] : sGs[C - 1]);
+    if (tid < D) a.wGam[(size_t)u * D + tid] = expf(CHAN ? sZ[(C - 1) * LD + tid] : sGs[C - 1]);
     __syncthreads();
 
     // T and A: thread = 4 x 4 block of rows r0.., columns c0..
@@ -173,23 +258,25 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) aT[i][j] = aA[i][j] = 0.f;
-        if (c0 <= r0 + 3)
-            for (int d = 0; d < D; ++d) {
-                float e4[4], q4[4], k4[4];
+        if (c0 <= r0 + 3) {
+#pragma unroll 2
+            for (int d = 0; d < D; d += 4) {
+                f32x4 e4[4], q4[4], k4[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    e4[i] = sE[(r0 + i) * PD + d];
-                    q4[i] = sQ[(r0 + i) * PD + d];
-                    k4[i] = sK[(c0 + i) * PD + d];
+                    e4[i] = lds4(sE + (r0 + i) * LD + d);
+                    q4[i] = lds4(sQ + (r0 + i) * LD + d);
+                    k4[i] = lds4(sK + (c0 + i) * LD + d);
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        aT[i][j] = fmaf(e4[i], k4[j], aT[i][j]);
-                        aA[i][j] = fmaf(q4[i], k4[j], aA[i][j]);
+                        aT[i][j] = dot4(e4[i], k4[j], aT[i][j]);
+                        aA[i][j] = dot4(q4[i], k4[j], aA[i][j]);
                     }
             }
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int t = r0 + i;
@@ -201,190 +288,275 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
                 aA[i][j] = jj <= t ? aA[i][j] * f : 0.f;
             }
             const size_t o = (size_t)u * C * C + (size_t)t * C + c0;
-            *reinterpret_cast<f32x4 *>(a.wT + o) = f32x4{aT[i][0], aT[i][1], aT[i][2], aT[i][3]};
-            *reinterpret_cast<f32x4 *>(a.wA + o) = f32x4{aA[i][0], aA[i][1], aA[i][2], aA[i][3]};
+            sts4(a.wT + o, f32x4{aT[i][0], aT[i][1], aT[i][2], aT[i][3]});
+            sts4(a.wA + o, f32x4{aA[i][0], aA[i][1], aA[i][2], aA[i][3]});
         }
         __syncthreads();  // q, k and e tiles read: T goes where q was
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) sQ[(r0 + i) * PC + c0 + j] = aT[i][j];
+        for (int i = 0; i < 4; ++i) sts4(sQ + (r0 + i) * C + c0, f32x4{aT[i][0], aT[i][1], aT[i][2], aT[i][3]});
     }
     // Right-hand sides: E~ (scalar decay: the raw e scaled by exp(G_t)) and z.
-    for (int i = tid; i < C * D; i += NT) {
-        const int t = i / D, d = i - t * D;
-        if (!CHAN) sE[t * PD + d] *= expf(sGs[t]);
-        float zv = 0.f;
-        if (t < x.n) {
-            const size_t iv = (x.rowv + (size_t)t * a.Hv) * D + d;
-            zv = (BW ? ldio<IO>(a.wg, iv) : a.beta[x.rowv + (size_t)t * a.Hv]) * ldio<IO>(a.v, iv);
-        }
-        sZ[t * PD + d] = zv;
-    }
-    __syncthreads();
-    // (I + T) X = [E~ | Z], column by column, rows in order: X_i = R_i - sum_{m<i} T_im X_m.
-    if (tid < 2 * D) {
-        const float *sT = sQ;
-        float *X = tid < D ? sE + tid : sZ + (tid - D);
-        for (int i = 1; i < C; ++i) {
-            float p0 = X[i * PD], p1 = 0.f;
-            int m = 0;
-            for (; m + 1 < i; m += 2) {
-                p0 = fmaf(-sT[i * PC + m], X[m * PD], p0);
-                p1 = fmaf(-sT[i * PC + m + 1], X[(m + 1) * PD], p1);
+    {
+        f32x4 rz[NL];
+#pragma unroll
+        for (int l = 0; l < NL; ++l) {
+            int e, t, d;
+            rc<D>(l, e, t, d);
+            rz[l] = zero4();
+            if (t < x.n) {
+                const size_t iv = (x.rowv + (size_t)t * a.Hv) * D + d;
+                rz[l] = (BW ? ld4io<IO>(a.wg, iv) : splat(a.beta[x.rowv + (size_t)t * a.Hv])) * ld4io<IO>(a.v, iv);
             }
-            if (m < i) p0 = fmaf(-sT[i * PC + m], X[m * PD], p0);
-            X[i * PD] = p0 + p1;
+        }
+#pragma unroll
+        for (int l = 0; l < NL; ++l) {
+            int e, t, d;
+            rc<D>(l, e, t, d);
+            sts4(sZ + t * LD + d, rz[l]);
+            if (!CHAN) sts4(sE + t * LD + d, lds4(sE + t * LD + d) * expf(sGs[t]));
         }
     }
     __syncthreads();
-    for (int i = tid; i < C * D; i += NT) {
-        const int t = i / D, d = i - t * D;
-        a.wY[ucd + i] = sE[t * PD + d];
-        a.wUz[ucd + i] = sZ[t * PD + d];
+    // (I + T) X = [E~ | Z], one column per thread.
+    if (tid < 2 * D) {
+        float *X = tid < D ? sE + tid : sZ + (tid - D);
+        float xc[C];
+#pragma unroll
+        for (int i = 0; i < C; ++i) xc[i] = X[i * LD];
+        solve_lower(xc, sQ);
+#pragma unroll
+        for (int i = 0; i < C; ++i) X[i * LD] = xc[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+        int e, t, d;
+        rc<D>(l, e, t, d);
+        sts4(a.wY + ucd + e, lds4(sE + t * LD + d));
+        sts4(a.wUz + ucd + e, lds4(sZ + t * LD + d));
     }
 }
 
 // ---------------------------------------------------------------------------
-// 2. Forward over chunks for one (sequence, V head, 32 value columns): the
-//    state entering each chunk, and U = U_z - Y S.
+// Sweeps over chunks. A workgroup owns (sequence, V head, 32 value columns);
+// each chunk's operands are fetched into registers one chunk ahead (the
+// whole workgroup together) and moved to shared memory at the start of the
+// chunk, so that the loop reads its operands from shared memory.
+
+// 2. Forward over chunks: the state entering each chunk, and U = U_z - Y S.
 template <int D>
 __global__ __launch_bounds__(NT) void cb_fsweep(ChunkBwdArgs a) {
-    constexpr int NTL = D / BV, TPR = NT / D, CPT = BV / TPR;
-    __shared__ float sS[D * PB];
-    __shared__ float sU[C * PB];
+    using K = Cfg<D>;
+    constexpr int NTL = K::NTL, TPR = K::TPR, CPT = K::CPT, LD = K::LD, NL = K::NL;
+    extern __shared__ __align__(16) float smem[];
+    float *sS = smem, *sU = sS + D * LB, *sY = sU + C * LB, *sKt = sY + C * LD;  // Kend transposed: [D][LC]
     const int tid = threadIdx.x, tile = blockIdx.x % NTL, bh = blockIdx.x / NTL, col0 = tile * BV;
     const size_t sb = (size_t)bh * D * D;
-    for (int i = tid; i < D * BV; i += NT) {
-        const int d = i / BV, j = i - d * BV;
-        sS[d * PB + j] = a.S0 ? a.S0[sb + (size_t)d * D + col0 + j] : 0.f;
+    for (int i = tid; i < D * BV / 4; i += NT) {
+        const int d = 4 * i / BV, j = 4 * i - d * BV;
+        sts4(sS + d * LB + j, a.S0 ? lds4(a.S0 + sb + (size_t)d * D + col0 + j) : zero4());
     }
-    __syncthreads();
     const int ut = tid >> 2, uj = (tid & 3) * 8;       // U: row ut, columns uj..uj+7
     const int sd = tid / TPR, sj = (tid % TPR) * CPT;  // S: row sd, columns sj..
+    f32x4 pY[NL], pK[NL], pZ[2];
+    float pg;
+    const auto fetch = [&](int c) {
+        const size_t u = (size_t)bh * a.NC + c, ucd = u * C * D;
+#pragma unroll
+        for (int l = 0; l < NL; ++l) {
+            int e, t, d;
+            rc<D>(l, e, t, d);
+            pY[l] = lds4(a.wY + ucd + e);
+            pK[l] = lds4(a.wKe + ucd + e);
+        }
+        const float *z = a.wUz + ucd + (size_t)ut * D + col0 + uj;
+        pZ[0] = lds4(z);
+        pZ[1] = lds4(z + 4);
+        pg = a.wGam[u * D + sd];
+    };
+    fetch(0);
     for (int c = 0; c < a.NC; ++c) {
         const size_t u = (size_t)bh * a.NC + c, ucd = u * C * D;
-        for (int i = tid; i < D * BV; i += NT) {
-            const int d = i / BV, j = i - d * BV;
-            a.wS[u * D * D + (size_t)d * D + col0 + j] = sS[d * PB + j];
-        }
-        float acc[8];
-        const float *Y = a.wY + ucd + (size_t)ut * D;
+        __syncthreads();  // the previous chunk is done with the operand tiles; S written
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = a.wUz[ucd + (size_t)ut * D + col0 + uj + j];
+        for (int l = 0; l < NL; ++l) {
+            int e, t, d;
+            rc<D>(l, e, t, d);
+            sts4(sY + t * LD + d, pY[l]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sKt[(d + r) * LC + t] = pK[l][r];
+        }
+        f32x4 acc0 = pZ[0], acc1 = pZ[1];
+        const float gam = pg;
+        if (c + 1 < a.NC) fetch(c + 1);
+        for (int i = tid; i < D * BV / 4; i += NT) {
+            const int d = 4 * i / BV, j = 4 * i - d * BV;
+            sts4(a.wS + u * D * D + (size_t)d * D + col0 + j, lds4(sS + d * LB + j));
+        }
+        __syncthreads();
+#pragma unroll 4
         for (int d = 0; d < D; d += 4) {
-            const f32x4 y = *reinterpret_cast<const f32x4 *>(Y + d);
+            const f32x4 y = lds4(sY + ut * LD + d);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                acc0 -= y[r] * lds4(sS + (d + r) * LB + uj);
+                acc1 -= y[r] * lds4(sS + (d + r) * LB + uj + 4);
+            }
+        }
+        sts4(sU + ut * LB + uj, acc0);
+        sts4(sU + ut * LB + uj + 4, acc1);
+        float *wu = a.wU + ucd + (size_t)ut * D + col0 + uj;
+        sts4(wu, acc0);
+        sts4(wu + 4, acc1);
+        __syncthreads();
+        f32x4 sv[CPT / 4];
+#pragma unroll
+        for (int q = 0; q < CPT / 4; ++q) sv[q] = gam * lds4(sS + sd * LB + sj + 4 * q);
+#pragma unroll 4
+        for (int t = 0; t < C; t += 4) {
+            const f32x4 kv = lds4(sKt + sd * LC + t);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
 #pragma unroll
-                for (int j = 0; j < 8; ++j) acc[j] = fmaf(-y[r], sS[(d + r) * PB + uj + j], acc[j]);
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            sU[ut * PB + uj + j] = acc[j];
-            a.wU[ucd + (size_t)ut * D + col0 + uj + j] = acc[j];
-        }
-        __syncthreads();
-        const float gam = a.wGam[u * D + sd];
-        float s[CPT];
-#pragma unroll
-        for (int j = 0; j < CPT; ++j) s[j] = gam * sS[sd * PB + sj + j];
-        const float *Ke = a.wKe + ucd + sd;
-        for (int t = 0; t < C; ++t) {
-            const float kv = Ke[(size_t)t * D];
-#pragma unroll
-            for (int j = 0; j < CPT; ++j) s[j] = fmaf(kv, sU[t * PB + sj + j], s[j]);
+                for (int q = 0; q < CPT / 4; ++q) sv[q] += kv[r] * lds4(sU + (t + r) * LB + sj + 4 * q);
         }
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) sS[sd * PB + sj + j] = s[j];
-        __syncthreads();
+        for (int q = 0; q < CPT / 4; ++q) sts4(sS + sd * LB + sj + 4 * q, sv[q]);
     }
 }
 
-// ---------------------------------------------------------------------------
 // 3. Backward over chunks for the same work items: X = dL/d(state leaving
 //    the chunk), dU, and X for the chunk before.
 template <typename IO, int D>
 __global__ __launch_bounds__(NT) void cb_bsweep(ChunkBwdArgs a) {
-    constexpr int NTL = D / BV, TPR = NT / D, CPT = BV / TPR;
-    __shared__ float sX[D * PB];
-    __shared__ float sO[C * PB];
-    __shared__ float sdU[C * PB];
+    using K = Cfg<D>;
+    constexpr int NTL = K::NTL, TPR = K::TPR, CPT = K::CPT, LD = K::LD, NL = K::NL;
+    constexpr int NA = C * C / (4 * NT), NO = C * BV / (4 * NT);  // 4-element groups per thread: A, dO tile
+    extern __shared__ __align__(16) float smem[];
+    float *sX = smem, *sO = sX + D * LB, *sdU = sO + C * LB;
+    float *sAt = sdU + C * LB;   // A^T [C][LC]
+    float *sK = sAt + C * LC;    // Kend [C][LD]
+    float *sQt = sK + C * LD;    // Q~^T [D][LC]
+    float *sYt = sQt + D * LC;   // Y^T [D][LC]
     const int tid = threadIdx.x, tile = blockIdx.x % NTL, bh = blockIdx.x / NTL, col0 = tile * BV;
     const int b = bh / a.Hv, h = bh - b * a.Hv;
     const size_t sb = (size_t)bh * D * D;
-    for (int i = tid; i < D * BV; i += NT) {
-        const int d = i / BV, j = i - d * BV;
-        sX[d * PB + j] = a.dST ? a.dST[sb + (size_t)d * D + col0 + j] : 0.f;
+    for (int i = tid; i < D * BV / 4; i += NT) {
+        const int d = 4 * i / BV, j = 4 * i - d * BV;
+        sts4(sX + d * LB + j, a.dST ? lds4(a.dST + sb + (size_t)d * D + col0 + j) : zero4());
     }
     const int ut = tid >> 2, uj = (tid & 3) * 8;
     const int sd = tid / TPR, sj = (tid % TPR) * CPT;
-    for (int c = a.NC - 1; c >= 0; --c) {
+    f32x4 pY[NL], pK[NL], pQ[NL], pA[NA], pO[NO];
+    float pg;
+    const auto fetch = [&](int c) {
         const size_t u = (size_t)bh * a.NC + c, ucd = u * C * D;
         const int t0 = c * C, n = min(C, a.T - t0);
-        __syncthreads();  // X written; the previous chunk's reads of dO and dU done
-        for (int i = tid; i < D * BV; i += NT) {
-            const int d = i / BV, j = i - d * BV;
-            a.wdS[u * D * D + (size_t)d * D + col0 + j] = sX[d * PB + j];
+#pragma unroll
+        for (int l = 0; l < NL; ++l) {
+            int e, t, d;
+            rc<D>(l, e, t, d);
+            pY[l] = lds4(a.wY + ucd + e);
+            pK[l] = lds4(a.wKe + ucd + e);
+            pQ[l] = lds4(a.wQt + ucd + e);
         }
-        for (int i = tid; i < C * BV; i += NT) {
-            const int t = i / BV, j = i - t * BV;
-            sO[t * PB + j] = t < n ? ldio<IO>(a.dO, (((size_t)b * a.T + t0 + t) * a.Hv + h) * D + col0 + j) : 0.f;
+#pragma unroll
+        for (int l = 0; l < NA; ++l) pA[l] = lds4(a.wA + u * C * C + 4 * (l * NT + tid));
+#pragma unroll
+        for (int l = 0; l < NO; ++l) {
+            const int e = 4 * (l * NT + tid), t = e / BV, j = e - t * BV;
+            pO[l] = t < n ? ld4io<IO>(a.dO, (((size_t)b * a.T + t0 + t) * a.Hv + h) * D + col0 + j) : zero4();
+        }
+        pg = a.wGam[u * D + sd];
+    };
+    fetch(a.NC - 1);
+    for (int c = a.NC - 1; c >= 0; --c) {
+        const size_t u = (size_t)bh * a.NC + c, ucd = u * C * D;
+        __syncthreads();  // X written; the previous chunk is done with the operand tiles
+#pragma unroll
+        for (int l = 0; l < NL; ++l) {
+            int e, t, d;
+            rc<D>(l, e, t, d);
+            sts4(sK + t * LD + d, pK[l]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                sYt[(d + r) * LC + t] = pY[l][r];
+                sQt[(d + r) * LC + t] = pQ[l][r];
+            }
+        }
+#pragma unroll
+        for (int l = 0; l < NA; ++l) {
+            const int e = 4 * (l * NT + tid), t = e / C, j = e - t * C;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sAt[(j + r) * LC + t] = pA[l][r];
+        }
+#pragma unroll
+        for (int l = 0; l < NO; ++l) {
+            const int e = 4 * (l * NT + tid), t = e / BV, j = e - t * BV;
+            sts4(sO + t * LB + j, pO[l]);
+        }
+        const float gam = pg;
+        if (c > 0) fetch(c - 1);
+        for (int i = tid; i < D * BV / 4; i += NT) {
+            const int d = 4 * i / BV, j = 4 * i - d * BV;
+            sts4(a.wdS + u * D * D + (size_t)d * D + col0 + j, lds4(sX + d * LB + j));
         }
         __syncthreads();
-        // dU (row ut) = s sum_{t >= ut} A_t,ut dO_t + Kend_ut X
-        float acc[8];
+        // dU (row ut) = s (A^T dO)_ut + Kend_ut X
+        f32x4 p0 = zero4(), p1 = zero4(), k0 = zero4(), k1 = zero4();
+#pragma unroll 4
+        for (int t = 0; t < C; t += 4) {
+            const f32x4 av = lds4(sAt + ut * LC + t);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = 0.f;
-        const float *A = a.wA + u * C * C;
-        for (int t = ut; t < C; ++t) {
-            const float av = A[(size_t)t * C + ut];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc[j] = fmaf(av, sO[t * PB + uj + j], acc[j]);
+            for (int r = 0; r < 4; ++r) {
+                p0 += av[r] * lds4(sO + (t + r) * LB + uj);
+                p1 += av[r] * lds4(sO + (t + r) * LB + uj + 4);
+            }
         }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] *= a.scale;
-        const float *Ke = a.wKe + ucd + (size_t)ut * D;
+#pragma unroll 4
         for (int d = 0; d < D; d += 4) {
-            const f32x4 kv = *reinterpret_cast<const f32x4 *>(Ke + d);
+            const f32x4 kv = lds4(sK + ut * LD + d);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                k0 += kv[r] * lds4(sX + (d + r) * LB + uj);
+                k1 += kv[r] * lds4(sX + (d + r) * LB + uj + 4);
+            }
+        }
+        const f32x4 du0 = a.scale * p0 + k0, du1 = a.scale * p1 + k1;
+        sts4(sdU + ut * LB + uj, du0);
+        sts4(sdU + ut * LB + uj + 4, du1);
+        float *wd = a.wdU + ucd + (size_t)ut * D + col0 + uj;
+        sts4(wd, du0);
+        sts4(wd + 4, du1);
+        __syncthreads();
+        // X (row sd) = Gamma_sd X + s Q~^T dO - Y^T dU
+        f32x4 xa[CPT / 4], qa[CPT / 4];
+#pragma unroll
+        for (int q = 0; q < CPT / 4; ++q) {
+            xa[q] = gam * lds4(sX + sd * LB + sj + 4 * q);
+            qa[q] = zero4();
+        }
+#pragma unroll 4
+        for (int t = 0; t < C; t += 4) {
+            const f32x4 qv = lds4(sQt + sd * LC + t), yv = lds4(sYt + sd * LC + t);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
 #pragma unroll
-                for (int j = 0; j < 8; ++j) acc[j] = fmaf(kv[r], sX[(d + r) * PB + uj + j], acc[j]);
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            sdU[ut * PB + uj + j] = acc[j];
-            a.wdU[ucd + (size_t)ut * D + col0 + uj + j] = acc[j];
-        }
-        __syncthreads();
-        // X (row sd) = Gamma_sd X + s Q~^T dO - Y^T dU
-        const float gam = a.wGam[u * D + sd];
-        float xa[CPT], qa[CPT];
-#pragma unroll
-        for (int j = 0; j < CPT; ++j) {
-            xa[j] = gam * sX[sd * PB + sj + j];
-            qa[j] = 0.f;
-        }
-        const float *Qt = a.wQt + ucd + sd, *Y = a.wY + ucd + sd;
-        for (int t = 0; t < C; ++t) {
-            const float qv = Qt[(size_t)t * D], yv = Y[(size_t)t * D];
-#pragma unroll
-            for (int j = 0; j < CPT; ++j) {
-                qa[j] = fmaf(qv, sO[t * PB + sj + j], qa[j]);
-                xa[j] = fmaf(-yv, sdU[t * PB + sj + j], xa[j]);
-            }
+                for (int q = 0; q < CPT / 4; ++q) {
+                    qa[q] += qv[r] * lds4(sO + (t + r) * LB + sj + 4 * q);
+                    xa[q] -= yv[r] * lds4(sdU + (t + r) * LB + sj + 4 * q);
+                }
         }
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) sX[sd * PB + sj + j] = fmaf(a.scale, qa[j], xa[j]);
+        for (int q = 0; q < CPT / 4; ++q) sts4(sX + sd * LB + sj + 4 * q, a.scale * qa[q] + xa[q]);
     }
     __syncthreads();
     if (a.dS0)
-        for (int i = tid; i < D * BV; i += NT) {
-            const int d = i / BV, j = i - d * BV;
-            a.dS0[sb + (size_t)d * D + col0 + j] = sX[d * PB + j];
+        for (int i = tid; i < D * BV / 4; i += NT) {
+            const int d = 4 * i / BV, j = 4 * i - d * BV;
+            sts4(a.dS0 + sb + (size_t)d * D + col0 + j, lds4(sX + d * LB + j));
         }
 }
 
@@ -393,41 +565,57 @@ __global__ __launch_bounds__(NT) void cb_bsweep(ChunkBwdArgs a) {
 //    products with S and dS_next.
 template <typename IO, int D>
 __global__ __launch_bounds__(NT) void cb_grad_s(ChunkBwdArgs a) {
-    constexpr int PD = D + 1;
+    constexpr int LD = Cfg<D>::LD, NL = Cfg<D>::NL, R0 = C * C > 32 * LD ? C * C : 32 * LD;
+    constexpr int NB = 32 * D / (4 * NT), NTT = C * C / (4 * NT);
     extern __shared__ __align__(16) float smem[];
-    float *sT = smem, *sX = sT + C * PC, *sU = sX + C * PD, *sO = sU + C * PD, *sB = sO + C * PD;
+    float *sT = smem;  // T^T, row stride C; later 32 rows of S
+    float *sX = sT + R0, *sU = sX + C * LD, *sO = sU + C * LD, *sB = sO + C * LD;
     const int tid = threadIdx.x, u = blockIdx.x;
     const Unit x = decode(a, u);
     const size_t ucd = (size_t)u * C * D, ucc = (size_t)u * C * C, udd = (size_t)u * D * D;
-    for (int i = tid; i < C * C; i += NT) {
-        const int t = i / C, j = i - t * C;
-        sT[t * PC + j] = a.wT[ucc + i];
-    }
-    for (int i = tid; i < C * D; i += NT) {
-        const int t = i / D, d = i - t * D;
-        sX[t * PD + d] = a.wdU[ucd + i];
-        sU[t * PD + d] = a.wU[ucd + i];
-        sO[t * PD + d] = t < x.n ? ldio<IO>(a.dO, (x.rowv + (size_t)t * a.Hv) * D + d) : 0.f;
-    }
-    __syncthreads();
-    // Rows from the last: dR_i = dU_i - sum_{m > i} T_mi dR_m.
-    if (tid < D) {
-        float *X = sX + tid;
-        for (int i = C - 2; i >= 0; --i) {
-            float p0 = X[i * PD], p1 = 0.f;
-            int m = i + 1;
-            for (; m + 1 < C; m += 2) {
-                p0 = fmaf(-sT[m * PC + i], X[m * PD], p0);
-                p1 = fmaf(-sT[(m + 1) * PC + i], X[(m + 1) * PD], p1);
-            }
-            if (m < C) p0 = fmaf(-sT[m * PC + i], X[m * PD], p0);
-            X[i * PD] = p0 + p1;
+    {
+        f32x4 rX[NL], rU[NL], rO[NL], rT[NTT];
+#pragma unroll
+        for (int l = 0; l < NL; ++l) {
+            int e, t, d;
+            rc<D>(l, e, t, d);
+            rX[l] = lds4(a.wdU + ucd + e);
+            rU[l] = lds4(a.wU + ucd + e);
+            rO[l] = t < x.n ? ld4io<IO>(a.dO, (x.rowv + (size_t)t * a.Hv) * D + d) : zero4();
+        }
+#pragma unroll
+        for (int l = 0; l < NTT; ++l) rT[l] = lds4(a.wT + ucc + 4 * (l * NT + tid));
+#pragma unroll
+        for (int l = 0; l < NL; ++l) {
+            int e, t, d;
+            rc<D>(l, e, t, d);
+            sts4(sX + t * LD + d, rX[l]);
+            sts4(sU + t * LD + d, rU[l]);
+            sts4(sO + t * LD + d, rO[l]);
+        }
+#pragma unroll
+        for (int l = 0; l < NTT; ++l) {
+            const int e = 4 * (l * NT + tid), t = e / C, j = e - t * C;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sT[(j + r) * C + t] = rT[l][r];
         }
     }
     __syncthreads();
-    for (int i = tid; i < C * D; i += NT) {
-        const int t = i / D, d = i - t * D;
-        a.wdU[ucd + i] = sX[t * PD + d];  // dR replaces dU
+    if (tid < D) {  // one column of dU per thread
+        float *X = sX + tid;
+        float xc[C];
+#pragma unroll
+        for (int i = 0; i < C; ++i) xc[i] = X[i * LD];
+        solve_upper(xc, sT);
+#pragma unroll
+        for (int i = 0; i < C; ++i) X[i * LD] = xc[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+        int e, t, d;
+        rc<D>(l, e, t, d);
+        sts4(a.wdU + ucd + e, lds4(sX + t * LD + d));  // dR replaces dU
     }
     {
         const int r0 = (tid >> 4) * 4, c0 = (tid & 15) * 4;
@@ -436,23 +624,25 @@ __global__ __launch_bounds__(NT) void cb_grad_s(ChunkBwdArgs a) {
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) aT[i][j] = aA[i][j] = 0.f;
-        if (c0 <= r0 + 3)
-            for (int v = 0; v < D; ++v) {
-                float x4[4], o4[4], u4[4];
+        if (c0 <= r0 + 3) {
+#pragma unroll 2
+            for (int v = 0; v < D; v += 4) {
+                f32x4 x4[4], o4[4], u4[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    x4[i] = sX[(r0 + i) * PD + v];
-                    o4[i] = sO[(r0 + i) * PD + v];
-                    u4[i] = sU[(c0 + i) * PD + v];
+                    x4[i] = lds4(sX + (r0 + i) * LD + v);
+                    o4[i] = lds4(sO + (r0 + i) * LD + v);
+                    u4[i] = lds4(sU + (c0 + i) * LD + v);
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        aT[i][j] = fmaf(x4[i], u4[j], aT[i][j]);
-                        aA[i][j] = fmaf(o4[i], u4[j], aA[i][j]);
+                        aT[i][j] = dot4(x4[i], u4[j], aT[i][j]);
+                        aA[i][j] = dot4(o4[i], u4[j], aA[i][j]);
                     }
             }
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int t = r0 + i;
@@ -462,8 +652,8 @@ __global__ __launch_bounds__(NT) void cb_grad_s(ChunkBwdArgs a) {
                 dt[j] = c0 + j < t ? -aT[i][j] : 0.f;
                 da[j] = c0 + j <= t ? a.scale * aA[i][j] : 0.f;
             }
-            *reinterpret_cast<f32x4 *>(a.wdT + ucc + (size_t)t * C + c0) = dt;
-            *reinterpret_cast<f32x4 *>(a.wdA + ucc + (size_t)t * C + c0) = da;
+            sts4(a.wdT + ucc + (size_t)t * C + c0, dt);
+            sts4(a.wdA + ucc + (size_t)t * C + c0, da);
         }
     }
     // Products with S, then with dS_next, 32 state rows at a time.
@@ -472,39 +662,50 @@ __global__ __launch_bounds__(NT) void cb_grad_s(ChunkBwdArgs a) {
         for (int blk = 0; blk < D / 32; ++blk) {
             __syncthreads();
             const float *src = (pass == 0 ? a.wS : a.wdS) + udd + (size_t)blk * 32 * D;
-            for (int i = tid; i < 32 * D; i += NT) {
-                const int r = i / D, v = i - r * D;
-                sB[r * PD + v] = src[i];
+            {
+                f32x4 rb[NB], rs[NB];
+#pragma unroll
+                for (int l = 0; l < NB; ++l) {
+                    rb[l] = lds4(src + 4 * (l * NT + tid));
+                    if (pass == 1) rs[l] = lds4(a.wS + udd + (size_t)blk * 32 * D + 4 * (l * NT + tid));
+                }
+#pragma unroll
+                for (int l = 0; l < NB; ++l) {
+                    const int e = 4 * (l * NT + tid), r = e / D, v = e - r * D;
+                    sts4(sB + r * LD + v, rb[l]);
+                    if (pass == 1) sts4(sT + r * LD + v, rs[l]);  // S rows beside dS_next's
+                }
             }
             __syncthreads();
             float p[8], q[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) p[j] = q[j] = 0.f;
-            const float *L0 = (pass == 0 ? sX : sU) + bt * PD;
-            for (int v = 0; v < D; ++v) {
-                const float l0 = L0[v], o0 = sO[bt * PD + v];
+            const float *L0 = (pass == 0 ? sX : sU) + bt * LD;
+#pragma unroll 2
+            for (int v = 0; v < D; v += 4) {
+                const f32x4 l0 = lds4(L0 + v), o0 = lds4(sO + bt * LD + v);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const float sv = sB[(bd + j) * PD + v];
-                    p[j] = fmaf(l0, sv, p[j]);
-                    if (pass == 0) q[j] = fmaf(o0, sv, q[j]);
+                    const f32x4 b4 = lds4(sB + (bd + j) * LD + v);
+                    p[j] = dot4(l0, b4, p[j]);
+                    if (pass == 0) q[j] = dot4(o0, b4, q[j]);
                 }
             }
             const size_t o = ucd + (size_t)bt * D + blk * 32 + bd;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                if (pass == 0) {
-                    a.wdE[o + j] = -p[j];
-                    a.wdQ[o + j] = a.scale * q[j];
-                } else {
-                    a.wdK[o + j] = p[j];
+            if (pass == 0) {
+                sts4(a.wdE + o, -f32x4{p[0], p[1], p[2], p[3]});
+                sts4(a.wdE + o + 4, -f32x4{p[4], p[5], p[6], p[7]});
+                sts4(a.wdQ + o, a.scale * f32x4{q[0], q[1], q[2], q[3]});
+                sts4(a.wdQ + o + 4, a.scale * f32x4{q[4], q[5], q[6], q[7]});
+            } else {
+                sts4(a.wdK + o, f32x4{p[0], p[1], p[2], p[3]});
+                sts4(a.wdK + o + 4, f32x4{p[4], p[5], p[6], p[7]});
+                if (tid < 32) {
+                    float acc = 0.f;
+#pragma unroll 4
+                    for (int v = 0; v < D; v += 4) acc = dot4(lds4(sB + tid * LD + v), lds4(sT + tid * LD + v), acc);
+                    a.wdGam[(size_t)u * D + blk * 32 + tid] = acc;
                 }
-            }
-            if (pass == 1 && tid < 32) {
-                const float *Sr = a.wS + udd + (size_t)(blk * 32 + tid) * D;
-                float acc = 0.f;
-                for (int v = 0; v < D; ++v) acc = fmaf(sB[tid * PD + v], Sr[v], acc);
-                a.wdGam[(size_t)u * D + blk * 32 + tid] = acc;
             }
         }
 }
@@ -514,173 +715,190 @@ __global__ __launch_bounds__(NT) void cb_grad_s(ChunkBwdArgs a) {
 //    gates, and dg.
 template <typename IO, int D, bool CHAN, bool BW>
 __global__ __launch_bounds__(NT) void cb_grad_out(ChunkBwdArgs a) {
-    constexpr int PD = D + 1, CT = D / 16;
+    using K = Cfg<D>;
+    constexpr int LD = K::LD, NL = K::NL, NCG = K::NCG, RT = K::RT, NRG = K::NRG, NTT = C * C / (4 * NT);
     extern __shared__ __align__(16) float smem[];
     float *sP1 = smem;            // e (E~): left factor of T
-    float *sP2 = sP1 + C * PD;    // k (K~): right factor of T and A
-    float *sP3 = sP2 + C * PD;    // q (Q~): left factor of A
-    float *sdT = sP3 + C * PD;    // dT, scaled per entry by exp(G_t - G_j) for a scalar decay; then dG [C][PD]
-    float *sdA = sdT + C * PC;
-    // Reductions go through per-thread partials summed in a fixed order, so
-    // that the result does not depend on the order threads arrive in.
-    float *sRow = sdA + C * PC;    // [C] row sums of dT . T + dA . A (scalar decay)
-    float *sColW = sRow + C;       // [4 waves][C] their column sums
-    float *sCol = sColW + 4 * C;   // [C]
-    float *sTokG = sCol + C;       // [C][16] per-token dG parts of the 16 column groups (scalar decay)
-    float *sTokB = sTokG + 16 * C; // [C][16] per-token dbeta parts (tied gates)
-    float *sGeP = sTokB + 16 * C;  // [16 row groups][D] dG_end parts
-    float *sGe = sGeP + 16 * D;    // [D] dG_end (scalar decay: element 0)
+    float *sP2 = sP1 + C * LD;    // k (K~): right factor of T and A
+    float *sP3 = sP2 + C * LD;    // q (Q~): left factor of A
+    float *sdT = sP3 + C * LD;    // dT, for a scalar decay times exp(G_t - G_j); then dG [C][LD]
+    float *sdA = sdT + C * LC;
+    // Reductions go through per-thread parts summed in a fixed order, so that
+    // the result does not depend on the order threads arrive in.
+    float *sRow = sdA + C * LC;    // [C] row sums of dT . T + dA . A (scalar decay)
+    float *sColP = sRow + C;       // [16][C] their column sums by row group
+    float *sCol = sColP + 16 * C;  // [C]
+    float *sTokG = sCol + C;       // [C][32] per-token dG parts of the column groups (scalar decay)
+    float *sTokB = sTokG + 32 * C; // [C][32] per-token dbeta parts (tied gates)
+    float *sGeP = sTokB + 32 * C;  // [NRG][D] dG_end parts
+    float *sGe = sGeP + 1024;      // [D] dG_end (scalar decay: element 0)
     float *sGt = sdT;
-    static_assert(C * PD <= 2 * C * PC, "dG tile fits where dT and dA were");
+    static_assert(C * LD <= 2 * C * LC && NRG * D <= 1024 && NCG <= 32, "shared-memory layout");
     const int tid = threadIdx.x, u = blockIdx.x;
     const Unit x = decode(a, u);
     const size_t ucd = (size_t)u * C * D, ucc = (size_t)u * C * C;
     const float *wG = a.wG + ucd;
     const bool tied = !BW, grouped = a.Hv > a.Hqk;
-
-    for (int i = tid; i < C * D; i += NT) {
-        const int t = i / D, d = i - t * D;
-        float qv = 0.f, kv = 0.f, ev = 0.f;
-        if (t < x.n) {
-            const size_t iq = (x.rowq + (size_t)t * a.Hqk) * D + d, iv = (x.rowv + (size_t)t * a.Hv) * D + d;
-            qv = ldio<IO>(a.q, iq);
-            kv = ldio<IO>(a.k, iq);
-            ev = (BW ? ldio<IO>(a.bg, iv) : a.beta[x.rowv + (size_t)t * a.Hv]) * kv;
-        }
-        if (CHAN) {
-            const float G = wG[i], eg = expf(G);
-            qv *= eg;
-            ev *= eg;
-            kv *= expf(-G);
-        }
-        sP1[t * PD + d] = ev;
-        sP2[t * PD + d] = kv;
-        sP3[t * PD + d] = qv;
-    }
-    // One wave per row of dT and dA (lane = column; wave w takes rows w, w + 4, ...).
-    float colw = 0.f;
-    for (int i = tid; i < C * C; i += NT) {
-        const int t = i / C, j = i - t * C;
-        float dt = a.wdT[ucc + i], da = a.wdA[ucc + i];
-        if (!CHAN) {
-            float wv = 0.f;
-            if (j <= t) {
-                wv = dt * a.wT[ucc + i] + da * a.wA[ucc + i];
-                const float f = expf(wG[t] - wG[j]);
-                dt *= f;
-                da *= f;
+    {
+        f32x4 rq[NL], rk[NL], re[NL];
+#pragma unroll
+        for (int l = 0; l < NL; ++l) {
+            int e, t, d;
+            rc<D>(l, e, t, d);
+            rq[l] = rk[l] = re[l] = zero4();
+            if (t < x.n) {
+                const size_t iq = (x.rowq + (size_t)t * a.Hqk) * D + d, iv = (x.rowv + (size_t)t * a.Hv) * D + d;
+                rq[l] = ld4io<IO>(a.q, iq);
+                rk[l] = ld4io<IO>(a.k, iq);
+                re[l] = BW ? ld4io<IO>(a.bg, iv) : splat(a.beta[x.rowv + (size_t)t * a.Hv]);
             }
-            colw += wv;
-            wv = wave_sum(wv);
-            if (j == 0) sRow[t] = wv;
         }
-        sdT[t * PC + j] = dt;
-        sdA[t * PC + j] = da;
+#pragma unroll
+        for (int l = 0; l < NL; ++l) {
+            int e, t, d;
+            rc<D>(l, e, t, d);
+            f32x4 ev = re[l] * rk[l], kv = rk[l], qv = rq[l];
+            if (CHAN) {
+                const f32x4 G = lds4(wG + e), eg = exp4(G);
+                qv *= eg;
+                ev *= eg;
+                kv *= exp4(-G);
+            }
+            sts4(sP1 + t * LD + d, ev);
+            sts4(sP2 + t * LD + d, kv);
+            sts4(sP3 + t * LD + d, qv);
+        }
     }
-    if (!CHAN) sColW[(tid >> 6) * C + (tid & 63)] = colw;
+    {
+        // Thread: 4 consecutive columns j of rows t = 16 l + tid / 16; the 16
+        // threads of a row are 16 consecutive lanes.
+        f32x4 colw = zero4();
+#pragma unroll
+        for (int l = 0; l < NTT; ++l) {
+            const int e = 4 * (l * NT + tid), t = e / C, j = e - t * C;
+            f32x4 dt = lds4(a.wdT + ucc + e), da = lds4(a.wdA + ucc + e);
+            if (!CHAN) {
+                const f32x4 tt = lds4(a.wT + ucc + e), aa = lds4(a.wA + ucc + e);
+                float wrow = 0.f;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float wv = 0.f;
+                    if (j + r <= t) {
+                        wv = dt[r] * tt[r] + da[r] * aa[r];
+                        const float f = expf(wG[t] - wG[j + r]);
+                        dt[r] *= f;
+                        da[r] *= f;
+                    }
+                    colw[r] += wv;
+                    wrow += wv;
+                }
+#pragma unroll
+                for (int off = 1; off < 16; off <<= 1) wrow += __shfl_xor(wrow, off);
+                if ((tid & 15) == 0) sRow[t] = wrow;
+            }
+            sts4(sdT + t * LC + j, dt);
+            sts4(sdA + t * LC + j, da);
+        }
+        if (!CHAN) sts4(sColP + (tid >> 4) * C + 4 * (tid & 15), colw);
+    }
     __syncthreads();
-    if (!CHAN && tid < C) sCol[tid] = sColW[tid] + sColW[C + tid] + sColW[2 * C + tid] + sColW[3 * C + tid];
-    // X_e = dT' P2, X_q = dA' P2, X_k = dT'^T P1 + dA'^T P3; thread = rows m0..m0+3, columns n0..n0+CT-1.
-    const int m0 = (tid >> 4) * 4, n0 = (tid & 15) * CT;
-    float xe[4][CT], xq[4][CT], xk[4][CT];
+    if (!CHAN && tid < C) {
+        float cs = 0.f;
+        for (int r = 0; r < 16; ++r) cs += sColP[r * C + tid];
+        sCol[tid] = cs;
+    }
+    // X_e = dT' P2, X_q = dA' P2, X_k = dT'^T P1 + dA'^T P3; thread = rows m0..m0+RT-1, columns n0..n0+3.
+    const int cg = tid % NCG, rg = tid / NCG, m0 = rg * RT, n0 = 4 * cg;
+    f32x4 xe[RT], xq[RT], xk[RT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < RT; ++i) xe[i] = xq[i] = xk[i] = zero4();
+#pragma unroll 2
+    for (int j = 0; j < C; j += 4) {
+        f32x4 dt4[RT], da4[RT];
 #pragma unroll
-        for (int c = 0; c < CT; ++c) xe[i][c] = xq[i][c] = xk[i][c] = 0.f;
-    for (int j = 0; j < C; ++j) {
-        float dt4[4], da4[4], tt4[4], ta4[4], p1[CT], p2[CT], p3[CT];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            dt4[i] = sdT[(m0 + i) * PC + j];
-            da4[i] = sdA[(m0 + i) * PC + j];
-            tt4[i] = sdT[j * PC + m0 + i];
-            ta4[i] = sdA[j * PC + m0 + i];
+        for (int i = 0; i < RT; ++i) {
+            dt4[i] = lds4(sdT + (m0 + i) * LC + j);
+            da4[i] = lds4(sdA + (m0 + i) * LC + j);
         }
 #pragma unroll
-        for (int c = 0; c < CT; ++c) {
-            p1[c] = sP1[j * PD + n0 + c];
-            p2[c] = sP2[j * PD + n0 + c];
-            p3[c] = sP3[j * PD + n0 + c];
-        }
+        for (int r = 0; r < 4; ++r) {
+            const int jj = j + r;
+            const f32x4 p1 = lds4(sP1 + jj * LD + n0), p2 = lds4(sP2 + jj * LD + n0), p3 = lds4(sP3 + jj * LD + n0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int c = 0; c < CT; ++c) {
-                xe[i][c] = fmaf(dt4[i], p2[c], xe[i][c]);
-                xq[i][c] = fmaf(da4[i], p2[c], xq[i][c]);
-                xk[i][c] = fmaf(ta4[i], p3[c], fmaf(tt4[i], p1[c], xk[i][c]));
+            for (int i = 0; i < RT; ++i) {
+                const float tt = sdT[jj * LC + m0 + i], ta = sdA[jj * LC + m0 + i];
+                xe[i] += dt4[i][r] * p2;
+                xq[i] += da4[i][r] * p2;
+                xk[i] += tt * p1 + ta * p3;
             }
+        }
     }
     __syncthreads();  // dT and dA read: their space holds dG from here
 
-    float gend[CT];
+    f32x4 gend = zero4();
 #pragma unroll
-    for (int c = 0; c < CT; ++c) gend[c] = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < RT; ++i) {
         const int t = m0 + i;
         float dgs = 0.f, dbs = 0.f;
         if (t < x.n) {
-            const size_t iq = (x.rowq + (size_t)t * a.Hqk) * D, iv = (x.rowv + (size_t)t * a.Hv) * D;
+            const size_t iq = (x.rowq + (size_t)t * a.Hqk) * D + n0, iv = (x.rowv + (size_t)t * a.Hv) * D + n0;
+            const size_t o = ucd + (size_t)t * D + n0;
             const float bt = tied ? a.beta[x.rowv + (size_t)t * a.Hv] : 0.f;
-#pragma unroll
-            for (int c = 0; c < CT; ++c) {
-                const int d = n0 + c;
-                const float G = CHAN ? wG[t * D + d] : wG[t], Ge = CHAN ? wG[(C - 1) * D + d] : wG[C - 1];
-                const float eg = expf(G), egend = expf(Ge - G);
-                const float qv = ldio<IO>(a.q, iq + d), kv = ldio<IO>(a.k, iq + d), vv = ldio<IO>(a.v, iv + d);
-                const float gb = BW ? ldio<IO>(a.bg, iv + d) : bt, gw = BW ? ldio<IO>(a.wg, iv + d) : bt;
-                const size_t o = ucd + (size_t)t * D + d;
-                const float dEY = a.wdE[o], dQS = a.wdQ[o], dKE = a.wdK[o], dR = a.wdU[o];
-                const float de = (CHAN ? xe[i][c] * eg : xe[i][c]) + dEY * eg;
-                const float dq = (CHAN ? xq[i][c] * eg : xq[i][c]) + dQS * eg;
-                float dk = (CHAN ? xk[i][c] * expf(-G) : xk[i][c]) + dKE * egend;
-                const float ke = kv * egend;
-                float dG = gb * kv * eg * dEY + qv * eg * dQS - ke * dKE;
-                if (CHAN) dG += sP1[t * PD + d] * xe[i][c] - sP2[t * PD + d] * xk[i][c] + sP3[t * PD + d] * xq[i][c];
-                gend[c] += ke * dKE;
-                if (CHAN) sGt[t * PD + d] = dG;
-                else dgs += dG;
-                dk = fmaf(gb, de, dk);
-                if (BW) {
-                    a.db[iv + d] = de * kv;
-                    a.dw[iv + d] = dR * vv;
-                } else {
-                    dbs += de * kv + dR * vv;
-                }
-                a.dv[iv + d] = gw * dR;
-                if (grouped) {
-                    a.wdq[iv + d] = dq;
-                    a.wdk[iv + d] = dk;
-                } else {
-                    a.dq[iq + d] = dq;
-                    a.dk[iq + d] = dk;
-                }
+            const f32x4 G = CHAN ? lds4(wG + t * D + n0) : splat(wG[t]);
+            const f32x4 Ge = CHAN ? lds4(wG + (C - 1) * D + n0) : splat(wG[C - 1]);
+            const f32x4 eg = exp4(G), egend = exp4(Ge - G);
+            const f32x4 qv = ld4io<IO>(a.q, iq), kv = ld4io<IO>(a.k, iq), vv = ld4io<IO>(a.v, iv);
+            const f32x4 gb = BW ? ld4io<IO>(a.bg, iv) : splat(bt), gw = BW ? ld4io<IO>(a.wg, iv) : splat(bt);
+            const f32x4 dEY = lds4(a.wdE + o), dQS = lds4(a.wdQ + o), dKE = lds4(a.wdK + o), dR = lds4(a.wdU + o);
+            const f32x4 de = (CHAN ? xe[i] * eg : xe[i]) + dEY * eg;
+            const f32x4 dq = (CHAN ? xq[i] * eg : xq[i]) + dQS * eg;
+            const f32x4 ke = kv * egend;
+            f32x4 dk = (CHAN ? xk[i] * exp4(-G) : xk[i]) + dKE * egend;
+            f32x4 dG = gb * kv * eg * dEY + qv * eg * dQS - ke * dKE;
+            if (CHAN)
+                dG += lds4(sP1 + t * LD + n0) * xe[i] - lds4(sP2 + t * LD + n0) * xk[i] +
+                      lds4(sP3 + t * LD + n0) * xq[i];
+            gend += ke * dKE;
+            if (CHAN) sts4(sGt + t * LD + n0, dG);
+            else dgs = dG[0] + dG[1] + dG[2] + dG[3];
+            dk += gb * de;
+            if (BW) {
+                sts4(a.db + iv, de * kv);
+                sts4(a.dw + iv, dR * vv);
+            } else {
+                const f32x4 pb = de * kv + dR * vv;
+                dbs = pb[0] + pb[1] + pb[2] + pb[3];
             }
+            sts4(a.dv + iv, gw * dR);
+            if (grouped) {
+                sts4(a.wdq + iv, dq);
+                sts4(a.wdk + iv, dk);
+            } else {
+                sts4(a.dq + iq, dq);
+                sts4(a.dk + iq, dk);
+            }
+        } else if (CHAN) {
+            sts4(sGt + t * LD + n0, zero4());  // padded token
         }
-        else if (CHAN)
-#pragma unroll
-            for (int c = 0; c < CT; ++c) sGt[t * PD + n0 + c] = 0.f;  // padded token
-        sTokG[t * 16 + (tid & 15)] = dgs;
-        sTokB[t * 16 + (tid & 15)] = dbs;
+        sTokG[t * 32 + cg] = dgs;
+        sTokB[t * 32 + cg] = dbs;
     }
-#pragma unroll
-    for (int c = 0; c < CT; ++c) sGeP[(tid >> 4) * D + n0 + c] = gend[c];
+    sts4(sGeP + rg * D + n0, gend);
     __syncthreads();
     // dG_end = sum over the chunk of Kend . dKend, plus Gamma . dGamma.
     if (tid < D) {
         float g = a.wGam[(size_t)u * D + tid] * a.wdGam[(size_t)u * D + tid];
-        for (int r = 0; r < 16; ++r) g += sGeP[r * D + tid];
+        for (int r = 0; r < NRG; ++r) g += sGeP[r * D + tid];
         sGe[tid] = g;
     }
     if (tid < C) {
         float g = 0.f, bsum = 0.f;
-        for (int r = 0; r < 16; ++r) {
-            g += sTokG[tid * 16 + r];
-            bsum += sTokB[tid * 16 + r];
+        for (int r = 0; r < NCG; ++r) {
+            g += sTokG[tid * 32 + r];
+            bsum += sTokB[tid * 32 + r];
         }
-        sTokG[tid * 16] = g;
-        sTokB[tid * 16] = bsum;
+        sTokG[tid * 32] = g;
+        sTokB[tid * 32] = bsum;
     }
     __syncthreads();
     if (!CHAN && tid == 0) {
@@ -694,13 +912,13 @@ __global__ __launch_bounds__(NT) void cb_grad_out(ChunkBwdArgs a) {
             if (tid < D) {
                 float acc = sGe[tid];
                 for (int t = C - 1; t >= 0; --t) {
-                    acc += sGt[t * PD + tid];
+                    acc += sGt[t * LD + tid];
                     if (t < x.n) a.dg[(x.rowv + (size_t)t * a.Hv) * D + tid] = acc;
                 }
             }
         } else if (tid < 64) {
             // Suffix sums over the chunk's tokens; lane = token.
-            float v = sTokG[tid * 16] + sRow[tid] - sCol[tid];
+            float v = sTokG[tid * 32] + sRow[tid] - sCol[tid];
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const float y = __shfl_down(v, off);
@@ -709,50 +927,53 @@ __global__ __launch_bounds__(NT) void cb_grad_out(ChunkBwdArgs a) {
             if (tid < x.n) a.dg[x.rowv + (size_t)tid * a.Hv] = v + sGe[0];
         }
     }
-    if (tied && tid < x.n) a.dbeta[x.rowv + (size_t)tid * a.Hv] = sTokB[tid * 16];
+    if (tied && tid < x.n) a.dbeta[x.rowv + (size_t)tid * a.Hv] = sTokB[tid * 32];
 }
 
 // dq, dk of a QK head: the sum of its V heads' parts.
 template <int D>
 __global__ __launch_bounds__(NT) void cb_group_sum(ChunkBwdArgs a) {
     const int grp = a.Hv / a.Hqk;
-    const size_t n = (size_t)a.B * a.T * a.Hqk * D;
-    for (size_t i = (size_t)blockIdx.x * NT + threadIdx.x; i < n; i += (size_t)gridDim.x * NT) {
-        const size_t d = i % D, r = i / D, hq = r % a.Hqk, bt = r / a.Hqk;
+    const size_t n4 = (size_t)a.B * a.T * a.Hqk * D / 4;
+    for (size_t i = (size_t)blockIdx.x * NT + threadIdx.x; i < n4; i += (size_t)gridDim.x * NT) {
+        const size_t e = 4 * i, d = e % D, r = e / D, hq = r % a.Hqk, bt = r / a.Hqk;
         const size_t base = (bt * a.Hv + hq * grp) * D + d;
-        float sq = 0.f, sk = 0.f;
+        f32x4 sq = zero4(), sk = zero4();
         for (int j = 0; j < grp; ++j) {
-            sq += a.wdq[base + (size_t)j * D];
-            sk += a.wdk[base + (size_t)j * D];
+            sq += lds4(a.wdq + base + (size_t)j * D);
+            sk += lds4(a.wdk + base + (size_t)j * D);
         }
-        a.dq[i] = sq;
-        a.dk[i] = sk;
+        sts4(a.dq + e, sq);
+        sts4(a.dk + e, sk);
     }
 }
 
 template <typename IO, int D, bool CHAN, bool BW>
 hipError_t run(const ChunkBwdArgs &a, hipStream_t s) {
     static const hipError_t attr = [] {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&cb_prep<IO, D, CHAN, BW>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)prep_smem<D>());
-        if (e == hipSuccess)
-            e = hipFuncSetAttribute(reinterpret_cast<const void *>(&cb_grad_s<IO, D>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)grad_s_smem<D>());
-        if (e == hipSuccess)
-            e = hipFuncSetAttribute(reinterpret_cast<const void *>(&cb_grad_out<IO, D, CHAN, BW>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)grad_out_smem<D>());
-        return e;
+        const void *fn[5] = {reinterpret_cast<const void *>(&cb_prep<IO, D, CHAN, BW>),
+                             reinterpret_cast<const void *>(&cb_fsweep<D>),
+                             reinterpret_cast<const void *>(&cb_bsweep<IO, D>),
+                             reinterpret_cast<const void *>(&cb_grad_s<IO, D>),
+                             reinterpret_cast<const void *>(&cb_grad_out<IO, D, CHAN, BW>)};
+        const size_t bytes[5] = {prep_smem<D>(), fsweep_smem<D>(), bsweep_smem<D>(), grad_s_smem<D>(),
+                                 grad_out_smem<D>()};
+        for (int i = 0; i < 5; ++i) {
+            const hipError_t e = hipFuncSetAttribute(fn[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes[i]);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
     }();
     if (attr != hipSuccess) return attr;
     const unsigned units = (unsigned)((size_t)a.B * a.Hv * a.NC), items = (unsigned)((size_t)a.B * a.Hv * (D / BV));
     hipLaunchKernelGGL((cb_prep<IO, D, CHAN, BW>), dim3(units), dim3(NT), prep_smem<D>(), s, a);
-    hipLaunchKernelGGL((cb_fsweep<D>), dim3(items), dim3(NT), 0, s, a);
-    hipLaunchKernelGGL((cb_bsweep<IO, D>), dim3(items), dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((cb_fsweep<D>), dim3(items), dim3(NT), fsweep_smem<D>(), s, a);
+    hipLaunchKernelGGL((cb_bsweep<IO, D>), dim3(items), dim3(NT), bsweep_smem<D>(), s, a);
     hipLaunchKernelGGL((cb_grad_s<IO, D>), dim3(units), dim3(NT), grad_s_smem<D>(), s, a);
     hipLaunchKernelGGL((cb_grad_out<IO, D, CHAN, BW>), dim3(units), dim3(NT), grad_out_smem<D>(), s, a);
     if (a.Hv > a.Hqk) {
-        const size_t n = (size_t)a.B * a.T * a.Hqk * D;
-        const size_t blocks = (n + NT - 1) / NT;
+        const size_t n4 = (size_t)a.B * a.T * a.Hqk * D / 4;
+        const size_t blocks = (n4 + NT - 1) / NT;
         hipLaunchKernelGGL((cb_group_sum<D>), dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(NT), 0, s, a);
     }
     return hipGetLastError();
