@@ -103,6 +103,15 @@ __device__ __forceinline__ void rc(int l, int &e, int &t, int &d) {
     d = e - t * D;
 }
 
+// Workgroup barrier ordering shared-memory accesses only: it does not wait
+// for global loads in flight (the sweeps' prefetch of the next chunk) or
+// for global stores, which nothing in the same launch reads back.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
@@ -377,7 +386,7 @@ __global__ __launch_bounds__(NT) void cb_fsweep(ChunkBwdArgs a) {
     fetch(0);
     for (int c = 0; c < a.NC; ++c) {
         const size_t u = (size_t)bh * a.NC + c, ucd = u * C * D;
-        __syncthreads();  // the previous chunk is done with the operand tiles; S written
+        lds_barrier();  // the previous chunk is done with the operand tiles; S written
 #pragma unroll
         for (int l = 0; l < NL; ++l) {
             int e, t, d;
@@ -393,14 +402,22 @@ __global__ __launch_bounds__(NT) void cb_fsweep(ChunkBwdArgs a) {
             const int d = 4 * i / BV, j = 4 * i - d * BV;
             sts4(a.wS + u * D * D + (size_t)d * D + col0 + j, lds4(sS + d * LB + j));
         }
-        __syncthreads();
-#pragma unroll 4
-        for (int d = 0; d < D; d += 4) {
-            const f32x4 y = lds4(sY + ut * LD + d);
+        lds_barrier();
+        // Operands of 8 rows of S at a time are read before they are used.
+#pragma unroll 1
+        for (int d = 0; d < D; d += 8) {
+            const f32x4 y0 = lds4(sY + ut * LD + d), y1 = lds4(sY + ut * LD + d + 4);
+            f32x4 s0[8], s1[8];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                acc0 -= y[r] * lds4(sS + (d + r) * LB + uj);
-                acc1 -= y[r] * lds4(sS + (d + r) * LB + uj + 4);
+            for (int r = 0; r < 8; ++r) {
+                s0[r] = lds4(sS + (d + r) * LB + uj);
+                s1[r] = lds4(sS + (d + r) * LB + uj + 4);
+            }
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const float yv = r < 4 ? y0[r & 3] : y1[r & 3];
+                acc0 -= yv * s0[r];
+                acc1 -= yv * s1[r];
             }
         }
         sts4(sU + ut * LB + uj, acc0);
@@ -408,19 +425,24 @@ __global__ __launch_bounds__(NT) void cb_fsweep(ChunkBwdArgs a) {
         float *wu = a.wU + ucd + (size_t)ut * D + col0 + uj;
         sts4(wu, acc0);
         sts4(wu + 4, acc1);
-        __syncthreads();
+        lds_barrier();
         f32x4 sv[CPT / 4];
 #pragma unroll
         for (int q = 0; q < CPT / 4; ++q) sv[q] = gam * lds4(sS + sd * LB + sj + 4 * q);
-#pragma unroll 4
+#pragma unroll 1
         for (int t = 0; t < C; t += 4) {
             const f32x4 kv = lds4(sKt + sd * LC + t);
+            f32x4 uu[4][CPT / 4];
 #pragma unroll
             for (int r = 0; r < 4; ++r)
 #pragma unroll
-                for (int q = 0; q < CPT / 4; ++q) sv[q] += kv[r] * lds4(sU + (t + r) * LB + sj + 4 * q);
+                for (int q = 0; q < CPT / 4; ++q) uu[r][q] = lds4(sU + (t + r) * LB + sj + 4 * q);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int q = 0; q < CPT / 4; ++q) sv[q] += kv[r] * uu[r][q];
         }
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int q = 0; q < CPT / 4; ++q) sts4(sS + sd * LB + sj + 4 * q, sv[q]);
     }
@@ -473,7 +495,7 @@ __global__ __launch_bounds__(NT) void cb_bsweep(ChunkBwdArgs a) {
     fetch(a.NC - 1);
     for (int c = a.NC - 1; c >= 0; --c) {
         const size_t u = (size_t)bh * a.NC + c, ucd = u * C * D;
-        __syncthreads();  // X written; the previous chunk is done with the operand tiles
+        lds_barrier();  // X written; the previous chunk is done with the operand tiles
 #pragma unroll
         for (int l = 0; l < NL; ++l) {
             int e, t, d;
@@ -502,25 +524,39 @@ __global__ __launch_bounds__(NT) void cb_bsweep(ChunkBwdArgs a) {
             const int d = 4 * i / BV, j = 4 * i - d * BV;
             sts4(a.wdS + u * D * D + (size_t)d * D + col0 + j, lds4(sX + d * LB + j));
         }
-        __syncthreads();
+        lds_barrier();
         // dU (row ut) = s (A^T dO)_ut + Kend_ut X
         f32x4 p0 = zero4(), p1 = zero4(), k0 = zero4(), k1 = zero4();
-#pragma unroll 4
-        for (int t = 0; t < C; t += 4) {
-            const f32x4 av = lds4(sAt + ut * LC + t);
+#pragma unroll 1
+        for (int t = 0; t < C; t += 8) {
+            const f32x4 a0 = lds4(sAt + ut * LC + t), a1 = lds4(sAt + ut * LC + t + 4);
+            f32x4 o0[8], o1[8];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                p0 += av[r] * lds4(sO + (t + r) * LB + uj);
-                p1 += av[r] * lds4(sO + (t + r) * LB + uj + 4);
+            for (int r = 0; r < 8; ++r) {
+                o0[r] = lds4(sO + (t + r) * LB + uj);
+                o1[r] = lds4(sO + (t + r) * LB + uj + 4);
+            }
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const float av = r < 4 ? a0[r & 3] : a1[r & 3];
+                p0 += av * o0[r];
+                p1 += av * o1[r];
             }
         }
-#pragma unroll 4
-        for (int d = 0; d < D; d += 4) {
-            const f32x4 kv = lds4(sK + ut * LD + d);
+#pragma unroll 1
+        for (int d = 0; d < D; d += 8) {
+            const f32x4 c0 = lds4(sK + ut * LD + d), c1 = lds4(sK + ut * LD + d + 4);
+            f32x4 x0[8], x1[8];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                k0 += kv[r] * lds4(sX + (d + r) * LB + uj);
-                k1 += kv[r] * lds4(sX + (d + r) * LB + uj + 4);
+            for (int r = 0; r < 8; ++r) {
+                x0[r] = lds4(sX + (d + r) * LB + uj);
+                x1[r] = lds4(sX + (d + r) * LB + uj + 4);
+            }
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const float kv = r < 4 ? c0[r & 3] : c1[r & 3];
+                k0 += kv * x0[r];
+                k1 += kv * x1[r];
             }
         }
         const f32x4 du0 = a.scale * p0 + k0, du1 = a.scale * p1 + k1;
@@ -529,7 +565,7 @@ __global__ __launch_bounds__(NT) void cb_bsweep(ChunkBwdArgs a) {
         float *wd = a.wdU + ucd + (size_t)ut * D + col0 + uj;
         sts4(wd, du0);
         sts4(wd + 4, du1);
-        __syncthreads();
+        lds_barrier();
         // X (row sd) = Gamma_sd X + s Q~^T dO - Y^T dU
         f32x4 xa[CPT / 4], qa[CPT / 4];
 #pragma unroll
@@ -537,22 +573,30 @@ __global__ __launch_bounds__(NT) void cb_bsweep(ChunkBwdArgs a) {
             xa[q] = gam * lds4(sX + sd * LB + sj + 4 * q);
             qa[q] = zero4();
         }
-#pragma unroll 4
+#pragma unroll 1
         for (int t = 0; t < C; t += 4) {
             const f32x4 qv = lds4(sQt + sd * LC + t), yv = lds4(sYt + sd * LC + t);
+            f32x4 oo[4][CPT / 4], uu[4][CPT / 4];
 #pragma unroll
             for (int r = 0; r < 4; ++r)
 #pragma unroll
                 for (int q = 0; q < CPT / 4; ++q) {
-                    qa[q] += qv[r] * lds4(sO + (t + r) * LB + sj + 4 * q);
-                    xa[q] -= yv[r] * lds4(sdU + (t + r) * LB + sj + 4 * q);
+                    oo[r][q] = lds4(sO + (t + r) * LB + sj + 4 * q);
+                    uu[r][q] = lds4(sdU + (t + r) * LB + sj + 4 * q);
+                }
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int q = 0; q < CPT / 4; ++q) {
+                    qa[q] += qv[r] * oo[r][q];
+                    xa[q] -= yv[r] * uu[r][q];
                 }
         }
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int q = 0; q < CPT / 4; ++q) sts4(sX + sd * LB + sj + 4 * q, a.scale * qa[q] + xa[q]);
     }
-    __syncthreads();
+    lds_barrier();
     if (a.dS0)
         for (int i = tid; i < D * BV / 4; i += NT) {
             const int d = 4 * i / BV, j = 4 * i - d * BV;
