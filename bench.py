@@ -130,6 +130,16 @@ def backward_algorithmic(wl):
     return reads + writes, 16 * B * T * Hv * D * D
 
 
+def chunk_backward_flops(wl, C=64):
+    """Flops of one gdr_chunk_bwd call, the chunked form's dense products
+    counted once (triangular ones at half): per chunk unit 8 C D^2 + 6 C^2 D
+    multiply-adds (the factors' products and solve, both sweeps over chunks,
+    the gradient products); elementwise work is not counted."""
+    D = wl.dk
+    units = wl.B * wl.Hv * -(-wl.T // C)
+    return 2 * units * (8 * C * D * D + 6 * C * C * D)
+
+
 def cpu_baseline(wl, inp, heads, min_seconds=10.0, max_reps=200):
     """Time the fp64 oracle (as it stands) on the given V heads of the prefill
     workload, repeating the run until about min_seconds of CPU work."""
@@ -162,7 +172,7 @@ def main(argv=None):
     ap.add_argument("--recurrent-T", type=int, default=4,
                     help="tokens per sequence of the multi-token recurrent call timed at the decode shape (0 = skip)")
     ap.add_argument("--backward", type=int, default=1,
-                    help="also time gdr_recurrent_bwd on the prefill workload (0 = skip)")
+                    help="also time gdr_chunk_bwd and gdr_recurrent_bwd on the prefill workload (0 = skip)")
     ap.add_argument("--workload", default="qwen_gdn_prefill",
                     choices=["qwen_gdn_prefill", "kda_prefill", "gdn2_prefill", "gdn_small_f32"],
                     help="prefill workload of the timed step (default: the Qwen-shaped GDN layer, T=4096)")
@@ -326,37 +336,53 @@ def main(argv=None):
         bdesc = gdr.make_desc(wl.B, wl.T, wl.Hqk, wl.Hv, wl.dk, gdr.GDR_BF16 if wl.io == "bf16" else gdr.GDR_F32,
                               {"none": gdr.GDR_DECAY_NONE, "scalar": gdr.GDR_DECAY_SCALAR,
                                "channel": gdr.GDR_DECAY_CHANNEL}[wl.decay], wl.scale)
-        bws = torch.empty(gdr.gdr_recurrent_bwd_workspace_bytes(bdesc), dtype=torch.uint8, device=dev)
 
-        def backward():
-            gdr.gdr_recurrent_bwd(d["q"], d["k"], d["v"], do_d, g=d["g"], beta=d["beta"], b=d["b"], w=d["w"],
-                                  dST=dST_d, scale=wl.scale, workspace=bws, stream=cur())
+        def time_backward(fn, ws):
+            def call():
+                fn(d["q"], d["k"], d["v"], do_d, g=d["g"], beta=d["beta"], b=d["b"], w=d["w"], dST=dST_d,
+                   scale=wl.scale, workspace=ws, stream=cur())
 
-        backward()
-        torch.cuda.synchronize()
-        n_b = max(2, min(args.steps, 10))
-        bgraph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(bgraph):
-            for _ in range(n_b):
-                backward()
-        settle(bgraph.replay)
-        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        b0.record(cur())
-        bgraph.replay()
-        b1.record(cur())
-        torch.cuda.synchronize()
-        del bgraph
-        b_ms = b0.elapsed_time(b1) / n_b
-        b_bytes, b_flops = backward_algorithmic(wl)
-        bwd = {"entry": "gdr_recurrent_bwd", "workload": wl.name, "calls": n_b, "launch": "hip_graph",
+            call()
+            torch.cuda.synchronize()
+            n_b = max(2, min(args.steps, 10))
+            bgraph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(bgraph):
+                for _ in range(n_b):
+                    call()
+            settle(bgraph.replay)
+            b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            b0.record(cur())
+            bgraph.replay()
+            b1.record(cur())
+            torch.cuda.synchronize()
+            del bgraph
+            return b0.elapsed_time(b1) / n_b, n_b
+
+        b_bytes, r_flops = backward_algorithmic(wl)
+        c_flops = chunk_backward_flops(wl)
+        bws = torch.empty(gdr.gdr_chunk_bwd_workspace_bytes(bdesc), dtype=torch.uint8, device=dev)
+        b_ms, n_b = time_backward(gdr.gdr_chunk_bwd, bws)
+        del bws
+        rws = torch.empty(gdr.gdr_recurrent_bwd_workspace_bytes(bdesc), dtype=torch.uint8, device=dev)
+        r_ms, _ = time_backward(gdr.gdr_recurrent_bwd, rws)
+        del rws
+        bwd = {"entry": "gdr_chunk_bwd", "workload": wl.name, "calls": n_b, "launch": "hip_graph",
                "ms_per_call": b_ms, "tokens_per_s": wl.B * wl.T / (b_ms * 1e-3),
-               "roofline": {"kernel": "bwd_ckpt_kernel + bwd_kernel + bwd_reduce_kernel", "bound": "alu",
-                            "achieved": b_flops / (b_ms * 1e-3) / 1e12, "peak": FP32_VECTOR_PEAK_TFLOPS,
-                            "unit": "TFLOP/s", "frac": b_flops / (b_ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
-                            "algorithmic_flops": b_flops},
+               "roofline": {"kernel": "cb_prep + cb_fsweep + cb_bsweep + cb_grad_s + cb_grad_out (+ cb_group_sum)",
+                            "bound": "alu", "achieved": c_flops / (b_ms * 1e-3) / 1e12,
+                            "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                            "frac": c_flops / (b_ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
+                            "algorithmic_flops": c_flops},
                "hbm": {"achieved": b_bytes / (b_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                       "frac": b_bytes / (b_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, "algorithmic_bytes": b_bytes}}
-        del bws, do_d, dST_d
+                       "frac": b_bytes / (b_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, "algorithmic_bytes": b_bytes},
+               "recurrent": {"entry": "gdr_recurrent_bwd", "ms_per_call": r_ms,
+                             "tokens_per_s": wl.B * wl.T / (r_ms * 1e-3),
+                             "roofline": {"kernel": "bwd_ckpt_kernel + bwd_kernel + bwd_reduce_kernel",
+                                          "bound": "alu", "achieved": r_flops / (r_ms * 1e-3) / 1e12,
+                                          "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                          "frac": r_flops / (r_ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
+                                          "algorithmic_flops": r_flops}}}
+        del do_d, dST_d
 
     # ---- decode ----
     dec = None
