@@ -58,6 +58,22 @@ constexpr int BV = 32;      // value columns per sweep workgroup
 constexpr int LB = BV + 4;  // row stride of 32-column tiles
 constexpr int LC = C + 4;   // row stride of 64-column tiles
 
+constexpr int NS = 512;  // threads per sweep workgroup (two waves per SIMD)
+template <int D>
+struct SwCfg {
+    static constexpr int NL = C * D / (4 * NS);  // 4-element groups per thread of a C x D array
+    // State rows: threads per row and columns each (at least 4 columns; with
+    // d = 32 only the first D * TPR threads hold state rows).
+    static constexpr int NTL = D / BV, TPR = NS / D < BV / 4 ? NS / D : BV / 4, CPT = BV / TPR;
+};
+// Element e (a multiple of 4) of a row-major array with W columns, group l of this sweep thread.
+template <int W>
+__device__ __forceinline__ void rcs(int l, int &e, int &t, int &d) {
+    e = 4 * (l * NS + (int)threadIdx.x);
+    t = e / W;
+    d = e - t * W;
+}
+
 template <int D>
 struct Cfg {
     static constexpr int LD = D + 4;              // row stride of D-column tiles
@@ -353,34 +369,34 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
 // chunk, so that the loop reads its operands from shared memory.
 
 // 2. Forward over chunks: the state entering each chunk, and U = U_z - Y S.
+//    Thread: U row ut, columns uj..uj+3; state row sd, columns sj..sj+CPT-1.
 template <int D>
-__global__ __launch_bounds__(NT) void cb_fsweep(ChunkBwdArgs a) {
-    using K = Cfg<D>;
-    constexpr int NTL = K::NTL, TPR = K::TPR, CPT = K::CPT, LD = K::LD, NL = K::NL;
+__global__ __launch_bounds__(NS) void cb_fsweep(ChunkBwdArgs a) {
+    using K = SwCfg<D>;
+    constexpr int NTL = K::NTL, TPR = K::TPR, CPT = K::CPT, NL = K::NL, LD = D + 4;
     extern __shared__ __align__(16) float smem[];
     float *sS = smem, *sU = sS + D * LB, *sY = sU + C * LB, *sKt = sY + C * LD;  // Kend transposed: [D][LC]
     const int tid = threadIdx.x, tile = blockIdx.x % NTL, bh = blockIdx.x / NTL, col0 = tile * BV;
     const size_t sb = (size_t)bh * D * D;
-    for (int i = tid; i < D * BV / 4; i += NT) {
+    for (int i = tid; i < D * BV / 4; i += NS) {
         const int d = 4 * i / BV, j = 4 * i - d * BV;
         sts4(sS + d * LB + j, a.S0 ? lds4(a.S0 + sb + (size_t)d * D + col0 + j) : zero4());
     }
-    const int ut = tid >> 2, uj = (tid & 3) * 8;       // U: row ut, columns uj..uj+7
-    const int sd = tid / TPR, sj = (tid % TPR) * CPT;  // S: row sd, columns sj..
-    f32x4 pY[NL], pK[NL], pZ[2];
+    const int ut = tid >> 3, uj = (tid & 7) * 4;
+    const bool srow = tid < D * TPR;  // holds a state row
+    const int sd = srow ? tid / TPR : 0, sj = (tid % TPR) * CPT;
+    f32x4 pY[NL], pK[NL], pZ;
     float pg;
     const auto fetch = [&](int c) {
         const size_t u = (size_t)bh * a.NC + c, ucd = u * C * D;
 #pragma unroll
         for (int l = 0; l < NL; ++l) {
             int e, t, d;
-            rc<D>(l, e, t, d);
+            rcs<D>(l, e, t, d);
             pY[l] = lds4(a.wY + ucd + e);
             pK[l] = lds4(a.wKe + ucd + e);
         }
-        const float *z = a.wUz + ucd + (size_t)ut * D + col0 + uj;
-        pZ[0] = lds4(z);
-        pZ[1] = lds4(z + 4);
+        pZ = lds4(a.wUz + ucd + (size_t)ut * D + col0 + uj);
         pg = a.wGam[u * D + sd];
     };
     fetch(0);
@@ -390,15 +406,15 @@ __global__ __launch_bounds__(NT) void cb_fsweep(ChunkBwdArgs a) {
 #pragma unroll
         for (int l = 0; l < NL; ++l) {
             int e, t, d;
-            rc<D>(l, e, t, d);
+            rcs<D>(l, e, t, d);
             sts4(sY + t * LD + d, pY[l]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) sKt[(d + r) * LC + t] = pK[l][r];
         }
-        f32x4 acc0 = pZ[0], acc1 = pZ[1];
+        f32x4 acc = pZ;
         const float gam = pg;
         if (c + 1 < a.NC) fetch(c + 1);
-        for (int i = tid; i < D * BV / 4; i += NT) {
+        for (int i = tid; i < D * BV / 4; i += NS) {
             const int d = 4 * i / BV, j = 4 * i - d * BV;
             sts4(a.wS + u * D * D + (size_t)d * D + col0 + j, lds4(sS + d * LB + j));
         }
@@ -407,54 +423,45 @@ __global__ __launch_bounds__(NT) void cb_fsweep(ChunkBwdArgs a) {
 #pragma unroll 1
         for (int d = 0; d < D; d += 8) {
             const f32x4 y0 = lds4(sY + ut * LD + d), y1 = lds4(sY + ut * LD + d + 4);
-            f32x4 s0[8], s1[8];
+            f32x4 s0[8];
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                s0[r] = lds4(sS + (d + r) * LB + uj);
-                s1[r] = lds4(sS + (d + r) * LB + uj + 4);
-            }
+            for (int r = 0; r < 8; ++r) s0[r] = lds4(sS + (d + r) * LB + uj);
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const float yv = r < 4 ? y0[r & 3] : y1[r & 3];
-                acc0 -= yv * s0[r];
-                acc1 -= yv * s1[r];
-            }
+            for (int r = 0; r < 8; ++r) acc -= (r < 4 ? y0[r & 3] : y1[r & 3]) * s0[r];
         }
-        sts4(sU + ut * LB + uj, acc0);
-        sts4(sU + ut * LB + uj + 4, acc1);
-        float *wu = a.wU + ucd + (size_t)ut * D + col0 + uj;
-        sts4(wu, acc0);
-        sts4(wu + 4, acc1);
+        sts4(sU + ut * LB + uj, acc);
+        sts4(a.wU + ucd + (size_t)ut * D + col0 + uj, acc);
         lds_barrier();
         f32x4 sv[CPT / 4];
 #pragma unroll
         for (int q = 0; q < CPT / 4; ++q) sv[q] = gam * lds4(sS + sd * LB + sj + 4 * q);
 #pragma unroll 1
-        for (int t = 0; t < C; t += 4) {
-            const f32x4 kv = lds4(sKt + sd * LC + t);
-            f32x4 uu[4][CPT / 4];
+        for (int t = 0; t < (srow ? C : 0); t += 8) {
+            const f32x4 k0 = lds4(sKt + sd * LC + t), k1 = lds4(sKt + sd * LC + t + 4);
+            f32x4 uu[8][CPT / 4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
+            for (int r = 0; r < 8; ++r)
 #pragma unroll
                 for (int q = 0; q < CPT / 4; ++q) uu[r][q] = lds4(sU + (t + r) * LB + sj + 4 * q);
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
+            for (int r = 0; r < 8; ++r)
 #pragma unroll
-                for (int q = 0; q < CPT / 4; ++q) sv[q] += kv[r] * uu[r][q];
+                for (int q = 0; q < CPT / 4; ++q) sv[q] += (r < 4 ? k0[r & 3] : k1[r & 3]) * uu[r][q];
         }
         lds_barrier();
+        if (srow)
 #pragma unroll
-        for (int q = 0; q < CPT / 4; ++q) sts4(sS + sd * LB + sj + 4 * q, sv[q]);
+            for (int q = 0; q < CPT / 4; ++q) sts4(sS + sd * LB + sj + 4 * q, sv[q]);
     }
 }
 
 // 3. Backward over chunks for the same work items: X = dL/d(state leaving
 //    the chunk), dU, and X for the chunk before.
 template <typename IO, int D>
-__global__ __launch_bounds__(NT) void cb_bsweep(ChunkBwdArgs a) {
-    using K = Cfg<D>;
-    constexpr int NTL = K::NTL, TPR = K::TPR, CPT = K::CPT, LD = K::LD, NL = K::NL;
-    constexpr int NA = C * C / (4 * NT), NO = C * BV / (4 * NT);  // 4-element groups per thread: A, dO tile
+__global__ __launch_bounds__(NS) void cb_bsweep(ChunkBwdArgs a) {
+    using K = SwCfg<D>;
+    constexpr int NTL = K::NTL, TPR = K::TPR, CPT = K::CPT, NL = K::NL, LD = D + 4;
+    constexpr int NA = C * C / (4 * NS), NO = C * BV / (4 * NS);  // 4-element groups per thread: A, dO tile
     extern __shared__ __align__(16) float smem[];
     float *sX = smem, *sO = sX + D * LB, *sdU = sO + C * LB;
     float *sAt = sdU + C * LB;   // A^T [C][LC]
@@ -464,12 +471,13 @@ __global__ __launch_bounds__(NT) void cb_bsweep(ChunkBwdArgs a) {
     const int tid = threadIdx.x, tile = blockIdx.x % NTL, bh = blockIdx.x / NTL, col0 = tile * BV;
     const int b = bh / a.Hv, h = bh - b * a.Hv;
     const size_t sb = (size_t)bh * D * D;
-    for (int i = tid; i < D * BV / 4; i += NT) {
+    for (int i = tid; i < D * BV / 4; i += NS) {
         const int d = 4 * i / BV, j = 4 * i - d * BV;
         sts4(sX + d * LB + j, a.dST ? lds4(a.dST + sb + (size_t)d * D + col0 + j) : zero4());
     }
-    const int ut = tid >> 2, uj = (tid & 3) * 8;
-    const int sd = tid / TPR, sj = (tid % TPR) * CPT;
+    const int ut = tid >> 3, uj = (tid & 7) * 4;
+    const bool srow = tid < D * TPR;  // holds a state row
+    const int sd = srow ? tid / TPR : 0, sj = (tid % TPR) * CPT;
     f32x4 pY[NL], pK[NL], pQ[NL], pA[NA], pO[NO];
     float pg;
     const auto fetch = [&](int c) {
@@ -478,16 +486,17 @@ __global__ __launch_bounds__(NT) void cb_bsweep(ChunkBwdArgs a) {
 #pragma unroll
         for (int l = 0; l < NL; ++l) {
             int e, t, d;
-            rc<D>(l, e, t, d);
+            rcs<D>(l, e, t, d);
             pY[l] = lds4(a.wY + ucd + e);
             pK[l] = lds4(a.wKe + ucd + e);
             pQ[l] = lds4(a.wQt + ucd + e);
         }
 #pragma unroll
-        for (int l = 0; l < NA; ++l) pA[l] = lds4(a.wA + u * C * C + 4 * (l * NT + tid));
+        for (int l = 0; l < NA; ++l) pA[l] = lds4(a.wA + u * C * C + 4 * (l * NS + tid));
 #pragma unroll
         for (int l = 0; l < NO; ++l) {
-            const int e = 4 * (l * NT + tid), t = e / BV, j = e - t * BV;
+            int e, t, j;
+            rcs<BV>(l, e, t, j);
             pO[l] = t < n ? ld4io<IO>(a.dO, (((size_t)b * a.T + t0 + t) * a.Hv + h) * D + col0 + j) : zero4();
         }
         pg = a.wGam[u * D + sd];
@@ -499,7 +508,7 @@ __global__ __launch_bounds__(NT) void cb_bsweep(ChunkBwdArgs a) {
 #pragma unroll
         for (int l = 0; l < NL; ++l) {
             int e, t, d;
-            rc<D>(l, e, t, d);
+            rcs<D>(l, e, t, d);
             sts4(sK + t * LD + d, pK[l]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -509,62 +518,47 @@ __global__ __launch_bounds__(NT) void cb_bsweep(ChunkBwdArgs a) {
         }
 #pragma unroll
         for (int l = 0; l < NA; ++l) {
-            const int e = 4 * (l * NT + tid), t = e / C, j = e - t * C;
+            int e, t, j;
+            rcs<C>(l, e, t, j);
 #pragma unroll
             for (int r = 0; r < 4; ++r) sAt[(j + r) * LC + t] = pA[l][r];
         }
 #pragma unroll
         for (int l = 0; l < NO; ++l) {
-            const int e = 4 * (l * NT + tid), t = e / BV, j = e - t * BV;
+            int e, t, j;
+            rcs<BV>(l, e, t, j);
             sts4(sO + t * LB + j, pO[l]);
         }
         const float gam = pg;
         if (c > 0) fetch(c - 1);
-        for (int i = tid; i < D * BV / 4; i += NT) {
+        for (int i = tid; i < D * BV / 4; i += NS) {
             const int d = 4 * i / BV, j = 4 * i - d * BV;
             sts4(a.wdS + u * D * D + (size_t)d * D + col0 + j, lds4(sX + d * LB + j));
         }
         lds_barrier();
         // dU (row ut) = s (A^T dO)_ut + Kend_ut X
-        f32x4 p0 = zero4(), p1 = zero4(), k0 = zero4(), k1 = zero4();
+        f32x4 p = zero4(), k = zero4();
 #pragma unroll 1
         for (int t = 0; t < C; t += 8) {
             const f32x4 a0 = lds4(sAt + ut * LC + t), a1 = lds4(sAt + ut * LC + t + 4);
-            f32x4 o0[8], o1[8];
+            f32x4 o[8];
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                o0[r] = lds4(sO + (t + r) * LB + uj);
-                o1[r] = lds4(sO + (t + r) * LB + uj + 4);
-            }
+            for (int r = 0; r < 8; ++r) o[r] = lds4(sO + (t + r) * LB + uj);
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const float av = r < 4 ? a0[r & 3] : a1[r & 3];
-                p0 += av * o0[r];
-                p1 += av * o1[r];
-            }
+            for (int r = 0; r < 8; ++r) p += (r < 4 ? a0[r & 3] : a1[r & 3]) * o[r];
         }
 #pragma unroll 1
         for (int d = 0; d < D; d += 8) {
             const f32x4 c0 = lds4(sK + ut * LD + d), c1 = lds4(sK + ut * LD + d + 4);
-            f32x4 x0[8], x1[8];
+            f32x4 xv[8];
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                x0[r] = lds4(sX + (d + r) * LB + uj);
-                x1[r] = lds4(sX + (d + r) * LB + uj + 4);
-            }
+            for (int r = 0; r < 8; ++r) xv[r] = lds4(sX + (d + r) * LB + uj);
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const float kv = r < 4 ? c0[r & 3] : c1[r & 3];
-                k0 += kv * x0[r];
-                k1 += kv * x1[r];
-            }
+            for (int r = 0; r < 8; ++r) k += (r < 4 ? c0[r & 3] : c1[r & 3]) * xv[r];
         }
-        const f32x4 du0 = a.scale * p0 + k0, du1 = a.scale * p1 + k1;
-        sts4(sdU + ut * LB + uj, du0);
-        sts4(sdU + ut * LB + uj + 4, du1);
-        float *wd = a.wdU + ucd + (size_t)ut * D + col0 + uj;
-        sts4(wd, du0);
-        sts4(wd + 4, du1);
+        const f32x4 du = a.scale * p + k;
+        sts4(sdU + ut * LB + uj, du);
+        sts4(a.wdU + ucd + (size_t)ut * D + col0 + uj, du);
         lds_barrier();
         // X (row sd) = Gamma_sd X + s Q~^T dO - Y^T dU
         f32x4 xa[CPT / 4], qa[CPT / 4];
@@ -574,7 +568,7 @@ __global__ __launch_bounds__(NT) void cb_bsweep(ChunkBwdArgs a) {
             qa[q] = zero4();
         }
 #pragma unroll 1
-        for (int t = 0; t < C; t += 4) {
+        for (int t = 0; t < (srow ? C : 0); t += 4) {
             const f32x4 qv = lds4(sQt + sd * LC + t), yv = lds4(sYt + sd * LC + t);
             f32x4 oo[4][CPT / 4], uu[4][CPT / 4];
 #pragma unroll
@@ -593,12 +587,13 @@ __global__ __launch_bounds__(NT) void cb_bsweep(ChunkBwdArgs a) {
                 }
         }
         lds_barrier();
+        if (srow)
 #pragma unroll
-        for (int q = 0; q < CPT / 4; ++q) sts4(sX + sd * LB + sj + 4 * q, a.scale * qa[q] + xa[q]);
+            for (int q = 0; q < CPT / 4; ++q) sts4(sX + sd * LB + sj + 4 * q, a.scale * qa[q] + xa[q]);
     }
     lds_barrier();
     if (a.dS0)
-        for (int i = tid; i < D * BV / 4; i += NT) {
+        for (int i = tid; i < D * BV / 4; i += NS) {
             const int d = 4 * i / BV, j = 4 * i - d * BV;
             sts4(a.dS0 + sb + (size_t)d * D + col0 + j, lds4(sX + d * LB + j));
         }
@@ -1011,8 +1006,8 @@ hipError_t run(const ChunkBwdArgs &a, hipStream_t s) {
     if (attr != hipSuccess) return attr;
     const unsigned units = (unsigned)((size_t)a.B * a.Hv * a.NC), items = (unsigned)((size_t)a.B * a.Hv * (D / BV));
     hipLaunchKernelGGL((cb_prep<IO, D, CHAN, BW>), dim3(units), dim3(NT), prep_smem<D>(), s, a);
-    hipLaunchKernelGGL((cb_fsweep<D>), dim3(items), dim3(NT), fsweep_smem<D>(), s, a);
-    hipLaunchKernelGGL((cb_bsweep<IO, D>), dim3(items), dim3(NT), bsweep_smem<D>(), s, a);
+    hipLaunchKernelGGL((cb_fsweep<D>), dim3(items), dim3(NS), fsweep_smem<D>(), s, a);
+    hipLaunchKernelGGL((cb_bsweep<IO, D>), dim3(items), dim3(NS), bsweep_smem<D>(), s, a);
     hipLaunchKernelGGL((cb_grad_s<IO, D>), dim3(units), dim3(NT), grad_s_smem<D>(), s, a);
     hipLaunchKernelGGL((cb_grad_out<IO, D, CHAN, BW>), dim3(units), dim3(NT), grad_out_smem<D>(), s, a);
     if (a.Hv > a.Hqk) {
