@@ -53,7 +53,7 @@ namespace gdr {
 namespace {
 
 constexpr int C = kChunk;
-constexpr int NT = 256;     // threads per workgroup
+constexpr int NT = 512;     // threads per workgroup of the per-chunk kernels (two waves per SIMD)
 constexpr int BV = 32;      // value columns per sweep workgroup
 constexpr int LB = BV + 4;  // row stride of 32-column tiles
 constexpr int LC = C + 4;   // row stride of 64-column tiles
@@ -78,8 +78,7 @@ template <int D>
 struct Cfg {
     static constexpr int LD = D + 4;              // row stride of D-column tiles
     static constexpr int NL = C * D / (4 * NT);   // 4-element groups per thread of a C x D array
-    static constexpr int NTL = D / BV, TPR = NT / D, CPT = BV / TPR;  // sweep state rows: threads per row, columns each
-    static constexpr int NCG = D / 4, RT = D / 16, NRG = NT / NCG;     // cb_grad_out: column groups, rows per thread
+    static constexpr int NCG = D / 4, NRG = NT / NCG, RT = C / NRG;  // cb_grad_out: column groups, row groups, rows each
 };
 
 __device__ __forceinline__ f32x4 lds4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
@@ -188,7 +187,7 @@ constexpr size_t grad_s_smem() {
 }
 template <int D>
 constexpr size_t grad_out_smem() {
-    return (3 * (size_t)C * (D + 4) + 2 * (size_t)C * LC + 2 * C + 16 * C + 2 * 32 * C + 1024 + D) * 4;
+    return (3 * (size_t)C * (D + 4) + 2 * (size_t)C * LC + 2 * C + 2 * 32 * C + 2048 + D) * 4;
 }
 
 // ---------------------------------------------------------------------------
@@ -275,26 +274,27 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
     if (tid < D) a.wGam[(size_t)u * D + tid] = expf(CHAN ? sZ[(C - 1) * LD + tid] : sGs[C - 1]);
     __syncthreads();
 
-    // T and A: thread = 4 x 4 block of rows r0.., columns c0..
+    // T and A: thread = 2 x 4 block of rows r0.., columns c0..
     {
-        const int r0 = (tid >> 4) * 4, c0 = (tid & 15) * 4;
-        float aT[4][4], aA[4][4];
+        const int r0 = (tid >> 4) * 2, c0 = (tid & 15) * 4;
+        float aT[2][4], aA[2][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) aT[i][j] = aA[i][j] = 0.f;
-        if (c0 <= r0 + 3) {
+        if (c0 <= r0 + 1) {
 #pragma unroll 2
             for (int d = 0; d < D; d += 4) {
-                f32x4 e4[4], q4[4], k4[4];
+                f32x4 e4[2], q4[2], k4[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
+                for (int i = 0; i < 2; ++i) {
                     e4[i] = lds4(sE + (r0 + i) * LD + d);
                     q4[i] = lds4(sQ + (r0 + i) * LD + d);
-                    k4[i] = lds4(sK + (c0 + i) * LD + d);
                 }
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                for (int j = 0; j < 4; ++j) k4[j] = lds4(sK + (c0 + j) * LD + d);
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         aT[i][j] = dot4(e4[i], k4[j], aT[i][j]);
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
             }
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 2; ++i) {
             const int t = r0 + i;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -318,7 +318,7 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
         }
         __syncthreads();  // q, k and e tiles read: T goes where q was
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sts4(sQ + (r0 + i) * C + c0, f32x4{aT[i][0], aT[i][1], aT[i][2], aT[i][3]});
+        for (int i = 0; i < 2; ++i) sts4(sQ + (r0 + i) * C + c0, f32x4{aT[i][0], aT[i][1], aT[i][2], aT[i][3]});
     }
     // Right-hand sides: E~ (scalar decay: the raw e scaled by exp(G_t)) and z.
     {
@@ -605,7 +605,7 @@ __global__ __launch_bounds__(NS) void cb_bsweep(ChunkBwdArgs a) {
 template <typename IO, int D>
 __global__ __launch_bounds__(NT) void cb_grad_s(ChunkBwdArgs a) {
     constexpr int LD = Cfg<D>::LD, NL = Cfg<D>::NL, R0 = C * C > 32 * LD ? C * C : 32 * LD;
-    constexpr int NB = 32 * D / (4 * NT), NTT = C * C / (4 * NT);
+    constexpr int NG = 32 * D / 4, NB = (NG + NT - 1) / NT, NTT = C * C / (4 * NT);  // 4-element groups: S block, T
     extern __shared__ __align__(16) float smem[];
     float *sT = smem;  // T^T, row stride C; later 32 rows of S
     float *sX = sT + R0, *sU = sX + C * LD, *sO = sU + C * LD, *sB = sO + C * LD;
@@ -657,24 +657,25 @@ __global__ __launch_bounds__(NT) void cb_grad_s(ChunkBwdArgs a) {
         sts4(a.wdU + ucd + e, lds4(sX + t * LD + d));  // dR replaces dU
     }
     {
-        const int r0 = (tid >> 4) * 4, c0 = (tid & 15) * 4;
-        float aT[4][4], aA[4][4];
+        const int r0 = (tid >> 4) * 2, c0 = (tid & 15) * 4;
+        float aT[2][4], aA[2][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) aT[i][j] = aA[i][j] = 0.f;
-        if (c0 <= r0 + 3) {
+        if (c0 <= r0 + 1) {
 #pragma unroll 2
             for (int v = 0; v < D; v += 4) {
-                f32x4 x4[4], o4[4], u4[4];
+                f32x4 x4[2], o4[2], u4[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
+                for (int i = 0; i < 2; ++i) {
                     x4[i] = lds4(sX + (r0 + i) * LD + v);
                     o4[i] = lds4(sO + (r0 + i) * LD + v);
-                    u4[i] = lds4(sU + (c0 + i) * LD + v);
                 }
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                for (int j = 0; j < 4; ++j) u4[j] = lds4(sU + (c0 + j) * LD + v);
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         aT[i][j] = dot4(x4[i], u4[j], aT[i][j]);
@@ -683,7 +684,7 @@ __global__ __launch_bounds__(NT) void cb_grad_s(ChunkBwdArgs a) {
             }
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 2; ++i) {
             const int t = r0 + i;
             f32x4 dt, da;
 #pragma unroll
@@ -696,7 +697,7 @@ __global__ __launch_bounds__(NT) void cb_grad_s(ChunkBwdArgs a) {
         }
     }
     // Products with S, then with dS_next, 32 state rows at a time.
-    const int bt = tid >> 2, bd = (tid & 3) * 8;
+    const int bt = tid >> 3, bd = (tid & 7) * 4;
     for (int pass = 0; pass < 2; ++pass)
         for (int blk = 0; blk < D / 32; ++blk) {
             __syncthreads();
@@ -705,40 +706,44 @@ __global__ __launch_bounds__(NT) void cb_grad_s(ChunkBwdArgs a) {
                 f32x4 rb[NB], rs[NB];
 #pragma unroll
                 for (int l = 0; l < NB; ++l) {
-                    rb[l] = lds4(src + 4 * (l * NT + tid));
-                    if (pass == 1) rs[l] = lds4(a.wS + udd + (size_t)blk * 32 * D + 4 * (l * NT + tid));
+                    const int g = l * NT + tid;
+                    if (g < NG) {
+                        rb[l] = lds4(src + 4 * g);
+                        if (pass == 1) rs[l] = lds4(a.wS + udd + (size_t)blk * 32 * D + 4 * g);
+                    }
                 }
 #pragma unroll
                 for (int l = 0; l < NB; ++l) {
-                    const int e = 4 * (l * NT + tid), r = e / D, v = e - r * D;
-                    sts4(sB + r * LD + v, rb[l]);
-                    if (pass == 1) sts4(sT + r * LD + v, rs[l]);  // S rows beside dS_next's
+                    const int g = l * NT + tid, e = 4 * g, r = e / D, v = e - r * D;
+                    if (g < NG) {
+                        sts4(sB + r * LD + v, rb[l]);
+                        if (pass == 1) sts4(sT + r * LD + v, rs[l]);  // S rows beside dS_next's
+                    }
                 }
             }
             __syncthreads();
-            float p[8], q[8];
+            float p[4], q[4];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) p[j] = q[j] = 0.f;
+            for (int j = 0; j < 4; ++j) p[j] = q[j] = 0.f;
             const float *L0 = (pass == 0 ? sX : sU) + bt * LD;
 #pragma unroll 2
             for (int v = 0; v < D; v += 4) {
                 const f32x4 l0 = lds4(L0 + v), o0 = lds4(sO + bt * LD + v);
+                f32x4 b4[4];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const f32x4 b4 = lds4(sB + (bd + j) * LD + v);
-                    p[j] = dot4(l0, b4, p[j]);
-                    if (pass == 0) q[j] = dot4(o0, b4, q[j]);
+                for (int j = 0; j < 4; ++j) b4[j] = lds4(sB + (bd + j) * LD + v);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    p[j] = dot4(l0, b4[j], p[j]);
+                    if (pass == 0) q[j] = dot4(o0, b4[j], q[j]);
                 }
             }
             const size_t o = ucd + (size_t)bt * D + blk * 32 + bd;
             if (pass == 0) {
                 sts4(a.wdE + o, -f32x4{p[0], p[1], p[2], p[3]});
-                sts4(a.wdE + o + 4, -f32x4{p[4], p[5], p[6], p[7]});
                 sts4(a.wdQ + o, a.scale * f32x4{q[0], q[1], q[2], q[3]});
-                sts4(a.wdQ + o + 4, a.scale * f32x4{q[4], q[5], q[6], q[7]});
             } else {
                 sts4(a.wdK + o, f32x4{p[0], p[1], p[2], p[3]});
-                sts4(a.wdK + o + 4, f32x4{p[4], p[5], p[6], p[7]});
                 if (tid < 32) {
                     float acc = 0.f;
 #pragma unroll 4
@@ -765,14 +770,14 @@ __global__ __launch_bounds__(NT) void cb_grad_out(ChunkBwdArgs a) {
     // Reductions go through per-thread parts summed in a fixed order, so that
     // the result does not depend on the order threads arrive in.
     float *sRow = sdA + C * LC;    // [C] row sums of dT . T + dA . A (scalar decay)
-    float *sColP = sRow + C;       // [16][C] their column sums by row group
-    float *sCol = sColP + 16 * C;  // [C]
-    float *sTokG = sCol + C;       // [C][32] per-token dG parts of the column groups (scalar decay)
-    float *sTokB = sTokG + 32 * C; // [C][32] per-token dbeta parts (tied gates)
+    float *sColP = sRow + C;       // [32][C] their column sums by row group; later sTokG
+    float *sTokG = sColP;          // [C][32] per-token dG parts of the column groups (scalar decay)
+    float *sCol = sColP + 32 * C;  // [C]
+    float *sTokB = sCol + C;       // [C][32] per-token dbeta parts (tied gates)
     float *sGeP = sTokB + 32 * C;  // [NRG][D] dG_end parts
-    float *sGe = sGeP + 1024;      // [D] dG_end (scalar decay: element 0)
+    float *sGe = sGeP + 2048;      // [D] dG_end (scalar decay: element 0)
     float *sGt = sdT;
-    static_assert(C * LD <= 2 * C * LC && NRG * D <= 1024 && NCG <= 32, "shared-memory layout");
+    static_assert(C * LD <= 2 * C * LC && NRG * D <= 2048 && NCG <= 32 && NT / 16 == 32, "shared-memory layout");
     const int tid = threadIdx.x, u = blockIdx.x;
     const Unit x = decode(a, u);
     const size_t ucd = (size_t)u * C * D, ucc = (size_t)u * C * C;
@@ -809,7 +814,7 @@ __global__ __launch_bounds__(NT) void cb_grad_out(ChunkBwdArgs a) {
         }
     }
     {
-        // Thread: 4 consecutive columns j of rows t = 16 l + tid / 16; the 16
+        // Thread: 4 consecutive columns j of rows t = 32 l + tid / 16; the 16
         // threads of a row are 16 consecutive lanes.
         f32x4 colw = zero4();
 #pragma unroll
@@ -843,7 +848,7 @@ __global__ __launch_bounds__(NT) void cb_grad_out(ChunkBwdArgs a) {
     __syncthreads();
     if (!CHAN && tid < C) {
         float cs = 0.f;
-        for (int r = 0; r < 16; ++r) cs += sColP[r * C + tid];
+        for (int r = 0; r < 32; ++r) cs += sColP[r * C + tid];
         sCol[tid] = cs;
     }
     // X_e = dT' P2, X_q = dA' P2, X_k = dT'^T P1 + dA'^T P3; thread = rows m0..m0+RT-1, columns n0..n0+3.
