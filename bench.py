@@ -368,7 +368,7 @@ def main(argv=None):
         del rws
         bwd = {"entry": "gdr_chunk_bwd", "workload": wl.name, "calls": n_b, "launch": "hip_graph",
                "ms_per_call": b_ms, "tokens_per_s": wl.B * wl.T / (b_ms * 1e-3),
-               "roofline": {"kernel": "cb_prep + cb_fsweep + cb_bsweep + cb_grad_s + cb_grad_out (+ cb_group_sum)",
+               "roofline": {"kernel": "cb_prep + cb_sweeps + cb_grad_s + cb_grad_out (+ cb_group_sum)",
                             "bound": "alu", "achieved": c_flops / (b_ms * 1e-3) / 1e12,
                             "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
                             "frac": c_flops / (b_ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,

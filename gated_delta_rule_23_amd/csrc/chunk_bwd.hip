@@ -34,13 +34,12 @@
 // floats) and the inner loops read them 16 bytes at a time; global arrays
 // are staged through registers with 16-byte (8-byte for bf16) loads.
 //
-// Five launches, all arithmetic in fp32:
+// Four launches (five with grouped heads), all arithmetic in fp32:
 //  1. cb_prep (per chunk unit): G, the factors above, T and A, and the
 //     triangular solve (I + T)[Y | U_z] = [E~ | Z] by forward substitution.
-//  2. cb_fsweep (per sequence, V head, 32 value columns): the states S
-//     entering every chunk, and U, walking the chunks forward.
-//  3. cb_bsweep (same work items): dS_next of every chunk and dU, walking the
-//     chunks backward; dS_0 at the end.
+//  2. cb_sweeps, per (sequence, V head, 32 value columns) twice over: the
+//     states S entering every chunk and U, walking the chunks forward; and
+//     dS_next of every chunk and dU, walking them backward (dS_0 at the end).
 //  4. cb_grad_s (per unit): dR by back substitution, dT, dA and the products
 //     with S and dS_next.
 //  5. cb_grad_out (per unit): the products through T and A, the exponential
@@ -371,12 +370,11 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
 // 2. Forward over chunks: the state entering each chunk, and U = U_z - Y S.
 //    Thread: U row ut, columns uj..uj+3; state row sd, columns sj..sj+CPT-1.
 template <int D>
-__global__ __launch_bounds__(NS) void cb_fsweep(ChunkBwdArgs a) {
+__device__ __forceinline__ void fsweep(const ChunkBwdArgs &a, float *smem, int item) {
     using K = SwCfg<D>;
     constexpr int NTL = K::NTL, TPR = K::TPR, CPT = K::CPT, NL = K::NL, LD = D + 4;
-    extern __shared__ __align__(16) float smem[];
     float *sS = smem, *sU = sS + D * LB, *sY = sU + C * LB, *sKt = sY + C * LD;  // Kend transposed: [D][LC]
-    const int tid = threadIdx.x, tile = blockIdx.x % NTL, bh = blockIdx.x / NTL, col0 = tile * BV;
+    const int tid = threadIdx.x, tile = item % NTL, bh = item / NTL, col0 = tile * BV;
     const size_t sb = (size_t)bh * D * D;
     for (int i = tid; i < D * BV / 4; i += NS) {
         const int d = 4 * i / BV, j = 4 * i - d * BV;
@@ -458,17 +456,16 @@ __global__ __launch_bounds__(NS) void cb_fsweep(ChunkBwdArgs a) {
 // 3. Backward over chunks for the same work items: X = dL/d(state leaving
 //    the chunk), dU, and X for the chunk before.
 template <typename IO, int D>
-__global__ __launch_bounds__(NS) void cb_bsweep(ChunkBwdArgs a) {
+__device__ __forceinline__ void bsweep(const ChunkBwdArgs &a, float *smem, int item) {
     using K = SwCfg<D>;
     constexpr int NTL = K::NTL, TPR = K::TPR, CPT = K::CPT, NL = K::NL, LD = D + 4;
     constexpr int NA = C * C / (4 * NS), NO = C * BV / (4 * NS);  // 4-element groups per thread: A, dO tile
-    extern __shared__ __align__(16) float smem[];
     float *sX = smem, *sO = sX + D * LB, *sdU = sO + C * LB;
     float *sAt = sdU + C * LB;   // A^T [C][LC]
     float *sK = sAt + C * LC;    // Kend [C][LD]
     float *sQt = sK + C * LD;    // Q~^T [D][LC]
     float *sYt = sQt + D * LC;   // Y^T [D][LC]
-    const int tid = threadIdx.x, tile = blockIdx.x % NTL, bh = blockIdx.x / NTL, col0 = tile * BV;
+    const int tid = threadIdx.x, tile = item % NTL, bh = item / NTL, col0 = tile * BV;
     const int b = bh / a.Hv, h = bh - b * a.Hv;
     const size_t sb = (size_t)bh * D * D;
     for (int i = tid; i < D * BV / 4; i += NS) {
@@ -597,6 +594,17 @@ __global__ __launch_bounds__(NS) void cb_bsweep(ChunkBwdArgs a) {
             const int d = 4 * i / BV, j = 4 * i - d * BV;
             sts4(a.dS0 + sb + (size_t)d * D + col0 + j, lds4(sX + d * LB + j));
         }
+}
+
+// The two sweeps do not depend on each other (the chain of dL/dS does not
+// use the forward states), so one launch runs both: the backward sweep's
+// workgroups first, then the forward sweep's, which fill the CUs the first
+// set leaves free and then follow as workgroups finish.
+template <typename IO, int D>
+__global__ __launch_bounds__(NS) void cb_sweeps(ChunkBwdArgs a, int items) {
+    extern __shared__ __align__(16) float smem[];
+    if ((int)blockIdx.x < items) bsweep<IO, D>(a, smem, blockIdx.x);
+    else fsweep<D>(a, smem, blockIdx.x - items);
 }
 
 // ---------------------------------------------------------------------------
@@ -994,15 +1002,14 @@ __global__ __launch_bounds__(NT) void cb_group_sum(ChunkBwdArgs a) {
 
 template <typename IO, int D, bool CHAN, bool BW>
 hipError_t run(const ChunkBwdArgs &a, hipStream_t s) {
+    constexpr size_t sweep_smem = bsweep_smem<D>() > fsweep_smem<D>() ? bsweep_smem<D>() : fsweep_smem<D>();
     static const hipError_t attr = [] {
-        const void *fn[5] = {reinterpret_cast<const void *>(&cb_prep<IO, D, CHAN, BW>),
-                             reinterpret_cast<const void *>(&cb_fsweep<D>),
-                             reinterpret_cast<const void *>(&cb_bsweep<IO, D>),
+        const void *fn[4] = {reinterpret_cast<const void *>(&cb_prep<IO, D, CHAN, BW>),
+                             reinterpret_cast<const void *>(&cb_sweeps<IO, D>),
                              reinterpret_cast<const void *>(&cb_grad_s<IO, D>),
                              reinterpret_cast<const void *>(&cb_grad_out<IO, D, CHAN, BW>)};
-        const size_t bytes[5] = {prep_smem<D>(), fsweep_smem<D>(), bsweep_smem<D>(), grad_s_smem<D>(),
-                                 grad_out_smem<D>()};
-        for (int i = 0; i < 5; ++i) {
+        const size_t bytes[4] = {prep_smem<D>(), sweep_smem, grad_s_smem<D>(), grad_out_smem<D>()};
+        for (int i = 0; i < 4; ++i) {
             const hipError_t e = hipFuncSetAttribute(fn[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes[i]);
             if (e != hipSuccess) return e;
         }
@@ -1011,8 +1018,7 @@ hipError_t run(const ChunkBwdArgs &a, hipStream_t s) {
     if (attr != hipSuccess) return attr;
     const unsigned units = (unsigned)((size_t)a.B * a.Hv * a.NC), items = (unsigned)((size_t)a.B * a.Hv * (D / BV));
     hipLaunchKernelGGL((cb_prep<IO, D, CHAN, BW>), dim3(units), dim3(NT), prep_smem<D>(), s, a);
-    hipLaunchKernelGGL((cb_fsweep<D>), dim3(items), dim3(NS), fsweep_smem<D>(), s, a);
-    hipLaunchKernelGGL((cb_bsweep<IO, D>), dim3(items), dim3(NS), bsweep_smem<D>(), s, a);
+    hipLaunchKernelGGL((cb_sweeps<IO, D>), dim3(2 * items), dim3(NS), sweep_smem, s, a, (int)items);
     hipLaunchKernelGGL((cb_grad_s<IO, D>), dim3(units), dim3(NT), grad_s_smem<D>(), s, a);
     hipLaunchKernelGGL((cb_grad_out<IO, D, CHAN, BW>), dim3(units), dim3(NT), grad_out_smem<D>(), s, a);
     if (a.Hv > a.Hqk) {
