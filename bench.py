@@ -374,7 +374,8 @@ def main(argv=None):
                             "frac": c_flops / (b_ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
                             "algorithmic_flops": c_flops},
                "hbm": {"achieved": b_bytes / (b_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                       "frac": b_bytes / (b_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, "algorithmic_bytes": b_bytes},
+                       "frac": b_bytes / (b_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, "algorithmic_bytes": b_bytes,
+                       "traffic": recorded_traffic(wl.name + "_backward_chunked")},
                "recurrent": {"entry": "gdr_recurrent_bwd", "ms_per_call": r_ms,
                              "tokens_per_s": wl.B * wl.T / (r_ms * 1e-3),
                              "roofline": {"kernel": "bwd_ckpt_kernel + bwd_kernel + bwd_reduce_kernel",

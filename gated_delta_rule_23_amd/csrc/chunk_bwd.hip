@@ -599,12 +599,18 @@ __device__ __forceinline__ void bsweep(const ChunkBwdArgs &a, float *smem, int i
 // The two sweeps do not depend on each other (the chain of dL/dS does not
 // use the forward states), so one launch runs both: the backward sweep's
 // workgroups first, then the forward sweep's, which fill the CUs the first
-// set leaves free and then follow as workgroups finish.
+// set leaves free and then follow as workgroups finish. Each set has P
+// workgroups (items rounded up to a multiple of 8); workgroups that share an
+// XCD (block index mod 8) take consecutive work items, so that the value
+// tiles of one head read its chunk factors through the same L2.
 template <typename IO, int D>
-__global__ __launch_bounds__(NS) void cb_sweeps(ChunkBwdArgs a, int items) {
+__global__ __launch_bounds__(NS) void cb_sweeps(ChunkBwdArgs a, int items, int P) {
     extern __shared__ __align__(16) float smem[];
-    if ((int)blockIdx.x < items) bsweep<IO, D>(a, smem, blockIdx.x);
-    else fsweep<D>(a, smem, blockIdx.x - items);
+    const int x = (int)blockIdx.x, back = x < P, xl = back ? x : x - P;
+    const int wi = (xl & 7) * (P >> 3) + (xl >> 3);
+    if (wi >= items) return;
+    if (back) bsweep<IO, D>(a, smem, wi);
+    else fsweep<D>(a, smem, wi);
 }
 
 // ---------------------------------------------------------------------------
@@ -1018,7 +1024,8 @@ hipError_t run(const ChunkBwdArgs &a, hipStream_t s) {
     if (attr != hipSuccess) return attr;
     const unsigned units = (unsigned)((size_t)a.B * a.Hv * a.NC), items = (unsigned)((size_t)a.B * a.Hv * (D / BV));
     hipLaunchKernelGGL((cb_prep<IO, D, CHAN, BW>), dim3(units), dim3(NT), prep_smem<D>(), s, a);
-    hipLaunchKernelGGL((cb_sweeps<IO, D>), dim3(2 * items), dim3(NS), sweep_smem, s, a, (int)items);
+    const unsigned P = (items + 7) / 8 * 8;
+    hipLaunchKernelGGL((cb_sweeps<IO, D>), dim3(2 * P), dim3(NS), sweep_smem, s, a, (int)items, (int)P);
     hipLaunchKernelGGL((cb_grad_s<IO, D>), dim3(units), dim3(NT), grad_s_smem<D>(), s, a);
     hipLaunchKernelGGL((cb_grad_out<IO, D, CHAN, BW>), dim3(units), dim3(NT), grad_out_smem<D>(), s, a);
     if (a.Hv > a.Hqk) {
