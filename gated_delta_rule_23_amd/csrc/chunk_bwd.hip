@@ -260,7 +260,6 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
         const f32x4 G = CHAN ? lds4(sZ + t * LD + d) : splat(sGs[t]);
         const f32x4 Ge = CHAN ? lds4(sZ + (C - 1) * LD + d) : splat(sGs[C - 1]);
         const f32x4 eg = exp4(G), qv = lds4(sQ + t * LD + d), kv = lds4(sK + t * LD + d);
-        sts4(a.wQt + ucd + e, qv * eg);
         sts4(a.wKe + ucd + e, kv * exp4(Ge - G));
         if (CHAN) {
             sts4(wG + e, G);
@@ -272,6 +271,29 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
     if (!CHAN && tid < C) wG[tid] = sGs[tid];
     if (tid < D) a.wGam[(size_t)u * D + tid] = expf(CHAN ? sZ[(C - 1) * LD + tid] : sGs[C - 1]);
     __syncthreads();
+    // Q~^T and Kend^T (row = channel), which the sweeps over chunks read.
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+        int e, dd, t;
+        rc<C>(l, e, dd, t);
+        f32x4 qv, kv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            qv[r] = sQ[(t + r) * LD + dd];
+            kv[r] = sK[(t + r) * LD + dd];
+        }
+        if (CHAN) {
+            kv *= expf(sZ[(C - 1) * LD + dd]);  // Kend = K~ exp(G_end)
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                qv[r] *= expf(sGs[t + r]);
+                kv[r] *= expf(sGs[C - 1] - sGs[t + r]);
+            }
+        }
+        sts4(a.wQt + ucd + e, qv);
+        sts4(a.wKet + ucd + e, kv);
+    }
 
     // T and A: thread = 2 x 4 block of rows r0.., columns c0..
     {
@@ -314,6 +336,8 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
             const size_t o = (size_t)u * C * C + (size_t)t * C + c0;
             sts4(a.wT + o, f32x4{aT[i][0], aT[i][1], aT[i][2], aT[i][3]});
             sts4(a.wA + o, f32x4{aA[i][0], aA[i][1], aA[i][2], aA[i][3]});
+#pragma unroll
+            for (int j = 0; j < 4; ++j) a.wAt[(size_t)u * C * C + (size_t)(c0 + j) * C + t] = aA[i][j];
         }
         __syncthreads();  // q, k and e tiles read: T goes where q was
 #pragma unroll
@@ -359,6 +383,12 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
         sts4(a.wY + ucd + e, lds4(sE + t * LD + d));
         sts4(a.wUz + ucd + e, lds4(sZ + t * LD + d));
     }
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {  // Y^T
+        int e, dd, t;
+        rc<C>(l, e, dd, t);
+        sts4(a.wYt + ucd + e, f32x4{sE[t * LD + dd], sE[(t + 1) * LD + dd], sE[(t + 2) * LD + dd], sE[(t + 3) * LD + dd]});
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -389,10 +419,9 @@ __device__ __forceinline__ void fsweep(const ChunkBwdArgs &a, float *smem, int i
         const size_t u = (size_t)bh * a.NC + c, ucd = u * C * D;
 #pragma unroll
         for (int l = 0; l < NL; ++l) {
-            int e, t, d;
-            rcs<D>(l, e, t, d);
-            pY[l] = lds4(a.wY + ucd + e);
-            pK[l] = lds4(a.wKe + ucd + e);
+            const int e = 4 * (l * NS + tid);
+            pY[l] = lds4(a.wY + ucd + e);    // [C][D]
+            pK[l] = lds4(a.wKet + ucd + e);  // [D][C]
         }
         pZ = lds4(a.wUz + ucd + (size_t)ut * D + col0 + uj);
         pg = a.wGam[u * D + sd];
@@ -406,8 +435,8 @@ __device__ __forceinline__ void fsweep(const ChunkBwdArgs &a, float *smem, int i
             int e, t, d;
             rcs<D>(l, e, t, d);
             sts4(sY + t * LD + d, pY[l]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sKt[(d + r) * LC + t] = pK[l][r];
+            rcs<C>(l, e, d, t);
+            sts4(sKt + d * LC + t, pK[l]);
         }
         f32x4 acc = pZ;
         const float gam = pg;
@@ -482,14 +511,13 @@ __device__ __forceinline__ void bsweep(const ChunkBwdArgs &a, float *smem, int i
         const int t0 = c * C, n = min(C, a.T - t0);
 #pragma unroll
         for (int l = 0; l < NL; ++l) {
-            int e, t, d;
-            rcs<D>(l, e, t, d);
-            pY[l] = lds4(a.wY + ucd + e);
-            pK[l] = lds4(a.wKe + ucd + e);
-            pQ[l] = lds4(a.wQt + ucd + e);
+            const int e = 4 * (l * NS + tid);
+            pY[l] = lds4(a.wYt + ucd + e);  // [D][C]
+            pK[l] = lds4(a.wKe + ucd + e);  // [C][D]
+            pQ[l] = lds4(a.wQt + ucd + e);  // [D][C]
         }
 #pragma unroll
-        for (int l = 0; l < NA; ++l) pA[l] = lds4(a.wA + u * C * C + 4 * (l * NS + tid));
+        for (int l = 0; l < NA; ++l) pA[l] = lds4(a.wAt + u * C * C + 4 * (l * NS + tid));
 #pragma unroll
         for (int l = 0; l < NO; ++l) {
             int e, t, j;
@@ -507,18 +535,15 @@ __device__ __forceinline__ void bsweep(const ChunkBwdArgs &a, float *smem, int i
             int e, t, d;
             rcs<D>(l, e, t, d);
             sts4(sK + t * LD + d, pK[l]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                sYt[(d + r) * LC + t] = pY[l][r];
-                sQt[(d + r) * LC + t] = pQ[l][r];
-            }
+            rcs<C>(l, e, d, t);
+            sts4(sYt + d * LC + t, pY[l]);
+            sts4(sQt + d * LC + t, pQ[l]);
         }
 #pragma unroll
         for (int l = 0; l < NA; ++l) {
-            int e, t, j;
-            rcs<C>(l, e, t, j);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sAt[(j + r) * LC + t] = pA[l][r];
+            int e, j, t;
+            rcs<C>(l, e, j, t);
+            sts4(sAt + j * LC + t, pA[l]);
         }
 #pragma unroll
         for (int l = 0; l < NO; ++l) {
