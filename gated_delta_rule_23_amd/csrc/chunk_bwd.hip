@@ -735,62 +735,70 @@ __global__ __launch_bounds__(NT) void cb_grad_s(ChunkBwdArgs a) {
             sts4(a.wdA + ucc + (size_t)t * C + c0, da);
         }
     }
-    // Products with S, then with dS_next, 32 state rows at a time.
+    // Products with S and with dS_next, 32 state rows at a time; the next
+    // block's rows are fetched into registers while the current one is used.
+    float *sB2 = sT;  // S rows of the block (T^T is no longer needed)
     const int bt = tid >> 3, bd = (tid & 7) * 4;
-    for (int pass = 0; pass < 2; ++pass)
-        for (int blk = 0; blk < D / 32; ++blk) {
-            __syncthreads();
-            const float *src = (pass == 0 ? a.wS : a.wdS) + udd + (size_t)blk * 32 * D;
-            {
-                f32x4 rb[NB], rs[NB];
+    f32x4 rb[NB], rs[NB];
+    const auto fetch = [&](int blk) {
 #pragma unroll
-                for (int l = 0; l < NB; ++l) {
-                    const int g = l * NT + tid;
-                    if (g < NG) {
-                        rb[l] = lds4(src + 4 * g);
-                        if (pass == 1) rs[l] = lds4(a.wS + udd + (size_t)blk * 32 * D + 4 * g);
-                    }
-                }
-#pragma unroll
-                for (int l = 0; l < NB; ++l) {
-                    const int g = l * NT + tid, e = 4 * g, r = e / D, v = e - r * D;
-                    if (g < NG) {
-                        sts4(sB + r * LD + v, rb[l]);
-                        if (pass == 1) sts4(sT + r * LD + v, rs[l]);  // S rows beside dS_next's
-                    }
-                }
-            }
-            __syncthreads();
-            float p[4], q[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) p[j] = q[j] = 0.f;
-            const float *L0 = (pass == 0 ? sX : sU) + bt * LD;
-#pragma unroll 2
-            for (int v = 0; v < D; v += 4) {
-                const f32x4 l0 = lds4(L0 + v), o0 = lds4(sO + bt * LD + v);
-                f32x4 b4[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) b4[j] = lds4(sB + (bd + j) * LD + v);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    p[j] = dot4(l0, b4[j], p[j]);
-                    if (pass == 0) q[j] = dot4(o0, b4[j], q[j]);
-                }
-            }
-            const size_t o = ucd + (size_t)bt * D + blk * 32 + bd;
-            if (pass == 0) {
-                sts4(a.wdE + o, -f32x4{p[0], p[1], p[2], p[3]});
-                sts4(a.wdQ + o, a.scale * f32x4{q[0], q[1], q[2], q[3]});
-            } else {
-                sts4(a.wdK + o, f32x4{p[0], p[1], p[2], p[3]});
-                if (tid < 32) {
-                    float acc = 0.f;
-#pragma unroll 4
-                    for (int v = 0; v < D; v += 4) acc = dot4(lds4(sB + tid * LD + v), lds4(sT + tid * LD + v), acc);
-                    a.wdGam[(size_t)u * D + blk * 32 + tid] = acc;
-                }
+        for (int l = 0; l < NB; ++l) {
+            const int g = l * NT + tid;
+            if (g < NG) {
+                rs[l] = lds4(a.wS + udd + (size_t)blk * 32 * D + 4 * g);
+                rb[l] = lds4(a.wdS + udd + (size_t)blk * 32 * D + 4 * g);
             }
         }
+    };
+    fetch(0);
+    for (int blk = 0; blk < D / 32; ++blk) {
+        __syncthreads();  // the previous block's rows are read
+#pragma unroll
+        for (int l = 0; l < NB; ++l) {
+            const int g = l * NT + tid, e = 4 * g, r = e / D, v = e - r * D;
+            if (g < NG) {
+                sts4(sB2 + r * LD + v, rs[l]);
+                sts4(sB + r * LD + v, rb[l]);
+            }
+        }
+        if (blk + 1 < D / 32) fetch(blk + 1);
+        __syncthreads();
+        float pe[4], pq[4], pk[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pe[j] = pq[j] = pk[j] = 0.f;
+#pragma unroll 2
+        for (int v = 0; v < D; v += 4) {
+            const f32x4 x0 = lds4(sX + bt * LD + v), o0 = lds4(sO + bt * LD + v), u0 = lds4(sU + bt * LD + v);
+            f32x4 s4[4], d4[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                s4[j] = lds4(sB2 + (bd + j) * LD + v);
+                d4[j] = lds4(sB + (bd + j) * LD + v);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                pe[j] = dot4(x0, s4[j], pe[j]);
+                pq[j] = dot4(o0, s4[j], pq[j]);
+                pk[j] = dot4(u0, d4[j], pk[j]);
+            }
+        }
+        const size_t o = ucd + (size_t)bt * D + blk * 32 + bd;
+        sts4(a.wdE + o, -f32x4{pe[0], pe[1], pe[2], pe[3]});
+        sts4(a.wdQ + o, a.scale * f32x4{pq[0], pq[1], pq[2], pq[3]});
+        sts4(a.wdK + o, f32x4{pk[0], pk[1], pk[2], pk[3]});
+        {  // dGamma of the block's 32 rows: TG consecutive threads per row, D / TG columns each
+            constexpr int TG = D / 4 < 16 ? D / 4 : 16;
+            const int r = tid / TG, c0 = (tid % TG) * (D / TG);
+            float acc = 0.f;
+            if (r < 32)
+#pragma unroll
+                for (int v = 0; v < D / TG; v += 4)
+                    acc = dot4(lds4(sB + r * LD + c0 + v), lds4(sB2 + r * LD + c0 + v), acc);
+#pragma unroll
+            for (int off = 1; off < TG; off <<= 1) acc += __shfl_xor(acc, off);
+            if (r < 32 && tid % TG == 0) a.wdGam[(size_t)u * D + blk * 32 + r] = acc;
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
