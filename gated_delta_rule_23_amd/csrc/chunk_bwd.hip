@@ -133,36 +133,34 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // (I + T) x = r for one column x (in registers, r on entry), T strictly
-// lower triangular, row-major with row stride C in shared memory:
-// x_i = r_i - sum_{m < i} T_im x_m, rows in order.
-__device__ __forceinline__ void solve_lower(float (&x)[C], const float *sT) {
+// lower triangular. Right-looking: once x_m is final it is taken out of every
+// later row at once, so the dependent chain is one multiply-add per row and
+// the rest is independent work. sTt = T^T, row-major with row stride C
+// (row m = column m of T, 16-byte aligned rows).
+__device__ __forceinline__ void solve_lower(float (&x)[C], const float *sTt) {
 #pragma unroll
-    for (int i = 1; i < C; ++i) {
-        float acc = x[i];
+    for (int m = 0; m < C - 1; ++m) {
 #pragma unroll
-        for (int m4 = 0; m4 < i; m4 += 4) {
-            const f32x4 t = lds4(sT + i * C + m4);
+        for (int i4 = (m + 1) & ~3; i4 < C; i4 += 4) {
+            const f32x4 t = lds4(sTt + m * C + i4);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                if (m4 + r < i) acc = fmaf(-t[r], x[m4 + r], acc);
+                if (i4 + r > m) x[i4 + r] = fmaf(-t[r], x[m], x[i4 + r]);
         }
-        x[i] = acc;
     }
 }
-// (I + T)^T x = r, with sTt = T^T (row i = column i of T), rows from the
-// last: x_i = r_i - sum_{m > i} T_mi x_m.
-__device__ __forceinline__ void solve_upper(float (&x)[C], const float *sTt) {
+// (I + T)^T x = r, rows from the last: x_i = r_i - sum_{m > i} T_mi x_m,
+// right-looking as above. sT = T, row-major with row stride C.
+__device__ __forceinline__ void solve_upper(float (&x)[C], const float *sT) {
 #pragma unroll
-    for (int i = C - 2; i >= 0; --i) {
-        float acc = x[i];
+    for (int m = C - 1; m > 0; --m) {
 #pragma unroll
-        for (int m4 = (i + 1) & ~3; m4 < C; m4 += 4) {
-            const f32x4 t = lds4(sTt + i * C + m4);
+        for (int i4 = 0; i4 < m; i4 += 4) {
+            const f32x4 t = lds4(sT + m * C + i4);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                if (m4 + r > i) acc = fmaf(-t[r], x[m4 + r], acc);
+                if (i4 + r < m) x[i4 + r] = fmaf(-t[r], x[m], x[i4 + r]);
         }
-        x[i] = acc;
     }
 }
 
@@ -195,7 +193,7 @@ template <typename IO, int D, bool CHAN, bool BW>
 __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
     constexpr int LD = Cfg<D>::LD, NL = Cfg<D>::NL, R0 = C * LD > C * C ? C * LD : C * C;
     extern __shared__ __align__(16) float smem[];
-    float *sQ = smem;           // q (Q~ with a per-channel decay); then T, row stride C
+    float *sQ = smem;           // q (Q~ with a per-channel decay); then T^T, row stride C
     float *sK = sQ + R0;        // k (K~)
     float *sE = sK + C * LD;    // e, then E~, then Y
     float *sZ = sE + C * LD;    // per-channel decay: g, then G; then z, then U_z
@@ -339,9 +337,11 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) a.wAt[(size_t)u * C * C + (size_t)(c0 + j) * C + t] = aA[i][j];
         }
-        __syncthreads();  // q, k and e tiles read: T goes where q was
+        __syncthreads();  // q, k and e tiles read: T^T goes where q was
 #pragma unroll
-        for (int i = 0; i < 2; ++i) sts4(sQ + (r0 + i) * C + c0, f32x4{aT[i][0], aT[i][1], aT[i][2], aT[i][3]});
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sQ[(c0 + j) * C + r0 + i] = aT[i][j];
     }
     // Right-hand sides: E~ (scalar decay: the raw e scaled by exp(G_t)) and z.
     {
@@ -646,7 +646,7 @@ __global__ __launch_bounds__(NT) void cb_grad_s(ChunkBwdArgs a) {
     constexpr int LD = Cfg<D>::LD, NL = Cfg<D>::NL, R0 = C * C > 32 * LD ? C * C : 32 * LD;
     constexpr int NG = 32 * D / 4, NB = (NG + NT - 1) / NT, NTT = C * C / (4 * NT);  // 4-element groups: S block, T
     extern __shared__ __align__(16) float smem[];
-    float *sT = smem;  // T^T, row stride C; later 32 rows of S
+    float *sT = smem;  // T, row stride C; later 32 rows of S
     float *sX = sT + R0, *sU = sX + C * LD, *sO = sU + C * LD, *sB = sO + C * LD;
     const int tid = threadIdx.x, u = blockIdx.x;
     const Unit x = decode(a, u);
@@ -672,11 +672,7 @@ __global__ __launch_bounds__(NT) void cb_grad_s(ChunkBwdArgs a) {
             sts4(sO + t * LD + d, rO[l]);
         }
 #pragma unroll
-        for (int l = 0; l < NTT; ++l) {
-            const int e = 4 * (l * NT + tid), t = e / C, j = e - t * C;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sT[(j + r) * C + t] = rT[l][r];
-        }
+        for (int l = 0; l < NTT; ++l) sts4(sT + 4 * (l * NT + tid), rT[l]);  // T, row stride C
     }
     __syncthreads();
     if (tid < D) {  // one column of dU per thread
@@ -737,7 +733,7 @@ __global__ __launch_bounds__(NT) void cb_grad_s(ChunkBwdArgs a) {
     }
     // Products with S and with dS_next, 32 state rows at a time; the next
     // block's rows are fetched into registers while the current one is used.
-    float *sB2 = sT;  // S rows of the block (T^T is no longer needed)
+    float *sB2 = sT;  // S rows of the block (T is no longer needed)
     const int bt = tid >> 3, bd = (tid & 7) * 4;
     f32x4 rb[NB], rs[NB];
     const auto fetch = [&](int blk) {
