@@ -83,6 +83,14 @@ def test_backward_grouped_heads(decay, gates):
     _check(got, ref, 1e-4)
 
 
+@pytest.mark.parametrize("decay,gates", [("channel", "beta"), ("scalar", "bw")])
+def test_backward_ungrouped_heads(decay, gates):
+    """As many QK heads as V heads (the KDA and GDN-2 layouts)."""
+    wl = small_workload("bf16", 64, decay, gates, T=37, B=2, Hqk=3, Hv=3, S0=True, scale=0.5)
+    got, ref = _run(wl, seed=15)
+    _check(got, ref, 1e-4)
+
+
 def test_backward_qwen_shape_medium():
     wl = gs.QWEN_GDN_PREFILL.scaled(T=300, Hqk=2, Hv=6, name="qwen_like_T300")
     got, ref = _run(wl, seed=7)

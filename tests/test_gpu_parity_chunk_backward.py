@@ -96,6 +96,15 @@ def test_chunk_backward_grouped_heads(decay, gates):
     _check(got, ref, 1e-4)
 
 
+@pytest.mark.parametrize("decay,gates", [("channel", "beta"), ("scalar", "bw"), ("none", "beta")])
+def test_chunk_backward_ungrouped_heads(decay, gates):
+    """As many QK heads as V heads (the KDA and GDN-2 layouts): dq and dk are
+    written directly, without the sum over grouped heads."""
+    wl = small_workload("bf16", 64, decay, gates, T=130, B=2, Hqk=3, Hv=3, S0=True, scale=0.5)
+    got, ref = _run(wl, seed=15)
+    _check(got, ref, 1e-4)
+
+
 @pytest.mark.parametrize("io,D", [("f32", 32), ("bf16", 128)])
 def test_chunk_backward_strong_scalar_decay(io, D):
     """Per-token decays exp(g) with g = log sigmoid(-(2 + N(0, 1))): over a
