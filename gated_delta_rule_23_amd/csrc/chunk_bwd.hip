@@ -734,7 +734,6 @@ __global__ __launch_bounds__(NT) void cb_grad_s(ChunkBwdArgs a) {
     // Products with S and with dS_next, 32 state rows at a time; the next
     // block's rows are fetched into registers while the current one is used.
     float *sB2 = sT;  // S rows of the block (T is no longer needed)
-    const int bt = tid >> 3, bd = (tid & 7) * 4;
     f32x4 rb[NB], rs[NB];
     const auto fetch = [&](int blk) {
 #pragma unroll
@@ -759,29 +758,30 @@ __global__ __launch_bounds__(NT) void cb_grad_s(ChunkBwdArgs a) {
         }
         if (blk + 1 < D / 32) fetch(blk + 1);
         __syncthreads();
-        float pe[4], pq[4], pk[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) pe[j] = pq[j] = pk[j] = 0.f;
-#pragma unroll 2
-        for (int v = 0; v < D; v += 4) {
-            const f32x4 x0 = lds4(sX + bt * LD + v), o0 = lds4(sO + bt * LD + v), u0 = lds4(sU + bt * LD + v);
-            f32x4 s4[4], d4[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                s4[j] = lds4(sB2 + (bd + j) * LD + v);
-                d4[j] = lds4(sB + (bd + j) * LD + v);
+        {
+            // The block's 64 x 32 outputs of each product on the matrix cores
+            // (fp32 in, fp32 accumulate): wave w takes the 16 x 16 tile
+            // (rows 16 (w / 2), columns 16 (w % 2)). A lane holds rows
+            // 4 (l / 16) + r of column l % 16 of its tile.
+            const int w = tid >> 6, l = tid & 63, rt = w >> 1, ct = w & 1;
+            const int ao = (rt * 16 + (l & 15)) * LD + (l >> 4), bo = (ct * 16 + (l & 15)) * LD + (l >> 4);
+            f32x4 ae = zero4(), aq = zero4(), ak = zero4();
+#pragma unroll 4
+            for (int v = 0; v < D; v += 4) {
+                const float bs = sB2[bo + v], bdv = sB[bo + v];
+                ae = __builtin_amdgcn_mfma_f32_16x16x4f32(sX[ao + v], bs, ae, 0, 0, 0);
+                aq = __builtin_amdgcn_mfma_f32_16x16x4f32(sO[ao + v], bs, aq, 0, 0, 0);
+                ak = __builtin_amdgcn_mfma_f32_16x16x4f32(sU[ao + v], bdv, ak, 0, 0, 0);
             }
+            const int col = blk * 32 + ct * 16 + (l & 15);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                pe[j] = dot4(x0, s4[j], pe[j]);
-                pq[j] = dot4(o0, s4[j], pq[j]);
-                pk[j] = dot4(u0, d4[j], pk[j]);
+            for (int r = 0; r < 4; ++r) {
+                const size_t o = ucd + (size_t)(rt * 16 + 4 * (l >> 4) + r) * D + col;
+                a.wdE[o] = -ae[r];
+                a.wdQ[o] = a.scale * aq[r];
+                a.wdK[o] = ak[r];
             }
         }
-        const size_t o = ucd + (size_t)bt * D + blk * 32 + bd;
-        sts4(a.wdE + o, -f32x4{pe[0], pe[1], pe[2], pe[3]});
-        sts4(a.wdQ + o, a.scale * f32x4{pq[0], pq[1], pq[2], pq[3]});
-        sts4(a.wdK + o, f32x4{pk[0], pk[1], pk[2], pk[3]});
         {  // dGamma of the block's 32 rows: TG consecutive threads per row, D / TG columns each
             constexpr int TG = D / 4 < 16 ? D / 4 : 16;
             const int r = tid / TG, c0 = (tid % TG) * (D / TG);
