@@ -171,11 +171,11 @@ constexpr size_t prep_smem() {
 }
 template <int D>
 constexpr size_t fsweep_smem() {
-    return ((size_t)D * LB + (size_t)C * LB + (size_t)C * (D + 4) + (size_t)D * LC) * 4;
+    return ((size_t)D * LB + (size_t)C * LB + (size_t)C * (D + 4) + (size_t)D * LC + D) * 4;
 }
 template <int D>
 constexpr size_t bsweep_smem() {
-    return ((size_t)D * LB + 2 * (size_t)C * LB + (size_t)C * LC + (size_t)C * (D + 4) + 2 * (size_t)D * LC) * 4;
+    return ((size_t)D * LB + 2 * (size_t)C * LB + (size_t)C * LC + (size_t)C * (D + 4) + 2 * (size_t)D * LC + D) * 4;
 }
 template <int D>
 constexpr size_t grad_s_smem() {
@@ -397,221 +397,220 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
 // whole workgroup together) and moved to shared memory at the start of the
 // chunk, so that the loop reads its operands from shared memory.
 
+// Products in the sweeps run on the matrix cores (fp32 in, fp32
+// accumulate), one 16 x 16 output tile per wave at a time: a lane holds rows
+// 4 (l / 16) + r, r < 4, of column l % 16 of the tile. mfma_kloop adds
+// A[16 x K] B[K x 16] with A row-major (row stride lda) and B row-major
+// (row stride ldb); K a multiple of 4.
+template <int K>
+__device__ __forceinline__ f32x4 mfma_kloop(f32x4 acc, const float *A, int lda, const float *B, int ldb) {
+    const int l = threadIdx.x & 63;
+    const float *pa = A + (l & 15) * lda + (l >> 4), *pb = B + (l >> 4) * ldb + (l & 15);
+#pragma unroll 8
+    for (int k = 0; k < K; k += 4) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[k], pb[k * ldb], acc, 0, 0, 0);
+    return acc;
+}
+
 // 2. Forward over chunks: the state entering each chunk, and U = U_z - Y S.
-//    Thread: U row ut, columns uj..uj+3; state row sd, columns sj..sj+CPT-1.
+//    Wave w: U tile (rows 16 (w / 2), columns 16 (w % 2)); state tiles w and
+//    w + 8 of the (D / 16) x 2 tiles of the state.
 template <int D>
 __device__ __forceinline__ void fsweep(const ChunkBwdArgs &a, float *smem, int item) {
     using K = SwCfg<D>;
-    constexpr int NTL = K::NTL, TPR = K::TPR, CPT = K::CPT, NL = K::NL, LD = D + 4;
+    constexpr int NTL = K::NTL, NL = K::NL, LD = D + 4, NST = D / 16 * 2;
     float *sS = smem, *sU = sS + D * LB, *sY = sU + C * LB, *sKt = sY + C * LD;  // Kend transposed: [D][LC]
+    float *sGam = sKt + D * LC;
     const int tid = threadIdx.x, tile = item % NTL, bh = item / NTL, col0 = tile * BV;
+    const int w = tid >> 6, l = tid & 63, rt = w >> 1, ct = w & 1;
     const size_t sb = (size_t)bh * D * D;
     for (int i = tid; i < D * BV / 4; i += NS) {
         const int d = 4 * i / BV, j = 4 * i - d * BV;
         sts4(sS + d * LB + j, a.S0 ? lds4(a.S0 + sb + (size_t)d * D + col0 + j) : zero4());
     }
-    const int ut = tid >> 3, uj = (tid & 7) * 4;
-    const bool srow = tid < D * TPR;  // holds a state row
-    const int sd = srow ? tid / TPR : 0, sj = (tid % TPR) * CPT;
-    f32x4 pY[NL], pK[NL], pZ;
-    float pg;
+    f32x4 pY[NL], pK[NL];
+    float pZ[4], pg;
     const auto fetch = [&](int c) {
         const size_t u = (size_t)bh * a.NC + c, ucd = u * C * D;
 #pragma unroll
-        for (int l = 0; l < NL; ++l) {
-            const int e = 4 * (l * NS + tid);
-            pY[l] = lds4(a.wY + ucd + e);    // [C][D]
-            pK[l] = lds4(a.wKet + ucd + e);  // [D][C]
+        for (int l2 = 0; l2 < NL; ++l2) {
+            const int e = 4 * (l2 * NS + tid);
+            pY[l2] = lds4(a.wY + ucd + e);    // [C][D]
+            pK[l2] = lds4(a.wKet + ucd + e);  // [D][C]
         }
-        pZ = lds4(a.wUz + ucd + (size_t)ut * D + col0 + uj);
-        pg = a.wGam[u * D + sd];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pZ[r] = a.wUz[ucd + (size_t)(rt * 16 + 4 * (l >> 4) + r) * D + col0 + ct * 16 + (l & 15)];
+        pg = tid < D ? a.wGam[u * D + tid] : 0.f;
     };
     fetch(0);
     for (int c = 0; c < a.NC; ++c) {
         const size_t u = (size_t)bh * a.NC + c, ucd = u * C * D;
         lds_barrier();  // the previous chunk is done with the operand tiles; S written
 #pragma unroll
-        for (int l = 0; l < NL; ++l) {
+        for (int l2 = 0; l2 < NL; ++l2) {
             int e, t, d;
-            rcs<D>(l, e, t, d);
-            sts4(sY + t * LD + d, pY[l]);
-            rcs<C>(l, e, d, t);
-            sts4(sKt + d * LC + t, pK[l]);
+            rcs<D>(l2, e, t, d);
+            sts4(sY + t * LD + d, pY[l2]);
+            rcs<C>(l2, e, d, t);
+            sts4(sKt + d * LC + t, pK[l2]);
         }
-        f32x4 acc = pZ;
-        const float gam = pg;
+        if (tid < D) sGam[tid] = pg;
+        float uz[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) uz[r] = pZ[r];
         if (c + 1 < a.NC) fetch(c + 1);
         for (int i = tid; i < D * BV / 4; i += NS) {
             const int d = 4 * i / BV, j = 4 * i - d * BV;
             sts4(a.wS + u * D * D + (size_t)d * D + col0 + j, lds4(sS + d * LB + j));
         }
         lds_barrier();
-        // Operands of 8 rows of S at a time are read before they are used.
-#pragma unroll 1
-        for (int d = 0; d < D; d += 8) {
-            const f32x4 y0 = lds4(sY + ut * LD + d), y1 = lds4(sY + ut * LD + d + 4);
-            f32x4 s0[8];
+        {  // U = U_z - Y S
+            const f32x4 p = mfma_kloop<D>(zero4(), sY + rt * 16 * LD, LD, sS + ct * 16, LB);
+            const int col = ct * 16 + (l & 15);
 #pragma unroll
-            for (int r = 0; r < 8; ++r) s0[r] = lds4(sS + (d + r) * LB + uj);
-#pragma unroll
-            for (int r = 0; r < 8; ++r) acc -= (r < 4 ? y0[r & 3] : y1[r & 3]) * s0[r];
-        }
-        sts4(sU + ut * LB + uj, acc);
-        sts4(a.wU + ucd + (size_t)ut * D + col0 + uj, acc);
-        lds_barrier();
-        f32x4 sv[CPT / 4];
-#pragma unroll
-        for (int q = 0; q < CPT / 4; ++q) sv[q] = gam * lds4(sS + sd * LB + sj + 4 * q);
-#pragma unroll 1
-        for (int t = 0; t < (srow ? C : 0); t += 8) {
-            const f32x4 k0 = lds4(sKt + sd * LC + t), k1 = lds4(sKt + sd * LC + t + 4);
-            f32x4 uu[8][CPT / 4];
-#pragma unroll
-            for (int r = 0; r < 8; ++r)
-#pragma unroll
-                for (int q = 0; q < CPT / 4; ++q) uu[r][q] = lds4(sU + (t + r) * LB + sj + 4 * q);
-#pragma unroll
-            for (int r = 0; r < 8; ++r)
-#pragma unroll
-                for (int q = 0; q < CPT / 4; ++q) sv[q] += (r < 4 ? k0[r & 3] : k1[r & 3]) * uu[r][q];
+            for (int r = 0; r < 4; ++r) {
+                const int row = rt * 16 + 4 * (l >> 4) + r;
+                const float uv = uz[r] - p[r];
+                sU[row * LB + col] = uv;
+                a.wU[ucd + (size_t)row * D + col0 + col] = uv;
+            }
         }
         lds_barrier();
-        if (srow)
+        // S = Gamma . S + Kend^T U
+        f32x4 sn[2];
 #pragma unroll
-            for (int q = 0; q < CPT / 4; ++q) sts4(sS + sd * LB + sj + 4 * q, sv[q]);
+        for (int q = 0; q < 2; ++q) {
+            const int st = w + 8 * q, dt = st >> 1, sc = st & 1;
+            if (st < NST) {
+                const f32x4 p = mfma_kloop<C>(zero4(), sKt + dt * 16 * LC, LC, sU + sc * 16, LB);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = dt * 16 + 4 * (l >> 4) + r;
+                    sn[q][r] = sGam[row] * sS[row * LB + sc * 16 + (l & 15)] + p[r];
+                }
+            }
+        }
+        lds_barrier();
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int st = w + 8 * q, dt = st >> 1, sc = st & 1;
+            if (st < NST)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sS[(dt * 16 + 4 * (l >> 4) + r) * LB + sc * 16 + (l & 15)] = sn[q][r];
+        }
     }
 }
 
 // 3. Backward over chunks for the same work items: X = dL/d(state leaving
-//    the chunk), dU, and X for the chunk before.
+//    the chunk), dU, and X for the chunk before. Tiles per wave as above.
 template <typename IO, int D>
 __device__ __forceinline__ void bsweep(const ChunkBwdArgs &a, float *smem, int item) {
     using K = SwCfg<D>;
-    constexpr int NTL = K::NTL, TPR = K::TPR, CPT = K::CPT, NL = K::NL, LD = D + 4;
+    constexpr int NTL = K::NTL, NL = K::NL, LD = D + 4, NST = D / 16 * 2;
     constexpr int NA = C * C / (4 * NS), NO = C * BV / (4 * NS);  // 4-element groups per thread: A, dO tile
     float *sX = smem, *sO = sX + D * LB, *sdU = sO + C * LB;
     float *sAt = sdU + C * LB;   // A^T [C][LC]
     float *sK = sAt + C * LC;    // Kend [C][LD]
     float *sQt = sK + C * LD;    // Q~^T [D][LC]
     float *sYt = sQt + D * LC;   // Y^T [D][LC]
+    float *sGam = sYt + D * LC;  // [D]
     const int tid = threadIdx.x, tile = item % NTL, bh = item / NTL, col0 = tile * BV;
+    const int w = tid >> 6, l = tid & 63, rt = w >> 1, ct = w & 1;
     const int b = bh / a.Hv, h = bh - b * a.Hv;
     const size_t sb = (size_t)bh * D * D;
     for (int i = tid; i < D * BV / 4; i += NS) {
         const int d = 4 * i / BV, j = 4 * i - d * BV;
         sts4(sX + d * LB + j, a.dST ? lds4(a.dST + sb + (size_t)d * D + col0 + j) : zero4());
     }
-    const int ut = tid >> 3, uj = (tid & 7) * 4;
-    const bool srow = tid < D * TPR;  // holds a state row
-    const int sd = srow ? tid / TPR : 0, sj = (tid % TPR) * CPT;
     f32x4 pY[NL], pK[NL], pQ[NL], pA[NA], pO[NO];
     float pg;
     const auto fetch = [&](int c) {
         const size_t u = (size_t)bh * a.NC + c, ucd = u * C * D;
         const int t0 = c * C, n = min(C, a.T - t0);
 #pragma unroll
-        for (int l = 0; l < NL; ++l) {
-            const int e = 4 * (l * NS + tid);
-            pY[l] = lds4(a.wYt + ucd + e);  // [D][C]
-            pK[l] = lds4(a.wKe + ucd + e);  // [C][D]
-            pQ[l] = lds4(a.wQt + ucd + e);  // [D][C]
+        for (int l2 = 0; l2 < NL; ++l2) {
+            const int e = 4 * (l2 * NS + tid);
+            pY[l2] = lds4(a.wYt + ucd + e);  // [D][C]
+            pK[l2] = lds4(a.wKe + ucd + e);  // [C][D]
+            pQ[l2] = lds4(a.wQt + ucd + e);  // [D][C]
         }
 #pragma unroll
-        for (int l = 0; l < NA; ++l) pA[l] = lds4(a.wAt + u * C * C + 4 * (l * NS + tid));
+        for (int l2 = 0; l2 < NA; ++l2) pA[l2] = lds4(a.wAt + u * C * C + 4 * (l2 * NS + tid));
 #pragma unroll
-        for (int l = 0; l < NO; ++l) {
+        for (int l2 = 0; l2 < NO; ++l2) {
             int e, t, j;
-            rcs<BV>(l, e, t, j);
-            pO[l] = t < n ? ld4io<IO>(a.dO, (((size_t)b * a.T + t0 + t) * a.Hv + h) * D + col0 + j) : zero4();
+            rcs<BV>(l2, e, t, j);
+            pO[l2] = t < n ? ld4io<IO>(a.dO, (((size_t)b * a.T + t0 + t) * a.Hv + h) * D + col0 + j) : zero4();
         }
-        pg = a.wGam[u * D + sd];
+        pg = tid < D ? a.wGam[u * D + tid] : 0.f;
     };
     fetch(a.NC - 1);
     for (int c = a.NC - 1; c >= 0; --c) {
         const size_t u = (size_t)bh * a.NC + c, ucd = u * C * D;
         lds_barrier();  // X written; the previous chunk is done with the operand tiles
 #pragma unroll
-        for (int l = 0; l < NL; ++l) {
+        for (int l2 = 0; l2 < NL; ++l2) {
             int e, t, d;
-            rcs<D>(l, e, t, d);
-            sts4(sK + t * LD + d, pK[l]);
-            rcs<C>(l, e, d, t);
-            sts4(sYt + d * LC + t, pY[l]);
-            sts4(sQt + d * LC + t, pQ[l]);
+            rcs<D>(l2, e, t, d);
+            sts4(sK + t * LD + d, pK[l2]);
+            rcs<C>(l2, e, d, t);
+            sts4(sYt + d * LC + t, pY[l2]);
+            sts4(sQt + d * LC + t, pQ[l2]);
         }
 #pragma unroll
-        for (int l = 0; l < NA; ++l) {
+        for (int l2 = 0; l2 < NA; ++l2) {
             int e, j, t;
-            rcs<C>(l, e, j, t);
-            sts4(sAt + j * LC + t, pA[l]);
+            rcs<C>(l2, e, j, t);
+            sts4(sAt + j * LC + t, pA[l2]);
         }
 #pragma unroll
-        for (int l = 0; l < NO; ++l) {
+        for (int l2 = 0; l2 < NO; ++l2) {
             int e, t, j;
-            rcs<BV>(l, e, t, j);
-            sts4(sO + t * LB + j, pO[l]);
+            rcs<BV>(l2, e, t, j);
+            sts4(sO + t * LB + j, pO[l2]);
         }
-        const float gam = pg;
+        if (tid < D) sGam[tid] = pg;
         if (c > 0) fetch(c - 1);
         for (int i = tid; i < D * BV / 4; i += NS) {
             const int d = 4 * i / BV, j = 4 * i - d * BV;
             sts4(a.wdS + u * D * D + (size_t)d * D + col0 + j, lds4(sX + d * LB + j));
         }
         lds_barrier();
-        // dU (row ut) = s (A^T dO)_ut + Kend_ut X
-        f32x4 p = zero4(), k = zero4();
-#pragma unroll 1
-        for (int t = 0; t < C; t += 8) {
-            const f32x4 a0 = lds4(sAt + ut * LC + t), a1 = lds4(sAt + ut * LC + t + 4);
-            f32x4 o[8];
+        {  // dU = s A^T dO + Kend X
+            const f32x4 p = mfma_kloop<C>(zero4(), sAt + rt * 16 * LC, LC, sO + ct * 16, LB);
+            const f32x4 k = mfma_kloop<D>(zero4(), sK + rt * 16 * LD, LD, sX + ct * 16, LB);
+            const int col = ct * 16 + (l & 15);
 #pragma unroll
-            for (int r = 0; r < 8; ++r) o[r] = lds4(sO + (t + r) * LB + uj);
-#pragma unroll
-            for (int r = 0; r < 8; ++r) p += (r < 4 ? a0[r & 3] : a1[r & 3]) * o[r];
-        }
-#pragma unroll 1
-        for (int d = 0; d < D; d += 8) {
-            const f32x4 c0 = lds4(sK + ut * LD + d), c1 = lds4(sK + ut * LD + d + 4);
-            f32x4 xv[8];
-#pragma unroll
-            for (int r = 0; r < 8; ++r) xv[r] = lds4(sX + (d + r) * LB + uj);
-#pragma unroll
-            for (int r = 0; r < 8; ++r) k += (r < 4 ? c0[r & 3] : c1[r & 3]) * xv[r];
-        }
-        const f32x4 du = a.scale * p + k;
-        sts4(sdU + ut * LB + uj, du);
-        sts4(a.wdU + ucd + (size_t)ut * D + col0 + uj, du);
-        lds_barrier();
-        // X (row sd) = Gamma_sd X + s Q~^T dO - Y^T dU
-        f32x4 xa[CPT / 4], qa[CPT / 4];
-#pragma unroll
-        for (int q = 0; q < CPT / 4; ++q) {
-            xa[q] = gam * lds4(sX + sd * LB + sj + 4 * q);
-            qa[q] = zero4();
-        }
-#pragma unroll 1
-        for (int t = 0; t < (srow ? C : 0); t += 4) {
-            const f32x4 qv = lds4(sQt + sd * LC + t), yv = lds4(sYt + sd * LC + t);
-            f32x4 oo[4][CPT / 4], uu[4][CPT / 4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int q = 0; q < CPT / 4; ++q) {
-                    oo[r][q] = lds4(sO + (t + r) * LB + sj + 4 * q);
-                    uu[r][q] = lds4(sdU + (t + r) * LB + sj + 4 * q);
-                }
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int q = 0; q < CPT / 4; ++q) {
-                    qa[q] += qv[r] * oo[r][q];
-                    xa[q] -= yv[r] * uu[r][q];
-                }
+            for (int r = 0; r < 4; ++r) {
+                const int row = rt * 16 + 4 * (l >> 4) + r;
+                const float du = fmaf(a.scale, p[r], k[r]);
+                sdU[row * LB + col] = du;
+                a.wdU[ucd + (size_t)row * D + col0 + col] = du;
+            }
         }
         lds_barrier();
-        if (srow)
+        // X = Gamma . X + s Q~^T dO - Y^T dU
+        f32x4 xn[2];
 #pragma unroll
-            for (int q = 0; q < CPT / 4; ++q) sts4(sX + sd * LB + sj + 4 * q, a.scale * qa[q] + xa[q]);
+        for (int q = 0; q < 2; ++q) {
+            const int st = w + 8 * q, dt = st >> 1, sc = st & 1;
+            if (st < NST) {
+                const f32x4 pq = mfma_kloop<C>(zero4(), sQt + dt * 16 * LC, LC, sO + sc * 16, LB);
+                const f32x4 py = mfma_kloop<C>(zero4(), sYt + dt * 16 * LC, LC, sdU + sc * 16, LB);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = dt * 16 + 4 * (l >> 4) + r;
+                    xn[q][r] = sGam[row] * sX[row * LB + sc * 16 + (l & 15)] + a.scale * pq[r] - py[r];
+                }
+            }
+        }
+        lds_barrier();
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int st = w + 8 * q, dt = st >> 1, sc = st & 1;
+            if (st < NST)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sX[(dt * 16 + 4 * (l >> 4) + r) * LB + sc * 16 + (l & 15)] = xn[q][r];
+        }
     }
     lds_barrier();
     if (a.dS0)
@@ -692,43 +691,30 @@ __global__ __launch_bounds__(NT) void cb_grad_s(ChunkBwdArgs a) {
         sts4(a.wdU + ucd + e, lds4(sX + t * LD + d));  // dR replaces dU
     }
     {
-        const int r0 = (tid >> 4) * 2, c0 = (tid & 15) * 4;
-        float aT[2][4], aA[2][4];
+        // dT = -dR U^T (strictly lower) and dA = s dO U^T (lower) on the matrix
+        // cores: the 16 x 16 tiles of the two 64 x 64 results, 2 per wave; a
+        // tile above the diagonal is written as zeros.
+        const int w = tid >> 6, l = tid & 63;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) aT[i][j] = aA[i][j] = 0.f;
-        if (c0 <= r0 + 1) {
-#pragma unroll 2
-            for (int v = 0; v < D; v += 4) {
-                f32x4 x4[2], o4[2], u4[4];
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    x4[i] = lds4(sX + (r0 + i) * LD + v);
-                    o4[i] = lds4(sO + (r0 + i) * LD + v);
+        for (int p = 0; p < 2; ++p) {
+            const int tile = w + 8 * p, rt = tile >> 2, ct = tile & 3;
+            f32x4 at = zero4(), aa = zero4();
+            if (ct <= rt) {
+                const int ao = (rt * 16 + (l & 15)) * LD + (l >> 4), bo = (ct * 16 + (l & 15)) * LD + (l >> 4);
+#pragma unroll 4
+                for (int v = 0; v < D; v += 4) {
+                    const float bu = sU[bo + v];
+                    at = __builtin_amdgcn_mfma_f32_16x16x4f32(sX[ao + v], bu, at, 0, 0, 0);
+                    aa = __builtin_amdgcn_mfma_f32_16x16x4f32(sO[ao + v], bu, aa, 0, 0, 0);
                 }
-#pragma unroll
-                for (int j = 0; j < 4; ++j) u4[j] = lds4(sU + (c0 + j) * LD + v);
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        aT[i][j] = dot4(x4[i], u4[j], aT[i][j]);
-                        aA[i][j] = dot4(o4[i], u4[j], aA[i][j]);
-                    }
             }
-        }
+            const int j = ct * 16 + (l & 15);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int t = r0 + i;
-            f32x4 dt, da;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                dt[j] = c0 + j < t ? -aT[i][j] : 0.f;
-                da[j] = c0 + j <= t ? a.scale * aA[i][j] : 0.f;
+            for (int r = 0; r < 4; ++r) {
+                const int t = rt * 16 + 4 * (l >> 4) + r;
+                a.wdT[ucc + (size_t)t * C + j] = j < t ? -at[r] : 0.f;
+                a.wdA[ucc + (size_t)t * C + j] = j <= t ? a.scale * aa[r] : 0.f;
             }
-            sts4(a.wdT + ucc + (size_t)t * C + c0, dt);
-            sts4(a.wdA + ucc + (size_t)t * C + c0, da);
         }
     }
     // Products with S and with dS_next, 32 state rows at a time; the next
