@@ -411,6 +411,16 @@ __device__ __forceinline__ f32x4 mfma_kloop(f32x4 acc, const float *A, int lda, 
     return acc;
 }
 
+// The same with A given transposed: A[row][k] at At[k * ldat + row].
+template <int K>
+__device__ __forceinline__ f32x4 mfma_kloop_at(f32x4 acc, const float *At, int ldat, const float *B, int ldb) {
+    const int l = threadIdx.x & 63;
+    const float *pa = At + (l >> 4) * ldat + (l & 15), *pb = B + (l >> 4) * ldb + (l & 15);
+#pragma unroll 8
+    for (int k = 0; k < K; k += 4) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[k * ldat], pb[k * ldb], acc, 0, 0, 0);
+    return acc;
+}
+
 // 2. Forward over chunks: the state entering each chunk, and U = U_z - Y S.
 //    Wave w: U tile (rows 16 (w / 2), columns 16 (w % 2)); state tiles w and
 //    w + 8 of the (D / 16) x 2 tiles of the state.
@@ -791,9 +801,9 @@ __global__ __launch_bounds__(NT) void cb_grad_out(ChunkBwdArgs a) {
     using K = Cfg<D>;
     constexpr int LD = K::LD, NL = K::NL, NCG = K::NCG, RT = K::RT, NRG = K::NRG, NTT = C * C / (4 * NT);
     extern __shared__ __align__(16) float smem[];
-    float *sP1 = smem;            // e (E~): left factor of T
-    float *sP2 = sP1 + C * LD;    // k (K~): right factor of T and A
-    float *sP3 = sP2 + C * LD;    // q (Q~): left factor of A
+    float *sP1 = smem;            // e (E~): left factor of T; then X_e
+    float *sP2 = sP1 + C * LD;    // k (K~): right factor of T and A; then X_q
+    float *sP3 = sP2 + C * LD;    // q (Q~): left factor of A; then X_k
     float *sdT = sP3 + C * LD;    // dT, for a scalar decay times exp(G_t - G_j); then dG [C][LD]
     float *sdA = sdT + C * LC;
     // Reductions go through per-thread parts summed in a fixed order, so that
@@ -880,33 +890,36 @@ __global__ __launch_bounds__(NT) void cb_grad_out(ChunkBwdArgs a) {
         for (int r = 0; r < 32; ++r) cs += sColP[r * C + tid];
         sCol[tid] = cs;
     }
-    // X_e = dT' P2, X_q = dA' P2, X_k = dT'^T P1 + dA'^T P3; thread = rows m0..m0+RT-1, columns n0..n0+3.
-    const int cg = tid % NCG, rg = tid / NCG, m0 = rg * RT, n0 = 4 * cg;
-    f32x4 xe[RT], xq[RT], xk[RT];
+    // X_e = dT' P2, X_q = dA' P2, X_k = dT'^T P1 + dA'^T P3 on the matrix
+    // cores: 16 x 16 output tiles, wave w taking tiles w, w + 8, ...; then
+    // through shared memory (where P1..P3 were) to the thread layout below.
+    {
+        constexpr int NTC = D / 16, NTW = C / 16 * NTC / 8;
+        const int w = tid >> 6, l = tid & 63;
+        f32x4 te[NTW], tq[NTW], tk[NTW];
 #pragma unroll
-    for (int i = 0; i < RT; ++i) xe[i] = xq[i] = xk[i] = zero4();
-#pragma unroll 2
-    for (int j = 0; j < C; j += 4) {
-        f32x4 dt4[RT], da4[RT];
-#pragma unroll
-        for (int i = 0; i < RT; ++i) {
-            dt4[i] = lds4(sdT + (m0 + i) * LC + j);
-            da4[i] = lds4(sdA + (m0 + i) * LC + j);
+        for (int q = 0; q < NTW; ++q) {
+            const int tile = w + 8 * q, rt = tile / NTC, ct = tile - rt * NTC;
+            te[q] = mfma_kloop<C>(zero4(), sdT + rt * 16 * LC, LC, sP2 + ct * 16, LD);
+            tq[q] = mfma_kloop<C>(zero4(), sdA + rt * 16 * LC, LC, sP2 + ct * 16, LD);
+            tk[q] = mfma_kloop_at<C>(zero4(), sdT + rt * 16, LC, sP1 + ct * 16, LD);
+            tk[q] = mfma_kloop_at<C>(tk[q], sdA + rt * 16, LC, sP3 + ct * 16, LD);
         }
+        __syncthreads();  // dT, dA and the P tiles read
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int jj = j + r;
-            const f32x4 p1 = lds4(sP1 + jj * LD + n0), p2 = lds4(sP2 + jj * LD + n0), p3 = lds4(sP3 + jj * LD + n0);
+        for (int q = 0; q < NTW; ++q) {
+            const int tile = w + 8 * q, rt = tile / NTC, ct = tile - rt * NTC;
 #pragma unroll
-            for (int i = 0; i < RT; ++i) {
-                const float tt = sdT[jj * LC + m0 + i], ta = sdA[jj * LC + m0 + i];
-                xe[i] += dt4[i][r] * p2;
-                xq[i] += da4[i][r] * p2;
-                xk[i] += tt * p1 + ta * p3;
+            for (int r = 0; r < 4; ++r) {
+                const int o = (rt * 16 + 4 * (l >> 4) + r) * LD + ct * 16 + (l & 15);
+                sP1[o] = te[q][r];
+                sP2[o] = tq[q][r];
+                sP3[o] = tk[q][r];
             }
         }
     }
-    __syncthreads();  // dT and dA read: their space holds dG from here
+    __syncthreads();  // X tiles written; dT's space holds dG from here
+    const int cg = tid % NCG, rg = tid / NCG, m0 = rg * RT, n0 = 4 * cg;
 
     f32x4 gend = zero4();
 #pragma unroll
@@ -923,14 +936,14 @@ __global__ __launch_bounds__(NT) void cb_grad_out(ChunkBwdArgs a) {
             const f32x4 qv = ld4io<IO>(a.q, iq), kv = ld4io<IO>(a.k, iq), vv = ld4io<IO>(a.v, iv);
             const f32x4 gb = BW ? ld4io<IO>(a.bg, iv) : splat(bt), gw = BW ? ld4io<IO>(a.wg, iv) : splat(bt);
             const f32x4 dEY = lds4(a.wdE + o), dQS = lds4(a.wdQ + o), dKE = lds4(a.wdK + o), dR = lds4(a.wdU + o);
-            const f32x4 de = (CHAN ? xe[i] * eg : xe[i]) + dEY * eg;
-            const f32x4 dq = (CHAN ? xq[i] * eg : xq[i]) + dQS * eg;
+            const f32x4 xe = lds4(sP1 + t * LD + n0), xq = lds4(sP2 + t * LD + n0), xk = lds4(sP3 + t * LD + n0);
+            const f32x4 emg = CHAN ? exp4(-G) : splat(1.f);
+            const f32x4 de = (CHAN ? xe * eg : xe) + dEY * eg;
+            const f32x4 dq = (CHAN ? xq * eg : xq) + dQS * eg;
             const f32x4 ke = kv * egend;
-            f32x4 dk = (CHAN ? xk[i] * exp4(-G) : xk[i]) + dKE * egend;
+            f32x4 dk = (CHAN ? xk * emg : xk) + dKE * egend;
             f32x4 dG = gb * kv * eg * dEY + qv * eg * dQS - ke * dKE;
-            if (CHAN)
-                dG += lds4(sP1 + t * LD + n0) * xe[i] - lds4(sP2 + t * LD + n0) * xk[i] +
-                      lds4(sP3 + t * LD + n0) * xq[i];
+            if (CHAN) dG += gb * kv * eg * xe - kv * emg * xk + qv * eg * xq;  // E~, K~, Q~ times their parts
             gend += ke * dKE;
             if (CHAN) sts4(sGt + t * LD + n0, dG);
             else dgs = dG[0] + dG[1] + dG[2] + dG[3];
