@@ -42,6 +42,7 @@ HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, published
 DECODE_COLD_LAYERS = 4        # states cycled in the decode "layers in turn" timing
 BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix, published
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published
+FP32_MFMA_PEAK_TFLOPS = 157.3    # MI355X dense fp32 matrix cores, published
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "gated_delta_rule_23_amd", "csrc")
@@ -369,9 +370,9 @@ def main(argv=None):
         bwd = {"entry": "gdr_chunk_bwd", "workload": wl.name, "calls": n_b, "launch": "hip_graph",
                "ms_per_call": b_ms, "tokens_per_s": wl.B * wl.T / (b_ms * 1e-3),
                "roofline": {"kernel": "cb_prep + cb_sweeps + cb_grad_s + cb_grad_out (+ cb_group_sum)",
-                            "bound": "alu", "achieved": c_flops / (b_ms * 1e-3) / 1e12,
-                            "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-                            "frac": c_flops / (b_ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
+                            "bound": "mfma", "dtype": "f32", "achieved": c_flops / (b_ms * 1e-3) / 1e12,
+                            "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                            "frac": c_flops / (b_ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS,
                             "algorithmic_flops": c_flops},
                "hbm": {"achieved": b_bytes / (b_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                        "frac": b_bytes / (b_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, "algorithmic_bytes": b_bytes,
