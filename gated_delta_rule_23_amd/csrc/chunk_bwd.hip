@@ -31,18 +31,20 @@
 // are kept per entry, exp(G_t - G_j) <= 1, so strong decays stay finite.
 //
 // Shared-memory tiles keep 16-byte aligned rows (stride a multiple of 4
-// floats) and the inner loops read them 16 bytes at a time; global arrays
-// are staged through registers with 16-byte (8-byte for bf16) loads.
+// floats); global arrays are staged through registers with 16-byte (8-byte
+// for bf16) loads. All arithmetic is fp32: the dense products of the sweeps,
+// of cb_grad_s and of cb_grad_out on the matrix cores
+// (v_mfma_f32_16x16x4_f32), the rest on the vector units.
 //
-// Four launches (five with grouped heads), all arithmetic in fp32:
+// Four launches (five with grouped heads):
 //  1. cb_prep (per chunk unit): G, the factors above, T and A, and the
 //     triangular solve (I + T)[Y | U_z] = [E~ | Z] by forward substitution.
 //  2. cb_sweeps, per (sequence, V head, 32 value columns) twice over: the
 //     states S entering every chunk and U, walking the chunks forward; and
 //     dS_next of every chunk and dU, walking them backward (dS_0 at the end).
-//  4. cb_grad_s (per unit): dR by back substitution, dT, dA and the products
+//  3. cb_grad_s (per unit): dR by back substitution, dT, dA and the products
 //     with S and dS_next.
-//  5. cb_grad_out (per unit): the products through T and A, the exponential
+//  4. cb_grad_out (per unit): the products through T and A, the exponential
 //     factors, the gates, and the reverse sums over the chunk giving dg; then
 //     (grouped heads) cb_group_sum adds the V heads' dq and dk per QK head.
 #include "common.hpp"
@@ -421,7 +423,7 @@ __device__ __forceinline__ f32x4 mfma_kloop_at(f32x4 acc, const float *At, int l
     return acc;
 }
 
-// 2. Forward over chunks: the state entering each chunk, and U = U_z - Y S.
+// 2a. Forward over chunks: the state entering each chunk, and U = U_z - Y S.
 //    Wave w: U tile (rows 16 (w / 2), columns 16 (w % 2)); state tiles w and
 //    w + 8 of the (D / 16) x 2 tiles of the state.
 template <int D>
@@ -510,7 +512,7 @@ __device__ __forceinline__ void fsweep(const ChunkBwdArgs &a, float *smem, int i
     }
 }
 
-// 3. Backward over chunks for the same work items: X = dL/d(state leaving
+// 2b. Backward over chunks for the same work items: X = dL/d(state leaving
 //    the chunk), dU, and X for the chunk before. Tiles per wave as above.
 template <typename IO, int D>
 __device__ __forceinline__ void bsweep(const ChunkBwdArgs &a, float *smem, int item) {
@@ -648,7 +650,7 @@ __global__ __launch_bounds__(NS) void cb_sweeps(ChunkBwdArgs a, int items, int P
 }
 
 // ---------------------------------------------------------------------------
-// 4. Per unit: dR = L^T dU (solve (I + T)^T dR = dU), dT, dA, and the
+// 3. Per unit: dR = L^T dU (solve (I + T)^T dR = dU), dT, dA, and the
 //    products with S and dS_next.
 template <typename IO, int D>
 __global__ __launch_bounds__(NT) void cb_grad_s(ChunkBwdArgs a) {
@@ -794,7 +796,7 @@ __global__ __launch_bounds__(NT) void cb_grad_s(ChunkBwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// 5. Per unit: the parts through T and A, the exponential factors, the
+// 4. Per unit: the parts through T and A, the exponential factors, the
 //    gates, and dg.
 template <typename IO, int D, bool CHAN, bool BW>
 __global__ __launch_bounds__(NT) void cb_grad_out(ChunkBwdArgs a) {
