@@ -404,13 +404,19 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
 // 4 (l / 16) + r, r < 4, of column l % 16 of the tile. mfma_kloop adds
 // A[16 x K] B[K x 16] with A row-major (row stride lda) and B row-major
 // (row stride ldb); K a multiple of 4.
+// Two accumulators over alternate K steps keep two independent chains in
+// flight; they are added at the end.
 template <int K>
 __device__ __forceinline__ f32x4 mfma_kloop(f32x4 acc, const float *A, int lda, const float *B, int ldb) {
     const int l = threadIdx.x & 63;
     const float *pa = A + (l & 15) * lda + (l >> 4), *pb = B + (l >> 4) * ldb + (l & 15);
+    f32x4 acc2 = zero4();
 #pragma unroll 8
-    for (int k = 0; k < K; k += 4) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[k], pb[k * ldb], acc, 0, 0, 0);
-    return acc;
+    for (int k = 0; k < K; k += 8) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[k], pb[k * ldb], acc, 0, 0, 0);
+        acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[k + 4], pb[(k + 4) * ldb], acc2, 0, 0, 0);
+    }
+    return acc + acc2;
 }
 
 // The same with A given transposed: A[row][k] at At[k * ldat + row].
@@ -418,9 +424,13 @@ template <int K>
 __device__ __forceinline__ f32x4 mfma_kloop_at(f32x4 acc, const float *At, int ldat, const float *B, int ldb) {
     const int l = threadIdx.x & 63;
     const float *pa = At + (l >> 4) * ldat + (l & 15), *pb = B + (l >> 4) * ldb + (l & 15);
+    f32x4 acc2 = zero4();
 #pragma unroll 8
-    for (int k = 0; k < K; k += 4) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[k * ldat], pb[k * ldb], acc, 0, 0, 0);
-    return acc;
+    for (int k = 0; k < K; k += 8) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[k * ldat], pb[k * ldb], acc, 0, 0, 0);
+        acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[(k + 4) * ldat], pb[(k + 4) * ldb], acc2, 0, 0, 0);
+    }
+    return acc + acc2;
 }
 
 // 2a. Forward over chunks: the state entering each chunk, and U = U_z - Y S.
