@@ -511,7 +511,8 @@ __device__ __forceinline__ void fsweep(const ChunkBwdArgs &a, float *smem, int i
                 }
             }
         }
-        lds_barrier();
+        // No barrier: each wave rewrites only the state entries it has just
+        // read, and every other read of S in this chunk was before the last one.
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const int st = w + 8 * q, dt = st >> 1, sc = st & 1;
@@ -625,7 +626,8 @@ __device__ __forceinline__ void bsweep(const ChunkBwdArgs &a, float *smem, int i
                 }
             }
         }
-        lds_barrier();
+        // No barrier: each wave rewrites only the entries of X it has just
+        // read, and every other read of X in this chunk was before the last one.
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const int st = w + 8 * q, dt = st >> 1, sc = st & 1;
