@@ -290,9 +290,9 @@ int bwd_call(bool chunked, const gdr_desc *d, const void *q, const void *k, cons
         a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.bg = b; a.wg = w; a.S0 = S0; a.dO = dO; a.dST = dST;
         a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.db = db; a.dw = dw; a.dS0 = dS0;
         const gdr::ChunkBwdWsLayout L = gdr::chunk_bwd_ws_layout(d->B, d->T, d->H_qk, d->H_v, d->d_k);
-        float **arr[gdr::kChunkBwdArrays] = {&a.wY, &a.wUz, &a.wKe, &a.wQt, &a.wU, &a.wdU, &a.wdE, &a.wdQ, &a.wdK,
+        float **arr[gdr::kChunkBwdArrays] = {&a.wUz, &a.wQt, &a.wU, &a.wdU, &a.wdE, &a.wdQ, &a.wdK,
                                              &a.wA, &a.wT, &a.wdA, &a.wdT, &a.wS, &a.wdS, &a.wG, &a.wGam, &a.wdGam,
-                                             &a.wdq, &a.wdk, &a.wYt, &a.wKet, &a.wAt};
+                                             &a.wdq, &a.wdk, &a.wYt, &a.wKet};
         char *p = static_cast<char *>(workspace);
         for (int i = 0; i < gdr::kChunkBwdArrays; ++i) {
             *arr[i] = L.floats[i] ? reinterpret_cast<float *>(p) : nullptr;

@@ -58,6 +58,7 @@ constexpr int NT = 512;     // threads per workgroup of the per-chunk kernels (t
 constexpr int BV = 32;      // value columns per sweep workgroup
 constexpr int LB = BV + 4;  // row stride of 32-column tiles
 constexpr int LC = C + 4;   // row stride of 64-column tiles
+constexpr int LT = C + 16;  // row stride of 64-column tiles that the matrix cores read down their columns
 
 constexpr int NS = 512;  // threads per sweep workgroup (two waves per SIMD)
 template <int D>
@@ -173,11 +174,11 @@ constexpr size_t prep_smem() {
 }
 template <int D>
 constexpr size_t fsweep_smem() {
-    return ((size_t)D * LB + (size_t)C * LB + (size_t)C * (D + 4) + (size_t)D * LC + D) * 4;
+    return ((size_t)D * LB + (size_t)C * LB + (size_t)D * LT + (size_t)D * LC + D) * 4;
 }
 template <int D>
 constexpr size_t bsweep_smem() {
-    return ((size_t)D * LB + 2 * (size_t)C * LB + (size_t)C * LC + (size_t)C * (D + 4) + 2 * (size_t)D * LC + D) * 4;
+    return ((size_t)D * LB + 2 * (size_t)C * LB + (size_t)C * LT + 3 * (size_t)D * LC + D) * 4;
 }
 template <int D>
 constexpr size_t grad_s_smem() {
@@ -260,7 +261,6 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
         const f32x4 G = CHAN ? lds4(sZ + t * LD + d) : splat(sGs[t]);
         const f32x4 Ge = CHAN ? lds4(sZ + (C - 1) * LD + d) : splat(sGs[C - 1]);
         const f32x4 eg = exp4(G), qv = lds4(sQ + t * LD + d), kv = lds4(sK + t * LD + d);
-        sts4(a.wKe + ucd + e, kv * exp4(Ge - G));
         if (CHAN) {
             sts4(wG + e, G);
             sts4(sQ + t * LD + d, qv * eg);
@@ -336,8 +336,6 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
             const size_t o = (size_t)u * C * C + (size_t)t * C + c0;
             sts4(a.wT + o, f32x4{aT[i][0], aT[i][1], aT[i][2], aT[i][3]});
             sts4(a.wA + o, f32x4{aA[i][0], aA[i][1], aA[i][2], aA[i][3]});
-#pragma unroll
-            for (int j = 0; j < 4; ++j) a.wAt[(size_t)u * C * C + (size_t)(c0 + j) * C + t] = aA[i][j];
         }
         __syncthreads();  // q, k and e tiles read: T^T goes where q was
 #pragma unroll
@@ -382,7 +380,6 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
     for (int l = 0; l < NL; ++l) {
         int e, t, d;
         rc<D>(l, e, t, d);
-        sts4(a.wY + ucd + e, lds4(sE + t * LD + d));
         sts4(a.wUz + ucd + e, lds4(sZ + t * LD + d));
     }
 #pragma unroll
@@ -440,7 +437,7 @@ template <int D>
 __device__ __forceinline__ void fsweep(const ChunkBwdArgs &a, float *smem, int item) {
     using K = SwCfg<D>;
     constexpr int NTL = K::NTL, NL = K::NL, LD = D + 4, NST = D / 16 * 2;
-    float *sS = smem, *sU = sS + D * LB, *sY = sU + C * LB, *sKt = sY + C * LD;  // Kend transposed: [D][LC]
+    float *sS = smem, *sU = sS + D * LB, *sYt = sU + C * LB, *sKt = sYt + D * LT;  // Y^T [D][LT], Kend^T [D][LC]
     float *sGam = sKt + D * LC;
     const int tid = threadIdx.x, tile = item % NTL, bh = item / NTL, col0 = tile * BV;
     const int w = tid >> 6, l = tid & 63, rt = w >> 1, ct = w & 1;
@@ -456,7 +453,7 @@ __device__ __forceinline__ void fsweep(const ChunkBwdArgs &a, float *smem, int i
 #pragma unroll
         for (int l2 = 0; l2 < NL; ++l2) {
             const int e = 4 * (l2 * NS + tid);
-            pY[l2] = lds4(a.wY + ucd + e);    // [C][D]
+            pY[l2] = lds4(a.wYt + ucd + e);   // [D][C]
             pK[l2] = lds4(a.wKet + ucd + e);  // [D][C]
         }
 #pragma unroll
@@ -469,10 +466,9 @@ __device__ __forceinline__ void fsweep(const ChunkBwdArgs &a, float *smem, int i
         lds_barrier();  // the previous chunk is done with the operand tiles; S written
 #pragma unroll
         for (int l2 = 0; l2 < NL; ++l2) {
-            int e, t, d;
-            rcs<D>(l2, e, t, d);
-            sts4(sY + t * LD + d, pY[l2]);
+            int e, d, t;
             rcs<C>(l2, e, d, t);
+            sts4(sYt + d * LT + t, pY[l2]);
             sts4(sKt + d * LC + t, pK[l2]);
         }
         if (tid < D) sGam[tid] = pg;
@@ -486,7 +482,7 @@ __device__ __forceinline__ void fsweep(const ChunkBwdArgs &a, float *smem, int i
         }
         lds_barrier();
         {  // U = U_z - Y S
-            const f32x4 p = mfma_kloop<D>(zero4(), sY + rt * 16 * LD, LD, sS + ct * 16, LB);
+            const f32x4 p = mfma_kloop_at<D>(zero4(), sYt + rt * 16, LT, sS + ct * 16, LB);
             const int col = ct * 16 + (l & 15);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -531,9 +527,9 @@ __device__ __forceinline__ void bsweep(const ChunkBwdArgs &a, float *smem, int i
     constexpr int NTL = K::NTL, NL = K::NL, LD = D + 4, NST = D / 16 * 2;
     constexpr int NA = C * C / (4 * NS), NO = C * BV / (4 * NS);  // 4-element groups per thread: A, dO tile
     float *sX = smem, *sO = sX + D * LB, *sdU = sO + C * LB;
-    float *sAt = sdU + C * LB;   // A^T [C][LC]
-    float *sK = sAt + C * LC;    // Kend [C][LD]
-    float *sQt = sK + C * LD;    // Q~^T [D][LC]
+    float *sA = sdU + C * LB;    // A [C][LT]
+    float *sKt = sA + C * LT;    // Kend^T [D][LC]
+    float *sQt = sKt + D * LC;   // Q~^T [D][LC]
     float *sYt = sQt + D * LC;   // Y^T [D][LC]
     float *sGam = sYt + D * LC;  // [D]
     const int tid = threadIdx.x, tile = item % NTL, bh = item / NTL, col0 = tile * BV;
@@ -552,12 +548,12 @@ __device__ __forceinline__ void bsweep(const ChunkBwdArgs &a, float *smem, int i
 #pragma unroll
         for (int l2 = 0; l2 < NL; ++l2) {
             const int e = 4 * (l2 * NS + tid);
-            pY[l2] = lds4(a.wYt + ucd + e);  // [D][C]
-            pK[l2] = lds4(a.wKe + ucd + e);  // [C][D]
-            pQ[l2] = lds4(a.wQt + ucd + e);  // [D][C]
+            pY[l2] = lds4(a.wYt + ucd + e);   // [D][C]
+            pK[l2] = lds4(a.wKet + ucd + e);  // [D][C]
+            pQ[l2] = lds4(a.wQt + ucd + e);   // [D][C]
         }
 #pragma unroll
-        for (int l2 = 0; l2 < NA; ++l2) pA[l2] = lds4(a.wAt + u * C * C + 4 * (l2 * NS + tid));
+        for (int l2 = 0; l2 < NA; ++l2) pA[l2] = lds4(a.wA + u * C * C + 4 * (l2 * NS + tid));
 #pragma unroll
         for (int l2 = 0; l2 < NO; ++l2) {
             int e, t, j;
@@ -572,18 +568,17 @@ __device__ __forceinline__ void bsweep(const ChunkBwdArgs &a, float *smem, int i
         lds_barrier();  // X written; the previous chunk is done with the operand tiles
 #pragma unroll
         for (int l2 = 0; l2 < NL; ++l2) {
-            int e, t, d;
-            rcs<D>(l2, e, t, d);
-            sts4(sK + t * LD + d, pK[l2]);
+            int e, d, t;
             rcs<C>(l2, e, d, t);
+            sts4(sKt + d * LC + t, pK[l2]);
             sts4(sYt + d * LC + t, pY[l2]);
             sts4(sQt + d * LC + t, pQ[l2]);
         }
 #pragma unroll
         for (int l2 = 0; l2 < NA; ++l2) {
-            int e, j, t;
-            rcs<C>(l2, e, j, t);
-            sts4(sAt + j * LC + t, pA[l2]);
+            int e, t, j;
+            rcs<C>(l2, e, t, j);
+            sts4(sA + t * LT + j, pA[l2]);
         }
 #pragma unroll
         for (int l2 = 0; l2 < NO; ++l2) {
@@ -599,8 +594,8 @@ __device__ __forceinline__ void bsweep(const ChunkBwdArgs &a, float *smem, int i
         }
         lds_barrier();
         {  // dU = s A^T dO + Kend X
-            const f32x4 p = mfma_kloop<C>(zero4(), sAt + rt * 16 * LC, LC, sO + ct * 16, LB);
-            const f32x4 k = mfma_kloop<D>(zero4(), sK + rt * 16 * LD, LD, sX + ct * 16, LB);
+            const f32x4 p = mfma_kloop_at<C>(zero4(), sA + rt * 16, LT, sO + ct * 16, LB);
+            const f32x4 k = mfma_kloop_at<D>(zero4(), sKt + rt * 16, LC, sX + ct * 16, LB);
             const int col = ct * 16 + (l & 15);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -1051,6 +1046,7 @@ __global__ __launch_bounds__(NT) void cb_group_sum(ChunkBwdArgs a) {
 template <typename IO, int D, bool CHAN, bool BW>
 hipError_t run(const ChunkBwdArgs &a, hipStream_t s) {
     constexpr size_t sweep_smem = bsweep_smem<D>() > fsweep_smem<D>() ? bsweep_smem<D>() : fsweep_smem<D>();
+    static_assert(sweep_smem <= 160 * 1024, "the sweeps' tiles exceed a workgroup's local data share");
     static const hipError_t attr = [] {
         const void *fn[4] = {reinterpret_cast<const void *>(&cb_prep<IO, D, CHAN, BW>),
                              reinterpret_cast<const void *>(&cb_sweeps<IO, D>),

@@ -167,7 +167,7 @@ struct ChunkBwdArgs {
     const void *dO;
     const float *dST;
     float *dq, *dk, *dv, *dg, *dbeta, *db, *dw, *dS0;
-    float *wY, *wUz, *wKe;        // [units][C][D]: Y = L E~, U_z = L Z, Kend
+    float *wUz;                   // [units][C][D]: U_z = L Z
     float *wQt;                   // [units][D][C]: Q~^T
     float *wU, *wdU;              // [units][C][D]: U of the chunk; dU, then dR = L^T dU
     float *wdE, *wdQ, *wdK;       // [units][C][D]: -dR S^T, s dO S^T, U dS_next^T
@@ -176,14 +176,13 @@ struct ChunkBwdArgs {
     float *wG;                    // [units][C][D] (per-channel decay) or [units][C]: in-chunk log-decay sums
     float *wGam, *wdGam;          // [units][D]: exp(G_end); rowsum(dS_next . S)
     float *wdq, *wdk;             // [B][T][Hv][D] per-V-head parts (grouped heads), else null
-    float *wYt, *wKet;            // [units][D][C]: Y^T, Kend^T
-    float *wAt;                   // [units][C][C]: A^T
+    float *wYt, *wKet;            // [units][D][C]: Y^T (Y = L E~), Kend^T
     int B, T, Hqk, Hv, decay, NC;
     float scale;
 };
 // The workspace is carved into kChunkBwdArrays arrays in the order of the
-// pointer fields wY .. wAt above, each starting on a 256-byte boundary.
-constexpr int kChunkBwdArrays = 23;
+// pointer fields wUz .. wKet above, each starting on a 256-byte boundary.
+constexpr int kChunkBwdArrays = 20;
 struct ChunkBwdWsLayout {
     size_t floats[kChunkBwdArrays];
     size_t total() const {
@@ -196,7 +195,7 @@ inline ChunkBwdWsLayout chunk_bwd_ws_layout(int B, int T, int Hqk, int Hv, int D
     const size_t units = (size_t)B * Hv * ((T + kChunk - 1) / kChunk);
     const size_t cd = units * kChunk * D, cc = units * kChunk * kChunk, dd = units * D * D, vd = units * D;
     const size_t part = Hv > Hqk ? (size_t)B * T * Hv * D : 0;
-    return ChunkBwdWsLayout{{cd, cd, cd, cd, cd, cd, cd, cd, cd, cc, cc, cc, cc, dd, dd, cd, vd, vd, part, part, cd, cd, cc}};
+    return ChunkBwdWsLayout{{cd, cd, cd, cd, cd, cd, cd, cc, cc, cc, cc, dd, dd, cd, vd, vd, part, part, cd, cd}};
 }
 
 hipError_t launch_backward(int io, int D, const BwdArgs &a, hipStream_t s);

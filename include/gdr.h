@@ -269,7 +269,7 @@ int gdr_recurrent_bwd(const gdr_desc *desc, const void *q, const void *k, const 
  *   with desc->chunk == 64 (GDR_E_UNSUPPORTED otherwise).
  *   workspace: gdr_chunk_bwd_workspace_bytes bytes, owned by the caller:
  *   float32 per chunk unit (sequence, V head, chunk), about
- *   4 * (12 * 64 * d + 5 * 64 * 64 + 2 * d * d) bytes, plus two
+ *   4 * (10 * 64 * d + 4 * 64 * 64 + 2 * d * d) bytes, plus two
  *   B * T * H_v * d_k float32 arrays when H_v > H_qk.
  *   Work: five launches (a per-chunk pass forming the factors and solving
  *   the unit lower triangular system, a forward pass over chunks storing the

@@ -218,17 +218,17 @@ def test_backward_workspace_bytes():
 
 
 def test_chunk_backward_workspace_bytes():
-    """Per chunk unit (sequence, V head, chunk of 64): twelve 64 x D arrays,
-    five 64 x 64, two D x D and two of D floats; with grouped heads two more
+    """Per chunk unit (sequence, V head, chunk of 64): ten 64 x D arrays,
+    four 64 x 64, two D x D and two of D floats; with grouped heads two more
     [B,T,H_v,D] arrays; each array rounded up to 256 bytes."""
     d = gdr.make_desc(1, 100, 2, 4, 128, gdr.GDR_BF16, gdr.GDR_DECAY_SCALAR)
     units = 1 * 4 * 2
-    per = [64 * 128] * 12 + [64 * 64] * 5 + [128 * 128] * 2 + [128] * 2
+    per = [64 * 128] * 10 + [64 * 64] * 4 + [128 * 128] * 2 + [128] * 2
     want = sum(_a256(units * f * 4) for f in per) + 2 * _a256(100 * 4 * 128 * 4)
     assert gdr.gdr_chunk_bwd_workspace_bytes(d) == want
     d = gdr.make_desc(2, 64, 4, 4, 64, gdr.GDR_F32, gdr.GDR_DECAY_CHANNEL)  # no grouping, float32 io, d = 64
     units = 2 * 4 * 1
-    per = [64 * 64] * 12 + [64 * 64] * 5 + [64 * 64] * 2 + [64] * 2
+    per = [64 * 64] * 10 + [64 * 64] * 4 + [64 * 64] * 2 + [64] * 2
     assert gdr.gdr_chunk_bwd_workspace_bytes(d) == sum(_a256(units * f * 4) for f in per)
     assert gdr.gdr_chunk_bwd_workspace_bytes(gdr.make_desc(1, 0, 2, 4, 128, gdr.GDR_BF16,
                                                            gdr.GDR_DECAY_SCALAR)) == 0
