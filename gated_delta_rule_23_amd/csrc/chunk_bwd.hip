@@ -692,7 +692,22 @@ __global__ __launch_bounds__(NT) void cb_grad_s(ChunkBwdArgs a) {
 #pragma unroll
         for (int l = 0; l < NTT; ++l) sts4(sT + 4 * (l * NT + tid), rT[l]);  // T, row stride C
     }
-    __syncthreads();
+    // The first block of S and dS_next rows is fetched into registers now, so
+    // that it arrives during the solve; the barriers up to its use order the
+    // shared tiles only and do not wait for it.
+    f32x4 rb[NB], rs[NB];
+    const auto fetch = [&](int blk) {
+#pragma unroll
+        for (int l = 0; l < NB; ++l) {
+            const int g = l * NT + tid;
+            if (g < NG) {
+                rs[l] = lds4(a.wS + udd + (size_t)blk * 32 * D + 4 * g);
+                rb[l] = lds4(a.wdS + udd + (size_t)blk * 32 * D + 4 * g);
+            }
+        }
+    };
+    fetch(0);
+    lds_barrier();
     if (tid < D) {  // one column of dU per thread
         float *X = sX + tid;
         float xc[C];
@@ -702,7 +717,7 @@ __global__ __launch_bounds__(NT) void cb_grad_s(ChunkBwdArgs a) {
 #pragma unroll
         for (int i = 0; i < C; ++i) X[i * LD] = xc[i];
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int l = 0; l < NL; ++l) {
         int e, t, d;
@@ -739,20 +754,8 @@ __global__ __launch_bounds__(NT) void cb_grad_s(ChunkBwdArgs a) {
     // Products with S and with dS_next, 32 state rows at a time; the next
     // block's rows are fetched into registers while the current one is used.
     float *sB2 = sT;  // S rows of the block (T is no longer needed)
-    f32x4 rb[NB], rs[NB];
-    const auto fetch = [&](int blk) {
-#pragma unroll
-        for (int l = 0; l < NB; ++l) {
-            const int g = l * NT + tid;
-            if (g < NG) {
-                rs[l] = lds4(a.wS + udd + (size_t)blk * 32 * D + 4 * g);
-                rb[l] = lds4(a.wdS + udd + (size_t)blk * 32 * D + 4 * g);
-            }
-        }
-    };
-    fetch(0);
     for (int blk = 0; blk < D / 32; ++blk) {
-        __syncthreads();  // the previous block's rows are read
+        lds_barrier();  // the previous block's rows (and T) are read
 #pragma unroll
         for (int l = 0; l < NB; ++l) {
             const int g = l * NT + tid, e = 4 * g, r = e / D, v = e - r * D;
@@ -762,7 +765,7 @@ __global__ __launch_bounds__(NT) void cb_grad_s(ChunkBwdArgs a) {
             }
         }
         if (blk + 1 < D / 32) fetch(blk + 1);
-        __syncthreads();
+        lds_barrier();
         {
             // The block's 64 x 32 outputs of each product on the matrix cores
             // (fp32 in, fp32 accumulate): wave w takes the 16 x 16 tile
