@@ -204,13 +204,14 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
     const int tid = threadIdx.x, u = blockIdx.x;
     const Unit x = decode(a, u);
     const size_t ucd = (size_t)u * C * D;
+    f32x4 rz[NL];  // z = beta v (or w v), loaded with the other inputs and staged after T and A
     {
         f32x4 rq[NL], rk[NL], re[NL], rg[CHAN ? NL : 1];
 #pragma unroll
         for (int l = 0; l < NL; ++l) {
             int e, t, d;
             rc<D>(l, e, t, d);
-            rq[l] = rk[l] = re[l] = zero4();
+            rq[l] = rk[l] = re[l] = rz[l] = zero4();
             if (CHAN) rg[l] = zero4();
             if (t < x.n) {
                 const size_t iq = (x.rowq + (size_t)t * a.Hqk) * D + d, iv = (x.rowv + (size_t)t * a.Hv) * D + d;
@@ -218,6 +219,7 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
                 rk[l] = ld4io<IO>(a.k, iq);
                 re[l] = BW ? ld4io<IO>(a.bg, iv) : splat(a.beta[x.rowv + (size_t)t * a.Hv]);
                 if (CHAN) rg[l] = lds4(a.g + iv);
+                rz[l] = (BW ? ld4io<IO>(a.wg, iv) : splat(a.beta[x.rowv + (size_t)t * a.Hv])) * ld4io<IO>(a.v, iv);
             }
         }
 #pragma unroll
@@ -345,17 +347,6 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
     }
     // Right-hand sides: E~ (scalar decay: the raw e scaled by exp(G_t)) and z.
     {
-        f32x4 rz[NL];
-#pragma unroll
-        for (int l = 0; l < NL; ++l) {
-            int e, t, d;
-            rc<D>(l, e, t, d);
-            rz[l] = zero4();
-            if (t < x.n) {
-                const size_t iv = (x.rowv + (size_t)t * a.Hv) * D + d;
-                rz[l] = (BW ? ld4io<IO>(a.wg, iv) : splat(a.beta[x.rowv + (size_t)t * a.Hv])) * ld4io<IO>(a.v, iv);
-            }
-        }
 #pragma unroll
         for (int l = 0; l < NL; ++l) {
             int e, t, d;
