@@ -298,11 +298,12 @@ def main(argv=None):
         raw = gs.make_raw_inputs(wl, seed=args.seed + 3)
         rd = {n: up(raw[n]) for n in ("q", "k", "v", "g", "beta", "b", "w", "conv_w", "conv_in", "decay_scale")}
         conv_out = torch.empty_like(rd["conv_in"])
+        ws_in = torch.empty(gdr.gdr_chunk_fwd_in_workspace_bytes(desc), dtype=torch.uint8, device=dev)
 
         def prefill_in():
             gdr.gdr_chunk_fwd_in(rd["q"], rd["k"], rd["v"], rd["conv_w"], conv_in=rd["conv_in"], conv_out=conv_out,
                                  decay_scale=rd["decay_scale"], g=rd["g"], beta=rd["beta"], b=rd["b"], w=rd["w"],
-                                 S0=None, scale=wl.scale, o=o, ST=ST, workspace=ws, stream=cur())
+                                 S0=None, scale=wl.scale, o=o, ST=ST, workspace=ws_in, stream=cur())
 
         for _ in range(args.warmup):
             prefill_in()
@@ -327,7 +328,7 @@ def main(argv=None):
                  "roofline": {"bound": "hbm", "achieved": s_bytes / (s_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
                               "unit": "GB/s", "frac": s_bytes / (s_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                               "traffic": recorded_traffic(wl.name + "_input_stage"), "algorithmic_bytes": s_bytes}}
-        del raw, rd, conv_out
+        del raw, rd, conv_out, ws_in
 
     # ---- backward (gradients of the recurrence) on the prefill workload ----
     bwd = None

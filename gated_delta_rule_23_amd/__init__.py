@@ -29,6 +29,7 @@ CHUNK = 64
 
 # Every symbol include/gdr.h declares.
 EXPORTS = ("gdr_state_bytes", "gdr_state_alloc", "gdr_state_free", "gdr_chunk_workspace_bytes",
+           "gdr_chunk_fwd_in_workspace_bytes",
            "gdr_chunk_fwd", "gdr_decode_step", "gdr_recurrent_fwd", "gdr_recurrent_fwd_in", "gdr_chunk_fwd_in",
            "gdr_recurrent_bwd_workspace_bytes", "gdr_recurrent_bwd", "gdr_chunk_bwd_workspace_bytes", "gdr_chunk_bwd",
            "gdr_last_error", "gdr_version")
@@ -73,6 +74,8 @@ def _load():
     lib.gdr_state_free.argtypes = [P]
     lib.gdr_chunk_workspace_bytes.restype = I
     lib.gdr_chunk_workspace_bytes.argtypes = [D, ctypes.POINTER(S)]
+    lib.gdr_chunk_fwd_in_workspace_bytes.restype = I
+    lib.gdr_chunk_fwd_in_workspace_bytes.argtypes = [D, ctypes.POINTER(S)]
     lib.gdr_chunk_fwd.restype = I
     lib.gdr_chunk_fwd.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, S, P]
     lib.gdr_decode_step.restype = I
@@ -177,6 +180,12 @@ def make_desc(B, T, Hqk, Hv, D, io, decay, scale=1.0, chunk=CHUNK) -> gdr_desc:
 def gdr_chunk_workspace_bytes(desc: gdr_desc) -> int:
     n = ctypes.c_size_t()
     _check(lib.gdr_chunk_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def gdr_chunk_fwd_in_workspace_bytes(desc: gdr_desc) -> int:
+    n = ctypes.c_size_t()
+    _check(lib.gdr_chunk_fwd_in_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)))
     return n.value
 
 
@@ -310,7 +319,7 @@ def gdr_chunk_fwd_in(q, k, v, conv_w, *, conv_in=None, conv_out=None, decay_scal
         ST = torch.empty((B, Hv, D, D), dtype=torch.float32, device=dev)
     _require(o, "o", (B, T, Hv, D), io_t, dev)
     _require(ST, "ST", (B, Hv, D, D), torch.float32, dev)
-    nbytes = gdr_chunk_workspace_bytes(desc)
+    nbytes = gdr_chunk_fwd_in_workspace_bytes(desc)
     if workspace is None and nbytes > 0:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()

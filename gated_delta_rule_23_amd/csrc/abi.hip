@@ -118,6 +118,49 @@ int check_stage(const gdr_desc *d, const gdr_input_stage *stage) {
     return GDR_OK;
 }
 
+// Byte ranges [x, x + nx) and [y, y + ny) intersect.
+bool ranges_meet(const void *x, size_t nx, const void *y, size_t ny) {
+    const char *a = static_cast<const char *>(x), *b = static_cast<const char *>(y);
+    return nx && ny && a < b + ny && b < a + nx;
+}
+
+// The chunked prefill's aliasing rules: S_T equals S0 or does not overlap
+// it (one sweep workgroup's state writes would otherwise land on entries
+// another has yet to read), and o, S_T (unless it is S0) and the workspace
+// overlap no input and no other output.
+int check_chunk_overlaps(const gdr_desc *d, const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, const void *b, const void *w, const float *S0, const void *o,
+                         const float *ST, const void *ws, size_t ws_bytes) {
+    if (d->B == 0) return GDR_OK;
+    const size_t esz = d->io_dtype == GDR_BF16 ? 2 : 4, D = d->d_k, tok = (size_t)d->B * d->T;
+    const size_t sbytes = (size_t)d->B * d->H_v * D * D * sizeof(float);
+    struct Range { const void *p; size_t n; };
+    const Range in[] = {{q, tok * d->H_qk * D * esz},
+                        {k, tok * d->H_qk * D * esz},
+                        {v, tok * d->H_v * D * esz},
+                        {g, g ? tok * d->H_v * (d->decay == GDR_DECAY_CHANNEL ? D : 1) * sizeof(float) : 0},
+                        {beta, beta ? tok * d->H_v * sizeof(float) : 0},
+                        {b, b ? tok * d->H_v * D * esz : 0},
+                        {w, w ? tok * d->H_v * D * esz : 0},
+                        {S0, S0 ? sbytes : 0}};
+    const Range out[] = {{o, tok * d->H_v * D * esz}, {ST, sbytes}, {ws, ws ? ws_bytes : 0}};
+    const char *name[] = {"o", "ST", "the workspace"};
+    for (int i = 0; i < 3; ++i) {
+        if (!out[i].p) continue;
+        for (const Range &x : in) {
+            if (i == 1 && x.p == S0 && ST == S0) continue;  // S_T may be S0 itself
+            if (x.p && ranges_meet(out[i].p, out[i].n, x.p, x.n)) {
+                if (i == 1 && x.p == S0) return fail(GDR_E_INVAL, "ST must equal S0 or not overlap it");
+                return fail(GDR_E_INVAL, "%s overlaps an input", name[i]);
+            }
+        }
+        for (int j = i + 1; j < 3; ++j)
+            if (out[j].p && ranges_meet(out[i].p, out[i].n, out[j].p, out[j].n))
+                return fail(GDR_E_INVAL, "%s overlaps %s", name[i], name[j]);
+    }
+    return GDR_OK;
+}
+
 int chunk_call(const gdr_desc *d, const gdr_input_stage *stage, const void *q, const void *k, const void *v,
                       const float *g, const float *beta, const void *b, const void *w, const float *S0, void *o,
                       float *ST, void *workspace, size_t workspace_bytes, void *stream) {
@@ -130,10 +173,17 @@ int chunk_call(const gdr_desc *d, const gdr_input_stage *stage, const void *q, c
     if (rc != GDR_OK) return rc;
     const int io = d->io_dtype == GDR_BF16 ? gdr::IO_BF16 : gdr::IO_F32;
     const int NC = (d->T + gdr::kChunk - 1) / gdr::kChunk;
-    const gdr::ChunkWsLayout L = gdr::chunk_ws_layout(d->B, d->H_qk, d->H_v, NC, d->d_k, io, d->decay == GDR_DECAY_CHANNEL);
-    const size_t need = L.total();
+    const bool chan = d->decay == GDR_DECAY_CHANNEL;
+    const gdr::ChunkWsLayout L = gdr::chunk_ws_layout(d->B, d->H_qk, d->H_v, NC, d->d_k, io, chan);
+    // Per-channel decay with the input stage: the stage runs as a pass of its
+    // own into the workspace, after the prefill's part.
+    const bool split_stage = stage && chan;
+    const gdr::StageWsLayout SL = gdr::stage_ws_layout(d->B, d->T, d->H_qk, d->H_v, d->d_k, io, beta == nullptr);
+    const size_t need = L.total() + (split_stage ? SL.total() : 0);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(GDR_E_INVAL, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+    rc = check_chunk_overlaps(d, q, k, v, g, beta, b, w, S0, o, ST, workspace, need);
+    if (rc != GDR_OK) return rc;
     if (d->B == 0) return ok();
     const size_t units = (size_t)d->B * d->H_v * NC;
     if (units > 0x7fffffffull) return fail(GDR_E_UNSUPPORTED, "too many chunks for one launch");
@@ -150,13 +200,31 @@ int chunk_call(const gdr_desc *d, const gdr_input_stage *stage, const void *q, c
     gdr::chunk_segments(d->B, d->H_v, d->d_k, NC, a.P, a.L);
     a.B = d->B; a.T = d->T; a.Hqk = d->H_qk; a.Hv = d->H_v; a.decay = d->decay; a.NC = NC;
     a.scale = d->scale;
-    if (stage) {
+    hipError_t e = hipSuccess;
+    if (split_stage && NC > 0) {
+        char *p = static_cast<char *>(workspace) + L.total();
+        gdr::StageArgs sa{};
+        sa.q = q; sa.k = k; sa.v = v; sa.g = g; sa.beta = beta; sa.bg = b; sa.wg = w;
+        sa.conv_w = stage->conv_w; sa.conv_in = stage->conv_in; sa.conv_out = stage->conv_out;
+        sa.decay_scale = stage->decay_scale;
+        sa.qo = p;
+        sa.ko = p + SL.qk;
+        sa.vo = p + 2 * SL.qk;
+        sa.go = reinterpret_cast<float *>(p + 2 * SL.qk + SL.v);
+        char *gates = p + 2 * SL.qk + SL.v + SL.g;
+        if (beta) sa.betao = reinterpret_cast<float *>(gates);
+        else { sa.bgo = gates; sa.wgo = gates + SL.gate; }
+        sa.B = d->B; sa.T = d->T; sa.Hqk = d->H_qk; sa.Hv = d->H_v;
+        e = gdr::launch_stage(io, d->d_k, sa, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return hip_fail(e, "input stage launch");
+        a.q = sa.qo; a.k = sa.ko; a.v = sa.vo; a.g = sa.go; a.beta = sa.betao; a.bg = sa.bgo; a.wg = sa.wgo;
+    } else if (stage) {
         a.conv_w = stage->conv_w;
         a.conv_in = stage->conv_in;
         a.conv_out = stage->conv_out;
         a.decay_scale = stage->decay_scale;
     }
-    hipError_t e = gdr::launch_chunk(io, d->d_k, a, static_cast<hipStream_t>(stream));
+    e = gdr::launch_chunk(io, d->d_k, a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "chunk prefill launch");
     if (stage && stage->conv_out && NC == 0) {  // no chunk: the state passes through unchanged
         e = gdr::launch_state_fill(static_cast<float *>(stage->conv_out), static_cast<const float *>(stage->conv_in),
@@ -365,6 +433,16 @@ int gdr_chunk_workspace_bytes(const gdr_desc *d, size_t *bytes) {
     const int NC = (d->T + gdr::kChunk - 1) / gdr::kChunk;
     *bytes = gdr::chunk_ws_layout(d->B, d->H_qk, d->H_v, NC, d->d_k, d->io_dtype == GDR_BF16 ? gdr::IO_BF16 : gdr::IO_F32,
                                   d->decay == GDR_DECAY_CHANNEL).total();
+    return ok();
+}
+
+int gdr_chunk_fwd_in_workspace_bytes(const gdr_desc *d, size_t *bytes) {
+    const int rc = gdr_chunk_workspace_bytes(d, bytes);
+    if (rc != GDR_OK) return rc;
+    // Per-channel decay: room for the processed inputs (decoupled gates, the larger case).
+    if (d->decay == GDR_DECAY_CHANNEL)
+        *bytes += gdr::stage_ws_layout(d->B, d->T, d->H_qk, d->H_v, d->d_k,
+                                       d->io_dtype == GDR_BF16 ? gdr::IO_BF16 : gdr::IO_F32, true).total();
     return ok();
 }
 

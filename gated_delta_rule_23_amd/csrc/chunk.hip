@@ -8,9 +8,10 @@
 // chunk of C = 64 tokens with entry state S_c (d_k x d_v), G_i the in-chunk
 // inclusive prefix sum of g = log(alpha), e the erase key and z the gated value:
 //
-//   E~ = e . exp(G)     K~ = k . exp(-G)     Q~ = q . exp(G)
-//   Kend = k . exp(G_end - G)                gamma = exp(G_end)
-//   T = strict_lower(E~ K~^T)      A = lower_incl(Q~ K~^T)
+//   E~ = e . exp(G)     Q~ = q . exp(G)     Kend = k . exp(G_end - G)
+//   gamma = exp(G_end)
+//   T_ij = sum_c e_ic k_jc exp(G_ic - G_jc)  (j < i)
+//   A_ij = sum_c q_ic k_jc exp(G_ic - G_jc)  (j <= i)
 //   L = (I + T)^-1                 (unit lower triangular; no dense solve)
 //   Y = L E~        U_z = L Z      (erase side / write side of the WY form)
 //   U = U_z - Y S_c                (the resolved errors)
@@ -19,7 +20,9 @@
 //
 // Two kernels. chunk_prep is parallel over every (sequence, V head, chunk):
 // it does everything that does not depend on the state -- prefix sums, decay
-// absorption, both Gram products, the triangular solve for Y and U_z -- and
+// absorption, both Gram products (never as E~ times k . exp(-G), which
+// overflows once a channel decays by more than about 88 inside a chunk; see
+// the block-referenced factors below), the triangular solve for Y and U_z -- and
 // stores Y, U_z^T and A (with per-channel decay also Q~, Kend^T and gamma;
 // with a scalar decay per-token decay factors and one k^T per QK head) in a
 // workspace, each matrix in the order the sweep's matrix-core operand loads
@@ -87,6 +90,43 @@ __device__ __forceinline__ void lower_tile(int idx, int &ti, int &tj) {
 
 // exp(x) = 2^(x log2 e) on the hardware exp2 (v_exp_f32, ~1 ulp).
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+
+// Per-channel decay inside a chunk, referenced block by block so that no
+// factor exceeds 1 (the pages' pipeline forms the 16-token diagonal blocks
+// first, then the off-diagonal ones). For the 16-token block b of a chunk let
+// B_b be its per-channel sum of g, R_b = B_0 + ... + B_{b-1} the sum before it
+// (R_0 = 0, R_4 = G_end), and Gb_i = G_i - R_b the in-block inclusive prefix of
+// token i in block b. The tiles hold
+//   Q^ = q . exp(Gb),  E^ = e . exp(Gb),  K^ = k . exp(B_b - Gb)   (all <= |x|).
+// For tokens i in block bi and j in block bj <= bi,
+//   exp(G_i - G_j) = exp(Gb_i) . exp(R_bi - R_{bj+1}) . exp(B_bj - Gb_j),
+// so a Gram tile is E^ (or Q^) rows times K^ rows with one per-channel factor
+// exp(R_bi - R_{bj+1}) on the K^ operand: 1 for bj = bi - 1, <= 1 further
+// below the diagonal, and exp(-B_bi) >= 1 on the diagonal, where the K^ rows
+// are read from a tile already scaled by it (k . exp(-Gb), at most
+// exp(kDiagRange)). A diagonal block whose decay exceeds kDiagRange on some
+// channel is instead formed entry by entry, sum_c e_ic k_jc exp(Gb_ic - Gb_jc),
+// so no factor can overflow or vanish at any decay. The chunk-referenced
+// operands follow by factors <= 1:
+//   Q~ = Q^ . exp(R_b),  E~ = E^ . exp(R_b),  Kend = K^ . exp(G_end - R_{b+1}).
+// kDecRows rows of per-channel factors, row r = exp(sum over the blocks in
+// mask r of B), negated and capped at kDiagRange for the diagonal rows:
+//   0-3   exp(R_b)                      (Q~, E~ of block b)
+//   4-6   exp(B_1), exp(B_2), exp(B_1 + B_2)   (Gram tiles (2,0), (3,1), (3,0))
+//   7-10  exp(-B_b)                     (diagonal Gram tile of block b)
+//   11-14 exp(G_end - R_{b+1})          (Kend of block b)
+// With bfloat16 io, phase A writes the diagonal K operand, E~ and Kend as
+// tiles of their own, so that no bfloat16 operand is unpacked and rescaled
+// on the matrix-core path; with float32 io (whose tiles are twice as large)
+// the operands are scaled as they are read, one multiply per element.
+constexpr int kDecRows = 16;
+constexpr float kDiagRange = 40.f;
+constexpr uint64_t kDecMask = 0x0ull | 0x1ull << 4 | 0x3ull << 8 | 0x7ull << 12 | 0x2ull << 16 | 0x4ull << 20 |
+                              0x6ull << 24 | 0x1ull << 28 | 0x2ull << 32 | 0x4ull << 36 | 0x8ull << 40 |
+                              0xEull << 44 | 0xCull << 48 | 0x8ull << 52 | 0x0ull << 56;
+__host__ __device__ constexpr int dec_row_far(int bi, int bj) {  // factor row of Gram tile (bi, bj), bi - bj >= 2
+    return bi == 2 ? 4 : bj == 1 ? 5 : 6;
+}
 
 // Orders this wave's shared-memory accesses around a point where lanes read
 // what other lanes of the same wave wrote (a wave executes its LDS accesses
@@ -203,11 +243,12 @@ __device__ __forceinline__ void st16_stream(void *p, uint4 x) {
 //
 // Shared memory holds the chunk's token-major tiles (row t = token, 16-byte
 // channel groups): q, k and z = gated v; for decoupled gates or per-channel
-// decay also the erase key; for per-channel decay the tiles already carry the
-// decay (Q~, K~, E~) and Kend has its own tile. With a scalar decay the tiles
-// stay undecayed and the decay is applied where they are read: to Gram
-// entries as exp(G_i - G_j) (no factor can overflow), and per token to the
-// E~ and Kend operands.
+// decay also the erase key; for per-channel decay the tiles carry the decay
+// referenced to their 16-token block (Q^, K^, E^ above), and the per-channel
+// factors between blocks are applied where the tiles are read. With a scalar
+// decay the tiles stay undecayed and the decay is applied where they are
+// read: to Gram entries as exp(G_i - G_j) (no factor can overflow), and per
+// token to the E~ and Kend operands.
 //  A. prefix sums of g, token tables, the tiles; gamma.
 //  B. Gram products T = E~ K~^T, A = Q~ K~^T on the matrix cores (20 lower
 //     16 x 16 tiles); T and A kept column-major; Q~ and Kend^T go to the
@@ -240,9 +281,15 @@ struct PrepCfg {
     static constexpr size_t TD = a16((size_t)4 * 16 * 17 * 4);
     static constexpr size_t TAB = a16((size_t)5 * C * 4);
     static constexpr size_t PART = a16((size_t)NGRP * D * 4);
+    static constexpr size_t DEC = a16((size_t)kDecRows * D * 4) + 16;  // decay factor rows + 4 block flags
     static_assert(NT % CO == 0 && NGRP * TPT == C && WC % 16 == 0, "phase mappings");
+    // Phase A: each wave holds the tokens of one 16-token block.
+    static_assert(TPT * (64 / CO) == 16 && C / 16 == NW, "one 16-token block per wave in phase A");
+    static_assert(PART <= MAT, "the per-group sums share the T tile's space");
+    // Per-channel decay: the diagonal K operand, E~ and Kend as tiles (bfloat16 io only).
+    static constexpr bool DTILES = sizeof(IO) == 2;
     static constexpr size_t bytes(bool has_e, bool chan) {
-        return R1 + TILE * (2 + (has_e ? 1 : 0) + (chan ? 1 : 0)) + 2 * MAT + TMP + TD + TAB + (chan ? PART : 0);
+        return R1 + TILE * (2 + (has_e ? 1 : 0) + (chan && DTILES ? 3 : 0)) + 2 * MAT + TMP + TD + TAB + (chan ? DEC : 0);
     }
 };
 
@@ -348,6 +395,7 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
     constexpr int KS = M::KS, FE = KS / 4, PD = Cfg::PD, LC = Cfg::LC, LY = Cfg::LY, LT = Cfg::LT;
     constexpr int WC = Cfg::WC, NCTS = Cfg::NCTS;
     constexpr bool HAS_E = CHAN || BW;
+    static_assert(!(RAW && CHAN), "with a per-channel decay the input stage runs as a pass of its own");
     static_assert(NT == 256, "launch bounds");
 
     extern __shared__ __align__(16) unsigned char smem[];
@@ -356,7 +404,10 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
     IO *tK = reinterpret_cast<IO *>(sp);  sp += Cfg::TILE;  // k (K~)
     IO *tZ = reinterpret_cast<IO *>(sp);  sp += Cfg::TILE;  // z
     IO *tE = reinterpret_cast<IO *>(sp);  sp += HAS_E ? Cfg::TILE : 0;  // erase key (E~)
-    IO *tKe = reinterpret_cast<IO *>(sp); sp += CHAN ? Cfg::TILE : 0;   // Kend (per-channel decay)
+    constexpr bool DT = CHAN && Cfg::DTILES;
+    IO *tKd = reinterpret_cast<IO *>(sp); sp += DT ? Cfg::TILE : 0;     // per-channel decay: k . exp(-Gb)
+    IO *tEt = reinterpret_cast<IO *>(sp); sp += DT ? Cfg::TILE : 0;     //   E~ (chunk-referenced)
+    IO *tKe = reinterpret_cast<IO *>(sp); sp += DT ? Cfg::TILE : 0;     //   Kend
     IO *sTc = reinterpret_cast<IO *>(sp); sp += Cfg::MAT;   // T(i, j) at sTc[j * LC + i], blocks below the diagonal
     IO *sAc = reinterpret_cast<IO *>(sp); sp += Cfg::MAT;   // A, same layout; then L
     IO *sLc = sAc;
@@ -366,7 +417,9 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
     float *sEG = sG + C;                                          //   exp(G),
     float *sBt = sG + 3 * C;                                      //   beta,
     float *sSE = sG + 4 * C;                                      //   the E~ factor of a raw erase-key tile
-    float *sPart = reinterpret_cast<float *>(sp);                 // [NGRP][D] per-group channel sums
+    float *sPart = reinterpret_cast<float *>(sTc);                // [NGRP][D] per-group channel sums (phase A only)
+    float *sDec = reinterpret_cast<float *>(sp);                  // [kDecRows][D] per-channel decay factors
+    int *sSlow = reinterpret_cast<int *>(sDec + kDecRows * D);    // [4]: diagonal block formed entry by entry
     IO *sYc = tQ;                                                 // Y(t, c) at sYc[c * LY + t]
 
     // The wave index is uniform across the wave: keep it in a scalar register
@@ -552,31 +605,104 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
             __syncthreads();  // every window read before the tiles are overwritten
         }
         float eGend[V];
+        float Bmy[CHAN ? V : 1];  // per-channel decay sum of this thread's 16-token block (the wave's block)
+        // exp(B), exp(R) and exp(G_end - R_{b+1}) of that block
+        float eB[CHAN ? V : 1], eR[CHAN ? V : 1], eG1[CHAN ? V : 1];
         if constexpr (CHAN) {
-            float off[V], tot[V];
+            // Block sums B_b (the first group of each block sums its block's
+            // group totals into sBlk, in the per-wave temporaries that are
+            // free until phase C), and the offset that turns this thread's
+            // local prefix into the in-block prefix Gb (groups of its block
+            // before it).
+            constexpr int GPB = NGRP / 4;
+            const int g0 = w * GPB;
+            float *sBlk = reinterpret_cast<float *>(sTmp);  // [4][D]
+            float off[V];
 #pragma unroll
-            for (int ch = 0; ch < V; ++ch) off[ch] = tot[ch] = 0.f;
-            for (int g2 = 0; g2 < NGRP; ++g2) {
+            for (int ch = 0; ch < V; ++ch) off[ch] = 0.f;
+            if (grp == g0) {
+                float bs[V];
+#pragma unroll
+                for (int ch = 0; ch < V; ++ch) bs[ch] = 0.f;
+#pragma unroll 4
+                for (int gg = 0; gg < GPB; ++gg)
+#pragma unroll
+                    for (int i = 0; i < V / 4; ++i) {
+                        const f32x4 p = load4f(sPart + (g0 + gg) * D + V * co + 4 * i);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) bs[4 * i + r] += p[r];
+                    }
+#pragma unroll
+                for (int i = 0; i < V / 4; ++i)
+                    store4f(sBlk + w * D + V * co + 4 * i, f32x4{bs[4 * i], bs[4 * i + 1], bs[4 * i + 2], bs[4 * i + 3]});
+            } else {
+#pragma unroll 4
+                for (int g2 = g0; g2 < grp; ++g2)
+#pragma unroll
+                    for (int i = 0; i < V / 4; ++i) {
+                        const f32x4 p = load4f(sPart + g2 * D + V * co + 4 * i);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) off[4 * i + r] += p[r];
+                    }
+            }
+            __syncthreads();
+            float Bs[4][V];
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
 #pragma unroll
                 for (int i = 0; i < V / 4; ++i) {
-                    const f32x4 p = load4f(sPart + g2 * D + V * co + 4 * i);
+                    const f32x4 p = load4f(sBlk + b * D + V * co + 4 * i);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        if (g2 < grp) off[4 * i + r] += p[r];
-                        tot[4 * i + r] += p[r];
-                    }
+                    for (int r = 0; r < 4; ++r) Bs[b][4 * i + r] = p[r];
                 }
-            }
 #pragma unroll
             for (int ch = 0; ch < V; ++ch) {
-                eGend[ch] = fast_exp(tot[ch]);
+                Bmy[ch] = w == 0 ? Bs[0][ch] : w == 1 ? Bs[1][ch] : w == 2 ? Bs[2][ch] : Bs[3][ch];
+                eB[ch] = fast_exp(Bmy[ch]);
+                eR[ch] = fast_exp(w == 0 ? 0.f : w == 1 ? Bs[0][ch] : w == 2 ? Bs[0][ch] + Bs[1][ch]
+                                                                   : Bs[0][ch] + Bs[1][ch] + Bs[2][ch]);
+                eG1[ch] = fast_exp(w == 0 ? Bs[1][ch] + Bs[2][ch] + Bs[3][ch] : w == 1 ? Bs[2][ch] + Bs[3][ch]
+                                                                   : w == 2 ? Bs[3][ch] : 0.f);
+                eGend[ch] = fast_exp(Bs[0][ch] + Bs[1][ch] + Bs[2][ch] + Bs[3][ch]);
 #pragma unroll
                 for (int j = 0; j < TPT; ++j) G[j][ch] += off[ch];
             }
+            // Row grp of the decay factor table, for this thread's channels.
+            if (grp < kDecRows - 1) {
+                const unsigned m = (unsigned)(kDecMask >> (4 * grp)) & 0xFu;
+                const bool neg = grp >= 7 && grp < 11;
+                float f[V];
+#pragma unroll
+                for (int ch = 0; ch < V; ++ch) {
+                    const float x = ((m & 1u) ? Bs[0][ch] : 0.f) + ((m & 2u) ? Bs[1][ch] : 0.f) +
+                                    ((m & 4u) ? Bs[2][ch] : 0.f) + ((m & 8u) ? Bs[3][ch] : 0.f);
+                    f[ch] = fast_exp(neg ? fminf(-x, kDiagRange) : x);
+                }
+#pragma unroll
+                for (int i = 0; i < V / 4; ++i)
+                    store4f(sDec + grp * D + V * co + 4 * i, f32x4{f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3]});
+            }
+            if (grp == NGRP - 1)  // gamma per channel for the sweep
+#pragma unroll
+                for (int i = 0; i < V / 4; ++i)
+                    store4f(tab + V * co + 4 * i, f32x4{eGend[4 * i], eGend[4 * i + 1], eGend[4 * i + 2], eGend[4 * i + 3]});
         } else {
             const float e = sEG[C - 1];
 #pragma unroll
             for (int ch = 0; ch < V; ++ch) eGend[ch] = e;
+        }
+        // Per-channel decay: a block whose decay exceeds kDiagRange on some
+        // channel ("slow"; the flag is uniform over the wave that holds it)
+        // keeps its raw q, k and e in the tiles until its diagonal Gram tiles
+        // have been formed entry by entry below; every other block's diagonal
+        // tiles read k . exp(-Gb) = K^ . exp(-B).
+        bool slow = false;
+        if constexpr (CHAN) {
+            bool big = false;
+#pragma unroll
+            for (int ch = 0; ch < V; ++ch) big = big || Bmy[ch] < -kDiagRange;
+            slow = __ballot(big) != 0;
+            if (l == 0) sSlow[w] = slow ? 1 : 0;
         }
 #pragma unroll
         for (int j = 0; j < TPT; ++j) {
@@ -600,17 +726,28 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
 #pragma unroll
                 for (int ch = 0; ch < V; ++ch) eb[ch] = wz[ch] = bt;
             }
-            float oq[V], ok[V], oz[V], oe[V], oke[V];
+            float oq[V], ok[V], oz[V], oe[V], okd[CHAN ? V : 1], oet[CHAN ? V : 1], oke[CHAN ? V : 1];
 #pragma unroll
             for (int ch = 0; ch < V; ++ch) {
                 const float kv = valid ? kk[ch] : 0.f, qv = valid ? qq[ch] : 0.f;
                 oz[ch] = valid ? wz[ch] * vv[ch] : 0.f;
                 if constexpr (CHAN) {
-                    const float eg = fast_exp(G[j][ch]), emg = __builtin_amdgcn_rcpf(eg);
+                    // Q^, E^ and K^ of the in-block prefix Gb, every factor <= 1
+                    // (raw values in a slow block, scaled once its diagonal is
+                    // formed); k . exp(-Gb) for the diagonal tiles, at most
+                    // exp(kDiagRange) outside slow blocks; E~ = E^ . exp(R) and
+                    // Kend = K^ . exp(G_end - R_{b+1}) (a slow block's Kend
+                    // is written once its K^ is).
+                    const float egt = fast_exp(G[j][ch]);
+                    const float ig = slow ? 1.f : __builtin_amdgcn_rcpf(egt);
+                    const float eg = slow ? 1.f : egt, ek = ig * eB[ch];
+                    const float ev = eb[ch] * kv;
                     oq[ch] = qv * eg;
-                    ok[ch] = kv * emg;
-                    oe[ch] = eb[ch] * kv * eg;
-                    oke[ch] = kv * (eGend[ch] * emg);
+                    ok[ch] = slow ? kv : kv * ek;
+                    oe[ch] = ev * eg;
+                    okd[ch] = kv * ig;
+                    oet[ch] = ev * egt * eR[ch];
+                    oke[ch] = kv * ek * eG1[ch];
                 } else {
                     oq[ch] = qv;
                     ok[ch] = kv;
@@ -622,13 +759,77 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
             *reinterpret_cast<uint4 *>(tK + o) = R::pack(ok);
             *reinterpret_cast<uint4 *>(tZ + o) = R::pack(oz);
             if constexpr (HAS_E) *reinterpret_cast<uint4 *>(tE + o) = R::pack(oe);
-            if constexpr (CHAN) *reinterpret_cast<uint4 *>(tKe + o) = R::pack(oke);
+            if constexpr (DT) {
+                *reinterpret_cast<uint4 *>(tKd + o) = R::pack(okd);
+                *reinterpret_cast<uint4 *>(tEt + o) = R::pack(oet);
+                *reinterpret_cast<uint4 *>(tKe + o) = R::pack(oke);
+            }
         }
-        if constexpr (CHAN)
-            if (grp == NGRP - 1)
+        if constexpr (CHAN) {
+            if (slow) {
+                // The block's diagonal Gram tiles entry by entry,
+                //   T_ij = sum_c e_ic k_jc exp(Gb_ic - Gb_jc) (j < i), A_ij likewise with q (j <= i),
+                // from the raw rows of the tiles. Each lane sums its channel
+                // group over the pairs (own token i, token j of the block); the
+                // prefix Gb_j of its channel group comes from the lane holding
+                // token j, and the partial sums are added over the channel groups.
+                constexpr int GPB = NGRP / 4;
+                const int gi = grp - w * GPB;
+                wave_sync();  // the wave's raw rows are in the tiles
 #pragma unroll
-                for (int i = 0; i < V / 4; ++i)
-                    store4f(tab + V * co + 4 * i, f32x4{eGend[4 * i], eGend[4 * i + 1], eGend[4 * i + 2], eGend[4 * i + 3]});
+                for (int ii = 0; ii < TPT; ++ii) {
+                    const int ti = TPT * grp + ii;
+                    float qq[V], ee[V];
+                    R::widen(*reinterpret_cast<const uint4 *>(tQ + ti * PD + V * co), qq);
+                    R::widen(*reinterpret_cast<const uint4 *>(tE + ti * PD + V * co), ee);
+#pragma unroll 1
+                    for (int sg = 0; sg < GPB; ++sg) {
+                        const int src = sg * CO + co;
+#pragma unroll
+                        for (int jj = 0; jj < TPT; ++jj) {
+                            float kk[V];
+                            R::widen(*reinterpret_cast<const uint4 *>(tK + (16 * w + TPT * sg + jj) * PD + V * co), kk);
+                            float pt = 0.f, pa = 0.f;
+#pragma unroll
+                            for (int ch = 0; ch < V; ++ch) {
+                                const float kf = kk[ch] * fast_exp(fminf(G[ii][ch] - __shfl(G[jj][ch], src), 0.f));
+                                pt += ee[ch] * kf;
+                                pa += qq[ch] * kf;
+                            }
+                            pt = lanes_allreduce<CO>(pt);
+                            pa = lanes_allreduce<CO>(pa);
+                            const int il = TPT * gi + ii, jl = TPT * sg + jj;
+                            if ((ii * TPT + jj) % CO == co) {
+                                sTd[(w * 16 + jl) * 17 + il] = jl < il ? pt : 0.f;
+                                sAc[(16 * w + jl) * LC + 16 * w + il] = Elem<IO>::to(jl <= il ? pa : 0.f);
+                            }
+                        }
+                    }
+                }
+                wave_sync();  // every raw row read: scale this thread's rows to Q^, K^, E^
+#pragma unroll
+                for (int j = 0; j < TPT; ++j) {
+                    const int o = (TPT * grp + j) * PD + V * co;
+                    float qq[V], kk[V], ee[V];
+                    R::widen(*reinterpret_cast<const uint4 *>(tQ + o), qq);
+                    R::widen(*reinterpret_cast<const uint4 *>(tK + o), kk);
+                    R::widen(*reinterpret_cast<const uint4 *>(tE + o), ee);
+                    float ke[V];
+#pragma unroll
+                    for (int ch = 0; ch < V; ++ch) {
+                        const float eg = fast_exp(G[j][ch]), ek = fast_exp(fminf(Bmy[ch] - G[j][ch], 0.f));
+                        qq[ch] *= eg;
+                        ee[ch] *= eg;
+                        kk[ch] *= ek;
+                        ke[ch] = kk[ch] * eG1[ch];
+                    }
+                    *reinterpret_cast<uint4 *>(tQ + o) = R::pack(qq);
+                    *reinterpret_cast<uint4 *>(tK + o) = R::pack(kk);
+                    *reinterpret_cast<uint4 *>(tE + o) = R::pack(ee);
+                    if constexpr (DT) *reinterpret_cast<uint4 *>(tKe + o) = R::pack(ke);
+                }
+            }
+        }
         // The raw inputs are consumed: start fetching the next unit's.
         if (has_next && !next_same) in.template load<0>(a, un, co, grp);
         __syncthreads();
@@ -643,13 +844,19 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
                 const int p = w + NW * s, kind = p / 10;
                 int ti, tj;
                 lower_tile(p - kind * 10, ti, tj);
-                const IO *X = (kind == 0 ? TL : tQ) + ti * 16 * PD, *Y = tK + tj * 16 * PD;
+                const IO *X = (kind == 0 ? TL : tQ) + ti * 16 * PD, *Y = (DT && ti == tj ? tKd : tK) + tj * 16 * PD;
                 Frag fa[KD], fb[KD];
 #pragma unroll
                 for (int ks = 0; ks < KD; ++ks) {
                     fa[ks] = M::load(X + ks * KS, PD);
                     fb[ks] = M::load(Y + ks * KS, PD);
                 }
+                if constexpr (CHAN)  // the tile's per-channel factor (the diagonal's is in tKd with bfloat16 io)
+                    if (ti - tj >= 2 || (!DT && ti == tj)) {
+                        const float *f = sDec + (ti == tj ? 7 + ti : dec_row_far(ti, tj)) * D + FE * lg;
+#pragma unroll
+                        for (int ks = 0; ks < KD; ++ks) fb[ks] = K::scale(fb[ks], f + ks * KS);
+                    }
                 x[s] = zero4();
 #pragma unroll
                 for (int ks = 0; ks < KD; ++ks) x[s] = M::mma(x[s], fa[ks], fb[ks]);
@@ -676,7 +883,9 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
                     const bool keep = kind == 0 ? col < row0 + r : col <= row0 + r;
                     y[r] = keep ? y[r] : 0.f;
                 }
-                if (kind == 0 && ti == tj) {
+                // (Diagonal tiles of a block formed entry by entry in phase A are kept.)
+                if (CHAN && ti == tj && sSlow[ti]) {
+                } else if (kind == 0 && ti == tj) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) sTd[(ti * 16 + lr) * 17 + 4 * lg + r] = y[r];
                 } else {
@@ -688,16 +897,22 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
                 const int ti = z < 3 ? 0 : z < 5 ? 1 : 2, tj = z < 3 ? z + 1 : z < 5 ? z - 1 : 3;
                 store4f(sAc + (tj * 16 + lr) * LC + ti * 16 + 4 * lg, zero4());
             }
+            // Q~ (or raw q once per QK head) fragments; per-channel decay: Q~ = Q^ . exp(R_b), b = rt.
             if (write_kT)
                 for (int f = w; f < (C / 16) * (D / KS); f += NW) {
                     const int rt = f / (D / KS), ks = f - rt * (D / KS);
-                    store_frag<IO>(CHAN ? wQ : wQh, rt, ks, D, M::load(tQ + rt * 16 * PD + ks * KS, PD));
+                    Frag x = M::load(tQ + rt * 16 * PD + ks * KS, PD);
+                    if constexpr (CHAN) x = K::scale(x, sDec + rt * D + ks * KS + FE * lg);
+                    store_frag<IO>(CHAN ? wQ : wQh, rt, ks, D, x);
                 }
             // Kend^T (or raw k^T) fragments: rows = channels, K = tokens, read K-major from the tiles.
             if (write_kT)
                 for (int f = w; f < (D / 16) * (C / KS); f += NW) {
                     const int rt = f / (C / KS), ks = f - rt * (C / KS);
-                    store_frag<IO>(wKT, rt, ks, C, K::frag((CHAN ? tKe : tK) + ks * KS * PD + rt * 16, PD));
+                    Frag x = K::frag((DT ? tKe : tK) + ks * KS * PD + rt * 16, PD);
+                    if constexpr (CHAN && !DT)  // Kend = K^ . exp(G_end - R_{b+1}), b = the fragment's token block
+                        x = K::scale(x, sDec[(11 + ((ks * KS + FE * lg) >> 4)) * D + rt * 16 + lr]);
+                    store_frag<IO>(wKT, rt, ks, C, x);
                 }
         }
         __syncthreads();
@@ -766,13 +981,17 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
             for (int ct = 0; ct < NCTS; ++ct) {
                 const int c0 = WC * w + 16 * ct;
                 const bool zside = c0 >= D;
-                const IO *src = zside ? tZ + (c0 - D) : (HAS_E ? tE : tK) + c0;
+                const IO *src = zside ? tZ + (c0 - D) : (DT ? tEt : HAS_E ? tE : tK) + c0;
                 Frag bf[NKS];
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) {
                     bf[ks] = K::frag(src + ks * KS * PD, PD);
-                    if constexpr (!CHAN)
-                        if (!zside) bf[ks] = K::scale(bf[ks], sSE + ks * KS + FE * lg);
+                    if (!zside) {
+                        if constexpr (!CHAN)
+                            bf[ks] = K::scale(bf[ks], sSE + ks * KS + FE * lg);
+                        else if constexpr (!DT)  // E~ = E^ . exp(R_b), b = the fragment's token block
+                            bf[ks] = K::scale(bf[ks], sDec[((ks * KS + FE * lg) >> 4) * D + c0 + lr]);
+                    }
                 }
 #pragma unroll
                 for (int ri = 0; ri < 4; ++ri) {
@@ -1276,17 +1495,17 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t s) {
     // decoupled-gate variants keep more tiles.
     // Once per process (thread-safe): allow each variant its shared memory.
     static const hipError_t attr_err = [] {
-        const void *fns[8] = {reinterpret_cast<const void *>(&chunk_prep<IO, D, false, false, false>),
+        // (With a per-channel decay the input stage runs as a pass of its own,
+        // stage.hip, so there is no input-stage variant of those preps.)
+        const void *fns[6] = {reinterpret_cast<const void *>(&chunk_prep<IO, D, false, false, false>),
                               reinterpret_cast<const void *>(&chunk_prep<IO, D, false, true, false>),
                               reinterpret_cast<const void *>(&chunk_prep<IO, D, true, false, false>),
                               reinterpret_cast<const void *>(&chunk_prep<IO, D, true, true, false>),
                               reinterpret_cast<const void *>(&chunk_prep<IO, D, false, false, true>),
-                              reinterpret_cast<const void *>(&chunk_prep<IO, D, false, true, true>),
-                              reinterpret_cast<const void *>(&chunk_prep<IO, D, true, false, true>),
-                              reinterpret_cast<const void *>(&chunk_prep<IO, D, true, true, true>)};
+                              reinterpret_cast<const void *>(&chunk_prep<IO, D, false, true, true>)};
         const size_t lds[4] = {Cfg::bytes(false, false), Cfg::bytes(true, false), Cfg::bytes(true, true),
                                Cfg::bytes(true, true)};
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 6; ++i) {
             hipError_t e = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds[i % 4]);
             if (e != hipSuccess) return e;
         }
@@ -1318,9 +1537,8 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t s) {
         const long long grid = items < slots ? items : slots;
         const dim3 g((unsigned)grid), b(Cfg::NT);
         if (a.conv_w) {
-            if (chan && bw) hipLaunchKernelGGL((chunk_prep<IO, D, true, true, true>), g, b, Cfg::bytes(true, true), s, ap);
-            else if (chan) hipLaunchKernelGGL((chunk_prep<IO, D, true, false, true>), g, b, Cfg::bytes(true, true), s, ap);
-            else if (bw) hipLaunchKernelGGL((chunk_prep<IO, D, false, true, true>), g, b, Cfg::bytes(true, false), s, ap);
+            if (chan) return hipErrorInvalidValue;  // the input stage runs first as a pass of its own
+            if (bw) hipLaunchKernelGGL((chunk_prep<IO, D, false, true, true>), g, b, Cfg::bytes(true, false), s, ap);
             else hipLaunchKernelGGL((chunk_prep<IO, D, false, false, true>), g, b, Cfg::bytes(false, false), s, ap);
         } else {
             if (chan && bw) hipLaunchKernelGGL((chunk_prep<IO, D, true, true, false>), g, b, Cfg::bytes(true, true), s, ap);

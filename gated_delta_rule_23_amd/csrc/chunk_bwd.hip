@@ -4,8 +4,10 @@
 // Eficiente por Blocos", names a backward pass that is parallel over blocks
 // of tokens and in which the gates enter the gradient accumulation; it prints
 // no formula. What is computed here is the exact gradient of the chunked
-// forward of the page "Gated Delta Networks", sections on the chunked
-// (WY/UT) form, which equals the token recurrence. Per (sequence, V head) and
+// (WY/UT) forward of the page "Uma análise das variantes de atenção linear
+// da família DeltaNet", section "Chunkwise KDA" and its subsections, with the
+// decoupled gates of that same "Treinamento Paralelo" section; the chunked
+// form equals the token recurrence. Per (sequence, V head) and
 // chunk of C = 64 tokens, with S the state entering the chunk, G the in-chunk
 // inclusive sums of the log-decay g, e = beta k or b . k, z = beta v or w . v:
 //

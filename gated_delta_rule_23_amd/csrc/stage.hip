@@ -1,0 +1,176 @@
+// stage.hip -- the input stage as a pass of its own, for the chunked prefill
+// of per-channel-decay layers (gdr_chunk_fwd_in with GDR_DECAY_CHANNEL).
+//
+// The input stage (page "Gated DeltaNet: o mixer em 48 das 64 camadas",
+// section "Conceito": a causal depthwise convolution of kernel 4 over the
+// projected q, k and v; normalised keys per the family analysis's notation;
+// sigmoid gates and a softplus-shaped decay) is fused into the prefill's load
+// stage for scalar-decay layers. With a per-channel decay the prefill's load
+// stage already holds seven token-major tiles of the chunk, so there the
+// stage runs first, over the whole call, and writes the processed q, k, v,
+// the activated gates and the decay g into the call's workspace; the
+// prefill then runs on them as gdr_chunk_fwd does. Both passes stream: the
+// convolution reads each raw row plus the 3 rows before it (L2-resident),
+// and each processed row is written once.
+//
+//  stage_conv: one thread per 16-byte channel group of one (sequence, token,
+//    head) row of q, k or v; the D / V threads of a row are consecutive lanes,
+//    so the norm of q and k is a DPP all-reduce inside the wave. The thread of
+//    the last token also writes the outgoing convolution state (the last 3
+//    raw tokens, rows before the call taken from conv_in).
+//  stage_gates: elementwise g = -c_h softplus(x) (per channel), beta, b and w
+//    = sigmoid(x).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace gdr {
+namespace {
+
+constexpr float kNormEps = 1e-12f;  // q, k = x / sqrt(|x|^2 + kNormEps)
+
+template <typename IO> struct Vec16;  // 16 bytes of io elements, widened to float and back
+template <> struct Vec16<bf16_t> {
+    static constexpr int N = 8;
+    __device__ __forceinline__ static void widen(uint4 r, float *f) {
+        const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = __uint_as_float(w[i] << 16);
+            f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+    __device__ __forceinline__ static uint4 pack(const float *f) {
+        return uint4{f2bf2(f[0], f[1]), f2bf2(f[2], f[3]), f2bf2(f[4], f[5]), f2bf2(f[6], f[7])};
+    }
+};
+template <> struct Vec16<float> {
+    static constexpr int N = 4;
+    __device__ __forceinline__ static void widen(uint4 r, float *f) {
+        f[0] = __uint_as_float(r.x); f[1] = __uint_as_float(r.y); f[2] = __uint_as_float(r.z); f[3] = __uint_as_float(r.w);
+    }
+    __device__ __forceinline__ static uint4 pack(const float *f) {
+        return uint4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3])};
+    }
+};
+
+template <typename IO, int D>
+__global__ __launch_bounds__(256) void stage_conv(StageArgs a) {
+    using W = Vec16<IO>;
+    constexpr int V = W::N, CO = D / V, RPB = 256 / CO;  // channel groups per row, rows per workgroup
+    static_assert(64 % CO == 0, "a row's lanes lie in one wave");
+    const int tid = threadIdx.x, co = tid % CO;
+    const long long row = (long long)blockIdx.x * RPB + tid / CO;
+    const int NH = 2 * a.Hqk + a.Hv;
+    const long long rows = (long long)a.B * a.T * NH;
+    const bool valid = row < rows;
+    const long long r = valid ? row : rows - 1;  // lanes past the end repeat the last row and store nothing
+    const int hh = (int)(r % NH);
+    const long long bt = r / NH;
+    const int t = (int)(bt % a.T), b = (int)(bt / a.T);
+    // Tensor, its head count and head, and the channel in the concatenated
+    // (q, k, v) channel space of the taps and the convolution state.
+    const int x = hh < a.Hqk ? 0 : hh < 2 * a.Hqk ? 1 : 2;
+    const int H = x == 2 ? a.Hv : a.Hqk, head = x == 2 ? hh - 2 * a.Hqk : hh - x * a.Hqk;
+    const IO *src = static_cast<const IO *>(x == 0 ? a.q : x == 1 ? a.k : a.v);
+    IO *dst = static_cast<IO *>(x == 0 ? a.qo : x == 1 ? a.ko : a.vo);
+    const size_t ch = (size_t)NH * D, c0 = (size_t)hh * D + V * co;
+    const auto at = [&](int tt) -> size_t { return (((size_t)b * a.T + tt) * H + head) * D + V * co; };
+
+    uint4 wnd[4];  // raw rows t-3 .. t of this channel group
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int tt = t - 3 + j;
+        wnd[j] = tt >= 0 ? *reinterpret_cast<const uint4 *>(src + at(tt))
+                 : a.conv_in ? *reinterpret_cast<const uint4 *>(static_cast<const IO *>(a.conv_in) +
+                                                                 ((size_t)b * 3 + 3 + tt) * ch + c0)
+                             : uint4{0u, 0u, 0u, 0u};
+    }
+    float xs[4][V], out[V];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) W::widen(wnd[j], xs[j]);
+#pragma unroll
+    for (int c = 0; c < V; ++c) {
+        const f32x4 tp = load4f(a.conv_w + (c0 + c) * 4);
+        out[c] = tp[0] * xs[0][c] + tp[1] * xs[1][c] + tp[2] * xs[2][c] + tp[3] * xs[3][c];
+    }
+    if (x < 2) {  // q and k: normalised over the head
+        float ss = 0.f;
+#pragma unroll
+        for (int c = 0; c < V; ++c) ss += out[c] * out[c];
+        if constexpr (CO == 32) {
+            ss = lanes_allreduce<16>(ss);
+            ss += __shfl_xor(ss, 16);
+        } else {
+            ss = lanes_allreduce<CO>(ss);
+        }
+        const float f = 1.f / sqrtf(ss + kNormEps);
+#pragma unroll
+        for (int c = 0; c < V; ++c) out[c] *= f;
+    }
+    if (valid) {
+        *reinterpret_cast<uint4 *>(dst + at(t)) = W::pack(out);
+        if (a.conv_out && t == a.T - 1)
+#pragma unroll
+            for (int j = 0; j < 3; ++j)
+                *reinterpret_cast<uint4 *>(static_cast<IO *>(a.conv_out) + ((size_t)b * 3 + j) * ch + c0) = wnd[1 + j];
+    }
+}
+
+// Elementwise activations: n4 groups of 4 elements of g (per channel, D a
+// multiple of 4) and of b, w (decoupled gates), then nb elements of beta.
+template <typename IO, int D>
+__global__ __launch_bounds__(256) void stage_gates(StageArgs a) {
+    const long long n4 = (long long)a.B * a.T * a.Hv * D / 4, nb = a.beta ? (long long)a.B * a.T * a.Hv : 0;
+    const long long step = (long long)gridDim.x * blockDim.x;
+    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n4 + nb; i += step) {
+        if (i < n4) {
+            const int h = (int)((4 * i / D) % a.Hv);
+            const float c = a.decay_scale ? a.decay_scale[h] : 1.f;
+            const f32x4 x = load4f(a.g + 4 * i);
+            store4f(a.go + 4 * i, f32x4{-c * act_softplus(x[0]), -c * act_softplus(x[1]), -c * act_softplus(x[2]),
+                                        -c * act_softplus(x[3])});
+            if (!a.beta) {
+                const f32x4 bx = load4f(static_cast<const IO *>(a.bg) + 4 * i), wx = load4f(static_cast<const IO *>(a.wg) + 4 * i);
+                store4f(static_cast<IO *>(a.bgo) + 4 * i, f32x4{act_sigmoid(bx[0]), act_sigmoid(bx[1]), act_sigmoid(bx[2]),
+                                                                act_sigmoid(bx[3])});
+                store4f(static_cast<IO *>(a.wgo) + 4 * i, f32x4{act_sigmoid(wx[0]), act_sigmoid(wx[1]), act_sigmoid(wx[2]),
+                                                                act_sigmoid(wx[3])});
+            }
+        } else {
+            const long long j = i - n4;
+            a.betao[j] = act_sigmoid(a.beta[j]);
+        }
+    }
+}
+
+template <typename IO, int D>
+hipError_t launch_stage_t(const StageArgs &a, hipStream_t s) {
+    constexpr int CO = D / (16 / (int)sizeof(IO)), RPB = 256 / CO;
+    const long long rows = (long long)a.B * a.T * (2 * a.Hqk + a.Hv);
+    if (rows > 0) {
+        const long long grid = (rows + RPB - 1) / RPB;
+        if (grid > 0x7fffffffll) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((stage_conv<IO, D>), dim3((unsigned)grid), dim3(256), 0, s, a);
+        const long long work = (long long)a.B * a.T * a.Hv * D / 4 + (a.beta ? (long long)a.B * a.T * a.Hv : 0);
+        const long long g2 = (work + 255) / 256 < 8192 ? (work + 255) / 256 : 8192;
+        hipLaunchKernelGGL((stage_gates<IO, D>), dim3((unsigned)g2), dim3(256), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_stage(int io, int D, const StageArgs &a, hipStream_t s) {
+    if (io == IO_BF16) {
+        if (D == 32) return launch_stage_t<bf16_t, 32>(a, s);
+        if (D == 64) return launch_stage_t<bf16_t, 64>(a, s);
+        if (D == 128) return launch_stage_t<bf16_t, 128>(a, s);
+    } else {
+        if (D == 32) return launch_stage_t<float, 32>(a, s);
+        if (D == 64) return launch_stage_t<float, 64>(a, s);
+        if (D == 128) return launch_stage_t<float, 128>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdr

@@ -59,9 +59,13 @@
  * - Supported: d_k, d_v in {32, 64, 128}; chunk == 64; io float32 or
  *   bfloat16. Arithmetic: state and accumulation in float32; bfloat16 io runs
  *   the chunk products on bf16 matrix cores, float32 io on float32 ones.
- *   With GDR_DECAY_CHANNEL the cumulative log-decay inside one 64-token chunk
- *   must stay above -80 (the chunk factors scale keys by exp(-G)); scalar
- *   decay has no such limit.
+ *   Any finite g <= 0 is accepted: the chunked forward references the decay
+ *   inside a chunk to its 16-token blocks ("Pipeline Triton da versão por
+ *   chunks": the diagonal 16-token blocks first), so no factor it forms
+ *   exceeds exp(40), and a block that decays further is formed entry by entry.
+ *   gdr_chunk_bwd with GDR_DECAY_CHANNEL still factors exp(G_i - G_j) as
+ *   exp(G_i) exp(-G_j) and needs the cumulative log-decay inside one chunk to
+ *   stay above -80 on every channel (gdr_recurrent_bwd has no such limit).
  */
 #ifndef GDR_H
 #define GDR_H
@@ -193,14 +197,21 @@ typedef struct {
     const float *decay_scale;  /* [H_v] float32 c_h > 0, or NULL for 1 */
 } gdr_input_stage;
 
-/* gdr_chunk_fwd with the input stage fused into the prefill's load stage:
- * the per-chunk kernel reads the raw projections (plus the 3 tokens before
- * each chunk) and applies the convolution, the normalisation and the
- * activations before building the chunk's factors, so the processed q, k, v
- * never travel through memory. Arguments as gdr_recurrent_fwd_in, plus the
- * workspace of gdr_chunk_fwd (same size, gdr_chunk_workspace_bytes). The
- * chunk products run on bf16 matrix cores for bf16 io, so the processed q, k
- * and v are rounded to bf16 there, as the io values of gdr_chunk_fwd are. */
+/* gdr_chunk_fwd with the input stage in front of it. With a scalar decay
+ * (or none) the stage is fused into the prefill's load stage: the per-chunk
+ * kernel reads the raw projections (plus the 3 tokens before each chunk) and
+ * applies the convolution, the normalisation and the activations before
+ * building the chunk's factors, so the processed q, k, v never travel
+ * through memory. With a per-channel decay the stage runs as a pass of its
+ * own that writes the processed q, k, v (io dtype), the decay g and the
+ * gates (beta float32, b and w io dtype) into the workspace, and the prefill
+ * reads them there. Arguments as gdr_recurrent_fwd_in, plus a workspace of
+ * at least gdr_chunk_fwd_in_workspace_bytes (gdr_chunk_workspace_bytes plus,
+ * for a per-channel decay, the processed inputs). The chunk products run on
+ * bf16 matrix cores for bf16 io, so the processed q, k and v are rounded to
+ * bf16 there, as the io values of gdr_chunk_fwd are. */
+int gdr_chunk_fwd_in_workspace_bytes(const gdr_desc *desc, size_t *bytes);
+
 int gdr_chunk_fwd_in(const gdr_desc *desc, const gdr_input_stage *stage, const void *q, const void *k,
                      const void *v, const float *g, const float *beta, const void *b, const void *w,
                      const float *S0, void *o, float *ST, void *workspace, size_t workspace_bytes,
@@ -255,8 +266,9 @@ int gdr_recurrent_bwd(const gdr_desc *desc, const void *q, const void *k, const 
 
 /* The same gradients in chunked form, parallel over chunks of 64 tokens
  * ("Resumo Técnico: Gated DeltaNet-2", section "Treinamento Paralelo
- * Eficiente por Blocos"; the chunked forward of "Gated Delta Networks",
- * differentiated line by line). Per chunk, with S the state entering it,
+ * Eficiente por Blocos"; the chunked forward of "Uma análise das variantes
+ * de atenção linear da família DeltaNet", section "Chunkwise KDA" and its
+ * subsections, differentiated line by line). Per chunk, with S the state entering it,
  * G the in-chunk sums of g, E~ = e . exp(G), Q~ = q . exp(G),
  * Kend = k . exp(G_end - G), Gamma = exp(G_end), T and A the decayed
  * products of e, q with k below the diagonal, L = (I + T)^-1, Y = L E~ and
