@@ -202,6 +202,36 @@ def make_raw_inputs(wl: Workload, seed: int = 0, conv_state: bool = True) -> dic
     return out
 
 
+NLA_ORDER = ("phq", "phk", "v", "S0", "z0")
+
+
+def make_norm_la_inputs(B, T, Hqk, Hv, D, io="bf16", seed=0, state=False) -> dict:
+    """Seeded inputs of the normalised linear-attention read, prefill layout:
+    phq, phk [B, T, H_qk, D] and v [B, T, H_v, D] in the io dtype, the
+    feature-mapped queries and keys drawn as non-negative values
+    elu(x) + 1 with x ~ N(0, 1) (a distribution choice for the inputs; the
+    feature map itself is the caller's); v ~ N(0, 1). With state, an incoming
+    state S0 = 0.02 N(0, 1) [B, H_v, D, D] and normaliser z0 = |N(0, 1)|
+    [B, H_v, D] in float32 (z0 as the sum of earlier non-negative keys would
+    be); otherwise None. One child stream per tensor in NLA_ORDER."""
+    streams = dict(zip(NLA_ORDER, (np.random.Generator(np.random.PCG64(s))
+                                   for s in np.random.SeedSequence([seed, 4]).spawn(len(NLA_ORDER)))))
+
+    def feat(x):
+        return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+
+    out = {"seed": seed, "io": io}
+    out["phq"] = _store(feat(streams["phq"].standard_normal((B, T, Hqk, D))), io)
+    out["phk"] = _store(feat(streams["phk"].standard_normal((B, T, Hqk, D))), io)
+    out["v"] = _store(streams["v"].standard_normal((B, T, Hv, D)), io)
+    if state:
+        out["S0"] = _store(0.02 * streams["S0"].standard_normal((B, Hv, D, D)), "f32")
+        out["z0"] = _store(np.abs(streams["z0"].standard_normal((B, Hv, D))), "f32")
+    else:
+        out["S0"] = out["z0"] = None
+    return out
+
+
 def as_sequence(inp: dict) -> dict:
     """Decode inputs are step-major [steps, B, ...]; return a copy with every
     per-step tensor reordered to [B, steps, ...] (a sequential run's layout)."""

@@ -19,6 +19,8 @@ Contents
                    the recurrence (numpy, fp64).
 ``backward``       the gradients of the recurrence by reverse-mode
                    differentiation (numpy, fp64).
+``norm_la``        normalised linear attention (the feature-mapped read with
+                   a normaliser), token by token (numpy, fp64).
 
 Stored values: a ``numpy.uint16`` array holds bfloat16 bit patterns, a
 ``float32`` or ``float64`` array holds its own values. Every value is widened
