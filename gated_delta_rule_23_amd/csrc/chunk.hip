@@ -109,21 +109,25 @@ __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp
 // so no factor can overflow or vanish at any decay. The chunk-referenced
 // operands follow by factors <= 1:
 //   Q~ = Q^ . exp(R_b),  E~ = E^ . exp(R_b),  Kend = K^ . exp(G_end - R_{b+1}).
-// kDecRows rows of per-channel factors, row r = exp(sum over the blocks in
-// mask r of B), negated and capped at kDiagRange for the diagonal rows:
+// kDecRows rows of per-channel factors (written by the wave of the block
+// whose sums give them):
 //   0-3   exp(R_b)                      (Q~, E~ of block b)
 //   4-6   exp(B_1), exp(B_2), exp(B_1 + B_2)   (Gram tiles (2,0), (3,1), (3,0))
-//   7-10  exp(-B_b)                     (diagonal Gram tile of block b)
+//   7-10  exp(-B_b), capped at exp(kDiagRange)   (diagonal Gram tile of block b)
 //   11-14 exp(G_end - R_{b+1})          (Kend of block b)
+//   15    exp(G_end)                    (Kend of a mild chunk)
 // With bfloat16 io, phase A writes the diagonal K operand, E~ and Kend as
 // tiles of their own, so that no bfloat16 operand is unpacked and rescaled
 // on the matrix-core path; with float32 io (whose tiles are twice as large)
 // the operands are scaled as they are read, one multiply per element.
 constexpr int kDecRows = 16;
 constexpr float kDiagRange = 40.f;
-constexpr uint64_t kDecMask = 0x0ull | 0x1ull << 4 | 0x3ull << 8 | 0x7ull << 12 | 0x2ull << 16 | 0x4ull << 20 |
-                              0x6ull << 24 | 0x1ull << 28 | 0x2ull << 32 | 0x4ull << 36 | 0x8ull << 40 |
-                              0xEull << 44 | 0xCull << 48 | 0x8ull << 52 | 0x0ull << 56;
+// A chunk whose every 16-token block decays by less than kMildBlock on every
+// channel keeps the chunk-referenced factors of the plain form (E~ and Q~ as
+// above, K~ = k . exp(-G) <= exp(4 kMildBlock), Kend = K~ . exp(G_end)): the
+// decays of ordinary layers stay far inside that range, and their chunks
+// then need neither the block factors nor their extra tiles.
+constexpr float kMildBlock = 15.f;
 __host__ __device__ constexpr int dec_row_far(int bi, int bj) {  // factor row of Gram tile (bi, bj), bi - bj >= 2
     return bi == 2 ? 4 : bj == 1 ? 5 : 6;
 }
@@ -281,7 +285,7 @@ struct PrepCfg {
     static constexpr size_t TD = a16((size_t)4 * 16 * 17 * 4);
     static constexpr size_t TAB = a16((size_t)5 * C * 4);
     static constexpr size_t PART = a16((size_t)NGRP * D * 4);
-    static constexpr size_t DEC = a16((size_t)kDecRows * D * 4) + 16;  // decay factor rows + 4 block flags
+    static constexpr size_t DEC = a16((size_t)kDecRows * D * 4) + 32;  // decay factor rows + 4 block flags
     static_assert(NT % CO == 0 && NGRP * TPT == C && WC % 16 == 0, "phase mappings");
     // Phase A: each wave holds the tokens of one 16-token block.
     static_assert(TPT * (64 / CO) == 16 && C / 16 == NW, "one 16-token block per wave in phase A");
@@ -417,7 +421,8 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
     float *sEG = sG + C;                                          //   exp(G),
     float *sBt = sG + 3 * C;                                      //   beta,
     float *sSE = sG + 4 * C;                                      //   the E~ factor of a raw erase-key tile
-    float *sPart = reinterpret_cast<float *>(sTc);                // [NGRP][D] per-group channel sums (phase A only)
+    float *sBlk = reinterpret_cast<float *>(sTmp);                // [4][D] block sums of g (phase A only)
+    float *sPart = reinterpret_cast<float *>(sTc);                // [NGRP][D] token-group sums of g (phase A only)
     float *sDec = reinterpret_cast<float *>(sp);                  // [kDecRows][D] per-channel decay factors
     int *sSlow = reinterpret_cast<int *>(sDec + kDecRows * D);    // [4]: diagonal block formed entry by entry
     IO *sYc = tQ;                                                 // Y(t, c) at sYc[c * LY + t]
@@ -485,6 +490,7 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
                     for (int c4 = 0; c4 < V; ++c4) taps[x * V + c4] = load4f(a.conv_w + (cb[x] + c4) * 4);
         }
         float G[CHAN ? TPT : 1][V];
+        float Bmy[CHAN ? V : 1];  // per-channel decay sum of this thread's 16-token block (the wave's block)
         if constexpr (CHAN) {
 #pragma unroll
             for (int j = 0; j < TPT; ++j)
@@ -492,10 +498,40 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
                 for (int ch = 0; ch < V; ++ch)
                     G[j][ch] = (TPT * grp + j < n ? stage_decay<RAW>(in.g[j * (V / 4) + ch / 4][ch % 4], dsc) : 0.f) +
                                (j > 0 ? G[j - 1][ch] : 0.f);
+            // The wave holds one 16-token block: its groups' totals, exchanged
+            // through shared memory inside the wave, give the offset that turns
+            // each local prefix into the in-block prefix Gb and the block's sum
+            // B, which goes to sBlk for the other waves.
 #pragma unroll
             for (int i = 0; i < V / 4; ++i)
                 store4f(sPart + grp * D + V * co + 4 * i,
                         f32x4{G[TPT - 1][4 * i], G[TPT - 1][4 * i + 1], G[TPT - 1][4 * i + 2], G[TPT - 1][4 * i + 3]});
+            wave_sync();
+            constexpr int GPB = NGRP / 4;
+            float Bw[V], off[V];
+#pragma unroll
+            for (int ch = 0; ch < V; ++ch) Bw[ch] = off[ch] = 0.f;
+#pragma unroll
+            for (int gg = 0; gg < GPB; ++gg)
+#pragma unroll
+                for (int i = 0; i < V / 4; ++i) {
+                    const f32x4 p = load4f(sPart + (w * GPB + gg) * D + V * co + 4 * i);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        Bw[4 * i + r] += p[r];
+                        if (w * GPB + gg < grp) off[4 * i + r] += p[r];
+                    }
+                }
+#pragma unroll
+            for (int ch = 0; ch < V; ++ch)
+#pragma unroll
+                for (int j = 0; j < TPT; ++j) G[j][ch] += off[ch];
+            if (l < CO)
+#pragma unroll
+                for (int i = 0; i < V / 4; ++i)
+                    store4f(sBlk + w * D + V * co + 4 * i, f32x4{Bw[4 * i], Bw[4 * i + 1], Bw[4 * i + 2], Bw[4 * i + 3]});
+#pragma unroll
+            for (int ch = 0; ch < V; ++ch) Bmy[ch] = Bw[ch];
         }
         if (w == 0) {
             float eg = 1.f;
@@ -604,92 +640,78 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
             stage(in.v, 2, cv, false);
             __syncthreads();  // every window read before the tiles are overwritten
         }
-        float eGend[V];
-        float Bmy[CHAN ? V : 1];  // per-channel decay sum of this thread's 16-token block (the wave's block)
-        // exp(B), exp(R) and exp(G_end - R_{b+1}) of that block
-        float eB[CHAN ? V : 1], eR[CHAN ? V : 1], eG1[CHAN ? V : 1];
+        // exp(B), exp(R) and exp(G_end - R_{b+1}) of that block; exp(G_end)
+        float eB[CHAN ? V : 1], eR[CHAN ? V : 1], eG1[CHAN ? V : 1], eGe[CHAN ? V : 1];
+        bool mild = true;  // the chunk keeps the chunk-referenced factors (uniform over the workgroup)
         if constexpr (CHAN) {
-            // Block sums B_b (the first group of each block sums its block's
-            // group totals into sBlk, in the per-wave temporaries that are
-            // free until phase C), and the offset that turns this thread's
-            // local prefix into the in-block prefix Gb (groups of its block
-            // before it).
+            // Sums over the blocks before this thread's block (R_b), its block
+            // (B_b), the blocks after it (G_end - R_{b+1}) and the block just
+            // before it; the wave's block is b = w, uniform over the wave.
+            // Every wave reads all four block sums of every channel, so the
+            // mild test (a ballot over them) agrees across the workgroup. The
+            // block index is taken per lane (grp / GPB, equal to w) so that
+            // the selects below stay branch-free.
             constexpr int GPB = NGRP / 4;
-            const int g0 = w * GPB;
-            float *sBlk = reinterpret_cast<float *>(sTmp);  // [4][D]
-            float off[V];
+            const int myb = grp / GPB;
+            float Rb[V], Pv[V], Af[V];
+            bool steep = false;
 #pragma unroll
-            for (int ch = 0; ch < V; ++ch) off[ch] = 0.f;
-            if (grp == g0) {
-                float bs[V];
+            for (int ch = 0; ch < V; ++ch) Rb[ch] = Pv[ch] = Af[ch] = 0.f;
 #pragma unroll
-                for (int ch = 0; ch < V; ++ch) bs[ch] = 0.f;
-#pragma unroll 4
-                for (int gg = 0; gg < GPB; ++gg)
-#pragma unroll
-                    for (int i = 0; i < V / 4; ++i) {
-                        const f32x4 p = load4f(sPart + (g0 + gg) * D + V * co + 4 * i);
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) bs[4 * i + r] += p[r];
-                    }
-#pragma unroll
-                for (int i = 0; i < V / 4; ++i)
-                    store4f(sBlk + w * D + V * co + 4 * i, f32x4{bs[4 * i], bs[4 * i + 1], bs[4 * i + 2], bs[4 * i + 3]});
-            } else {
-#pragma unroll 4
-                for (int g2 = g0; g2 < grp; ++g2)
-#pragma unroll
-                    for (int i = 0; i < V / 4; ++i) {
-                        const f32x4 p = load4f(sPart + g2 * D + V * co + 4 * i);
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) off[4 * i + r] += p[r];
-                    }
-            }
-            __syncthreads();
-            float Bs[4][V];
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
+            for (int b2 = 0; b2 < 4; ++b2)
 #pragma unroll
                 for (int i = 0; i < V / 4; ++i) {
-                    const f32x4 p = load4f(sBlk + b * D + V * co + 4 * i);
+                    const f32x4 p = load4f(sBlk + b2 * D + V * co + 4 * i);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) Bs[b][4 * i + r] = p[r];
+                    for (int r = 0; r < 4; ++r) {
+                        const float x = p[r];
+                        steep = steep || x <= -kMildBlock;
+                        Rb[4 * i + r] += b2 < myb ? x : 0.f;
+                        Af[4 * i + r] += b2 > myb ? x : 0.f;
+                        Pv[4 * i + r] = b2 == myb - 1 ? x : Pv[4 * i + r];
+                    }
                 }
+            mild = __ballot(steep) == 0;
 #pragma unroll
             for (int ch = 0; ch < V; ++ch) {
-                Bmy[ch] = w == 0 ? Bs[0][ch] : w == 1 ? Bs[1][ch] : w == 2 ? Bs[2][ch] : Bs[3][ch];
-                eB[ch] = fast_exp(Bmy[ch]);
-                eR[ch] = fast_exp(w == 0 ? 0.f : w == 1 ? Bs[0][ch] : w == 2 ? Bs[0][ch] + Bs[1][ch]
-                                                                   : Bs[0][ch] + Bs[1][ch] + Bs[2][ch]);
-                eG1[ch] = fast_exp(w == 0 ? Bs[1][ch] + Bs[2][ch] + Bs[3][ch] : w == 1 ? Bs[2][ch] + Bs[3][ch]
-                                                                   : w == 2 ? Bs[3][ch] : 0.f);
-                eGend[ch] = fast_exp(Bs[0][ch] + Bs[1][ch] + Bs[2][ch] + Bs[3][ch]);
-#pragma unroll
-                for (int j = 0; j < TPT; ++j) G[j][ch] += off[ch];
+                eR[ch] = fast_exp(Rb[ch]);
+                eGe[ch] = fast_exp(Rb[ch] + Bmy[ch] + Af[ch]);
             }
-            // Row grp of the decay factor table, for this thread's channels.
-            if (grp < kDecRows - 1) {
-                const unsigned m = (unsigned)(kDecMask >> (4 * grp)) & 0xFu;
-                const bool neg = grp >= 7 && grp < 11;
-                float f[V];
+            if (!mild)
 #pragma unroll
                 for (int ch = 0; ch < V; ++ch) {
-                    const float x = ((m & 1u) ? Bs[0][ch] : 0.f) + ((m & 2u) ? Bs[1][ch] : 0.f) +
-                                    ((m & 4u) ? Bs[2][ch] : 0.f) + ((m & 8u) ? Bs[3][ch] : 0.f);
-                    f[ch] = fast_exp(neg ? fminf(-x, kDiagRange) : x);
+                    eB[ch] = fast_exp(Bmy[ch]);
+                    eG1[ch] = fast_exp(Af[ch]);
                 }
+            // The decay factor table: the first group of each wave writes the
+            // rows its block's sums give.
+            const auto put_row = [&](int row, const float(&f)[V]) {
 #pragma unroll
                 for (int i = 0; i < V / 4; ++i)
-                    store4f(sDec + grp * D + V * co + 4 * i, f32x4{f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3]});
+                    store4f(sDec + row * D + V * co + 4 * i, f32x4{f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3]});
+            };
+            if (!Cfg::DTILES && w == 3 && l < CO) put_row(15, eGe);  // exp(G_end)
+            if (!mild && l < CO) {
+                put_row(w, eR);                                  // exp(R_b)
+                if (w == 1 || w == 2) put_row(3 + w, eB);        // exp(B_1), exp(B_2)
+                if (w == 2) {                                    // exp(B_1 + B_2)
+                    float f[V];
+#pragma unroll
+                    for (int ch = 0; ch < V; ++ch) f[ch] = fast_exp(Pv[ch] + Bmy[ch]);
+                    put_row(6, f);
+                }
+                if constexpr (!Cfg::DTILES) {
+                    float f[V];
+#pragma unroll
+                    for (int ch = 0; ch < V; ++ch) f[ch] = fast_exp(fminf(-Bmy[ch], kDiagRange));
+                    put_row(7 + w, f);                           // exp(-B_b)
+                    put_row(11 + w, eG1);                        // exp(G_end - R_{b+1})
+                }
             }
             if (grp == NGRP - 1)  // gamma per channel for the sweep
 #pragma unroll
                 for (int i = 0; i < V / 4; ++i)
-                    store4f(tab + V * co + 4 * i, f32x4{eGend[4 * i], eGend[4 * i + 1], eGend[4 * i + 2], eGend[4 * i + 3]});
-        } else {
-            const float e = sEG[C - 1];
-#pragma unroll
-            for (int ch = 0; ch < V; ++ch) eGend[ch] = e;
+                    store4f(tab + V * co + 4 * i, f32x4{eGe[4 * i], eGe[4 * i + 1], eGe[4 * i + 2], eGe[4 * i + 3]});
         }
         // Per-channel decay: a block whose decay exceeds kDiagRange on some
         // channel ("slow"; the flag is uniform over the wave that holds it)
@@ -704,6 +726,10 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
             slow = __ballot(big) != 0;
             if (l == 0) sSlow[w] = slow ? 1 : 0;
         }
+        // The tiles: mode 0 a mild chunk (chunk-referenced factors), 1 the
+        // block-referenced factors, 2 a slow block (raw q, k and e).
+        const auto write_tiles = [&](auto mode_c) {
+            constexpr int MODE = decltype(mode_c)::value;
 #pragma unroll
         for (int j = 0; j < TPT; ++j) {
             const int t = TPT * grp + j;
@@ -738,16 +764,26 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
                     // exp(kDiagRange) outside slow blocks; E~ = E^ . exp(R) and
                     // Kend = K^ . exp(G_end - R_{b+1}) (a slow block's Kend
                     // is written once its K^ is).
-                    const float egt = fast_exp(G[j][ch]);
-                    const float ig = slow ? 1.f : __builtin_amdgcn_rcpf(egt);
-                    const float eg = slow ? 1.f : egt, ek = ig * eB[ch];
-                    const float ev = eb[ch] * kv;
-                    oq[ch] = qv * eg;
-                    ok[ch] = slow ? kv : kv * ek;
-                    oe[ch] = ev * eg;
-                    okd[ch] = kv * ig;
-                    oet[ch] = ev * egt * eR[ch];
-                    oke[ch] = kv * ek * eG1[ch];
+                    const float egt = fast_exp(G[j][ch]), ev = eb[ch] * kv;
+                    if constexpr (MODE == 0) {
+                        const float eg = egt * eR[ch], emg = __builtin_amdgcn_rcpf(eg);
+                        oq[ch] = qv * eg;
+                        ok[ch] = okd[ch] = kv * emg;
+                        oe[ch] = oet[ch] = ev * eg;
+                        oke[ch] = ok[ch] * eGe[ch];
+                    } else if constexpr (MODE == 2) {
+                        oq[ch] = qv;
+                        ok[ch] = okd[ch] = oke[ch] = kv;
+                        oe[ch] = ev;
+                        oet[ch] = ev * egt * eR[ch];
+                    } else {
+                        okd[ch] = kv * __builtin_amdgcn_rcpf(egt);
+                        ok[ch] = okd[ch] * eB[ch];
+                        oke[ch] = ok[ch] * eG1[ch];
+                        oq[ch] = qv * egt;
+                        oe[ch] = ev * egt;
+                        oet[ch] = oe[ch] * eR[ch];
+                    }
                 } else {
                     oq[ch] = qv;
                     ok[ch] = kv;
@@ -760,10 +796,20 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
             *reinterpret_cast<uint4 *>(tZ + o) = R::pack(oz);
             if constexpr (HAS_E) *reinterpret_cast<uint4 *>(tE + o) = R::pack(oe);
             if constexpr (DT) {
-                *reinterpret_cast<uint4 *>(tKd + o) = R::pack(okd);
-                *reinterpret_cast<uint4 *>(tEt + o) = R::pack(oet);
+                if constexpr (MODE != 0) {
+                    *reinterpret_cast<uint4 *>(tKd + o) = R::pack(okd);
+                    *reinterpret_cast<uint4 *>(tEt + o) = R::pack(oet);
+                }
                 *reinterpret_cast<uint4 *>(tKe + o) = R::pack(oke);
             }
+        }
+        };
+        if constexpr (CHAN) {
+            if (mild) write_tiles(std::integral_constant<int, 0>{});
+            else if (slow) write_tiles(std::integral_constant<int, 2>{});
+            else write_tiles(std::integral_constant<int, 1>{});
+        } else {
+            write_tiles(std::integral_constant<int, 0>{});
         }
         if constexpr (CHAN) {
             if (slow) {
@@ -835,7 +881,9 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
         __syncthreads();
 
         // ---- B. Gram products: 20 lower 16 x 16 tiles, 10 of T and 10 of A ----
-        {
+        // (Instantiated apart for mild chunks, which need no factor table.)
+        const auto gram = [&](auto mild_c) {
+            constexpr bool MILD = decltype(mild_c)::value;
             const IO *TL = HAS_E ? tE : tK;  // left factor of T (raw k times beta for tied gates)
             constexpr int KD = D / KS;
             f32x4 x[5];
@@ -844,14 +892,15 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
                 const int p = w + NW * s, kind = p / 10;
                 int ti, tj;
                 lower_tile(p - kind * 10, ti, tj);
-                const IO *X = (kind == 0 ? TL : tQ) + ti * 16 * PD, *Y = (DT && ti == tj ? tKd : tK) + tj * 16 * PD;
+                const IO *X = (kind == 0 ? TL : tQ) + ti * 16 * PD;
+                const IO *Y = (DT && !MILD && ti == tj ? tKd : tK) + tj * 16 * PD;
                 Frag fa[KD], fb[KD];
 #pragma unroll
                 for (int ks = 0; ks < KD; ++ks) {
                     fa[ks] = M::load(X + ks * KS, PD);
                     fb[ks] = M::load(Y + ks * KS, PD);
                 }
-                if constexpr (CHAN)  // the tile's per-channel factor (the diagonal's is in tKd with bfloat16 io)
+                if constexpr (CHAN && !MILD)  // the tile's per-channel factor (the diagonal's is in tKd with bfloat16 io)
                     if (ti - tj >= 2 || (!DT && ti == tj)) {
                         const float *f = sDec + (ti == tj ? 7 + ti : dec_row_far(ti, tj)) * D + FE * lg;
 #pragma unroll
@@ -884,7 +933,7 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
                     y[r] = keep ? y[r] : 0.f;
                 }
                 // (Diagonal tiles of a block formed entry by entry in phase A are kept.)
-                if (CHAN && ti == tj && sSlow[ti]) {
+                if (CHAN && !MILD && ti == tj && sSlow[ti]) {
                 } else if (kind == 0 && ti == tj) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) sTd[(ti * 16 + lr) * 17 + 4 * lg + r] = y[r];
@@ -902,7 +951,7 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
                 for (int f = w; f < (C / 16) * (D / KS); f += NW) {
                     const int rt = f / (D / KS), ks = f - rt * (D / KS);
                     Frag x = M::load(tQ + rt * 16 * PD + ks * KS, PD);
-                    if constexpr (CHAN) x = K::scale(x, sDec + rt * D + ks * KS + FE * lg);
+                    if constexpr (CHAN && !MILD) x = K::scale(x, sDec + rt * D + ks * KS + FE * lg);
                     store_frag<IO>(CHAN ? wQ : wQh, rt, ks, D, x);
                 }
             // Kend^T (or raw k^T) fragments: rows = channels, K = tokens, read K-major from the tiles.
@@ -911,10 +960,12 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
                     const int rt = f / (C / KS), ks = f - rt * (C / KS);
                     Frag x = K::frag((DT ? tKe : tK) + ks * KS * PD + rt * 16, PD);
                     if constexpr (CHAN && !DT)  // Kend = K^ . exp(G_end - R_{b+1}), b = the fragment's token block
-                        x = K::scale(x, sDec[(11 + ((ks * KS + FE * lg) >> 4)) * D + rt * 16 + lr]);
+                        x = K::scale(x, sDec[(MILD ? 15 : 11 + ((ks * KS + FE * lg) >> 4)) * D + rt * 16 + lr]);
                     store_frag<IO>(wKT, rt, ks, C, x);
                 }
-        }
+        };
+        if (!CHAN || mild) gram(std::true_type{});
+        else if constexpr (CHAN) gram(std::false_type{});
         __syncthreads();
 
         if (has_next) in.template load<1>(a, un, co, grp);
@@ -981,7 +1032,7 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
             for (int ct = 0; ct < NCTS; ++ct) {
                 const int c0 = WC * w + 16 * ct;
                 const bool zside = c0 >= D;
-                const IO *src = zside ? tZ + (c0 - D) : (DT ? tEt : HAS_E ? tE : tK) + c0;
+                const IO *src = zside ? tZ + (c0 - D) : (DT && !mild ? tEt : HAS_E ? tE : tK) + c0;
                 Frag bf[NKS];
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) {
@@ -989,8 +1040,9 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
                     if (!zside) {
                         if constexpr (!CHAN)
                             bf[ks] = K::scale(bf[ks], sSE + ks * KS + FE * lg);
-                        else if constexpr (!DT)  // E~ = E^ . exp(R_b), b = the fragment's token block
-                            bf[ks] = K::scale(bf[ks], sDec[((ks * KS + FE * lg) >> 4) * D + c0 + lr]);
+                        else if constexpr (!DT) {  // E~ = E^ . exp(R_b), b = the fragment's token block
+                            if (!mild) bf[ks] = K::scale(bf[ks], sDec[((ks * KS + FE * lg) >> 4) * D + c0 + lr]);
+                        }
                     }
                 }
 #pragma unroll
