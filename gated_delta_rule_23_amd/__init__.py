@@ -26,13 +26,14 @@ GDR_OK, GDR_E_INVAL, GDR_E_UNSUPPORTED, GDR_E_HIP, GDR_E_NOMEM = 0, -1, -2, -3, 
 GDR_F32, GDR_BF16 = 0, 1
 GDR_DECAY_NONE, GDR_DECAY_SCALAR, GDR_DECAY_CHANNEL = 0, 1, 2
 CHUNK = 64
+GDR_NOALLOC_SCRATCH_BYTES = 64 << 20  # the workspace array of gdr_chunk_fwd_noalloc
 
 # Every symbol include/gdr.h declares.
 EXPORTS = ("gdr_state_bytes", "gdr_state_alloc", "gdr_state_free", "gdr_chunk_workspace_bytes",
            "gdr_chunk_fwd_in_workspace_bytes",
            "gdr_chunk_fwd", "gdr_decode_step", "gdr_recurrent_fwd", "gdr_recurrent_fwd_in", "gdr_chunk_fwd_in",
            "gdr_recurrent_bwd_workspace_bytes", "gdr_recurrent_bwd", "gdr_chunk_bwd_workspace_bytes", "gdr_chunk_bwd",
-           "gdr_last_error", "gdr_version")
+           "gdr_chunk_fwd_noalloc", "gdr_last_error", "gdr_version")
 
 
 class GdrError(RuntimeError):
@@ -78,6 +79,8 @@ def _load():
     lib.gdr_chunk_fwd_in_workspace_bytes.argtypes = [D, ctypes.POINTER(S)]
     lib.gdr_chunk_fwd.restype = I
     lib.gdr_chunk_fwd.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, S, P]
+    lib.gdr_chunk_fwd_noalloc.restype = I
+    lib.gdr_chunk_fwd_noalloc.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P]
     lib.gdr_decode_step.restype = I
     lib.gdr_decode_step.argtypes = [D, P, P, P, P, P, P, P, P, P, P]
     lib.gdr_recurrent_fwd.restype = I
@@ -227,6 +230,32 @@ def gdr_chunk_fwd(q, k, v, *, g=None, beta=None, b=None, w=None, S0=None, scale=
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.gdr_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(b),
                              _ptr(w), _ptr(S0), _ptr(o), _ptr(ST), _ptr(workspace), wsz, _stream(stream)))
+    return o, ST
+
+
+def gdr_chunk_fwd_noalloc(q, k, v, *, o, ST, g=None, beta=None, b=None, w=None, S0=None, scale=1.0, chunk=CHUNK,
+                          stream=None):
+    """gdr_chunk_fwd with the library's own device workspace: allocates
+    nothing, so the outputs o [B,T,Hv,D] and ST [B,Hv,D,D] are the caller's.
+    The call's workspace must fit GDR_NOALLOC_SCRATCH_BYTES; calls that
+    overlap in time on one GPU share that workspace and race."""
+    torch = _torch()
+    B, T, Hqk, D = q.shape
+    Hv = v.shape[2]
+    dev, io_t = q.device, q.dtype
+    for name, t, shape in (("q", q, (B, T, Hqk, D)), ("k", k, (B, T, Hqk, D)), ("v", v, (B, T, Hv, D)),
+                           ("b", b, (B, T, Hv, D)), ("w", w, (B, T, Hv, D))):
+        _require(t, name, shape, io_t, dev)
+    _require(beta, "beta", (B, T, Hv), torch.float32, dev)
+    _require(g, "g", None, torch.float32, dev)
+    _require(S0, "S0", (B, Hv, D, D), torch.float32, dev)
+    if o is None or ST is None:
+        raise ValueError("gdr_chunk_fwd_noalloc: o and ST are the caller's")
+    _require(o, "o", (B, T, Hv, D), io_t, dev)
+    _require(ST, "ST", (B, Hv, D, D), torch.float32, dev)
+    desc = make_desc(B, T, Hqk, Hv, D, _io_dtype(q), _decay_of(g, (B, T), Hv, D), scale, chunk)
+    _check(lib.gdr_chunk_fwd_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(b),
+                                     _ptr(w), _ptr(S0), _ptr(o), _ptr(ST), _stream(stream)))
     return o, ST
 
 

@@ -10,10 +10,17 @@
 #include <cstdint>
 #include <cstdio>
 #include <initializer_list>
+#include <mutex>
 #include <string>
 
 #include "gdr.h"
 #include "kernels.hpp"
+
+// The workspace of gdr_chunk_fwd_noalloc: one array per GPU, allocated when
+// the library's code is loaded on that GPU and held until the process ends.
+// Host code never passes its name to a kernel or a copy (on the host it only
+// names the symbol); it uses the device address hipGetSymbolAddress returns.
+static __device__ __align__(256) unsigned char scratch[GDR_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -36,6 +43,29 @@ int ok() {
 
 int hip_fail(hipError_t e, const char *what) {
     return fail(GDR_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_of_current_device(void **ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(GDR_E_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(GDR_E_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return GDR_OK;
 }
 
 bool supported_dim(int d) { return d == 32 || d == 64 || d == 128; }
@@ -161,9 +191,11 @@ int check_chunk_overlaps(const gdr_desc *d, const void *q, const void *k, const 
     return GDR_OK;
 }
 
+// lib_scratch: the workspace is the library's own `scratch` array (the
+// workspace arguments are ignored).
 int chunk_call(const gdr_desc *d, const gdr_input_stage *stage, const void *q, const void *k, const void *v,
                       const float *g, const float *beta, const void *b, const void *w, const float *S0, void *o,
-                      float *ST, void *workspace, size_t workspace_bytes, void *stream) {
+                      float *ST, void *workspace, size_t workspace_bytes, void *stream, bool lib_scratch = false) {
     int rc = validate(d, CALL_CHUNK, q, k, v, g, beta, b, w, o);
     if (rc != GDR_OK) return rc;
     if (!ST) return fail(GDR_E_INVAL, "ST must be non-NULL");
@@ -180,13 +212,23 @@ int chunk_call(const gdr_desc *d, const gdr_input_stage *stage, const void *q, c
     const bool split_stage = stage && chan;
     const gdr::StageWsLayout SL = gdr::stage_ws_layout(d->B, d->T, d->H_qk, d->H_v, d->d_k, io, beta == nullptr);
     const size_t need = L.total() + (split_stage ? SL.total() : 0);
-    if (need > 0 && (!workspace || workspace_bytes < need))
+    if (lib_scratch) {
+        workspace = nullptr;
+        if (need > GDR_NOALLOC_SCRATCH_BYTES)
+            return fail(GDR_E_UNSUPPORTED, "workspace of %zu bytes needed; the library's scratch holds %zu",
+                        need, (size_t)GDR_NOALLOC_SCRATCH_BYTES);
+    } else if (need > 0 && (!workspace || workspace_bytes < need)) {
         return fail(GDR_E_INVAL, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+    }
     rc = check_chunk_overlaps(d, q, k, v, g, beta, b, w, S0, o, ST, workspace, need);
     if (rc != GDR_OK) return rc;
     if (d->B == 0) return ok();
     const size_t units = (size_t)d->B * d->H_v * NC;
     if (units > 0x7fffffffull) return fail(GDR_E_UNSUPPORTED, "too many chunks for one launch");
+    if (lib_scratch) {
+        rc = scratch_of_current_device(&workspace);
+        if (rc != GDR_OK) return rc;
+    }
 
     gdr::ChunkArgs a{};
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.bg = b; a.wg = w;
@@ -477,6 +519,12 @@ int gdr_chunk_fwd(const gdr_desc *d, const void *q, const void *k, const void *v
                   const void *b, const void *w, const float *S0, void *o, float *ST, void *workspace,
                   size_t workspace_bytes, void *stream) {
     return chunk_call(d, nullptr, q, k, v, g, beta, b, w, S0, o, ST, workspace, workspace_bytes, stream);
+}
+
+int gdr_chunk_fwd_noalloc(const gdr_desc *d, const void *q, const void *k, const void *v, const float *g,
+                          const float *beta, const void *b, const void *w, const float *S0, void *o, float *ST,
+                          void *stream) {
+    return chunk_call(d, nullptr, q, k, v, g, beta, b, w, S0, o, ST, nullptr, 0, stream, true);
 }
 
 int gdr_chunk_fwd_in(const gdr_desc *d, const gdr_input_stage *stage, const void *q, const void *k, const void *v,

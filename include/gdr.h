@@ -142,6 +142,29 @@ int gdr_chunk_fwd(const gdr_desc *desc, const void *q, const void *k, const void
                   const float *S0, void *o, float *ST, void *workspace, size_t workspace_bytes,
                   void *stream);
 
+/* gdr_chunk_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, and harnesses that forbid
+ * hipMalloc. Same arguments, layouts, rules and results as gdr_chunk_fwd,
+ * without the workspace arguments: the workspace is the library's own
+ * device array of GDR_NOALLOC_SCRATCH_BYTES (64 MiB), one per GPU, reserved
+ * when the library's code is loaded on that GPU and held until the process
+ * ends. The call allocates nothing; its first call on a device looks the
+ * array's address up (hipGetSymbolAddress), with that device current.
+ *   Limit: gdr_chunk_workspace_bytes(desc) <= GDR_NOALLOC_SCRATCH_BYTES,
+ *   else GDR_E_UNSUPPORTED before anything is enqueued (a 64 MiB array
+ *   holds, for example, the workspace of a 1024-token call with 48 V heads
+ *   of d = 128 in bfloat16).
+ *   Every call on one GPU shares that GPU's array, which keeps the last
+ *   call's contents (the call needs none of them: every workspace element
+ *   it reads it first writes). Calls that overlap in time on one GPU (on
+ *   different streams, or from different host threads without ordering)
+ *   race on the array and give wrong results; order them on one stream.
+ *   The stream must belong to the current device. */
+#define GDR_NOALLOC_SCRATCH_BYTES (64u << 20)
+int gdr_chunk_fwd_noalloc(const gdr_desc *desc, const void *q, const void *k, const void *v,
+                          const float *g, const float *beta, const void *b, const void *w,
+                          const float *S0, void *o, float *ST, void *stream);
+
 /* One recurrent decode step for B sequences, one token each ("Kernel Triton
  * recorrente fundido para decode", family analysis page): reads and writes
  * every state S[b, h] in place exactly once. q, k: [B, H_qk, d_k];
