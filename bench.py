@@ -1,34 +1,31 @@
 """Benchmark of the gated delta-rule hot path on one MI355X.
 
-One step = one chunked prefill of the Qwen3.8-27B-shaped Gated DeltaNet layer
-(B=1, T=4096, 16 QK heads, 48 V heads, d=128, bf16 io, fp32 state, chunk 64)
-through gdr_chunk_fwd. In the same run the decode step is measured on its own
-workload (64 sequences x 48 V heads, 128 x 128 fp32 states, 256 consecutive
-gdr_decode_step calls). Inputs are seeded synthetic tensors already resident
-in device memory when timing starts, after the warmup steps and a further
---warmup-s seconds of untimed calls (the GPU's clocks take that long to
-settle). The timed calls are captured once as a
-HIP graph (the way a serving loop launches them, without per-launch host
-overhead) and timed over one replay with HIP events on the stream the graph
-runs on; the JSON also gives the eager per-call time (events around each
-call) for reference.
-
---workload picks another prefill workload for the timed step (the KDA and
-Gated DeltaNet-2 layers, or the small fp32 case); --decode-steps 0 skips the
-decode measurement. "input_stage" times the same prefill from raw
-projections through gdr_chunk_fwd_in (convolution, normalisation and gate
-activations fused into the load stage; --input-stage 0 skips it). Decode is
-also timed with the states of four layers
-advanced in turn, and the multi-token recurrent forward (gdr_recurrent_fwd,
---recurrent-T tokens per sequence at the decode shape, four layers' states in
-turn) gets its own object; --recurrent-T 0 skips it.
-
-Prints one JSON line: value = prefill tokens/s; "roofline" for the prefill
-call against HBM; "decode" with state GB/s and its own roofline; "copy", the
-bandwidth of a plain 1 GiB device copy timed in the same run, against which
-every HBM roofline also gives "frac_of_copy"; and "cpu_baseline", the fp64
-CPU oracle timed on a bounded sample of the same prefill workload on this
-host's cores.
+One step = one chunked prefill (gdr_chunk_fwd) of the Gated DeltaNet-2 long
+prefill: B=1, T=65536, 16 heads, d_k = d_v = 128, bf16 io, fp32 state,
+chunk 64, per-channel decay, decoupled erase and write gates. That is the
+largest configuration that fits one GPU, and the headline "value" is its
+tokens/s. In the same run, each as a sub-object of the one JSON line:
+  - "prefill_configs": the same call timed on the Qwen3.8-27B-shaped Gated
+    DeltaNet layer (B=1, T=4096, 16 QK / 48 V heads, scalar decay) and the
+    KDA layer (B=2, T=16384, 32 heads, per-channel decay);
+  - "decode": 256 consecutive gdr_decode_step calls for 64 sequences x 48 V
+    heads with 128 x 128 fp32 states (also with four layers' states in turn);
+  - "input_stage": the headline prefill from raw projections
+    (gdr_chunk_fwd_in: convolution, normalisation, gate activations);
+  - "backward": gdr_chunk_bwd and gdr_recurrent_bwd on the headline layer;
+  - "recurrent": gdr_recurrent_fwd, a few tokens per sequence at the decode
+    shape;
+  - "copy": a plain 1 GiB device copy, against which every HBM roofline also
+    gives "frac_of_copy";
+  - "cpu_baseline": the fp64 CPU oracle on the headline layer (all heads, all
+    tokens) on this host's cores.
+Inputs are seeded synthetic tensors already resident in device memory when
+timing starts, after the warmup steps and a further --warmup-s seconds of
+untimed calls (the GPU's clocks take that long to settle). The timed calls
+are captured once as a HIP graph (the way a serving loop launches them,
+without per-launch host overhead) and timed over one replay with HIP events
+on the stream the graph runs on; the JSON also gives the eager per-call time
+(events around each call) for reference.
 """
 from __future__ import annotations
 
@@ -49,35 +46,47 @@ CSRC = os.path.join(ROOT, "gated_delta_rule_23_amd", "csrc")
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def kernel_source_hash():
-    """sha256 over the kernel sources with comments and blank space removed, to
-    tell whether recorded memory counters still describe the kernels as built."""
+# The sources each measured call's kernels are built from (device code, the
+# shared device helpers, and the argument and workspace layouts).
+SOURCES = {
+    "prefill": ("chunk.hip", "common.hpp", "kernels.hpp"),
+    "input_stage": ("chunk.hip", "stage.hip", "common.hpp", "kernels.hpp"),
+    "decode": ("decode.hip", "common.hpp", "kernels.hpp"),
+    "recurrent": ("recurrent.hip", "common.hpp", "kernels.hpp"),
+    "backward_chunked": ("chunk_bwd.hip", "common.hpp", "kernels.hpp"),
+}
+
+
+def kernel_source_hash(names):
+    """sha256 over the named kernel sources with comments and blank space
+    removed, to tell whether recorded memory counters still describe the
+    kernels as built."""
     import hashlib
     import re
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".hpp")):
-            with open(os.path.join(CSRC, name)) as f:
-                src = f.read()
-            src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
-            src = re.sub(r"//[^\n]*", " ", src)
-            src = " ".join(src.split())
-            h.update(name.encode() + b"\0" + src.encode())
+    for name in sorted(names):
+        with open(os.path.join(CSRC, name)) as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        src = " ".join(src.split())
+        h.update(name.encode() + b"\0" + src.encode())
     return h.hexdigest()
 
 
-def recorded_traffic(key):
-    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
+def recorded_traffic(key, kind):
+    """HBM bytes per call measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
     (scaled by a plain copy of known size) for the kernels as they were when
-    the counters were taken; None once the kernel sources differ."""
+    the counters were taken; None once the sources of that call's kernels
+    differ."""
     try:
         with open(TRAFFIC_RECORD) as f:
-            rec = json.load(f)
+            rec = json.load(f).get("records", {}).get(key)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256") != kernel_source_hash():
+    if not rec or rec.get("sources_sha256") != kernel_source_hash(SOURCES[kind]):
         return None
-    return rec.get("bytes_per_launch", {}).get(key)
+    return rec.get("bytes_per_call")
 
 
 def prefill_algorithmic(wl):
@@ -159,6 +168,10 @@ def cpu_baseline(wl, inp, heads, min_seconds=10.0, max_reps=200):
                       f"{reps} runs, {dt:.2f} s per run (tokens/s scaled to the whole layer)"}
 
 
+PREFILLS = {"gdn2_prefill": "GDN2_PREFILL", "kda_prefill": "KDA_PREFILL", "qwen_gdn_prefill": "QWEN_GDN_PREFILL",
+            "gdn_small_f32": "GDN_SMALL_F32"}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -174,10 +187,13 @@ def main(argv=None):
                     help="tokens per sequence of the multi-token recurrent call timed at the decode shape (0 = skip)")
     ap.add_argument("--backward", type=int, default=1,
                     help="also time gdr_chunk_bwd and gdr_recurrent_bwd on the prefill workload (0 = skip)")
-    ap.add_argument("--workload", default="qwen_gdn_prefill",
-                    choices=["qwen_gdn_prefill", "kda_prefill", "gdn2_prefill", "gdn_small_f32"],
-                    help="prefill workload of the timed step (default: the Qwen-shaped GDN layer, T=4096)")
-    ap.add_argument("--cpu-heads", type=int, default=48, help="V heads in the CPU-oracle sample (0 = skip)")
+    ap.add_argument("--workload", default="gdn2_prefill", choices=sorted(PREFILLS),
+                    help="prefill workload of the timed step (default: the Gated DeltaNet-2 layer, T=65536)")
+    ap.add_argument("--sub-prefills", default="qwen_gdn_prefill,kda_prefill",
+                    help="comma-separated prefill workloads also timed, each as a sub-object ('' = none)")
+    ap.add_argument("--cpu-heads", type=int, default=16, help="V heads in the CPU-oracle sample (0 = skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="repeat the CPU-oracle run until this much time has passed (one run at least)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copy-mib", type=int, default=1024,
                     help="size of each buffer of the plain device-to-device copy timed in the same run, the "
@@ -196,6 +212,11 @@ def main(argv=None):
     import gdr_synth as gs
 
     dev = torch.device("cuda:0")
+    t_run = time.perf_counter()
+
+    def progress(msg):
+        """One line on stderr per finished section (the JSON line goes to stdout)."""
+        print(f"bench: {msg} ({time.perf_counter() - t_run:.0f} s)", file=sys.stderr, flush=True)
 
     def up(a):
         if a is None:
@@ -238,67 +259,97 @@ def main(argv=None):
                 "kind": "torch device-to-device copy of %d MiB (bytes read + written)" % args.copy_mib}
         del src, dst
 
-    # ---- prefill ----
-    wl = {"qwen_gdn_prefill": gs.QWEN_GDN_PREFILL, "kda_prefill": gs.KDA_PREFILL, "gdn2_prefill": gs.GDN2_PREFILL,
-          "gdn_small_f32": gs.GDN_SMALL_F32}[args.workload]
-    inp = gs.make_inputs(wl, seed=args.seed)
-    d = {n: up(inp[n]) for n in ("q", "k", "v", "g", "beta", "b", "w")}
-    io_t = torch.bfloat16 if wl.io == "bf16" else torch.float32
-    desc = gdr.make_desc(wl.B, wl.T, wl.Hqk, wl.Hv, wl.dk, gdr.GDR_BF16 if wl.io == "bf16" else gdr.GDR_F32,
-                         {"none": gdr.GDR_DECAY_NONE, "scalar": gdr.GDR_DECAY_SCALAR,
-                          "channel": gdr.GDR_DECAY_CHANNEL}[wl.decay], wl.scale)
-    ws = torch.empty(gdr.gdr_chunk_workspace_bytes(desc), dtype=torch.uint8, device=dev)
-    o = torch.empty((wl.B, wl.T, wl.Hv, wl.dv), dtype=io_t, device=dev)
-    ST = torch.empty((wl.B, wl.Hv, wl.dk, wl.dv), dtype=torch.float32, device=dev)
-
     cur = torch.cuda.current_stream  # the stream a call is made on (inside a capture: the capture stream)
 
-    def prefill():
-        gdr.gdr_chunk_fwd(d["q"], d["k"], d["v"], g=d["g"], beta=d["beta"], b=d["b"], w=d["w"], S0=None,
-                          scale=wl.scale, o=o, ST=ST, workspace=ws, stream=cur())
+    def make_desc(w):
+        return gdr.make_desc(w.B, w.T, w.Hqk, w.Hv, w.dk, gdr.GDR_BF16 if w.io == "bf16" else gdr.GDR_F32,
+                             {"none": gdr.GDR_DECAY_NONE, "scalar": gdr.GDR_DECAY_SCALAR,
+                              "channel": gdr.GDR_DECAY_CHANNEL}[w.decay], w.scale)
 
-    for _ in range(args.warmup):
-        prefill()
-    torch.cuda.synchronize()
-    settle(prefill)
-    # Reference: HIP events around each of K eager calls.
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for i in range(args.steps):
-        ev[i][0].record(cur())
-        prefill()
-        ev[i][1].record(cur())
-    torch.cuda.synchronize()
-    eager_call_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
-    # Timed region: the K calls captured once as a HIP graph (as a serving loop
-    # launches them), replayed untimed for --warmup-s seconds (the GPU idles
-    # while the graph is captured, and its clocks drop), then timed over one
-    # replay.
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for _ in range(args.steps):
+    # ---- prefill: one gdr_chunk_fwd call per step ----
+    def time_prefill(w, inp):
+        """Eager per-call time (events around each call), then the timed
+        region: the K calls captured once as a HIP graph (as a serving loop
+        launches them), replayed untimed for --warmup-s seconds (the GPU
+        idles while the graph is captured, and its clocks drop), then timed
+        over one replay."""
+        d = {n: up(inp[n]) for n in ("q", "k", "v", "g", "beta", "b", "w")}
+        io_t = torch.bfloat16 if w.io == "bf16" else torch.float32
+        ws = torch.empty(gdr.gdr_chunk_workspace_bytes(make_desc(w)), dtype=torch.uint8, device=dev)
+        o = torch.empty((w.B, w.T, w.Hv, w.dv), dtype=io_t, device=dev)
+        ST = torch.empty((w.B, w.Hv, w.dk, w.dv), dtype=torch.float32, device=dev)
+
+        def prefill():
+            gdr.gdr_chunk_fwd(d["q"], d["k"], d["v"], g=d["g"], beta=d["beta"], b=d["b"], w=d["w"], S0=None,
+                              scale=w.scale, o=o, ST=ST, workspace=ws, stream=cur())
+
+        for _ in range(args.warmup):
             prefill()
-    settle(graph.replay)
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(cur())
-    graph.replay()
-    t_end.record(cur())
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
+        torch.cuda.synchronize()
+        settle(prefill)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for i in range(args.steps):
+            ev[i][0].record(cur())
+            prefill()
+            ev[i][1].record(cur())
+        torch.cuda.synchronize()
+        eager_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(args.steps):
+                prefill()
+        settle(graph.replay)
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(cur())
+        graph.replay()
+        t1.record(cur())
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / args.steps
+        del graph, ws, o, ST
+        pbytes, pflops = prefill_algorithmic(w)
+        achieved = pbytes / (ms * 1e-3) / 1e9
+        kernels = "chunk_prep, [chunk_seg_state, chunk_seg_combine when the sweep is split], chunk_sweep"
+        res = {"workload": w.name, "steps": args.steps, "launch": "hip_graph", "ms_per_call": ms,
+               "eager_call_ms": eager_ms, "tokens_per_s": w.B * w.T / (ms * 1e-3),
+               "roofline": {"kernel": f"gdr_chunk_fwd ({kernels})", "bound": "hbm", "achieved": achieved,
+                            "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                            "traffic": recorded_traffic(w.name, "prefill"), "algorithmic_bytes": pbytes},
+               "mfma": {"algorithmic_tflops": pflops / (ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
+                        "frac": pflops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, "algorithmic_flops": pflops}}
+        return res, d
+
+    wl = getattr(gs, PREFILLS[args.workload])
+    desc = make_desc(wl)
+    inp = gs.make_inputs(wl, seed=args.seed)
+    progress(f"inputs of {wl.name} drawn")
+    head, d = time_prefill(wl, inp)
+    progress(f"prefill {wl.name}: {head['ms_per_call']:.4f} ms per call")
+    ms_per_step = head["ms_per_call"]
     avg_call_ms = ms_per_step
-    del graph
     tokens = wl.B * wl.T
     pbytes, pflops = prefill_algorithmic(wl)
-    achieved = pbytes / (avg_call_ms * 1e-3) / 1e9
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
-    # ---- the same layer from raw projections: input stage fused into the prefill ----
+    # ---- the other prefill configurations, each as a sub-object ----
+    sub = {}
+    for name in [x for x in args.sub_prefills.split(",") if x and x != args.workload]:
+        w2 = getattr(gs, PREFILLS[name])
+        res, d2 = time_prefill(w2, gs.make_inputs(w2, seed=args.seed))
+        sub[w2.name] = res
+        del d2
+        progress(f"prefill {w2.name}: {res['ms_per_call']:.4f} ms per call")
+
+    # ---- the same layer from raw projections: the input stage in front of the prefill ----
     stage = None
     if args.input_stage:
         raw = gs.make_raw_inputs(wl, seed=args.seed + 3)
         rd = {n: up(raw[n]) for n in ("q", "k", "v", "g", "beta", "b", "w", "conv_w", "conv_in", "decay_scale")}
         conv_out = torch.empty_like(rd["conv_in"])
         ws_in = torch.empty(gdr.gdr_chunk_fwd_in_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+        o = torch.empty((wl.B, wl.T, wl.Hv, wl.dv), dtype=torch.bfloat16 if wl.io == "bf16" else torch.float32,
+                        device=dev)
+        ST = torch.empty((wl.B, wl.Hv, wl.dk, wl.dv), dtype=torch.float32, device=dev)
 
         def prefill_in():
             gdr.gdr_chunk_fwd_in(rd["q"], rd["k"], rd["v"], rd["conv_w"], conv_in=rd["conv_in"], conv_out=conv_out,
@@ -322,22 +373,25 @@ def main(argv=None):
         s_ms = t_start.elapsed_time(t_end) / args.steps
         s_bytes = pbytes + raw["conv_w"].nbytes + 2 * raw["conv_in"].nbytes + (raw["decay_scale"].nbytes
                                                                                if raw["decay_scale"] is not None else 0)
+        fused = wl.decay != "channel"
         stage = {"entry": "gdr_chunk_fwd_in", "ms_per_call": s_ms, "tokens_per_s": tokens / (s_ms * 1e-3),
+                 "form": ("fused into the prefill's load stage" if fused else
+                          "a pass of its own (stage_conv + stage_gates) before the prefill"),
                  "extra_ms_vs_gdr_chunk_fwd": s_ms - avg_call_ms,
-                 "unfused_round_trip_bytes": 2 * (d["q"].nbytes + d["k"].nbytes + d["v"].nbytes),
+                 "unfused_round_trip_bytes": 2 * (d["q"].nbytes + d["k"].nbytes + d["v"].nbytes) if fused else None,
                  "roofline": {"bound": "hbm", "achieved": s_bytes / (s_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
                               "unit": "GB/s", "frac": s_bytes / (s_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                              "traffic": recorded_traffic(wl.name + "_input_stage"), "algorithmic_bytes": s_bytes}}
-        del raw, rd, conv_out, ws_in
+                              "traffic": recorded_traffic(wl.name + "_input_stage", "input_stage"),
+                              "algorithmic_bytes": s_bytes}}
+        del raw, rd, conv_out, ws_in, o, ST
+        progress(f"input stage: {s_ms:.4f} ms per call")
 
     # ---- backward (gradients of the recurrence) on the prefill workload ----
     bwd = None
     if args.backward:
         grads = gs.make_output_grads(wl, seed=args.seed + 3)
         do_d, dST_d = up(grads["do"]), up(grads["dST"])
-        bdesc = gdr.make_desc(wl.B, wl.T, wl.Hqk, wl.Hv, wl.dk, gdr.GDR_BF16 if wl.io == "bf16" else gdr.GDR_F32,
-                              {"none": gdr.GDR_DECAY_NONE, "scalar": gdr.GDR_DECAY_SCALAR,
-                               "channel": gdr.GDR_DECAY_CHANNEL}[wl.decay], wl.scale)
+        bdesc = desc
 
         def time_backward(fn, ws):
             def call():
@@ -377,7 +431,7 @@ def main(argv=None):
                             "algorithmic_flops": c_flops},
                "hbm": {"achieved": b_bytes / (b_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                        "frac": b_bytes / (b_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, "algorithmic_bytes": b_bytes,
-                       "traffic": recorded_traffic(wl.name + "_backward_chunked")},
+                       "traffic": recorded_traffic(wl.name + "_backward_chunked", "backward_chunked")},
                "recurrent": {"entry": "gdr_recurrent_bwd", "ms_per_call": r_ms,
                              "tokens_per_s": wl.B * wl.T / (r_ms * 1e-3),
                              "roofline": {"kernel": "bwd_ckpt_kernel + bwd_kernel + bwd_reduce_kernel",
@@ -386,6 +440,7 @@ def main(argv=None):
                                           "frac": r_flops / (r_ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
                                           "algorithmic_flops": r_flops}}}
         del do_d, dST_d
+        progress(f"backward: chunked {b_ms:.3f} ms, recurrent {r_ms:.3f} ms per call")
 
     # ---- decode ----
     dec = None
@@ -434,6 +489,7 @@ def main(argv=None):
         torch.cuda.synchronize()
         del dgraph
         d_step_ms = d0.elapsed_time(d1) / dwl.T
+        progress(f"decode: {d_step_ms * 1e3:.1f} us per step")
         # The same steps over the states of LAYERS layers in turn (step s
         # advances layer s % LAYERS), as in a model where every other layer's
         # state passes through the memory-side cache between two steps of one
@@ -469,7 +525,7 @@ def main(argv=None):
                                   "hbm_frac": d_bytes / (d_cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS},
                "roofline": {"kernel": "decode_kernel", "bound": "hbm", "achieved": d_achieved,
                             "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": d_achieved / HBM_PEAK_GBPS,
-                            "traffic": recorded_traffic(dwl.name) if dwl.T == 256 else None,
+                            "traffic": recorded_traffic(dwl.name, "decode") if dwl.T == 256 else None,
                             "algorithmic_bytes": d_bytes}}
 
     # ---- multi-token recurrent forward (a few tokens per sequence from a live state) ----
@@ -507,6 +563,7 @@ def main(argv=None):
         torch.cuda.synchronize()
         del rgraph, r_states
         r_ms = r0.elapsed_time(r1) / n_calls
+        progress(f"recurrent: {r_ms * 1e3:.1f} us per call")
         r_state, _ = decode_algorithmic(rwl)
         r_bytes = recurrent_algorithmic(rwl)
         rec = {"workload": rwl.name, "calls": n_calls, "layers_in_turn": DECODE_COLD_LAYERS, "launch": "hip_graph",
@@ -515,7 +572,7 @@ def main(argv=None):
                "roofline": {"kernel": "recurrent_kernel", "bound": "hbm",
                             "achieved": r_bytes / (r_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                             "frac": r_bytes / (r_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                            "traffic": recorded_traffic(rwl.name), "algorithmic_bytes": r_bytes}}
+                            "traffic": recorded_traffic(rwl.name, "recurrent"), "algorithmic_bytes": r_bytes}}
 
     out = {
         "metric": "prefill tokens/s and decode state GB/s for gated delta rule, % of roofline",
@@ -526,6 +583,7 @@ def main(argv=None):
         "warmup": args.warmup,
         "warmup_s": args.warmup_s,
         "ms_per_step": ms_per_step,
+        "eager_ms_per_step": head["eager_call_ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -533,13 +591,10 @@ def main(argv=None):
         "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), gates and decay per the workload recipe)",
         "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "H_qk": wl.Hqk, "H_v": wl.Hv, "d_k": wl.dk,
                    "d_v": wl.dv, "chunk": wl.chunk, "io": wl.io, "decay": wl.decay, "gates": wl.gates,
-                   "state": "fp32", "S0": "zeros", "launch": "hip_graph"},
-        "roofline": {"kernel": "gdr_chunk_fwd (chunk_prep + chunk_sweep)", "bound": "hbm",
-                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": recorded_traffic(wl.name), "algorithmic_bytes": pbytes, "avg_call_ms": avg_call_ms,
-                     "eager_call_ms": eager_call_ms},
-        "mfma": {"algorithmic_tflops": pflops / (avg_call_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
-                 "frac": pflops / (avg_call_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, "algorithmic_flops": pflops},
+                   "state": "fp32", "S0": "zeros", "entry": "gdr_chunk_fwd", "launch": "hip_graph"},
+        "roofline": dict(head["roofline"], avg_call_ms=avg_call_ms, eager_call_ms=head["eager_call_ms"]),
+        "mfma": head["mfma"],
+        "prefill_configs": sub,
         "input_stage": stage,
         "backward": bwd,
         "decode": dec,
@@ -547,13 +602,14 @@ def main(argv=None):
     }
     out["copy"] = copy
     if copy:  # the HBM rooflines also against the bandwidth a plain copy reaches on this GPU
-        for r in (out["roofline"], (stage or {}).get("roofline"), (dec or {}).get("roofline"),
-                  (rec or {}).get("roofline")):
+        for r in ([out["roofline"], (stage or {}).get("roofline"), (dec or {}).get("roofline"),
+                   (rec or {}).get("roofline")] + [x["roofline"] for x in sub.values()]):
             if r:
                 r["frac_of_copy"] = r["achieved"] / copy["GBps"]
     if args.cpu_heads > 0:
         heads = list(range(0, wl.Hv, max(1, wl.Hv // min(args.cpu_heads, wl.Hv))))[:args.cpu_heads]
-        out["cpu_baseline"] = cpu_baseline(wl, inp, heads)
+        out["cpu_baseline"] = cpu_baseline(wl, inp, heads, min_seconds=args.cpu_seconds)
+        progress("cpu baseline done")
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
