@@ -28,9 +28,22 @@
 // then through T and A to e, k, q and through the exponentials to G: a
 // factor exp(x) with x linear in G passes x' times its own value times its
 // gradient. dg_m is the sum of dG_t over t >= m in the chunk plus dG_end.
-// With a per-channel decay T and A are formed as E~ K~^T and Q~ K~^T with
-// K~ = k . exp(-G) (as in the forward); with a scalar decay the exponentials
-// are kept per entry, exp(G_t - G_j) <= 1, so strong decays stay finite.
+//
+// With a scalar decay the exponentials of T and A are kept per entry,
+// exp(G_t - G_j) <= 1. With a per-channel decay the products over channels
+// are referenced per 16-token block, as in the forward: with Gb the in-block
+// prefix of g, B_b the block's sum and R_b the sum of the blocks before it,
+//   E^ = e . exp(Gb),  Q^ = q . exp(Gb),  K^ = k . exp(B_b - Gb)  (<= |x|),
+// and for t in block bi, j in block bj < bi,
+//   exp(G_t - G_j) = exp(Gb_t) . exp(R_bi - R_{bj+1}) . exp(B_bj - Gb_j),
+// every factor <= 1; on a diagonal block the middle factor is exp(-B_bi),
+// at most exp(kBwdDiagRange), and a block that decays further on some
+// channel has its diagonal entries formed one by one, sum_c e_tc k_jc
+// exp(Gb_tc - Gb_jc). The same split serves the products through T and A in
+// the gradient pass, so no factor overflows or vanishes at any decay. The
+// chunk-referenced operands follow by factors <= 1: E~ = E^ . exp(R_b),
+// Q~ = Q^ . exp(R_b), Kend = K^ . exp(G_end - R_{b+1}). The workspace keeps
+// Gb (not G) per channel, from which every one of these is formed exactly.
 //
 // Shared-memory tiles keep 16-byte aligned rows (stride a multiple of 4
 // floats); global arrays are staged through registers with 16-byte (8-byte
@@ -61,6 +74,17 @@ constexpr int BV = 32;      // value columns per sweep workgroup
 constexpr int LB = BV + 4;  // row stride of 32-column tiles
 constexpr int LC = C + 4;   // row stride of 64-column tiles
 constexpr int LT = C + 16;  // row stride of 64-column tiles that the matrix cores read down their columns
+// Per-channel decay: a diagonal block whose decay exceeds kBwdDiagRange on
+// some channel is formed entry by entry (its factor exp(-B) is not used).
+constexpr float kBwdDiagRange = 40.f;
+// Rows of the per-channel factor table of cb_prep (each D floats):
+//   0-3 exp(R_b); 4-6 exp(B_1), exp(B_2), exp(B_1 + B_2) (tiles (2,0), (3,1),
+//   (3,0)); 7-10 exp(-B_b), capped at exp(kBwdDiagRange); 11-14
+//   exp(G_end - R_{b+1}). cb_grad_out keeps rows 4-10 only, as its rows 0-6.
+constexpr int kBwdDecRows = 15;
+__host__ __device__ constexpr int bwd_row_far(int bi, int bj) {  // row of tile (bi, bj), bi - bj >= 2
+    return bi == 2 ? 4 : bj == 1 ? 5 : 6;
+}
 
 constexpr int NS = 512;  // threads per sweep workgroup (two waves per SIMD)
 template <int D>
@@ -94,6 +118,11 @@ __device__ __forceinline__ float dot4(f32x4 a, f32x4 b, float acc) {
 template <typename IO>
 __device__ __forceinline__ f32x4 ld4io(const void *p, size_t i) {  // 4 consecutive io elements, widened
     return Raw4<IO>::widen(Raw4<IO>::load(static_cast<const IO *>(p) + i));
+}
+template <typename IO>
+__device__ __forceinline__ float ld1io(const void *p, size_t i) {  // one io element, widened
+    if constexpr (sizeof(IO) == 2) return bf2f(static_cast<const IO *>(p)[i]);
+    else return static_cast<const IO *>(p)[i];
 }
 __device__ __forceinline__ f32x4 exp4(f32x4 x) { return f32x4{expf(x[0]), expf(x[1]), expf(x[2]), expf(x[3])}; }
 
@@ -172,7 +201,7 @@ __device__ __forceinline__ void solve_upper(float (&x)[C], const float *sT) {
 template <int D>
 constexpr size_t prep_smem() {
     constexpr size_t LD = D + 4, R0 = C * LD > C * C ? C * LD : C * C;
-    return (R0 + 3 * C * LD + C) * 4;
+    return (R0 + 3 * C * LD + C + kBwdDecRows * D + 4) * 4;
 }
 template <int D>
 constexpr size_t fsweep_smem() {
@@ -201,11 +230,14 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
     float *sQ = smem;           // q (Q~ with a per-channel decay); then T^T, row stride C
     float *sK = sQ + R0;        // k (K~)
     float *sE = sK + C * LD;    // e, then E~, then Y
-    float *sZ = sE + C * LD;    // per-channel decay: g, then G; then z, then U_z
+    float *sZ = sE + C * LD;    // per-channel decay: g, then Gb; then z, then U_z
     float *sGs = sZ + C * LD;   // scalar decay: G per token
+    float *sF = sGs + C;        // per-channel decay: the factor table (kBwdDecRows rows of D)
+    int *sSlow = reinterpret_cast<int *>(sF + kBwdDecRows * D);  // bit b: block b formed entry by entry
     const int tid = threadIdx.x, u = blockIdx.x;
     const Unit x = decode(a, u);
     const size_t ucd = (size_t)u * C * D;
+    if (CHAN && tid == 0) *sSlow = 0;
     f32x4 rz[NL];  // z = beta v (or w v), loaded with the other inputs and staged after T and A
     {
         f32x4 rq[NL], rk[NL], re[NL], rg[CHAN ? NL : 1];
@@ -237,14 +269,31 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
     if (!CHAN && tid < C) sGs[tid] = a.g && tid < x.n ? a.g[x.rowv + (size_t)tid * a.Hv] : 0.f;
     __syncthreads();
     if (CHAN) {
-        if (tid < D) {  // per channel: the column into registers, summed, written back
+        if (tid < D) {  // per channel: the column into registers, summed per block, written back
             float gc[C];
 #pragma unroll
             for (int t = 0; t < C; ++t) gc[t] = sZ[t * LD + tid];
 #pragma unroll
-            for (int t = 1; t < C; ++t) gc[t] += gc[t - 1];
+            for (int t = 1; t < C; ++t)
+                if (t % 16) gc[t] += gc[t - 1];
 #pragma unroll
             for (int t = 0; t < C; ++t) sZ[t * LD + tid] = gc[t];
+            const float B0 = gc[15], B1 = gc[31], B2 = gc[47], B3 = gc[63], Bs[4] = {B0, B1, B2, B3};
+            const float R[5] = {0.f, B0, B0 + B1, B0 + B1 + B2, B0 + B1 + B2 + B3};
+            float *f = sF + tid;
+            int bits = 0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                f[b * D] = expf(R[b]);
+                f[(7 + b) * D] = expf(fminf(-Bs[b], kBwdDiagRange));
+                f[(11 + b) * D] = expf(R[4] - R[b + 1]);
+                bits |= Bs[b] < -kBwdDiagRange ? 1 << b : 0;
+            }
+            f[4 * D] = expf(B1);
+            f[5 * D] = expf(B2);
+            f[6 * D] = expf(B1 + B2);
+            a.wGam[(size_t)u * D + tid] = expf(R[4]);
+            if (bits) atomicOr(sSlow, bits);
         }
     } else if (tid < 64) {
         float G = sGs[tid];
@@ -257,23 +306,20 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
     }
     __syncthreads();
 
-    float *wG = a.wG + ucd;  // [C][D] per-channel decay, [C] scalar
+    float *wG = a.wG + ucd;  // [C][D] per-channel decay (Gb), [C] scalar (G)
+    if (CHAN)  // Q^, K^, E^ in place of q, k, e
 #pragma unroll
-    for (int l = 0; l < NL; ++l) {
-        int e, t, d;
-        rc<D>(l, e, t, d);
-        const f32x4 G = CHAN ? lds4(sZ + t * LD + d) : splat(sGs[t]);
-        const f32x4 Ge = CHAN ? lds4(sZ + (C - 1) * LD + d) : splat(sGs[C - 1]);
-        const f32x4 eg = exp4(G), qv = lds4(sQ + t * LD + d), kv = lds4(sK + t * LD + d);
-        if (CHAN) {
-            sts4(wG + e, G);
-            sts4(sQ + t * LD + d, qv * eg);
-            sts4(sK + t * LD + d, kv * exp4(-G));
+        for (int l = 0; l < NL; ++l) {
+            int e, t, d;
+            rc<D>(l, e, t, d);
+            const f32x4 Gb = lds4(sZ + t * LD + d), Bb = lds4(sZ + (t | 15) * LD + d), eg = exp4(Gb);
+            sts4(wG + e, Gb);
+            sts4(sQ + t * LD + d, lds4(sQ + t * LD + d) * eg);
+            sts4(sK + t * LD + d, lds4(sK + t * LD + d) * exp4(Bb - Gb));
             sts4(sE + t * LD + d, lds4(sE + t * LD + d) * eg);
         }
-    }
     if (!CHAN && tid < C) wG[tid] = sGs[tid];
-    if (tid < D) a.wGam[(size_t)u * D + tid] = expf(CHAN ? sZ[(C - 1) * LD + tid] : sGs[C - 1]);
+    if (!CHAN && tid < D) a.wGam[(size_t)u * D + tid] = expf(sGs[C - 1]);
     __syncthreads();
     // Q~^T and Kend^T (row = channel), which the sweeps over chunks read.
 #pragma unroll
@@ -286,8 +332,9 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
             qv[r] = sQ[(t + r) * LD + dd];
             kv[r] = sK[(t + r) * LD + dd];
         }
-        if (CHAN) {
-            kv *= expf(sZ[(C - 1) * LD + dd]);  // Kend = K~ exp(G_end)
+        if (CHAN) {  // Q~ = Q^ exp(R_b), Kend = K^ exp(G_end - R_{b+1}); the 4 tokens share block b
+            qv *= sF[(t >> 4) * D + dd];
+            kv *= sF[(11 + (t >> 4)) * D + dd];
         } else {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -299,15 +346,52 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
         sts4(a.wKet + ucd + e, kv);
     }
 
-    // T and A: thread = 2 x 4 block of rows r0.., columns c0..
+    // T and A: thread = 2 x 4 block of rows r0.., columns c0.. (the rows in
+    // token block bi, the columns in block bj).
     {
-        const int r0 = (tid >> 4) * 2, c0 = (tid & 15) * 4;
+        const int r0 = (tid >> 4) * 2, c0 = (tid & 15) * 4, bi = r0 >> 4, bj = c0 >> 4;
         float aT[2][4], aA[2][4];
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) aT[i][j] = aA[i][j] = 0.f;
-        if (c0 <= r0 + 1) {
+        // Per-channel decay: the tile's factor on the K^ rows (none for bj = bi - 1).
+        const float *fk = !CHAN || bi - bj == 1 ? nullptr
+                          : sF + (bi == bj ? 7 + bi : bwd_row_far(bi, bj)) * D;
+        if (CHAN && bi == bj && ((*sSlow >> bi) & 1)) {
+            // A strongly decaying diagonal block, entry by entry from the
+            // inputs: sum_c e_tc k_jc exp(Gb_tc - Gb_jc) (the same for q).
+            if (c0 <= r0 + 1)
+                for (int d = 0; d < D; d += 4) {
+                    f32x4 e4[2], q4[2], k4[4], g4[2], h4[4];
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        const int t = r0 + i;
+                        const size_t iq = (x.rowq + (size_t)t * a.Hqk) * D + d, iv = (x.rowv + (size_t)t * a.Hv) * D + d;
+                        q4[i] = t < x.n ? ld4io<IO>(a.q, iq) : zero4();
+                        e4[i] = t < x.n ? ld4io<IO>(a.k, iq) *
+                                              (BW ? ld4io<IO>(a.bg, iv) : splat(a.beta[x.rowv + (size_t)t * a.Hv]))
+                                        : zero4();
+                        g4[i] = lds4(sZ + t * LD + d);
+                    }
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int t = c0 + j;
+                        k4[j] = t < x.n ? ld4io<IO>(a.k, (x.rowq + (size_t)t * a.Hqk) * D + d) : zero4();
+                        h4[j] = lds4(sZ + t * LD + d);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            f32x4 kf;
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) kf[r] = k4[j][r] * expf(fminf(g4[i][r] - h4[j][r], 0.f));
+                            aT[i][j] = dot4(e4[i], kf, aT[i][j]);
+                            aA[i][j] = dot4(q4[i], kf, aA[i][j]);
+                        }
+                }
+        } else if (c0 <= r0 + 1) {
 #pragma unroll 2
             for (int d = 0; d < D; d += 4) {
                 f32x4 e4[2], q4[2], k4[4];
@@ -316,8 +400,9 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
                     e4[i] = lds4(sE + (r0 + i) * LD + d);
                     q4[i] = lds4(sQ + (r0 + i) * LD + d);
                 }
+                const f32x4 f4 = fk ? lds4(fk + d) : splat(1.f);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) k4[j] = lds4(sK + (c0 + j) * LD + d);
+                for (int j = 0; j < 4; ++j) k4[j] = lds4(sK + (c0 + j) * LD + d) * f4;
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -347,7 +432,8 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) sQ[(c0 + j) * C + r0 + i] = aT[i][j];
     }
-    // Right-hand sides: E~ (scalar decay: the raw e scaled by exp(G_t)) and z.
+    // Right-hand sides: E~ (scalar decay: the raw e scaled by exp(G_t); per
+    // channel: E^ scaled by exp(R_b)) and z.
     {
 #pragma unroll
         for (int l = 0; l < NL; ++l) {
@@ -355,6 +441,7 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
             rc<D>(l, e, t, d);
             sts4(sZ + t * LD + d, rz[l]);
             if (!CHAN) sts4(sE + t * LD + d, lds4(sE + t * LD + d) * expf(sGs[t]));
+            else sts4(sE + t * LD + d, lds4(sE + t * LD + d) * lds4(sF + (t >> 4) * D + d));
         }
     }
     __syncthreads();
@@ -821,7 +908,14 @@ __global__ __launch_bounds__(NT) void cb_grad_out(ChunkBwdArgs a) {
     float *sGeP = sTokB + 32 * C;  // [NRG][D] dG_end parts
     float *sGe = sGeP + 2048;      // [D] dG_end (scalar decay: element 0)
     float *sGt = sdT;
-    static_assert(C * LD <= 2 * C * LC && NRG * D <= 2048 && NCG <= 32 && NT / 16 == 32, "shared-memory layout");
+    // Per-channel decay, until the final pass: the tiles' factors (rows 0-2
+    // exp(B_1), exp(B_2), exp(B_1 + B_2); rows 3-6 exp(-B_b), capped) and
+    // each channel's bits of the blocks formed entry by entry, where the
+    // column sums of a scalar decay go.
+    float *sF = sColP;
+    int *sBits = reinterpret_cast<int *>(sColP + 7 * D);
+    static_assert(C * LD <= 2 * C * LC && NRG * D <= 2048 && NCG <= 32 && NT / 16 == 32 && 8 * D <= 32 * C,
+                  "shared-memory layout");
     const int tid = threadIdx.x, u = blockIdx.x;
     const Unit x = decode(a, u);
     const size_t ucd = (size_t)u * C * D, ucc = (size_t)u * C * C;
@@ -846,11 +940,11 @@ __global__ __launch_bounds__(NT) void cb_grad_out(ChunkBwdArgs a) {
             int e, t, d;
             rc<D>(l, e, t, d);
             f32x4 ev = re[l] * rk[l], kv = rk[l], qv = rq[l];
-            if (CHAN) {
-                const f32x4 G = lds4(wG + e), eg = exp4(G);
+            if (CHAN) {  // E^, K^, Q^
+                const f32x4 Gb = lds4(wG + e), Bb = lds4(wG + (t | 15) * D + d), eg = exp4(Gb);
                 qv *= eg;
                 ev *= eg;
-                kv *= exp4(-G);
+                kv *= exp4(Bb - Gb);
             }
             sts4(sP1 + t * LD + d, ev);
             sts4(sP2 + t * LD + d, kv);
@@ -889,6 +983,21 @@ __global__ __launch_bounds__(NT) void cb_grad_out(ChunkBwdArgs a) {
         }
         if (!CHAN) sts4(sColP + (tid >> 4) * C + 4 * (tid & 15), colw);
     }
+    if (CHAN && tid < D) {
+        float Bs[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) Bs[b] = wG[(16 * b + 15) * D + tid];
+        int bits = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            sF[(3 + b) * D + tid] = expf(fminf(-Bs[b], kBwdDiagRange));
+            bits |= Bs[b] < -kBwdDiagRange ? 1 << b : 0;
+        }
+        sF[tid] = expf(Bs[1]);
+        sF[D + tid] = expf(Bs[2]);
+        sF[2 * D + tid] = expf(Bs[1] + Bs[2]);
+        sBits[tid] = bits;
+    }
     __syncthreads();
     if (!CHAN && tid < C) {
         float cs = 0.f;
@@ -898,6 +1007,20 @@ __global__ __launch_bounds__(NT) void cb_grad_out(ChunkBwdArgs a) {
     // X_e = dT' P2, X_q = dA' P2, X_k = dT'^T P1 + dA'^T P3 on the matrix
     // cores: 16 x 16 output tiles, wave w taking tiles w, w + 8, ...; then
     // through shared memory (where P1..P3 were) to the thread layout below.
+    // Per-channel decay: with P1..P3 = E^, K^, Q^ the products split by
+    // 16-token blocks, each block pair (bi, bj) taking its factor per channel
+    // (1 for bj = bi - 1; exp(-B) on the diagonal, which a strongly decaying
+    // block forms entry by entry further below); then exp(Gb_t) (X_e, X_q) and
+    // exp(B - Gb_j) (X_k) per element make them the exact parts of de, dq, dk.
+    int slow = 0;
+    if (CHAN) {
+        const int l = tid & 63;
+        int m = 0;
+        for (int c = l; c < D; c += 64) m |= sBits[c];
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            if (__ballot((m >> b) & 1)) slow |= 1 << b;
+    }
     {
         constexpr int NTC = D / 16, NTW = C / 16 * NTC / 8;
         const int w = tid >> 6, l = tid & 63;
@@ -905,28 +1028,104 @@ __global__ __launch_bounds__(NT) void cb_grad_out(ChunkBwdArgs a) {
 #pragma unroll
         for (int q = 0; q < NTW; ++q) {
             const int tile = w + 8 * q, rt = tile / NTC, ct = tile - rt * NTC;
-            te[q] = mfma_kloop<C>(zero4(), sdT + rt * 16 * LC, LC, sP2 + ct * 16, LD);
-            tq[q] = mfma_kloop<C>(zero4(), sdA + rt * 16 * LC, LC, sP2 + ct * 16, LD);
-            tk[q] = mfma_kloop_at<C>(zero4(), sdT + rt * 16, LC, sP1 + ct * 16, LD);
-            tk[q] = mfma_kloop_at<C>(tk[q], sdA + rt * 16, LC, sP3 + ct * 16, LD);
+            if constexpr (CHAN) {
+                const int col = ct * 16 + (l & 15);
+                const auto factor = [&](int bi, int bj) {
+                    return bi == bj ? sF[(3 + bi) * D + col] : bi - bj == 1 ? 1.f : sF[(bwd_row_far(bi, bj) - 4) * D + col];
+                };
+                te[q] = tq[q] = tk[q] = zero4();
+                for (int bj = 0; bj <= rt; ++bj) {  // rows t in block rt, columns j in block bj
+                    if (bj == rt && ((slow >> rt) & 1)) continue;
+                    const float f = factor(rt, bj);
+                    te[q] += f * mfma_kloop<16>(zero4(), sdT + rt * 16 * LC + bj * 16, LC, sP2 + bj * 16 * LD + ct * 16, LD);
+                    tq[q] += f * mfma_kloop<16>(zero4(), sdA + rt * 16 * LC + bj * 16, LC, sP2 + bj * 16 * LD + ct * 16, LD);
+                }
+                for (int bi = rt; bi < 4; ++bi) {  // rows j in block rt, tokens t in block bi
+                    if (bi == rt && ((slow >> rt) & 1)) continue;
+                    f32x4 p = mfma_kloop_at<16>(zero4(), sdT + bi * 16 * LC + rt * 16, LC, sP1 + bi * 16 * LD + ct * 16, LD);
+                    p = mfma_kloop_at<16>(p, sdA + bi * 16 * LC + rt * 16, LC, sP3 + bi * 16 * LD + ct * 16, LD);
+                    tk[q] += factor(bi, rt) * p;
+                }
+            } else {
+                te[q] = mfma_kloop<C>(zero4(), sdT + rt * 16 * LC, LC, sP2 + ct * 16, LD);
+                tq[q] = mfma_kloop<C>(zero4(), sdA + rt * 16 * LC, LC, sP2 + ct * 16, LD);
+                tk[q] = mfma_kloop_at<C>(zero4(), sdT + rt * 16, LC, sP1 + ct * 16, LD);
+                tk[q] = mfma_kloop_at<C>(tk[q], sdA + rt * 16, LC, sP3 + ct * 16, LD);
+            }
         }
         __syncthreads();  // dT, dA and the P tiles read
 #pragma unroll
         for (int q = 0; q < NTW; ++q) {
-            const int tile = w + 8 * q, rt = tile / NTC, ct = tile - rt * NTC;
+            const int tile = w + 8 * q, rt = tile / NTC, ct = tile - rt * NTC, col = ct * 16 + (l & 15);
+            const float Bb = CHAN ? wG[(rt * 16 + 15) * D + col] : 0.f;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int o = (rt * 16 + 4 * (l >> 4) + r) * LD + ct * 16 + (l & 15);
-                sP1[o] = te[q][r];
-                sP2[o] = tq[q][r];
-                sP3[o] = tk[q][r];
+                const int row = rt * 16 + 4 * (l >> 4) + r, o = row * LD + col;
+                float fe = 1.f, fk = 1.f;
+                if (CHAN) {
+                    const float Gb = wG[row * D + col];
+                    fe = expf(Gb);
+                    fk = expf(Bb - Gb);
+                }
+                sP1[o] = te[q][r] * fe;
+                sP2[o] = tq[q][r] * fe;
+                sP3[o] = tk[q][r] * fk;
             }
         }
     }
-    __syncthreads();  // X tiles written; dT's space holds dG from here
+    __syncthreads();  // X tiles written
+    if (CHAN && slow) {
+        // The diagonal blocks formed entry by entry: for token t and channel
+        // d of such a block, the sums over the block's tokens m of
+        // dT_tm k_m, dA_tm k_m (m before t) and dT_mt e_m + dA_mt q_m (m after
+        // t), each times exp(Gb_t - Gb_m) or exp(Gb_m - Gb_t).
+        for (int b = 0; b < 4; ++b) {
+            if (!((slow >> b) & 1)) continue;
+            for (int idx = tid; idx < 16 * D; idx += NT) {
+                const int i = idx / D, d = idx - i * D, t = 16 * b + i;
+                const float gt = wG[t * D + d];
+                float xe = 0.f, xq = 0.f, xk = 0.f;
+                for (int mm = 0; mm < 16; ++mm) {
+                    const int m = 16 * b + mm;
+                    if (m >= x.n) break;
+                    const size_t iq = (x.rowq + (size_t)m * a.Hqk) * D + d, iv = (x.rowv + (size_t)m * a.Hv) * D + d;
+                    const float km = ld1io<IO>(a.k, iq), gm = wG[m * D + d];
+                    if (m <= t) {
+                        const float f = expf(fminf(gt - gm, 0.f)) * km;
+                        xq = fmaf(sdA[t * LC + m], f, xq);
+                        if (m < t) xe = fmaf(sdT[t * LC + m], f, xe);
+                    }
+                    if (m >= t) {
+                        const float f = expf(fminf(gm - gt, 0.f));
+                        const float em = km * (BW ? ld1io<IO>(a.bg, iv) : a.beta[x.rowv + (size_t)m * a.Hv]);
+                        xk = fmaf(sdA[m * LC + t], f * ld1io<IO>(a.q, iq), xk);
+                        if (m > t) xk = fmaf(sdT[m * LC + t], f * em, xk);
+                    }
+                }
+                sP1[t * LD + d] += xe;
+                sP2[t * LD + d] += xq;
+                sP3[t * LD + d] += xk;
+            }
+        }
+        __syncthreads();
+    }
+    // dT's space holds dG from here.
     const int cg = tid % NCG, rg = tid / NCG, m0 = rg * RT, n0 = 4 * cg;
 
     f32x4 gend = zero4();
+    // Per-channel decay: this thread's rows lie in one block b; G_t = R_b +
+    // Gb_t and G_end - G_t = B_b - Gb_t + (the blocks after b).
+    f32x4 Rb = zero4(), Aft = zero4(), Bb = zero4();
+    if (CHAN) {
+        const int b = m0 >> 4;
+#pragma unroll
+        for (int b2 = 0; b2 < 4; ++b2) {
+            const f32x4 B2 = lds4(wG + (16 * b2 + 15) * D + n0);
+            if (b2 < b) Rb += B2;
+            if (b2 > b) Aft += B2;
+            if (b2 == b) Bb = B2;
+        }
+    }
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
         const int t = m0 + i;
@@ -936,19 +1135,18 @@ __global__ __launch_bounds__(NT) void cb_grad_out(ChunkBwdArgs a) {
             const size_t o = ucd + (size_t)t * D + n0;
             const float bt = tied ? a.beta[x.rowv + (size_t)t * a.Hv] : 0.f;
             const f32x4 G = CHAN ? lds4(wG + t * D + n0) : splat(wG[t]);
-            const f32x4 Ge = CHAN ? lds4(wG + (C - 1) * D + n0) : splat(wG[C - 1]);
-            const f32x4 eg = exp4(G), egend = exp4(Ge - G);
+            const f32x4 eg = CHAN ? exp4(Rb + G) : exp4(G);
+            const f32x4 egend = CHAN ? exp4(Bb - G + Aft) : exp4(splat(wG[C - 1]) - G);
             const f32x4 qv = ld4io<IO>(a.q, iq), kv = ld4io<IO>(a.k, iq), vv = ld4io<IO>(a.v, iv);
             const f32x4 gb = BW ? ld4io<IO>(a.bg, iv) : splat(bt), gw = BW ? ld4io<IO>(a.wg, iv) : splat(bt);
             const f32x4 dEY = lds4(a.wdE + o), dQS = lds4(a.wdQ + o), dKE = lds4(a.wdK + o), dR = lds4(a.wdU + o);
             const f32x4 xe = lds4(sP1 + t * LD + n0), xq = lds4(sP2 + t * LD + n0), xk = lds4(sP3 + t * LD + n0);
-            const f32x4 emg = CHAN ? exp4(-G) : splat(1.f);
-            const f32x4 de = (CHAN ? xe * eg : xe) + dEY * eg;
-            const f32x4 dq = (CHAN ? xq * eg : xq) + dQS * eg;
+            const f32x4 de = xe + dEY * eg;
+            const f32x4 dq = xq + dQS * eg;
             const f32x4 ke = kv * egend;
-            f32x4 dk = (CHAN ? xk * emg : xk) + dKE * egend;
+            f32x4 dk = xk + dKE * egend;
             f32x4 dG = gb * kv * eg * dEY + qv * eg * dQS - ke * dKE;
-            if (CHAN) dG += gb * kv * eg * xe - kv * emg * xk + qv * eg * xq;  // E~, K~, Q~ times their parts
+            if (CHAN) dG += gb * kv * xe - kv * xk + qv * xq;  // the exponentials of T and A
             gend += ke * dKE;
             if (CHAN) sts4(sGt + t * LD + n0, dG);
             else dgs = dG[0] + dG[1] + dG[2] + dG[3];

@@ -59,13 +59,11 @@
  * - Supported: d_k, d_v in {32, 64, 128}; chunk == 64; io float32 or
  *   bfloat16. Arithmetic: state and accumulation in float32; bfloat16 io runs
  *   the chunk products on bf16 matrix cores, float32 io on float32 ones.
- *   Any finite g <= 0 is accepted: the chunked forward references the decay
- *   inside a chunk to its 16-token blocks ("Pipeline Triton da versão por
- *   chunks": the diagonal 16-token blocks first), so no factor it forms
- *   exceeds exp(40), and a block that decays further is formed entry by entry.
- *   gdr_chunk_bwd with GDR_DECAY_CHANNEL still factors exp(G_i - G_j) as
- *   exp(G_i) exp(-G_j) and needs the cumulative log-decay inside one chunk to
- *   stay above -80 on every channel (gdr_recurrent_bwd has no such limit).
+ *   Any finite g <= 0 is accepted by every call: the chunked forward and
+ *   backward reference the decay inside a chunk to its 16-token blocks
+ *   ("Pipeline Triton da versão por chunks": the diagonal 16-token blocks
+ *   first), so no factor they form exceeds exp(40), and a block that decays
+ *   further is formed entry by entry.
  */
 #ifndef GDR_H
 #define GDR_H

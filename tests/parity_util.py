@@ -140,3 +140,19 @@ def small_workload(io, D, decay, gates, T, B=2, Hqk=1, Hv=2, S0=False, decode=Fa
     g_recipe = {"none": "none", "scalar": "softplus_0.1", "channel": "softplus_0.05"}[decay]
     return gs.Workload(f"small_{io}_D{D}_{decay}_{gates}_T{T}", B, T, Hqk, Hv, D, D, io, decay, gates, g_recipe,
                        S0="normal_0.02" if S0 else "zero", scale=scale, decode=decode)
+
+
+def strong_channel_decay(g, T, D):
+    """Per-channel log decays the chunked prefill must survive: -1.5 held on
+    some channels over whole chunks (in-chunk sums near -96, beyond where
+    exp(-G) overflows float32), a gradual -2.6 per token over one 16-token
+    block (a block sum just past 40), and spikes of -30 and -200 (alpha
+    underflows to zero) on single tokens and channels."""
+    g = g.copy()
+    g[:, 64:min(T, 192), :, : D // 8] = -1.5
+    if T > 146:
+        g[:, 130:146, 0, D // 4: D // 4 + 2] = -2.6
+    g[:, min(20, T - 1), :, 3] = -30.0
+    g[:, min(37, T - 1), -1, 5:9] = -200.0
+    g[:, min(100, T - 1), 0, :] = -45.0
+    return g

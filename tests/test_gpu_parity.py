@@ -10,7 +10,7 @@ import pytest
 
 import gdr_synth as gs
 from parity_util import (TOL, from_dev, gpu_decode, gpu_prefill, gpu_prefill_in, gpu_recurrent, gpu_recurrent_in,
-                         oracle_input_stage, oracle_prefill, rel_err, say, small_workload, to_dev)
+                         oracle_input_stage, oracle_prefill, rel_err, say, small_workload, strong_channel_decay, to_dev)
 
 torch = pytest.importorskip("torch")
 pytestmark = [pytest.mark.gpu,
@@ -83,22 +83,6 @@ def test_prefill_grouped_heads_and_scale(io, D):
     assert rel_err(from_dev(ST), S_ref) < TOL[io]
 
 
-def _strong_channel_decay(g, T, D):
-    """Per-channel log decays the chunked prefill must survive: -1.5 held on
-    some channels over whole chunks (in-chunk sums near -96, beyond where
-    exp(-G) overflows float32), a gradual -2.6 per token over one 16-token
-    block (a block sum just past 40), and spikes of -30 and -200 (alpha
-    underflows to zero) on single tokens and channels."""
-    g = g.copy()
-    g[:, 64:min(T, 192), :, : D // 8] = -1.5
-    if T > 146:
-        g[:, 130:146, 0, D // 4: D // 4 + 2] = -2.6
-    g[:, min(20, T - 1), :, 3] = -30.0
-    g[:, min(37, T - 1), -1, 5:9] = -200.0
-    g[:, min(100, T - 1), 0, :] = -45.0
-    return g
-
-
 @pytest.mark.parametrize("io,D,gates,T", [
     ("bf16", 128, "beta", 150), ("bf16", 128, "bw", 200), ("bf16", 64, "beta", 150), ("bf16", 32, "bw", 150),
     ("f32", 64, "bw", 150), ("f32", 32, "beta", 70),
@@ -108,7 +92,7 @@ def test_prefill_strong_channel_decay(io, D, gates, T):
     must give the token recurrence, with no overflow inside a chunk."""
     wl = small_workload(io, D, "channel", gates, T=T, B=2, Hqk=1, Hv=2, S0=True, scale=D ** -0.5)
     inp = gs.make_inputs(wl, seed=61 + D)
-    inp = dict(inp, g=_strong_channel_decay(inp["g"], T, D))
+    inp = dict(inp, g=strong_channel_decay(inp["g"], T, D))
     say(f"prefill strong channel decay {wl.name}")
     o, ST = gpu_prefill(inp, S0=to_dev(inp["S0"]))
     o_ref, S_ref = oracle_prefill(inp)
@@ -122,7 +106,7 @@ def test_prefill_strong_channel_decay_segmented():
     wl = small_workload("bf16", 128, "channel", "bw", T=2200, B=1, Hqk=1, Hv=1, S0=True)
     assert _sweep_segments(1, 1, 128, 2200) > 1
     inp = gs.make_inputs(wl, seed=66)
-    g = _strong_channel_decay(inp["g"], 2200, 128)
+    g = strong_channel_decay(inp["g"], 2200, 128)
     g[:, 1000:1400, :, 40:44] = -1.5
     g[:, 1601, :, 90] = -200.0
     inp = dict(inp, g=g)
@@ -152,6 +136,31 @@ def test_prefill_input_stage_strong_channel_decay(io, D, gates):
     x[:, 130:146, 0, D // 4: D // 4 + 2] = 2.6
     raw = dict(raw, g=x)
     say(f"prefill input stage strong channel decay {wl.name}")
+    o, ST, cout = gpu_prefill_in(raw, S0=to_dev(raw["S0"]))
+    o_ref, S_ref, c_ref = oracle_input_stage(raw)
+    assert rel_err(from_dev(o), o_ref) < TOL[io]
+    assert rel_err(from_dev(ST), S_ref) < TOL[io]
+    assert _conv_equal(cout, c_ref)
+
+
+@pytest.mark.parametrize("io,D,gates", [("bf16", 128, "bw"), ("bf16", 64, "beta"), ("f32", 32, "bw")])
+def test_prefill_in_stage_pass_strong_channel_decay(io, D, gates):
+    """gdr_chunk_fwd_in with a per-channel decay runs the input stage as a
+    pass of its own, then the prefill. Decay inputs x with g = -softplus(x)
+    (decay constant 1) give -1.5 held over two chunks on some channels, a
+    block of -2.6, and spikes near -30, -45 and -200."""
+    T = 200
+    wl = small_workload(io, D, "channel", gates, T=T, B=2, Hqk=1, Hv=2, S0=True, scale=D ** -0.5)
+    wl = wl.scaled(g_recipe="logsigmoid_n21")  # decay constant c = 1
+    raw = gs.make_raw_inputs(wl, seed=97 + D)
+    x = raw["g"].copy()
+    x[:, 64:192, :, : D // 8] = 1.25       # softplus(1.25) = 1.52
+    x[:, 130:146, 0, D // 4: D // 4 + 2] = 2.5
+    x[:, 20, :, 3] = 30.0
+    x[:, 100, 0, :] = 45.0
+    x[:, 37, -1, 5:9] = 200.0
+    raw = dict(raw, g=x)
+    say(f"prefill stage pass strong channel decay {wl.name}")
     o, ST, cout = gpu_prefill_in(raw, S0=to_dev(raw["S0"]))
     o_ref, S_ref, c_ref = oracle_input_stage(raw)
     assert rel_err(from_dev(o), o_ref) < TOL[io]

@@ -19,7 +19,7 @@ import pytest
 
 import gdr_synth as gs
 from oracle import backward as obw
-from parity_util import rel_err, say, small_workload, to_dev
+from parity_util import rel_err, say, small_workload, strong_channel_decay, to_dev
 
 torch = pytest.importorskip("torch")
 pytestmark = [pytest.mark.gpu,
@@ -28,8 +28,10 @@ pytestmark = [pytest.mark.gpu,
 MODES = [("none", "beta"), ("scalar", "beta"), ("channel", "beta"), ("channel", "bw"), ("scalar", "bw")]
 
 
-def _dev_inputs(wl, seed, dST=True):
+def _dev_inputs(wl, seed, dST=True, g_fn=None):
     inp = gs.make_inputs(wl, seed)
+    if g_fn is not None:
+        inp = dict(inp, g=g_fn(inp["g"]))
     gr = gs.make_output_grads(wl, seed, dST=dST)
     d = {n: to_dev(inp[n]) for n in ("q", "k", "v", "g", "beta", "b", "w", "S0")}
     return inp, gr, d
@@ -40,9 +42,9 @@ def _call(fn, d, gr, wl):
               dST=to_dev(gr["dST"]), scale=wl.scale)
 
 
-def _run(wl, seed=0, dST=True, heads=None):
+def _run(wl, seed=0, dST=True, heads=None, g_fn=None):
     import gated_delta_rule_23_amd as gdr
-    inp, gr, d = _dev_inputs(wl, seed, dST)
+    inp, gr, d = _dev_inputs(wl, seed, dST, g_fn)
     say(f"chunk backward {wl.name} seed={seed} dST={dST}")
     out = _call(gdr.gdr_chunk_bwd, d, gr, wl)
     torch.cuda.synchronize()
@@ -113,6 +115,20 @@ def test_chunk_backward_strong_scalar_decay(io, D):
     wl = gs.Workload(f"strong_decay_{io}_D{D}", 2, 200, 1, 2, D, D, io, "scalar", "beta", "logsigmoid_n21",
                      S0="normal_0.02", scale=D ** -0.5)
     got, ref = _run(wl, seed=9)
+    _check(got, ref, 1e-4)
+
+
+@pytest.mark.parametrize("io,D,gates,T,Hv", [
+    ("f32", 32, "beta", 150, 2), ("f32", 64, "bw", 200, 2), ("bf16", 128, "bw", 200, 2), ("bf16", 128, "beta", 150, 2),
+    ("bf16", 64, "beta", 150, 3),
+])
+def test_chunk_backward_strong_channel_decay(io, D, gates, T, Hv):
+    """Per-channel decays far stronger than the workloads' (-1.5 held over
+    whole chunks, one block past 40, spikes of -30, -45 and -200): the
+    chunked gradients must match the recurrence's, with no factor
+    overflowing inside a chunk."""
+    wl = small_workload(io, D, "channel", gates, T=T, B=2, Hqk=1, Hv=Hv, S0=True, scale=D ** -0.5)
+    got, ref = _run(wl, seed=81 + D, g_fn=lambda g: strong_channel_decay(g, T, D))
     _check(got, ref, 1e-4)
 
 
