@@ -15,6 +15,7 @@
 
 #include "gdr.h"
 #include "kernels.hpp"
+#include "norm_la.hpp"
 
 // The workspace of gdr_chunk_fwd_noalloc: one array per GPU, allocated when
 // the library's code is loaded on that GPU and held until the process ends.
@@ -425,6 +426,63 @@ int bwd_call(bool chunked, const gdr_desc *d, const void *q, const void *k, cons
     return ok();
 }
 
+// Normalised linear attention: checks shared by the prefill and the decode
+// step (T = 1 for decode). S0/z0 and ST/zT may be the same arrays.
+int nla_call(const gdr_desc *d, bool decode, const void *q, const void *k, const void *v, const float *S0,
+             const float *z0, void *o, float *ST, float *zT, void *ws, size_t ws_bytes, void *stream) {
+    if (!d) return fail(GDR_E_INVAL, "desc is NULL");
+    const int T = decode ? 1 : d->T;
+    if (d->B < 0) return fail(GDR_E_INVAL, "B = %d must be >= 0", d->B);
+    if (T < 0) return fail(GDR_E_INVAL, "T = %d must be >= 0", T);
+    if (d->H_qk <= 0 || d->H_v <= 0) return fail(GDR_E_INVAL, "H_qk = %d and H_v = %d must be > 0", d->H_qk, d->H_v);
+    if (d->H_v % d->H_qk != 0)
+        return fail(GDR_E_INVAL, "H_v = %d must be a multiple of H_qk = %d", d->H_v, d->H_qk);
+    if (d->io_dtype != GDR_F32 && d->io_dtype != GDR_BF16) return fail(GDR_E_INVAL, "io_dtype = %d", d->io_dtype);
+    if (d->decay != GDR_DECAY_NONE) return fail(GDR_E_INVAL, "normalised linear attention has no decay: decay must be GDR_DECAY_NONE");
+    if (d->d_k != d->d_v || !supported_dim(d->d_k))
+        return fail(GDR_E_UNSUPPORTED, "d_k = %d, d_v = %d: supported are d_k == d_v in {32, 64, 128}", d->d_k, d->d_v);
+    if (!decode && d->chunk != gdr::kChunk) return fail(GDR_E_UNSUPPORTED, "chunk = %d: only 64 is supported", d->chunk);
+    if (!size_ok(d->B, T, d->H_v, d->d_k)) return fail(GDR_E_INVAL, "sizes too large");
+    if (d->B == 0) return ok();
+    if (!ST || !zT) return fail(GDR_E_INVAL, decode ? "S and z must be non-NULL" : "ST and zT must be non-NULL");
+    if (T > 0 && (!q || !k || !v || !o)) return fail(GDR_E_INVAL, "phq, phk, v and o must be non-NULL");
+    for (const void *p : std::initializer_list<const void *>{q, k, v, o, S0, z0, ST, zT, ws})
+        if (p && !aligned(p, 16)) return fail(GDR_E_INVAL, "array pointers must be 16-byte aligned");
+    const int D = d->d_k, NC = (T + gdr::kChunk - 1) / gdr::kChunk;
+    const size_t need = gdr::nla_ws_bytes(d->B, d->H_v, D, NC);
+    if (need > 0 && (!ws || ws_bytes < need))
+        return fail(GDR_E_INVAL, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : 0);
+    // Outputs against inputs and one another (S_T may be S0, z_T may be z0).
+    const size_t esz = d->io_dtype == GDR_BF16 ? 2 : 4, tok = (size_t)d->B * T;
+    const size_t sb = (size_t)d->B * d->H_v * D * D * sizeof(float), zb = (size_t)d->B * d->H_v * D * sizeof(float);
+    struct Range { const void *p; size_t n; };
+    const Range in[] = {{q, tok * d->H_qk * D * esz}, {k, tok * d->H_qk * D * esz}, {v, tok * d->H_v * D * esz},
+                        {S0, S0 ? sb : 0}, {z0, z0 ? zb : 0}};
+    const Range out[] = {{o, T > 0 ? tok * d->H_v * D * esz : 0}, {ST, sb}, {zT, zb}, {ws, need}};
+    const char *name[] = {"o", "ST", "zT", "the workspace"};
+    for (int i = 0; i < 4; ++i) {
+        if (!out[i].p || !out[i].n) continue;
+        for (const Range &x : in) {
+            if (!x.p || !x.n || (i == 1 && x.p == S0 && ST == S0) || (i == 2 && x.p == z0 && zT == z0)) continue;
+            if (ranges_meet(out[i].p, out[i].n, x.p, x.n))
+                return fail(GDR_E_INVAL, "%s overlaps an input (ST may equal S0 and zT z0, nothing else)", name[i]);
+        }
+        for (int j = i + 1; j < 4; ++j)
+            if (out[j].p && out[j].n && ranges_meet(out[i].p, out[i].n, out[j].p, out[j].n))
+                return fail(GDR_E_INVAL, "%s overlaps %s", name[i], name[j]);
+    }
+    gdr::NlaArgs a{};
+    a.q = q; a.k = k; a.v = v; a.S0 = S0; a.z0 = z0; a.o = o; a.ST = ST; a.zT = zT;
+    a.ws = static_cast<float *>(ws);
+    a.B = d->B; a.T = T; a.Hqk = d->H_qk; a.Hv = d->H_v; a.NC = NC;
+    gdr::nla_segments(d->B, d->H_v, D, NC, a.P, a.L);
+    a.z_apart = a.P == 1 && z0 && z0 == zT;
+    const hipError_t e = gdr::launch_nla(d->io_dtype == GDR_BF16 ? gdr::IO_BF16 : gdr::IO_F32, D, a,
+                                         static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "normalised linear attention launch");
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -542,6 +600,29 @@ int gdr_recurrent_fwd_in(const gdr_desc *d, const gdr_input_stage *stage, const 
 }
 
 int gdr_recurrent_bwd_workspace_bytes(const gdr_desc *d, size_t *bytes) { return bwd_workspace_bytes(d, bytes, false); }
+
+int gdr_norm_la_workspace_bytes(const gdr_desc *d, size_t *bytes) {
+    if (!bytes) return fail(GDR_E_INVAL, "bytes is NULL");
+    *bytes = 0;
+    if (!d) return fail(GDR_E_INVAL, "desc is NULL");
+    if (d->B < 0 || d->T < 0 || d->H_v <= 0) return fail(GDR_E_INVAL, "B, T must be >= 0 and H_v > 0");
+    if (d->d_k != d->d_v || !supported_dim(d->d_k))
+        return fail(GDR_E_UNSUPPORTED, "d_k = %d, d_v = %d: supported are d_k == d_v in {32, 64, 128}", d->d_k, d->d_v);
+    if (!size_ok(d->B, d->T, d->H_v, d->d_k)) return fail(GDR_E_INVAL, "sizes too large");
+    *bytes = gdr::nla_ws_bytes(d->B, d->H_v, d->d_k, (d->T + gdr::kChunk - 1) / gdr::kChunk);
+    return ok();
+}
+
+int gdr_norm_la_fwd(const gdr_desc *d, const void *phq, const void *phk, const void *v, const float *S0,
+                    const float *z0, void *o, float *ST, float *zT, void *workspace, size_t workspace_bytes,
+                    void *stream) {
+    return nla_call(d, false, phq, phk, v, S0, z0, o, ST, zT, workspace, workspace_bytes, stream);
+}
+
+int gdr_norm_la_decode_step(const gdr_desc *d, const void *phq, const void *phk, const void *v, float *S, float *z,
+                            void *o, void *stream) {
+    return nla_call(d, true, phq, phk, v, S, z, o, S, z, nullptr, 0, stream);
+}
 
 int gdr_recurrent_bwd(const gdr_desc *d, const void *q, const void *k, const void *v, const float *g,
                       const float *beta, const void *b, const void *w, const float *S0, const void *dO,

@@ -317,6 +317,47 @@ int gdr_chunk_bwd(const gdr_desc *desc, const void *q, const void *k, const void
                   const float *dST, float *dq, float *dk, float *dv, float *dg, float *dbeta, float *db, float *dw,
                   float *dS0, void *workspace, size_t workspace_bytes, void *stream);
 
+/* ---- Normalised linear attention ----
+ * The read with a normaliser of page "Linear attention e fast weights",
+ * section "Conceito": the output for token t is the average of the values
+ * v_i, i <= t, weighted by phi(q_t) . phi(k_i), kept incrementally as a
+ * matrix state and a normaliser per (sequence, V head):
+ *   S_t = S_{t-1} + phi(k_t) v_t^T,   z_t = z_{t-1} + phi(k_t),
+ *   o_t = S_t^T phi(q_t) / (z_t^T phi(q_t)).
+ * The feature map phi is the caller's: phq and phk are phi(q) and phi(k)
+ * (for a weighted average phi must be non-negative and z_t^T phi(q_t) > 0;
+ * a zero normaliser gives the IEEE quotient, not an error).
+ *   desc: decay must be GDR_DECAY_NONE; scale, and the gates of the other
+ *   calls, do not apply (the normaliser cancels any read scale). d_k == d_v
+ *   in {32, 64, 128}, io float32 or bfloat16; chunk == 64 for the prefill.
+ *   phq, phk: [B, T, H_qk, d] io; v, o: [B, T, H_v, d] io; V head h reads QK
+ *   head h / (H_v / H_qk). S: [B, H_v, d, d] float32 (row = key channel);
+ *   z: [B, H_v, d] float32. Alignment 16 bytes for every array.
+ *   Arithmetic: float32 state and normaliser; with bfloat16 io the chunk
+ *   products run on bf16 matrix cores (the state enters Q S rounded to
+ *   bf16), with float32 io on float32 matrix cores. */
+
+/* Device workspace bytes gdr_norm_la_fwd needs (0 when the sequence is not
+ * split into segments); needs no GPU. It holds, per (sequence, V head,
+ * segment of the sequence run side by side), a d x d + d float32 slab: the
+ * segment's sums, then the state entering it. */
+int gdr_norm_la_workspace_bytes(const gdr_desc *desc, size_t *bytes);
+
+/* Prefill over T tokens from (S0, z0) (NULL: zeros) to (ST, zT), in the
+ * chunked form (64-token chunks: A = tril(phq phk^T), O = (Q S + A V) /
+ * (Q z + rowsum A)). ST may be S0 and zT may be z0 (in-place update);
+ * outputs must not otherwise overlap inputs or one another (GDR_E_INVAL).
+ * T == 0 writes S0 and z0 (or zeros) to ST and zT. */
+int gdr_norm_la_fwd(const gdr_desc *desc, const void *phq, const void *phk, const void *v,
+                    const float *S0, const float *z0, void *o, float *ST, float *zT,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* One decode step for B sequences, one token each: phq, phk [B, H_qk, d],
+ * v, o [B, H_v, d]; S and z updated in place. desc->T and desc->chunk are
+ * ignored. */
+int gdr_norm_la_decode_step(const gdr_desc *desc, const void *phq, const void *phk, const void *v,
+                            float *S, float *z, void *o, void *stream);
+
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char *gdr_last_error(void);
 
