@@ -33,7 +33,8 @@ EXPORTS = ("gdr_state_bytes", "gdr_state_alloc", "gdr_state_free", "gdr_chunk_wo
            "gdr_chunk_fwd_in_workspace_bytes",
            "gdr_chunk_fwd", "gdr_decode_step", "gdr_recurrent_fwd", "gdr_recurrent_fwd_in", "gdr_chunk_fwd_in",
            "gdr_recurrent_bwd_workspace_bytes", "gdr_recurrent_bwd", "gdr_chunk_bwd_workspace_bytes", "gdr_chunk_bwd",
-           "gdr_chunk_fwd_noalloc", "gdr_last_error", "gdr_version")
+           "gdr_chunk_fwd_noalloc", "gdr_norm_la_workspace_bytes", "gdr_norm_la_fwd", "gdr_norm_la_decode_step",
+           "gdr_last_error", "gdr_version")
 
 
 class GdrError(RuntimeError):
@@ -81,6 +82,12 @@ def _load():
     lib.gdr_chunk_fwd.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, S, P]
     lib.gdr_chunk_fwd_noalloc.restype = I
     lib.gdr_chunk_fwd_noalloc.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P]
+    lib.gdr_norm_la_workspace_bytes.restype = I
+    lib.gdr_norm_la_workspace_bytes.argtypes = [D, ctypes.POINTER(S)]
+    lib.gdr_norm_la_fwd.restype = I
+    lib.gdr_norm_la_fwd.argtypes = [D, P, P, P, P, P, P, P, P, P, S, P]
+    lib.gdr_norm_la_decode_step.restype = I
+    lib.gdr_norm_la_decode_step.argtypes = [D, P, P, P, P, P, P, P]
     lib.gdr_decode_step.restype = I
     lib.gdr_decode_step.argtypes = [D, P, P, P, P, P, P, P, P, P, P]
     lib.gdr_recurrent_fwd.restype = I
@@ -143,6 +150,19 @@ def _torch():
 
 def _ptr(t):
     return None if t is None else t.data_ptr()
+
+
+def _torch_stream(stream, dev):
+    """The torch stream a call runs on: the current one, a torch stream, or a
+    raw HIP stream handle. Tensors a call allocates are made on it (under
+    torch.cuda.stream), so that the caching allocator does not hand their
+    memory to another stream while the call's kernels may still use it."""
+    torch = _torch()
+    if stream is None:
+        return torch.cuda.current_stream(dev)
+    if isinstance(stream, int):
+        return torch.cuda.ExternalStream(stream, device=dev)
+    return stream
 
 
 def _stream(stream):
@@ -218,18 +238,20 @@ def gdr_chunk_fwd(q, k, v, *, g=None, beta=None, b=None, w=None, S0=None, scale=
     _require(g, "g", None, torch.float32, dev)
     _require(S0, "S0", (B, Hv, D, D), torch.float32, dev)
     desc = make_desc(B, T, Hqk, Hv, D, _io_dtype(q), _decay_of(g, (B, T), Hv, D), scale, chunk)
-    if o is None:
-        o = torch.empty((B, T, Hv, D), dtype=io_t, device=dev)
-    if ST is None:
-        ST = torch.empty((B, Hv, D, D), dtype=torch.float32, device=dev)
+    s = _torch_stream(stream, dev)
+    with torch.cuda.stream(s):
+        if o is None:
+            o = torch.empty((B, T, Hv, D), dtype=io_t, device=dev)
+        if ST is None:
+            ST = torch.empty((B, Hv, D, D), dtype=torch.float32, device=dev)
+        nbytes = gdr_chunk_workspace_bytes(desc)
+        if workspace is None and nbytes > 0:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     _require(o, "o", (B, T, Hv, D), io_t, dev)
     _require(ST, "ST", (B, Hv, D, D), torch.float32, dev)
-    nbytes = gdr_chunk_workspace_bytes(desc)
-    if workspace is None and nbytes > 0:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.gdr_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(b),
-                             _ptr(w), _ptr(S0), _ptr(o), _ptr(ST), _ptr(workspace), wsz, _stream(stream)))
+                             _ptr(w), _ptr(S0), _ptr(o), _ptr(ST), _ptr(workspace), wsz, _stream(s)))
     return o, ST
 
 
@@ -259,6 +281,67 @@ def gdr_chunk_fwd_noalloc(q, k, v, *, o, ST, g=None, beta=None, b=None, w=None, 
     return o, ST
 
 
+def gdr_norm_la_workspace_bytes(desc: gdr_desc) -> int:
+    n = ctypes.c_size_t()
+    _check(lib.gdr_norm_la_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def gdr_norm_la_fwd(phq, phk, v, *, S0=None, z0=None, o=None, ST=None, zT=None, workspace=None, stream=None):
+    """Normalised linear attention over the T tokens of phq [B,T,Hqk,D]
+    (phi already applied to q and k). Returns (o, ST, zT); ST may be S0 and
+    zT may be z0 for an in-place update."""
+    torch = _torch()
+    B, T, Hqk, D = phq.shape
+    Hv = v.shape[2]
+    dev, io_t = phq.device, phq.dtype
+    for name, t, shape in (("phq", phq, (B, T, Hqk, D)), ("phk", phk, (B, T, Hqk, D)), ("v", v, (B, T, Hv, D))):
+        _require(t, name, shape, io_t, dev)
+    _require(S0, "S0", (B, Hv, D, D), torch.float32, dev)
+    _require(z0, "z0", (B, Hv, D), torch.float32, dev)
+    desc = make_desc(B, T, Hqk, Hv, D, _io_dtype(phq), GDR_DECAY_NONE)
+    s = _torch_stream(stream, dev)
+    with torch.cuda.stream(s):  # tensors made here belong to the stream the call runs on
+        if o is None:
+            o = torch.empty((B, T, Hv, D), dtype=io_t, device=dev)
+        if ST is None:
+            ST = torch.empty((B, Hv, D, D), dtype=torch.float32, device=dev)
+        if zT is None:
+            zT = torch.empty((B, Hv, D), dtype=torch.float32, device=dev)
+        nbytes = gdr_norm_la_workspace_bytes(desc)
+        if workspace is None and nbytes > 0:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    _require(o, "o", (B, T, Hv, D), io_t, dev)
+    _require(ST, "ST", (B, Hv, D, D), torch.float32, dev)
+    _require(zT, "zT", (B, Hv, D), torch.float32, dev)
+    wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.gdr_norm_la_fwd(ctypes.byref(desc), _ptr(phq), _ptr(phk), _ptr(v), _ptr(S0), _ptr(z0), _ptr(o),
+                               _ptr(ST), _ptr(zT), _ptr(workspace), wsz, _stream(s)))
+    return o, ST, zT
+
+
+def gdr_norm_la_decode_step(phq, phk, v, S, z, *, o=None, stream=None):
+    """One normalised linear-attention step per sequence: phq, phk [B,Hqk,D],
+    v [B,Hv,D]; S [B,Hv,D,D] and z [B,Hv,D] updated in place. Returns o."""
+    torch = _torch()
+    B, Hqk, D = phq.shape
+    Hv = v.shape[1]
+    dev, io_t = phq.device, phq.dtype
+    for name, t, shape in (("phq", phq, (B, Hqk, D)), ("phk", phk, (B, Hqk, D)), ("v", v, (B, Hv, D))):
+        _require(t, name, shape, io_t, dev)
+    _require(S, "S", (B, Hv, D, D), torch.float32, dev)
+    _require(z, "z", (B, Hv, D), torch.float32, dev)
+    desc = make_desc(B, 1, Hqk, Hv, D, _io_dtype(phq), GDR_DECAY_NONE)
+    s = _torch_stream(stream, dev)
+    if o is None:
+        with torch.cuda.stream(s):
+            o = torch.empty((B, Hv, D), dtype=io_t, device=dev)
+    _require(o, "o", (B, Hv, D), io_t, dev)
+    _check(lib.gdr_norm_la_decode_step(ctypes.byref(desc), _ptr(phq), _ptr(phk), _ptr(v), _ptr(S), _ptr(z), _ptr(o),
+                                       _stream(s)))
+    return o
+
+
 def gdr_decode_step(q, k, v, S, *, g=None, beta=None, b=None, w=None, scale=1.0, o=None, stream=None):
     """One decode step, updating S [B,Hv,D,D] in place. Returns o [B,Hv,D]."""
     torch = _torch()
@@ -272,11 +355,13 @@ def gdr_decode_step(q, k, v, S, *, g=None, beta=None, b=None, w=None, scale=1.0,
     _require(g, "g", None, torch.float32, dev)
     _require(S, "S", (B, Hv, D, D), torch.float32, dev)
     desc = make_desc(B, 1, Hqk, Hv, D, _io_dtype(q), _decay_of(g, (B,), Hv, D), scale)
+    s = _torch_stream(stream, dev)
     if o is None:
-        o = torch.empty((B, Hv, D), dtype=io_t, device=dev)
+        with torch.cuda.stream(s):
+            o = torch.empty((B, Hv, D), dtype=io_t, device=dev)
     _require(o, "o", (B, Hv, D), io_t, dev)
     _check(lib.gdr_decode_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(b),
-                               _ptr(w), _ptr(S), _ptr(o), _stream(stream)))
+                               _ptr(w), _ptr(S), _ptr(o), _stream(s)))
     return o
 
 
@@ -296,14 +381,16 @@ def gdr_recurrent_fwd(q, k, v, *, g=None, beta=None, b=None, w=None, S0=None, sc
     _require(g, "g", None, torch.float32, dev)
     _require(S0, "S0", (B, Hv, D, D), torch.float32, dev)
     desc = make_desc(B, T, Hqk, Hv, D, _io_dtype(q), _decay_of(g, (B, T), Hv, D), scale)
-    if o is None:
-        o = torch.empty((B, T, Hv, D), dtype=io_t, device=dev)
-    if ST is None:
-        ST = torch.empty((B, Hv, D, D), dtype=torch.float32, device=dev)
+    s = _torch_stream(stream, dev)
+    with torch.cuda.stream(s):
+        if o is None:
+            o = torch.empty((B, T, Hv, D), dtype=io_t, device=dev)
+        if ST is None:
+            ST = torch.empty((B, Hv, D, D), dtype=torch.float32, device=dev)
     _require(o, "o", (B, T, Hv, D), io_t, dev)
     _require(ST, "ST", (B, Hv, D, D), torch.float32, dev)
     _check(lib.gdr_recurrent_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(b),
-                                 _ptr(w), _ptr(S0), _ptr(o), _ptr(ST), _stream(stream)))
+                                 _ptr(w), _ptr(S0), _ptr(o), _ptr(ST), _stream(s)))
     return o, ST
 
 
@@ -340,21 +427,23 @@ def gdr_chunk_fwd_in(q, k, v, conv_w, *, conv_in=None, conv_out=None, decay_scal
     _require(beta, "beta", (B, T, Hv), torch.float32, dev)
     _require(g, "g", None, torch.float32, dev)
     _require(S0, "S0", (B, Hv, D, D), torch.float32, dev)
-    stage, conv_out = _stage_args(q, v, conv_w, conv_in, conv_out, decay_scale)
     desc = make_desc(B, T, Hqk, Hv, D, _io_dtype(q), _decay_of(g, (B, T), Hv, D), scale, chunk)
-    if o is None:
-        o = torch.empty((B, T, Hv, D), dtype=io_t, device=dev)
-    if ST is None:
-        ST = torch.empty((B, Hv, D, D), dtype=torch.float32, device=dev)
+    s = _torch_stream(stream, dev)
+    with torch.cuda.stream(s):
+        stage, conv_out = _stage_args(q, v, conv_w, conv_in, conv_out, decay_scale)
+        if o is None:
+            o = torch.empty((B, T, Hv, D), dtype=io_t, device=dev)
+        if ST is None:
+            ST = torch.empty((B, Hv, D, D), dtype=torch.float32, device=dev)
+        nbytes = gdr_chunk_fwd_in_workspace_bytes(desc)
+        if workspace is None and nbytes > 0:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     _require(o, "o", (B, T, Hv, D), io_t, dev)
     _require(ST, "ST", (B, Hv, D, D), torch.float32, dev)
-    nbytes = gdr_chunk_fwd_in_workspace_bytes(desc)
-    if workspace is None and nbytes > 0:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.gdr_chunk_fwd_in(ctypes.byref(desc), ctypes.byref(stage), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                 _ptr(beta), _ptr(b), _ptr(w), _ptr(S0), _ptr(o), _ptr(ST), _ptr(workspace), wsz,
-                                _stream(stream)))
+                                _stream(s)))
     return o, ST, conv_out
 
 
@@ -377,15 +466,17 @@ def gdr_recurrent_fwd_in(q, k, v, conv_w, *, conv_in=None, conv_out=None, decay_
     _require(g, "g", None, torch.float32, dev)
     _require(S0, "S0", (B, Hv, D, D), torch.float32, dev)
     desc = make_desc(B, T, Hqk, Hv, D, _io_dtype(q), _decay_of(g, (B, T), Hv, D), scale)
-    if o is None:
-        o = torch.empty((B, T, Hv, D), dtype=io_t, device=dev)
-    if ST is None:
-        ST = torch.empty((B, Hv, D, D), dtype=torch.float32, device=dev)
-    stage, conv_out = _stage_args(q, v, conv_w, conv_in, conv_out, decay_scale)
+    s = _torch_stream(stream, dev)
+    with torch.cuda.stream(s):
+        if o is None:
+            o = torch.empty((B, T, Hv, D), dtype=io_t, device=dev)
+        if ST is None:
+            ST = torch.empty((B, Hv, D, D), dtype=torch.float32, device=dev)
+        stage, conv_out = _stage_args(q, v, conv_w, conv_in, conv_out, decay_scale)
     _require(o, "o", (B, T, Hv, D), io_t, dev)
     _require(ST, "ST", (B, Hv, D, D), torch.float32, dev)
     _check(lib.gdr_recurrent_fwd_in(ctypes.byref(desc), ctypes.byref(stage), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
-                                    _ptr(beta), _ptr(b), _ptr(w), _ptr(S0), _ptr(o), _ptr(ST), _stream(stream)))
+                                    _ptr(beta), _ptr(b), _ptr(w), _ptr(S0), _ptr(o), _ptr(ST), _stream(s)))
     return o, ST, conv_out
 
 
@@ -431,24 +522,26 @@ def _bwd(chunked, q, k, v, do, g, beta, b, w, S0, dST, scale, want_dS0, workspac
     _require(dST, "dST", (B, Hv, D, D), torch.float32, dev)
     desc = make_desc(B, T, Hqk, Hv, D, _io_dtype(q), _decay_of(g, (B, T), Hv, D), scale)
     f32 = dict(dtype=torch.float32, device=dev)
-    out = {"dq": torch.empty((B, T, Hqk, D), **f32), "dk": torch.empty((B, T, Hqk, D), **f32),
-           "dv": torch.empty((B, T, Hv, D), **f32)}
-    if g is not None:
-        out["dg"] = torch.empty(g.shape, **f32)
-    if beta is not None:
-        out["dbeta"] = torch.empty((B, T, Hv), **f32)
-    if b is not None:
-        out["db"] = torch.empty((B, T, Hv, D), **f32)
-        out["dw"] = torch.empty((B, T, Hv, D), **f32)
-    if want_dS0:
-        out["dS0"] = torch.empty((B, Hv, D, D), **f32)
-    nbytes = (gdr_chunk_bwd_workspace_bytes if chunked else gdr_recurrent_bwd_workspace_bytes)(desc)
-    if workspace is None and nbytes > 0:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    s = _torch_stream(stream, dev)
+    with torch.cuda.stream(s):
+        out = {"dq": torch.empty((B, T, Hqk, D), **f32), "dk": torch.empty((B, T, Hqk, D), **f32),
+               "dv": torch.empty((B, T, Hv, D), **f32)}
+        if g is not None:
+            out["dg"] = torch.empty(g.shape, **f32)
+        if beta is not None:
+            out["dbeta"] = torch.empty((B, T, Hv), **f32)
+        if b is not None:
+            out["db"] = torch.empty((B, T, Hv, D), **f32)
+            out["dw"] = torch.empty((B, T, Hv, D), **f32)
+        if want_dS0:
+            out["dS0"] = torch.empty((B, Hv, D, D), **f32)
+        nbytes = (gdr_chunk_bwd_workspace_bytes if chunked else gdr_recurrent_bwd_workspace_bytes)(desc)
+        if workspace is None and nbytes > 0:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
     fn = lib.gdr_chunk_bwd if chunked else lib.gdr_recurrent_bwd
     _check(fn(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(b), _ptr(w), _ptr(S0),
               _ptr(do), _ptr(dST), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out.get("dg")),
               _ptr(out.get("dbeta")), _ptr(out.get("db")), _ptr(out.get("dw")), _ptr(out.get("dS0")),
-              _ptr(workspace), wsz, _stream(stream)))
+              _ptr(workspace), wsz, _stream(s)))
     return out
