@@ -15,6 +15,9 @@ tokens/s. In the same run, each as a sub-object of the one JSON line:
   - "backward": gdr_chunk_bwd and gdr_recurrent_bwd on the headline layer;
   - "recurrent": gdr_recurrent_fwd, a few tokens per sequence at the decode
     shape;
+  - "norm_la": normalised linear attention, gdr_norm_la_fwd on a Qwen-like
+    layer (B=1, T=4096, 16 QK / 48 V heads, d=128, bf16) and 256
+    gdr_norm_la_decode_step calls at the decode shape;
   - "copy": a plain 1 GiB device copy, against which every HBM roofline also
     gives "frac_of_copy";
   - "cpu_baseline": the fp64 CPU oracle on the headline layer (all heads, all
@@ -54,6 +57,7 @@ SOURCES = {
     "decode": ("decode.hip", "common.hpp", "kernels.hpp"),
     "recurrent": ("recurrent.hip", "common.hpp", "kernels.hpp"),
     "backward_chunked": ("chunk_bwd.hip", "common.hpp", "kernels.hpp"),
+    "norm_la": ("norm_la.hip", "norm_la.hpp", "common.hpp", "kernels.hpp"),
 }
 
 
@@ -140,6 +144,15 @@ def backward_algorithmic(wl):
     return reads + writes, 16 * B * T * Hv * D * D
 
 
+def norm_la_algorithmic(B, T, Hqk, Hv, D, esz=2, C=64):
+    """Bytes and flops of one normalised linear-attention prefill: phi(q),
+    phi(k) read once per QK head, v read and o written once, the final state
+    and normaliser written (and read when given); flops of the chunked form
+    on dense C x C tiles: A = Q K^T, Q S, A V and K^T V per (token, V head)."""
+    by = 2 * B * T * Hqk * D * esz + 2 * B * T * Hv * D * esz + B * Hv * (D * D + D) * 4
+    return by, (2 * C * D + 2 * D * D + 2 * C * D + 2 * D * D) * B * T * Hv
+
+
 def chunk_backward_flops(wl, C=64):
     """Flops of one gdr_chunk_bwd call, the chunked form's dense products
     counted once (triangular ones at half): per chunk unit 8 C D^2 + 6 C^2 D
@@ -183,6 +196,9 @@ def main(argv=None):
     ap.add_argument("--decode-steps", type=int, default=256, help="consecutive decode steps timed (0 = skip decode)")
     ap.add_argument("--input-stage", type=int, default=1,
                     help="also time the prefill from raw projections (input stage fused; 0 = skip)")
+    ap.add_argument("--norm-la", type=int, default=1,
+                    help="also time normalised linear attention: the Qwen-like prefill (T=4096, 16/48 heads, d=128) "
+                         "and the decode step at the decode shape (0 = skip)")
     ap.add_argument("--recurrent-T", type=int, default=4,
                     help="tokens per sequence of the multi-token recurrent call timed at the decode shape (0 = skip)")
     ap.add_argument("--backward", type=int, default=1,
@@ -528,6 +544,92 @@ def main(argv=None):
                             "traffic": recorded_traffic(dwl.name, "decode") if dwl.T == 256 else None,
                             "algorithmic_bytes": d_bytes}}
 
+    # ---- normalised linear attention: Qwen-like prefill and the decode step ----
+    nla = None
+    if args.norm_la:
+        NB, NT_, NHqk, NHv, ND = 1, 4096, 16, 48, 128
+        nin = gs.make_norm_la_inputs(NB, NT_, NHqk, NHv, ND, io="bf16", seed=args.seed + 5)
+        nq, nk, nv = up(nin["phq"]), up(nin["phk"]), up(nin["v"])
+        ndesc = gdr.make_desc(NB, NT_, NHqk, NHv, ND, gdr.GDR_BF16, gdr.GDR_DECAY_NONE)
+        nws = gdr.gdr_norm_la_workspace_bytes(ndesc)
+        nws_t = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+        no = torch.empty((NB, NT_, NHv, ND), dtype=torch.bfloat16, device=dev)
+        nS = torch.empty((NB, NHv, ND, ND), dtype=torch.float32, device=dev)
+        nz = torch.empty((NB, NHv, ND), dtype=torch.float32, device=dev)
+
+        def nla_call():
+            gdr.gdr_norm_la_fwd(nq, nk, nv, o=no, ST=nS, zT=nz, workspace=nws_t if nws else None, stream=cur())
+
+        for _ in range(args.warmup):
+            nla_call()
+        torch.cuda.synchronize()
+        settle(nla_call)
+        ngraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(ngraph):
+            for _ in range(args.steps):
+                nla_call()
+        settle(ngraph.replay)
+        t_start.record(cur())
+        ngraph.replay()
+        t_end.record(cur())
+        torch.cuda.synchronize()
+        del ngraph
+        n_ms = t_start.elapsed_time(t_end) / args.steps
+        n_bytes, n_flops = norm_la_algorithmic(NB, NT_, NHqk, NHv, ND)
+        # Decode: 256 consecutive steps at the decode shape (64 sequences x 48 V heads).
+        DB, DS = 64, 256
+        din = gs.make_norm_la_inputs(DB, DS, NHqk, NHv, ND, io="bf16", seed=args.seed + 6, state=True)
+        dq_, dk_, dv_ = up(din["phq"]), up(din["phk"]), up(din["v"])
+        S0n, z0n = up(din["S0"]), up(din["z0"])
+        Sn, zn = S0n.clone(), z0n.clone()
+        dout = torch.empty((DB, NHv, ND), dtype=torch.bfloat16, device=dev)
+        steps_q = [(dq_[:, t].contiguous(), dk_[:, t].contiguous(), dv_[:, t].contiguous()) for t in range(DS)]
+
+        def nla_step(t):
+            a_, b_, c_ = steps_q[t]
+            gdr.gdr_norm_la_decode_step(a_, b_, c_, Sn, zn, o=dout, stream=cur())
+
+        for t in range(8):
+            nla_step(t)
+        dgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(dgraph):
+            for t in range(DS):
+                nla_step(t)
+        settle(dgraph.replay)
+        Sn.copy_(S0n)
+        zn.copy_(z0n)
+        torch.cuda.synchronize()
+        t_start.record(cur())
+        dgraph.replay()
+        t_end.record(cur())
+        torch.cuda.synchronize()
+        del dgraph
+        nd_ms = t_start.elapsed_time(t_end) / DS
+        nd_state = 2 * DB * NHv * (ND * ND + ND) * 4
+        nd_bytes = nd_state + 2 * DB * NHqk * ND * 2 + 2 * DB * NHv * ND * 2
+        nla = {"prefill": {"entry": "gdr_norm_la_fwd", "workload": "norm_la_prefill_T4096_Hqk16_Hv48_d128",
+                           "launch": "hip_graph", "steps": args.steps, "ms_per_call": n_ms,
+                           "tokens_per_s": NB * NT_ / (n_ms * 1e-3),
+                           "roofline": {"kernel": "nla_chunks (segment sums, nla_scan, segment sweeps)",
+                                        "bound": "hbm", "achieved": n_bytes / (n_ms * 1e-3) / 1e9,
+                                        "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                        "frac": n_bytes / (n_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                                        "traffic": recorded_traffic("norm_la_prefill_T4096_Hqk16_Hv48_d128", "norm_la"),
+                                        "algorithmic_bytes": n_bytes},
+                           "mfma": {"algorithmic_tflops": n_flops / (n_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
+                                    "frac": n_flops / (n_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                                    "algorithmic_flops": n_flops}},
+               "decode": {"entry": "gdr_norm_la_decode_step", "workload": "norm_la_decode_B64_Hv48_d128_256steps",
+                          "launch": "hip_graph", "steps": DS, "ms_per_step": nd_ms,
+                          "tokens_per_s": DB / (nd_ms * 1e-3), "state_GBps": nd_state / (nd_ms * 1e-3) / 1e9,
+                          "roofline": {"kernel": "nla_chunks (one token) + nla_zsum", "bound": "hbm",
+                                       "achieved": nd_bytes / (nd_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
+                                       "unit": "GB/s", "frac": nd_bytes / (nd_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                                       "traffic": recorded_traffic("norm_la_decode_B64_Hv48_d128_256steps", "norm_la"),
+                                       "algorithmic_bytes": nd_bytes}}}
+        del nin, nq, nk, nv, no, nS, nz, nws_t, din, dq_, dk_, dv_, S0n, z0n, Sn, zn, dout, steps_q
+        progress(f"normalised linear attention: prefill {n_ms:.4f} ms, decode {nd_ms * 1e3:.1f} us per step")
+
     # ---- multi-token recurrent forward (a few tokens per sequence from a live state) ----
     rec = None
     if args.recurrent_T > 0:
@@ -599,11 +701,13 @@ def main(argv=None):
         "backward": bwd,
         "decode": dec,
         "recurrent": rec,
+        "norm_la": nla,
     }
     out["copy"] = copy
     if copy:  # the HBM rooflines also against the bandwidth a plain copy reaches on this GPU
         for r in ([out["roofline"], (stage or {}).get("roofline"), (dec or {}).get("roofline"),
-                   (rec or {}).get("roofline")] + [x["roofline"] for x in sub.values()]):
+                   (rec or {}).get("roofline")] + [x["roofline"] for x in sub.values()] +
+                  [x["roofline"] for x in (nla or {}).values()]):
             if r:
                 r["frac_of_copy"] = r["achieved"] / copy["GBps"]
     if args.cpu_heads > 0:

@@ -476,8 +476,8 @@ int nla_call(const gdr_desc *d, bool decode, const void *q, const void *k, const
     a.ws = static_cast<float *>(ws);
     a.B = d->B; a.T = T; a.Hqk = d->H_qk; a.Hv = d->H_v; a.NC = NC;
     gdr::nla_segments(d->B, d->H_v, D, NC, a.P, a.L);
-    a.z_apart = a.P == 1 && z0 && z0 == zT;
-    const hipError_t e = gdr::launch_nla(d->io_dtype == GDR_BF16 ? gdr::IO_BF16 : gdr::IO_F32, D, a,
+    a.z_apart = !decode && a.P == 1 && z0 && z0 == zT;
+    const hipError_t e = gdr::launch_nla(d->io_dtype == GDR_BF16 ? gdr::IO_BF16 : gdr::IO_F32, D, a, decode,
                                          static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "normalised linear attention launch");
     return ok();

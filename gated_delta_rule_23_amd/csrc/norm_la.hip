@@ -22,7 +22,16 @@
 // accumulators in fp32 for the whole segment. All products run on the
 // matrix cores: bf16 io on v_mfma_f32_16x16x32_bf16 (the state is rounded
 // to bf16 as an operand of Q S, A to bf16 as an operand of A V; the
-// normaliser is formed in fp32), fp32 io on v_mfma_f32_16x16x4_f32.
+// normaliser is formed in fp32), fp32 io on v_mfma_f32_16x16x4_f32. The
+// chunk's rows stay token-major in shared memory; the products that
+// contract over tokens (K^T V, A V) read them with the LDS transpose read.
+// The next chunk's rows are fetched into registers while the current one
+// is computed.
+//
+// The decode step (one token per sequence) is a streaming kernel of its
+// own, nla_decode: one workgroup per (sequence, V head) reads the state
+// once, adds phi(k) v^T, reduces phi(q)^T S over the key axis and writes the
+// state back; HBM-bound.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "norm_la.hpp"
@@ -34,21 +43,50 @@ constexpr int C = 64;     // tokens per chunk
 constexpr int VT = 32;    // value columns per workgroup
 constexpr int NTH = 256;  // threads per workgroup
 
-// Shared-memory tiles (element type IO unless noted), rows padded by 16 bytes:
-//   Q, K [C][LQ] token-major (phi(q), phi(k));  Kt [D][LT], Vt [VT][LT]
-//   channel-major (token axis contiguous); A [C][LT]; S [VT][LQ] (the state
-//   entering the chunk, transposed); z [2][D] fp32 (double-buffered); den
-//   [C] fp32. The output of a 16-token block is staged in its own rows of A.
+// Operands read K-major from token-major shared memory: element (row r, k)
+// at M[k * ld + r]. For bfloat16, gfx950's LDS transpose read
+// ds_read_b64_tr_b16: inside each group of 16 lanes, lane s supplies the
+// address of 4 consecutive 16-bit elements and lane j receives element j % 4
+// of the words of lanes j / 4, 4 + j / 4, 8 + j / 4 and 12 + j / 4, so lane s
+// pointing at rows 4 (s % 4) .. + 3 of K-row k0 + s / 4 hands lane j row j
+// of K-rows k0 .. k0 + 3 (the same reading as the chunked prefill's).
+template <typename IO> struct KmRead;
+template <> struct KmRead<bf16_t> {
+    __device__ __forceinline__ static u16x8 frag(const bf16_t *M, int ld) {
+        const int l = lane_id(), s = l & 15, g = l >> 4;
+        const bf16_t *p = M + (8 * g + (s >> 2)) * ld + 4 * (s & 3);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
+        const s16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p + 4 * ld));
+        return __builtin_bit_cast(u16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+};
+template <> struct KmRead<float> {
+    __device__ __forceinline__ static float frag(const float *M, int ld) {
+        const int l = lane_id();
+        return M[(l >> 4) * ld + (l & 15)];
+    }
+};
+
+// Shared-memory tiles (element type IO unless noted), token-major, rows
+// padded by 16 bytes: Q, K [C][LQ] (phi(q), phi(k)); V [C][LV] (this
+// workgroup's 32 value columns); A [C][LT]; S [VT][LQ] (the state entering
+// the chunk, transposed); z [2][D] fp32 (double-buffered); den [C] fp32.
+// The output of a 16-token block is staged in its own rows of A. The
+// segment-sum pass uses K and V only.
 template <typename IO, int D>
 struct NlaCfg {
     static constexpr int E = 16 / (int)sizeof(IO);  // elements per 16-byte access
-    static constexpr int LQ = D + E, LT = C + E;
-    static constexpr size_t OQ = 0, OK = OQ + (size_t)C * LQ * sizeof(IO), OKT = OK + (size_t)C * LQ * sizeof(IO),
-                            OVT = OKT + (size_t)D * LT * sizeof(IO), OA = OVT + (size_t)VT * LT * sizeof(IO),
-                            OS = OA + (size_t)C * LT * sizeof(IO), OZ = OS + (size_t)VT * LQ * sizeof(IO),
-                            ODEN = OZ + 2 * (size_t)D * 4, BYTES = ODEN + (size_t)C * 4;
+    static constexpr int LQ = D + E, LV = VT + E, LT = C + E;
+    static constexpr size_t OK = 0, OV = OK + (size_t)C * LQ * sizeof(IO), OZ = OV + (size_t)C * LV * sizeof(IO),
+                            OQ = OZ + 2 * (size_t)D * 4, OA = OQ + (size_t)C * LQ * sizeof(IO),
+                            OS = OA + (size_t)C * LT * sizeof(IO), ODEN = OS + (size_t)VT * LQ * sizeof(IO),
+                            BYTES0 = OQ, BYTES1 = ODEN + (size_t)C * 4;
     static constexpr int LO = VT + 4;  // staged output row (floats)
     static_assert((size_t)16 * LO * 4 <= (size_t)16 * LT * sizeof(IO), "a block's output fits its rows of A");
+    static constexpr int GR = D / E, NLD = C * GR / NTH;   // 16-byte pieces of a q or k row; per thread
+    static constexpr int GV = VT / E, NLV = C * GV / NTH;  // of a v row's tile; per thread
+    static_assert(C * GR % NTH == 0 && C * GV % NTH == 0 && NLV >= 1, "load mapping");
 };
 
 template <typename IO>
@@ -64,18 +102,58 @@ __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// One chunk's rows in registers: phi(q), phi(k) (16-byte pieces) and v's tile.
+template <typename IO, int D, bool WITH_Q>
+struct ChunkRegs {
+    using Cf = NlaCfg<IO, D>;
+    uint4 q[WITH_Q ? Cf::NLD : 1], k[Cf::NLD], v[Cf::NLV];
+    __device__ __forceinline__ void load(const NlaArgs &a, int b, int hq, int h, int t0, int n, int col0) {
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int i = 0; i < Cf::NLD; ++i) {
+            const int idx = i * NTH + tid, t = idx / Cf::GR, g = (idx - t * Cf::GR) * Cf::E;
+            const size_t row = (((size_t)b * a.T + t0 + t) * a.Hqk + hq) * D + g;
+            k[i] = t < n ? *reinterpret_cast<const uint4 *>(static_cast<const IO *>(a.k) + row) : uint4{0u, 0u, 0u, 0u};
+            if constexpr (WITH_Q)
+                q[i] = t < n ? *reinterpret_cast<const uint4 *>(static_cast<const IO *>(a.q) + row) : uint4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int i = 0; i < Cf::NLV; ++i) {
+            const int idx = i * NTH + tid, t = idx / Cf::GV, g = (idx - t * Cf::GV) * Cf::E;
+            v[i] = t < n ? *reinterpret_cast<const uint4 *>(static_cast<const IO *>(a.v) +
+                                                            (((size_t)b * a.T + t0 + t) * a.Hv + h) * D + col0 + g)
+                         : uint4{0u, 0u, 0u, 0u};
+        }
+    }
+    __device__ __forceinline__ void store(IO *sQ, IO *sK, IO *sV) const {
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int i = 0; i < Cf::NLD; ++i) {
+            const int idx = i * NTH + tid, t = idx / Cf::GR, g = (idx - t * Cf::GR) * Cf::E;
+            *reinterpret_cast<uint4 *>(sK + t * Cf::LQ + g) = k[i];
+            if constexpr (WITH_Q) *reinterpret_cast<uint4 *>(sQ + t * Cf::LQ + g) = q[i];
+        }
+#pragma unroll
+        for (int i = 0; i < Cf::NLV; ++i) {
+            const int idx = i * NTH + tid, t = idx / Cf::GV, g = (idx - t * Cf::GV) * Cf::E;
+            *reinterpret_cast<uint4 *>(sV + t * Cf::LV + g) = v[i];
+        }
+    }
+};
+
 // MODE 0: per-segment sums K^T V and colsum(K) into the workspace.
 // MODE 1: the sweep: outputs, and the final state from the last segment.
 template <typename IO, int D, int MODE>
 __global__ __launch_bounds__(NTH) void nla_chunks(NlaArgs a) {
     using M = Mma<IO>;
     using Cf = NlaCfg<IO, D>;
-    constexpr int E = Cf::E, LQ = Cf::LQ, LT = Cf::LT, KS = M::KS, NVT = D / VT, NSW = D / 32;
+    constexpr int LQ = Cf::LQ, LV = Cf::LV, LT = Cf::LT, KS = M::KS, NVT = D / VT, NSW = D / 32;
     extern __shared__ __align__(16) unsigned char smem[];
-    IO *sQ = reinterpret_cast<IO *>(smem + Cf::OQ), *sK = reinterpret_cast<IO *>(smem + Cf::OK);
-    IO *sKt = reinterpret_cast<IO *>(smem + Cf::OKT), *sVt = reinterpret_cast<IO *>(smem + Cf::OVT);
-    IO *sA = reinterpret_cast<IO *>(smem + Cf::OA), *sS = reinterpret_cast<IO *>(smem + Cf::OS);
-    float *sZ = reinterpret_cast<float *>(smem + Cf::OZ), *sDen = reinterpret_cast<float *>(smem + Cf::ODEN);
+    IO *sK = reinterpret_cast<IO *>(smem + Cf::OK), *sV = reinterpret_cast<IO *>(smem + Cf::OV);
+    float *sZ = reinterpret_cast<float *>(smem + Cf::OZ);
+    IO *sQ = reinterpret_cast<IO *>(smem + Cf::OQ), *sA = reinterpret_cast<IO *>(smem + Cf::OA);
+    IO *sS = reinterpret_cast<IO *>(smem + Cf::OS);
+    float *sDen = reinterpret_cast<float *>(smem + Cf::ODEN);
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
     int id = blockIdx.x;
     const int vt = id % NVT;
@@ -103,6 +181,8 @@ __global__ __launch_bounds__(NTH) void nla_chunks(NlaArgs a) {
     }
     int zb = 0;  // the z buffer holding z entering the chunk
 
+    ChunkRegs<IO, D, MODE == 1> rg;
+    if (c0 < c1) rg.load(a, b, hq, h, c0 * C, min(C, a.T - c0 * C), col0);
     for (int c = c0; c < c1; ++c) {
         const int t0 = c * C, n = min(C, a.T - t0);
         if constexpr (MODE == 1)  // S entering the chunk, transposed, as the operand of Q S
@@ -111,40 +191,8 @@ __global__ __launch_bounds__(NTH) void nla_chunks(NlaArgs a) {
                 const int dt = (w * NSW + i) >> 1, ct = (w * NSW + i) & 1;
                 put4<IO>(sS + (ct * 16 + lr) * LQ + dt * 16 + 4 * lg, Sacc[i]);
             }
-        // Load the chunk: phi(q) and phi(k) rows (and k channel-major), v's tile channel-major.
-        {
-            constexpr int GR = D / E, NLD = C * GR / NTH;
-            static_assert(C * GR % NTH == 0, "load mapping");
-#pragma unroll
-            for (int i = 0; i < NLD; ++i) {
-                const int idx = i * NTH + tid, t = idx / GR, g = (idx - t * GR) * E;
-                const size_t row = (((size_t)b * a.T + t0 + t) * a.Hqk + hq) * D + g;
-                uint4 kr = uint4{0u, 0u, 0u, 0u}, qr = uint4{0u, 0u, 0u, 0u};
-                if (t < n) {
-                    kr = *reinterpret_cast<const uint4 *>(static_cast<const IO *>(a.k) + row);
-                    if (MODE == 1) qr = *reinterpret_cast<const uint4 *>(static_cast<const IO *>(a.q) + row);
-                }
-                *reinterpret_cast<uint4 *>(sK + t * LQ + g) = kr;
-                if (MODE == 1) *reinterpret_cast<uint4 *>(sQ + t * LQ + g) = qr;
-                const IO *ke = reinterpret_cast<const IO *>(&kr);
-#pragma unroll
-                for (int e = 0; e < E; ++e) sKt[(g + e) * LT + t] = ke[e];
-            }
-            constexpr int GV = VT / E, NLV = (C * GV + NTH - 1) / NTH;
-#pragma unroll
-            for (int i = 0; i < NLV; ++i) {
-                const int idx = i * NTH + tid, t = idx / GV, g = (idx - t * GV) * E;
-                if (idx < C * GV) {
-                    uint4 vr = uint4{0u, 0u, 0u, 0u};
-                    if (t < n)
-                        vr = *reinterpret_cast<const uint4 *>(static_cast<const IO *>(a.v) +
-                                                              (((size_t)b * a.T + t0 + t) * a.Hv + h) * D + col0 + g);
-                    const IO *ve = reinterpret_cast<const IO *>(&vr);
-#pragma unroll
-                    for (int e = 0; e < E; ++e) sVt[(g + e) * LT + t] = ve[e];
-                }
-            }
-        }
+        rg.store(sQ, sK, sV);
+        if (c + 1 < c1) rg.load(a, b, hq, h, t0 + C, min(C, a.T - t0 - C), col0);  // in flight meanwhile
         __syncthreads();
 
         if constexpr (MODE == 1) {
@@ -187,7 +235,8 @@ __global__ __launch_bounds__(NTH) void nla_chunks(NlaArgs a) {
 #pragma unroll
                 for (int ks = 0; ks < D; ks += KS) acc = M::step(acc, sQ + 16 * w * LQ + ks, LQ, sS + ct * 16 * LQ + ks, LQ);
 #pragma unroll
-                for (int ks = 0; ks < C; ks += KS) acc = M::step(acc, sA + 16 * w * LT + ks, LT, sVt + ct * 16 * LT + ks, LT);
+                for (int ks = 0; ks < C; ks += KS)
+                    acc = M::mma(acc, M::load(sA + 16 * w * LT + ks, LT), KmRead<IO>::frag(sV + ks * LV + ct * 16, LV));
                 num[ct] = acc;
             }
             wave_sync();  // this block's rows of A are read: they take its output
@@ -200,7 +249,7 @@ __global__ __launch_bounds__(NTH) void nla_chunks(NlaArgs a) {
                     stage[tr * Cf::LO + ct * 16 + lr] = num[ct][r] / sDen[16 * w + tr];
                 }
             wave_sync();
-            constexpr int GO = VT / E, NST = 16 * GO / 64;
+            constexpr int E = Cf::E, GO = VT / E, NST = 16 * GO / 64;
 #pragma unroll
             for (int i = 0; i < (NST > 0 ? NST : 1); ++i) {
                 const int idx = i * 64 + l, tr = idx / GO, g = (idx - tr * GO) * E, tt = 16 * w + tr;
@@ -217,15 +266,18 @@ __global__ __launch_bounds__(NTH) void nla_chunks(NlaArgs a) {
         for (int i = 0; i < NSW; ++i) {
             const int dt = (w * NSW + i) >> 1, ct = (w * NSW + i) & 1;
 #pragma unroll
-            for (int ks = 0; ks < C; ks += KS) Sacc[i] = M::step(Sacc[i], sKt + dt * 16 * LT + ks, LT, sVt + ct * 16 * LT + ks, LT);
+            for (int ks = 0; ks < C; ks += KS)
+                Sacc[i] = M::mma(Sacc[i], KmRead<IO>::frag(sK + ks * LQ + dt * 16, LQ),
+                                 KmRead<IO>::frag(sV + ks * LV + ct * 16, LV));
         }
         if (tid < D) {
-            float s = sZ[zb * D + tid];
-            for (int t = 0; t < C; t += 4) {
-                const f32x4 kv = load4f(sKt + tid * LT + t);
-                s += (kv[0] + kv[1]) + (kv[2] + kv[3]);
+            float s0 = 0.f, s1 = 0.f;
+#pragma unroll 8
+            for (int t = 0; t < C; t += 2) {
+                s0 += Elem<IO>::load(sK + t * LQ + tid);
+                s1 += Elem<IO>::load(sK + (t + 1) * LQ + tid);
             }
-            sZ[(zb ^ 1) * D + tid] = s;
+            sZ[(zb ^ 1) * D + tid] = sZ[zb * D + tid] + (s0 + s1);
         }
         zb ^= 1;
         __syncthreads();  // the tiles, S^T and z are read before the next chunk overwrites them
@@ -280,28 +332,81 @@ __global__ __launch_bounds__(NTH) void nla_zsum(NlaArgs a) {
     a.zT[i] = a.z0[i] + s;
 }
 
+// The decode step: one workgroup per (sequence, V head). Thread (rg, cg)
+// holds rows RPT rg .. of the state's column group cg (4 columns), read and
+// written once with streaming accesses; q, k, v of the token and z in
+// shared memory. num_c = sum_i q_i (S_ic + k_i v_c), den = q . (z + k).
 template <typename IO, int D>
-hipError_t launch_t(const NlaArgs &a, hipStream_t s) {
+__global__ __launch_bounds__(NTH) void nla_decode(NlaArgs a) {
+    constexpr int CG = D / 4, RG = NTH / CG, RPT = D / RG;
+    static_assert(RG * RPT == D && RPT >= 1, "decode mapping");
+    __shared__ float sq[D], sk[D], sv[D], sz[D], spart[RG][D + 4], sden;
+    const int tid = threadIdx.x, cg = tid % CG, rgi = tid / CG;
+    const int bh = blockIdx.x, b = bh / a.Hv, h = bh - b * a.Hv, hq = h / (a.Hv / a.Hqk);
+    float *S = a.ST + (size_t)bh * D * D;
+    f32x4 st[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) st[m] = load_state4(S + (size_t)(rgi * RPT + m) * D + 4 * cg);
+    if (tid < D) {
+        sq[tid] = Elem<IO>::load(static_cast<const IO *>(a.q) + ((size_t)b * a.Hqk + hq) * D + tid);
+        sk[tid] = Elem<IO>::load(static_cast<const IO *>(a.k) + ((size_t)b * a.Hqk + hq) * D + tid);
+        sv[tid] = Elem<IO>::load(static_cast<const IO *>(a.v) + ((size_t)b * a.Hv + h) * D + tid);
+        sz[tid] = a.z0[(size_t)bh * D + tid];
+    }
+    __syncthreads();
+    if (tid < 64) {  // den = q . (z + k), one wave
+        float x = 0.f;
+        for (int i = tid; i < D; i += 64) x += sq[i] * (sz[i] + sk[i]);
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+        if (tid == 0) sden = x;
+    }
+    const f32x4 vc = load4f(sv + 4 * cg);
+    f32x4 part = zero4();
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const int i = rgi * RPT + m;
+        st[m] += sk[i] * vc;
+        part += sq[i] * st[m];
+        store_state4(S + (size_t)i * D + 4 * cg, st[m]);
+    }
+    store4f(&spart[rgi][4 * cg], part);
+    __syncthreads();
+    if (tid < D) {
+        float num = 0.f;
+#pragma unroll
+        for (int r = 0; r < RG; ++r) num += spart[r][tid];
+        static_cast<IO *>(a.o)[((size_t)b * a.Hv + h) * D + tid] = Elem<IO>::to(num / sden);
+        a.zT[(size_t)bh * D + tid] = sz[tid] + sk[tid];
+    }
+}
+
+template <typename IO, int D>
+hipError_t launch_t(const NlaArgs &a, bool decode, hipStream_t s) {
     using Cf = NlaCfg<IO, D>;
-    const size_t smem = Cf::BYTES;
     static const hipError_t attr_err = [] {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&nla_chunks<IO, D, 0>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cf::BYTES);
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cf::BYTES0);
         if (e == hipSuccess)
             e = hipFuncSetAttribute(reinterpret_cast<const void *>(&nla_chunks<IO, D, 1>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cf::BYTES);
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cf::BYTES1);
         return e;
     }();
     if (attr_err != hipSuccess) return attr_err;
+    if (decode) {
+        if ((long long)a.B * a.Hv > 0x7fffffffll) return hipErrorInvalidValue;
+        if (a.B * a.Hv > 0) hipLaunchKernelGGL((nla_decode<IO, D>), dim3((unsigned)(a.B * a.Hv)), dim3(NTH), 0, s, a);
+        return hipGetLastError();
+    }
     const long long items = (long long)a.B * a.Hv * a.P * (D / VT);
     if (items <= 0) return hipSuccess;
     if (items > 0x7fffffffll) return hipErrorInvalidValue;
     if (a.P > 1) {
-        hipLaunchKernelGGL((nla_chunks<IO, D, 0>), dim3((unsigned)items), dim3(NTH), smem, s, a);
+        hipLaunchKernelGGL((nla_chunks<IO, D, 0>), dim3((unsigned)items), dim3(NTH), Cf::BYTES0, s, a);
         const unsigned gx = (unsigned)(((size_t)D * D + D + NTH - 1) / NTH);
         hipLaunchKernelGGL((nla_scan<D>), dim3(gx, (unsigned)(a.B * a.Hv)), dim3(NTH), 0, s, a);
     }
-    hipLaunchKernelGGL((nla_chunks<IO, D, 1>), dim3((unsigned)items), dim3(NTH), smem, s, a);
+    hipLaunchKernelGGL((nla_chunks<IO, D, 1>), dim3((unsigned)items), dim3(NTH), Cf::BYTES1, s, a);
     if (a.z_apart) {
         const size_t nz = (size_t)a.B * a.Hv * D;
         hipLaunchKernelGGL((nla_zsum<IO, D>), dim3((unsigned)((nz + NTH - 1) / NTH)), dim3(NTH), 0, s, a);
@@ -311,15 +416,15 @@ hipError_t launch_t(const NlaArgs &a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_nla(int io, int D, const NlaArgs &a, hipStream_t s) {
+hipError_t launch_nla(int io, int D, const NlaArgs &a, bool decode, hipStream_t s) {
     if (io == IO_BF16) {
-        if (D == 32) return launch_t<bf16_t, 32>(a, s);
-        if (D == 64) return launch_t<bf16_t, 64>(a, s);
-        if (D == 128) return launch_t<bf16_t, 128>(a, s);
+        if (D == 32) return launch_t<bf16_t, 32>(a, decode, s);
+        if (D == 64) return launch_t<bf16_t, 64>(a, decode, s);
+        if (D == 128) return launch_t<bf16_t, 128>(a, decode, s);
     } else {
-        if (D == 32) return launch_t<float, 32>(a, s);
-        if (D == 64) return launch_t<float, 64>(a, s);
-        if (D == 128) return launch_t<float, 128>(a, s);
+        if (D == 32) return launch_t<float, 32>(a, decode, s);
+        if (D == 64) return launch_t<float, 64>(a, decode, s);
+        if (D == 128) return launch_t<float, 128>(a, decode, s);
     }
     return hipErrorInvalidValue;
 }

@@ -36,6 +36,7 @@ inline size_t nla_ws_bytes(int B, int Hv, int D, int NC) {
     return P > 1 ? (size_t)B * Hv * P * ((size_t)D * D + D) * sizeof(float) : 0;
 }
 
-hipError_t launch_nla(int io, int D, const NlaArgs &a, hipStream_t s);
+// decode: the one-token step (T = 1, ST = S0 and zT = z0 updated in place).
+hipError_t launch_nla(int io, int D, const NlaArgs &a, bool decode, hipStream_t s);
 
 }  // namespace gdr

@@ -39,6 +39,34 @@ def from_dev(t):
     return t.detach().cpu().numpy().astype(np.float64)
 
 
+def rms_rel_err(x, ref):
+    """Root-mean-square error over the root-mean-square of the reference:
+    unlike the max-normalised error it is not dominated by the largest
+    entries, so an error spread over small outputs shows."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert x.shape == ref.shape, (x.shape, ref.shape)
+    if not np.all(np.isfinite(x)):
+        return float("inf")
+    den = np.sqrt(np.mean(ref * ref)) if ref.size else 0.0
+    return float(np.sqrt(np.mean((x - ref) ** 2)) / (den if den > 0 else 1.0)) if ref.size else 0.0
+
+
+def out_err(x, ref):
+    """The bound the outputs o meet: both the max-normalised and the
+    RMS-relative error."""
+    return max(rel_err(x, ref), rms_rel_err(x, ref))
+
+
+def record(name, **pairs):
+    """Print the achieved errors of a parity case (max-normalised and
+    RMS-relative per tensor) on one line tagged PARITY."""
+    parts = []
+    for key, (x, ref) in pairs.items():
+        parts.append(f"{key}_max={rel_err(x, ref):.2e} {key}_rms={rms_rel_err(x, ref):.2e}")
+    say(f"PARITY {name} " + " ".join(parts))
+
+
 def rel_err(x, ref):
     x = np.asarray(x, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)

@@ -10,7 +10,8 @@ import pytest
 
 import gdr_synth as gs
 from parity_util import (TOL, from_dev, gpu_decode, gpu_prefill, gpu_prefill_in, gpu_recurrent, gpu_recurrent_in,
-                         oracle_input_stage, oracle_prefill, rel_err, say, small_workload, strong_channel_decay, to_dev)
+                         oracle_input_stage, oracle_prefill, out_err, record, rel_err, say, small_workload,
+                         strong_channel_decay, to_dev)
 
 torch = pytest.importorskip("torch")
 pytestmark = [pytest.mark.gpu,
@@ -33,7 +34,7 @@ def test_decode_small(io, D, decay, gates):
     say(f"decode {wl.name}")
     o_gpu, S_gpu = gpu_decode(inp)
     o_ref, S_ref = oracle_prefill(gs.as_sequence(inp))
-    assert rel_err(o_gpu, np.swapaxes(o_ref, 0, 1)) < TOL[io]
+    assert out_err(o_gpu, np.swapaxes(o_ref, 0, 1)) < TOL[io]
     assert rel_err(S_gpu, S_ref) < TOL[io]
 
 
@@ -47,7 +48,8 @@ def test_decode_qwen_shape_256_steps():
     o_gpu, S_gpu = gpu_decode(inp)
     heads = [0, 1, 2, 25, 47]
     o_ref, S_ref = oracle_prefill(gs.as_sequence(inp), heads=heads)
-    assert rel_err(o_gpu[:, :, heads], np.swapaxes(o_ref, 0, 1)[:, :, heads]) < TOL["bf16"]
+    record(wl.name, o=(o_gpu[:, :, heads], np.swapaxes(o_ref, 0, 1)[:, :, heads]), S=(S_gpu[:, heads], S_ref[:, heads]))
+    assert out_err(o_gpu[:, :, heads], np.swapaxes(o_ref, 0, 1)[:, :, heads]) < TOL["bf16"]
     assert rel_err(S_gpu[:, heads], S_ref[:, heads]) < TOL["bf16"]
     assert np.all(np.isfinite(S_gpu))
 
@@ -65,7 +67,7 @@ def test_prefill_small(io, D, decay, gates, T):
     S0 = to_dev(inp["S0"])
     o, ST = gpu_prefill(inp, S0=S0)
     o_ref, S_ref = oracle_prefill(inp)
-    assert rel_err(from_dev(o), o_ref) < TOL[io]
+    assert out_err(from_dev(o), o_ref) < TOL[io]
     assert rel_err(from_dev(ST), S_ref) < TOL[io]
 
 
@@ -79,7 +81,7 @@ def test_prefill_grouped_heads_and_scale(io, D):
     say(f"prefill {wl.name}")
     o, ST = gpu_prefill(inp, S0=to_dev(inp["S0"]))
     o_ref, S_ref = oracle_prefill(inp)
-    assert rel_err(from_dev(o), o_ref) < TOL[io]
+    assert out_err(from_dev(o), o_ref) < TOL[io]
     assert rel_err(from_dev(ST), S_ref) < TOL[io]
 
 
@@ -96,7 +98,7 @@ def test_prefill_strong_channel_decay(io, D, gates, T):
     say(f"prefill strong channel decay {wl.name}")
     o, ST = gpu_prefill(inp, S0=to_dev(inp["S0"]))
     o_ref, S_ref = oracle_prefill(inp)
-    assert rel_err(from_dev(o), o_ref) < TOL[io]
+    assert out_err(from_dev(o), o_ref) < TOL[io]
     assert rel_err(from_dev(ST), S_ref) < TOL[io]
 
 
@@ -113,7 +115,7 @@ def test_prefill_strong_channel_decay_segmented():
     say(f"prefill strong channel decay segmented {wl.name}")
     o, ST = gpu_prefill(inp, S0=to_dev(inp["S0"]))
     o_ref, S_ref = oracle_prefill(inp)
-    assert rel_err(from_dev(o), o_ref) < TOL["bf16"]
+    assert out_err(from_dev(o), o_ref) < TOL["bf16"]
     assert rel_err(from_dev(ST), S_ref) < TOL["bf16"]
 
 
@@ -138,7 +140,7 @@ def test_prefill_input_stage_strong_channel_decay(io, D, gates):
     say(f"prefill input stage strong channel decay {wl.name}")
     o, ST, cout = gpu_prefill_in(raw, S0=to_dev(raw["S0"]))
     o_ref, S_ref, c_ref = oracle_input_stage(raw)
-    assert rel_err(from_dev(o), o_ref) < TOL[io]
+    assert out_err(from_dev(o), o_ref) < TOL[io]
     assert rel_err(from_dev(ST), S_ref) < TOL[io]
     assert _conv_equal(cout, c_ref)
 
@@ -163,7 +165,7 @@ def test_prefill_in_stage_pass_strong_channel_decay(io, D, gates):
     say(f"prefill stage pass strong channel decay {wl.name}")
     o, ST, cout = gpu_prefill_in(raw, S0=to_dev(raw["S0"]))
     o_ref, S_ref, c_ref = oracle_input_stage(raw)
-    assert rel_err(from_dev(o), o_ref) < TOL[io]
+    assert out_err(from_dev(o), o_ref) < TOL[io]
     assert rel_err(from_dev(ST), S_ref) < TOL[io]
     assert _conv_equal(cout, c_ref)
 
@@ -177,7 +179,8 @@ def test_prefill_gdn_small_f32_full():
     say(f"prefill {wl.name}")
     o, ST = gpu_prefill(inp)
     o_ref, S_ref = oracle_prefill(inp)
-    assert rel_err(from_dev(o), o_ref) < TOL["f32"]
+    record(wl.name, o=(from_dev(o), o_ref), S=(from_dev(ST), S_ref))
+    assert out_err(from_dev(o), o_ref) < TOL["f32"]
     assert rel_err(from_dev(ST), S_ref) < TOL["f32"]
 
 
@@ -195,7 +198,8 @@ def test_prefill_full_size_sampled(wl, heads, cols):
     c0, c1 = cols if cols else (0, wl.dv)
     o_g = from_dev(o[:, :, heads, c0:c1])
     S_g = from_dev(ST[:, heads, :, c0:c1])
-    assert rel_err(o_g, o_ref[:, :, heads, c0:c1]) < TOL["bf16"]
+    record(wl.name, o=(o_g, o_ref[:, :, heads, c0:c1]), S=(S_g, S_ref[:, heads, :, c0:c1]))
+    assert out_err(o_g, o_ref[:, :, heads, c0:c1]) < TOL["bf16"]
     assert rel_err(S_g, S_ref[:, heads, :, c0:c1]) < TOL["bf16"]
     assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(ST).all())
 
@@ -230,7 +234,7 @@ def test_prefill_segmented_sweep(io, D, decay, gates, T, Hv, B):
     say(f"segmented {wl.name}")
     o, ST = gpu_prefill(inp, S0=to_dev(inp["S0"]))
     o_ref, S_ref = oracle_prefill(inp)
-    assert rel_err(from_dev(o), o_ref) < TOL[io]
+    assert out_err(from_dev(o), o_ref) < TOL[io]
     assert rel_err(from_dev(ST), S_ref) < TOL[io]
 
 
@@ -247,7 +251,7 @@ def test_prefill_segmented_sweep_in_place():
     o2, S2 = gpu_prefill(inp, S0=S, ST=S)
     assert torch.equal(o1, o2) and torch.equal(S, S1)
     o_ref, S_ref = oracle_prefill(inp)
-    assert rel_err(from_dev(o2), o_ref) < TOL["bf16"] and rel_err(from_dev(S), S_ref) < TOL["bf16"]
+    assert out_err(from_dev(o2), o_ref) < TOL["bf16"] and rel_err(from_dev(S), S_ref) < TOL["bf16"]
 
 
 # ---------------------------------------------------------------------------
@@ -390,7 +394,7 @@ def test_recurrent_small(io, D, decay, gates, T):
     say(f"recurrent {wl.name}")
     o, ST = gpu_recurrent(inp, S0=to_dev(inp["S0"]))
     o_ref, S_ref = oracle_prefill(inp)
-    assert rel_err(from_dev(o), o_ref) < TOL[io]
+    assert out_err(from_dev(o), o_ref) < TOL[io]
     assert rel_err(from_dev(ST), S_ref) < TOL[io]
 
 
@@ -412,7 +416,7 @@ def test_recurrent_many_heads(io, D, decay, gates, T):
     o, ST = gpu_recurrent(inp, S0=to_dev(inp["S0"]))
     heads = [0, 5, Hv // 2, Hv - 1]
     o_ref, S_ref = oracle_prefill(inp, heads=heads)
-    assert rel_err(from_dev(o[:, :, heads]), o_ref[:, :, heads]) < TOL[io]
+    assert out_err(from_dev(o[:, :, heads]), o_ref[:, :, heads]) < TOL[io]
     assert rel_err(from_dev(ST[:, heads]), S_ref[:, heads]) < TOL[io]
     assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(ST).all())
 
@@ -425,7 +429,7 @@ def test_recurrent_grouped_heads_strong_decay(io, D):
     say(f"recurrent {wl.name}")
     o, ST = gpu_recurrent(inp, S0=to_dev(inp["S0"]))
     o_ref, S_ref = oracle_prefill(inp)
-    assert rel_err(from_dev(o), o_ref) < TOL[io]
+    assert out_err(from_dev(o), o_ref) < TOL[io]
     assert rel_err(from_dev(ST), S_ref) < TOL[io]
 
 
@@ -441,7 +445,7 @@ def test_recurrent_equals_decode_steps_and_chunked():
     dec = dict(inp, **step_major)
     dec["workload"] = wl.scaled(decode=True)
     o_d, S_d = gpu_decode(dec)
-    assert rel_err(from_dev(o_r), np.swapaxes(o_d, 0, 1)) < 1e-5
+    assert out_err(from_dev(o_r), np.swapaxes(o_d, 0, 1)) < 1e-5
     assert rel_err(from_dev(S_r), S_d) < 1e-5
 
     wl = small_workload("bf16", 128, "scalar", "beta", T=100, B=1, Hqk=1, Hv=3, S0=True)
@@ -449,7 +453,7 @@ def test_recurrent_equals_decode_steps_and_chunked():
     S0 = to_dev(inp["S0"])
     o_r, S_r = gpu_recurrent(inp, S0=S0)
     o_c, S_c = gpu_prefill(inp, S0=S0)
-    assert rel_err(from_dev(o_r), from_dev(o_c)) < TOL["bf16"]
+    assert out_err(from_dev(o_r), from_dev(o_c)) < TOL["bf16"]
     assert rel_err(from_dev(S_r), from_dev(S_c)) < TOL["bf16"]
 
 
@@ -496,7 +500,7 @@ def test_recurrent_extreme_decay(io, decay, D):
     say(f"recurrent extreme decay {wl.name}")
     o, ST = gpu_recurrent(inp, S0=to_dev(inp["S0"]))
     o_ref, S_ref = oracle_prefill(inp)
-    assert rel_err(from_dev(o), o_ref) < TOL[io]
+    assert out_err(from_dev(o), o_ref) < TOL[io]
     assert rel_err(from_dev(ST), S_ref) < TOL[io]
 
 
@@ -564,7 +568,7 @@ def test_recurrent_input_stage_small(io, D, decay, gates, T):
     say(f"input stage {wl.name}")
     o, ST, cout = gpu_recurrent_in(raw, S0=to_dev(raw["S0"]))
     o_ref, S_ref, c_ref = oracle_input_stage(raw)
-    assert rel_err(from_dev(o), o_ref) < TOL[io]
+    assert out_err(from_dev(o), o_ref) < TOL[io]
     assert rel_err(from_dev(ST), S_ref) < TOL[io]
     assert _conv_equal(cout, c_ref)
 
@@ -575,7 +579,7 @@ def test_recurrent_input_stage_without_conv_state(io, D, decay, gates):
     raw = gs.make_raw_inputs(wl, seed=41, conv_state=False)
     o, ST, cout = gpu_recurrent_in(raw, conv_in=None)
     o_ref, S_ref, c_ref = oracle_input_stage(raw, conv_in=None)
-    assert rel_err(from_dev(o), o_ref) < TOL[io]
+    assert out_err(from_dev(o), o_ref) < TOL[io]
     assert rel_err(from_dev(ST), S_ref) < TOL[io]
     assert _conv_equal(cout, c_ref)
 
@@ -591,7 +595,7 @@ def test_recurrent_input_stage_serving_shape():
     o, ST, cout = gpu_recurrent_in(raw, S0=to_dev(raw["S0"]))
     heads = [0, 1, 2, 30, 47]
     o_ref, S_ref, c_ref = oracle_input_stage(raw, heads=heads)
-    assert rel_err(from_dev(o[:, :, heads]), o_ref[:, :, heads]) < TOL["bf16"]
+    assert out_err(from_dev(o[:, :, heads]), o_ref[:, :, heads]) < TOL["bf16"]
     assert rel_err(from_dev(ST[:, heads]), S_ref[:, heads]) < TOL["bf16"]
     assert _conv_equal(cout, c_ref)
 
@@ -639,7 +643,7 @@ def test_prefill_input_stage_small(io, D, decay, gates, T):
     say(f"prefill input stage {wl.name}")
     o, ST, cout = gpu_prefill_in(raw, S0=to_dev(raw["S0"]))
     o_ref, S_ref, c_ref = oracle_input_stage(raw)
-    assert rel_err(from_dev(o), o_ref) < TOL[io]
+    assert out_err(from_dev(o), o_ref) < TOL[io]
     assert rel_err(from_dev(ST), S_ref) < TOL[io]
     assert _conv_equal(cout, c_ref)
 
@@ -655,7 +659,7 @@ def test_prefill_input_stage_larger(io, D, decay, gates, T, Hqk, Hv, B):
     say(f"prefill input stage {wl.name}")
     o, ST, cout = gpu_prefill_in(raw, S0=to_dev(raw["S0"]), conv_in="stored" if T != 333 else None)
     o_ref, S_ref, c_ref = oracle_input_stage(raw, conv_in="stored" if T != 333 else None)
-    assert rel_err(from_dev(o), o_ref) < TOL[io]
+    assert out_err(from_dev(o), o_ref) < TOL[io]
     assert rel_err(from_dev(ST), S_ref) < TOL[io]
     assert _conv_equal(cout, c_ref)
 
@@ -671,7 +675,7 @@ def test_prefill_input_stage_qwen_full_size_sampled():
     torch.cuda.synchronize()
     heads = [0, 2, 25, 47]
     o_ref, S_ref, c_ref = oracle_input_stage(raw, heads=heads, S0=None)
-    assert rel_err(from_dev(o[:, :, heads]), o_ref[:, :, heads]) < TOL["bf16"]
+    assert out_err(from_dev(o[:, :, heads]), o_ref[:, :, heads]) < TOL["bf16"]
     assert rel_err(from_dev(ST[:, heads]), S_ref[:, heads]) < TOL["bf16"]
     assert _conv_equal(cout, c_ref)
 
@@ -688,7 +692,7 @@ def test_prefill_input_stage_wide_groups_sampled():
     torch.cuda.synchronize()
     heads = [0, 1, 6, 7]
     o_ref, S_ref, c_ref = oracle_input_stage(raw, heads=heads)
-    assert rel_err(from_dev(o[:, :, heads]), o_ref[:, :, heads]) < TOL["bf16"]
+    assert out_err(from_dev(o[:, :, heads]), o_ref[:, :, heads]) < TOL["bf16"]
     assert rel_err(from_dev(ST[:, heads]), S_ref[:, heads]) < TOL["bf16"]
     assert _conv_equal(cout, c_ref)
 
@@ -709,14 +713,14 @@ def test_prefill_input_stage_split_and_serving_handoff():
     assert rel_err(from_dev(S3), from_dev(S_all)) < TOL["bf16"]
     assert torch.equal(c3, c_all)
     o_r, S_r, c_r = gpu_recurrent_in(raw, S0=S0)
-    assert rel_err(from_dev(o_r), from_dev(o_all)) < TOL["bf16"]
+    assert out_err(from_dev(o_r), from_dev(o_all)) < TOL["bf16"]
     assert torch.equal(c_r, c_all)
     S = S2.clone()
     bufs = [c2.clone(), torch.empty_like(c2)]
     for t in range(200, 210):
         o, _, _ = gpu_recurrent_in(raw, S0=S, ST=S, conv_in=bufs[t % 2], conv_out=bufs[(t + 1) % 2],
                                    T_slice=slice(t, t + 1))
-        assert rel_err(from_dev(o), from_dev(o_all[:, t:t + 1])) < TOL["bf16"]
+        assert out_err(from_dev(o), from_dev(o_all[:, t:t + 1])) < TOL["bf16"]
     assert torch.equal(bufs[210 % 2], c_all)
     assert rel_err(from_dev(S), from_dev(S_all)) < TOL["bf16"]
 
@@ -762,9 +766,9 @@ def test_random_configurations(seed):
     o_ref, S_ref = oracle_prefill(inp)
     if io == "bf16" or D <= 64:
         o, ST = gpu_prefill(inp, S0=S0)
-        assert rel_err(from_dev(o), o_ref) < TOL[io] and rel_err(from_dev(ST), S_ref) < TOL[io]
+        assert out_err(from_dev(o), o_ref) < TOL[io] and rel_err(from_dev(ST), S_ref) < TOL[io]
     o, ST = gpu_recurrent(inp, S0=S0)
-    assert rel_err(from_dev(o), o_ref) < TOL[io] and rel_err(from_dev(ST), S_ref) < TOL[io]
+    assert out_err(from_dev(o), o_ref) < TOL[io] and rel_err(from_dev(ST), S_ref) < TOL[io]
     raw = gs.make_raw_inputs(wl, seed=seed, conv_state=bool(seed % 2))
     cin = "stored" if seed % 2 else None
     o_ref, S_ref, c_ref = oracle_input_stage(raw, conv_in=cin)
@@ -773,7 +777,7 @@ def test_random_configurations(seed):
     if io == "bf16" or D <= 64:
         runs.append(gpu_prefill_in(raw, S0=S0, conv_in=cin))
     for o, ST, cout in runs:
-        assert rel_err(from_dev(o), o_ref) < TOL[io] and rel_err(from_dev(ST), S_ref) < TOL[io]
+        assert out_err(from_dev(o), o_ref) < TOL[io] and rel_err(from_dev(ST), S_ref) < TOL[io]
         assert _conv_equal(cout, c_ref)
 
 
