@@ -9,15 +9,16 @@
 // stage already holds seven token-major tiles of the chunk, so there the
 // stage runs first, over the whole call, and writes the processed q, k, v,
 // the activated gates and the decay g into the call's workspace; the
-// prefill then runs on them as gdr_chunk_fwd does. Both passes stream: the
-// convolution reads each raw row plus the 3 rows before it (L2-resident),
-// and each processed row is written once.
+// prefill then runs on them as gdr_chunk_fwd does. Both passes stream: each
+// raw row is read once and each processed row written once.
 //
-//  stage_conv: one thread per 16-byte channel group of one (sequence, token,
-//    head) row of q, k or v; the D / V threads of a row are consecutive lanes,
-//    so the norm of q and k is a DPP all-reduce inside the wave. The thread of
-//    the last token also writes the outgoing convolution state (the last 3
-//    raw tokens, rows before the call taken from conv_in).
+//  stage_conv: one thread per 16-byte channel group of one (sequence, head)
+//    row of q, k or v and a run of 16 tokens, walked in order with the 3 rows
+//    before the current one kept in registers, so each raw row is read once
+//    (plus 3 rows before each run); the D / V threads of a row are
+//    consecutive lanes, so the norm of q and k is a DPP all-reduce inside the
+//    wave. The thread of the last run also writes the outgoing convolution
+//    state (the last 3 raw tokens, rows before the call taken from conv_in).
 //  stage_gates: elementwise g = -c_h softplus(x) (per channel), beta, b and w
 //    = sigmoid(x).
 #include "common.hpp"
@@ -27,6 +28,7 @@ namespace gdr {
 namespace {
 
 constexpr float kNormEps = 1e-12f;  // q, k = x / sqrt(|x|^2 + kNormEps)
+constexpr int kRun = 16;            // tokens per thread of the convolution
 
 template <typename IO> struct Vec16;  // 16 bytes of io elements, widened to float and back
 template <> struct Vec16<bf16_t> {
@@ -56,63 +58,89 @@ template <> struct Vec16<float> {
 template <typename IO, int D>
 __global__ __launch_bounds__(256) void stage_conv(StageArgs a) {
     using W = Vec16<IO>;
-    constexpr int V = W::N, CO = D / V, RPB = 256 / CO;  // channel groups per row, rows per workgroup
+    constexpr int V = W::N, CO = D / V;  // channel groups per row
     static_assert(64 % CO == 0, "a row's lanes lie in one wave");
-    const int tid = threadIdx.x, co = tid % CO;
-    const long long row = (long long)blockIdx.x * RPB + tid / CO;
-    const int NH = 2 * a.Hqk + a.Hv;
-    const long long rows = (long long)a.B * a.T * NH;
-    const bool valid = row < rows;
-    const long long r = valid ? row : rows - 1;  // lanes past the end repeat the last row and store nothing
-    const int hh = (int)(r % NH);
-    const long long bt = r / NH;
-    const int t = (int)(bt % a.T), b = (int)(bt / a.T);
-    // Tensor, its head count and head, and the channel in the concatenated
-    // (q, k, v) channel space of the taps and the convolution state.
+    const int NH = 2 * a.Hqk + a.Hv, NR = (a.T + kRun - 1) / kRun;
+    // Thread: channel group cg of head row hh (q heads, then k, then v) for
+    // the run of kRun tokens r kRun ..; lanes of a wave cover consecutive
+    // head rows of one run, so each step's loads and stores are contiguous.
+    const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long rows = (long long)a.B * NR * NH * CO;
+    const bool valid = gid < rows;
+    const long long g = valid ? gid : rows - 1;  // lanes past the end repeat the last group and store nothing
+    const int cg = (int)(g % CO);
+    const long long rh = g / CO;
+    const int hh = (int)(rh % NH);
+    const long long br = rh / NH;
+    const int run = (int)(br % NR), b = (int)(br / NR);
     const int x = hh < a.Hqk ? 0 : hh < 2 * a.Hqk ? 1 : 2;
     const int H = x == 2 ? a.Hv : a.Hqk, head = x == 2 ? hh - 2 * a.Hqk : hh - x * a.Hqk;
     const IO *src = static_cast<const IO *>(x == 0 ? a.q : x == 1 ? a.k : a.v);
     IO *dst = static_cast<IO *>(x == 0 ? a.qo : x == 1 ? a.ko : a.vo);
-    const size_t ch = (size_t)NH * D, c0 = (size_t)hh * D + V * co;
-    const auto at = [&](int tt) -> size_t { return (((size_t)b * a.T + tt) * H + head) * D + V * co; };
+    const size_t ch = (size_t)NH * D, c0 = (size_t)hh * D + V * cg;
+    const auto at = [&](int tt) -> size_t { return (((size_t)b * a.T + tt) * H + head) * D + V * cg; };
+    const int t0 = run * kRun, n = min(kRun, a.T - t0);
 
-    uint4 wnd[4];  // raw rows t-3 .. t of this channel group
+    f32x4 tp[V];  // this thread's channels' taps
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int tt = t - 3 + j;
+    for (int c = 0; c < V; ++c) tp[c] = load4f(a.conv_w + (c0 + c) * 4);
+    // The 3 raw rows before the run (from the incoming state, or zeros, before the sequence).
+    uint4 wnd[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        const int tt = t0 - 3 + j;
         wnd[j] = tt >= 0 ? *reinterpret_cast<const uint4 *>(src + at(tt))
                  : a.conv_in ? *reinterpret_cast<const uint4 *>(static_cast<const IO *>(a.conv_in) +
                                                                  ((size_t)b * 3 + 3 + tt) * ch + c0)
                              : uint4{0u, 0u, 0u, 0u};
     }
-    float xs[4][V], out[V];
+    uint4 raw[kRun];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) W::widen(wnd[j], xs[j]);
+    for (int j = 0; j < kRun; ++j) raw[j] = j < n ? *reinterpret_cast<const uint4 *>(src + at(t0 + j)) : uint4{0u, 0u, 0u, 0u};
+    float xs[3][V];
 #pragma unroll
-    for (int c = 0; c < V; ++c) {
-        const f32x4 tp = load4f(a.conv_w + (c0 + c) * 4);
-        out[c] = tp[0] * xs[0][c] + tp[1] * xs[1][c] + tp[2] * xs[2][c] + tp[3] * xs[3][c];
-    }
-    if (x < 2) {  // q and k: normalised over the head
-        float ss = 0.f;
+    for (int j = 0; j < 3; ++j) W::widen(wnd[j], xs[j]);
+    // wnd keeps the 3 raw rows before the next token: after the run, the
+    // sequence's last 3 when the run ends it.
 #pragma unroll
-        for (int c = 0; c < V; ++c) ss += out[c] * out[c];
-        if constexpr (CO == 32) {
-            ss = lanes_allreduce<16>(ss);
-            ss += __shfl_xor(ss, 16);
-        } else {
-            ss = lanes_allreduce<CO>(ss);
+    for (int j = 0; j < kRun; ++j) {
+        float cur[V], out[V];
+        W::widen(raw[j], cur);
+#pragma unroll
+        for (int c = 0; c < V; ++c) out[c] = tp[c][0] * xs[0][c] + tp[c][1] * xs[1][c] + tp[c][2] * xs[2][c] + tp[c][3] * cur[c];
+        if (x < 2) {  // q and k: normalised over the head
+            float ss = 0.f;
+#pragma unroll
+            for (int c = 0; c < V; ++c) ss += out[c] * out[c];
+            if constexpr (CO == 32) {
+                ss = lanes_allreduce<16>(ss);
+                ss += __shfl_xor(ss, 16);
+            } else {
+                ss = lanes_allreduce<CO>(ss);
+            }
+            const float f = 1.f / sqrtf(ss + kNormEps);
+#pragma unroll
+            for (int c = 0; c < V; ++c) out[c] *= f;
         }
-        const float f = 1.f / sqrtf(ss + kNormEps);
+        if (valid && j < n) *reinterpret_cast<uint4 *>(dst + at(t0 + j)) = W::pack(out);
 #pragma unroll
-        for (int c = 0; c < V; ++c) out[c] *= f;
+        for (int c = 0; c < V; ++c) {
+            xs[0][c] = xs[1][c];
+            xs[1][c] = xs[2][c];
+            xs[2][c] = cur[c];
+        }
+        if (j < n) {
+            wnd[0] = wnd[1];
+            wnd[1] = wnd[2];
+            wnd[2] = raw[j];
+        }
     }
-    if (valid) {
-        *reinterpret_cast<uint4 *>(dst + at(t)) = W::pack(out);
-        if (a.conv_out && t == a.T - 1)
+    // The outgoing convolution state: the sequence's last 3 raw rows (rows
+    // before the call come from the incoming state when T < 3).
+    if (valid && a.conv_out && t0 + n == a.T) {
+        IO *cout = static_cast<IO *>(a.conv_out) + (size_t)b * 3 * ch + c0;
 #pragma unroll
-            for (int j = 0; j < 3; ++j)
-                *reinterpret_cast<uint4 *>(static_cast<IO *>(a.conv_out) + ((size_t)b * 3 + j) * ch + c0) = wnd[1 + j];
+        for (int j = 0; j < 3; ++j) *reinterpret_cast<uint4 *>(cout + (size_t)j * ch) = wnd[j];
     }
 }
 
@@ -145,10 +173,10 @@ __global__ __launch_bounds__(256) void stage_gates(StageArgs a) {
 
 template <typename IO, int D>
 hipError_t launch_stage_t(const StageArgs &a, hipStream_t s) {
-    constexpr int CO = D / (16 / (int)sizeof(IO)), RPB = 256 / CO;
-    const long long rows = (long long)a.B * a.T * (2 * a.Hqk + a.Hv);
-    if (rows > 0) {
-        const long long grid = (rows + RPB - 1) / RPB;
+    constexpr int CO = D / (16 / (int)sizeof(IO));
+    const long long groups = (long long)a.B * ((a.T + kRun - 1) / kRun) * (2 * a.Hqk + a.Hv) * CO;
+    if (groups > 0) {
+        const long long grid = (groups + 255) / 256;
         if (grid > 0x7fffffffll) return hipErrorInvalidValue;
         hipLaunchKernelGGL((stage_conv<IO, D>), dim3((unsigned)grid), dim3(256), 0, s, a);
         const long long work = (long long)a.B * a.T * a.Hv * D / 4 + (a.beta ? (long long)a.B * a.T * a.Hv : 0);
