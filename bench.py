@@ -622,7 +622,7 @@ def main(argv=None):
                "decode": {"entry": "gdr_norm_la_decode_step", "workload": "norm_la_decode_B64_Hv48_d128_256steps",
                           "launch": "hip_graph", "steps": DS, "ms_per_step": nd_ms,
                           "tokens_per_s": DB / (nd_ms * 1e-3), "state_GBps": nd_state / (nd_ms * 1e-3) / 1e9,
-                          "roofline": {"kernel": "nla_chunks (one token) + nla_zsum", "bound": "hbm",
+                          "roofline": {"kernel": "nla_decode", "bound": "hbm",
                                        "achieved": nd_bytes / (nd_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
                                        "unit": "GB/s", "frac": nd_bytes / (nd_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                                        "traffic": recorded_traffic("norm_la_decode_B64_Hv48_d128_256steps", "norm_la"),
