@@ -16,10 +16,10 @@
 // each segment's chunks from its start state. Short sequences (or many
 // heads) run one segment and skip the first two launches.
 //
-// A workgroup owns (sequence, V head, segment, 32 value columns); its 4
-// waves each take one 16-token block of the chunk for A and O, and D / 32
-// of the 16 x 16 tiles of its d x 32 state, which stays in matrix-core
-// accumulators in fp32 for the whole segment. All products run on the
+// A workgroup owns (sequence, V head, segment, VT = 64 value columns; 32 at
+// d = 32); its 4 waves each take one 16-token block of the chunk for A and
+// O, and a quarter of the 16 x 16 tiles of its d x VT state, which stays in
+// matrix-core accumulators in fp32 for the whole segment. All products run on the
 // matrix cores: bf16 io on v_mfma_f32_16x16x32_bf16 (the state is rounded
 // to bf16 as an operand of Q S, A to bf16 as an operand of A V; the
 // normaliser is formed in fp32), fp32 io on v_mfma_f32_16x16x4_f32. The
@@ -40,7 +40,8 @@ namespace gdr {
 namespace {
 
 constexpr int C = 64;     // tokens per chunk
-constexpr int VT = 32;    // value columns per workgroup
+template <int D>
+constexpr int vtile() { return D >= 64 ? 64 : 32; }  // value columns per workgroup
 constexpr int NTH = 256;  // threads per workgroup
 
 // Operands read K-major from token-major shared memory: element (row r, k)
@@ -70,20 +71,22 @@ template <> struct KmRead<float> {
 
 // Shared-memory tiles (element type IO unless noted), token-major, rows
 // padded by 16 bytes: Q, K [C][LQ] (phi(q), phi(k)); V [C][LV] (this
-// workgroup's 32 value columns); A [C][LT]; S [VT][LQ] (the state entering
+// workgroup's VT value columns); A [C][LT]; S [VT][LQ] (the state entering
 // the chunk, transposed); z [2][D] fp32 (double-buffered); den [C] fp32.
 // The output of a 16-token block is staged in its own rows of A. The
 // segment-sum pass uses K and V only.
 template <typename IO, int D>
 struct NlaCfg {
     static constexpr int E = 16 / (int)sizeof(IO);  // elements per 16-byte access
+    static constexpr int VT = vtile<D>(), NCT = VT / 16;  // value columns; their 16-column tiles
+    static constexpr int NSW = D * VT / 1024;            // state tiles per wave (4 waves)
     static constexpr int LQ = D + E, LV = VT + E, LT = C + E;
     static constexpr size_t OK = 0, OV = OK + (size_t)C * LQ * sizeof(IO), OZ = OV + (size_t)C * LV * sizeof(IO),
                             OQ = OZ + 2 * (size_t)D * 4, OA = OQ + (size_t)C * LQ * sizeof(IO),
                             OS = OA + (size_t)C * LT * sizeof(IO), ODEN = OS + (size_t)VT * LQ * sizeof(IO),
                             BYTES0 = OQ, BYTES1 = ODEN + (size_t)C * 4;
-    static constexpr int LO = VT + 4;  // staged output row (floats)
-    static_assert((size_t)16 * LO * 4 <= (size_t)16 * LT * sizeof(IO), "a block's output fits its rows of A");
+    static constexpr int LO = VT + E;  // staged output row (io elements)
+    static_assert(LO <= LT, "a block's output fits its rows of A");
     static constexpr int GR = D / E, NLD = C * GR / NTH;   // 16-byte pieces of a q or k row; per thread
     static constexpr int GV = VT / E, NLV = C * GV / NTH;  // of a v row's tile; per thread
     static_assert(C * GR % NTH == 0 && C * GV % NTH == 0 && NLV >= 1, "load mapping");
@@ -106,6 +109,7 @@ __device__ __forceinline__ void wave_sync() {
 template <typename IO, int D, bool WITH_Q>
 struct ChunkRegs {
     using Cf = NlaCfg<IO, D>;
+    static constexpr int VT = Cf::VT;
     uint4 q[WITH_Q ? Cf::NLD : 1], k[Cf::NLD], v[Cf::NLV];
     __device__ __forceinline__ void load(const NlaArgs &a, int b, int hq, int h, int t0, int n, int col0) {
         const int tid = threadIdx.x;
@@ -147,7 +151,8 @@ template <typename IO, int D, int MODE>
 __global__ __launch_bounds__(NTH) void nla_chunks(NlaArgs a) {
     using M = Mma<IO>;
     using Cf = NlaCfg<IO, D>;
-    constexpr int LQ = Cf::LQ, LV = Cf::LV, LT = Cf::LT, KS = M::KS, NVT = D / VT, NSW = D / 32;
+    constexpr int LQ = Cf::LQ, LV = Cf::LV, LT = Cf::LT, KS = M::KS, VT = Cf::VT, NCT = Cf::NCT, NVT = D / VT,
+                  NSW = Cf::NSW;
     extern __shared__ __align__(16) unsigned char smem[];
     IO *sK = reinterpret_cast<IO *>(smem + Cf::OK), *sV = reinterpret_cast<IO *>(smem + Cf::OV);
     float *sZ = reinterpret_cast<float *>(smem + Cf::OZ);
@@ -155,22 +160,33 @@ __global__ __launch_bounds__(NTH) void nla_chunks(NlaArgs a) {
     IO *sS = reinterpret_cast<IO *>(smem + Cf::OS);
     float *sDen = reinterpret_cast<float *>(smem + Cf::ODEN);
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
-    int id = blockIdx.x;
+    // Work items in the order value tile, V head of the QK group, segment,
+    // (sequence, QK head), so that the items sharing one QK head's rows are
+    // consecutive; the grid is a multiple of 8 and consecutive items go to
+    // the same XCD (workgroups are dealt to the 8 XCDs in turn), whose L2
+    // then serves those rows to all of them.
+    const int grp = a.Hv / a.Hqk;
+    const int x = blockIdx.x, wi = (x & 7) * (int)(gridDim.x >> 3) + (x >> 3);
+    if (wi >= a.B * a.Hv * a.P * NVT) return;
+    int id = wi;
     const int vt = id % NVT;
     id /= NVT;
-    const int seg = id % a.P, bh = id / a.P, b = bh / a.Hv, h = bh - b * a.Hv, hq = h / (a.Hv / a.Hqk);
+    const int hg = id % grp;
+    id /= grp;
+    const int seg = id % a.P, bq = id / a.P, b = bq / a.Hqk, hq = bq - b * a.Hqk, h = hq * grp + hg;
+    const int bh = b * a.Hv + h;
     if (MODE == 0 && seg == a.P - 1) return;  // the last segment's sum is not needed
     const int c0 = seg * a.L, c1 = min(a.NC, c0 + a.L), col0 = vt * VT;
     const size_t slab = (size_t)D * D + D;
     float *wseg = a.ws ? a.ws + ((size_t)bh * a.P + seg) * slab : nullptr;
 
     // This wave's state tiles: tile i is rows 16 * dt.., columns 16 * ct.. of
-    // the D x VT tile, (dt, ct) = ((w NSW + i) / 2, (w NSW + i) % 2).
+    // the D x VT tile, (dt, ct) = ((w NSW + i) / NCT, (w NSW + i) % NCT).
     f32x4 Sacc[NSW];
     const float *Sst = MODE == 1 ? (a.P > 1 ? wseg : a.S0 ? a.S0 + (size_t)bh * D * D : nullptr) : nullptr;
 #pragma unroll
     for (int i = 0; i < NSW; ++i) {
-        const int dt = (w * NSW + i) >> 1, ct = (w * NSW + i) & 1;
+        const int dt = (w * NSW + i) / NCT, ct = (w * NSW + i) % NCT;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             Sacc[i][r] = Sst ? Sst[(size_t)(dt * 16 + 4 * lg + r) * D + col0 + ct * 16 + lr] : 0.f;
@@ -188,7 +204,7 @@ __global__ __launch_bounds__(NTH) void nla_chunks(NlaArgs a) {
         if constexpr (MODE == 1)  // S entering the chunk, transposed, as the operand of Q S
 #pragma unroll
             for (int i = 0; i < NSW; ++i) {
-                const int dt = (w * NSW + i) >> 1, ct = (w * NSW + i) & 1;
+                const int dt = (w * NSW + i) / NCT, ct = (w * NSW + i) % NCT;
                 put4<IO>(sS + (ct * 16 + lr) * LQ + dt * 16 + 4 * lg, Sacc[i]);
             }
         rg.store(sQ, sK, sV);
@@ -227,10 +243,10 @@ __global__ __launch_bounds__(NTH) void nla_chunks(NlaArgs a) {
             den += __shfl_xor(den, 32);
             if (lg == 0) sDen[t] = den;
             wave_sync();
-            // O rows of block w: (Q S + A V) / den, two 16-column tiles.
-            f32x4 num[2];
+            // O rows of block w: (Q S + A V) / den, NCT 16-column tiles.
+            f32x4 num[NCT];
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
+            for (int ct = 0; ct < NCT; ++ct) {
                 f32x4 acc = zero4();
 #pragma unroll
                 for (int ks = 0; ks < D; ks += KS) acc = M::step(acc, sQ + 16 * w * LQ + ks, LQ, sS + ct * 16 * LQ + ks, LQ);
@@ -240,31 +256,28 @@ __global__ __launch_bounds__(NTH) void nla_chunks(NlaArgs a) {
                 num[ct] = acc;
             }
             wave_sync();  // this block's rows of A are read: they take its output
-            float *stage = reinterpret_cast<float *>(sA + 16 * w * LT);
+            IO *stage = sA + 16 * w * LT;
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
+            for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int tr = 4 * lg + r;
-                    stage[tr * Cf::LO + ct * 16 + lr] = num[ct][r] / sDen[16 * w + tr];
+                    stage[tr * Cf::LO + ct * 16 + lr] = Elem<IO>::to(num[ct][r] / sDen[16 * w + tr]);
                 }
             wave_sync();
-            constexpr int E = Cf::E, GO = VT / E, NST = 16 * GO / 64;
+            constexpr int E = Cf::E, GO = VT / E, NST = (16 * GO + 63) / 64;
 #pragma unroll
-            for (int i = 0; i < (NST > 0 ? NST : 1); ++i) {
+            for (int i = 0; i < NST; ++i) {
                 const int idx = i * 64 + l, tr = idx / GO, g = (idx - tr * GO) * E, tt = 16 * w + tr;
-                if (idx < 16 * GO && tt < n) {
-                    IO *dst = static_cast<IO *>(a.o) + (((size_t)b * a.T + t0 + tt) * a.Hv + h) * D + col0 + g;
-                    const float *src = stage + tr * Cf::LO + g;
-#pragma unroll
-                    for (int e = 0; e < E; e += 4) put4<IO>(dst + e, load4f(src + e));
-                }
+                if (idx < 16 * GO && tt < n)
+                    *reinterpret_cast<uint4 *>(static_cast<IO *>(a.o) + (((size_t)b * a.T + t0 + tt) * a.Hv + h) * D +
+                                               col0 + g) = *reinterpret_cast<const uint4 *>(stage + tr * Cf::LO + g);
             }
         }
         // S += K^T V on this wave's state tiles; z += colsum(K) into the other buffer.
 #pragma unroll
         for (int i = 0; i < NSW; ++i) {
-            const int dt = (w * NSW + i) >> 1, ct = (w * NSW + i) & 1;
+            const int dt = (w * NSW + i) / NCT, ct = (w * NSW + i) % NCT;
 #pragma unroll
             for (int ks = 0; ks < C; ks += KS)
                 Sacc[i] = M::mma(Sacc[i], KmRead<IO>::frag(sK + ks * LQ + dt * 16, LQ),
@@ -288,7 +301,7 @@ __global__ __launch_bounds__(NTH) void nla_chunks(NlaArgs a) {
     if (Sdst) {
 #pragma unroll
         for (int i = 0; i < NSW; ++i) {
-            const int dt = (w * NSW + i) >> 1, ct = (w * NSW + i) & 1;
+            const int dt = (w * NSW + i) / NCT, ct = (w * NSW + i) % NCT;
 #pragma unroll
             for (int r = 0; r < 4; ++r) Sdst[(size_t)(dt * 16 + 4 * lg + r) * D + col0 + ct * 16 + lr] = Sacc[i][r];
         }
@@ -310,11 +323,15 @@ __global__ __launch_bounds__(NTH) void nla_scan(NlaArgs a) {
     float acc = e < (size_t)D * D ? (a.S0 ? a.S0[(size_t)bh * D * D + e] : 0.f)
                                   : (a.z0 ? a.z0[(size_t)bh * D + (e - (size_t)D * D)] : 0.f);
     float *p = a.ws + (size_t)bh * a.P * slab + e;
-    for (int s = 0; s < a.P; ++s) {
-        const float x = s < a.P - 1 ? p[(size_t)s * slab] : 0.f;
-        p[(size_t)s * slab] = acc;
-        acc += x;
-    }
+    float x[32];  // the segments' sums (P <= 32), read before any is overwritten
+#pragma unroll
+    for (int s = 0; s < 32; ++s) x[s] = s < a.P - 1 ? p[(size_t)s * slab] : 0.f;
+#pragma unroll
+    for (int s = 0; s < 32; ++s)
+        if (s < a.P) {
+            p[(size_t)s * slab] = acc;
+            acc += x[s];
+        }
 }
 
 // z_T = z0 + the sum of the call's phi(k) rows, one thread per (sequence, V
@@ -398,15 +415,16 @@ hipError_t launch_t(const NlaArgs &a, bool decode, hipStream_t s) {
         if (a.B * a.Hv > 0) hipLaunchKernelGGL((nla_decode<IO, D>), dim3((unsigned)(a.B * a.Hv)), dim3(NTH), 0, s, a);
         return hipGetLastError();
     }
-    const long long items = (long long)a.B * a.Hv * a.P * (D / VT);
+    const long long items = (long long)a.B * a.Hv * a.P * (D / Cf::VT);
     if (items <= 0) return hipSuccess;
-    if (items > 0x7fffffffll) return hipErrorInvalidValue;
+    if (items > 0x7ffffff0ll) return hipErrorInvalidValue;
+    const unsigned grid = (unsigned)((items + 7) / 8 * 8);
     if (a.P > 1) {
-        hipLaunchKernelGGL((nla_chunks<IO, D, 0>), dim3((unsigned)items), dim3(NTH), Cf::BYTES0, s, a);
+        hipLaunchKernelGGL((nla_chunks<IO, D, 0>), dim3(grid), dim3(NTH), Cf::BYTES0, s, a);
         const unsigned gx = (unsigned)(((size_t)D * D + D + NTH - 1) / NTH);
         hipLaunchKernelGGL((nla_scan<D>), dim3(gx, (unsigned)(a.B * a.Hv)), dim3(NTH), 0, s, a);
     }
-    hipLaunchKernelGGL((nla_chunks<IO, D, 1>), dim3((unsigned)items), dim3(NTH), Cf::BYTES1, s, a);
+    hipLaunchKernelGGL((nla_chunks<IO, D, 1>), dim3(grid), dim3(NTH), Cf::BYTES1, s, a);
     if (a.z_apart) {
         const size_t nz = (size_t)a.B * a.Hv * D;
         hipLaunchKernelGGL((nla_zsum<IO, D>), dim3((unsigned)((nz + NTH - 1) / NTH)), dim3(NTH), 0, s, a);
