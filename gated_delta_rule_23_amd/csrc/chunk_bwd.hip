@@ -510,13 +510,49 @@ __device__ __forceinline__ f32x4 mfma_kloop_at(f32x4 acc, const float *At, int l
     return acc + acc2;
 }
 
+// The same as accumulation over k in [K0, K1) into two chains (acc over k =
+// K0, K0 + 8, ...; acc2 over k = K0 + 4, ...), so that a product can be split
+// into pieces with other work between them; the pieces of mfma_kloop's
+// range in order give its sums exactly.
+template <int K0, int K1>
+__device__ __forceinline__ void mfma_krange(f32x4 &acc, f32x4 &acc2, const float *A, int lda, const float *B,
+                                            int ldb) {
+    const int l = threadIdx.x & 63;
+    const float *pa = A + (l & 15) * lda + (l >> 4), *pb = B + (l >> 4) * ldb + (l & 15);
+#pragma unroll
+    for (int k = K0; k < K1; k += 8) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[k], pb[k * ldb], acc, 0, 0, 0);
+        acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[k + 4], pb[(k + 4) * ldb], acc2, 0, 0, 0);
+    }
+}
+template <int K0, int K1>
+__device__ __forceinline__ void mfma_krange_at(f32x4 &acc, f32x4 &acc2, const float *At, int ldat, const float *B,
+                                               int ldb) {
+    const int l = threadIdx.x & 63;
+    const float *pa = At + (l >> 4) * ldat + (l & 15), *pb = B + (l >> 4) * ldb + (l & 15);
+#pragma unroll
+    for (int k = K0; k < K1; k += 8) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[k * ldat], pb[k * ldb], acc, 0, 0, 0);
+        acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[(k + 4) * ldat], pb[(k + 4) * ldb], acc2, 0, 0, 0);
+    }
+}
+
+// f(integral_constant<I>) for I = I0 .. I1 - 1, in order.
+template <int I0, int I1, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (I0 < I1) {
+        f(std::integral_constant<int, I0>{});
+        static_for<I0 + 1, I1>(f);
+    }
+}
+
 // 2a. Forward over chunks: the state entering each chunk, and U = U_z - Y S.
 //    Wave w: U tile (rows 16 (w / 2), columns 16 (w % 2)); state tiles w and
 //    w + 8 of the (D / 16) x 2 tiles of the state.
 template <int D>
 __device__ __forceinline__ void fsweep(const ChunkBwdArgs &a, float *smem, int item) {
     using K = SwCfg<D>;
-    constexpr int NTL = K::NTL, NL = K::NL, LD = D + 4, NST = D / 16 * 2;
+    constexpr int NTL = K::NTL, NL = K::NL, NST = D / 16 * 2;
     float *sS = smem, *sU = sS + D * LB, *sYt = sU + C * LB, *sKt = sYt + D * LT;  // Y^T [D][LT], Kend^T [D][LC]
     float *sGam = sKt + D * LC;
     const int tid = threadIdx.x, tile = item % NTL, bh = item / NTL, col0 = tile * BV;
@@ -526,23 +562,38 @@ __device__ __forceinline__ void fsweep(const ChunkBwdArgs &a, float *smem, int i
         const int d = 4 * i / BV, j = 4 * i - d * BV;
         sts4(sS + d * LB + j, a.S0 ? lds4(a.S0 + sb + (size_t)d * D + col0 + j) : zero4());
     }
+    // The next chunk's operands, numbered -- Y^T (NL per thread), this
+    // thread's 4 entries of U_z, Gamma (1), Kend^T (NL) -- and spread over
+    // the current chunk's products as in the backward sweep.
     f32x4 pY[NL], pK[NL];
     float pZ[4], pg;
-    const auto fetch = [&](int c) {
+    constexpr int NLD = 2 * NL + 4 + 1;
+    const auto load = [&](auto ic, int c) {
+        constexpr int i = decltype(ic)::value;
         const size_t u = (size_t)bh * a.NC + c, ucd = u * C * D;
-#pragma unroll
-        for (int l2 = 0; l2 < NL; ++l2) {
-            const int e = 4 * (l2 * NS + tid);
-            pY[l2] = lds4(a.wYt + ucd + e);   // [D][C]
-            pK[l2] = lds4(a.wKet + ucd + e);  // [D][C]
+        if constexpr (i < NL) {
+            pY[i] = lds4(a.wYt + ucd + 4 * (i * NS + tid));  // [D][C]
+        } else if constexpr (i < NL + 4) {
+            constexpr int r = i - NL;
+            pZ[r] = a.wUz[ucd + (size_t)(rt * 16 + 4 * (l >> 4) + r) * D + col0 + ct * 16 + (l & 15)];
+        } else if constexpr (i == NL + 4) {
+            pg = tid < D ? a.wGam[u * D + tid] : 0.f;
+        } else {
+            pK[i - (NL + 5)] = lds4(a.wKet + ucd + 4 * ((i - (NL + 5)) * NS + tid));  // [D][C]
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) pZ[r] = a.wUz[ucd + (size_t)(rt * 16 + 4 * (l >> 4) + r) * D + col0 + ct * 16 + (l & 15)];
-        pg = tid < D ? a.wGam[u * D + tid] : 0.f;
     };
-    fetch(0);
+    constexpr int NXT = NST > 8 ? 2 : 1;  // state tiles per wave
+    constexpr int NG = D / 32 + NXT * (C / 32);
+    const auto spread = [&](auto gc, int c) {
+        constexpr int g = decltype(gc)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<g * NLD / NG, (g + 1) * NLD / NG>([&](auto ic) { load(ic, c); });
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    static_for<0, NLD>([&](auto ic) { load(ic, 0); });
     for (int c = 0; c < a.NC; ++c) {
         const size_t u = (size_t)bh * a.NC + c, ucd = u * C * D;
+        const int cn = c + 1 < a.NC ? c + 1 : c;  // the chunk fetched during this one (the last one's loads go unused)
         lds_barrier();  // the previous chunk is done with the operand tiles; S written
 #pragma unroll
         for (int l2 = 0; l2 < NL; ++l2) {
@@ -555,14 +606,19 @@ __device__ __forceinline__ void fsweep(const ChunkBwdArgs &a, float *smem, int i
         float uz[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) uz[r] = pZ[r];
-        if (c + 1 < a.NC) fetch(c + 1);
         for (int i = tid; i < D * BV / 4; i += NS) {
             const int d = 4 * i / BV, j = 4 * i - d * BV;
             sts4(a.wS + u * D * D + (size_t)d * D + col0 + j, lds4(sS + d * LB + j));
         }
         lds_barrier();
         {  // U = U_z - Y S
-            const f32x4 p = mfma_kloop_at<D>(zero4(), sYt + rt * 16, LT, sS + ct * 16, LB);
+            f32x4 p0 = zero4(), p1 = zero4();
+            static_for<0, D / 32>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                mfma_krange_at<32 * j, 32 * j + 32>(p0, p1, sYt + rt * 16, LT, sS + ct * 16, LB);
+                spread(jc, cn);
+            });
+            const f32x4 p = p0 + p1;
             const int col = ct * 16 + (l & 15);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -574,23 +630,30 @@ __device__ __forceinline__ void fsweep(const ChunkBwdArgs &a, float *smem, int i
         }
         lds_barrier();
         // S = Gamma . S + Kend^T U
-        f32x4 sn[2];
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        f32x4 sn[NXT];
+        static_for<0, NXT>([&](auto qc) {
+            constexpr int q = decltype(qc)::value;
             const int st = w + 8 * q, dt = st >> 1, sc = st & 1;
-            if (st < NST) {
-                const f32x4 p = mfma_kloop<C>(zero4(), sKt + dt * 16 * LC, LC, sU + sc * 16, LB);
+            const bool on = st < NST;
+            f32x4 p0 = zero4(), p1 = zero4();
+            static_for<0, C / 32>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                if (on) mfma_krange<32 * j, 32 * j + 32>(p0, p1, sKt + dt * 16 * LC, LC, sU + sc * 16, LB);
+                spread(std::integral_constant<int, D / 32 + q * (C / 32) + j>{}, cn);
+            });
+            if (on) {
+                const f32x4 p = p0 + p1;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = dt * 16 + 4 * (l >> 4) + r;
                     sn[q][r] = sGam[row] * sS[row * LB + sc * 16 + (l & 15)] + p[r];
                 }
             }
-        }
+        });
         // No barrier: each wave rewrites only the state entries it has just
         // read, and every other read of S in this chunk was before the last one.
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        for (int q = 0; q < NXT; ++q) {
             const int st = w + 8 * q, dt = st >> 1, sc = st & 1;
             if (st < NST)
 #pragma unroll
@@ -604,7 +667,7 @@ __device__ __forceinline__ void fsweep(const ChunkBwdArgs &a, float *smem, int i
 template <typename IO, int D>
 __device__ __forceinline__ void bsweep(const ChunkBwdArgs &a, float *smem, int item) {
     using K = SwCfg<D>;
-    constexpr int NTL = K::NTL, NL = K::NL, LD = D + 4, NST = D / 16 * 2;
+    constexpr int NTL = K::NTL, NL = K::NL, NST = D / 16 * 2;
     constexpr int NA = C * C / (4 * NS), NO = C * BV / (4 * NS);  // 4-element groups per thread: A, dO tile
     float *sX = smem, *sO = sX + D * LB, *sdU = sO + C * LB;
     float *sA = sdU + C * LB;    // A [C][LT]
@@ -620,31 +683,49 @@ __device__ __forceinline__ void bsweep(const ChunkBwdArgs &a, float *smem, int i
         const int d = 4 * i / BV, j = 4 * i - d * BV;
         sts4(sX + d * LB + j, a.dST ? lds4(a.dST + sb + (size_t)d * D + col0 + j) : zero4());
     }
+    // A chunk's operands, fetched by the whole workgroup one chunk ahead. The
+    // loads are numbered -- Kend^T (NL per thread), A (NA), the dO tile (NO),
+    // Gamma (1), Y^T (NL), Q~^T (NL) -- and spread over the pieces of the
+    // current chunk's products, so that their latency overlaps the matrix
+    // cores' work rather than stalling every wave at once.
     f32x4 pY[NL], pK[NL], pQ[NL], pA[NA], pO[NO];
     float pg;
-    const auto fetch = [&](int c) {
+    constexpr int NLD = 3 * NL + NA + NO + 1;
+    const auto load = [&](auto ic, int c) {
+        constexpr int i = decltype(ic)::value;
         const size_t u = (size_t)bh * a.NC + c, ucd = u * C * D;
-        const int t0 = c * C, n = min(C, a.T - t0);
-#pragma unroll
-        for (int l2 = 0; l2 < NL; ++l2) {
-            const int e = 4 * (l2 * NS + tid);
-            pY[l2] = lds4(a.wYt + ucd + e);   // [D][C]
-            pK[l2] = lds4(a.wKet + ucd + e);  // [D][C]
-            pQ[l2] = lds4(a.wQt + ucd + e);   // [D][C]
-        }
-#pragma unroll
-        for (int l2 = 0; l2 < NA; ++l2) pA[l2] = lds4(a.wA + u * C * C + 4 * (l2 * NS + tid));
-#pragma unroll
-        for (int l2 = 0; l2 < NO; ++l2) {
+        if constexpr (i < NL) {
+            pK[i] = lds4(a.wKet + ucd + 4 * (i * NS + tid));  // [D][C]
+        } else if constexpr (i < NL + NA) {
+            pA[i - NL] = lds4(a.wA + u * C * C + 4 * ((i - NL) * NS + tid));
+        } else if constexpr (i < NL + NA + NO) {
+            const int t0 = c * C, n = min(C, a.T - t0);
             int e, t, j;
-            rcs<BV>(l2, e, t, j);
-            pO[l2] = t < n ? ld4io<IO>(a.dO, (((size_t)b * a.T + t0 + t) * a.Hv + h) * D + col0 + j) : zero4();
+            rcs<BV>(i - NL - NA, e, t, j);
+            pO[i - NL - NA] = t < n ? ld4io<IO>(a.dO, (((size_t)b * a.T + t0 + t) * a.Hv + h) * D + col0 + j) : zero4();
+        } else if constexpr (i == NL + NA + NO) {
+            pg = tid < D ? a.wGam[u * D + tid] : 0.f;
+        } else if constexpr (i < 2 * NL + NA + NO + 1) {
+            pY[i - (NL + NA + NO + 1)] = lds4(a.wYt + ucd + 4 * ((i - (NL + NA + NO + 1)) * NS + tid));  // [D][C]
+        } else {
+            pQ[i - (2 * NL + NA + NO + 1)] = lds4(a.wQt + ucd + 4 * ((i - (2 * NL + NA + NO + 1)) * NS + tid));  // [D][C]
         }
-        pg = tid < D ? a.wGam[u * D + tid] : 0.f;
     };
-    fetch(a.NC - 1);
+    // The chunk's products run in NG pieces of 8 matrix instructions; after
+    // piece g come loads [g NLD / NG, (g + 1) NLD / NG), fenced so that the
+    // compiler keeps them there.
+    constexpr int NXT = NST > 8 ? 2 : 1;  // X tiles per wave
+    constexpr int NG = C / 32 + D / 32 + NXT * 2 * (C / 32);
+    const auto spread = [&](auto gc, int c) {
+        constexpr int g = decltype(gc)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<g * NLD / NG, (g + 1) * NLD / NG>([&](auto ic) { load(ic, c); });
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    static_for<0, NLD>([&](auto ic) { load(ic, a.NC - 1); });
     for (int c = a.NC - 1; c >= 0; --c) {
         const size_t u = (size_t)bh * a.NC + c, ucd = u * C * D;
+        const int cn = c > 0 ? c - 1 : 0;  // the chunk fetched during this one (at c = 0 the loads go unused)
         lds_barrier();  // X written; the previous chunk is done with the operand tiles
 #pragma unroll
         for (int l2 = 0; l2 < NL; ++l2) {
@@ -667,15 +748,24 @@ __device__ __forceinline__ void bsweep(const ChunkBwdArgs &a, float *smem, int i
             sts4(sO + t * LB + j, pO[l2]);
         }
         if (tid < D) sGam[tid] = pg;
-        if (c > 0) fetch(c - 1);
         for (int i = tid; i < D * BV / 4; i += NS) {
             const int d = 4 * i / BV, j = 4 * i - d * BV;
             sts4(a.wdS + u * D * D + (size_t)d * D + col0 + j, lds4(sX + d * LB + j));
         }
         lds_barrier();
         {  // dU = s A^T dO + Kend X
-            const f32x4 p = mfma_kloop_at<C>(zero4(), sA + rt * 16, LT, sO + ct * 16, LB);
-            const f32x4 k = mfma_kloop_at<D>(zero4(), sKt + rt * 16, LC, sX + ct * 16, LB);
+            f32x4 p0 = zero4(), p1 = zero4(), k0 = zero4(), k1 = zero4();
+            static_for<0, C / 32>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                mfma_krange_at<32 * j, 32 * j + 32>(p0, p1, sA + rt * 16, LT, sO + ct * 16, LB);
+                spread(std::integral_constant<int, j>{}, cn);
+            });
+            static_for<0, D / 32>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                mfma_krange_at<32 * j, 32 * j + 32>(k0, k1, sKt + rt * 16, LC, sX + ct * 16, LB);
+                spread(std::integral_constant<int, C / 32 + j>{}, cn);
+            });
+            const f32x4 p = p0 + p1, k = k0 + k1;
             const int col = ct * 16 + (l & 15);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -687,24 +777,35 @@ __device__ __forceinline__ void bsweep(const ChunkBwdArgs &a, float *smem, int i
         }
         lds_barrier();
         // X = Gamma . X + s Q~^T dO - Y^T dU
-        f32x4 xn[2];
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        f32x4 xn[NXT];
+        static_for<0, NXT>([&](auto qc) {
+            constexpr int q = decltype(qc)::value;
             const int st = w + 8 * q, dt = st >> 1, sc = st & 1;
-            if (st < NST) {
-                const f32x4 pq = mfma_kloop<C>(zero4(), sQt + dt * 16 * LC, LC, sO + sc * 16, LB);
-                const f32x4 py = mfma_kloop<C>(zero4(), sYt + dt * 16 * LC, LC, sdU + sc * 16, LB);
+            const bool on = st < NST;
+            f32x4 q0 = zero4(), q1 = zero4(), y0 = zero4(), y1 = zero4();
+            static_for<0, C / 32>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                if (on) mfma_krange<32 * j, 32 * j + 32>(q0, q1, sQt + dt * 16 * LC, LC, sO + sc * 16, LB);
+                spread(std::integral_constant<int, C / 32 + D / 32 + q * 2 * (C / 32) + j>{}, cn);
+            });
+            static_for<0, C / 32>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                if (on) mfma_krange<32 * j, 32 * j + 32>(y0, y1, sYt + dt * 16 * LC, LC, sdU + sc * 16, LB);
+                spread(std::integral_constant<int, C / 32 + D / 32 + q * 2 * (C / 32) + C / 32 + j>{}, cn);
+            });
+            if (on) {
+                const f32x4 pq = q0 + q1, py = y0 + y1;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = dt * 16 + 4 * (l >> 4) + r;
                     xn[q][r] = sGam[row] * sX[row * LB + sc * 16 + (l & 15)] + a.scale * pq[r] - py[r];
                 }
             }
-        }
+        });
         // No barrier: each wave rewrites only the entries of X it has just
         // read, and every other read of X in this chunk was before the last one.
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        for (int q = 0; q < NXT; ++q) {
             const int st = w + 8 * q, dt = st >> 1, sc = st & 1;
             if (st < NST)
 #pragma unroll
