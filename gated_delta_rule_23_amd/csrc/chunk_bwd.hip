@@ -583,7 +583,7 @@ __device__ __forceinline__ void fsweep(const ChunkBwdArgs &a, float *smem, int i
         }
     };
     constexpr int NXT = NST > 8 ? 2 : 1;  // state tiles per wave
-    constexpr int NG = D / 32 + NXT * (C / 32);
+    constexpr int NG = D / 32 + C / 16;
     const auto spread = [&](auto gc, int c) {
         constexpr int g = decltype(gc)::value;
         __builtin_amdgcn_sched_barrier(0);
@@ -629,33 +629,53 @@ __device__ __forceinline__ void fsweep(const ChunkBwdArgs &a, float *smem, int i
             }
         }
         lds_barrier();
-        // S = Gamma . S + Kend^T U
+        // S = Gamma . S + Kend^T U; a wave's tiles share their columns, so
+        // each k step reads the U operand once for both.
         f32x4 sn[NXT];
-        static_for<0, NXT>([&](auto qc) {
-            constexpr int q = decltype(qc)::value;
-            const int st = w + 8 * q, dt = st >> 1, sc = st & 1;
-            const bool on = st < NST;
-            f32x4 p0 = zero4(), p1 = zero4();
-            static_for<0, C / 32>([&](auto jc) {
-                constexpr int j = decltype(jc)::value;
-                if (on) mfma_krange<32 * j, 32 * j + 32>(p0, p1, sKt + dt * 16 * LC, LC, sU + sc * 16, LB);
-                spread(std::integral_constant<int, D / 32 + q * (C / 32) + j>{}, cn);
-            });
-            if (on) {
-                const f32x4 p = p0 + p1;
+        {
+            const int sc = w & 1;
+            const float *pb = sU + sc * 16 + (l >> 4) * LB + (l & 15);
+            const float *pa[NXT];
+            bool on[NXT];
+            f32x4 acc[NXT][2];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = dt * 16 + 4 * (l >> 4) + r;
-                    sn[q][r] = sGam[row] * sS[row * LB + sc * 16 + (l & 15)] + p[r];
-                }
+            for (int q = 0; q < NXT; ++q) {
+                on[q] = NST >= 8 * (q + 1) || w + 8 * q < NST;
+                pa[q] = sKt + (((w + 8 * q) >> 1) * 16 + (l & 15)) * LC + (l >> 4);
+                acc[q][0] = acc[q][1] = zero4();
             }
-        });
+            static_for<0, C / 16>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+#pragma unroll
+                for (int k = 16 * j; k < 16 * j + 16; k += 8) {
+                    const float b0 = pb[k * LB], b1 = pb[(k + 4) * LB];
+#pragma unroll
+                    for (int q = 0; q < NXT; ++q)
+                        if (on[q]) {
+                            acc[q][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[q][k], b0, acc[q][0], 0, 0, 0);
+                            acc[q][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[q][k + 4], b1, acc[q][1], 0, 0, 0);
+                        }
+                }
+                spread(std::integral_constant<int, D / 32 + j>{}, cn);
+            });
+#pragma unroll
+            for (int q = 0; q < NXT; ++q)
+                if (on[q]) {
+                    const int dt = (w + 8 * q) >> 1;
+                    const f32x4 p = acc[q][0] + acc[q][1];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = dt * 16 + 4 * (l >> 4) + r;
+                        sn[q][r] = sGam[row] * sS[row * LB + sc * 16 + (l & 15)] + p[r];
+                    }
+                }
+        }
         // No barrier: each wave rewrites only the state entries it has just
         // read, and every other read of S in this chunk was before the last one.
 #pragma unroll
         for (int q = 0; q < NXT; ++q) {
             const int st = w + 8 * q, dt = st >> 1, sc = st & 1;
-            if (st < NST)
+            if (NST >= 8 * (q + 1) || st < NST)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) sS[(dt * 16 + 4 * (l >> 4) + r) * LB + sc * 16 + (l & 15)] = sn[q][r];
         }
@@ -715,7 +735,7 @@ __device__ __forceinline__ void bsweep(const ChunkBwdArgs &a, float *smem, int i
     // piece g come loads [g NLD / NG, (g + 1) NLD / NG), fenced so that the
     // compiler keeps them there.
     constexpr int NXT = NST > 8 ? 2 : 1;  // X tiles per wave
-    constexpr int NG = C / 32 + D / 32 + NXT * 2 * (C / 32);
+    constexpr int NG = C / 32 + D / 32 + C / 16;
     const auto spread = [&](auto gc, int c) {
         constexpr int g = decltype(gc)::value;
         __builtin_amdgcn_sched_barrier(0);
@@ -776,38 +796,57 @@ __device__ __forceinline__ void bsweep(const ChunkBwdArgs &a, float *smem, int i
             }
         }
         lds_barrier();
-        // X = Gamma . X + s Q~^T dO - Y^T dU
+        // X = Gamma . X + s Q~^T dO - Y^T dU. A wave's tiles share their
+        // columns, so each k step reads the dO and dU operands once for both.
         f32x4 xn[NXT];
-        static_for<0, NXT>([&](auto qc) {
-            constexpr int q = decltype(qc)::value;
-            const int st = w + 8 * q, dt = st >> 1, sc = st & 1;
-            const bool on = st < NST;
-            f32x4 q0 = zero4(), q1 = zero4(), y0 = zero4(), y1 = zero4();
-            static_for<0, C / 32>([&](auto jc) {
-                constexpr int j = decltype(jc)::value;
-                if (on) mfma_krange<32 * j, 32 * j + 32>(q0, q1, sQt + dt * 16 * LC, LC, sO + sc * 16, LB);
-                spread(std::integral_constant<int, C / 32 + D / 32 + q * 2 * (C / 32) + j>{}, cn);
-            });
-            static_for<0, C / 32>([&](auto jc) {
-                constexpr int j = decltype(jc)::value;
-                if (on) mfma_krange<32 * j, 32 * j + 32>(y0, y1, sYt + dt * 16 * LC, LC, sdU + sc * 16, LB);
-                spread(std::integral_constant<int, C / 32 + D / 32 + q * 2 * (C / 32) + C / 32 + j>{}, cn);
-            });
-            if (on) {
-                const f32x4 pq = q0 + q1, py = y0 + y1;
+        {
+            const int sc = w & 1;
+            const float *pbq = sO + sc * 16 + (l >> 4) * LB + (l & 15), *pby = sdU + sc * 16 + (l >> 4) * LB + (l & 15);
+            const float *paq[NXT], *pay[NXT];
+            bool on[NXT];
+            f32x4 aq[NXT][2], ay[NXT][2];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = dt * 16 + 4 * (l >> 4) + r;
-                    xn[q][r] = sGam[row] * sX[row * LB + sc * 16 + (l & 15)] + a.scale * pq[r] - py[r];
-                }
+            for (int q = 0; q < NXT; ++q) {
+                const int dt = (w + 8 * q) >> 1;
+                on[q] = NST >= 8 * (q + 1) || w + 8 * q < NST;
+                paq[q] = sQt + (dt * 16 + (l & 15)) * LC + (l >> 4);
+                pay[q] = sYt + (dt * 16 + (l & 15)) * LC + (l >> 4);
+                aq[q][0] = aq[q][1] = ay[q][0] = ay[q][1] = zero4();
             }
-        });
+            static_for<0, C / 16>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+#pragma unroll
+                for (int k = 16 * j; k < 16 * j + 16; k += 8) {
+                    const float bq0 = pbq[k * LB], bq1 = pbq[(k + 4) * LB], by0 = pby[k * LB], by1 = pby[(k + 4) * LB];
+#pragma unroll
+                    for (int q = 0; q < NXT; ++q)
+                        if (on[q]) {
+                            aq[q][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(paq[q][k], bq0, aq[q][0], 0, 0, 0);
+                            aq[q][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(paq[q][k + 4], bq1, aq[q][1], 0, 0, 0);
+                            ay[q][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(pay[q][k], by0, ay[q][0], 0, 0, 0);
+                            ay[q][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pay[q][k + 4], by1, ay[q][1], 0, 0, 0);
+                        }
+                }
+                spread(std::integral_constant<int, C / 32 + D / 32 + j>{}, cn);
+            });
+#pragma unroll
+            for (int q = 0; q < NXT; ++q)
+                if (on[q]) {
+                    const int dt = (w + 8 * q) >> 1;
+                    const f32x4 pq = aq[q][0] + aq[q][1], py = ay[q][0] + ay[q][1];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = dt * 16 + 4 * (l >> 4) + r;
+                        xn[q][r] = sGam[row] * sX[row * LB + sc * 16 + (l & 15)] + a.scale * pq[r] - py[r];
+                    }
+                }
+        }
         // No barrier: each wave rewrites only the entries of X it has just
         // read, and every other read of X in this chunk was before the last one.
 #pragma unroll
         for (int q = 0; q < NXT; ++q) {
             const int st = w + 8 * q, dt = st >> 1, sc = st & 1;
-            if (st < NST)
+            if (NST >= 8 * (q + 1) || st < NST)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) sX[(dt * 16 + 4 * (l >> 4) + r) * LB + sc * 16 + (l & 15)] = xn[q][r];
         }
