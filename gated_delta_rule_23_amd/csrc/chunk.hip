@@ -1528,18 +1528,6 @@ __global__ __launch_bounds__(256) void chunk_seg_combine(ChunkArgs a) {
     }
 }
 
-// Compute units of the device in use when first asked (thread-safe; 256 if unknown).
-static int device_cus() {
-    static const int cus = [] {
-        int dev = 0, n = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-            return n;
-        return 256;
-    }();
-    return cus;
-}
-
 template <typename IO, int D, int NCT>
 static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t s) {
     using Cfg = PrepCfg<IO, D>;

@@ -234,239 +234,267 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
     float *sGs = sZ + C * LD;   // scalar decay: G per token
     float *sF = sGs + C;        // per-channel decay: the factor table (kBwdDecRows rows of D)
     int *sSlow = reinterpret_cast<int *>(sF + kBwdDecRows * D);  // bit b: block b formed entry by entry
-    const int tid = threadIdx.x, u = blockIdx.x;
-    const Unit x = decode(a, u);
-    const size_t ucd = (size_t)u * C * D;
-    if (CHAN && tid == 0) *sSlow = 0;
-    f32x4 rz[NL];  // z = beta v (or w v), loaded with the other inputs and staged after T and A
-    {
-        f32x4 rq[NL], rk[NL], re[NL], rg[CHAN ? NL : 1];
+    const int tid = threadIdx.x, units = a.B * a.Hv * a.NC;
+    // The workgroups are persistent: each takes units blockIdx.x, + gridDim.x,
+    // ..., and fetches the next one's inputs into registers once the current
+    // ones are staged in shared memory (before the solve), so that the input
+    // loads overlap the solve instead of stalling every workgroup at its start.
+    // The fetched values stay in the io type until they are staged.
+    using R4 = typename Raw4<IO>::type;
+    R4 rq[NL], rk[NL], rb[BW ? NL : 1], rw[BW ? NL : 1], rv[NL];
+    f32x4 rg[CHAN ? NL : 1];
+    float rbeta[BW ? 1 : NL];
+    const auto fetch = [&](int u) {
+        const Unit x = decode(a, u);
 #pragma unroll
         for (int l = 0; l < NL; ++l) {
             int e, t, d;
             rc<D>(l, e, t, d);
-            rq[l] = rk[l] = re[l] = rz[l] = zero4();
+            rq[l] = rk[l] = rv[l] = R4{};
+            if (BW) rb[l] = rw[l] = R4{};
+            else rbeta[l] = 0.f;
             if (CHAN) rg[l] = zero4();
             if (t < x.n) {
                 const size_t iq = (x.rowq + (size_t)t * a.Hqk) * D + d, iv = (x.rowv + (size_t)t * a.Hv) * D + d;
-                rq[l] = ld4io<IO>(a.q, iq);
-                rk[l] = ld4io<IO>(a.k, iq);
-                re[l] = BW ? ld4io<IO>(a.bg, iv) : splat(a.beta[x.rowv + (size_t)t * a.Hv]);
+                rq[l] = Raw4<IO>::load(static_cast<const IO *>(a.q) + iq);
+                rk[l] = Raw4<IO>::load(static_cast<const IO *>(a.k) + iq);
+                rv[l] = Raw4<IO>::load(static_cast<const IO *>(a.v) + iv);
+                if (BW) {
+                    rb[l] = Raw4<IO>::load(static_cast<const IO *>(a.bg) + iv);
+                    rw[l] = Raw4<IO>::load(static_cast<const IO *>(a.wg) + iv);
+                } else {
+                    rbeta[l] = a.beta[x.rowv + (size_t)t * a.Hv];
+                }
                 if (CHAN) rg[l] = lds4(a.g + iv);
-                rz[l] = (BW ? ld4io<IO>(a.wg, iv) : splat(a.beta[x.rowv + (size_t)t * a.Hv])) * ld4io<IO>(a.v, iv);
             }
         }
+    };
+    // (With fp32 io the fetched values would not fit in registers beside the
+    // solve's; each unit then fetches its own inputs at its start.)
+    constexpr bool PREF = sizeof(IO) == 2;
+    if (PREF && (int)blockIdx.x < units) fetch(blockIdx.x);
+    for (int u = blockIdx.x; u < units; u += gridDim.x) {
+        const int un = u + (int)gridDim.x;  // the unit fetched during this one
+        const Unit x = decode(a, u);
+        const size_t ucd = (size_t)u * C * D;
+        if (CHAN && tid == 0) *sSlow = 0;
+        if (!PREF) fetch(u);
+        {
 #pragma unroll
-        for (int l = 0; l < NL; ++l) {
-            int e, t, d;
-            rc<D>(l, e, t, d);
-            sts4(sQ + t * LD + d, rq[l]);
-            sts4(sK + t * LD + d, rk[l]);
-            sts4(sE + t * LD + d, re[l] * rk[l]);
-            if (CHAN) sts4(sZ + t * LD + d, rg[l]);
-        }
-    }
-    if (!CHAN && tid < C) sGs[tid] = a.g && tid < x.n ? a.g[x.rowv + (size_t)tid * a.Hv] : 0.f;
-    __syncthreads();
-    if (CHAN) {
-        if (tid < D) {  // per channel: the column into registers, summed per block, written back
-            float gc[C];
-#pragma unroll
-            for (int t = 0; t < C; ++t) gc[t] = sZ[t * LD + tid];
-#pragma unroll
-            for (int t = 1; t < C; ++t)
-                if (t % 16) gc[t] += gc[t - 1];
-#pragma unroll
-            for (int t = 0; t < C; ++t) sZ[t * LD + tid] = gc[t];
-            const float B0 = gc[15], B1 = gc[31], B2 = gc[47], B3 = gc[63], Bs[4] = {B0, B1, B2, B3};
-            const float R[5] = {0.f, B0, B0 + B1, B0 + B1 + B2, B0 + B1 + B2 + B3};
-            float *f = sF + tid;
-            int bits = 0;
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                f[b * D] = expf(R[b]);
-                f[(7 + b) * D] = expf(fminf(-Bs[b], kBwdDiagRange));
-                f[(11 + b) * D] = expf(R[4] - R[b + 1]);
-                bits |= Bs[b] < -kBwdDiagRange ? 1 << b : 0;
+            for (int l = 0; l < NL; ++l) {
+                int e, t, d;
+                rc<D>(l, e, t, d);
+                const f32x4 k4 = Raw4<IO>::widen(rk[l]);
+                sts4(sQ + t * LD + d, Raw4<IO>::widen(rq[l]));
+                sts4(sK + t * LD + d, k4);
+                sts4(sE + t * LD + d, (BW ? Raw4<IO>::widen(rb[BW ? l : 0]) : splat(rbeta[BW ? 0 : l])) * k4);
+                if (CHAN) sts4(sZ + t * LD + d, rg[CHAN ? l : 0]);
             }
-            f[4 * D] = expf(B1);
-            f[5 * D] = expf(B2);
-            f[6 * D] = expf(B1 + B2);
-            a.wGam[(size_t)u * D + tid] = expf(R[4]);
-            if (bits) atomicOr(sSlow, bits);
         }
-    } else if (tid < 64) {
-        float G = sGs[tid];
+        if (!CHAN && tid < C) sGs[tid] = a.g && tid < x.n ? a.g[x.rowv + (size_t)tid * a.Hv] : 0.f;
+        __syncthreads();
+        if (CHAN) {
+            if (tid < D) {  // per channel: the column into registers, summed per block, written back
+                float gc[C];
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_up(G, off);
-            if (tid >= off) G += y;
+                for (int t = 0; t < C; ++t) gc[t] = sZ[t * LD + tid];
+#pragma unroll
+                for (int t = 1; t < C; ++t)
+                    if (t % 16) gc[t] += gc[t - 1];
+#pragma unroll
+                for (int t = 0; t < C; ++t) sZ[t * LD + tid] = gc[t];
+                const float B0 = gc[15], B1 = gc[31], B2 = gc[47], B3 = gc[63], Bs[4] = {B0, B1, B2, B3};
+                const float R[5] = {0.f, B0, B0 + B1, B0 + B1 + B2, B0 + B1 + B2 + B3};
+                float *f = sF + tid;
+                int bits = 0;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    f[b * D] = expf(R[b]);
+                    f[(7 + b) * D] = expf(fminf(-Bs[b], kBwdDiagRange));
+                    f[(11 + b) * D] = expf(R[4] - R[b + 1]);
+                    bits |= Bs[b] < -kBwdDiagRange ? 1 << b : 0;
+                }
+                f[4 * D] = expf(B1);
+                f[5 * D] = expf(B2);
+                f[6 * D] = expf(B1 + B2);
+                a.wGam[(size_t)u * D + tid] = expf(R[4]);
+                if (bits) atomicOr(sSlow, bits);
+            }
+        } else if (tid < 64) {
+            float G = sGs[tid];
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_up(G, off);
+                if (tid >= off) G += y;
+            }
+            sGs[tid] = G;
         }
-        sGs[tid] = G;
-    }
-    __syncthreads();
+        __syncthreads();
 
-    float *wG = a.wG + ucd;  // [C][D] per-channel decay (Gb), [C] scalar (G)
-    if (CHAN)  // Q^, K^, E^ in place of q, k, e
+        float *wG = a.wG + ucd;  // [C][D] per-channel decay (Gb), [C] scalar (G)
+        if (CHAN)  // Q^, K^, E^ in place of q, k, e
+#pragma unroll
+            for (int l = 0; l < NL; ++l) {
+                int e, t, d;
+                rc<D>(l, e, t, d);
+                const f32x4 Gb = lds4(sZ + t * LD + d), Bb = lds4(sZ + (t | 15) * LD + d), eg = exp4(Gb);
+                sts4(wG + e, Gb);
+                sts4(sQ + t * LD + d, lds4(sQ + t * LD + d) * eg);
+                sts4(sK + t * LD + d, lds4(sK + t * LD + d) * exp4(Bb - Gb));
+                sts4(sE + t * LD + d, lds4(sE + t * LD + d) * eg);
+            }
+        if (!CHAN && tid < C) wG[tid] = sGs[tid];
+        if (!CHAN && tid < D) a.wGam[(size_t)u * D + tid] = expf(sGs[C - 1]);
+        __syncthreads();
+        // Q~^T and Kend^T (row = channel), which the sweeps over chunks read.
 #pragma unroll
         for (int l = 0; l < NL; ++l) {
-            int e, t, d;
-            rc<D>(l, e, t, d);
-            const f32x4 Gb = lds4(sZ + t * LD + d), Bb = lds4(sZ + (t | 15) * LD + d), eg = exp4(Gb);
-            sts4(wG + e, Gb);
-            sts4(sQ + t * LD + d, lds4(sQ + t * LD + d) * eg);
-            sts4(sK + t * LD + d, lds4(sK + t * LD + d) * exp4(Bb - Gb));
-            sts4(sE + t * LD + d, lds4(sE + t * LD + d) * eg);
-        }
-    if (!CHAN && tid < C) wG[tid] = sGs[tid];
-    if (!CHAN && tid < D) a.wGam[(size_t)u * D + tid] = expf(sGs[C - 1]);
-    __syncthreads();
-    // Q~^T and Kend^T (row = channel), which the sweeps over chunks read.
-#pragma unroll
-    for (int l = 0; l < NL; ++l) {
-        int e, dd, t;
-        rc<C>(l, e, dd, t);
-        f32x4 qv, kv;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            qv[r] = sQ[(t + r) * LD + dd];
-            kv[r] = sK[(t + r) * LD + dd];
-        }
-        if (CHAN) {  // Q~ = Q^ exp(R_b), Kend = K^ exp(G_end - R_{b+1}); the 4 tokens share block b
-            qv *= sF[(t >> 4) * D + dd];
-            kv *= sF[(11 + (t >> 4)) * D + dd];
-        } else {
+            int e, dd, t;
+            rc<C>(l, e, dd, t);
+            f32x4 qv, kv;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                qv[r] *= expf(sGs[t + r]);
-                kv[r] *= expf(sGs[C - 1] - sGs[t + r]);
+                qv[r] = sQ[(t + r) * LD + dd];
+                kv[r] = sK[(t + r) * LD + dd];
             }
+            if (CHAN) {  // Q~ = Q^ exp(R_b), Kend = K^ exp(G_end - R_{b+1}); the 4 tokens share block b
+                qv *= sF[(t >> 4) * D + dd];
+                kv *= sF[(11 + (t >> 4)) * D + dd];
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    qv[r] *= expf(sGs[t + r]);
+                    kv[r] *= expf(sGs[C - 1] - sGs[t + r]);
+                }
+            }
+            sts4(a.wQt + ucd + e, qv);
+            sts4(a.wKet + ucd + e, kv);
         }
-        sts4(a.wQt + ucd + e, qv);
-        sts4(a.wKet + ucd + e, kv);
-    }
 
-    // T and A: thread = 2 x 4 block of rows r0.., columns c0.. (the rows in
-    // token block bi, the columns in block bj).
-    {
-        const int r0 = (tid >> 4) * 2, c0 = (tid & 15) * 4, bi = r0 >> 4, bj = c0 >> 4;
-        float aT[2][4], aA[2][4];
+        // T and A: thread = 2 x 4 block of rows r0.., columns c0.. (the rows in
+        // token block bi, the columns in block bj).
+        {
+            const int r0 = (tid >> 4) * 2, c0 = (tid & 15) * 4, bi = r0 >> 4, bj = c0 >> 4;
+            float aT[2][4], aA[2][4];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) aT[i][j] = aA[i][j] = 0.f;
-        // Per-channel decay: the tile's factor on the K^ rows (none for bj = bi - 1).
-        const float *fk = !CHAN || bi - bj == 1 ? nullptr
-                          : sF + (bi == bj ? 7 + bi : bwd_row_far(bi, bj)) * D;
-        if (CHAN && bi == bj && ((*sSlow >> bi) & 1)) {
-            // A strongly decaying diagonal block, entry by entry from the
-            // inputs: sum_c e_tc k_jc exp(Gb_tc - Gb_jc) (the same for q).
-            if (c0 <= r0 + 1)
+                for (int j = 0; j < 4; ++j) aT[i][j] = aA[i][j] = 0.f;
+            // Per-channel decay: the tile's factor on the K^ rows (none for bj = bi - 1).
+            const float *fk = !CHAN || bi - bj == 1 ? nullptr
+                              : sF + (bi == bj ? 7 + bi : bwd_row_far(bi, bj)) * D;
+            if (CHAN && bi == bj && ((*sSlow >> bi) & 1)) {
+                // A strongly decaying diagonal block, entry by entry from the
+                // inputs: sum_c e_tc k_jc exp(Gb_tc - Gb_jc) (the same for q).
+                if (c0 <= r0 + 1)
+                    for (int d = 0; d < D; d += 4) {
+                        f32x4 e4[2], q4[2], k4[4], g4[2], h4[4];
+#pragma unroll
+                        for (int i = 0; i < 2; ++i) {
+                            const int t = r0 + i;
+                            const size_t iq = (x.rowq + (size_t)t * a.Hqk) * D + d, iv = (x.rowv + (size_t)t * a.Hv) * D + d;
+                            q4[i] = t < x.n ? ld4io<IO>(a.q, iq) : zero4();
+                            e4[i] = t < x.n ? ld4io<IO>(a.k, iq) *
+                                                  (BW ? ld4io<IO>(a.bg, iv) : splat(a.beta[x.rowv + (size_t)t * a.Hv]))
+                                            : zero4();
+                            g4[i] = lds4(sZ + t * LD + d);
+                        }
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const int t = c0 + j;
+                            k4[j] = t < x.n ? ld4io<IO>(a.k, (x.rowq + (size_t)t * a.Hqk) * D + d) : zero4();
+                            h4[j] = lds4(sZ + t * LD + d);
+                        }
+#pragma unroll
+                        for (int i = 0; i < 2; ++i)
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                f32x4 kf;
+#pragma unroll
+                                for (int r = 0; r < 4; ++r) kf[r] = k4[j][r] * expf(fminf(g4[i][r] - h4[j][r], 0.f));
+                                aT[i][j] = dot4(e4[i], kf, aT[i][j]);
+                                aA[i][j] = dot4(q4[i], kf, aA[i][j]);
+                            }
+                    }
+            } else if (c0 <= r0 + 1) {
+#pragma unroll 2
                 for (int d = 0; d < D; d += 4) {
-                    f32x4 e4[2], q4[2], k4[4], g4[2], h4[4];
+                    f32x4 e4[2], q4[2], k4[4];
 #pragma unroll
                     for (int i = 0; i < 2; ++i) {
-                        const int t = r0 + i;
-                        const size_t iq = (x.rowq + (size_t)t * a.Hqk) * D + d, iv = (x.rowv + (size_t)t * a.Hv) * D + d;
-                        q4[i] = t < x.n ? ld4io<IO>(a.q, iq) : zero4();
-                        e4[i] = t < x.n ? ld4io<IO>(a.k, iq) *
-                                              (BW ? ld4io<IO>(a.bg, iv) : splat(a.beta[x.rowv + (size_t)t * a.Hv]))
-                                        : zero4();
-                        g4[i] = lds4(sZ + t * LD + d);
+                        e4[i] = lds4(sE + (r0 + i) * LD + d);
+                        q4[i] = lds4(sQ + (r0 + i) * LD + d);
                     }
+                    const f32x4 f4 = fk ? lds4(fk + d) : splat(1.f);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int t = c0 + j;
-                        k4[j] = t < x.n ? ld4io<IO>(a.k, (x.rowq + (size_t)t * a.Hqk) * D + d) : zero4();
-                        h4[j] = lds4(sZ + t * LD + d);
-                    }
+                    for (int j = 0; j < 4; ++j) k4[j] = lds4(sK + (c0 + j) * LD + d) * f4;
 #pragma unroll
                     for (int i = 0; i < 2; ++i)
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
-                            f32x4 kf;
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) kf[r] = k4[j][r] * expf(fminf(g4[i][r] - h4[j][r], 0.f));
-                            aT[i][j] = dot4(e4[i], kf, aT[i][j]);
-                            aA[i][j] = dot4(q4[i], kf, aA[i][j]);
+                            aT[i][j] = dot4(e4[i], k4[j], aT[i][j]);
+                            aA[i][j] = dot4(q4[i], k4[j], aA[i][j]);
                         }
                 }
-        } else if (c0 <= r0 + 1) {
-#pragma unroll 2
-            for (int d = 0; d < D; d += 4) {
-                f32x4 e4[2], q4[2], k4[4];
+            }
 #pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    e4[i] = lds4(sE + (r0 + i) * LD + d);
-                    q4[i] = lds4(sQ + (r0 + i) * LD + d);
+            for (int i = 0; i < 2; ++i) {
+                const int t = r0 + i;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int jj = c0 + j;
+                    const float f = !CHAN && jj <= t ? expf(sGs[t] - sGs[jj]) : 1.f;
+                    aT[i][j] = jj < t ? aT[i][j] * f : 0.f;
+                    aA[i][j] = jj <= t ? aA[i][j] * f : 0.f;
                 }
-                const f32x4 f4 = fk ? lds4(fk + d) : splat(1.f);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) k4[j] = lds4(sK + (c0 + j) * LD + d) * f4;
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        aT[i][j] = dot4(e4[i], k4[j], aT[i][j]);
-                        aA[i][j] = dot4(q4[i], k4[j], aA[i][j]);
-                    }
+                const size_t o = (size_t)u * C * C + (size_t)t * C + c0;
+                sts4(a.wT + o, f32x4{aT[i][0], aT[i][1], aT[i][2], aT[i][3]});
+                sts4(a.wA + o, f32x4{aA[i][0], aA[i][1], aA[i][2], aA[i][3]});
             }
+            __syncthreads();  // q, k and e tiles read: T^T goes where q was
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sQ[(c0 + j) * C + r0 + i] = aT[i][j];
         }
+        // Right-hand sides: E~ (scalar decay: the raw e scaled by exp(G_t); per
+        // channel: E^ scaled by exp(R_b)) and z.
+        {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int t = r0 + i;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int jj = c0 + j;
-                const float f = !CHAN && jj <= t ? expf(sGs[t] - sGs[jj]) : 1.f;
-                aT[i][j] = jj < t ? aT[i][j] * f : 0.f;
-                aA[i][j] = jj <= t ? aA[i][j] * f : 0.f;
+            for (int l = 0; l < NL; ++l) {
+                int e, t, d;
+                rc<D>(l, e, t, d);
+                sts4(sZ + t * LD + d, (BW ? Raw4<IO>::widen(rw[BW ? l : 0]) : splat(rbeta[BW ? 0 : l])) * Raw4<IO>::widen(rv[l]));
+                if (!CHAN) sts4(sE + t * LD + d, lds4(sE + t * LD + d) * expf(sGs[t]));
+                else sts4(sE + t * LD + d, lds4(sE + t * LD + d) * lds4(sF + (t >> 4) * D + d));
             }
-            const size_t o = (size_t)u * C * C + (size_t)t * C + c0;
-            sts4(a.wT + o, f32x4{aT[i][0], aT[i][1], aT[i][2], aT[i][3]});
-            sts4(a.wA + o, f32x4{aA[i][0], aA[i][1], aA[i][2], aA[i][3]});
+            if (PREF && un < units) fetch(un);
         }
-        __syncthreads();  // q, k and e tiles read: T^T goes where q was
+        __syncthreads();
+        // (I + T) X = [E~ | Z], one column per thread.
+        if (tid < 2 * D) {
+            float *X = tid < D ? sE + tid : sZ + (tid - D);
+            float xc[C];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < C; ++i) xc[i] = X[i * LD];
+            solve_lower(xc, sQ);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sQ[(c0 + j) * C + r0 + i] = aT[i][j];
-    }
-    // Right-hand sides: E~ (scalar decay: the raw e scaled by exp(G_t); per
-    // channel: E^ scaled by exp(R_b)) and z.
-    {
+            for (int i = 0; i < C; ++i) X[i * LD] = xc[i];
+        }
+        __syncthreads();
 #pragma unroll
         for (int l = 0; l < NL; ++l) {
             int e, t, d;
             rc<D>(l, e, t, d);
-            sts4(sZ + t * LD + d, rz[l]);
-            if (!CHAN) sts4(sE + t * LD + d, lds4(sE + t * LD + d) * expf(sGs[t]));
-            else sts4(sE + t * LD + d, lds4(sE + t * LD + d) * lds4(sF + (t >> 4) * D + d));
+            sts4(a.wUz + ucd + e, lds4(sZ + t * LD + d));
         }
-    }
-    __syncthreads();
-    // (I + T) X = [E~ | Z], one column per thread.
-    if (tid < 2 * D) {
-        float *X = tid < D ? sE + tid : sZ + (tid - D);
-        float xc[C];
 #pragma unroll
-        for (int i = 0; i < C; ++i) xc[i] = X[i * LD];
-        solve_lower(xc, sQ);
-#pragma unroll
-        for (int i = 0; i < C; ++i) X[i * LD] = xc[i];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int l = 0; l < NL; ++l) {
-        int e, t, d;
-        rc<D>(l, e, t, d);
-        sts4(a.wUz + ucd + e, lds4(sZ + t * LD + d));
-    }
-#pragma unroll
-    for (int l = 0; l < NL; ++l) {  // Y^T
-        int e, dd, t;
-        rc<C>(l, e, dd, t);
-        sts4(a.wYt + ucd + e, f32x4{sE[t * LD + dd], sE[(t + 1) * LD + dd], sE[(t + 2) * LD + dd], sE[(t + 3) * LD + dd]});
+        for (int l = 0; l < NL; ++l) {  // Y^T
+            int e, dd, t;
+            rc<C>(l, e, dd, t);
+            sts4(a.wYt + ucd + e, f32x4{sE[t * LD + dd], sE[(t + 1) * LD + dd], sE[(t + 2) * LD + dd], sE[(t + 3) * LD + dd]});
+        }
+        __syncthreads();  // shared memory read; the next unit overwrites it
     }
 }
 
@@ -1395,7 +1423,9 @@ hipError_t run(const ChunkBwdArgs &a, hipStream_t s) {
     }();
     if (attr != hipSuccess) return attr;
     const unsigned units = (unsigned)((size_t)a.B * a.Hv * a.NC), items = (unsigned)((size_t)a.B * a.Hv * (D / BV));
-    hipLaunchKernelGGL((cb_prep<IO, D, CHAN, BW>), dim3(units), dim3(NT), prep_smem<D>(), s, a);
+    // One persistent prep workgroup per compute unit (its shared memory takes the unit's).
+    const unsigned pgrid = units < (unsigned)device_cus() ? units : (unsigned)device_cus();
+    hipLaunchKernelGGL((cb_prep<IO, D, CHAN, BW>), dim3(pgrid), dim3(NT), prep_smem<D>(), s, a);
     const unsigned P = (items + 7) / 8 * 8;
     hipLaunchKernelGGL((cb_sweeps<IO, D>), dim3(2 * P), dim3(NS), sweep_smem, s, a, (int)items, (int)P);
     hipLaunchKernelGGL((cb_grad_s<IO, D>), dim3(units), dim3(NT), grad_s_smem<D>(), s, a);

@@ -24,6 +24,18 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
 typedef uint16_t bf16_t;
 
+// Compute units of the device in use when first asked (thread-safe; 256 if unknown).
+inline int device_cus() {
+    static const int cus = [] {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+            return n;
+        return 256;
+    }();
+    return cus;
+}
+
 __device__ __forceinline__ float bf2f(bf16_t u) { return __uint_as_float((uint32_t)u << 16); }
 
 // float -> bfloat16, round to nearest even (gfx950 converts in hardware,
