@@ -145,10 +145,14 @@ __device__ __forceinline__ Unit decode(const ChunkBwdArgs &a, int u) {
 }
 // Element e (a multiple of 4) of a row-major C x D array: token row and column.
 template <int D>
-__device__ __forceinline__ void rc(int l, int &e, int &t, int &d) {
-    e = 4 * (l * NT + (int)threadIdx.x);
+__device__ __forceinline__ void rc(int l, int &e, int &t, int &d, int tid) {
+    e = 4 * (l * NT + tid);
     t = e / D;
     d = e - t * D;
+}
+template <int D>
+__device__ __forceinline__ void rc(int l, int &e, int &t, int &d) {
+    rc<D>(l, e, t, d, (int)threadIdx.x);
 }
 
 // Workgroup barrier ordering shared-memory accesses only: it does not wait
@@ -166,41 +170,75 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-// (I + T) x = r for one column x (in registers, r on entry), T strictly
-// lower triangular. Right-looking: once x_m is final it is taken out of every
-// later row at once, so the dependent chain is one multiply-add per row and
-// the rest is independent work. sTt = T^T, row-major with row stride C
-// (row m = column m of T, 16-byte aligned rows).
-__device__ __forceinline__ void solve_lower(float (&x)[C], const float *sTt) {
+// Blocked solves on the matrix cores. The 64 x 64 unit triangular system
+// splits into 16 x 16 blocks: the diagonal blocks are inverted first (one
+// wave), then each wave carries 16-column tiles of the right-hand side
+// through block substitution, X_b = L_b (R_b - sum_c M_bc X_c), with the
+// products on v_mfma_f32_16x16x4_f32. A tile lives in registers in the
+// accumulator layout (lane l: rows 4 (l / 16) + r of column l % 16 of each
+// 16-row block), and each product takes its k index in the order 4 (l / 16)
+// + i at step i, so a lane's accumulator rows are exactly the B operand it
+// supplies and its A operand is one 16-byte read.
+constexpr int LTT = C + 4;  // row stride of the negated 64 x 64 triangle in shared memory
+constexpr int LL = 16 + 4;  // row stride of the inverted 16 x 16 diagonal blocks
+constexpr int kSolveFloats = C * LTT + C * LL;
+
+// Wave-wide: lane (b, j) = (l / 16, l % 16) forms column j of
+// (I + T_bb)^-1 by forward substitution, with nt(i, k) = -T_ik for rows and
+// columns of the 64 x 64 matrix, and writes it to L[(16 b + i) LL + j]
+// (row-major blocks) or, TRANS, to L[(16 b + j) LL + i] (the transposes).
+template <bool TRANS, typename F>
+__device__ __forceinline__ void invert_diag16(F nt, float *L) {
+    const int l = threadIdx.x & 63, b = l >> 4, j = l & 15;
+    float x[16];
 #pragma unroll
-    for (int m = 0; m < C - 1; ++m) {
+    for (int i = 0; i < 16; ++i) {
+        float acc = i == j ? 1.f : 0.f;
 #pragma unroll
-        for (int i4 = (m + 1) & ~3; i4 < C; i4 += 4) {
-            const f32x4 t = lds4(sTt + m * C + i4);
+        for (int k = 0; k < i; ++k) acc = fmaf(nt(16 * b + i, 16 * b + k), x[k], acc);
+        x[i] = acc;
+        if (i % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // bounds the entries held in registers
+    }
+    if (TRANS) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (i4 + r > m) x[i4 + r] = fmaf(-t[r], x[m], x[i4 + r]);
-        }
+        for (int i = 0; i < 16; i += 4) *reinterpret_cast<f32x4 *>(L + (16 * b + j) * LL + i) = f32x4{x[i], x[i + 1], x[i + 2], x[i + 3]};
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) L[(16 * b + i) * LL + j] = x[i];
     }
 }
-// (I + T)^T x = r, rows from the last: x_i = r_i - sum_{m > i} T_mi x_m,
-// right-looking as above. sT = T, row-major with row stride C.
-__device__ __forceinline__ void solve_upper(float (&x)[C], const float *sT) {
+
+// One 64 x 16 tile x (registers, accumulator layout, the right-hand side on
+// entry) through the block substitution: UP = false solves (I + T) X = R
+// from the first block (M = -T, L = the inverted diagonal blocks, both
+// row-major); UP = true solves (I + T)^T X = R from the last block (M = -T^T,
+// L = the transposed inverted blocks).
+template <bool UP>
+__device__ __forceinline__ void block_solve(f32x4 (&x)[4], const float *M, const float *L) {
+    const int l = threadIdx.x & 63, row = l & 15, g = l >> 4;
 #pragma unroll
-    for (int m = C - 1; m > 0; --m) {
+    for (int s = 0; s < 4; ++s) {
+        const int b = UP ? 3 - s : s;
+        f32x4 w = x[b];
 #pragma unroll
-        for (int i4 = 0; i4 < m; i4 += 4) {
-            const f32x4 t = lds4(sT + m * C + i4);
+        for (int c = 0; c < 4; ++c) {
+            if (UP ? c <= b : c >= b) continue;
+            const f32x4 t = *reinterpret_cast<const f32x4 *>(M + (16 * b + row) * LTT + 16 * c + 4 * g);
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (i4 + r < m) x[i4 + r] = fmaf(-t[r], x[m], x[i4 + r]);
+            for (int i = 0; i < 4; ++i) w = __builtin_amdgcn_mfma_f32_16x16x4f32(t[i], x[c][i], w, 0, 0, 0);
         }
+        const f32x4 li = *reinterpret_cast<const f32x4 *>(L + (16 * b + row) * LL + 4 * g);
+        f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y = __builtin_amdgcn_mfma_f32_16x16x4f32(li[i], w[i], y, 0, 0, 0);
+        x[b] = y;
+        __builtin_amdgcn_sched_barrier(0);  // one block at a time: bounds the operands held in registers
     }
 }
 
 template <int D>
 constexpr size_t prep_smem() {
-    constexpr size_t LD = D + 4, R0 = C * LD > C * C ? C * LD : C * C;
+    constexpr size_t LD = D + 4, R0 = C * LD > (size_t)kSolveFloats ? C * LD : kSolveFloats;
     return (R0 + 3 * C * LD + C + kBwdDecRows * D + 4) * 4;
 }
 template <int D>
@@ -213,7 +251,7 @@ constexpr size_t bsweep_smem() {
 }
 template <int D>
 constexpr size_t grad_s_smem() {
-    constexpr size_t LD = D + 4, R0 = C * C > 32 * LD ? C * C : 32 * LD;
+    constexpr size_t LD = D + 4, R0 = kSolveFloats > 32 * LD ? kSolveFloats : 32 * LD;
     return (R0 + 3 * C * LD + 32 * LD) * 4;
 }
 template <int D>
@@ -225,16 +263,16 @@ constexpr size_t grad_out_smem() {
 // 1. Per chunk unit: G, E~, Q~, Kend, Gamma, T, A, then [Y | U_z].
 template <typename IO, int D, bool CHAN, bool BW>
 __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
-    constexpr int LD = Cfg<D>::LD, NL = Cfg<D>::NL, R0 = C * LD > C * C ? C * LD : C * C;
+    constexpr int LD = Cfg<D>::LD, NL = Cfg<D>::NL, R0 = C * LD > kSolveFloats ? C * LD : kSolveFloats;
     extern __shared__ __align__(16) float smem[];
-    float *sQ = smem;           // q (Q~ with a per-channel decay); then T^T, row stride C
+    float *sQ = smem;           // q (Q~ with a per-channel decay); then -T (row stride LTT) and the inverted blocks
     float *sK = sQ + R0;        // k (K~)
     float *sE = sK + C * LD;    // e, then E~, then Y
     float *sZ = sE + C * LD;    // per-channel decay: g, then Gb; then z, then U_z
     float *sGs = sZ + C * LD;   // scalar decay: G per token
     float *sF = sGs + C;        // per-channel decay: the factor table (kBwdDecRows rows of D)
     int *sSlow = reinterpret_cast<int *>(sF + kBwdDecRows * D);  // bit b: block b formed entry by entry
-    const int tid = threadIdx.x, units = a.B * a.Hv * a.NC;
+    const int tid0 = threadIdx.x, units = a.B * a.Hv * a.NC;
     // The workgroups are persistent: each takes units blockIdx.x, + gridDim.x,
     // ..., and fetches the next one's inputs into registers once the current
     // ones are staged in shared memory (before the solve), so that the input
@@ -244,12 +282,12 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
     R4 rq[NL], rk[NL], rb[BW ? NL : 1], rw[BW ? NL : 1], rv[NL];
     f32x4 rg[CHAN ? NL : 1];
     float rbeta[BW ? 1 : NL];
-    const auto fetch = [&](int u) {
+    const auto fetch = [&](int u, int tid) {
         const Unit x = decode(a, u);
 #pragma unroll
         for (int l = 0; l < NL; ++l) {
             int e, t, d;
-            rc<D>(l, e, t, d);
+            rc<D>(l, e, t, d, tid);
             rq[l] = rk[l] = rv[l] = R4{};
             if (BW) rb[l] = rw[l] = R4{};
             else rbeta[l] = 0.f;
@@ -272,18 +310,23 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
     // (With fp32 io the fetched values would not fit in registers beside the
     // solve's; each unit then fetches its own inputs at its start.)
     constexpr bool PREF = sizeof(IO) == 2;
-    if (PREF && (int)blockIdx.x < units) fetch(blockIdx.x);
+    if (PREF && (int)blockIdx.x < units) fetch(blockIdx.x, tid0);
     for (int u = blockIdx.x; u < units; u += gridDim.x) {
+        // The thread index passes through an empty asm statement each
+        // iteration, so that the many index computations derived from it are
+        // redone per unit rather than held in registers across the loop.
+        int tid = tid0;
+        asm volatile("" : "+v"(tid));
         const int un = u + (int)gridDim.x;  // the unit fetched during this one
         const Unit x = decode(a, u);
         const size_t ucd = (size_t)u * C * D;
         if (CHAN && tid == 0) *sSlow = 0;
-        if (!PREF) fetch(u);
+        if (!PREF) fetch(u, tid);
         {
 #pragma unroll
             for (int l = 0; l < NL; ++l) {
                 int e, t, d;
-                rc<D>(l, e, t, d);
+                rc<D>(l, e, t, d, tid);
                 const f32x4 k4 = Raw4<IO>::widen(rk[l]);
                 sts4(sQ + t * LD + d, Raw4<IO>::widen(rq[l]));
                 sts4(sK + t * LD + d, k4);
@@ -336,7 +379,7 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
 #pragma unroll
             for (int l = 0; l < NL; ++l) {
                 int e, t, d;
-                rc<D>(l, e, t, d);
+                rc<D>(l, e, t, d, tid);
                 const f32x4 Gb = lds4(sZ + t * LD + d), Bb = lds4(sZ + (t | 15) * LD + d), eg = exp4(Gb);
                 sts4(wG + e, Gb);
                 sts4(sQ + t * LD + d, lds4(sQ + t * LD + d) * eg);
@@ -350,7 +393,7 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
 #pragma unroll
         for (int l = 0; l < NL; ++l) {
             int e, dd, t;
-            rc<C>(l, e, dd, t);
+            rc<C>(l, e, dd, t, tid);
             f32x4 qv, kv;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -451,11 +494,9 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
                 sts4(a.wT + o, f32x4{aT[i][0], aT[i][1], aT[i][2], aT[i][3]});
                 sts4(a.wA + o, f32x4{aA[i][0], aA[i][1], aA[i][2], aA[i][3]});
             }
-            __syncthreads();  // q, k and e tiles read: T^T goes where q was
+            __syncthreads();  // q, k and e tiles read: -T goes where q was
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) sQ[(c0 + j) * C + r0 + i] = aT[i][j];
+            for (int i = 0; i < 2; ++i) sts4(sQ + (r0 + i) * LTT + c0, -f32x4{aT[i][0], aT[i][1], aT[i][2], aT[i][3]});
         }
         // Right-hand sides: E~ (scalar decay: the raw e scaled by exp(G_t); per
         // channel: E^ scaled by exp(R_b)) and z.
@@ -463,35 +504,51 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
 #pragma unroll
             for (int l = 0; l < NL; ++l) {
                 int e, t, d;
-                rc<D>(l, e, t, d);
+                rc<D>(l, e, t, d, tid);
                 sts4(sZ + t * LD + d, (BW ? Raw4<IO>::widen(rw[BW ? l : 0]) : splat(rbeta[BW ? 0 : l])) * Raw4<IO>::widen(rv[l]));
                 if (!CHAN) sts4(sE + t * LD + d, lds4(sE + t * LD + d) * expf(sGs[t]));
                 else sts4(sE + t * LD + d, lds4(sE + t * LD + d) * lds4(sF + (t >> 4) * D + d));
             }
-            if (PREF && un < units) fetch(un);
+            if (PREF && un < units) fetch(un, tid);
         }
         __syncthreads();
-        // (I + T) X = [E~ | Z], one column per thread.
-        if (tid < 2 * D) {
-            float *X = tid < D ? sE + tid : sZ + (tid - D);
-            float xc[C];
+        // (I + T) X = [E~ | Z] by blocks: the inverted diagonal blocks (wave
+        // 0), then 16-column tiles of E~ and Z, each carried by one wave.
+        float *sL = sQ + C * LTT;
+        if (tid < 64) invert_diag16<false>([&](int i, int k) { return sQ[i * LTT + k]; }, sL);
+        __syncthreads();
+        {
+            constexpr int NTI = D / 8, NQ = (NTI + 7) / 8;  // tiles of [E~ | Z]; per wave
+            const int w = tid >> 6, l = tid & 63;
 #pragma unroll
-            for (int i = 0; i < C; ++i) xc[i] = X[i * LD];
-            solve_lower(xc, sQ);
+            for (int q = 0; q < NQ; ++q) {
+                const int tl = w + 8 * q;
+                if (tl < NTI) {
+                    float *X = (tl < D / 16 ? sE + 16 * tl : sZ + 16 * (tl - D / 16)) + (l & 15) + 4 * (l >> 4) * LD;
+                    f32x4 xt[4];
 #pragma unroll
-            for (int i = 0; i < C; ++i) X[i * LD] = xc[i];
+                    for (int b = 0; b < 4; ++b)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) xt[b][r] = X[(16 * b + r) * LD];
+                    block_solve<false>(xt, sQ, sL);
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) X[(16 * b + r) * LD] = xt[b][r];
+                }
+            }
         }
         __syncthreads();
 #pragma unroll
         for (int l = 0; l < NL; ++l) {
             int e, t, d;
-            rc<D>(l, e, t, d);
+            rc<D>(l, e, t, d, tid);
             sts4(a.wUz + ucd + e, lds4(sZ + t * LD + d));
         }
 #pragma unroll
         for (int l = 0; l < NL; ++l) {  // Y^T
             int e, dd, t;
-            rc<C>(l, e, dd, t);
+            rc<C>(l, e, dd, t, tid);
             sts4(a.wYt + ucd + e, f32x4{sE[t * LD + dd], sE[(t + 1) * LD + dd], sE[(t + 2) * LD + dd], sE[(t + 3) * LD + dd]});
         }
         __syncthreads();  // shared memory read; the next unit overwrites it
@@ -909,10 +966,10 @@ __global__ __launch_bounds__(NS) void cb_sweeps(ChunkBwdArgs a, int items, int P
 //    products with S and dS_next.
 template <typename IO, int D>
 __global__ __launch_bounds__(NT) void cb_grad_s(ChunkBwdArgs a) {
-    constexpr int LD = Cfg<D>::LD, NL = Cfg<D>::NL, R0 = C * C > 32 * LD ? C * C : 32 * LD;
+    constexpr int LD = Cfg<D>::LD, NL = Cfg<D>::NL, R0 = kSolveFloats > 32 * LD ? kSolveFloats : 32 * LD;
     constexpr int NG = 32 * D / 4, NB = (NG + NT - 1) / NT, NTT = C * C / (4 * NT);  // 4-element groups: S block, T
     extern __shared__ __align__(16) float smem[];
-    float *sT = smem;  // T, row stride C; later 32 rows of S
+    float *sT = smem;  // -T^T (row stride LTT) and the inverted blocks; later 32 rows of S
     float *sX = sT + R0, *sU = sX + C * LD, *sO = sU + C * LD, *sB = sO + C * LD;
     const int tid = threadIdx.x, u = blockIdx.x;
     const Unit x = decode(a, u);
@@ -938,7 +995,11 @@ __global__ __launch_bounds__(NT) void cb_grad_s(ChunkBwdArgs a) {
             sts4(sO + t * LD + d, rO[l]);
         }
 #pragma unroll
-        for (int l = 0; l < NTT; ++l) sts4(sT + 4 * (l * NT + tid), rT[l]);  // T, row stride C
+        for (int l = 0; l < NTT; ++l) {  // -T^T
+            const int e = 4 * (l * NT + tid), t = e / C, j = e - t * C;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sT[(j + r) * LTT + t] = -rT[l][r];
+        }
     }
     // The first block of S and dS_next rows is fetched into registers now, so
     // that it arrives during the solve; the barriers up to its use order the
@@ -956,14 +1017,24 @@ __global__ __launch_bounds__(NT) void cb_grad_s(ChunkBwdArgs a) {
     };
     fetch(0);
     lds_barrier();
-    if (tid < D) {  // one column of dU per thread
-        float *X = sX + tid;
-        float xc[C];
+    // (I + T)^T dR = dU by blocks: the inverted diagonal blocks (wave 0), then
+    // one 16-column tile of dU per wave.
+    float *sL = sT + C * LTT;
+    if (tid < 64) invert_diag16<true>([&](int i, int k) { return sT[k * LTT + i]; }, sL);
+    lds_barrier();
+    if ((tid >> 6) < D / 16) {
+        const int l = tid & 63;
+        float *X = sX + 16 * (tid >> 6) + (l & 15) + 4 * (l >> 4) * LD;
+        f32x4 xt[4];
 #pragma unroll
-        for (int i = 0; i < C; ++i) xc[i] = X[i * LD];
-        solve_upper(xc, sT);
+        for (int b = 0; b < 4; ++b)
 #pragma unroll
-        for (int i = 0; i < C; ++i) X[i * LD] = xc[i];
+            for (int r = 0; r < 4; ++r) xt[b][r] = X[(16 * b + r) * LD];
+        block_solve<true>(xt, sT, sL);
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) X[(16 * b + r) * LD] = xt[b][r];
     }
     lds_barrier();
 #pragma unroll
