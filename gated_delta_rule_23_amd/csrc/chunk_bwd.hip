@@ -414,89 +414,130 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
             sts4(a.wKet + ucd + e, kv);
         }
 
-        // T and A: thread = 2 x 4 block of rows r0.., columns c0.. (the rows in
-        // token block bi, the columns in block bj).
+        // T and A on the matrix cores: the ten 16 x 16 tiles (bi, bj) on and
+        // below the block diagonal, T = E^ diag(f) K^T and A = Q^ diag(f) K^T
+        // with the tile's per-channel factor f (none with a scalar decay,
+        // whose factor exp(G_t - G_j) is applied per entry, or next to the
+        // diagonal). Wave w takes tile w and, for w < 2, tile w + 8. Each
+        // product takes its k index in the order 4 (l / 16) + i at step i,
+        // so that a lane's operands are 16-byte reads.
         {
-            const int r0 = (tid >> 4) * 2, c0 = (tid & 15) * 4, bi = r0 >> 4, bj = c0 >> 4;
-            float aT[2][4], aA[2][4];
+            const int w = tid >> 6, l = tid & 63, lr = l & 15, g = l >> 4;
+            const int slow = CHAN ? *sSlow : 0;  // diagonal blocks formed entry by entry below
+            f32x4 tT[2];                         // this lane's T entries of its tiles, for -T after the barrier
+            int tb[2];                           // the tiles' (bi, bj) as 4 bi + bj, or -1
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int q = 0; q < 2; ++q) {
+                const int tile = w + 8 * q;
+                const int bi = tile < 1 ? 0 : tile < 3 ? 1 : tile < 6 ? 2 : 3, bj = tile - bi * (bi + 1) / 2;
+                tb[q] = tile < 10 && !(bi == bj && ((slow >> bi) & 1)) ? 4 * bi + bj : -1;
+                if (tb[q] < 0) continue;
+                const float *fk = !CHAN || bi - bj == 1 ? nullptr
+                                  : sF + (bi == bj ? 7 + bi : bwd_row_far(bi, bj)) * D + 4 * g;
+                const float *pe = sE + (16 * bi + lr) * LD + 4 * g, *pq = sQ + (16 * bi + lr) * LD + 4 * g;
+                const float *pk = sK + (16 * bj + lr) * LD + 4 * g;
+                f32x4 at = zero4(), aa = zero4();
+#pragma unroll 4
+                for (int kb = 0; kb < D; kb += 16) {
+                    const f32x4 e4 = lds4(pe + kb), q4 = lds4(pq + kb);
+                    const f32x4 k4 = fk ? lds4(pk + kb) * lds4(fk + kb) : lds4(pk + kb);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) aT[i][j] = aA[i][j] = 0.f;
-            // Per-channel decay: the tile's factor on the K^ rows (none for bj = bi - 1).
-            const float *fk = !CHAN || bi - bj == 1 ? nullptr
-                              : sF + (bi == bj ? 7 + bi : bwd_row_far(bi, bj)) * D;
-            if (CHAN && bi == bj && ((*sSlow >> bi) & 1)) {
-                // A strongly decaying diagonal block, entry by entry from the
-                // inputs: sum_c e_tc k_jc exp(Gb_tc - Gb_jc) (the same for q).
-                if (c0 <= r0 + 1)
-                    for (int d = 0; d < D; d += 4) {
-                        f32x4 e4[2], q4[2], k4[4], g4[2], h4[4];
-#pragma unroll
-                        for (int i = 0; i < 2; ++i) {
-                            const int t = r0 + i;
-                            const size_t iq = (x.rowq + (size_t)t * a.Hqk) * D + d, iv = (x.rowv + (size_t)t * a.Hv) * D + d;
-                            q4[i] = t < x.n ? ld4io<IO>(a.q, iq) : zero4();
-                            e4[i] = t < x.n ? ld4io<IO>(a.k, iq) *
-                                                  (BW ? ld4io<IO>(a.bg, iv) : splat(a.beta[x.rowv + (size_t)t * a.Hv]))
-                                            : zero4();
-                            g4[i] = lds4(sZ + t * LD + d);
-                        }
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const int t = c0 + j;
-                            k4[j] = t < x.n ? ld4io<IO>(a.k, (x.rowq + (size_t)t * a.Hqk) * D + d) : zero4();
-                            h4[j] = lds4(sZ + t * LD + d);
-                        }
-#pragma unroll
-                        for (int i = 0; i < 2; ++i)
-#pragma unroll
-                            for (int j = 0; j < 4; ++j) {
-                                f32x4 kf;
-#pragma unroll
-                                for (int r = 0; r < 4; ++r) kf[r] = k4[j][r] * expf(fminf(g4[i][r] - h4[j][r], 0.f));
-                                aT[i][j] = dot4(e4[i], kf, aT[i][j]);
-                                aA[i][j] = dot4(q4[i], kf, aA[i][j]);
-                            }
+                    for (int i = 0; i < 4; ++i) {
+                        at = __builtin_amdgcn_mfma_f32_16x16x4f32(e4[i], k4[i], at, 0, 0, 0);
+                        aa = __builtin_amdgcn_mfma_f32_16x16x4f32(q4[i], k4[i], aa, 0, 0, 0);
                     }
-            } else if (c0 <= r0 + 1) {
-#pragma unroll 2
-                for (int d = 0; d < D; d += 4) {
-                    f32x4 e4[2], q4[2], k4[4];
+                }
+                const int j = 16 * bj + lr;
 #pragma unroll
-                    for (int i = 0; i < 2; ++i) {
-                        e4[i] = lds4(sE + (r0 + i) * LD + d);
-                        q4[i] = lds4(sQ + (r0 + i) * LD + d);
-                    }
-                    const f32x4 f4 = fk ? lds4(fk + d) : splat(1.f);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) k4[j] = lds4(sK + (c0 + j) * LD + d) * f4;
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * bi + 4 * g + r;
+                    const float f = !CHAN && j <= t ? expf(sGs[t] - sGs[j]) : 1.f;
+                    tT[q][r] = j < t ? at[r] * f : 0.f;
+                    const size_t o = (size_t)u * C * C + (size_t)t * C + j;
+                    a.wT[o] = tT[q][r];
+                    a.wA[o] = j <= t ? aa[r] * f : 0.f;
+                }
+            }
+            // The six tiles above the block diagonal are zero: rows 0-15 from
+            // column 16 on (12 groups of 4 per row), rows 16-31 from column 32
+            // (8), rows 32-47 from column 48 (4); 384 groups per matrix.
+            for (int i = tid; i < 2 * 384; i += NT) {
+                const int k = i % 384;
+                const int t = k < 192 ? k / 12 : k < 320 ? 16 + (k - 192) / 8 : 32 + (k - 320) / 4;
+                const int j = 4 * (k < 192 ? 4 + k % 12 : k < 320 ? 8 + (k - 192) % 8 : 12 + (k - 320) % 4);
+                sts4((i < 384 ? a.wT : a.wA) + (size_t)u * C * C + (size_t)t * C + j, zero4());
+            }
+            // A strongly decaying diagonal block, entry by entry from the
+            // inputs: sum_c e_tc k_jc exp(Gb_tc - Gb_jc) (the same for q).
+            // Thread = 2 x 4 block of rows r0.., columns c0.. of the block.
+            float sT8[2][4];
+            bool sOwn = false;
+            const int r0 = (tid >> 4) * 2, c0 = (tid & 15) * 4;
+            if (CHAN && slow) {
+                const int bi = r0 >> 4, bj = c0 >> 4;
+                if (bi == bj && ((slow >> bi) & 1)) {
+                    sOwn = true;
+                    float aT[2][4], aA[2][4];
 #pragma unroll
                     for (int i = 0; i < 2; ++i)
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            aT[i][j] = dot4(e4[i], k4[j], aT[i][j]);
-                            aA[i][j] = dot4(q4[i], k4[j], aA[i][j]);
+                        for (int j = 0; j < 4; ++j) aT[i][j] = aA[i][j] = 0.f;
+                    if (c0 <= r0 + 1)
+                        for (int d = 0; d < D; d += 4) {
+                            f32x4 e4[2], q4[2], k4[4], g4[2], h4[4];
+#pragma unroll
+                            for (int i = 0; i < 2; ++i) {
+                                const int t = r0 + i;
+                                const size_t iq = (x.rowq + (size_t)t * a.Hqk) * D + d, iv = (x.rowv + (size_t)t * a.Hv) * D + d;
+                                q4[i] = t < x.n ? ld4io<IO>(a.q, iq) : zero4();
+                                e4[i] = t < x.n ? ld4io<IO>(a.k, iq) *
+                                                      (BW ? ld4io<IO>(a.bg, iv) : splat(a.beta[x.rowv + (size_t)t * a.Hv]))
+                                                : zero4();
+                                g4[i] = lds4(sZ + t * LD + d);
+                            }
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                const int t = c0 + j;
+                                k4[j] = t < x.n ? ld4io<IO>(a.k, (x.rowq + (size_t)t * a.Hqk) * D + d) : zero4();
+                                h4[j] = lds4(sZ + t * LD + d);
+                            }
+#pragma unroll
+                            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                                for (int j = 0; j < 4; ++j) {
+                                    f32x4 kf;
+#pragma unroll
+                                    for (int r = 0; r < 4; ++r) kf[r] = k4[j][r] * expf(fminf(g4[i][r] - h4[j][r], 0.f));
+                                    aT[i][j] = dot4(e4[i], kf, aT[i][j]);
+                                    aA[i][j] = dot4(q4[i], kf, aA[i][j]);
+                                }
                         }
-                }
-            }
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int t = r0 + i;
+                    for (int i = 0; i < 2; ++i) {
+                        const int t = r0 + i;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int jj = c0 + j;
-                    const float f = !CHAN && jj <= t ? expf(sGs[t] - sGs[jj]) : 1.f;
-                    aT[i][j] = jj < t ? aT[i][j] * f : 0.f;
-                    aA[i][j] = jj <= t ? aA[i][j] * f : 0.f;
+                        for (int j = 0; j < 4; ++j) {
+                            sT8[i][j] = c0 + j < t ? aT[i][j] : 0.f;
+                            aA[i][j] = c0 + j <= t ? aA[i][j] : 0.f;
+                        }
+                        const size_t o = (size_t)u * C * C + (size_t)t * C + c0;
+                        sts4(a.wT + o, f32x4{sT8[i][0], sT8[i][1], sT8[i][2], sT8[i][3]});
+                        sts4(a.wA + o, f32x4{aA[i][0], aA[i][1], aA[i][2], aA[i][3]});
+                    }
                 }
-                const size_t o = (size_t)u * C * C + (size_t)t * C + c0;
-                sts4(a.wT + o, f32x4{aT[i][0], aT[i][1], aT[i][2], aT[i][3]});
-                sts4(a.wA + o, f32x4{aA[i][0], aA[i][1], aA[i][2], aA[i][3]});
             }
             __syncthreads();  // q, k and e tiles read: -T goes where q was
 #pragma unroll
-            for (int i = 0; i < 2; ++i) sts4(sQ + (r0 + i) * LTT + c0, -f32x4{aT[i][0], aT[i][1], aT[i][2], aT[i][3]});
+            for (int q = 0; q < 2; ++q)
+                if (tb[q] >= 0) {
+                    const int bi = tb[q] >> 2, bj = tb[q] & 3;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sQ[(16 * bi + 4 * g + r) * LTT + 16 * bj + lr] = -tT[q][r];
+                }
+            if (sOwn)
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    sts4(sQ + (r0 + i) * LTT + c0, -f32x4{sT8[i][0], sT8[i][1], sT8[i][2], sT8[i][3]});
         }
         // Right-hand sides: E~ (scalar decay: the raw e scaled by exp(G_t); per
         // channel: E^ scaled by exp(R_b)) and z.
