@@ -409,6 +409,8 @@ int bwd_call(bool chunked, const gdr_desc *d, const void *q, const void *k, cons
             *arr[i] = L.floats[i] ? reinterpret_cast<float *>(p) : nullptr;
             p += gdr::align256(L.floats[i] * 4);
         }
+        a.wP = a.wdE;  // p and b of the backward sweep (see ChunkBwdArgs); wdK follows wdQ directly
+        a.wB = a.wdQ;
         a.B = d->B; a.T = d->T; a.Hqk = d->H_qk; a.Hv = d->H_v; a.decay = d->decay; a.scale = d->scale;
         a.NC = (int)chunks;
         e = gdr::launch_chunk_backward(io, d->d_k, a, static_cast<hipStream_t>(stream));

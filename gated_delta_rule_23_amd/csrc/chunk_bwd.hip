@@ -156,8 +156,8 @@ __device__ __forceinline__ void rc(int l, int &e, int &t, int &d) {
 }
 
 // Workgroup barrier ordering shared-memory accesses only: it does not wait
-// for global loads in flight (the sweeps' prefetch of the next chunk) or
-// for global stores, which nothing in the same launch reads back.
+// for global loads in flight (the prefetch of the next chunk or unit) or for
+// global stores, which no other thread of the same launch reads back.
 __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
@@ -246,8 +246,16 @@ constexpr size_t fsweep_smem() {
     return ((size_t)D * LB + (size_t)C * LB + (size_t)D * LT + (size_t)D * LC + D) * 4;
 }
 template <int D>
-constexpr size_t bsweep_smem() {
+constexpr size_t bsweep_full_smem() {
     return ((size_t)D * LB + 2 * (size_t)C * LB + (size_t)C * LT + 3 * (size_t)D * LC + D) * 4;
+}
+template <int D>
+constexpr size_t bsweep_rhs_smem() {
+    return ((size_t)D * LB + (size_t)C * LB + 2 * (size_t)D * LC + D) * 4;
+}
+template <int D>
+constexpr size_t rhs_smem() {
+    return (2 * (size_t)D * LC + (size_t)C * LC + (size_t)C * (D + 16)) * 4;
 }
 template <int D>
 constexpr size_t grad_s_smem() {
@@ -335,7 +343,7 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
             }
         }
         if (!CHAN && tid < C) sGs[tid] = a.g && tid < x.n ? a.g[x.rowv + (size_t)tid * a.Hv] : 0.f;
-        __syncthreads();
+        lds_barrier();
         if (CHAN) {
             if (tid < D) {  // per channel: the column into registers, summed per block, written back
                 float gc[C];
@@ -372,7 +380,7 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
             }
             sGs[tid] = G;
         }
-        __syncthreads();
+        lds_barrier();
 
         float *wG = a.wG + ucd;  // [C][D] per-channel decay (Gb), [C] scalar (G)
         if (CHAN)  // Q^, K^, E^ in place of q, k, e
@@ -388,7 +396,7 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
             }
         if (!CHAN && tid < C) wG[tid] = sGs[tid];
         if (!CHAN && tid < D) a.wGam[(size_t)u * D + tid] = expf(sGs[C - 1]);
-        __syncthreads();
+        lds_barrier();
         // Q~^T and Kend^T (row = channel), which the sweeps over chunks read.
 #pragma unroll
         for (int l = 0; l < NL; ++l) {
@@ -526,7 +534,7 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
                     }
                 }
             }
-            __syncthreads();  // q, k and e tiles read: -T goes where q was
+            lds_barrier();  // q, k and e tiles read: -T goes where q was
 #pragma unroll
             for (int q = 0; q < 2; ++q)
                 if (tb[q] >= 0) {
@@ -552,12 +560,12 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
             }
             if (PREF && un < units) fetch(un, tid);
         }
-        __syncthreads();
+        lds_barrier();
         // (I + T) X = [E~ | Z] by blocks: the inverted diagonal blocks (wave
         // 0), then 16-column tiles of E~ and Z, each carried by one wave.
         float *sL = sQ + C * LTT;
         if (tid < 64) invert_diag16<false>([&](int i, int k) { return sQ[i * LTT + k]; }, sL);
-        __syncthreads();
+        lds_barrier();
         {
             constexpr int NTI = D / 8, NQ = (NTI + 7) / 8;  // tiles of [E~ | Z]; per wave
             const int w = tid >> 6, l = tid & 63;
@@ -579,7 +587,7 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int l = 0; l < NL; ++l) {
             int e, t, d;
@@ -592,7 +600,7 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
             rc<C>(l, e, dd, t, tid);
             sts4(a.wYt + ucd + e, f32x4{sE[t * LD + dd], sE[(t + 1) * LD + dd], sE[(t + 2) * LD + dd], sE[(t + 3) * LD + dd]});
         }
-        __syncthreads();  // shared memory read; the next unit overwrites it
+        lds_barrier();  // shared memory read; the next unit overwrites it
     }
 }
 
@@ -669,6 +677,88 @@ __device__ __forceinline__ void static_for(F &&f) {
     if constexpr (I0 < I1) {
         f(std::integral_constant<int, I0>{});
         static_for<I0 + 1, I1>(f);
+    }
+}
+
+// 1b. Per chunk unit, the parts of the backward sweep's step that do not
+//     depend on dL/dS: p = s A^T dO and b = s P^T dO with P = Q~ - A Y. Then
+//     dU = p + Kend dS_next and dS = Diag(Gamma) dS_next + b - Y^T Kend dS_next,
+//     since s Q~^T dO - Y^T (s A^T dO) = s (Q~ - A Y)^T dO. The products run
+//     on the matrix cores in 16 x 16 tiles, wave w taking tiles w, w + 8, ...
+//     p goes to wP ([units][C][D]) and b to wB ([units][D][D]).
+template <typename IO, int D>
+__global__ __launch_bounds__(NT) void cb_rhs(ChunkBwdArgs a) {
+    constexpr int NL = Cfg<D>::NL, NTT = C * C / (4 * NT), LO = D + 16, NQT = (D / 4 + 7) / 8;
+    extern __shared__ __align__(16) float smem[];
+    float *sYn = smem;          // -Y^T [D][LC]
+    float *sAt = sYn + D * LC;  // A^T [C][LC]
+    float *sPt = sAt + C * LC;  // P^T [D][LC]
+    float *sO = sPt + D * LC;   // dO [C][LO]
+    const int tid = threadIdx.x, u = blockIdx.x, w = tid >> 6, l = tid & 63;
+    const Unit x = decode(a, u);
+    const size_t ucd = (size_t)u * C * D, ucc = (size_t)u * C * C, udd = (size_t)u * D * D;
+    f32x4 qacc[NQT];  // this lane's Q~^T entries of its P^T tiles, loaded with the other operands
+    {
+        f32x4 rY[NL], rO[NL], rA[NTT];
+#pragma unroll
+        for (int l2 = 0; l2 < NL; ++l2) {
+            int e, t, d;
+            rc<D>(l2, e, t, d);
+            rY[l2] = lds4(a.wYt + ucd + e);
+            rO[l2] = t < x.n ? ld4io<IO>(a.dO, (x.rowv + (size_t)t * a.Hv) * D + d) : zero4();
+        }
+#pragma unroll
+        for (int l2 = 0; l2 < NTT; ++l2) rA[l2] = lds4(a.wA + ucc + 4 * (l2 * NT + tid));
+#pragma unroll
+        for (int q = 0; q < NQT; ++q) {
+            const int tile = w + 8 * q, rt = tile >> 2, ct = tile & 3;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                qacc[q][r] = tile < D / 4 ? a.wQt[ucd + (size_t)(rt * 16 + 4 * (l >> 4) + r) * C + ct * 16 + (l & 15)] : 0.f;
+        }
+#pragma unroll
+        for (int l2 = 0; l2 < NL; ++l2) {
+            int e, dd, t;
+            rc<C>(l2, e, dd, t);
+            sts4(sYn + dd * LC + t, -rY[l2]);
+            rc<D>(l2, e, t, dd);
+            sts4(sO + t * LO + dd, rO[l2]);
+        }
+#pragma unroll
+        for (int l2 = 0; l2 < NTT; ++l2) {  // A^T
+            const int e = 4 * (l2 * NT + tid), t = e / C, j = e - t * C;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sAt[(j + r) * LC + t] = rA[l2][r];
+        }
+    }
+    lds_barrier();
+    // The products in 16 x 16 tiles, wave w taking tiles w, w + 8, ...
+    // P^T = Q~^T - Y^T A^T: (D / 16) x 4 tiles; Q~^T enters as the accumulator.
+#pragma unroll
+    for (int q = 0; q < NQT; ++q) {
+        const int tile = w + 8 * q, rt = tile >> 2, ct = tile & 3;
+        if (tile < D / 4) {
+            const f32x4 acc = mfma_kloop<C>(qacc[q], sYn + rt * 16 * LC, LC, sAt + ct * 16, LC);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sPt[(rt * 16 + 4 * (l >> 4) + r) * LC + ct * 16 + (l & 15)] = acc[r];
+        }
+    }
+    // p = s A^T dO: 4 x (D / 16) tiles.
+    for (int tile = w; tile < D / 4; tile += 8) {
+        const int rt = tile / (D / 16), ct = tile % (D / 16);
+        const f32x4 acc = mfma_kloop<C>(zero4(), sAt + rt * 16 * LC, LC, sO + ct * 16, LO);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            a.wP[ucd + (size_t)(rt * 16 + 4 * (l >> 4) + r) * D + ct * 16 + (l & 15)] = a.scale * acc[r];
+    }
+    lds_barrier();
+    // b = s P^T dO: (D / 16) x (D / 16) tiles.
+    for (int tile = w; tile < D * D / 256; tile += 8) {
+        const int rt = tile / (D / 16), ct = tile % (D / 16);
+        const f32x4 acc = mfma_kloop<C>(zero4(), sPt + rt * 16 * LC, LC, sO + ct * 16, LO);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            a.wB[udd + (size_t)(rt * 16 + 4 * (l >> 4) + r) * D + ct * 16 + (l & 15)] = a.scale * acc[r];
     }
 }
 
@@ -810,8 +900,14 @@ __device__ __forceinline__ void fsweep(const ChunkBwdArgs &a, float *smem, int i
 
 // 2b. Backward over chunks for the same work items: X = dL/d(state leaving
 //    the chunk), dU, and X for the chunk before. Tiles per wave as above.
+//    Two forms: bsweep_full forms every product of the step itself (four
+//    per chunk); bsweep_rhs takes the two that do not depend on X from
+//    cb_rhs (two per chunk on the chain). The second pays when the sweep's
+//    serial chain bounds the call (few sequences and heads, most compute
+//    units idle); with enough work items to fill the GPU, cb_rhs's extra
+//    pass over the units costs more than the sweep saves.
 template <typename IO, int D>
-__device__ __forceinline__ void bsweep(const ChunkBwdArgs &a, float *smem, int item) {
+__device__ __forceinline__ void bsweep_full(const ChunkBwdArgs &a, float *smem, int item) {
     using K = SwCfg<D>;
     constexpr int NTL = K::NTL, NL = K::NL, NST = D / 16 * 2;
     constexpr int NA = C * C / (4 * NS), NO = C * BV / (4 * NS);  // 4-element groups per thread: A, dO tile
@@ -985,6 +1081,158 @@ __device__ __forceinline__ void bsweep(const ChunkBwdArgs &a, float *smem, int i
         }
 }
 
+// With p = s A^T dO and b = s P^T dO from cb_rhs, V = Kend X gives dU = p +
+// V and the X of the chunk before, Gamma . X + b - Y^T V.
+template <typename IO, int D>
+__device__ __forceinline__ void bsweep_rhs(const ChunkBwdArgs &a, float *smem, int item) {
+    using K = SwCfg<D>;
+    constexpr int NTL = K::NTL, NL = K::NL, NST = D / 16 * 2;
+    constexpr int NXT = NST > 8 ? 2 : 1;  // X tiles per wave
+    float *sX = smem, *sV = sX + D * LB;  // X [D][LB]; V = Kend X [C][LB]
+    float *sKt = sV + C * LB;             // Kend^T [D][LC]
+    float *sYt = sKt + D * LC;            // Y^T [D][LC]
+    float *sGam = sYt + D * LC;           // [D]
+    const int tid = threadIdx.x, tile = item % NTL, bh = item / NTL, col0 = tile * BV;
+    const int w = tid >> 6, l = tid & 63, rt = w >> 1, ct = w & 1, sc = w & 1;
+    const size_t sb = (size_t)bh * D * D;
+    bool on[NXT];
+#pragma unroll
+    for (int q = 0; q < NXT; ++q) on[q] = NST >= 8 * (q + 1) || w + 8 * q < NST;
+    for (int i = tid; i < D * BV / 4; i += NS) {
+        const int d = 4 * i / BV, j = 4 * i - d * BV;
+        sts4(sX + d * LB + j, a.dST ? lds4(a.dST + sb + (size_t)d * D + col0 + j) : zero4());
+    }
+    // A chunk's operands, fetched by the whole workgroup one chunk ahead. The
+    // loads are numbered -- Kend^T (NL per thread), this lane's 4 entries of
+    // p, its 4 entries of b per X tile, Gamma (1), Y^T (NL) -- and spread
+    // over the pieces of the current chunk's products, so that their latency
+    // overlaps the matrix cores' work rather than stalling every wave at once.
+    f32x4 pY[NL], pK[NL], pP, pB[NXT];
+    float pg;
+    constexpr int NLD = 2 * NL + 4 + 4 * NXT + 1;
+    const auto load = [&](auto ic, int c) {
+        constexpr int i = decltype(ic)::value;
+        const size_t u = (size_t)bh * a.NC + c, ucd = u * C * D;
+        if constexpr (i < NL) {
+            pK[i] = lds4(a.wKet + ucd + 4 * (i * NS + tid));  // [D][C]
+        } else if constexpr (i < NL + 4) {
+            constexpr int r = i - NL;
+            pP[r] = a.wP[ucd + (size_t)(rt * 16 + 4 * (l >> 4) + r) * D + col0 + ct * 16 + (l & 15)];
+        } else if constexpr (i < NL + 4 + 4 * NXT) {
+            constexpr int q = (i - NL - 4) / 4, r = (i - NL - 4) % 4;
+            const int row = ((w + 8 * q) >> 1) * 16 + 4 * (l >> 4) + r;
+            pB[q][r] = on[q] ? a.wB[u * D * D + (size_t)row * D + col0 + sc * 16 + (l & 15)] : 0.f;
+        } else if constexpr (i == NL + 4 + 4 * NXT) {
+            pg = tid < D ? a.wGam[u * D + tid] : 0.f;
+        } else {
+            pY[i - (NL + 5 + 4 * NXT)] = lds4(a.wYt + ucd + 4 * ((i - (NL + 5 + 4 * NXT)) * NS + tid));  // [D][C]
+        }
+    };
+    // The chunk's products run in NG pieces of 8 matrix instructions per
+    // tile; after piece g come loads [g NLD / NG, (g + 1) NLD / NG), fenced so
+    // that the compiler keeps them there.
+    constexpr int NG = D / 32 + C / 16;
+    const auto spread = [&](auto gc, int c) {
+        constexpr int g = decltype(gc)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<g * NLD / NG, (g + 1) * NLD / NG>([&](auto ic) { load(ic, c); });
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    static_for<0, NLD>([&](auto ic) { load(ic, a.NC - 1); });
+    for (int c = a.NC - 1; c >= 0; --c) {
+        const size_t u = (size_t)bh * a.NC + c, ucd = u * C * D;
+        const int cn = c > 0 ? c - 1 : 0;  // the chunk fetched during this one (at c = 0 the loads go unused)
+        lds_barrier();  // X written; the previous chunk is done with the operand tiles
+#pragma unroll
+        for (int l2 = 0; l2 < NL; ++l2) {
+            int e, d, t;
+            rcs<C>(l2, e, d, t);
+            sts4(sKt + d * LC + t, pK[l2]);
+            sts4(sYt + d * LC + t, pY[l2]);
+        }
+        if (tid < D) sGam[tid] = pg;
+        const f32x4 pv = pP;
+        f32x4 bv[NXT];
+#pragma unroll
+        for (int q = 0; q < NXT; ++q) bv[q] = pB[q];
+        for (int i = tid; i < D * BV / 4; i += NS) {
+            const int d = 4 * i / BV, j = 4 * i - d * BV;
+            sts4(a.wdS + u * D * D + (size_t)d * D + col0 + j, lds4(sX + d * LB + j));
+        }
+        lds_barrier();
+        {  // V = Kend X; dU = p + V
+            f32x4 k0 = zero4(), k1 = zero4();
+            static_for<0, D / 32>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                mfma_krange_at<32 * j, 32 * j + 32>(k0, k1, sKt + rt * 16, LC, sX + ct * 16, LB);
+                spread(jc, cn);
+            });
+            const f32x4 k = k0 + k1;
+            const int col = ct * 16 + (l & 15);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = rt * 16 + 4 * (l >> 4) + r;
+                sV[row * LB + col] = k[r];
+                a.wdU[ucd + (size_t)row * D + col0 + col] = pv[r] + k[r];
+            }
+        }
+        lds_barrier();
+        // X = Gamma . X + b - Y^T V. A wave's tiles share their columns, so
+        // each k step reads the V operand once for both.
+        f32x4 xn[NXT];
+        {
+            const float *pbv = sV + sc * 16 + (l >> 4) * LB + (l & 15);
+            const float *pay[NXT];
+            f32x4 ay[NXT][2];
+#pragma unroll
+            for (int q = 0; q < NXT; ++q) {
+                pay[q] = sYt + (((w + 8 * q) >> 1) * 16 + (l & 15)) * LC + (l >> 4);
+                ay[q][0] = ay[q][1] = zero4();
+            }
+            static_for<0, C / 16>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+#pragma unroll
+                for (int k = 16 * j; k < 16 * j + 16; k += 8) {
+                    const float b0 = pbv[k * LB], b1 = pbv[(k + 4) * LB];
+#pragma unroll
+                    for (int q = 0; q < NXT; ++q)
+                        if (on[q]) {
+                            ay[q][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(pay[q][k], b0, ay[q][0], 0, 0, 0);
+                            ay[q][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pay[q][k + 4], b1, ay[q][1], 0, 0, 0);
+                        }
+                }
+                spread(std::integral_constant<int, D / 32 + j>{}, cn);
+            });
+#pragma unroll
+            for (int q = 0; q < NXT; ++q)
+                if (on[q]) {
+                    const int dt = (w + 8 * q) >> 1;
+                    const f32x4 py = ay[q][0] + ay[q][1];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = dt * 16 + 4 * (l >> 4) + r;
+                        xn[q][r] = sGam[row] * sX[row * LB + sc * 16 + (l & 15)] + bv[q][r] - py[r];
+                    }
+                }
+        }
+        // No barrier: each wave rewrites only the entries of X it has just
+        // read, and every other read of X in this chunk was before the last one.
+#pragma unroll
+        for (int q = 0; q < NXT; ++q) {
+            const int dt = (w + 8 * q) >> 1;
+            if (on[q])
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sX[(dt * 16 + 4 * (l >> 4) + r) * LB + sc * 16 + (l & 15)] = xn[q][r];
+        }
+    }
+    lds_barrier();
+    if (a.dS0)
+        for (int i = tid; i < D * BV / 4; i += NS) {
+            const int d = 4 * i / BV, j = 4 * i - d * BV;
+            sts4(a.dS0 + sb + (size_t)d * D + col0 + j, lds4(sX + d * LB + j));
+        }
+}
+
 // The two sweeps do not depend on each other (the chain of dL/dS does not
 // use the forward states), so one launch runs both: the backward sweep's
 // workgroups first, then the forward sweep's, which fill the CUs the first
@@ -992,14 +1240,15 @@ __device__ __forceinline__ void bsweep(const ChunkBwdArgs &a, float *smem, int i
 // workgroups (items rounded up to a multiple of 8); workgroups that share an
 // XCD (block index mod 8) take consecutive work items, so that the value
 // tiles of one head read its chunk factors through the same L2.
-template <typename IO, int D>
+template <typename IO, int D, bool RHS>
 __global__ __launch_bounds__(NS) void cb_sweeps(ChunkBwdArgs a, int items, int P) {
     extern __shared__ __align__(16) float smem[];
     const int x = (int)blockIdx.x, back = x < P, xl = back ? x : x - P;
     const int wi = (xl & 7) * (P >> 3) + (xl >> 3);
     if (wi >= items) return;
-    if (back) bsweep<IO, D>(a, smem, wi);
-    else fsweep<D>(a, smem, wi);
+    if (!back) fsweep<D>(a, smem, wi);
+    else if constexpr (RHS) bsweep_rhs<IO, D>(a, smem, wi);
+    else bsweep_full<IO, D>(a, smem, wi);
 }
 
 // ---------------------------------------------------------------------------
@@ -1519,15 +1768,18 @@ __global__ __launch_bounds__(NT) void cb_group_sum(ChunkBwdArgs a) {
 
 template <typename IO, int D, bool CHAN, bool BW>
 hipError_t run(const ChunkBwdArgs &a, hipStream_t s) {
-    constexpr size_t sweep_smem = bsweep_smem<D>() > fsweep_smem<D>() ? bsweep_smem<D>() : fsweep_smem<D>();
+    constexpr size_t bmax = bsweep_full_smem<D>() > bsweep_rhs_smem<D>() ? bsweep_full_smem<D>() : bsweep_rhs_smem<D>();
+    constexpr size_t sweep_smem = bmax > fsweep_smem<D>() ? bmax : fsweep_smem<D>();
     static_assert(sweep_smem <= 160 * 1024, "the sweeps' tiles exceed a workgroup's local data share");
     static const hipError_t attr = [] {
-        const void *fn[4] = {reinterpret_cast<const void *>(&cb_prep<IO, D, CHAN, BW>),
-                             reinterpret_cast<const void *>(&cb_sweeps<IO, D>),
+        const void *fn[6] = {reinterpret_cast<const void *>(&cb_prep<IO, D, CHAN, BW>),
+                             reinterpret_cast<const void *>(&cb_rhs<IO, D>),
+                             reinterpret_cast<const void *>(&cb_sweeps<IO, D, false>),
+                             reinterpret_cast<const void *>(&cb_sweeps<IO, D, true>),
                              reinterpret_cast<const void *>(&cb_grad_s<IO, D>),
                              reinterpret_cast<const void *>(&cb_grad_out<IO, D, CHAN, BW>)};
-        const size_t bytes[4] = {prep_smem<D>(), sweep_smem, grad_s_smem<D>(), grad_out_smem<D>()};
-        for (int i = 0; i < 4; ++i) {
+        const size_t bytes[6] = {prep_smem<D>(), rhs_smem<D>(), sweep_smem, sweep_smem, grad_s_smem<D>(), grad_out_smem<D>()};
+        for (int i = 0; i < 6; ++i) {
             const hipError_t e = hipFuncSetAttribute(fn[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes[i]);
             if (e != hipSuccess) return e;
         }
@@ -1539,7 +1791,15 @@ hipError_t run(const ChunkBwdArgs &a, hipStream_t s) {
     const unsigned pgrid = units < (unsigned)device_cus() ? units : (unsigned)device_cus();
     hipLaunchKernelGGL((cb_prep<IO, D, CHAN, BW>), dim3(pgrid), dim3(NT), prep_smem<D>(), s, a);
     const unsigned P = (items + 7) / 8 * 8;
-    hipLaunchKernelGGL((cb_sweeps<IO, D>), dim3(2 * P), dim3(NS), sweep_smem, s, a, (int)items, (int)P);
+    // The X-independent products leave the backward sweep's chain when both
+    // sweeps' workgroups fit on the compute units at once (the chain then
+    // bounds the call).
+    if (2 * P <= (unsigned)device_cus()) {
+        hipLaunchKernelGGL((cb_rhs<IO, D>), dim3(units), dim3(NT), rhs_smem<D>(), s, a);
+        hipLaunchKernelGGL((cb_sweeps<IO, D, true>), dim3(2 * P), dim3(NS), sweep_smem, s, a, (int)items, (int)P);
+    } else {
+        hipLaunchKernelGGL((cb_sweeps<IO, D, false>), dim3(2 * P), dim3(NS), sweep_smem, s, a, (int)items, (int)P);
+    }
     hipLaunchKernelGGL((cb_grad_s<IO, D>), dim3(units), dim3(NT), grad_s_smem<D>(), s, a);
     hipLaunchKernelGGL((cb_grad_out<IO, D, CHAN, BW>), dim3(units), dim3(NT), grad_out_smem<D>(), s, a);
     if (a.Hv > a.Hqk) {

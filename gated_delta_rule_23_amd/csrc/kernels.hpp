@@ -214,6 +214,11 @@ struct ChunkBwdArgs {
     float *wGam, *wdGam;          // [units][D]: exp(G_end); rowsum(dS_next . S)
     float *wdq, *wdk;             // [B][T][Hv][D] per-V-head parts (grouped heads), else null
     float *wYt, *wKet;            // [units][D][C]: Y^T (Y = L E~), Kend^T
+    // Not separate arrays: p = s A^T dO and b = s (Q~ - A Y)^T dO of the
+    // backward sweep, from its first kernel to its last reader, live where
+    // cb_grad_s later writes -dR S^T (wP = wdE) and s dO S^T, U dS_next^T
+    // (wB = wdQ, which with wdK after it holds 2 C D >= D D floats per unit).
+    float *wP, *wB;
     int B, T, Hqk, Hv, decay, NC;
     float scale;
 };
