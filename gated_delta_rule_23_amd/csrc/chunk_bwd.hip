@@ -1261,41 +1261,34 @@ __global__ __launch_bounds__(NT) void cb_grad_s(ChunkBwdArgs a) {
     extern __shared__ __align__(16) float smem[];
     float *sT = smem;  // -T^T (row stride LTT) and the inverted blocks; later 32 rows of S
     float *sX = sT + R0, *sU = sX + C * LD, *sO = sU + C * LD, *sB = sO + C * LD;
-    const int tid = threadIdx.x, u = blockIdx.x;
-    const Unit x = decode(a, u);
-    const size_t ucd = (size_t)u * C * D, ucc = (size_t)u * C * C, udd = (size_t)u * D * D;
-    {
-        f32x4 rX[NL], rU[NL], rO[NL], rT[NTT];
+    const int tid0 = threadIdx.x, units = a.B * a.Hv * a.NC;
+    // Persistent, as cb_prep: each workgroup takes units blockIdx.x, +
+    // gridDim.x, ..., and fetches the next unit's dU, U, dO and T into
+    // registers (dO in the io type) while it works on the current one; the
+    // barriers order shared memory only and do not wait for them. Each
+    // unit's S and dS_next rows come in blocks of 32, the next block fetched
+    // while the current one is used (the first block of the next unit during
+    // the current unit's last).
+    using R4 = typename Raw4<IO>::type;
+    f32x4 rX[NL], rU[NL], rT[NTT];
+    R4 rO[NL];
+    const auto fetch_unit = [&](int u, int tid) {
+        const Unit x = decode(a, u);
+        const size_t ucd = (size_t)u * C * D, ucc = (size_t)u * C * C;
 #pragma unroll
         for (int l = 0; l < NL; ++l) {
             int e, t, d;
-            rc<D>(l, e, t, d);
+            rc<D>(l, e, t, d, tid);
             rX[l] = lds4(a.wdU + ucd + e);
             rU[l] = lds4(a.wU + ucd + e);
-            rO[l] = t < x.n ? ld4io<IO>(a.dO, (x.rowv + (size_t)t * a.Hv) * D + d) : zero4();
+            rO[l] = t < x.n ? Raw4<IO>::load(static_cast<const IO *>(a.dO) + (x.rowv + (size_t)t * a.Hv) * D + d) : R4{};
         }
 #pragma unroll
         for (int l = 0; l < NTT; ++l) rT[l] = lds4(a.wT + ucc + 4 * (l * NT + tid));
-#pragma unroll
-        for (int l = 0; l < NL; ++l) {
-            int e, t, d;
-            rc<D>(l, e, t, d);
-            sts4(sX + t * LD + d, rX[l]);
-            sts4(sU + t * LD + d, rU[l]);
-            sts4(sO + t * LD + d, rO[l]);
-        }
-#pragma unroll
-        for (int l = 0; l < NTT; ++l) {  // -T^T
-            const int e = 4 * (l * NT + tid), t = e / C, j = e - t * C;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sT[(j + r) * LTT + t] = -rT[l][r];
-        }
-    }
-    // The first block of S and dS_next rows is fetched into registers now, so
-    // that it arrives during the solve; the barriers up to its use order the
-    // shared tiles only and do not wait for it.
+    };
     f32x4 rb[NB], rs[NB];
-    const auto fetch = [&](int blk) {
+    const auto fetch = [&](int u, int blk, int tid) {
+        const size_t udd = (size_t)u * D * D;
 #pragma unroll
         for (int l = 0; l < NB; ++l) {
             const int g = l * NT + tid;
@@ -1305,112 +1298,138 @@ __global__ __launch_bounds__(NT) void cb_grad_s(ChunkBwdArgs a) {
             }
         }
     };
-    fetch(0);
-    lds_barrier();
-    // (I + T)^T dR = dU by blocks: the inverted diagonal blocks (wave 0), then
-    // one 16-column tile of dU per wave.
-    float *sL = sT + C * LTT;
-    if (tid < 64) invert_diag16<true>([&](int i, int k) { return sT[k * LTT + i]; }, sL);
-    lds_barrier();
-    if ((tid >> 6) < D / 16) {
-        const int l = tid & 63;
-        float *X = sX + 16 * (tid >> 6) + (l & 15) + 4 * (l >> 4) * LD;
-        f32x4 xt[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) xt[b][r] = X[(16 * b + r) * LD];
-        block_solve<true>(xt, sT, sL);
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) X[(16 * b + r) * LD] = xt[b][r];
+    if ((int)blockIdx.x < units) {
+        fetch_unit(blockIdx.x, tid0);
+        fetch(blockIdx.x, 0, tid0);
     }
-    lds_barrier();
+    for (int u = blockIdx.x; u < units; u += gridDim.x) {
+        int tid = tid0;  // redone per unit (see cb_prep)
+        asm volatile("" : "+v"(tid));
+        const int un = u + (int)gridDim.x;
+        const size_t ucd = (size_t)u * C * D, ucc = (size_t)u * C * C;
 #pragma unroll
-    for (int l = 0; l < NL; ++l) {
-        int e, t, d;
-        rc<D>(l, e, t, d);
-        sts4(a.wdU + ucd + e, lds4(sX + t * LD + d));  // dR replaces dU
-    }
-    {
-        // dT = -dR U^T (strictly lower) and dA = s dO U^T (lower) on the matrix
-        // cores: the 16 x 16 tiles of the two 64 x 64 results, 2 per wave; a
-        // tile above the diagonal is written as zeros.
-        const int w = tid >> 6, l = tid & 63;
+        for (int l = 0; l < NL; ++l) {
+            int e, t, d;
+            rc<D>(l, e, t, d, tid);
+            sts4(sX + t * LD + d, rX[l]);
+            sts4(sU + t * LD + d, rU[l]);
+            sts4(sO + t * LD + d, Raw4<IO>::widen(rO[l]));
+        }
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int tile = w + 8 * p, rt = tile >> 2, ct = tile & 3;
-            f32x4 at = zero4(), aa = zero4();
-            if (ct <= rt) {
-                const int ao = (rt * 16 + (l & 15)) * LD + (l >> 4), bo = (ct * 16 + (l & 15)) * LD + (l >> 4);
+        for (int l = 0; l < NTT; ++l) {  // -T^T
+            const int e = 4 * (l * NT + tid), t = e / C, j = e - t * C;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sT[(j + r) * LTT + t] = -rT[l][r];
+        }
+        if (un < units) fetch_unit(un, tid);
+        lds_barrier();
+        // (I + T)^T dR = dU by blocks: the inverted diagonal blocks (wave 0), then
+        // one 16-column tile of dU per wave.
+        float *sL = sT + C * LTT;
+        if (tid < 64) invert_diag16<true>([&](int i, int k) { return sT[k * LTT + i]; }, sL);
+        lds_barrier();
+        if ((tid >> 6) < D / 16) {
+            const int l = tid & 63;
+            float *X = sX + 16 * (tid >> 6) + (l & 15) + 4 * (l >> 4) * LD;
+            f32x4 xt[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) xt[b][r] = X[(16 * b + r) * LD];
+            block_solve<true>(xt, sT, sL);
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) X[(16 * b + r) * LD] = xt[b][r];
+        }
+        lds_barrier();
+#pragma unroll
+        for (int l = 0; l < NL; ++l) {
+            int e, t, d;
+            rc<D>(l, e, t, d, tid);
+            sts4(a.wdU + ucd + e, lds4(sX + t * LD + d));  // dR replaces dU
+        }
+        {
+            // dT = -dR U^T (strictly lower) and dA = s dO U^T (lower) on the matrix
+            // cores: the 16 x 16 tiles of the two 64 x 64 results, 2 per wave; a
+            // tile above the diagonal is written as zeros.
+            const int w = tid >> 6, l = tid & 63;
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const int tile = w + 8 * p, rt = tile >> 2, ct = tile & 3;
+                f32x4 at = zero4(), aa = zero4();
+                if (ct <= rt) {
+                    const int ao = (rt * 16 + (l & 15)) * LD + (l >> 4), bo = (ct * 16 + (l & 15)) * LD + (l >> 4);
 #pragma unroll 4
-                for (int v = 0; v < D; v += 4) {
-                    const float bu = sU[bo + v];
-                    at = __builtin_amdgcn_mfma_f32_16x16x4f32(sX[ao + v], bu, at, 0, 0, 0);
-                    aa = __builtin_amdgcn_mfma_f32_16x16x4f32(sO[ao + v], bu, aa, 0, 0, 0);
+                    for (int v = 0; v < D; v += 4) {
+                        const float bu = sU[bo + v];
+                        at = __builtin_amdgcn_mfma_f32_16x16x4f32(sX[ao + v], bu, at, 0, 0, 0);
+                        aa = __builtin_amdgcn_mfma_f32_16x16x4f32(sO[ao + v], bu, aa, 0, 0, 0);
+                    }
+                }
+                const int j = ct * 16 + (l & 15);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = rt * 16 + 4 * (l >> 4) + r;
+                    a.wdT[ucc + (size_t)t * C + j] = j < t ? -at[r] : 0.f;
+                    a.wdA[ucc + (size_t)t * C + j] = j <= t ? a.scale * aa[r] : 0.f;
                 }
             }
-            const int j = ct * 16 + (l & 15);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = rt * 16 + 4 * (l >> 4) + r;
-                a.wdT[ucc + (size_t)t * C + j] = j < t ? -at[r] : 0.f;
-                a.wdA[ucc + (size_t)t * C + j] = j <= t ? a.scale * aa[r] : 0.f;
-            }
         }
-    }
-    // Products with S and with dS_next, 32 state rows at a time; the next
-    // block's rows are fetched into registers while the current one is used.
-    float *sB2 = sT;  // S rows of the block (T is no longer needed)
-    for (int blk = 0; blk < D / 32; ++blk) {
-        lds_barrier();  // the previous block's rows (and T) are read
+        // Products with S and with dS_next, 32 state rows at a time; the next
+        // block's rows are fetched into registers while the current one is used.
+        float *sB2 = sT;  // S rows of the block (T is no longer needed)
+        for (int blk = 0; blk < D / 32; ++blk) {
+            lds_barrier();  // the previous block's rows (and T) are read
 #pragma unroll
-        for (int l = 0; l < NB; ++l) {
-            const int g = l * NT + tid, e = 4 * g, r = e / D, v = e - r * D;
-            if (g < NG) {
-                sts4(sB2 + r * LD + v, rs[l]);
-                sts4(sB + r * LD + v, rb[l]);
+            for (int l = 0; l < NB; ++l) {
+                const int g = l * NT + tid, e = 4 * g, r = e / D, v = e - r * D;
+                if (g < NG) {
+                    sts4(sB2 + r * LD + v, rs[l]);
+                    sts4(sB + r * LD + v, rb[l]);
+                }
             }
-        }
-        if (blk + 1 < D / 32) fetch(blk + 1);
-        lds_barrier();
-        {
-            // The block's 64 x 32 outputs of each product on the matrix cores
-            // (fp32 in, fp32 accumulate): wave w takes the 16 x 16 tile
-            // (rows 16 (w / 2), columns 16 (w % 2)). A lane holds rows
-            // 4 (l / 16) + r of column l % 16 of its tile.
-            const int w = tid >> 6, l = tid & 63, rt = w >> 1, ct = w & 1;
-            const int ao = (rt * 16 + (l & 15)) * LD + (l >> 4), bo = (ct * 16 + (l & 15)) * LD + (l >> 4);
-            f32x4 ae = zero4(), aq = zero4(), ak = zero4();
+            if (blk + 1 < D / 32) fetch(u, blk + 1, tid);
+            else if (un < units) fetch(un, 0, tid);
+            lds_barrier();
+            {
+                // The block's 64 x 32 outputs of each product on the matrix cores
+                // (fp32 in, fp32 accumulate): wave w takes the 16 x 16 tile
+                // (rows 16 (w / 2), columns 16 (w % 2)). A lane holds rows
+                // 4 (l / 16) + r of column l % 16 of its tile.
+                const int w = tid >> 6, l = tid & 63, rt = w >> 1, ct = w & 1;
+                const int ao = (rt * 16 + (l & 15)) * LD + (l >> 4), bo = (ct * 16 + (l & 15)) * LD + (l >> 4);
+                f32x4 ae = zero4(), aq = zero4(), ak = zero4();
 #pragma unroll 4
-            for (int v = 0; v < D; v += 4) {
-                const float bs = sB2[bo + v], bdv = sB[bo + v];
-                ae = __builtin_amdgcn_mfma_f32_16x16x4f32(sX[ao + v], bs, ae, 0, 0, 0);
-                aq = __builtin_amdgcn_mfma_f32_16x16x4f32(sO[ao + v], bs, aq, 0, 0, 0);
-                ak = __builtin_amdgcn_mfma_f32_16x16x4f32(sU[ao + v], bdv, ak, 0, 0, 0);
-            }
-            const int col = blk * 32 + ct * 16 + (l & 15);
+                for (int v = 0; v < D; v += 4) {
+                    const float bs = sB2[bo + v], bdv = sB[bo + v];
+                    ae = __builtin_amdgcn_mfma_f32_16x16x4f32(sX[ao + v], bs, ae, 0, 0, 0);
+                    aq = __builtin_amdgcn_mfma_f32_16x16x4f32(sO[ao + v], bs, aq, 0, 0, 0);
+                    ak = __builtin_amdgcn_mfma_f32_16x16x4f32(sU[ao + v], bdv, ak, 0, 0, 0);
+                }
+                const int col = blk * 32 + ct * 16 + (l & 15);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const size_t o = ucd + (size_t)(rt * 16 + 4 * (l >> 4) + r) * D + col;
-                a.wdE[o] = -ae[r];
-                a.wdQ[o] = a.scale * aq[r];
-                a.wdK[o] = ak[r];
+                for (int r = 0; r < 4; ++r) {
+                    const size_t o = ucd + (size_t)(rt * 16 + 4 * (l >> 4) + r) * D + col;
+                    a.wdE[o] = -ae[r];
+                    a.wdQ[o] = a.scale * aq[r];
+                    a.wdK[o] = ak[r];
+                }
+            }
+            {  // dGamma of the block's 32 rows: TG consecutive threads per row, D / TG columns each
+                constexpr int TG = D / 4 < 16 ? D / 4 : 16;
+                const int r = tid / TG, c0 = (tid % TG) * (D / TG);
+                float acc = 0.f;
+                if (r < 32)
+#pragma unroll
+                    for (int v = 0; v < D / TG; v += 4)
+                        acc = dot4(lds4(sB + r * LD + c0 + v), lds4(sB2 + r * LD + c0 + v), acc);
+#pragma unroll
+                for (int off = 1; off < TG; off <<= 1) acc += __shfl_xor(acc, off);
+                if (r < 32 && tid % TG == 0) a.wdGam[(size_t)u * D + blk * 32 + r] = acc;
             }
         }
-        {  // dGamma of the block's 32 rows: TG consecutive threads per row, D / TG columns each
-            constexpr int TG = D / 4 < 16 ? D / 4 : 16;
-            const int r = tid / TG, c0 = (tid % TG) * (D / TG);
-            float acc = 0.f;
-            if (r < 32)
-#pragma unroll
-                for (int v = 0; v < D / TG; v += 4)
-                    acc = dot4(lds4(sB + r * LD + c0 + v), lds4(sB2 + r * LD + c0 + v), acc);
-#pragma unroll
-            for (int off = 1; off < TG; off <<= 1) acc += __shfl_xor(acc, off);
-            if (r < 32 && tid % TG == 0) a.wdGam[(size_t)u * D + blk * 32 + r] = acc;
-        }
+        lds_barrier();  // shared memory read; the next unit overwrites it
     }
 }
 
@@ -1800,7 +1819,7 @@ hipError_t run(const ChunkBwdArgs &a, hipStream_t s) {
     } else {
         hipLaunchKernelGGL((cb_sweeps<IO, D, false>), dim3(2 * P), dim3(NS), sweep_smem, s, a, (int)items, (int)P);
     }
-    hipLaunchKernelGGL((cb_grad_s<IO, D>), dim3(units), dim3(NT), grad_s_smem<D>(), s, a);
+    hipLaunchKernelGGL((cb_grad_s<IO, D>), dim3(pgrid), dim3(NT), grad_s_smem<D>(), s, a);
     hipLaunchKernelGGL((cb_grad_out<IO, D, CHAN, BW>), dim3(units), dim3(NT), grad_out_smem<D>(), s, a);
     if (a.Hv > a.Hqk) {
         const size_t n4 = (size_t)a.B * a.T * a.Hqk * D / 4;
