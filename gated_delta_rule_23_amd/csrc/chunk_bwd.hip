@@ -47,13 +47,15 @@
 //
 // Shared-memory tiles keep 16-byte aligned rows (stride a multiple of 4
 // floats); global arrays are staged through registers with 16-byte (8-byte
-// for bf16) loads. All arithmetic is fp32: the dense products of the sweeps,
-// of cb_grad_s and of cb_grad_out on the matrix cores
-// (v_mfma_f32_16x16x4_f32), the rest on the vector units.
+// for bf16) loads. All arithmetic is fp32: the dense products (T and A, the
+// triangular solves, the sweeps' steps and the gradient products) on the
+// matrix cores (v_mfma_f32_16x16x4_f32), the rest on the vector units.
 //
-// Four launches (five with grouped heads):
+// Four launches (five or six: grouped heads; a sweep whose chain bounds the call):
 //  1. cb_prep (per chunk unit): G, the factors above, T and A, and the
-//     triangular solve (I + T)[Y | U_z] = [E~ | Z] by forward substitution.
+//     triangular solve (I + T)[Y | U_z] = [E~ | Z] by 16 x 16 blocks.
+//  1b. cb_rhs (per unit, when both sweeps fit on the GPU at once): the
+//     products of the backward sweep's step that do not depend on dS_next.
 //  2. cb_sweeps, per (sequence, V head, 32 value columns) twice over: the
 //     states S entering every chunk and U, walking the chunks forward; and
 //     dS_next of every chunk and dU, walking them backward (dS_0 at the end).
