@@ -132,6 +132,20 @@ def test_chunk_backward_strong_channel_decay(io, D, gates, T, Hv):
     _check(got, ref, 1e-4)
 
 
+@pytest.mark.parametrize("D,B,H,decay,gates", [(128, 1, 40, "channel", "bw"), (128, 1, 40, "scalar", "beta"),
+                                                (64, 2, 36, "channel", "beta")])
+def test_chunk_backward_many_heads(D, B, H, decay, gates):
+    """Enough (sequence, head) pairs that the two sweeps' workgroups do not
+    fit on the GPU at once: the backward sweep then forms every product of
+    its step itself (with fewer pairs, as in the other tests, the
+    dS_next-independent products come from a pass of their own). Sampled
+    heads against the oracle."""
+    wl = small_workload("bf16", D, decay, gates, T=130, B=B, Hqk=H, Hv=H, S0=True, scale=D ** -0.5)
+    heads = [0, H // 2 - 1, H - 1]
+    got, ref = _run(wl, seed=21 + D, heads=heads)
+    _check(got, ref, 1e-4, heads=heads, qk_heads=heads)
+
+
 def test_chunk_backward_qwen_shape_medium():
     wl = gs.QWEN_GDN_PREFILL.scaled(T=300, Hqk=2, Hv=6, name="qwen_like_T300")
     got, ref = _run(wl, seed=7)
