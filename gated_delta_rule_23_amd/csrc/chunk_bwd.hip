@@ -1583,19 +1583,36 @@ __global__ __launch_bounds__(NT) void cb_grad_out(ChunkBwdArgs a) {
                 const auto factor = [&](int bi, int bj) {
                     return bi == bj ? sF[(3 + bi) * D + col] : bi - bj == 1 ? 1.f : sF[(bwd_row_far(bi, bj) - 4) * D + col];
                 };
+                // The factor depends on the output column only, so it scales
+                // the B operand, and each product accumulates over its block
+                // pairs in one chain.
                 te[q] = tq[q] = tk[q] = zero4();
+                f32x4 tk2 = zero4();
+                const int g = l >> 4, r16 = l & 15;
                 for (int bj = 0; bj <= rt; ++bj) {  // rows t in block rt, columns j in block bj
                     if (bj == rt && ((slow >> rt) & 1)) continue;
                     const float f = factor(rt, bj);
-                    te[q] += f * mfma_kloop<16>(zero4(), sdT + rt * 16 * LC + bj * 16, LC, sP2 + bj * 16 * LD + ct * 16, LD);
-                    tq[q] += f * mfma_kloop<16>(zero4(), sdA + rt * 16 * LC + bj * 16, LC, sP2 + bj * 16 * LD + ct * 16, LD);
+                    const float *pt = sdT + (rt * 16 + r16) * LC + bj * 16 + g, *pa = sdA + (rt * 16 + r16) * LC + bj * 16 + g;
+                    const float *pb = sP2 + (bj * 16 + g) * LD + col;
+#pragma unroll
+                    for (int k = 0; k < 16; k += 4) {
+                        const float b = pb[k * LD] * f;
+                        te[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(pt[k], b, te[q], 0, 0, 0);
+                        tq[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[k], b, tq[q], 0, 0, 0);
+                    }
                 }
                 for (int bi = rt; bi < 4; ++bi) {  // rows j in block rt, tokens t in block bi
                     if (bi == rt && ((slow >> rt) & 1)) continue;
-                    f32x4 p = mfma_kloop_at<16>(zero4(), sdT + bi * 16 * LC + rt * 16, LC, sP1 + bi * 16 * LD + ct * 16, LD);
-                    p = mfma_kloop_at<16>(p, sdA + bi * 16 * LC + rt * 16, LC, sP3 + bi * 16 * LD + ct * 16, LD);
-                    tk[q] += factor(bi, rt) * p;
+                    const float f = factor(bi, rt);
+                    const float *pt = sdT + (bi * 16 + g) * LC + rt * 16 + r16, *pa = sdA + (bi * 16 + g) * LC + rt * 16 + r16;
+                    const float *p1 = sP1 + (bi * 16 + g) * LD + col, *p3 = sP3 + (bi * 16 + g) * LD + col;
+#pragma unroll
+                    for (int k = 0; k < 16; k += 4) {
+                        tk[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(pt[k * LC], p1[k * LD] * f, tk[q], 0, 0, 0);
+                        tk2 = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[k * LC], p3[k * LD] * f, tk2, 0, 0, 0);
+                    }
                 }
+                tk[q] += tk2;
             } else {
                 te[q] = mfma_kloop<C>(zero4(), sdT + rt * 16 * LC, LC, sP2 + ct * 16, LD);
                 tq[q] = mfma_kloop<C>(zero4(), sdA + rt * 16 * LC, LC, sP2 + ct * 16, LD);
