@@ -1457,10 +1457,9 @@ __global__ __launch_bounds__(2 * D) void chunk_seg_state(ChunkArgs a, int NVT, i
     int c = 0;
     for (; c + PF <= NC - 1; c += PF) {
 #pragma unroll
-        for (int j = 0; j < PF; ++j) {
-            chain_chunk<IO, D, NCT, CHAN>(ring[j], S, sST, sUT, sUK, w, mpart);
-            ring[j].load(src, min(c + j + PF, NC - 1), w, col0);
-        }
+        for (int j = 0; j < PF; ++j)  // the refill goes out in two parts, each once its operands are used
+            chain_chunk<IO, D, NCT, CHAN, true>(ring[j], S, sST, sUT, sUK, w, mpart, &src, min(c + j + PF, NC - 1),
+                                                col0);
     }
 #pragma unroll
     for (int j = 0; j < PF; ++j)
