@@ -99,7 +99,7 @@ int validate(const gdr_desc *d, CallKind kind, const void *q, const void *k, con
     if (kind == CALL_CHUNK || kind == CALL_CHUNK_BWD) {
         if (d->chunk != gdr::kChunk) return fail(GDR_E_UNSUPPORTED, "chunk = %d: only 64 is supported", d->chunk);
         if (kind == CALL_CHUNK && !gdr::chunk_supported(d->io_dtype == GDR_BF16 ? gdr::IO_BF16 : gdr::IO_F32, d->d_k))
-            return fail(GDR_E_UNSUPPORTED, "prefill with float32 io supports d in {32, 64}");
+            return fail(GDR_E_UNSUPPORTED, "prefill with float32 io supports d in {32, 64, 128}");
     }
     if (!size_ok(d->B, prefill ? d->T : 1, d->H_v, d->d_k) || !size_ok(d->B, prefill ? d->T : 1, d->H_qk, d->d_k))
         return fail(GDR_E_INVAL, "sizes too large");
@@ -207,6 +207,9 @@ int chunk_call(const gdr_desc *d, const gdr_input_stage *stage, const void *q, c
     const int io = d->io_dtype == GDR_BF16 ? gdr::IO_BF16 : gdr::IO_F32;
     const int NC = (d->T + gdr::kChunk - 1) / gdr::kChunk;
     const bool chan = d->decay == GDR_DECAY_CHANNEL;
+    if (io == gdr::IO_F32 && d->d_k == 128 && (chan || !beta || stage))
+        return fail(GDR_E_UNSUPPORTED, "prefill with float32 io at d = 128 supports tied gates (beta) with a scalar "
+                                       "decay or none, without the input stage");
     const gdr::ChunkWsLayout L = gdr::chunk_ws_layout(d->B, d->H_qk, d->H_v, NC, d->d_k, io, chan);
     // Per-channel decay with the input stage: the stage runs as a pass of its
     // own into the workspace, after the prefill's part.

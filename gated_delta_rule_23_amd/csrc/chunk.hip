@@ -385,8 +385,13 @@ struct PrepIn {
     }
 };
 
+// Workgroups per CU the prep is compiled for: two where two fit in shared
+// memory and the variant keeps few tiles, else one (which lets the compiler
+// use the whole register file).
 template <typename IO, int D, bool CHAN, bool BW>
-constexpr int prep_occupancy() { return (CHAN || BW) ? 1 : 2; }
+constexpr int prep_occupancy() {
+    return (CHAN || BW || 2 * PrepCfg<IO, D>::bytes(false, false) > (size_t)160 * 1024) ? 1 : 2;
+}
 
 template <typename IO, int D, bool CHAN, bool BW, bool RAW>
 __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chunk_prep(ChunkArgs a) {
@@ -1533,22 +1538,32 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t s) {
     // Shared memory per prep variant (CHAN, BW): the per-channel-decay and
     // decoupled-gate variants keep more tiles.
     // Once per process (thread-safe): allow each variant its shared memory.
+    // Float32 io at d = 128 has only the tied-gate, scalar-decay prep: the
+    // variants with an erase-key tile would need more than a CU's 160 KiB of
+    // shared memory, and the input-stage and per-channel variants reduce over
+    // a token row's lanes in 16-lane groups (a row spans 32 lanes there).
+    constexpr bool ALL = !(sizeof(IO) == 4 && D == 128);
     static const hipError_t attr_err = [] {
-        // (With a per-channel decay the input stage runs as a pass of its own,
-        // stage.hip, so there is no input-stage variant of those preps.)
-        const void *fns[6] = {reinterpret_cast<const void *>(&chunk_prep<IO, D, false, false, false>),
-                              reinterpret_cast<const void *>(&chunk_prep<IO, D, false, true, false>),
-                              reinterpret_cast<const void *>(&chunk_prep<IO, D, true, false, false>),
-                              reinterpret_cast<const void *>(&chunk_prep<IO, D, true, true, false>),
-                              reinterpret_cast<const void *>(&chunk_prep<IO, D, false, false, true>),
-                              reinterpret_cast<const void *>(&chunk_prep<IO, D, false, true, true>)};
-        const size_t lds[4] = {Cfg::bytes(false, false), Cfg::bytes(true, false), Cfg::bytes(true, true),
-                               Cfg::bytes(true, true)};
-        for (int i = 0; i < 6; ++i) {
-            hipError_t e = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds[i % 4]);
-            if (e != hipSuccess) return e;
+        if constexpr (!ALL) {
+            return hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_prep<IO, D, false, false, false>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::bytes(false, false));
+        } else {
+            // (With a per-channel decay the input stage runs as a pass of its
+            // own, stage.hip, so there is no input-stage variant of those preps.)
+            const void *fns[6] = {reinterpret_cast<const void *>(&chunk_prep<IO, D, false, false, false>),
+                                  reinterpret_cast<const void *>(&chunk_prep<IO, D, false, true, false>),
+                                  reinterpret_cast<const void *>(&chunk_prep<IO, D, true, false, false>),
+                                  reinterpret_cast<const void *>(&chunk_prep<IO, D, true, true, false>),
+                                  reinterpret_cast<const void *>(&chunk_prep<IO, D, false, false, true>),
+                                  reinterpret_cast<const void *>(&chunk_prep<IO, D, false, true, true>)};
+            const size_t lds[4] = {Cfg::bytes(false, false), Cfg::bytes(true, false), Cfg::bytes(true, true),
+                                   Cfg::bytes(true, true)};
+            for (int i = 0; i < 6; ++i) {
+                hipError_t e = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds[i % 4]);
+                if (e != hipSuccess) return e;
+            }
+            return hipSuccess;
         }
-        return hipSuccess;
     }();
     if (attr_err != hipSuccess) return attr_err;
     const long long units = (long long)a.B * a.Hv * a.NC;
@@ -1575,7 +1590,10 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t s) {
         const long long items = units / pg;
         const long long grid = items < slots ? items : slots;
         const dim3 g((unsigned)grid), b(Cfg::NT);
-        if (a.conv_w) {
+        if constexpr (!ALL) {
+            if (a.conv_w || chan || bw) return hipErrorInvalidValue;
+            hipLaunchKernelGGL((chunk_prep<IO, D, false, false, false>), g, b, Cfg::bytes(false, false), s, ap);
+        } else if (a.conv_w) {
             if (chan) return hipErrorInvalidValue;  // the input stage runs first as a pass of its own
             if (bw) hipLaunchKernelGGL((chunk_prep<IO, D, false, true, true>), g, b, Cfg::bytes(true, false), s, ap);
             else hipLaunchKernelGGL((chunk_prep<IO, D, false, false, true>), g, b, Cfg::bytes(false, false), s, ap);
@@ -1597,7 +1615,8 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t s) {
         if (a.decay == DECAY_CHANNEL)
             hipLaunchKernelGGL((chunk_seg_state<IO, D, NCT1, PF, true>), dim3(grid1), dim3(2 * D), 0, s, a, NVT1, G1);
         else
-            hipLaunchKernelGGL((chunk_seg_state<IO, D, NCT1, PF, false>), dim3(grid1), dim3(2 * D), 0, s, a, NVT1, G1);
+
+        hipLaunchKernelGGL((chunk_seg_state<IO, D, NCT1, PF, false>), dim3(grid1), dim3(2 * D), 0, s, a, NVT1, G1);
         hipLaunchKernelGGL((chunk_seg_combine<D>), dim3(a.B * a.Hv * (D / 16)), dim3(256), 0, s, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -1611,10 +1630,7 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-bool chunk_supported(int io, int D) {
-    if (io == IO_BF16) return D == 32 || D == 64 || D == 128;
-    return D == 32 || D == 64;
-}
+bool chunk_supported(int io, int D) { return D == 32 || D == 64 || D == 128; }
 
 hipError_t launch_chunk(int io, int D, const ChunkArgs &a, hipStream_t s) {
     if (io == IO_BF16) {
@@ -1624,6 +1640,7 @@ hipError_t launch_chunk(int io, int D, const ChunkArgs &a, hipStream_t s) {
     } else {
         if (D == 32) return launch_chunk_t<float, 32, 1>(a, s);
         if (D == 64) return launch_chunk_t<float, 64, 2>(a, s);
+        if (D == 128) return launch_chunk_t<float, 128, 2>(a, s);
     }
     return hipErrorInvalidValue;
 }

@@ -134,7 +134,9 @@ int gdr_chunk_workspace_bytes(const gdr_desc *desc, size_t *bytes);
  *   S0: initial state, or NULL for zeros. ST: final state; may equal S0
  *   (in-place update). o: outputs. T may be any positive length (the last
  *   chunk may be partial). workspace: at least gdr_chunk_workspace_bytes;
- *   its contents on entry are ignored. */
+ *   its contents on entry are ignored. Float32 io at d = 128 takes tied
+ *   gates (beta) with a scalar decay or none; other gate and decay modes
+ *   at that size return GDR_E_UNSUPPORTED (gdr_recurrent_fwd serves them). */
 int gdr_chunk_fwd(const gdr_desc *desc, const void *q, const void *k, const void *v,
                   const float *g, const float *beta, const void *b, const void *w,
                   const float *S0, void *o, float *ST, void *workspace, size_t workspace_bytes,

@@ -86,7 +86,8 @@ def _desc(**kw):
     (dict(desc=dict(D=256)), gdr.GDR_E_UNSUPPORTED),
     (dict(desc=dict(io=7)), gdr.GDR_E_INVAL),
     (dict(desc=dict(decay=5)), gdr.GDR_E_INVAL),
-    (dict(desc=dict(io=gdr.GDR_F32, D=128)), gdr.GDR_E_UNSUPPORTED),
+    (dict(desc=dict(io=gdr.GDR_F32, D=128, decay=gdr.GDR_DECAY_CHANNEL)), gdr.GDR_E_UNSUPPORTED),
+    (dict(desc=dict(io=gdr.GDR_F32, D=128), args=dict(beta=None, b=P, w=P)), gdr.GDR_E_UNSUPPORTED),
     (dict(args=dict(q=None)), gdr.GDR_E_INVAL),
     (dict(args=dict(o=None)), gdr.GDR_E_INVAL),
     (dict(args=dict(ST=None)), gdr.GDR_E_INVAL),

@@ -629,6 +629,41 @@ def test_recurrent_input_stage_zero_tokens():
 
 
 # ---------------------------------------------------------------------------
+# Float32 io at d = 128: tied gates with a scalar decay or none.
+
+@pytest.mark.parametrize("decay", ["none", "scalar"])
+@pytest.mark.parametrize("T,B,Hqk,Hv", [(1, 2, 1, 2), (64, 2, 1, 2), (150, 2, 1, 2), (333, 2, 2, 6),
+                                        (2100, 1, 1, 1)])
+def test_prefill_f32_d128(decay, T, B, Hqk, Hv):
+    """Several chunks and a ragged tail, grouped heads (three V heads per QK
+    head), and one head over 33 chunks, which the sweep splits into segments."""
+    wl = small_workload("f32", 128, decay, "beta", T=T, B=B, Hqk=Hqk, Hv=Hv, S0=True, scale=128 ** -0.5)
+    inp = gs.make_inputs(wl, seed=T + 128)
+    say(f"prefill {wl.name}")
+    o, ST = gpu_prefill(inp, S0=to_dev(inp["S0"]))
+    o_ref, S_ref = oracle_prefill(inp)
+    record(wl.name, o=(from_dev(o), o_ref), S=(from_dev(ST), S_ref))
+    assert out_err(from_dev(o), o_ref) < TOL["f32"]
+    assert rel_err(from_dev(ST), S_ref) < TOL["f32"]
+
+
+def test_prefill_f32_d128_strong_decay_in_place():
+    """Decays down to -30 per token (whole chunks decay below float32's
+    range), the state updated in place."""
+    wl = small_workload("f32", 128, "scalar", "beta", T=200, B=1, Hqk=1, Hv=3, S0=True)
+    inp = gs.make_inputs(wl, seed=5)
+    rng = np.random.default_rng(5)
+    inp["g"] = np.where(rng.random(inp["g"].shape) < 0.1, -30.0, inp["g"]).astype(np.float32)
+    say(f"prefill {wl.name} strong decay")
+    S = to_dev(inp["S0"])
+    o, ST = gpu_prefill(inp, S0=S, ST=S)
+    o_ref, S_ref = oracle_prefill(inp)
+    assert ST.data_ptr() == S.data_ptr()
+    assert out_err(from_dev(o), o_ref) < TOL["f32"]
+    assert rel_err(from_dev(S), S_ref) < TOL["f32"]
+
+
+# ---------------------------------------------------------------------------
 # Input stage fused into the chunked prefill's load stage.
 
 @pytest.mark.parametrize("io,D", PREFILL_DIMS)
