@@ -392,7 +392,7 @@ def main(argv=None):
         fused = wl.decay != "channel"
         stage = {"entry": "gdr_chunk_fwd_in", "ms_per_call": s_ms, "tokens_per_s": tokens / (s_ms * 1e-3),
                  "form": ("fused into the prefill's load stage" if fused else
-                          "a pass of its own (stage_conv + stage_gates) before the prefill"),
+                          "the convolution and normalisation as a pass of their own (stage_conv) before the prefill, the gate and decay activations in its load stage"),
                  "extra_ms_vs_gdr_chunk_fwd": s_ms - avg_call_ms,
                  "unfused_round_trip_bytes": 2 * (d["q"].nbytes + d["k"].nbytes + d["v"].nbytes) if fused else None,
                  "roofline": {"bound": "hbm", "achieved": s_bytes / (s_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,

@@ -211,10 +211,12 @@ int chunk_call(const gdr_desc *d, const gdr_input_stage *stage, const void *q, c
         return fail(GDR_E_UNSUPPORTED, "prefill with float32 io at d = 128 supports tied gates (beta) with a scalar "
                                        "decay or none, without the input stage");
     const gdr::ChunkWsLayout L = gdr::chunk_ws_layout(d->B, d->H_qk, d->H_v, NC, d->d_k, io, chan);
-    // Per-channel decay with the input stage: the stage runs as a pass of its
-    // own into the workspace, after the prefill's part.
+    // Per-channel decay with the input stage: the convolution and the
+    // normalisation of q, k, v run as a pass of their own into the workspace,
+    // after the prefill's part; the prefill applies the gate and decay
+    // activations as it loads them.
     const bool split_stage = stage && chan;
-    const gdr::StageWsLayout SL = gdr::stage_ws_layout(d->B, d->T, d->H_qk, d->H_v, d->d_k, io, beta == nullptr);
+    const gdr::StageWsLayout SL = gdr::stage_ws_layout(d->B, d->T, d->H_qk, d->H_v, d->d_k, io);
     const size_t need = L.total() + (split_stage ? SL.total() : 0);
     if (lib_scratch) {
         workspace = nullptr;
@@ -250,20 +252,17 @@ int chunk_call(const gdr_desc *d, const gdr_input_stage *stage, const void *q, c
     if (split_stage && NC > 0) {
         char *p = static_cast<char *>(workspace) + L.total();
         gdr::StageArgs sa{};
-        sa.q = q; sa.k = k; sa.v = v; sa.g = g; sa.beta = beta; sa.bg = b; sa.wg = w;
+        sa.q = q; sa.k = k; sa.v = v;
         sa.conv_w = stage->conv_w; sa.conv_in = stage->conv_in; sa.conv_out = stage->conv_out;
-        sa.decay_scale = stage->decay_scale;
         sa.qo = p;
         sa.ko = p + SL.qk;
         sa.vo = p + 2 * SL.qk;
-        sa.go = reinterpret_cast<float *>(p + 2 * SL.qk + SL.v);
-        char *gates = p + 2 * SL.qk + SL.v + SL.g;
-        if (beta) sa.betao = reinterpret_cast<float *>(gates);
-        else { sa.bgo = gates; sa.wgo = gates + SL.gate; }
         sa.B = d->B; sa.T = d->T; sa.Hqk = d->H_qk; sa.Hv = d->H_v;
         e = gdr::launch_stage(io, d->d_k, sa, static_cast<hipStream_t>(stream));
         if (e != hipSuccess) return hip_fail(e, "input stage launch");
-        a.q = sa.qo; a.k = sa.ko; a.v = sa.vo; a.g = sa.go; a.beta = sa.betao; a.bg = sa.bgo; a.wg = sa.wgo;
+        a.q = sa.qo; a.k = sa.ko; a.v = sa.vo;
+        a.raw_gates = 1;
+        a.decay_scale = stage->decay_scale;
     } else if (stage) {
         a.conv_w = stage->conv_w;
         a.conv_in = stage->conv_in;
@@ -544,10 +543,10 @@ int gdr_chunk_workspace_bytes(const gdr_desc *d, size_t *bytes) {
 int gdr_chunk_fwd_in_workspace_bytes(const gdr_desc *d, size_t *bytes) {
     const int rc = gdr_chunk_workspace_bytes(d, bytes);
     if (rc != GDR_OK) return rc;
-    // Per-channel decay: room for the processed inputs (decoupled gates, the larger case).
+    // Per-channel decay: room for the convolved and normalised q, k, v.
     if (d->decay == GDR_DECAY_CHANNEL)
         *bytes += gdr::stage_ws_layout(d->B, d->T, d->H_qk, d->H_v, d->d_k,
-                                       d->io_dtype == GDR_BF16 ? gdr::IO_BF16 : gdr::IO_F32, true).total();
+                                       d->io_dtype == GDR_BF16 ? gdr::IO_BF16 : gdr::IO_F32).total();
     return ok();
 }
 

@@ -404,7 +404,11 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
     constexpr int KS = M::KS, FE = KS / 4, PD = Cfg::PD, LC = Cfg::LC, LY = Cfg::LY, LT = Cfg::LT;
     constexpr int WC = Cfg::WC, NCTS = Cfg::NCTS;
     constexpr bool HAS_E = CHAN || BW;
-    static_assert(!(RAW && CHAN), "with a per-channel decay the input stage runs as a pass of its own");
+    // RAW: the gates and the decay arrive before their activations. Without a
+    // per-channel decay q, k and v arrive raw as well, and the whole input
+    // stage runs here; with one, the convolution and the normalisation of q,
+    // k and v ran as a pass of their own before this kernel.
+    constexpr bool RQKV = RAW && !CHAN;
     static_assert(NT == 256, "launch bounds");
 
     extern __shared__ __align__(16) unsigned char smem[];
@@ -452,7 +456,7 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
         return (b * a.Hv + hg * PG + hh) * a.NC + c;
     };
 
-    PrepIn<IO, D, CHAN, BW, RAW> in;
+    PrepIn<IO, D, CHAN, BW, RQKV> in;
     if ((int)blockIdx.x < gunits) in.load_all(a, unit_of(blockIdx.x, 0), co, grp);
 
     for (int gu = blockIdx.x, hh = 0; gu < gunits;) {
@@ -482,7 +486,7 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
         // The one-workgroup-per-CU variants have the registers to request
         // them first, so that their latency hides behind phase A; the others
         // load each tensor's taps where they are used.
-        constexpr bool EARLY_TAPS = RAW && prep_occupancy<IO, D, CHAN, BW>() == 1;
+        constexpr bool EARLY_TAPS = RQKV && prep_occupancy<IO, D, CHAN, BW>() == 1;
         f32x4 taps[EARLY_TAPS ? 3 * V : 1];
         if constexpr (EARLY_TAPS) {
             const size_t sqk = (size_t)a.Hqk * D;
@@ -560,7 +564,7 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
             sSE[l] = BW ? eg : bt * eg;
         }
         IO *sHalo = sTmp;  // input stage: [3 tokens][q, k, v][D], the window before the chunk
-        if constexpr (RAW) {
+        if constexpr (RQKV) {
             // The raw rows go to the tiles (token-major, as the processed
             // ones will) and the 3 tokens before the chunk to sHalo, so that
             // each thread can read the 3 rows before its own.
@@ -582,7 +586,7 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
             }
         }
         __syncthreads();
-        if constexpr (RAW) {
+        if constexpr (RQKV) {
             const size_t sqk = (size_t)a.Hqk * D, ch = 2 * sqk + (size_t)a.Hv * D;
             const int hq = h / grpsz, b = bh / a.Hv;
             const size_t cq = (size_t)hq * D + V * co, ck = sqk + cq, cv = 2 * sqk + (size_t)h * D + V * co;
@@ -1548,17 +1552,20 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t s) {
             return hipFuncSetAttribute(reinterpret_cast<const void *>(&chunk_prep<IO, D, false, false, false>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::bytes(false, false));
         } else {
-            // (With a per-channel decay the input stage runs as a pass of its
-            // own, stage.hip, so there is no input-stage variant of those preps.)
-            const void *fns[6] = {reinterpret_cast<const void *>(&chunk_prep<IO, D, false, false, false>),
+            // (With a per-channel decay and the input stage, the convolution
+            // runs as a pass of its own, stage.hip, and the prep applies only
+            // the gate and decay activations.)
+            const void *fns[8] = {reinterpret_cast<const void *>(&chunk_prep<IO, D, false, false, false>),
                                   reinterpret_cast<const void *>(&chunk_prep<IO, D, false, true, false>),
                                   reinterpret_cast<const void *>(&chunk_prep<IO, D, true, false, false>),
                                   reinterpret_cast<const void *>(&chunk_prep<IO, D, true, true, false>),
                                   reinterpret_cast<const void *>(&chunk_prep<IO, D, false, false, true>),
-                                  reinterpret_cast<const void *>(&chunk_prep<IO, D, false, true, true>)};
+                                  reinterpret_cast<const void *>(&chunk_prep<IO, D, false, true, true>),
+                                  reinterpret_cast<const void *>(&chunk_prep<IO, D, true, false, true>),
+                                  reinterpret_cast<const void *>(&chunk_prep<IO, D, true, true, true>)};
             const size_t lds[4] = {Cfg::bytes(false, false), Cfg::bytes(true, false), Cfg::bytes(true, true),
                                    Cfg::bytes(true, true)};
-            for (int i = 0; i < 6; ++i) {
+            for (int i = 0; i < 8; ++i) {
                 hipError_t e = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds[i % 4]);
                 if (e != hipSuccess) return e;
             }
@@ -1593,8 +1600,12 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t s) {
         if constexpr (!ALL) {
             if (a.conv_w || chan || bw) return hipErrorInvalidValue;
             hipLaunchKernelGGL((chunk_prep<IO, D, false, false, false>), g, b, Cfg::bytes(false, false), s, ap);
+        } else if (chan && a.raw_gates) {  // q, k, v from the stage pass; gate and decay activations here
+            if (a.conv_w) return hipErrorInvalidValue;
+            if (bw) hipLaunchKernelGGL((chunk_prep<IO, D, true, true, true>), g, b, Cfg::bytes(true, true), s, ap);
+            else hipLaunchKernelGGL((chunk_prep<IO, D, true, false, true>), g, b, Cfg::bytes(true, true), s, ap);
         } else if (a.conv_w) {
-            if (chan) return hipErrorInvalidValue;  // the input stage runs first as a pass of its own
+            if (chan) return hipErrorInvalidValue;  // the convolution runs first as a pass of its own
             if (bw) hipLaunchKernelGGL((chunk_prep<IO, D, false, true, true>), g, b, Cfg::bytes(true, false), s, ap);
             else hipLaunchKernelGGL((chunk_prep<IO, D, false, false, true>), g, b, Cfg::bytes(false, false), s, ap);
         } else {
@@ -1615,8 +1626,7 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t s) {
         if (a.decay == DECAY_CHANNEL)
             hipLaunchKernelGGL((chunk_seg_state<IO, D, NCT1, PF, true>), dim3(grid1), dim3(2 * D), 0, s, a, NVT1, G1);
         else
-
-        hipLaunchKernelGGL((chunk_seg_state<IO, D, NCT1, PF, false>), dim3(grid1), dim3(2 * D), 0, s, a, NVT1, G1);
+            hipLaunchKernelGGL((chunk_seg_state<IO, D, NCT1, PF, false>), dim3(grid1), dim3(2 * D), 0, s, a, NVT1, G1);
         hipLaunchKernelGGL((chunk_seg_combine<D>), dim3(a.B * a.Hv * (D / 16)), dim3(256), 0, s, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

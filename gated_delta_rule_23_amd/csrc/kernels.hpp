@@ -70,6 +70,11 @@ struct ChunkArgs {
     // chunk_prep: V heads of one QK head that a work item runs back to back
     // (divides Hv / Hqk; chosen by the launcher, 0 from callers).
     int prep_grp;
+    // Per-channel decay with the input stage: q, k, v come convolved and
+    // normalised from the stage pass, while g, beta, b and w are the raw
+    // inputs of their activations, which the prep applies as it loads them
+    // (decay_scale as for the input stage).
+    int raw_gates;
 };
 
 constexpr int kTab = 2 * kChunk;  // floats per chunk unit in ws_tab (>= D for every supported D)
@@ -161,34 +166,24 @@ inline BwdWsLayout bwd_ws_layout(int B, int T, int Hv, int D) {
 // processed q, k, v, activated gates and the decay g out (prefill layouts).
 struct StageArgs {
     const void *q, *k, *v;       // raw [B,T,Hqk,D], [B,T,Hqk,D], [B,T,Hv,D] (io)
-    const float *g;              // decay input [B,T,Hv,D]
-    const float *beta;           // beta input [B,T,Hv], or null (decoupled gates)
-    const void *bg, *wg;         // b, w inputs [B,T,Hv,D] (io), or null
     const float *conv_w;         // [(2 Hqk + Hv) D, 4]
     const void *conv_in;         // [B, 3, (2 Hqk + Hv) D] (io) or null (zeros)
     void *conv_out;              // same layout, or null
-    const float *decay_scale;    // [Hv] or null (1)
     void *qo, *ko, *vo;          // processed q, k, v (io)
-    float *go, *betao;           // g = -c softplus(x); beta = sigmoid(x) (tied gates)
-    void *bgo, *wgo;             // b, w = sigmoid(x) (io; decoupled gates)
     int B, T, Hqk, Hv;
 };
 // Bytes of each processed array in the workspace, in this order, each on a
-// 256-byte boundary: q, k, v (io), g (float32), then beta (float32) or b and
-// w (io).
+// 256-byte boundary: q, k, v (io). The gates and the decay stay in the
+// caller's arrays: the prefill's load stage applies their activations.
 struct StageWsLayout {
-    size_t qk, v, g, gate;       // bytes of q (= k), v, g, and beta or each of b, w
-    bool bw;
-    size_t total() const { return 2 * qk + v + g + (bw ? 2 * gate : gate); }
+    size_t qk, v;                // bytes of q (= k) and of v
+    size_t total() const { return 2 * qk + v; }
 };
-inline StageWsLayout stage_ws_layout(int B, int T, int Hqk, int Hv, int D, int io, bool bw) {
+inline StageWsLayout stage_ws_layout(int B, int T, int Hqk, int Hv, int D, int io) {
     const size_t esz = io == IO_BF16 ? 2 : 4, tok = (size_t)B * T;
     StageWsLayout L;
     L.qk = align256(tok * Hqk * D * esz);
     L.v = align256(tok * Hv * D * esz);
-    L.g = align256(tok * Hv * D * 4);
-    L.gate = bw ? align256(tok * Hv * D * esz) : align256(tok * Hv * 4);
-    L.bw = bw;
     return L;
 }
 hipError_t launch_stage(int io, int D, const StageArgs &a, hipStream_t s);

@@ -1,5 +1,6 @@
-// stage.hip -- the input stage as a pass of its own, for the chunked prefill
-// of per-channel-decay layers (gdr_chunk_fwd_in with GDR_DECAY_CHANNEL).
+// stage.hip -- the input stage's convolution as a pass of its own, for the
+// chunked prefill of per-channel-decay layers (gdr_chunk_fwd_in with
+// GDR_DECAY_CHANNEL).
 //
 // The input stage (page "Gated DeltaNet: o mixer em 48 das 64 camadas",
 // section "Conceito": a causal depthwise convolution of kernel 4 over the
@@ -7,10 +8,10 @@
 // sigmoid gates and a softplus-shaped decay) is fused into the prefill's load
 // stage for scalar-decay layers. With a per-channel decay the prefill's load
 // stage already holds seven token-major tiles of the chunk, so there the
-// stage runs first, over the whole call, and writes the processed q, k, v,
-// the activated gates and the decay g into the call's workspace; the
-// prefill then runs on them as gdr_chunk_fwd does. Both passes stream: each
-// raw row is read once and each processed row written once.
+// convolution and the normalisation run first, over the whole call, and
+// write the processed q, k, v into the call's workspace; the gate and decay
+// activations, elementwise, stay in the prefill's load stage. The pass
+// streams: each raw row is read once and each processed row written once.
 //
 //  stage_conv: one thread per 16-byte channel group of one (sequence, head)
 //    row of q, k or v and a run of 16 tokens, walked in order with the 3 rows
@@ -19,8 +20,6 @@
 //    consecutive lanes, so the norm of q and k is a DPP all-reduce inside the
 //    wave. The thread of the last run also writes the outgoing convolution
 //    state (the last 3 raw tokens, rows before the call taken from conv_in).
-//  stage_gates: elementwise g = -c_h softplus(x) (per channel), beta, b and w
-//    = sigmoid(x).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -144,33 +143,6 @@ __global__ __launch_bounds__(256) void stage_conv(StageArgs a) {
     }
 }
 
-// Elementwise activations: n4 groups of 4 elements of g (per channel, D a
-// multiple of 4) and of b, w (decoupled gates), then nb elements of beta.
-template <typename IO, int D>
-__global__ __launch_bounds__(256) void stage_gates(StageArgs a) {
-    const long long n4 = (long long)a.B * a.T * a.Hv * D / 4, nb = a.beta ? (long long)a.B * a.T * a.Hv : 0;
-    const long long step = (long long)gridDim.x * blockDim.x;
-    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n4 + nb; i += step) {
-        if (i < n4) {
-            const int h = (int)((4 * i / D) % a.Hv);
-            const float c = a.decay_scale ? a.decay_scale[h] : 1.f;
-            const f32x4 x = load4f(a.g + 4 * i);
-            store4f(a.go + 4 * i, f32x4{-c * act_softplus(x[0]), -c * act_softplus(x[1]), -c * act_softplus(x[2]),
-                                        -c * act_softplus(x[3])});
-            if (!a.beta) {
-                const f32x4 bx = load4f(static_cast<const IO *>(a.bg) + 4 * i), wx = load4f(static_cast<const IO *>(a.wg) + 4 * i);
-                store4f(static_cast<IO *>(a.bgo) + 4 * i, f32x4{act_sigmoid(bx[0]), act_sigmoid(bx[1]), act_sigmoid(bx[2]),
-                                                                act_sigmoid(bx[3])});
-                store4f(static_cast<IO *>(a.wgo) + 4 * i, f32x4{act_sigmoid(wx[0]), act_sigmoid(wx[1]), act_sigmoid(wx[2]),
-                                                                act_sigmoid(wx[3])});
-            }
-        } else {
-            const long long j = i - n4;
-            a.betao[j] = act_sigmoid(a.beta[j]);
-        }
-    }
-}
-
 template <typename IO, int D>
 hipError_t launch_stage_t(const StageArgs &a, hipStream_t s) {
     constexpr int CO = D / (16 / (int)sizeof(IO));
@@ -179,9 +151,6 @@ hipError_t launch_stage_t(const StageArgs &a, hipStream_t s) {
         const long long grid = (groups + 255) / 256;
         if (grid > 0x7fffffffll) return hipErrorInvalidValue;
         hipLaunchKernelGGL((stage_conv<IO, D>), dim3((unsigned)grid), dim3(256), 0, s, a);
-        const long long work = (long long)a.B * a.T * a.Hv * D / 4 + (a.beta ? (long long)a.B * a.T * a.Hv : 0);
-        const long long g2 = (work + 255) / 256 < 8192 ? (work + 255) / 256 : 8192;
-        hipLaunchKernelGGL((stage_gates<IO, D>), dim3((unsigned)g2), dim3(256), 0, s, a);
     }
     return hipGetLastError();
 }

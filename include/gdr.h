@@ -225,12 +225,13 @@ typedef struct {
  * kernel reads the raw projections (plus the 3 tokens before each chunk) and
  * applies the convolution, the normalisation and the activations before
  * building the chunk's factors, so the processed q, k, v never travel
- * through memory. With a per-channel decay the stage runs as a pass of its
- * own that writes the processed q, k, v (io dtype), the decay g and the
- * gates (beta float32, b and w io dtype) into the workspace, and the prefill
- * reads them there. Arguments as gdr_recurrent_fwd_in, plus a workspace of
- * at least gdr_chunk_fwd_in_workspace_bytes (gdr_chunk_workspace_bytes plus,
- * for a per-channel decay, the processed inputs). The chunk products run on
+ * through memory. With a per-channel decay the convolution and the
+ * normalisation run as a pass of their own that writes the processed q, k,
+ * v (io dtype) into the workspace; the prefill reads them there and applies
+ * the gate and decay activations to the raw g, beta, b and w as it loads
+ * them. Arguments as gdr_recurrent_fwd_in, plus a workspace of at least
+ * gdr_chunk_fwd_in_workspace_bytes (gdr_chunk_workspace_bytes plus, for a
+ * per-channel decay, the processed q, k, v). The chunk products run on
  * bf16 matrix cores for bf16 io, so the processed q, k and v are rounded to
  * bf16 there, as the io values of gdr_chunk_fwd are. */
 int gdr_chunk_fwd_in_workspace_bytes(const gdr_desc *desc, size_t *bytes);
