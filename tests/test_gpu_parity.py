@@ -124,9 +124,10 @@ def test_prefill_input_stage_strong_channel_decay(io, D, gates):
     """From raw projections: decay inputs x with g = -c softplus(x) for c = 1,
     so x = 1.5, 30 and 200 give the strong decays above."""
     pytest.skip("held off the GPU: the first case faulted the GPU in an earlier build whose per-chunk kernel "
-                "fused the input stage with per-channel decay; no cause was found in that kernel, which has "
-                "since been removed (the stage now runs as a pass of its own, covered by the other input-stage "
-                "tests, and the strong-decay prefill by test_prefill_strong_channel_decay)")
+                "fused the whole input stage (convolution included) with per-channel decay; no cause was found "
+                "in that kernel, which has since been removed (the convolution now runs as a pass of its own and "
+                "the gate and decay activations in the prefill's load stage, covered on the same kind of decays "
+                "by test_prefill_in_stage_pass_strong_channel_decay)")
     T = 150
     wl = small_workload(io, D, "channel", gates, T=T, B=2, Hqk=1, Hv=2, S0=True, scale=D ** -0.5)
     wl = wl.scaled(g_recipe="logsigmoid_n21")  # decay constant c = 1
@@ -147,8 +148,9 @@ def test_prefill_input_stage_strong_channel_decay(io, D, gates):
 
 @pytest.mark.parametrize("io,D,gates", [("bf16", 128, "bw"), ("bf16", 64, "beta"), ("f32", 32, "bw")])
 def test_prefill_in_stage_pass_strong_channel_decay(io, D, gates):
-    """gdr_chunk_fwd_in with a per-channel decay runs the input stage as a
-    pass of its own, then the prefill. Decay inputs x with g = -softplus(x)
+    """gdr_chunk_fwd_in with a per-channel decay runs the convolution and
+    normalisation as a pass of their own, then the prefill, which applies the
+    gate and decay activations as it loads them. Decay inputs x with g = -softplus(x)
     (decay constant 1) give -1.5 held over two chunks on some channels, a
     block of -2.6, and spikes near -30, -45 and -200."""
     T = 200
