@@ -245,7 +245,7 @@ int chunk_call(const gdr_desc *d, const gdr_input_stage *stage, const void *q, c
     a.ws_seg = L.seg_bytes ? reinterpret_cast<float *>(static_cast<char *>(workspace) + L.io_bytes + L.tab_bytes +
                                                        L.kT_bytes)
                            : nullptr;
-    gdr::chunk_segments(d->B, d->H_v, d->d_k, NC, a.P, a.L);
+    gdr::chunk_segments(d->B, d->H_v, d->d_k, NC, io, a.P, a.L);
     a.B = d->B; a.T = d->T; a.Hqk = d->H_qk; a.Hv = d->H_v; a.decay = d->decay; a.NC = NC;
     a.scale = d->scale;
     hipError_t e = hipSuccess;

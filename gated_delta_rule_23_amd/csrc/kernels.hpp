@@ -97,14 +97,23 @@ struct ChunkWsLayout {
 // the chunks are split into P segments that run in parallel from their true
 // entry states, found by a short scan over the segments' transitions. The
 // policy depends only on the shapes (sized for MI355X's 256 compute units),
-// so the workspace size needs no device query.
+// so the workspace size needs no device query. The sweep is split when its
+// 32-column work items would fill at most half the device. With bf16 io at
+// d = 128 the split sweep then runs 64-column work items (half as many per
+// segment), so one more segment still fits the device in one round, and the
+// segment pass (32-column items, two per CU) fills it: P = 1 + 256 / items.
 constexpr int kSegCUs = 256, kSegMinChunks = 16, kSegMax = 8;
-inline void chunk_segments(int B, int Hv, int D, int NC, int &P, int &L) {
+inline void chunk_segments(int B, int Hv, int D, int NC, int io, int &P, int &L) {
     const long long items = (long long)B * Hv * (D / 32);
     long long p = items > 0 ? kSegCUs / items : 1;
     p = p < NC / kSegMinChunks ? p : NC / kSegMinChunks;
     p = p < kSegMax ? p : kSegMax;
     if (p < 2) { P = 1; L = NC; return; }
+    if (io == IO_BF16 && D == 128) {
+        p = 1 + kSegCUs / items;
+        p = p < NC / kSegMinChunks ? p : NC / kSegMinChunks;
+        p = p < kSegMax ? p : kSegMax;
+    }
     L = (int)((NC + p - 1) / p);
     P = (NC + L - 1) / L;
 }
@@ -117,7 +126,7 @@ inline ChunkWsLayout chunk_ws_layout(int B, int Hqk, int Hv, int NC, int D, int 
     L.tab_bytes = align256(units * kTab * sizeof(float));
     L.kT_bytes = chan ? 0 : align256((size_t)2 * B * Hqk * NC * D * kChunk * esz);
     int P, Ls;
-    chunk_segments(B, Hv, D, NC, P, Ls);
+    chunk_segments(B, Hv, D, NC, io, P, Ls);
     L.seg_bytes = P > 1 ? align256((size_t)3 * B * Hv * (P - 1) * D * D * sizeof(float)) : 0;
     return L;
 }

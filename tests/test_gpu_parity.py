@@ -206,14 +206,18 @@ def test_prefill_full_size_sampled(wl, heads, cols):
     assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(ST).all())
 
 
-def _sweep_segments(B, Hv, D, T):
+def _sweep_segments(B, Hv, D, T, io="bf16"):
     """The library's split of a long sweep (256 compute units, at least 16
-    chunks per segment, at most 8 segments), restated to check that a test
-    takes the segmented path."""
+    chunks per segment, at most 8 segments; one more segment with bf16 io at
+    d = 128, whose split sweep runs 64-column work items), restated to check
+    that a test takes the segmented path."""
     NC = -(-T // 64)
-    p = min(256 // (B * Hv * (D // 32)), NC // 16, 8)
+    items = B * Hv * (D // 32)
+    p = min(256 // items, NC // 16, 8)
     if p < 2:
         return 1
+    if io == "bf16" and D == 128:
+        p = min(1 + 256 // items, NC // 16, 8)
     L = -(-NC // p)
     return -(-NC // L)
 
@@ -224,13 +228,14 @@ def _sweep_segments(B, Hv, D, T):
     ("bf16", 128, "channel", "bw", 4113, 1, 1),
     ("f32", 32, "channel", "beta", 2100, 1, 1),
     ("bf16", 64, "channel", "beta", 2100, 1, 2),
+    ("bf16", 128, "channel", "bw", 5200, 16, 1),      # five segments, the last one shorter
 ])
 def test_prefill_segmented_sweep(io, D, decay, gates, T, Hv, B):
     """Long sequences with few heads split the sequential sweep into segments
     that run in parallel from entry states found by a scan over the segments'
     transitions; the result is still the token-by-token recurrence, here from
     a non-zero initial state and with a partial last chunk in one case."""
-    assert _sweep_segments(B, Hv, D, T) > 1
+    assert _sweep_segments(B, Hv, D, T, io) > 1
     wl = small_workload(io, D, decay, gates, T, B=B, Hqk=1, Hv=Hv, S0=True)
     inp = gs.make_inputs(wl, seed=7)
     say(f"segmented {wl.name}")
