@@ -60,6 +60,22 @@ def test_workspace_bytes():
     assert gdr.gdr_chunk_workspace_bytes(d0) == 0
 
 
+@pytest.mark.parametrize("io,segments", [(gdr.GDR_BF16, 5), (gdr.GDR_F32, 4)])
+def test_workspace_bytes_split_sweep(io, segments):
+    """A long sequence with few heads (T = 65536, 16 heads, d = 128): 64 sweep
+    work items of 32 columns fill a quarter of the 256 CUs, so the sweep is
+    split into 4 segments, or 5 with bf16 io (whose split sweep takes 64
+    columns per work item); the workspace adds three d x d fp32 matrices
+    (transition, end state, next entry state) per head and segment but the
+    last."""
+    NC, units = 1024, 16 * 1024
+    esz = 2 if io == gdr.GDR_BF16 else 4
+    d = gdr.make_desc(1, 65536, 16, 16, 128, io, gdr.GDR_DECAY_CHANNEL)
+    expect = (_a256(units * (4 * 64 * 128 + 64 * 64) * esz) + _a256(units * 128 * 4)
+              + _a256(3 * 16 * (segments - 1) * 128 * 128 * 4))
+    assert gdr.gdr_chunk_workspace_bytes(d) == expect
+
+
 P = 0x1000  # a fake non-NULL device pointer: validation never dereferences it
 
 
