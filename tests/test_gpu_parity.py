@@ -309,7 +309,8 @@ def test_hip_graph_replay_matches_eager():
     import gated_delta_rule_23_amd as gdr
     cur = torch.cuda.current_stream
     for wl in (small_workload("bf16", 128, "scalar", "beta", T=300, B=1, Hqk=1, Hv=3, S0=True),
-               small_workload("bf16", 64, "channel", "bw", T=2100, B=1, Hqk=1, Hv=1, S0=True)):
+               small_workload("bf16", 64, "channel", "bw", T=2100, B=1, Hqk=1, Hv=1, S0=True),
+               small_workload("bf16", 128, "channel", "bw", T=2100, B=1, Hqk=1, Hv=1, S0=True)):
         inp = gs.make_inputs(wl, seed=21)
         say(f"graph {wl.name}")
         d = {n: to_dev(inp[n]) for n in ("q", "k", "v", "g", "beta", "b", "w")}
