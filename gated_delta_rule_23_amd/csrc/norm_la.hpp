@@ -19,11 +19,14 @@ struct NlaArgs {
 };
 
 // Segments of the sequence run side by side: P of L chunks each (P = 1 for
-// short sequences or many heads), so that B * Hv * P * (D / 32) workgroups
-// fill the GPU.
+// short sequences or many heads). At d = 128 the sweep's B * Hv * 2 work
+// items of 64 value columns per segment run two per CU, so P is the most
+// segments whose sweep fills the 256 CUs in one round (a second, partial
+// round would cost a whole segment's walk again); at smaller d, P is such
+// that B * Hv * P * (D / 32) workgroups fill the GPU.
 inline void nla_segments(int B, int Hv, int D, int NC, int &P, int &L) {
     const long long items = (long long)B * Hv * (D / 32);
-    long long p = items > 0 ? (2048 + items - 1) / items : 1;
+    long long p = items <= 0 ? 1 : D == 128 ? 512 / (items / 2) : (2048 + items - 1) / items;
     p = p < 32 ? p : 32;
     p = p < NC / 2 ? p : NC / 2;
     if (p < 2) { P = 1; L = NC; return; }

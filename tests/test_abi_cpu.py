@@ -76,6 +76,15 @@ def test_workspace_bytes_split_sweep(io, segments):
     assert gdr.gdr_chunk_workspace_bytes(d) == expect
 
 
+def test_norm_la_workspace_bytes_segments():
+    """Normalised linear attention on the Qwen-like layer (T = 4096, 48 V
+    heads, d = 128): 96 sweep work items of 64 columns per segment at two per
+    CU, so 5 segments fill the 256 CUs in one round; the workspace holds each
+    segment's d x d sum and its d-vector normaliser in fp32."""
+    d = gdr.make_desc(1, 4096, 16, 48, 128, gdr.GDR_BF16, gdr.GDR_DECAY_NONE)
+    assert gdr.gdr_norm_la_workspace_bytes(d) == 48 * 5 * (128 * 128 + 128) * 4
+
+
 P = 0x1000  # a fake non-NULL device pointer: validation never dereferences it
 
 
