@@ -1620,8 +1620,10 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t s) {
     constexpr int NVT = D / (16 * NCT);
     constexpr int PF = sizeof(IO) == 2 ? SWEEP_PF : 1;  // prefetch depth (fp32 fragments are 2x larger)
     // A split sweep with bf16 io at d = 128 runs 64-column work items (the
-    // segment policy counts on it); the segment pass keeps 32-column items.
+    // segment policy counts on it), fetching 2 chunks ahead; the segment
+    // pass keeps 32-column items.
     constexpr int NCTS = sizeof(IO) == 2 && D == 128 ? 4 : NCT, NVTS = D / (16 * NCTS);
+    constexpr int PFS = NCTS != NCT ? 2 : PF;
     if (a.P > 1) {  // segmented: transitions and end states, then the scan over segments
         constexpr int NCT1 = NCT, NVT1 = NVT;
         const int G1 = a.B * a.Hv * (a.P - 1) * 2 * NVT1;
@@ -1639,9 +1641,9 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t s) {
             const int G = a.B * a.Hv * a.P * NVTS;
             const int grid = (G + 7) / 8 * 8;
             if (a.decay == DECAY_CHANNEL)
-                hipLaunchKernelGGL((chunk_sweep<IO, D, NCTS, PF, true>), dim3(grid), dim3(4 * D), 0, s, a, NVTS, G);
+                hipLaunchKernelGGL((chunk_sweep<IO, D, NCTS, PFS, true>), dim3(grid), dim3(4 * D), 0, s, a, NVTS, G);
             else
-                hipLaunchKernelGGL((chunk_sweep<IO, D, NCTS, PF, false>), dim3(grid), dim3(4 * D), 0, s, a, NVTS, G);
+                hipLaunchKernelGGL((chunk_sweep<IO, D, NCTS, PFS, false>), dim3(grid), dim3(4 * D), 0, s, a, NVTS, G);
             return hipGetLastError();
         }
     }
