@@ -1488,37 +1488,63 @@ __global__ __launch_bounds__(2 * D) void chunk_seg_state(ChunkArgs a, int NVT, i
 
 // Segmented sweep, scan over segments: S_in(s + 1) = M_s S_in(s) + N_s in fp32
 // on the matrix cores (v_mfma_f32_16x16x4_f32), one workgroup per (sequence,
-// V head, 16 state columns); S_in(s) stays in shared memory.
+// V head, 16 state columns); S_in(s) stays in shared memory. Each lane reads
+// 4 consecutive entries of an M row at once and feeds them to 4 successive
+// products (the k index of product (j, i) at lane group g is 16 j + 4 g + i,
+// the same for the S_in operand), and the next segment's M and N are
+// fetched while the current one is multiplied.
 template <int D>
 __global__ __launch_bounds__(256) void chunk_seg_combine(ChunkArgs a) {
-    constexpr int NTC = 16;
+    constexpr int NTC = 16, NKG = D / 16;
+    constexpr int RPW = (D / 16 + 3) / 4;  // row tiles per wave
     __shared__ __align__(16) float sIn[D * NTC];
     const int bh = blockIdx.x / (D / NTC), c0 = (blockIdx.x % (D / NTC)) * NTC;
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, lr = l & 15, lg = l >> 4;
     for (int i = tid; i < D * NTC; i += 256)
         sIn[i] = a.S0 ? a.S0[((size_t)bh * D + i / NTC) * D + c0 + i % NTC] : 0.f;
-    constexpr int RPW = (D / 16 + 3) / 4;  // row tiles per wave
-    for (int s = 0; s < a.P - 1; ++s) {
-        const float *M = a.ws_seg + ((size_t)(bh * (a.P - 1) + s) * 3) * D * D, *N = M + D * D;
-        float *Sn = const_cast<float *>(M) + 2 * D * D;
+    const auto seg = [&](int s) { return a.ws_seg + ((size_t)(bh * (a.P - 1) + s) * 3) * D * D; };
+    f32x4 mr[2][RPW][NKG], nv[2][RPW];
+    const auto fetch = [&](int s, auto bc) {
+        constexpr int buf = decltype(bc)::value;
+        const float *M = seg(s), *N = M + D * D;
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            const int rt = w + 4 * i;
+            if (rt < D / 16) {
+#pragma unroll
+                for (int j = 0; j < NKG; ++j) mr[buf][i][j] = load4f(M + (size_t)(16 * rt + lr) * D + 16 * j + 4 * lg);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) nv[buf][i][r] = N[(size_t)(16 * rt + 4 * lg + r) * D + c0 + lr];
+            }
+        }
+    };
+    // Steps alternate between the two operand buffers (compile-time indices,
+    // so the buffers stay in registers).
+    const auto step = [&](int s, auto cc) {
+        constexpr int cur = decltype(cc)::value;
+        if (s + 1 < a.P - 1) fetch(s + 1, std::integral_constant<int, cur ^ 1>{});
+        float *N = seg(s) + D * D, *Sn = seg(s) + 2 * D * D;
         __syncthreads();  // S_in(s) complete
         f32x4 acc[RPW];
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
             const int rt = w + 4 * i;
             if (rt < D / 16) {
+                acc[i] = nv[cur][i];
+                // Once read, N_0 keeps a copy of S0 for the sweep's first
+                // segment (S_T may alias S0).
+                if (s == 0)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 16 * rt + 4 * lg + r;
-                    acc[i][r] = N[(size_t)row * D + c0 + lr];
-                    // Once read, N_0 keeps a copy of S0 for the sweep's first
-                    // segment (S_T may alias S0).
-                    if (s == 0) const_cast<float *>(N)[(size_t)row * D + c0 + lr] = sIn[row * NTC + lr];
-                }
-                const float *Mr = M + (size_t)(16 * rt + lr) * D + lg;
-#pragma unroll 8
-                for (int ks = 0; ks < D / 4; ++ks)
-                    acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(Mr[4 * ks], sIn[(4 * ks + lg) * NTC + lr], acc[i], 0, 0, 0);
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = 16 * rt + 4 * lg + r;
+                        N[(size_t)row * D + c0 + lr] = sIn[row * NTC + lr];
+                    }
+#pragma unroll
+                for (int j = 0; j < NKG; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(mr[cur][i][j][q],
+                                                                      sIn[(16 * j + 4 * lg + q) * NTC + lr], acc[i], 0, 0, 0);
             }
         }
         __syncthreads();  // everyone has read S_in(s)
@@ -1533,6 +1559,11 @@ __global__ __launch_bounds__(256) void chunk_seg_combine(ChunkArgs a) {
                     Sn[(size_t)row * D + c0 + lr] = acc[i][r];
                 }
         }
+    };
+    fetch(0, std::integral_constant<int, 0>{});
+    for (int s = 0; s < a.P - 1; s += 2) {
+        step(s, std::integral_constant<int, 0>{});
+        if (s + 1 < a.P - 1) step(s + 1, std::integral_constant<int, 1>{});
     }
 }
 
