@@ -69,9 +69,27 @@ template <typename IO>
 __device__ __forceinline__ typename Mma<IO>::Frag load_frag(const IO *M, int rt, int ks, int K) {
     return *reinterpret_cast<const typename Mma<IO>::Frag *>(M + frag_slot<IO>(rt, ks, K));
 }
-template <typename IO>
+// NT: a non-temporal store, for workspaces far larger than the memory-side
+// cache (the per-channel prefill's), which it would only churn; a smaller
+// one (the Qwen-shaped layer's 161 MB) stays cached for the sweep.
+template <typename IO, bool NT = false>
 __device__ __forceinline__ void store_frag(IO *M, int rt, int ks, int K, typename Mma<IO>::Frag f) {
-    *reinterpret_cast<typename Mma<IO>::Frag *>(M + frag_slot<IO>(rt, ks, K)) = f;
+    auto *p = reinterpret_cast<typename Mma<IO>::Frag *>(M + frag_slot<IO>(rt, ks, K));
+    if constexpr (NT) __builtin_nontemporal_store(f, p);
+    else *p = f;
+}
+// Four consecutive values to a workspace in the io dtype, as store_frag.
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+template <bool NT>
+__device__ __forceinline__ void store4_ws(float *p, f32x4 x) {
+    if constexpr (NT) __builtin_nontemporal_store(x, reinterpret_cast<f32x4 *>(p));
+    else store4f(p, x);
+}
+template <bool NT>
+__device__ __forceinline__ void store4_ws(bf16_t *p, f32x4 x) {
+    const u32x2 v{f2bf2(x[0], x[1]), f2bf2(x[2], x[3])};
+    if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x2 *>(p));
+    else *reinterpret_cast<u32x2 *>(p) = v;
 }
 // ... and a token-contiguous D x C matrix read in accumulator layout (lane
 // l = col % 16 + 16 (tok % 16) / 4 holds 4 consecutive tokens of one column)
@@ -961,7 +979,7 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
                     const int rt = f / (D / KS), ks = f - rt * (D / KS);
                     Frag x = M::load(tQ + rt * 16 * PD + ks * KS, PD);
                     if constexpr (CHAN && !MILD) x = K::scale(x, sDec + rt * D + ks * KS + FE * lg);
-                    store_frag<IO>(CHAN ? wQ : wQh, rt, ks, D, x);
+                    store_frag<IO, CHAN>(CHAN ? wQ : wQh, rt, ks, D, x);
                 }
             // Kend^T (or raw k^T) fragments: rows = channels, K = tokens, read K-major from the tiles.
             if (write_kT)
@@ -970,7 +988,7 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
                     Frag x = K::frag((DT ? tKe : tK) + ks * KS * PD + rt * 16, PD);
                     if constexpr (CHAN && !DT)  // Kend = K^ . exp(G_end - R_{b+1}), b = the fragment's token block
                         x = K::scale(x, sDec[(MILD ? 15 : 11 + ((ks * KS + FE * lg) >> 4)) * D + rt * 16 + lr]);
-                    store_frag<IO>(wKT, rt, ks, C, x);
+                    store_frag<IO, CHAN>(wKT, rt, ks, C, x);
                 }
         };
         if (!CHAN || mild) gram(std::true_type{});
@@ -982,7 +1000,7 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
         // ---- C. A to the workspace; L = (I + T)^-1 ----
         for (int f = w; f < (C / 16) * (C / KS); f += NW) {
             const int rt = f / (C / KS), ks = f - rt * (C / KS);
-            store_frag<IO>(wA, rt, ks, C, K::frag(sAc + ks * KS * LC + rt * 16, LC));
+            store_frag<IO, CHAN>(wA, rt, ks, C, K::frag(sAc + ks * KS * LC + rt * 16, LC));
         }
         // Diagonal block w of L: (I + T_ww)^-1 by fp32 substitution, lane lr < 16 forms column lr.
         float xd[16];
@@ -1060,7 +1078,7 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
 #pragma unroll
                     for (int ks = 0; ks < NKS; ++ks)
                         if (ks * KS < 16 * ri + 16) acc = M::mma(acc, la[ri][ks], bf[ks]);
-                    if (zside) store4f(wUzT + cfrag_off<D>(c0 - D + lr, 16 * ri + 4 * lg), acc);
+                    if (zside) store4_ws<CHAN>(wUzT + cfrag_off<D>(c0 - D + lr, 16 * ri + 4 * lg), acc);
                     else store4f(sYc + (c0 + lr) * LY + 16 * ri + 4 * lg, acc);
                 }
             }
@@ -1070,7 +1088,7 @@ __global__ __launch_bounds__(256, (prep_occupancy<IO, D, CHAN, BW>())) void chun
         // ---- E. Y to the workspace ----
         for (int f = w; f < (C / 16) * (D / KS); f += NW) {
             const int rt = f / (D / KS), ks = f - rt * (D / KS);
-            store_frag<IO>(wY, rt, ks, D, K::frag(sYc + ks * KS * LY + rt * 16, LY));
+            store_frag<IO, CHAN>(wY, rt, ks, D, K::frag(sYc + ks * KS * LY + rt * 16, LY));
         }
         if (!GROUPED || ++hh == PG) {
             hh = 0;
