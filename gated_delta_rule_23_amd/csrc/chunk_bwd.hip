@@ -114,6 +114,10 @@ struct Cfg {
 __device__ __forceinline__ f32x4 lds4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
 __device__ __forceinline__ void sts4(float *p, f32x4 v) { *reinterpret_cast<f32x4 *>(p) = v; }
 __device__ __forceinline__ f32x4 splat(float x) { return f32x4{x, x, x, x}; }
+// Workspace stores between the passes, non-temporal: the fp32 factors,
+// states and partial gradients of one call (0.5-3 GB a pass at these
+// shapes) outgrow the memory-side cache, so caching them only churns it.
+__device__ __forceinline__ void stg4(float *p, f32x4 v) { __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(p)); }
 __device__ __forceinline__ float dot4(f32x4 a, f32x4 b, float acc) {
     return fmaf(a[3], b[3], fmaf(a[2], b[2], fmaf(a[1], b[1], fmaf(a[0], b[0], acc))));
 }
@@ -420,8 +424,8 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
                     kv[r] *= expf(sGs[C - 1] - sGs[t + r]);
                 }
             }
-            sts4(a.wQt + ucd + e, qv);
-            sts4(a.wKet + ucd + e, kv);
+            stg4(a.wQt + ucd + e, qv);
+            stg4(a.wKet + ucd + e, kv);
         }
 
         // T and A on the matrix cores: the ten 16 x 16 tiles (bi, bj) on and
@@ -531,8 +535,8 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
                             aA[i][j] = c0 + j <= t ? aA[i][j] : 0.f;
                         }
                         const size_t o = (size_t)u * C * C + (size_t)t * C + c0;
-                        sts4(a.wT + o, f32x4{sT8[i][0], sT8[i][1], sT8[i][2], sT8[i][3]});
-                        sts4(a.wA + o, f32x4{aA[i][0], aA[i][1], aA[i][2], aA[i][3]});
+                        stg4(a.wT + o, f32x4{sT8[i][0], sT8[i][1], sT8[i][2], sT8[i][3]});
+                        stg4(a.wA + o, f32x4{aA[i][0], aA[i][1], aA[i][2], aA[i][3]});
                     }
                 }
             }
@@ -594,13 +598,13 @@ __global__ __launch_bounds__(NT) void cb_prep(ChunkBwdArgs a) {
         for (int l = 0; l < NL; ++l) {
             int e, t, d;
             rc<D>(l, e, t, d, tid);
-            sts4(a.wUz + ucd + e, lds4(sZ + t * LD + d));
+            stg4(a.wUz + ucd + e, lds4(sZ + t * LD + d));
         }
 #pragma unroll
         for (int l = 0; l < NL; ++l) {  // Y^T
             int e, dd, t;
             rc<C>(l, e, dd, t, tid);
-            sts4(a.wYt + ucd + e, f32x4{sE[t * LD + dd], sE[(t + 1) * LD + dd], sE[(t + 2) * LD + dd], sE[(t + 3) * LD + dd]});
+            stg4(a.wYt + ucd + e, f32x4{sE[t * LD + dd], sE[(t + 1) * LD + dd], sE[(t + 2) * LD + dd], sE[(t + 3) * LD + dd]});
         }
         lds_barrier();  // shared memory read; the next unit overwrites it
     }
@@ -826,7 +830,7 @@ __device__ __forceinline__ void fsweep(const ChunkBwdArgs &a, float *smem, int i
         for (int r = 0; r < 4; ++r) uz[r] = pZ[r];
         for (int i = tid; i < D * BV / 4; i += NS) {
             const int d = 4 * i / BV, j = 4 * i - d * BV;
-            sts4(a.wS + u * D * D + (size_t)d * D + col0 + j, lds4(sS + d * LB + j));
+            stg4(a.wS + u * D * D + (size_t)d * D + col0 + j, lds4(sS + d * LB + j));
         }
         lds_barrier();
         {  // U = U_z - Y S
@@ -994,7 +998,7 @@ __device__ __forceinline__ void bsweep_full(const ChunkBwdArgs &a, float *smem, 
         if (tid < D) sGam[tid] = pg;
         for (int i = tid; i < D * BV / 4; i += NS) {
             const int d = 4 * i / BV, j = 4 * i - d * BV;
-            sts4(a.wdS + u * D * D + (size_t)d * D + col0 + j, lds4(sX + d * LB + j));
+            stg4(a.wdS + u * D * D + (size_t)d * D + col0 + j, lds4(sX + d * LB + j));
         }
         lds_barrier();
         {  // dU = s A^T dO + Kend X
@@ -1159,7 +1163,7 @@ __device__ __forceinline__ void bsweep_rhs(const ChunkBwdArgs &a, float *smem, i
         for (int q = 0; q < NXT; ++q) bv[q] = pB[q];
         for (int i = tid; i < D * BV / 4; i += NS) {
             const int d = 4 * i / BV, j = 4 * i - d * BV;
-            sts4(a.wdS + u * D * D + (size_t)d * D + col0 + j, lds4(sX + d * LB + j));
+            stg4(a.wdS + u * D * D + (size_t)d * D + col0 + j, lds4(sX + d * LB + j));
         }
         lds_barrier();
         {  // V = Kend X; dU = p + V
@@ -1349,7 +1353,7 @@ __global__ __launch_bounds__(NT) void cb_grad_s(ChunkBwdArgs a) {
         for (int l = 0; l < NL; ++l) {
             int e, t, d;
             rc<D>(l, e, t, d, tid);
-            sts4(a.wdU + ucd + e, lds4(sX + t * LD + d));  // dR replaces dU
+            stg4(a.wdU + ucd + e, lds4(sX + t * LD + d));  // dR replaces dU
         }
         {
             // dT = -dR U^T (strictly lower) and dA = s dO U^T (lower) on the matrix
