@@ -31,7 +31,11 @@
 // keeps the fp32 state in matrix-core accumulator registers and per chunk
 // does U = U_z - Y S_c, O = s (Q~ S_c + A U) and
 // S_{c+1} = gamma . S_c + Kend^T U. Value columns of the state evolve
-// independently, so the sweep is split over value tiles.
+// independently, so the sweep is split over value tiles. When few work items
+// would leave the device idle on a long sequence, the sweep is also split
+// over time: chunk_seg_state forms each segment's affine map (transition and
+// end state from zero), chunk_seg_combine chains the maps into each
+// segment's entry state, and chunk_sweep runs the segments side by side.
 //
 // Matrix products run on gfx950 MFMA: bf16 operands with fp32 accumulation
 // for bfloat16 io, fp32 operands for float32 io. The triangular inverse is
