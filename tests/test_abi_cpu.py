@@ -76,6 +76,24 @@ def test_workspace_bytes_split_sweep(io, segments):
     assert gdr.gdr_chunk_workspace_bytes(d) == expect
 
 
+@pytest.mark.parametrize("io", [gdr.GDR_BF16, gdr.GDR_F32])
+@pytest.mark.parametrize("B,T,Hv,D", [(1, 65536, 16, 128), (1, 4113, 1, 128), (1, 2200, 1, 128), (1, 4096, 48, 128),
+                                      (2, 16384, 32, 128), (1, 2500, 2, 64), (2, 2100, 1, 64), (1, 2100, 1, 32),
+                                      (1, 5200, 16, 128), (3, 9000, 4, 128), (1, 640, 2, 128)])
+def test_workspace_matches_segment_policy(io, B, T, Hv, D):
+    """The segment count the GPU tests restate (to know which cases take the
+    split sweep) is the one the library sizes its workspace for: three d x d
+    fp32 matrices per (sequence, V head, segment but the last)."""
+    from parity_util import sweep_segments
+    NC, units = -(-T // 64), B * Hv * -(-T // 64)
+    esz = 2 if io == gdr.GDR_BF16 else 4
+    P = sweep_segments(B, Hv, D, T, "bf16" if io == gdr.GDR_BF16 else "f32")
+    d = gdr.make_desc(B, T, Hv, Hv, D, io, gdr.GDR_DECAY_CHANNEL)
+    expect = (_a256(units * (4 * 64 * D + 64 * 64) * esz) + _a256(units * 128 * 4)
+              + (_a256(3 * B * Hv * (P - 1) * D * D * 4) if P > 1 else 0))
+    assert gdr.gdr_chunk_workspace_bytes(d) == expect
+
+
 def test_norm_la_workspace_bytes_segments():
     """Normalised linear attention on the Qwen-like layer (T = 4096, 48 V
     heads, d = 128): 96 sweep work items of 64 columns per segment at two per

@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 
 import gdr_synth as gs
+from parity_util import sweep_segments as _sweep_segments
 from parity_util import (TOL, from_dev, gpu_decode, gpu_prefill, gpu_prefill_in, gpu_recurrent, gpu_recurrent_in,
                          oracle_input_stage, oracle_prefill, out_err, record, rel_err, say, small_workload,
                          strong_channel_decay, to_dev)
@@ -204,22 +205,6 @@ def test_prefill_full_size_sampled(wl, heads, cols):
     assert out_err(o_g, o_ref[:, :, heads, c0:c1]) < TOL["bf16"]
     assert rel_err(S_g, S_ref[:, heads, :, c0:c1]) < TOL["bf16"]
     assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(ST).all())
-
-
-def _sweep_segments(B, Hv, D, T, io="bf16"):
-    """The library's split of a long sweep (256 compute units, at least 16
-    chunks per segment, at most 8 segments; one more segment with bf16 io at
-    d = 128, whose split sweep runs 64-column work items), restated to check
-    that a test takes the segmented path."""
-    NC = -(-T // 64)
-    items = B * Hv * (D // 32)
-    p = min(256 // items, NC // 16, 8)
-    if p < 2:
-        return 1
-    if io == "bf16" and D == 128:
-        p = min(1 + 256 // items, NC // 16, 8)
-    L = -(-NC // p)
-    return -(-NC // L)
 
 
 @pytest.mark.parametrize("io,D,decay,gates,T,Hv,B", [
