@@ -1447,9 +1447,11 @@ __global__ __launch_bounds__(4 * D) void chunk_sweep(ChunkArgs a, int NVT, int G
 // Segmented sweep, first pass: for every segment but the last, run the state
 // chain from a zero entry state to get the segment's end state N, and on d_k
 // more columns from the identity with U_z = 0 to get its transition M (the
-// state after the segment is M S_in + N). Chain waves only.
+// state after the segment is M S_in + N). Chain waves only. Fetching one chunk
+// ahead, the pass is held to at least three waves per SIMD, so that three of
+// its workgroups share a compute unit and hide each other's loads.
 template <typename IO, int D, int NCT, int PF, bool CHAN>
-__global__ __launch_bounds__(2 * D) void chunk_seg_state(ChunkArgs a, int NVT, int G) {
+__global__ __launch_bounds__(2 * D, (PF == 1 ? 3 : 1)) void chunk_seg_state(ChunkArgs a, int NVT, int G) {
     using Sh = SweepShape<IO, D, NCT>;
     constexpr int BV = Sh::BV, LS = Sh::LS, LU = Sh::LU;
     __shared__ __align__(16) IO sST[BV * LS];
@@ -1678,11 +1680,13 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t s) {
     constexpr int NCTS = sizeof(IO) == 2 && D == 128 ? 4 : NCT, NVTS = D / (16 * NCTS);
     constexpr int PFS = NCTS != NCT ? 2 : PF;
     if (a.P > 1) {  // segmented: transitions and end states, then the scan over segments
+        // With per-channel decay the segment pass fetches one chunk ahead and
+        // runs three workgroups per CU instead of prefetching deeper.
         constexpr int NCT1 = NCT, NVT1 = NVT;
         const int G1 = a.B * a.Hv * (a.P - 1) * 2 * NVT1;
         const int grid1 = (G1 + 7) / 8 * 8;
         if (a.decay == DECAY_CHANNEL)
-            hipLaunchKernelGGL((chunk_seg_state<IO, D, NCT1, PF, true>), dim3(grid1), dim3(2 * D), 0, s, a, NVT1, G1);
+            hipLaunchKernelGGL((chunk_seg_state<IO, D, NCT1, 1, true>), dim3(grid1), dim3(2 * D), 0, s, a, NVT1, G1);
         else
             hipLaunchKernelGGL((chunk_seg_state<IO, D, NCT1, PF, false>), dim3(grid1), dim3(2 * D), 0, s, a, NVT1, G1);
         hipLaunchKernelGGL((chunk_seg_combine<D>), dim3(a.B * a.Hv * (D / 16)), dim3(256), 0, s, a);

@@ -188,15 +188,16 @@ def strong_channel_decay(g, T, D):
 
 def sweep_segments(B, Hv, D, T, io="bf16"):
     """The library's split of a long sweep (256 compute units, at least 16
-    chunks per segment, at most 8 segments; one more segment with bf16 io at
-    d = 128, whose split sweep runs 64-column work items), restated to check
-    that a test takes the segmented path."""
+    chunks per segment, at most 8 segments; half again as many with bf16 io
+    at d = 128, whose split sweep runs 64-column work items and whose segment
+    pass runs three work items per CU), restated to check that a test takes
+    the segmented path."""
     NC = -(-T // 64)
     items = B * Hv * (D // 32)
     p = min(256 // items, NC // 16, 8)
     if p < 2:
         return 1
     if io == "bf16" and D == 128:
-        p = min(1 + 256 // items, NC // 16, 8)
+        p = min(1 + 384 // items, NC // 16, 8)
     L = -(-NC // p)
     return -(-NC // L)

@@ -60,12 +60,13 @@ def test_workspace_bytes():
     assert gdr.gdr_chunk_workspace_bytes(d0) == 0
 
 
-@pytest.mark.parametrize("io,segments", [(gdr.GDR_BF16, 5), (gdr.GDR_F32, 4)])
+@pytest.mark.parametrize("io,segments", [(gdr.GDR_BF16, 7), (gdr.GDR_F32, 4)])
 def test_workspace_bytes_split_sweep(io, segments):
     """A long sequence with few heads (T = 65536, 16 heads, d = 128): 64 sweep
     work items of 32 columns fill a quarter of the 256 CUs, so the sweep is
-    split into 4 segments, or 5 with bf16 io (whose split sweep takes 64
-    columns per work item); the workspace adds three d x d fp32 matrices
+    split into 4 segments, or 1 + 384 / 64 = 7 with bf16 io (whose split sweep
+    takes 64 columns per work item and whose segment pass runs three work
+    items per CU); the workspace adds three d x d fp32 matrices
     (transition, end state, next entry state) per head and segment but the
     last."""
     NC, units = 1024, 16 * 1024
