@@ -121,8 +121,10 @@ int gdr_state_free(float *state);
  * (d_k float32); with a scalar decay (or none) instead two per-token decay
  * tables (2 C float32), and one k^T (d_k x C) and one q (C x d_k), io dtype,
  * per (sequence, QK head, chunk). For long sequences with few heads it also
- * holds, per (sequence, V head, sweep segment), three d_k x d_v float32
- * matrices of the segmented sweep. Returns 0 bytes when B or T is 0. */
+ * holds, per (sequence, V head, sweep segment but the last), three
+ * d_k x d_v float32 matrices of the segmented sweep (the segment's
+ * transition, its end state from a zero entry, and the entry state of the
+ * next segment). Returns 0 bytes when B or T is 0. */
 int gdr_chunk_workspace_bytes(const gdr_desc *desc, size_t *bytes);
 
 /* Chunkwise-parallel prefill over T tokens: "Chunkwise KDA" and "Pipeline
